@@ -1,0 +1,194 @@
+"""Python binding of librq, the C-ABI ResidualQuant decode library for MI355X.
+
+Argument marshalling only: every step of the decode path (rotation,
+quantization, packing, fused dequantize + attention, combine) runs in the HIP
+kernels of ``librq.so``. PyTorch provides device memory and streams.
+
+Importing this package loads ``librq.so`` from the package directory and fails
+loudly if it is missing; build it with ``python -m
+decode_attention_quantize_amd.build`` (or ``__graft_entry__.build()``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librq.so")
+MAX_LOOPS = 16
+
+OK = 0
+STATUS = {0: "RQ_OK", 1: "RQ_E_NULL", 2: "RQ_E_SHAPE", 3: "RQ_E_BITS", 4: "RQ_E_CAPACITY",
+          5: "RQ_E_WORKSPACE", 6: "RQ_E_UNSUPPORTED", 7: "RQ_E_HIP", 8: "RQ_E_POLICY", 9: "RQ_E_LOOP"}
+POLICY_LAST_LOOP, POLICY_PREV_LOOP = 0, 1
+DEVERR_CAPACITY, DEVERR_LENGTH = 1, 2
+
+
+class RQError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {STATUS.get(code, code)} ({status_str(code)})")
+        self.code = code
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("loops", ctypes.c_int32), ("max_tokens", ctypes.c_int32), ("policy", ctypes.c_int32),
+                ("bits", ctypes.c_uint8 * MAX_LOOPS), ("group", ctypes.c_uint8 * MAX_LOOPS)]
+
+
+class LayerCacheC(ctypes.Structure):
+    _fields_ = [("codes", (ctypes.c_void_p * MAX_LOOPS) * 2), ("meta", (ctypes.c_void_p * MAX_LOOPS) * 2),
+                ("alpha", (ctypes.c_void_p * MAX_LOOPS) * 2), ("rot", ctypes.c_void_p * 2)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"librq.so not found at {LIB_PATH}; build it first "
+                          "(python -m decode_attention_quantize_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    L.rq_buffer_bytes.restype = Z
+    L.rq_buffer_bytes.argtypes = [P, ctypes.c_int, ctypes.c_int]
+    L.rq_workspace_bytes.restype = Z
+    L.rq_workspace_bytes.argtypes = [P]
+    L.rq_check_desc.restype = ctypes.c_int
+    L.rq_check_desc.argtypes = [P]
+    L.rq_quantize_append.restype = ctypes.c_int
+    L.rq_quantize_append.argtypes = [P, P, P, P, I, P, P]
+    L.rq_decode_attn.restype = ctypes.c_int
+    L.rq_decode_attn.argtypes = [P, P, I, P, P, P, P, ctypes.c_float, P, P, Z, P, P]
+    L.rq_decode_attn_bf16.restype = ctypes.c_int
+    L.rq_decode_attn_bf16.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, P, P, Z, P, P]
+    L.rq_status_str.restype = ctypes.c_char_p
+    L.rq_status_str.argtypes = [ctypes.c_int]
+    L.rq_version.restype = ctypes.c_char_p
+    L.rq_version.argtypes = []
+    return L
+
+
+lib = _load()
+
+
+def status_str(code: int) -> str:
+    return lib.rq_status_str(code).decode()
+
+
+def version() -> str:
+    return lib.rq_version().decode()
+
+
+def make_desc(batch: int, heads: int, head_dim: int, bits, max_tokens: int,
+              policy: int = POLICY_LAST_LOOP, group: int = 32) -> Desc:
+    d = Desc()
+    d.batch, d.heads, d.head_dim = batch, heads, head_dim
+    d.loops, d.max_tokens, d.policy = len(bits), max_tokens, policy
+    for r, b in enumerate(bits):
+        d.bits[r] = b
+        d.group[r] = group
+    return d
+
+
+def check_desc(d: Desc) -> int:
+    return lib.rq_check_desc(ctypes.byref(d))
+
+
+def buffer_bytes(d: Desc, kind: int, loop: int) -> int:
+    return lib.rq_buffer_bytes(ctypes.byref(d), kind, loop)
+
+
+def workspace_bytes(d: Desc) -> int:
+    return lib.rq_workspace_bytes(ctypes.byref(d))
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if isinstance(stream, int):
+        return stream
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+@dataclass
+class LayerCache:
+    """Device buffers of one layer's compressed cache (caller-owned, allocated by torch)."""
+    desc: Desc
+    codes: list      # [2][L] uint8 tensors [B][H][T_max][D*bits/8]
+    meta: list       # [2][L] int16 tensors [B][H][T_max][D/32][2] (fp16 bit patterns)
+    alpha: list      # [2][L] int16 tensors [B][H][T_max] or None for the anchor
+    rot: list        # [2] float32 [H][D][D]
+
+    @staticmethod
+    def allocate(d: Desc, rot_k: torch.Tensor, rot_v: torch.Tensor, device="cuda") -> "LayerCache":
+        B, H, T, D, L = d.batch, d.heads, d.max_tokens, d.head_dim, d.loops
+        anchor = L - 1 if d.policy == POLICY_LAST_LOOP else 0
+        codes = [[torch.empty(B, H, T, D * d.bits[r] // 8, dtype=torch.uint8, device=device)
+                  for r in range(L)] for _ in range(2)]
+        meta = [[torch.empty(B, H, T, D // d.group[r], 2, dtype=torch.int16, device=device)
+                 for r in range(L)] for _ in range(2)]
+        alpha = [[None if r == anchor else torch.empty(B, H, T, dtype=torch.int16, device=device)
+                  for r in range(L)] for _ in range(2)]
+        rot = [rot_k.to(device=device, dtype=torch.float32).contiguous(),
+               rot_v.to(device=device, dtype=torch.float32).contiguous()]
+        return LayerCache(d, codes, meta, alpha, rot)
+
+    def c(self) -> LayerCacheC:
+        c = LayerCacheC()
+        for kv in range(2):
+            for r in range(self.desc.loops):
+                c.codes[kv][r] = _ptr(self.codes[kv][r])
+                c.meta[kv][r] = _ptr(self.meta[kv][r])
+                c.alpha[kv][r] = _ptr(self.alpha[kv][r])
+            c.rot[kv] = _ptr(self.rot[kv])
+        return c
+
+    def nbytes(self) -> int:
+        n = 0
+        for kv in range(2):
+            for r in range(self.desc.loops):
+                n += self.codes[kv][r].numel() + 2 * self.meta[kv][r].numel()
+                if self.alpha[kv][r] is not None:
+                    n += 2 * self.alpha[kv][r].numel()
+        return n
+
+
+def _check(code: int, where: str):
+    if code != OK:
+        raise RQError(code, where)
+
+
+def quantize_append(cache: LayerCache, kv: torch.Tensor, pos: torch.Tensor, n: int,
+                    dev_err: torch.Tensor | None = None, stream=None):
+    """kv: bf16 [2][L][B][H][n][D]; pos: int32 [B] on the device."""
+    cc = cache.c()
+    _check(lib.rq_quantize_append(ctypes.byref(cache.desc), ctypes.byref(cc), _ptr(kv), _ptr(pos), n,
+                                  _ptr(dev_err), _stream(stream)), "rq_quantize_append")
+
+
+def decode_attn(cache: LayerCache, loop: int, q, k_cur, v_cur, past_len, scale: float, out, workspace,
+                dev_err=None, stream=None):
+    cc = cache.c()
+    _check(lib.rq_decode_attn(ctypes.byref(cache.desc), ctypes.byref(cc), loop, _ptr(q), _ptr(k_cur),
+                              _ptr(v_cur), _ptr(past_len), scale, _ptr(out), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _ptr(dev_err), _stream(stream)),
+           "rq_decode_attn")
+
+
+def decode_attn_bf16(d: Desc, k_cache, v_cache, q, k_cur, v_cur, past_len, scale: float, out, workspace,
+                     dev_err=None, stream=None):
+    _check(lib.rq_decode_attn_bf16(ctypes.byref(d), _ptr(k_cache), _ptr(v_cache), _ptr(q), _ptr(k_cur),
+                                   _ptr(v_cur), _ptr(past_len), scale, _ptr(out), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _ptr(dev_err),
+                                   _stream(stream)), "rq_decode_attn_bf16")
+
+
+def alloc_workspace(d: Desc, device="cuda") -> torch.Tensor:
+    n = workspace_bytes(d)
+    # torch's caching allocator returns blocks aligned to at least 512 bytes
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)

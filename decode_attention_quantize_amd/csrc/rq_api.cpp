@@ -1,0 +1,282 @@
+// Host side of librq: argument validation, buffer sizes, split planning and
+// kernel dispatch for the C ABI declared in include/rq.h.
+#include <cmath>
+#include <cstring>
+
+#include "rq_internal.hpp"
+
+namespace rq {
+
+SplitPlan split_plan(const rq_desc* d) {
+  // Enough (b, h, split) workgroups to keep every CU busy several times over,
+  // each wave walking at least one full tile; chunks are whole workgroup passes.
+  const int unit = kWaves * tile_tokens(d->head_dim);
+  const long long bh = (long long)d->batch * d->heads;
+  const long long target_wgs = 2048;
+  long long chunk = ((long long)d->max_tokens * bh + target_wgs - 1) / target_wgs;
+  chunk = ((chunk + unit - 1) / unit) * unit;
+  if (chunk < unit) chunk = unit;
+  if (chunk > 64LL * unit) chunk = 64LL * unit;
+  SplitPlan p;
+  p.chunk = (int)chunk;
+  p.nsplit = (int)((d->max_tokens + chunk - 1) / chunk);
+  return p;
+}
+
+}  // namespace rq
+
+using namespace rq;
+
+namespace {
+
+bool dim_ok(int D) { return D == 64 || D == 96 || D == 128; }
+
+rq_status check_shape(const rq_desc* d) {
+  if (!d) return RQ_E_NULL;
+  if (d->batch < 1 || d->heads < 1 || !dim_ok(d->head_dim) || d->loops < 1 || d->loops > RQ_MAX_LOOPS ||
+      d->max_tokens < 1)
+    return RQ_E_SHAPE;
+  return RQ_OK;
+}
+
+rq_status check_plan(const rq_desc* d) {
+  rq_status s = check_shape(d);
+  if (s != RQ_OK) return s;
+  if (d->policy != RQ_POLICY_LAST_LOOP && d->policy != RQ_POLICY_PREV_LOOP) return RQ_E_POLICY;
+  for (int r = 0; r < d->loops; ++r) {
+    if (d->bits[r] != 2 && d->bits[r] != 4) return RQ_E_BITS;
+    if (d->group[r] != 32) return RQ_E_BITS;
+  }
+  return RQ_OK;
+}
+
+int anchor_loop(const rq_desc* d) { return d->policy == RQ_POLICY_LAST_LOOP ? d->loops - 1 : 0; }
+
+size_t workspace_for(const rq_desc* d) {
+  const SplitPlan sp = split_plan(d);
+  const size_t bh = (size_t)d->batch * d->heads;
+  const size_t q = bh * qprep_words(d->head_dim) * 4;
+  const size_t qa = (q + 255) & ~(size_t)255;
+  return qa + bh * sp.nsplit * part_floats(d->head_dim) * 4;
+}
+
+// Components decode loop r reads, in order anchor first (§3.2, App. D).
+int components(const rq_desc* d, int r, int* loops) {
+  if (d->policy == RQ_POLICY_LAST_LOOP) {
+    const int a = d->loops - 1;
+    loops[0] = a;
+    if (r == a) return 1;
+    loops[1] = r;
+    return 2;
+  }
+  for (int c = 0; c <= r; ++c) loops[c] = c;
+  return r + 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rq_status_str(rq_status s) {
+  switch (s) {
+    case RQ_OK: return "ok";
+    case RQ_E_NULL: return "required pointer is NULL";
+    case RQ_E_SHAPE: return "shape out of range (batch, heads, head_dim in {64,96,128}, loops 1..16, max_tokens >= 1, n)";
+    case RQ_E_BITS: return "unsupported bit width or group size (bits 2 or 4, group 32)";
+    case RQ_E_CAPACITY: return "size exceeds max_tokens";
+    case RQ_E_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case RQ_E_UNSUPPORTED: return "no kernel for this combination (e.g. more than 4 chained components)";
+    case RQ_E_HIP: return "HIP launch failed";
+    case RQ_E_POLICY: return "unknown reference policy";
+    case RQ_E_LOOP: return "loop index out of range";
+  }
+  return "unknown status";
+}
+
+const char* rq_version(void) { return "rq 0.1 (gfx950)"; }
+
+rq_status rq_check_desc(const rq_desc* d) { return check_plan(d); }
+
+size_t rq_buffer_bytes(const rq_desc* d, int kind, int loop) {
+  if (check_plan(d) != RQ_OK || loop < 0 || loop >= d->loops) return 0;
+  const size_t toks = (size_t)d->batch * d->heads * d->max_tokens;
+  switch (kind) {
+    case 0: return toks * d->head_dim * d->bits[loop] / 8;
+    case 1: return toks * (d->head_dim / d->group[loop]) * 4;
+    case 2: return toks * 2;
+  }
+  return 0;
+}
+
+size_t rq_workspace_bytes(const rq_desc* d) {
+  if (check_shape(d) != RQ_OK) return 0;
+  return workspace_for(d);
+}
+
+rq_status rq_quantize_append(const rq_desc* d, const rq_layer_cache* c, const uint16_t* kv,
+                             const int32_t* pos, int32_t n, int32_t* dev_err, void* stream) {
+  rq_status s = check_plan(d);
+  if (s != RQ_OK) return s;
+  if (!c) return RQ_E_NULL;
+  if (n < 0) return RQ_E_SHAPE;
+  if (n > d->max_tokens) return RQ_E_CAPACITY;
+  if (n == 0) return RQ_OK;
+  if (!kv || !pos || !c->rot[0] || !c->rot[1]) return RQ_E_NULL;
+  const int a = anchor_loop(d);
+  AppendParams p;
+  std::memset(&p, 0, sizeof(p));
+  for (int kvi = 0; kvi < 2; ++kvi) {
+    for (int r = 0; r < d->loops; ++r) {
+      if (!c->codes[kvi][r] || !c->meta[kvi][r]) return RQ_E_NULL;
+      if (r != a && !c->alpha[kvi][r]) return RQ_E_NULL;
+      p.codes[kvi][r] = c->codes[kvi][r];
+      p.meta[kvi][r] = reinterpret_cast<uint32_t*>(c->meta[kvi][r]);
+      p.alpha[kvi][r] = c->alpha[kvi][r];
+    }
+    p.rot[kvi] = c->rot[kvi];
+  }
+  p.kv = kv;
+  p.pos = pos;
+  p.dev_err = dev_err;
+  p.B = d->batch;
+  p.H = d->heads;
+  p.L = d->loops;
+  p.n = n;
+  p.T_max = d->max_tokens;
+  p.policy = d->policy;
+  for (int r = 0; r < d->loops; ++r) p.bits[r] = d->bits[r];
+  return launch_append(p, d->head_dim, stream) == 0 ? RQ_OK : RQ_E_HIP;
+}
+
+rq_status rq_decode_attn(const rq_desc* d, const rq_layer_cache* c, int32_t loop, const uint16_t* q,
+                         const uint16_t* k_cur, const uint16_t* v_cur, const int32_t* past_len,
+                         float softmax_scale, float* out, void* ws, size_t ws_bytes, int32_t* dev_err,
+                         void* stream) {
+  rq_status s = check_plan(d);
+  if (s != RQ_OK) return s;
+  if (!c) return RQ_E_NULL;
+  if (loop < 0 || loop >= d->loops) return RQ_E_LOOP;
+  if (!q || !k_cur || !v_cur || !past_len || !out || !c->rot[0] || !c->rot[1]) return RQ_E_NULL;
+  if (!ws || ws_bytes < workspace_for(d) || ((uintptr_t)ws & 255) != 0) return RQ_E_WORKSPACE;
+  if (!std::isfinite(softmax_scale)) return RQ_E_SHAPE;
+  int loops[RQ_MAX_LOOPS];
+  const int nc = components(d, loop, loops);
+  if (nc > kMaxComp) return RQ_E_UNSUPPORTED;
+  int bits[kMaxComp];
+  for (int i = 0; i < nc; ++i) bits[i] = d->bits[loops[i]];
+  if (!have_decode_kernel(d->head_dim, nc, bits)) return RQ_E_UNSUPPORTED;
+
+  const SplitPlan sp = split_plan(d);
+  const int D = d->head_dim;
+  const size_t bh = (size_t)d->batch * d->heads;
+  uint32_t* qprep = static_cast<uint32_t*>(ws);
+  const size_t qa = ((bh * qprep_words(D) * 4) + 255) & ~(size_t)255;
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + qa);
+  const float scale_log2 = softmax_scale * 1.4426950408889634f;
+
+  DecodeParams p;
+  std::memset(&p, 0, sizeof(p));
+  for (int i = 0; i < nc; ++i) {
+    const int r = loops[i];
+    if (!c->codes[0][r] || !c->meta[0][r] || !c->codes[1][r] || !c->meta[1][r]) return RQ_E_NULL;
+    p.kcodes[i] = c->codes[0][r];
+    p.kmeta[i] = reinterpret_cast<const uint32_t*>(c->meta[0][r]);
+    p.vcodes[i] = c->codes[1][r];
+    p.vmeta[i] = reinterpret_cast<const uint32_t*>(c->meta[1][r]);
+    if (i > 0) {
+      if (!c->alpha[0][r] || !c->alpha[1][r]) return RQ_E_NULL;
+      p.kalpha[i] = c->alpha[0][r];
+      p.valpha[i] = c->alpha[1][r];
+    }
+  }
+  p.past_len = past_len;
+  p.qprep = qprep;
+  p.part = part;
+  p.dev_err = dev_err;
+  p.B = d->batch;
+  p.H = d->heads;
+  p.T_max = d->max_tokens;
+  p.chunk = sp.chunk;
+  p.nsplit = sp.nsplit;
+
+  QPrepParams qp;
+  qp.q = q;
+  qp.rotk = c->rot[0];
+  qp.qprep = qprep;
+  qp.scale_log2 = scale_log2;
+  qp.B = d->batch;
+  qp.H = d->heads;
+
+  CombineParams cp;
+  cp.part = part;
+  cp.past_len = past_len;
+  cp.q = q;
+  cp.kcur = k_cur;
+  cp.vcur = v_cur;
+  cp.rotv = c->rot[1];
+  cp.out = out;
+  cp.dev_err = dev_err;
+  cp.scale_log2 = scale_log2;
+  cp.B = d->batch;
+  cp.H = d->heads;
+  cp.T_max = d->max_tokens;
+  cp.chunk = sp.chunk;
+  cp.nsplit = sp.nsplit;
+
+  if (launch_qprep(qp, D, stream) != 0) return RQ_E_HIP;
+  if (launch_decode_main(p, D, nc, bits, stream) != 0) return RQ_E_HIP;
+  if (launch_combine(cp, D, stream) != 0) return RQ_E_HIP;
+  return RQ_OK;
+}
+
+rq_status rq_decode_attn_bf16(const rq_desc* d, const uint16_t* k_cache, const uint16_t* v_cache,
+                              const uint16_t* q, const uint16_t* k_cur, const uint16_t* v_cur,
+                              const int32_t* past_len, float softmax_scale, float* out, void* ws,
+                              size_t ws_bytes, int32_t* dev_err, void* stream) {
+  rq_status s = check_shape(d);
+  if (s != RQ_OK) return s;
+  if (!k_cache || !v_cache || !q || !k_cur || !v_cur || !past_len || !out) return RQ_E_NULL;
+  if (!ws || ws_bytes < workspace_for(d) || ((uintptr_t)ws & 255) != 0) return RQ_E_WORKSPACE;
+  if (!std::isfinite(softmax_scale)) return RQ_E_SHAPE;
+  const SplitPlan sp = split_plan(d);
+  const int D = d->head_dim;
+  const size_t bh = (size_t)d->batch * d->heads;
+  const size_t qa = ((bh * qprep_words(D) * 4) + 255) & ~(size_t)255;
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + qa);
+  const float scale_log2 = softmax_scale * 1.4426950408889634f;
+
+  Bf16Params p;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.q = q;
+  p.past_len = past_len;
+  p.part = part;
+  p.dev_err = dev_err;
+  p.scale_log2 = scale_log2;
+  p.B = d->batch;
+  p.H = d->heads;
+  p.T_max = d->max_tokens;
+  p.chunk = sp.chunk;
+  p.nsplit = sp.nsplit;
+
+  CombineParams cp;
+  cp.part = part;
+  cp.past_len = past_len;
+  cp.q = q;
+  cp.kcur = k_cur;
+  cp.vcur = v_cur;
+  cp.rotv = nullptr;
+  cp.out = out;
+  cp.dev_err = dev_err;
+  cp.scale_log2 = scale_log2;
+  cp.B = d->batch;
+  cp.H = d->heads;
+  cp.T_max = d->max_tokens;
+  cp.chunk = sp.chunk;
+  cp.nsplit = sp.nsplit;
+  if (launch_bf16_main(p, D, stream) != 0) return RQ_E_HIP;
+  if (launch_combine(cp, D, stream) != 0) return RQ_E_HIP;
+  return RQ_OK;
+}
+
+}  // extern "C"

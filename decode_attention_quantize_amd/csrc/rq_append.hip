@@ -1,0 +1,228 @@
+// Quantize-and-append kernel of the ResidualQuant cache (paper "KV Cache
+// Quantization for Looped Transformers with 2-Bit Residuals": §2.1 affine
+// group quantization, §3.2 Last-loop / Previous-loop references and the LS
+// coefficient, §3.3 shared rotation, §3.4 per-loop bit widths, §4.2 deferred
+// store after the final loop, App. G.1 the quantize-anchor-then-residual order).
+//
+// One wave owns a tile of 16 matrix rows = floor(16/L) (sequence, token) units
+// times their L loops. The rotation Z = X H^T of the tile runs on the fp64
+// matrix cores (v_mfma_f64_16x16x4_f64): the products of fp32 rotation entries
+// and bf16 inputs are exact in fp64, so Z agrees with any other fp64 evaluation
+// to the last bit or so, and the integer code decisions that follow are taken
+// in fp64 as well. This file is compiled with -ffp-contract=off: every product
+// and sum below is rounded on its own.
+#include <hip/hip_runtime.h>
+
+#include "rq_internal.hpp"
+
+namespace rq {
+namespace {
+
+typedef double d4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ double bf16_to_f64(uint16_t h) {
+  return (double)__uint_as_float((uint32_t)h << 16);
+}
+
+__device__ __forceinline__ double f16_to_f64(uint16_t h) {
+  return (double)(float)__builtin_bit_cast(_Float16, h);
+}
+
+// binary64 -> binary16 bits. mode 0: nearest-even, 1: toward -inf, 2: toward +inf.
+// The magnitude M * 2^(E-52) is cut at the fp16 spacing of its binade
+// (2^(E-10), or 2^-24 below the normal range); the dropped bits decide rounding.
+__device__ uint16_t f64_to_f16(double x, int mode) {
+  const uint64_t bits = (uint64_t)__double_as_longlong(x);
+  const bool neg = (bits >> 63) != 0;
+  const uint16_t sign = neg ? 0x8000 : 0;
+  const int e = (int)((bits >> 52) & 0x7ff);
+  const uint64_t frac = bits & 0xFFFFFFFFFFFFFull;
+  if (e == 0x7ff) return frac ? (uint16_t)0x7e00 : (uint16_t)(sign | 0x7c00);
+  if (e == 0 && frac == 0) return sign;
+  const int E = (e == 0) ? -1022 : e - 1023;
+  const uint64_t M = (e == 0) ? frac : (frac | (1ull << 52));
+  const int qexp = (E < -14) ? -24 : E - 10;
+  const int shift = qexp - (E - 52);  // >= 42
+  uint64_t n = 0;
+  bool up;
+  if (shift >= 64) {
+    up = (mode == 1 && neg) || (mode == 2 && !neg);  // nonzero remainder below half a spacing
+  } else {
+    n = M >> shift;
+    const uint64_t rem = M & ((1ull << shift) - 1);
+    const uint64_t half = 1ull << (shift - 1);
+    if (mode == 0) up = rem > half || (rem == half && (n & 1));
+    else if (mode == 1) up = neg && rem != 0;
+    else up = !neg && rem != 0;
+  }
+  n += up ? 1 : 0;
+  if (qexp == -24) return (uint16_t)(sign | (uint16_t)n);  // n <= 1024; 1024 is 2^-14
+  int EE = E;
+  if (n == 2048) {
+    n = 1024;
+    EE += 1;
+  }
+  if (EE > 15) {
+    const bool toward_zero = (mode == 1 && !neg) || (mode == 2 && neg);
+    return (uint16_t)(sign | (toward_zero ? 0x7bff : 0x7c00));
+  }
+  return (uint16_t)(sign | (uint16_t)((EE + 15) << 10) | (uint16_t)(n - 1024));
+}
+
+__device__ __forceinline__ double shfl_xor_f64(double v, int m) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __shfl_xor((int)(b & 0xffffffff), m, 64);
+  const int hi = __shfl_xor((int)(b >> 32), m, 64);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  for (int m = 1; m < 64; m <<= 1) v += shfl_xor_f64(v, m);
+  return v;
+}
+
+// Quantize one row's group pair (elements e0 = 32 gi + k, e1 = e0 + 16 held by
+// lane k of group gi), store codes and metadata, return the dequantized pair.
+template <int D>
+__device__ void quantize_pair(double v0, double v1, int bits, bool lane_on, int gi, int k,
+                              uint8_t* codes, uint32_t* meta, size_t tok, double& d0, double& d1) {
+  constexpr int G = D / 32;
+  double mn = lane_on ? fmin(v0, v1) : 0.0, mx = lane_on ? fmax(v0, v1) : 0.0;
+  for (int m = 1; m < 16; m <<= 1) {            // the 16 lanes of one group
+    mn = fmin(mn, shfl_xor_f64(mn, m));
+    mx = fmax(mx, shfl_xor_f64(mx, m));
+  }
+  const uint16_t o16 = f64_to_f16(mn, 1);
+  const double od = f16_to_f64(o16);
+  const double qmax = (double)((1 << bits) - 1);
+  const double sp = (mx - od) / qmax;
+  const uint16_t s16 = f64_to_f16(sp, 2);
+  const double sd = f16_to_f64(s16);
+  uint32_t c0 = 0, c1 = 0;
+  if (sd != 0.0) {
+    c0 = (uint32_t)fmin(fmax(rint((v0 - od) / sd), 0.0), qmax);
+    c1 = (uint32_t)fmin(fmax(rint((v1 - od) / sd), 0.0), qmax);
+  }
+  d0 = od + sd * (double)c0;
+  d1 = od + sd * (double)c1;
+  const int per = 16 / bits;                    // codes per 16-bit half-word
+  const int sh = bits * (k % per);
+  uint32_t word = (c0 << sh) | (c1 << (16 + sh));
+  for (int m = 1; m < per; m <<= 1) word |= (uint32_t)__shfl_xor((int)word, m, 64);
+  if (lane_on) {
+    if (k % per == 0) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(codes + tok * (size_t)(D * bits / 8) + gi * 4 * bits);
+      dst[k / per] = word;
+    }
+    if (k == 0) meta[tok * G + gi] = (uint32_t)o16 | ((uint32_t)s16 << 16);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
+  constexpr int NT = D / 16;   // 16-wide output column tiles
+  constexpr int NK = D / 4;    // k steps of the 16x16x4 instruction
+  constexpr int HP = D + 16;   // padded row of the transposed rotation in LDS
+  __shared__ float Ht[D * HP];                 // Ht[k][n] = H[n][k]
+  __shared__ double Zs[kWaves][16][D + 1];
+  const int kv = blockIdx.z, h = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const float* Hg = p.rot[kv] + (size_t)h * D * D;
+  for (int idx = threadIdx.x; idx < D * D; idx += blockDim.x) {
+    const int n = idx / D, k = idx % D;
+    Ht[k * HP + n] = Hg[idx];
+  }
+  __syncthreads();
+
+  const int L = p.L;
+  const int U = 16 / L;                        // (sequence, token) units per tile
+  const int units = p.B * p.n;
+  const int u0 = (blockIdx.x * kWaves + wave) * U;
+  if (u0 >= units) return;                     // no block-wide barrier follows
+
+  // ---- Z = X H^T on the matrix cores ----------------------------------------
+  const int m = lane & 15;
+  const int mu = m / L, mr = m % L;
+  const bool row_ok = mu < U && u0 + mu < units;
+  const int urow = row_ok ? u0 + mu : 0;
+  const int b_row = urow / p.n, i_row = urow % p.n;
+  const uint16_t* xrow =
+      p.kv + (((((size_t)kv * L + mr) * p.B + b_row) * p.H + h) * p.n + i_row) * (size_t)D;
+  d4 acc[NT];
+  for (int ct = 0; ct < NT; ++ct) acc[ct] = d4{0.0, 0.0, 0.0, 0.0};
+  for (int kk = 0; kk < NK; ++kk) {
+    const int k = kk * 4 + (lane >> 4);
+    const double a = row_ok ? bf16_to_f64(xrow[k]) : 0.0;
+    const float* hk = &Ht[k * HP + (lane & 15)];
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct)
+      acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)hk[ct * 16], acc[ct], 0, 0, 0);
+  }
+  // lane l, register j of column tile ct holds Z[4j + l/16][16 ct + l%16]
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) Zs[wave][4 * j + (lane >> 4)][ct * 16 + (lane & 15)] = acc[ct][j];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+
+  // ---- per unit: anchor, LS alpha, residuals ---------------------------------
+  const int gi = lane >> 4, k = lane & 15;
+  const bool lane_on = gi < D / 32;
+  const int e0 = lane_on ? 32 * gi + k : 0, e1 = e0 + 16;
+  for (int uu = 0; uu < U; ++uu) {
+    const int u = u0 + uu;
+    if (u >= units) break;
+    const int b = u / p.n, i = u % p.n;
+    const int t = p.pos[b] + i;
+    if (t < 0 || t >= p.T_max) {
+      if (lane == 0 && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_CAPACITY);
+      continue;
+    }
+    const size_t tok = ((size_t)b * p.H + h) * p.T_max + t;
+    const double(*Z)[D + 1] = &Zs[wave][uu * L];
+    const int a = (p.policy == RQ_POLICY_LAST_LOOP) ? L - 1 : 0;
+    double r0, r1;  // reference (reconstructed anchor, or previous loop) at e0, e1
+    quantize_pair<D>(Z[a][e0], Z[a][e1], p.bits[a], lane_on, gi, k, p.codes[kv][a], p.meta[kv][a], tok, r0,
+                     r1);
+    if (!lane_on) r0 = r1 = 0.0;
+    const double den = wave_sum_f64(r0 * r0 + r1 * r1);
+    double den_cur = den;
+    for (int step = 1; step < L; ++step) {
+      const int r = (p.policy == RQ_POLICY_LAST_LOOP) ? step - 1 : step;
+      const double z0 = lane_on ? Z[r][e0] : 0.0, z1 = lane_on ? Z[r][e1] : 0.0;
+      const double num = wave_sum_f64(z0 * r0 + z1 * r1);
+      const double alpha = den_cur > 0.0 ? num / den_cur : 0.0;
+      const uint16_t a16 = f64_to_f16(alpha, 0);
+      const double at = f16_to_f64(a16);
+      if (lane == 0) p.alpha[kv][r][tok] = a16;
+      double q0, q1;
+      quantize_pair<D>(z0 - at * r0, z1 - at * r1, p.bits[r], lane_on, gi, k, p.codes[kv][r], p.meta[kv][r],
+                       tok, q0, q1);
+      if (p.policy == RQ_POLICY_PREV_LOOP) {    // zhat_r = alpha_r zhat_{r-1} + D(c_r)
+        r0 = lane_on ? at * r0 + q0 : 0.0;
+        r1 = lane_on ? at * r1 + q1 : 0.0;
+        den_cur = wave_sum_f64(r0 * r0 + r1 * r1);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int launch_append(const AppendParams& p, int D, void* stream) {
+  const int U = 16 / p.L;
+  const long long tiles = ((long long)p.B * p.n + U - 1) / U;
+  const dim3 grid((unsigned)((tiles + kWaves - 1) / kWaves), (unsigned)p.H, 2);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (D) {
+    case 64: hipLaunchKernelGGL(append_kernel<64>, grid, dim3(kThreads), 0, s, p); break;
+    case 96: hipLaunchKernelGGL(append_kernel<96>, grid, dim3(kThreads), 0, s, p); break;
+    case 128: hipLaunchKernelGGL(append_kernel<128>, grid, dim3(kThreads), 0, s, p); break;
+    default: return -1;
+  }
+  return (int)hipGetLastError();
+}
+
+}  // namespace rq

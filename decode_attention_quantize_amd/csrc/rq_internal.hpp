@@ -1,0 +1,103 @@
+// Internal declarations shared by the host API and the HIP kernels of librq.
+// Citations name the paper "KV Cache Quantization for Looped Transformers with
+// 2-Bit Residuals" (ResidualQuant) by section.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "rq.h"
+
+namespace rq {
+
+constexpr int kMaxComp = 4;          // stored components one decode call may read
+constexpr int kWaves = 4;            // waves per decode workgroup
+constexpr int kThreads = 64 * kWaves;
+
+// Token-pair tile of one wave: G = D/32 lanes cover one token's groups, and a
+// lane holds two tokens (t, t + TPW) so that value codes pair up for the
+// fp16 dot-2 instruction.
+constexpr int groups_of(int D) { return D / 32; }
+constexpr int pairs_per_wave(int D) { return 64 / groups_of(D); }
+constexpr int tile_tokens(int D) { return 2 * pairs_per_wave(D); }
+
+// Split of the token axis: every (b, h) has nsplit chunks of `chunk` tokens.
+struct SplitPlan {
+  int chunk;
+  int nsplit;
+};
+SplitPlan split_plan(const rq_desc* d);
+
+// Per-(b,h) prepared query: hi/lo fp16 pairs (q'_k, q'_{k+16}) per group and
+// the per-group sum of q' (fp32), q' = scale * log2(e) * H_K q.
+constexpr size_t qprep_words(int D) { return (size_t)groups_of(D) * 33; }
+constexpr size_t part_floats(int D) { return (size_t)D + 4; }
+
+struct DecodeParams {
+  const uint8_t* kcodes[kMaxComp];
+  const uint32_t* kmeta[kMaxComp];
+  const uint16_t* kalpha[kMaxComp];   // [c] for c >= 1: the coefficient between c-1 and c
+  const uint8_t* vcodes[kMaxComp];
+  const uint32_t* vmeta[kMaxComp];
+  const uint16_t* valpha[kMaxComp];
+  const int32_t* past_len;
+  const uint32_t* qprep;
+  float* part;
+  int32_t* dev_err;
+  int B, H, T_max, chunk, nsplit;
+};
+
+struct QPrepParams {
+  const uint16_t* q;        // bf16 [B][H][D]
+  const float* rotk;        // fp32 [H][D][D]
+  uint32_t* qprep;
+  float scale_log2;         // softmax_scale * log2(e)
+  int B, H;
+};
+
+struct CombineParams {
+  const float* part;
+  const int32_t* past_len;
+  const uint16_t* q;
+  const uint16_t* kcur;
+  const uint16_t* vcur;
+  const float* rotv;        // fp32 [H][D][D], nullptr: values are not rotated (BF16 path)
+  float* out;
+  int32_t* dev_err;
+  float scale_log2;
+  int B, H, T_max, chunk, nsplit;
+};
+
+struct Bf16Params {
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* q;
+  const int32_t* past_len;
+  float* part;
+  int32_t* dev_err;
+  float scale_log2;
+  int B, H, T_max, chunk, nsplit;
+};
+
+struct AppendParams {
+  uint8_t* codes[2][RQ_MAX_LOOPS];
+  uint32_t* meta[2][RQ_MAX_LOOPS];
+  uint16_t* alpha[2][RQ_MAX_LOOPS];
+  const float* rot[2];
+  const uint16_t* kv;       // bf16 [2][L][B][H][n][D]
+  const int32_t* pos;
+  int32_t* dev_err;
+  int B, H, L, n, T_max, policy;
+  int bits[RQ_MAX_LOOPS];
+};
+
+// Launchers (return hipError_t as int; 0 = success). Defined in the .hip files.
+int launch_append(const AppendParams& p, int D, void* stream);
+int launch_qprep(const QPrepParams& p, int D, void* stream);
+// ncomp components with bit widths bits[0..ncomp-1]; returns -1 if no kernel exists.
+int launch_decode_main(const DecodeParams& p, int D, int ncomp, const int* bits, void* stream);
+int launch_combine(const CombineParams& p, int D, void* stream);
+int launch_bf16_main(const Bf16Params& p, int D, void* stream);
+bool have_decode_kernel(int D, int ncomp, const int* bits);
+
+}  // namespace rq

@@ -1,0 +1,167 @@
+/*
+ * rq.h -- C ABI of the ResidualQuant decode hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one of the paper "KV Cache Quantization for Looped
+ * Transformers with 2-Bit Residuals" (ResidualQuant); section numbers below
+ * refer to it. A looped Transformer produces keys/values X_r for every loop
+ * r = 1..L. The cache stores
+ *   - an anchor (loop L under the Last-loop policy, §3.2), group-quantized in
+ *     the rotated domain: A = D(Q(H X_L));
+ *   - for every other loop r, a least-squares coefficient
+ *     alpha_r = <Z_r, A> / |A|^2 (Z_r = H X_r, stored fp16; §3.2 "Scaling
+ *     coefficient", App. G.1) and the group-quantized rotated residual
+ *     Q(Z_r - alpha_r A) (§3.2, §3.3), with a bit width chosen per loop (§3.4).
+ * Decode rebuilds zhat_r = alpha_r A + D(c_r) tile by tile inside the attention
+ * kernel, scores keys against the rotated query H_K q and rotates the value sum
+ * back once (§4.1, App. G.2 "Reconstruction and attention"). The current
+ * token stays bf16 until the final loop, then all its loops are quantized and
+ * appended (§3.2, §4.2 "Decode").
+ *
+ * Conventions for every entry point
+ *   - All data pointers are DEVICE pointers unless stated otherwise; the
+ *     descriptor and layer-cache structs themselves live in host memory.
+ *   - The caller owns all memory. The library never allocates, keeps no state
+ *     between calls and may be called from several host threads.
+ *   - Every call validates its arguments on the host first; on error it returns
+ *     a non-zero rq_status and enqueues nothing. Otherwise it enqueues its
+ *     kernels on `stream` (a hipStream_t; NULL = default stream), does not
+ *     synchronize, and returns RQ_OK, or RQ_E_HIP if a launch fails. Faults of
+ *     enqueued work surface at the caller's next synchronization.
+ *   - Token counts that change every step (positions, cached lengths) are read
+ *     from device memory by the kernels, so a decode step can be captured once
+ *     in a hipGraph and replayed. Kernels clamp them to [0, max_tokens] and, if
+ *     `dev_err` (device int32, may be NULL) is given, OR an RQ_DEVERR_* bit into it.
+ *   - No C++ exception crosses this interface.
+ *
+ * Data types: bf16 and fp16 values travel as uint16_t bit patterns.
+ */
+#ifndef RQ_H
+#define RQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RQ_MAX_LOOPS 16
+
+typedef enum {
+  RQ_OK = 0,
+  RQ_E_NULL = 1,         /* a required pointer is NULL */
+  RQ_E_SHAPE = 2,        /* batch/heads/head_dim/loops/max_tokens/n out of range */
+  RQ_E_BITS = 3,         /* a bit width or group size is not supported */
+  RQ_E_CAPACITY = 4,     /* a host-known size exceeds max_tokens */
+  RQ_E_WORKSPACE = 5,    /* workspace too small (see rq_workspace_bytes) */
+  RQ_E_UNSUPPORTED = 6,  /* valid request this build has no kernel for */
+  RQ_E_HIP = 7,          /* a HIP launch failed */
+  RQ_E_POLICY = 8,       /* unknown reference policy */
+  RQ_E_LOOP = 9          /* loop index out of range */
+} rq_status;
+
+/* Device-side error bits (OR-ed into *dev_err when given). */
+#define RQ_DEVERR_CAPACITY 1  /* append: pos[b] + n > max_tokens; tokens past capacity were dropped */
+#define RQ_DEVERR_LENGTH 2    /* decode: past_len[b] outside [0, max_tokens]; it was clamped */
+
+/* Reference policy (§3.2, App. D).
+ * LAST_LOOP: the anchor is loop L; loop r < L stores Q(Z_r - alpha_r A).
+ * PREV_LOOP: the anchor is loop 1; loop r > 1 refers to the reconstruction of
+ *   loop r-1 (a chain: zhat_r = alpha_r zhat_{r-1} + D(c_r)), so decoding loop r
+ *   reads r stored components. Kept as the comparator the paper measures against. */
+typedef enum { RQ_POLICY_LAST_LOOP = 0, RQ_POLICY_PREV_LOOP = 1 } rq_policy;
+
+/* Shapes and the quantization plan of one layer's cache. */
+typedef struct {
+  int32_t batch;       /* B >= 1 */
+  int32_t heads;       /* H >= 1 */
+  int32_t head_dim;    /* D: 64, 96 or 128 */
+  int32_t loops;       /* L: 1 .. RQ_MAX_LOOPS */
+  int32_t max_tokens;  /* T_max >= 1: token capacity of every cache buffer */
+  int32_t policy;      /* rq_policy */
+  uint8_t bits[RQ_MAX_LOOPS];   /* bit width per loop (0-based), 2 or 4 (§2.1, §3.4) */
+  uint8_t group[RQ_MAX_LOOPS];  /* group size per loop along the rotated head_dim: 32 */
+} rq_desc;
+
+/* Device buffers of one layer's compressed cache. kv index 0 = keys, 1 = values;
+ * loop index is 0-based.
+ *   codes[kv][r]: uint8 [B][H][T_max][D*bits[r]/8]. Each group of g = group[r]
+ *     consecutive channels of the rotated vector occupies g*bits/8 bytes, i.e.
+ *     g*bits/32 little-endian 32-bit words. Element e of a group lies in half
+ *     h = e/(g/2) at index k = e%(g/2); bits-wide codes fill 16-bit half-words,
+ *     16/bits per half-word, element k at bit offset bits*(k%(16/bits)) of
+ *     half-word k/(16/bits); 32-bit word j = half-word j of half 0 (bits 0..15)
+ *     | half-word j of half 1 (bits 16..31). (Pairs e, e+g/2 share bit
+ *     positions, so one mask yields a pair of codes.)
+ *   meta[kv][r]: fp16 [B][H][T_max][D/g][2] = (offset o, scale s) per group;
+ *     dequantized value = o + s*code (§2.1).
+ *   alpha[kv][r]: fp16 [B][H][T_max], the LS coefficient; unused (may be NULL)
+ *     for the anchor loop.
+ *   rot[kv]: fp32 [H][D][D] row-major, z = rot[h] x. Any orthogonal matrix works
+ *     (randomized Hadamard, §2.2, or learned rotations such as OptR-H, §3.3). */
+typedef struct {
+  uint8_t* codes[2][RQ_MAX_LOOPS];
+  uint16_t* meta[2][RQ_MAX_LOOPS];
+  uint16_t* alpha[2][RQ_MAX_LOOPS];
+  const float* rot[2];
+} rq_layer_cache;
+
+/* Bytes of one cache buffer of `loop` for one tensor (K or V): kind 0 = codes,
+ * 1 = meta, 2 = alpha. Returns 0 if the descriptor or arguments are invalid. */
+size_t rq_buffer_bytes(const rq_desc* desc, int kind, int loop);
+
+/* Bytes of device workspace rq_decode_attn / rq_decode_attn_bf16 need (0 if invalid). */
+size_t rq_workspace_bytes(const rq_desc* desc);
+
+/* Host-side check of a descriptor: RQ_OK or the first problem found. */
+rq_status rq_check_desc(const rq_desc* desc);
+
+/* Quantize and store n tokens per sequence (§4.2 "Prefill" bulk store and
+ * "Decode" deferred store; App. G.1 recipe).
+ *   kv:  bf16 [2][L][B][H][n][D] keys (index 0) and values (1) of all loops of
+ *        n consecutive tokens, original (unrotated) domain.
+ *   pos: device int32 [B], the cache position of the first of the n tokens of
+ *        each sequence; token i goes to position pos[b] + i.
+ * For every (tensor, b, h, token): Z_r = rot x_r (fp64 accumulation), anchor
+ * group quantization, alpha_r (fp64, stored fp16 nearest-even), residual
+ * E_r = Z_r - alpha_r * ref, group quantization of E_r, packing. Offsets are
+ * rounded toward -inf and scales toward +inf to fp16, codes to nearest-even,
+ * so every group's range is covered. Tokens at positions >= max_tokens are
+ * dropped (RQ_DEVERR_CAPACITY). n == 0 is a no-op. */
+rq_status rq_quantize_append(const rq_desc* desc, const rq_layer_cache* cache,
+                             const uint16_t* kv, const int32_t* pos, int32_t n,
+                             int32_t* dev_err, void* stream);
+
+/* Decode attention of loop `loop` (0-based) over the compressed cache plus the
+ * current token held in bf16 (§4.1, §4.2 "Decode", App. G.2).
+ *   q, k_cur, v_cur: bf16 [B][H][D], original domain (current token's q/k/v of
+ *     this loop).
+ *   past_len: device int32 [B], cached tokens of each sequence (positions
+ *     0 .. past_len[b]-1 are attended, then the current token).
+ *   out: fp32 [B][H][D] = softmax(scale [q.k_t ..., q.k_cur]) [v_t ..., v_cur].
+ *   workspace: device, >= rq_workspace_bytes(desc) bytes, 256-byte aligned.
+ * Keys are scored as (scale * H_K q) . zhat_t; values accumulate in the rotated
+ * domain and are rotated back once per (b, h). */
+rq_status rq_decode_attn(const rq_desc* desc, const rq_layer_cache* cache, int32_t loop,
+                         const uint16_t* q, const uint16_t* k_cur, const uint16_t* v_cur,
+                         const int32_t* past_len, float softmax_scale, float* out,
+                         void* workspace, size_t workspace_bytes, int32_t* dev_err, void* stream);
+
+/* BF16 decode baseline (the paper's comparison point, §5.3): the same attention
+ * over an uncompressed cache. k_cache, v_cache: bf16 [B][H][T_max][D]. Only
+ * batch, heads, head_dim and max_tokens of desc are used. */
+rq_status rq_decode_attn_bf16(const rq_desc* desc, const uint16_t* k_cache, const uint16_t* v_cache,
+                              const uint16_t* q, const uint16_t* k_cur, const uint16_t* v_cur,
+                              const int32_t* past_len, float softmax_scale, float* out,
+                              void* workspace, size_t workspace_bytes, int32_t* dev_err, void* stream);
+
+/* Static description of a status code. */
+const char* rq_status_str(rq_status status);
+
+/* Library version string. */
+const char* rq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RQ_H */

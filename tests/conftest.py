@@ -25,3 +25,14 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def _ensure_built():
+    """Build the in-tree libraries if they are missing (never rebuilds)."""
+    lib = os.path.join(ROOT, "decode_attention_quantize_amd", "librq.so")
+    if not os.path.exists(lib):
+        from decode_attention_quantize_amd import build as b
+        b.build()
+
+
+_ensure_built()

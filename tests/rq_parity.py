@@ -1,0 +1,194 @@
+"""Helpers for the GPU parity tests: build caches through the C ABI, build the
+oracle's caches from the same bf16 inputs, and compare.
+
+Comparison rules (the oracle is the reference; nothing the HIP path writes is
+ever fed to an oracle computation):
+  * fp16 metadata (offset o, scale s) and LS coefficients are compared bit for
+    bit. A mismatch is exempt only if the oracle's binary64 value before fp16
+    rounding lies so close to a rounding breakpoint that a relative
+    perturbation of 1e-12 changes its fp16 rounding (the GPU accumulates the
+    same binary64 sums in another order).
+  * codes are compared bit for bit in groups whose metadata (and LS
+    coefficient) matched; an element is exempt when the oracle's (v - o)/s lies
+    within 1e-6 of a rounding boundary k + 1/2.
+  * every mismatch must be exempt, and exempt elements must stay <= 1e-5 of all.
+"""
+from __future__ import annotations
+
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import torch
+
+import decode_attention_quantize_amd as rq
+import oracle as O
+import synth
+
+REL_BREAK = 1e-12
+CODE_DELTA = 1e-6
+TOL_ATTN = 2e-3
+
+
+def log(msg: str):
+    print(f"[parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def u16(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def unpack_np(row: np.ndarray, D: int, bits: int, g: int = 32) -> np.ndarray:
+    """Test-local unpack of one token's packed codes (layout of include/rq.h)."""
+    words = row.view("<u4")
+    per = 16 // bits
+    half = g // 2
+    out = np.zeros(D, np.int64)
+    wpg = g * bits // 32
+    for e in range(D):
+        grp, idx = divmod(e, g)
+        h, k = divmod(idx, half)
+        j, p = divmod(k, per)
+        w = int(words[grp * wpg + j])
+        out[e] = (w >> (16 * h + bits * p)) & ((1 << bits) - 1)
+    return out
+
+
+def _ambiguous(pre: float, mode: int) -> bool:
+    a = O.f16_encode(np.array([pre * (1 - REL_BREAK), pre * (1 + REL_BREAK)]), mode)
+    return a[0] != a[1]
+
+
+def oracle_series_for(X: np.ndarray, H: np.ndarray, bits, policy) -> O.Series:
+    cfg = O.Config(D=X.shape[-1], bits=list(bits), policy=policy)
+    return O.quantize_series(cfg, X, H, diagnostics=True)
+
+
+def oracle_layer(Xall: torch.Tensor, rot_k: torch.Tensor, rot_v: torch.Tensor, bits, policy, T: int,
+                 units=None, threads: int = 16):
+    """Oracle caches for (kv, b, h) series of tokens [0, T). Xall: bf16 [2][L][B][H][>=T][D]."""
+    X = Xall[..., :T, :]
+    _, L, B, H, _, D = X.shape
+    units = units if units is not None else [(b, h) for b in range(B) for h in range(H)]
+    Xc = {(b, h): u16(X[:, :, b, h]) for (b, h) in units}
+    Hk, Hv = rot_k.cpu().numpy(), rot_v.cpu().numpy()
+    jobs = [(kv, b, h) for (b, h) in units for kv in range(2)]
+
+    def run(job):
+        kv, b, h = job
+        return job, oracle_series_for(Xc[(b, h)][kv], (Hk if kv == 0 else Hv)[h], bits, policy)
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        return dict(ex.map(run, jobs))
+
+
+def compare_cache(cache: rq.LayerCache, series: dict, T: int) -> dict:
+    d = cache.desc
+    L, D = d.loops, d.head_dim
+    anchor = L - 1 if d.policy == rq.POLICY_LAST_LOOP else 0
+    stats = dict(elements=0, exempt_elements=0, meta_exempt=0, alpha_exempt=0, bad=[])
+    host = {}
+    for (kv, b, h) in series:
+        for r in range(L):
+            key = (kv, r)
+            if key not in host:
+                host[key] = (cache.codes[kv][r].cpu().numpy(), u16(cache.meta[kv][r]),
+                             None if cache.alpha[kv][r] is None else u16(cache.alpha[kv][r]))
+    for (kv, b, h), s in series.items():
+        for r in range(L):
+            gc, gm, ga = host[(kv, r)]
+            bits = d.bits[r]
+            skip_tok = np.zeros(T, bool)
+            if r != anchor:
+                oa = s.alpha[r][:T]
+                ga_ = ga[b, h, :T]
+                for t in np.nonzero(oa != ga_)[0]:
+                    if _ambiguous(s.alpha_pre[r, t], O.RNE):
+                        stats["alpha_exempt"] += 1
+                        skip_tok[t] = True
+                    else:
+                        stats["bad"].append(("alpha", kv, b, h, r, int(t), int(oa[t]), int(ga_[t])))
+            om = s.meta[r][:T]
+            gmm = gm[b, h, :T]
+            meta_bad = om != gmm                      # [T][G][2]
+            grp_skip = np.zeros(om.shape[:2], bool)
+            for t, j, w in zip(*np.nonzero(meta_bad)):
+                if skip_tok[t]:
+                    continue
+                pre = (s.pre_o if w == 0 else s.pre_s)[r, t, j]
+                if _ambiguous(pre, O.RD if w == 0 else O.RU):
+                    stats["meta_exempt"] += 1
+                    grp_skip[t, j] = True
+                else:
+                    stats["bad"].append(("meta", kv, b, h, r, int(t), int(j), int(w)))
+            oc = s.codes[r][:T]
+            gcc = gc[b, h, :T]
+            rows = np.nonzero(np.any(oc != gcc, axis=1))[0]
+            G = D // 32
+            stats["elements"] += T * D
+            stats["exempt_elements"] += int(skip_tok.sum()) * D + int(grp_skip.sum()) * 32
+            for t in rows:
+                if skip_tok[t]:
+                    continue
+                a = unpack_np(oc[t], D, bits)
+                g = unpack_np(gcc[t], D, bits)
+                for e in np.nonzero(a != g)[0]:
+                    if grp_skip[t, e // 32]:
+                        continue
+                    if s.delta[r, t, e] < CODE_DELTA:
+                        stats["exempt_elements"] += 1
+                    else:
+                        stats["bad"].append(("code", kv, b, h, r, int(t), int(e), int(a[e]), int(g[e])))
+    return stats
+
+
+def assert_cache_parity(stats: dict, label: str):
+    frac = stats["exempt_elements"] / max(stats["elements"], 1)
+    log(f"{label}: elements={stats['elements']} exempt={stats['exempt_elements']} (frac {frac:.2e}) "
+        f"meta_exempt={stats['meta_exempt']} alpha_exempt={stats['alpha_exempt']} bad={len(stats['bad'])}")
+    assert not stats["bad"], f"{label}: {len(stats['bad'])} non-exempt mismatches, first {stats['bad'][:5]}"
+    assert frac <= 1e-5, f"{label}: exempt fraction {frac}"
+
+
+def oracle_attention(series: dict, units, loop: int, T_of_b, rot_k, rot_v, q, kcur, vcur, scale,
+                     threads: int = 16) -> dict:
+    """Oracle outputs for (b, h) units; q/kcur/vcur: bf16 [B][H][D] torch tensors."""
+    Hk, Hv = rot_k.cpu().numpy(), rot_v.cpu().numpy()
+    qn, kn, vn = u16(q), u16(kcur), u16(vcur)
+
+    def run(u):
+        b, h = u
+        return u, O.attend(series[(0, b, h)], series[(1, b, h)], loop, int(T_of_b[b]), Hk[h], Hv[h],
+                           qn[b, h], kn[b, h], vn[b, h], scale)
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        return dict(ex.map(run, units))
+
+
+def max_rel_err(gpu_out: torch.Tensor, ref: dict) -> float:
+    g = gpu_out.detach().cpu().double().numpy()
+    worst = 0.0
+    for (b, h), o in ref.items():
+        err = np.abs(g[b, h] - o).max() / max(np.abs(o).max(), 1e-30)
+        worst = max(worst, err)
+    return worst
+
+
+def build_gpu_layer(X: torch.Tensor, rot_k, rot_v, bits, policy, T_max: int, T: int,
+                    steps_of_one: int = 0, pos0=None) -> rq.LayerCache:
+    """Fill a GPU cache with tokens [0, T) of X (bf16 [2][L][B][H][*][D] on the GPU): one
+    bulk append of the first T - steps_of_one tokens, then single-token appends."""
+    _, L, B, H, _, D = X.shape
+    d = rq.make_desc(B, H, D, bits, T_max, policy)
+    cache = rq.LayerCache.allocate(d, rot_k, rot_v)
+    n0 = T - steps_of_one
+    pos = torch.zeros(B, dtype=torch.int32, device="cuda") if pos0 is None else pos0
+    if n0 > 0:
+        rq.quantize_append(cache, X[..., :n0, :].contiguous(), pos, n0)
+    for i in range(steps_of_one):
+        t = n0 + i
+        p = torch.full((B,), t, dtype=torch.int32, device="cuda")
+        rq.quantize_append(cache, X[..., t:t + 1, :].contiguous(), p, 1)
+    torch.cuda.synchronize()
+    return cache

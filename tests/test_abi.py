@@ -1,0 +1,133 @@
+"""The C-ABI library loads, exports every symbol include/rq.h declares, and its
+host-side validation rejects bad arguments before enqueuing anything (CPU only:
+every call below fails validation, so no GPU work is ever issued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_quantize_amd as rq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x100000)      # never dereferenced: validation fails first
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "rq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert {"rq_quantize_append", "rq_decode_attn", "rq_decode_attn_bf16"} <= set(names)
+    lib = ctypes.CDLL(rq.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in rq.version()
+    for code in range(10):
+        assert rq.status_str(code) and rq.status_str(code) != "unknown status"
+
+
+def _desc(**kw):
+    a = dict(batch=2, heads=3, head_dim=128, bits=[2, 2, 4, 4], max_tokens=100)
+    a.update(kw)
+    return rq.make_desc(**a)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=80), 2), (dict(batch=0), 2), (dict(max_tokens=0), 2), (dict(bits=[2, 3, 4]), 3),
+    (dict(bits=[2] * 17), None), (dict(policy=5), 8),
+])
+def test_check_desc(kw, code):
+    if code is None:
+        with pytest.raises(IndexError):
+            _desc(**kw)
+        return
+    assert rq.check_desc(_desc(**kw)) == code
+
+
+def test_group_must_be_32():
+    d = _desc()
+    d.group[1] = 16
+    assert rq.check_desc(d) == 3
+
+
+def test_buffer_and_workspace_sizes():
+    d = _desc()
+    toks = 2 * 3 * 100
+    assert rq.buffer_bytes(d, 0, 0) == toks * 128 * 2 // 8
+    assert rq.buffer_bytes(d, 0, 3) == toks * 128 * 4 // 8
+    assert rq.buffer_bytes(d, 1, 2) == toks * 4 * 4
+    assert rq.buffer_bytes(d, 2, 1) == toks * 2
+    assert rq.buffer_bytes(d, 0, 4) == 0 and rq.buffer_bytes(d, 7, 0) == 0
+    assert rq.workspace_bytes(d) > 0
+    bad = _desc(head_dim=80)
+    assert rq.workspace_bytes(bad) == 0
+
+
+def _cache(d, null_alpha=False):
+    c = rq.LayerCacheC()
+    for kv in range(2):
+        for r in range(d.loops):
+            c.codes[kv][r] = 0x100000
+            c.meta[kv][r] = 0x100000
+            c.alpha[kv][r] = None if null_alpha else 0x100000
+        c.rot[kv] = 0x100000
+    return c
+
+
+def test_append_validation():
+    L = rq.lib
+    d = _desc()
+    c = _cache(d)
+    by = ctypes.byref
+    assert L.rq_quantize_append(None, by(c), FAKE, FAKE, 1, None, 0) == 1
+    assert L.rq_quantize_append(by(d), None, FAKE, FAKE, 1, None, 0) == 1
+    assert L.rq_quantize_append(by(d), by(c), FAKE, FAKE, -1, None, 0) == 2
+    assert L.rq_quantize_append(by(d), by(c), FAKE, FAKE, 101, None, 0) == 4
+    assert L.rq_quantize_append(by(d), by(c), None, FAKE, 1, None, 0) == 1
+    assert L.rq_quantize_append(by(d), by(c), FAKE, None, 1, None, 0) == 1
+    assert L.rq_quantize_append(by(d), by(c), None, None, 0, None, 0) == 0      # n == 0: no-op
+    cn = _cache(d, null_alpha=True)                                            # residual loops need alpha
+    assert L.rq_quantize_append(by(d), by(cn), FAKE, FAKE, 1, None, 0) == 1
+
+
+def test_decode_validation():
+    L = rq.lib
+    d = _desc()
+    c = _cache(d)
+    by = ctypes.byref
+    ws = rq.workspace_bytes(d)
+    args = lambda loop=0, q=FAKE, ws_ptr=FAKE, ws_n=ws, scale=0.1: (
+        by(d), by(c), loop, q, FAKE, FAKE, FAKE, ctypes.c_float(scale), FAKE, ws_ptr, ws_n, None, 0)
+    assert L.rq_decode_attn(*args(loop=4)) == 9
+    assert L.rq_decode_attn(*args(loop=-1)) == 9
+    assert L.rq_decode_attn(*args(q=None)) == 1
+    assert L.rq_decode_attn(*args(ws_ptr=None)) == 5
+    assert L.rq_decode_attn(*args(ws_n=ws - 1)) == 5
+    assert L.rq_decode_attn(*args(ws_ptr=ctypes.c_void_p(0x100010))) == 5    # not 256-byte aligned
+    assert L.rq_decode_attn(*args(scale=float("nan"))) == 2
+    # chained policy with more components than the fused kernel takes
+    d6 = _desc(bits=[4, 4, 2, 2, 2, 2], policy=1)
+    c6 = _cache(d6)
+    ws6 = rq.workspace_bytes(d6)
+    assert L.rq_decode_attn(by(d6), by(c6), 5, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE,
+                            ws6, None, 0) == 6
+
+
+def test_bf16_validation():
+    L = rq.lib
+    d = _desc()
+    by = ctypes.byref
+    ws = rq.workspace_bytes(d)
+    assert L.rq_decode_attn_bf16(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE,
+                                 ws, None, 0) == 1
+    assert L.rq_decode_attn_bf16(by(d), None, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE,
+                                 ws, None, 0) == 1
+    assert L.rq_decode_attn_bf16(by(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE,
+                                 ws - 1, None, 0) == 5
