@@ -1,0 +1,331 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark of the ResidualQuant path on one MI355X.
+
+Workload (default "ouro_16k"): Ouro-1.4B-shaped looped decoder, 24 layers,
+batch 8, 16 MHA heads, head_dim 128, 4 loops, 16384 cached tokens, INT2/4
+plan [2,2,4,4] (loops 1-2 INT2 residuals, loop 3 INT4 residual, INT4 anchor),
+group 32, synthetic seeded inputs (synth/). One step = one decoded token per
+sequence: for each loop r and layer l, rq_decode_attn over the compressed
+cache with the current token's bf16 K/V; after the final loop, each layer's
+rq_quantize_append of the current token (all loops) at position past_len; then
+past_len += 1 on the device. Each step is one captured hipGraph.
+
+Reported next to it, in the same process and on the same logical inputs:
+  * the BF16 decode baseline (rq_decode_attn_bf16 over the uncompressed cache);
+  * the chained Previous-loop reference policy ([4,4,2,2], anchor on loop 1);
+  * per-call HIP-event timing of the dominant call for the roofline;
+  * the CPU oracle timed on a bounded sample (cpu_baseline).
+
+Prints one JSON line (rank 0). --gpus N > 1 exits: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn tokens/s + achieved HBM GB/s (% of peak) at 16k ctx, 4 loops"
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- traffic model
+def comp_bytes(D, bits, with_alpha, group=32):
+    return D * bits // 8 + (D // group) * 4 + (2 if with_alpha else 0)
+
+
+def call_bytes(D, bits, policy, r):
+    """Algorithmic HBM bytes one decode call of loop r reads per (b, h, cached token):
+    the stored components the reconstruction needs, K and V (fp16 meta and alpha)."""
+    L = len(bits)
+    if policy == "last":
+        a = L - 1
+        comps = [a] if r == a else [a, r]
+    else:
+        a = 0
+        comps = list(range(r + 1))
+    return 2 * sum(comp_bytes(D, bits[c], c != a) for c in comps)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--workload", default="ouro_16k")
+    ap.add_argument("--layers", type=int, default=0, help="override layer count (0: workload's)")
+    ap.add_argument("--batch", type=int, default=0, help="override batch (0: workload's)")
+    ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--no-chained", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--call-reps", type=int, default=50)
+    ap.add_argument("--cpu-sample-units", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum timed CPU-oracle seconds")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 1 GiB read + 1 GiB write elementwise kernel (counter scaling)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this decode path runs on one GPU; --gpus {args.gpus} (WORLD_SIZE {world}) is "
+              "not supported (multi-GPU sharding is a design note, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import decode_attention_quantize_amd as rq
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    if args.layers:
+        w = w.with_(layers=args.layers)
+    if args.batch:
+        w = w.with_(batch=args.batch)
+    B, H, D, L, T, K = w.batch, w.heads, w.D, w.L, w.T, args.steps
+    T_max = T + max(K, args.warmup)
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    scale = 1.0 / math.sqrt(D)
+    bits, cbits = list(w.bits), list(w.chained_bits)
+
+    # ---------------------------------------------------------------- build (untimed)
+    t_build = time.time()
+    d_rq = rq.make_desc(B, H, D, bits, T_max, rq.POLICY_LAST_LOOP)
+    d_ch = rq.make_desc(B, H, D, cbits, T_max, rq.POLICY_PREV_LOOP)
+    caches, chained, bf16, rots = [], [], [], []
+    kvcur = torch.empty(K, w.layers, 2, L, B, H, 1, D, dtype=torch.bfloat16, device=dev)
+    qs = torch.empty(K, w.layers, L, B, H, D, dtype=torch.bfloat16, device=dev)
+    pos0 = torch.zeros(B, dtype=torch.int32, device=dev)
+    for l in range(w.layers):
+        X = synth.kv(w, l, 0, T_max, device=dev)                      # [2][L][B][H][T_max][D]
+        rk, rv = synth.rotation(w, l, 0), synth.rotation(w, l, 1)
+        past = X[..., :T, :].contiguous()
+        c = rq.LayerCache.allocate(d_rq, rk, rv)
+        rq.quantize_append(c, past, pos0, T)
+        caches.append(c)
+        if not args.no_chained:
+            cc = rq.LayerCache.allocate(d_ch, rk, rv)
+            rq.quantize_append(cc, past, pos0, T)
+            chained.append(cc)
+        del past
+        for k in range(K):
+            kvcur[k, l] = X[..., T + k:T + k + 1, :]
+            for r in range(L):
+                qs[k, l, r] = synth.query(w, l, r, k, device=dev)
+        if args.no_bf16:
+            del X
+        else:
+            bf16.append(X)
+        torch.cuda.synchronize()
+        if l % 6 == 5 or l == w.layers - 1:
+            log(f"built layer {l + 1}/{w.layers} ({time.time() - t_build:.1f}s)")
+    ws = rq.alloc_workspace(d_rq)
+    ws_ch = rq.alloc_workspace(d_ch)
+    out = torch.empty(w.layers, L, B, H, D, dtype=torch.float32, device=dev)
+    past_len = torch.full((B,), T, dtype=torch.int32, device=dev)
+    rq_bytes_gb = sum(c.nbytes() for c in caches) / 1e9
+    log(f"caches built: RQ {rq_bytes_gb:.2f} GB, BF16 {sum(x.numel() * 2 for x in bf16) / 1e9:.2f} GB, "
+        f"{time.time() - t_build:.1f}s")
+
+    # ---------------------------------------------------------------- steps as graphs
+    def rq_step(k, cs, workspace):
+        for r in range(L):
+            for l in range(w.layers):
+                kc = kvcur[k, l, 0, r, :, :, 0]
+                vc = kvcur[k, l, 1, r, :, :, 0]
+                rq.decode_attn(cs[l], r, qs[k, l, r], kc, vc, past_len, scale, out[l, r], workspace)
+                if r == L - 1:
+                    rq.quantize_append(cs[l], kvcur[k, l], past_len, 1)
+        past_len.add_(1)
+
+    def bf16_step(k):
+        for r in range(L):
+            for l in range(w.layers):
+                kc = kvcur[k, l, 0, r, :, :, 0]
+                vc = kvcur[k, l, 1, r, :, :, 0]
+                rq.decode_attn_bf16(d_rq, bf16[l][0, r], bf16[l][1, r], qs[k, l, r], kc, vc, past_len, scale,
+                                    out[l, r], ws)
+        past_len.add_(1)
+
+    side = torch.cuda.Stream()
+
+    def capture(fn):
+        graphs = []
+        torch.cuda.synchronize()
+        for k in range(K):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                fn(k)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        return graphs
+
+    def run(graphs, warm):
+        for k in range(min(warm, K)):
+            graphs[k].replay()
+        torch.cuda.synchronize()
+        past_len.fill_(T)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        past_len.fill_(T)
+        torch.cuda.synchronize()
+        return dt
+
+    log("capturing RQ steps")
+    g_rq = capture(lambda k: rq_step(k, caches, ws))
+    dt_rq = run(g_rq, args.warmup)
+    log(f"RQ: {K} steps in {dt_rq * 1e3:.2f} ms")
+    del g_rq
+
+    per_token_bytes = sum(call_bytes(D, bits, "last", r) for r in range(L)) * H * w.layers
+    mean_ctx = T + (K - 1) / 2.0
+    step_bytes = per_token_bytes * B * mean_ctx
+    result = {
+        "metric": METRIC, "value": B * K / dt_rq, "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": dt_rq * 1e3 / K, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.layers, "batch": B, "heads": H, "head_dim": D, "loops": L,
+                   "context": T, "bits": bits, "group": w.group, "codes": "int2/int4 + fp16 scale/offset + fp16 alpha",
+                   "arith": "fp16 dot2 products, fp32 accumulation"},
+        "hbm_gbps_step": step_bytes / (dt_rq / K) / 1e9,
+        "hbm_frac_step": step_bytes / (dt_rq / K) / 1e9 / HBM_PEAK_GBPS,
+        "algorithmic_bytes_per_step": step_bytes,
+    }
+
+    if not args.no_chained:
+        log("capturing chained steps")
+        g_ch = capture(lambda k: rq_step(k, chained, ws_ch))
+        dt_ch = run(g_ch, args.warmup)
+        del g_ch
+        ch_bytes = sum(call_bytes(D, cbits, "prev", r) for r in range(L)) * H * w.layers * B * mean_ctx
+        result["chained"] = {"policy": "previous-loop", "bits": cbits, "value": B * K / dt_ch,
+                             "unit": "tokens/s", "ms_per_step": dt_ch * 1e3 / K,
+                             "hbm_gbps_step": ch_bytes / (dt_ch / K) / 1e9,
+                             "rq_speedup_over_chained": dt_ch / dt_rq}
+        log(f"chained: {K} steps in {dt_ch * 1e3:.2f} ms")
+
+    if not args.no_bf16:
+        log("capturing BF16 steps")
+        g_bf = capture(bf16_step)
+        dt_bf = run(g_bf, args.warmup)
+        del g_bf
+        bf_bytes = 2 * L * D * 2 * H * w.layers * B * mean_ctx
+        result["bf16"] = {"value": B * K / dt_bf, "unit": "tokens/s", "ms_per_step": dt_bf * 1e3 / K,
+                          "hbm_gbps_step": bf_bytes / (dt_bf / K) / 1e9,
+                          "rq_speedup_over_bf16": dt_bf / dt_rq}
+        log(f"bf16: {K} steps in {dt_bf * 1e3:.2f} ms")
+
+    # ---------------------------------------------------------------- dominant call, HIP events
+    # loops 1-2 (INT4 anchor + INT2 residual) are the most frequent and largest calls
+    reps = args.call_reps
+    stream = torch.cuda.current_stream()
+    percall = {}
+    for r in range(L):
+        kc = kvcur[0, 0, 0, r, :, :, 0]
+        vc = kvcur[0, 0, 1, r, :, :, 0]
+        for _ in range(3):
+            rq.decode_attn(caches[0], r, qs[0, 0, r], kc, vc, past_len, scale, out[0, r], ws, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            rq.decode_attn(caches[i % w.layers], r, qs[0, 0, r], kc, vc, past_len, scale, out[0, r], ws,
+                           stream=stream)
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nbytes = call_bytes(D, bits, "last", r) * B * H * T
+        percall[r] = {"ms": ms, "bytes": nbytes, "gbps": nbytes / (ms * 1e-3) / 1e9}
+    dom = percall[0]
+    result["roofline"] = {"bound": "hbm", "achieved": dom["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                          "frac": dom["gbps"] / HBM_PEAK_GBPS, "traffic": None,
+                          "kernel": "rq_decode_attn loop 1 (INT4 anchor + INT2 residual), one call = "
+                                    "query prep + fused split-K kernel + combine",
+                          "bytes_per_launch": dom["bytes"], "ms_per_launch": dom["ms"]}
+    result["per_call"] = {f"loop{r + 1}": v for r, v in percall.items()}
+
+    if args.calibrate_copy:
+        a = torch.ones(1 << 28, dtype=torch.float32, device=dev)       # 1 GiB
+        b = torch.empty_like(a)
+        torch.add(a, 0.0, out=b)
+        torch.cuda.synchronize()
+        del a, b
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, bits, args.cpu_sample_units, args.cpu_seconds, torch, synth,
+                                              scale)
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, bits, units, min_seconds, torch, synth, scale):
+    """Time the CPU oracle's decode work on a bounded sample of (b, h) series of
+    layer 0 (its own cache, built untimed), scaled to the whole step. The sample
+    is repeated until at least min_seconds of wall time have been measured."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle as O
+
+    cores = min(16, os.cpu_count() or 1)
+    units = units or w.batch * w.heads
+    T, L, D = w.T, w.L, w.D
+    pairs = [(u // w.heads % w.batch, u % w.heads) for u in range(units)]
+    X = synth.kv(w, 0, 0, T + 1, device="cuda")
+    rk, rv = synth.rotation(w, 0, 0).numpy(), synth.rotation(w, 0, 1).numpy()
+    u16 = lambda t: t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    Xh = {p: u16(X[:, :, p[0], p[1]]) for p in pairs}
+    qn = [u16(synth.query(w, 0, r, 0, device="cpu")) for r in range(L)]
+    cfg = O.Config(D=D, bits=list(bits))
+    t0 = time.time()
+
+    def build(p):
+        b, h = p
+        return p, (O.quantize_series(cfg, Xh[p][0, :, :T], rk[h], diagnostics=False),
+                   O.quantize_series(cfg, Xh[p][1, :, :T], rv[h], diagnostics=False))
+
+    with ThreadPoolExecutor(max_workers=cores) as ex:
+        ser = dict(ex.map(build, pairs))
+    log(f"cpu baseline: oracle caches for {units} series built in {time.time() - t0:.1f}s")
+
+    def step(p):
+        b, h = p
+        ks, vs = ser[p]
+        for r in range(L):
+            O.attend(ks, vs, r, T, rk[h], rv[h], qn[r][b, h], Xh[p][0, r, T], Xh[p][1, r, T], scale)
+        O.quantize_series(cfg, Xh[p][0, :, T:T + 1], rk[h], diagnostics=False)
+        O.quantize_series(cfg, Xh[p][1, :, T:T + 1], rv[h], diagnostics=False)
+
+    passes, dt = 0, 0.0
+    with ThreadPoolExecutor(max_workers=cores) as ex:
+        while dt < min_seconds:
+            t0 = time.perf_counter()
+            list(ex.map(step, pairs))
+            dt += time.perf_counter() - t0
+            passes += 1
+    per_pass = dt / passes
+    full = per_pass * (w.batch * w.heads * w.layers) / units
+    log(f"cpu baseline: {units} (b,h) series x {L} loops, {passes} passes in {dt:.2f}s on {cores} threads")
+    return {"value": w.batch / full, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{units} (batch, head) series of layer 0 at {T} cached tokens: all {L} loops of "
+                      f"fp64 oracle attention plus one-token quantize-append, on {cores} threads, "
+                      f"{passes} passes; per-pass time scaled by {w.batch * w.heads * w.layers}/{units}",
+            "sample_seconds": dt}
+
+
+if __name__ == "__main__":
+    main()

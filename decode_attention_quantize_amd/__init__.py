@@ -189,6 +189,7 @@ def decode_attn_bf16(d: Desc, k_cache, v_cache, q, k_cur, v_cur, past_len, scale
 
 
 def alloc_workspace(d: Desc, device="cuda") -> torch.Tensor:
+    """Zero-filled workspace (the arrival counters in it must start at zero)."""
     n = workspace_bytes(d)
     # torch's caching allocator returns blocks aligned to at least 512 bytes
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)

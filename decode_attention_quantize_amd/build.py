@@ -26,26 +26,27 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-Wno-unused-result"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC, *COMMON, *SOURCES[src], "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str, extra: tuple) -> str:
+    obj = os.path.join(build_dir, src + ".o")
+    cmd = [HIPCC, *COMMON, *SOURCES[src], *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
     return obj
 
 
-def build(jobs: int = 4) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int = 4, out: str = LIB, extra_flags=(), build_dir: str = BUILD) -> str:
+    """Compile every source and link `out` (default: the in-tree librq.so)."""
+    os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + f".tmp{os.getpid()}"
+        objs = list(ex.map(lambda s: _compile(s, build_dir, tuple(extra_flags)), SOURCES))
+    tmp = out + f".tmp{os.getpid()}"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -3,20 +3,38 @@
 #include <cmath>
 #include <cstring>
 
+#include <hip/hip_runtime.h>
+
 #include "rq_internal.hpp"
 
 namespace rq {
 
+// Compute units of the current device (the workspace size depends on it).
+static int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  return cus;
+}
+
+#ifndef RQ_WGS_PER_CU
+#define RQ_WGS_PER_CU 2
+#endif
+
 SplitPlan split_plan(const rq_desc* d) {
-  // Enough (b, h, split) workgroups to keep every CU busy several times over,
-  // each wave walking at least one full tile; chunks are whole workgroup passes.
-  const int unit = kWaves * tile_tokens(d->head_dim);
+  // About RQ_WGS_PER_CU workgroups per compute unit over the whole call, each a
+  // contiguous run of whole wave tiles of one (b, h), so the per-workgroup query
+  // rotation and partial merge are amortized over many tokens.
+  const long long unit = (long long)kWaves * tile_tokens(d->head_dim);
   const long long bh = (long long)d->batch * d->heads;
-  const long long target_wgs = 2048;
-  long long chunk = ((long long)d->max_tokens * bh + target_wgs - 1) / target_wgs;
+  const long long target = (long long)RQ_WGS_PER_CU * device_cus();
+  long long nsplit = (target + bh - 1) / bh;
+  if (nsplit < 1) nsplit = 1;
+  long long chunk = (d->max_tokens + nsplit - 1) / nsplit;
   chunk = ((chunk + unit - 1) / unit) * unit;
-  if (chunk < unit) chunk = unit;
-  if (chunk > 64LL * unit) chunk = 64LL * unit;
   SplitPlan p;
   p.chunk = (int)chunk;
   p.nsplit = (int)((d->max_tokens + chunk - 1) / chunk);
@@ -55,9 +73,28 @@ int anchor_loop(const rq_desc* d) { return d->policy == RQ_POLICY_LAST_LOOP ? d-
 size_t workspace_for(const rq_desc* d) {
   const SplitPlan sp = split_plan(d);
   const size_t bh = (size_t)d->batch * d->heads;
-  const size_t q = bh * qprep_words(d->head_dim) * 4;
-  const size_t qa = (q + 255) & ~(size_t)255;
-  return qa + bh * sp.nsplit * part_floats(d->head_dim) * 4;
+  return bh * sp.nsplit * part_floats(d->head_dim) * 4;
+}
+
+CombineParams combine_params(const rq_desc* d, void* ws, const uint16_t* q, const uint16_t* k_cur,
+                             const uint16_t* v_cur, const int32_t* past_len, const float* rotv, float* out,
+                             int32_t* dev_err, float scale_log2) {
+  const SplitPlan sp = split_plan(d);
+  CombineParams a;
+  a.part = static_cast<float*>(ws);
+  a.past_len = past_len;
+  a.q = q;
+  a.kcur = k_cur;
+  a.vcur = v_cur;
+  a.rotv = rotv;
+  a.out = out;
+  a.dev_err = dev_err;
+  a.scale_log2 = scale_log2;
+  a.H = d->heads;
+  a.T_max = d->max_tokens;
+  a.chunk = sp.chunk;
+  a.nsplit = sp.nsplit;
+  return a;
 }
 
 // Components decode loop r reads, in order anchor first (§3.2, App. D).
@@ -167,13 +204,6 @@ rq_status rq_decode_attn(const rq_desc* d, const rq_layer_cache* c, int32_t loop
   if (!have_decode_kernel(d->head_dim, nc, bits)) return RQ_E_UNSUPPORTED;
 
   const SplitPlan sp = split_plan(d);
-  const int D = d->head_dim;
-  const size_t bh = (size_t)d->batch * d->heads;
-  uint32_t* qprep = static_cast<uint32_t*>(ws);
-  const size_t qa = ((bh * qprep_words(D) * 4) + 255) & ~(size_t)255;
-  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + qa);
-  const float scale_log2 = softmax_scale * 1.4426950408889634f;
-
   DecodeParams p;
   std::memset(&p, 0, sizeof(p));
   for (int i = 0; i < nc; ++i) {
@@ -189,44 +219,20 @@ rq_status rq_decode_attn(const rq_desc* d, const rq_layer_cache* c, int32_t loop
       p.valpha[i] = c->alpha[1][r];
     }
   }
+  const float scale_log2 = softmax_scale * 1.4426950408889634f;
+  p.rotk = c->rot[0];
+  p.q = q;
   p.past_len = past_len;
-  p.qprep = qprep;
-  p.part = part;
-  p.dev_err = dev_err;
+  p.part = static_cast<float*>(ws);
+  p.scale_log2 = scale_log2;
   p.B = d->batch;
   p.H = d->heads;
   p.T_max = d->max_tokens;
   p.chunk = sp.chunk;
   p.nsplit = sp.nsplit;
-
-  QPrepParams qp;
-  qp.q = q;
-  qp.rotk = c->rot[0];
-  qp.qprep = qprep;
-  qp.scale_log2 = scale_log2;
-  qp.B = d->batch;
-  qp.H = d->heads;
-
-  CombineParams cp;
-  cp.part = part;
-  cp.past_len = past_len;
-  cp.q = q;
-  cp.kcur = k_cur;
-  cp.vcur = v_cur;
-  cp.rotv = c->rot[1];
-  cp.out = out;
-  cp.dev_err = dev_err;
-  cp.scale_log2 = scale_log2;
-  cp.B = d->batch;
-  cp.H = d->heads;
-  cp.T_max = d->max_tokens;
-  cp.chunk = sp.chunk;
-  cp.nsplit = sp.nsplit;
-
-  if (launch_qprep(qp, D, stream) != 0) return RQ_E_HIP;
-  if (launch_decode_main(p, D, nc, bits, stream) != 0) return RQ_E_HIP;
-  if (launch_combine(cp, D, stream) != 0) return RQ_E_HIP;
-  return RQ_OK;
+  if (launch_decode(p, d->head_dim, nc, bits, sp.nsplit, stream) != 0) return RQ_E_HIP;
+  const CombineParams cp = combine_params(d, ws, q, k_cur, v_cur, past_len, c->rot[1], out, dev_err, scale_log2);
+  return launch_combine(cp, d->head_dim, d->batch, stream) == 0 ? RQ_OK : RQ_E_HIP;
 }
 
 rq_status rq_decode_attn_bf16(const rq_desc* d, const uint16_t* k_cache, const uint16_t* v_cache,
@@ -239,44 +245,22 @@ rq_status rq_decode_attn_bf16(const rq_desc* d, const uint16_t* k_cache, const u
   if (!ws || ws_bytes < workspace_for(d) || ((uintptr_t)ws & 255) != 0) return RQ_E_WORKSPACE;
   if (!std::isfinite(softmax_scale)) return RQ_E_SHAPE;
   const SplitPlan sp = split_plan(d);
-  const int D = d->head_dim;
-  const size_t bh = (size_t)d->batch * d->heads;
-  const size_t qa = ((bh * qprep_words(D) * 4) + 255) & ~(size_t)255;
-  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + qa);
   const float scale_log2 = softmax_scale * 1.4426950408889634f;
-
   Bf16Params p;
   p.k = k_cache;
   p.v = v_cache;
   p.q = q;
   p.past_len = past_len;
-  p.part = part;
-  p.dev_err = dev_err;
+  p.part = static_cast<float*>(ws);
   p.scale_log2 = scale_log2;
   p.B = d->batch;
   p.H = d->heads;
   p.T_max = d->max_tokens;
   p.chunk = sp.chunk;
   p.nsplit = sp.nsplit;
-
-  CombineParams cp;
-  cp.part = part;
-  cp.past_len = past_len;
-  cp.q = q;
-  cp.kcur = k_cur;
-  cp.vcur = v_cur;
-  cp.rotv = nullptr;
-  cp.out = out;
-  cp.dev_err = dev_err;
-  cp.scale_log2 = scale_log2;
-  cp.B = d->batch;
-  cp.H = d->heads;
-  cp.T_max = d->max_tokens;
-  cp.chunk = sp.chunk;
-  cp.nsplit = sp.nsplit;
-  if (launch_bf16_main(p, D, stream) != 0) return RQ_E_HIP;
-  if (launch_combine(cp, D, stream) != 0) return RQ_E_HIP;
-  return RQ_OK;
+  if (launch_bf16(p, d->head_dim, sp.nsplit, stream) != 0) return RQ_E_HIP;
+  const CombineParams cp = combine_params(d, ws, q, k_cur, v_cur, past_len, nullptr, out, dev_err, scale_log2);
+  return launch_combine(cp, d->head_dim, d->batch, stream) == 0 ? RQ_OK : RQ_E_HIP;
 }
 
 }  // extern "C"

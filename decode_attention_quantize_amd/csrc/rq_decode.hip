@@ -1,8 +1,10 @@
 // Fused dequantize + split-K decode attention over the ResidualQuant cache
 // (paper "KV Cache Quantization for Looped Transformers with 2-Bit Residuals":
 // §4.1 kernel, §4.2 "Decode" past/current merge, App. G.2 "Reconstruction and
-// attention"), plus the query preparation and the cross-split combine that the
-// BF16 baseline shares.
+// attention"). Two launches per call: the fused kernel rotates the query in
+// every workgroup, streams its range of the compressed cache and stores a
+// split partial; the combine merges the partials of each (b, h) with the
+// current bf16 token and applies the single inverse value rotation.
 //
 // Per (b, h) the attended keys are zhat_t = sum_c beta_{c,t} D(c_{c,t}) in the
 // rotated domain, with components c = anchor, residual (Last-loop) or the
@@ -11,72 +13,58 @@
 // With the rotation folded into the query (q' = H_K q) the score is
 //   s_t = sum_c beta_{c,t} sum_groups [ s_{c,g} (q'_g . code_{c,g}) + o_{c,g} sum(q'_g) ],
 // and values accumulate sum_t p_t zhat_V,t in the rotated domain with the same
-// per-group split into a code part (weight p beta s) and an offset part
-// (p beta o); H_V^T is applied once in the combine.
+// per-group split into a code part (weight p beta s) and an offset part.
 //
 // Code unpacking: a masked code field read as an fp16 bit pattern is the
 // subnormal number code * 2^(shift - 24), exactly, and v_dot2c_f32_f16 keeps
 // fp16 subnormals, so one AND yields two codes ready for the dot product.
 // The packed layout places group elements e and e+16 at the same bit offset of
-// the low and high halves of a word, which is what makes one mask yield a pair.
+// the low and high halves of a word, which is what makes one mask yield a pair
+// for the keys; for the values a byte permute pairs the same element of two
+// tokens.
 #include <hip/hip_runtime.h>
 
+#include "rq_combine.hpp"
 #include "rq_device.hpp"
 #include "rq_internal.hpp"
 
 namespace rq {
 namespace {
 
+#ifndef RQ_WAVES_SMALL
+#define RQ_WAVES_SMALL 3
+#endif
+
 constexpr float kTwo24 = 16777216.0f;
-constexpr float kWScale = 64.0f;              // value weights are stored as fp16(2^6 p beta s)
+constexpr float kWScale = 64.0f;                // value weights are fp16(2^6 p beta s)
+constexpr float kWMax = 16376.0f;               // keeps 4x the weight finite in fp16
 constexpr float kMinNormal = 6.103515625e-05f;  // smallest normal fp16, 2^-14
 
-// ---------------------------------------------------------------- query prep
-template <int D>
-__global__ __launch_bounds__(D) void qprep_kernel(QPrepParams p) {
-  constexpr int G = D / 32;
-  __shared__ float qs[D];
-  __shared__ float qr[D];
-  const int bh = blockIdx.x, h = bh % p.H, i = threadIdx.x;
-  qs[i] = bf16f(p.q[(size_t)bh * D + i]);
-  __syncthreads();
-  const float* row = p.rotk + ((size_t)h * D + i) * D;
-  float acc = 0.0f;
-  for (int j = 0; j < D; ++j) acc = fmaf(row[j], qs[j], acc);
-  qr[i] = acc * p.scale_log2;
-  __syncthreads();
-  uint32_t* out = p.qprep + (size_t)bh * qprep_words(D);
-  if (i < D / 2) {
-    const int gi = i / 16, k = i % 16;
-    const float a = qr[32 * gi + k], c = qr[32 * gi + 16 + k];
-    const _Float16 ah = (_Float16)a, ch = (_Float16)c;
-    out[gi * 33 + k] = pack_h2((float)ah, (float)ch);
-    out[gi * 33 + 16 + k] = pack_h2(a - (float)ah, c - (float)ch);
-  }
-  if (i < G) {
-    float s = 0.0f;
-    for (int e = 0; e < 32; ++e) s += qr[32 * i + e];
-    out[i * 33 + 32] = __float_as_uint(s);
-  }
-}
-
-// ---------------------------------------------------------------- main kernel
 template <int BITS>
 struct Words {
   uint32_t w[BITS];  // one group of 32 codes = BITS 32-bit words
 };
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer descriptor over [base, base + bytes): loads past the end return zero
+// without touching memory (raw buffer, hardware range check).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 template <int BITS>
-__device__ __forceinline__ Words<BITS> load_group(const uint8_t* base) {
-  Words<BITS> r;
+__device__ __forceinline__ Words<BITS> load_group(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  Words<BITS> w;
   if constexpr (BITS == 4) {
-    const uint4 v = *reinterpret_cast<const uint4*>(base);
-    r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    w.w[0] = v.x; w.w[1] = v.y; w.w[2] = v.z; w.w[3] = v.w;
   } else {
-    const uint2 v = *reinterpret_cast<const uint2*>(base);
-    r.w[0] = v.x; r.w[1] = v.y;
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    w.w[0] = v.x; w.w[1] = v.y;
   }
-  return r;
+  return w;
 }
 
 // sum_e q'_e code_e over one group (q' as hi [+ lo] fp16 pairs (e, e+16)).
@@ -116,15 +104,30 @@ __device__ __forceinline__ float kdot(const Words<BITS>& c, const uint32_t (&QH)
         }
       }
     }
-    return a[0] + a[1] * 0.25f + a[2] * (1.0f / 16.0f) + a[3] * (1.0f / 64.0f);
+    return (a[0] + a[1] * 0.25f) + (a[2] * (1.0f / 16.0f) + a[3] * (1.0f / 64.0f));
   }
 }
 
-// acc[e] += w_t0 code_{t0,e} + w_t1 code_{t1,e} for the 32 elements of a group.
-// Element e of the group lands in accumulator e with an extra factor 2^shift(e)
-// (its field offset inside the selected byte), removed at the end.
+// Field scale 2^shift of element e of a group (index k = e mod 16 in its half)
+// once vacc() has moved it to a byte: INT4 k even 1, odd 16; INT2 4^(k mod 4).
 template <int BITS>
+__host__ __device__ constexpr float vclass(int e) {
+  return BITS == 4 ? (((e & 15) & 1) ? 16.0f : 1.0f) : (float)(1 << (2 * ((e & 15) & 3)));
+}
+
+// acc[e] += W.lo code_{t0,e} + W.hi code_{t1,e} for the 32 elements of a group,
+// accumulated at the field scale of reference width REF (the widest component),
+// so that every component shares one accumulator per element.
+template <int BITS, int REF>
 __device__ __forceinline__ void vacc(const Words<BITS>& c0, const Words<BITS>& c1, uint32_t W, float (&acc)[32]) {
+  uint32_t Wq[4] = {W, W, W, W};
+  if constexpr (BITS == 2 && REF == 4) {
+    // INT2 field scales 1, 4, 16, 64 -> INT4 reference 1, 16, 1, 16: weights x 1, 4, 1/16, 1/4
+    const h2_t w = __builtin_bit_cast(h2_t, W);
+    Wq[1] = __builtin_bit_cast(uint32_t, w * h2_t{(_Float16)4.0f, (_Float16)4.0f});
+    Wq[2] = __builtin_bit_cast(uint32_t, w * h2_t{(_Float16)0.0625f, (_Float16)0.0625f});
+    Wq[3] = __builtin_bit_cast(uint32_t, w * h2_t{(_Float16)0.25f, (_Float16)0.25f});
+  }
 #pragma unroll
   for (int j = 0; j < BITS; ++j) {
 #pragma unroll
@@ -140,23 +143,23 @@ __device__ __forceinline__ void vacc(const Words<BITS>& c0, const Words<BITS>& c
       } else {
         const int e = 16 * half + 8 * j + 4 * hb;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[e + q] = dot2(x & (0x00030003u << (2 * q)), W, acc[e + q]);
+        for (int q = 0; q < 4; ++q) acc[e + q] = dot2(x & (0x00030003u << (2 * q)), Wq[q], acc[e + q]);
       }
     }
   }
 }
 
-// 2^shift of element e's field in the byte vacc() selected.
-template <int BITS>
-__device__ __forceinline__ float vclass(int e) {
-  const int k = e & 15;
-  if constexpr (BITS == 4) return (k & 1) ? 16.0f : 1.0f;
-  else return (float)(1 << (2 * (k & 3)));
-}
-
 template <uint32_t CB, int c>
 constexpr int cbits() {
   return (int)((CB >> (4 * c)) & 0xF);
+}
+
+template <uint32_t CB, int NC>
+constexpr int ref_bits() {
+  int r = 2;
+  for (int c = 0; c < NC; ++c)
+    if (((CB >> (4 * c)) & 0xF) == 4) r = 4;
+  return r;
 }
 
 // Per-component tile data of one lane: codes of tokens t0, t1 for K and V, metadata, alpha.
@@ -167,24 +170,54 @@ struct CompTile {
   uint16_t ka0, ka1, va0, va1;
 };
 
+// Descriptors of one component's six streams over this workgroup's token range.
+struct CompRsrc {
+  __amdgpu_buffer_rsrc_t kc, vc, km, vm, ka, va;
+};
+
 template <int D, int BITS>
-__device__ __forceinline__ void load_comp(CompTile<BITS>& T, const DecodeParams& p, int c, size_t row0, size_t row1,
-                                          int gi) {
+__device__ __forceinline__ CompRsrc comp_rsrc(const DecodeParams& p, int c, size_t row0, uint32_t ntok) {
   constexpr int G = D / 32;
-  constexpr int RB = D * BITS / 8, GB = 4 * BITS;
-  T.k0 = load_group<BITS>(p.kcodes[c] + row0 * RB + gi * GB);
-  T.k1 = load_group<BITS>(p.kcodes[c] + row1 * RB + gi * GB);
-  T.v0 = load_group<BITS>(p.vcodes[c] + row0 * RB + gi * GB);
-  T.v1 = load_group<BITS>(p.vcodes[c] + row1 * RB + gi * GB);
-  T.km0 = p.kmeta[c][row0 * G + gi];
-  T.km1 = p.kmeta[c][row1 * G + gi];
-  T.vm0 = p.vmeta[c][row0 * G + gi];
-  T.vm1 = p.vmeta[c][row1 * G + gi];
+  constexpr uint32_t RB = D * BITS / 8;
+  CompRsrc r;
+  r.kc = make_rsrc(p.kcodes[c] + row0 * RB, ntok * RB);
+  r.vc = make_rsrc(p.vcodes[c] + row0 * RB, ntok * RB);
+  r.km = make_rsrc(p.kmeta[c] + row0 * G, ntok * G * 4);
+  r.vm = make_rsrc(p.vmeta[c] + row0 * G, ntok * G * 4);
   if (c > 0) {
-    T.ka0 = p.kalpha[c][row0];
-    T.ka1 = p.kalpha[c][row1];
-    T.va0 = p.valpha[c][row0];
-    T.va1 = p.valpha[c][row1];
+    r.ka = make_rsrc(p.kalpha[c] + row0, ntok * 2);
+    r.va = make_rsrc(p.valpha[c] + row0, ntok * 2);
+  } else {
+    r.ka = r.va = r.kc;
+  }
+  return r;
+}
+
+// Byte offsets of this lane's rows in the current tile: codes (per width),
+// metadata and alpha; token t1 = t0 + TPW sits a fixed distance further.
+struct Offs {
+  uint32_t c4, c2, m, a;
+};
+
+template <int D, int BITS>
+__device__ __forceinline__ void load_comp(CompTile<BITS>& T, const CompRsrc& r, bool has_alpha, const Offs& o) {
+  constexpr int G = D / 32;
+  constexpr int TPW = 64 / G;
+  constexpr uint32_t RB = D * BITS / 8;
+  const uint32_t oc = BITS == 4 ? o.c4 : o.c2;
+  T.k0 = load_group<BITS>(r.kc, oc);
+  T.k1 = load_group<BITS>(r.kc, oc + TPW * RB);
+  T.v0 = load_group<BITS>(r.vc, oc);
+  T.v1 = load_group<BITS>(r.vc, oc + TPW * RB);
+  T.km0 = __builtin_amdgcn_raw_buffer_load_b32(r.km, o.m, 0, 0);
+  T.km1 = __builtin_amdgcn_raw_buffer_load_b32(r.km, o.m + TPW * G * 4, 0, 0);
+  T.vm0 = __builtin_amdgcn_raw_buffer_load_b32(r.vm, o.m, 0, 0);
+  T.vm1 = __builtin_amdgcn_raw_buffer_load_b32(r.vm, o.m + TPW * G * 4, 0, 0);
+  if (has_alpha) {
+    T.ka0 = __builtin_amdgcn_raw_buffer_load_b16(r.ka, o.a, 0, 0);
+    T.ka1 = __builtin_amdgcn_raw_buffer_load_b16(r.ka, o.a + TPW * 2, 0, 0);
+    T.va0 = __builtin_amdgcn_raw_buffer_load_b16(r.va, o.a, 0, 0);
+    T.va1 = __builtin_amdgcn_raw_buffer_load_b16(r.va, o.a + TPW * 2, 0, 0);
   } else {
     T.ka0 = T.ka1 = T.va0 = T.va1 = 0x3c00;  // 1.0, unused
   }
@@ -199,57 +232,101 @@ struct Tile {
 };
 
 template <int D, int NC, uint32_t CB>
-__device__ __forceinline__ void load_tile(Tile<D, NC, CB>& T, const DecodeParams& p, size_t row0, size_t row1, int gi) {
-  load_comp<D, cbits<CB, 0>()>(T.c0, p, 0, row0, row1, gi);
-  if constexpr (NC > 1) load_comp<D, cbits<CB, 1>()>(T.c1, p, 1, row0, row1, gi);
-  if constexpr (NC > 2) load_comp<D, cbits<CB, 2>()>(T.c2, p, 2, row0, row1, gi);
-  if constexpr (NC > 3) load_comp<D, cbits<CB, 3>()>(T.c3, p, 3, row0, row1, gi);
+__device__ __forceinline__ void load_tile(Tile<D, NC, CB>& T, const CompRsrc (&R)[NC], const Offs& o) {
+  load_comp<D, cbits<CB, 0>()>(T.c0, R[0], false, o);
+  if constexpr (NC > 1) load_comp<D, cbits<CB, 1>()>(T.c1, R[1], true, o);
+  if constexpr (NC > 2) load_comp<D, cbits<CB, 2>()>(T.c2, R[2], true, o);
+  if constexpr (NC > 3) load_comp<D, cbits<CB, 3>()>(T.c3, R[3], true, o);
 }
 
-template <int D, int NC, uint32_t CB, bool HILO>
-__global__ __launch_bounds__(kThreads) void decode_main(DecodeParams p) {
+// Waves per SIMD the register budget is tuned for: three for plans whose tile
+// data is small enough (one INT4 and one INT2 component at most), two otherwise.
+template <int NC, uint32_t CB>
+constexpr int waves_for() {
+  int bits = 0;
+  for (int c = 0; c < NC; ++c) bits += (int)((CB >> (4 * c)) & 0xF);
+  return (NC <= 2 && bits <= 6) ? RQ_WAVES_SMALL : 2;
+}
+
+template <int D, int NC, uint32_t CB, bool HILO, int DEPTH>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_for<NC, CB>()))) void decode_fused(
+    DecodeParams p) {
   constexpr int G = D / 32;
   constexpr int TPW = 64 / G;
   constexpr int TILE = 2 * TPW;
+  constexpr int REF = ref_bits<CB, NC>();
   __shared__ float red[kWaves][64][33];
-  __shared__ float wm[kWaves], wl[kWaves];
+  __shared__ float qr[D];
+  __shared__ float qsrc[D];
+  __shared__ PartialLds S;
 
   const int split = blockIdx.x, bh = blockIdx.y;
-  const int b = bh / p.H;
+  const int b = bh / p.H, h = bh % p.H;
   int len = p.past_len[b];
   len = len < 0 ? 0 : (len > p.T_max ? p.T_max : len);
+  const int nvalid = len > 0 ? (len + p.chunk - 1) / p.chunk : 1;
+  if (split >= nvalid) return;  // whole block, before any barrier
   const int start = split * p.chunk;
   const int end = min(start + p.chunk, len);
-  if (start >= end) return;  // whole block, before any barrier
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+
+  // This workgroup reads rows [start, end) of its (b, h); the descriptors cover
+  // exactly that range, so tiles running past its end load zeros (masked).
+  const size_t row0 = (size_t)bh * p.T_max + start;
+  const uint32_t ntok = (uint32_t)(end - start);
   const int pi = lane / G, gi = lane % G;
   const bool lane_on = pi < TPW;
   const int gsel = lane_on ? gi : 0;
+  CompRsrc R[NC];
+  R[0] = comp_rsrc<D, cbits<CB, 0>()>(p, 0, row0, ntok);
+  if constexpr (NC > 1) R[1] = comp_rsrc<D, cbits<CB, (NC > 1 ? 1 : 0)>()>(p, 1, row0, ntok);
+  if constexpr (NC > 2) R[2] = comp_rsrc<D, cbits<CB, (NC > 2 ? 2 : 0)>()>(p, 2, row0, ntok);
+  if constexpr (NC > 3) R[3] = comp_rsrc<D, cbits<CB, (NC > 3 ? 3 : 0)>()>(p, 3, row0, ntok);
+
+  // ---- q' = scale log2(e) H_K q for this (b, h): two threads per row
+  if (tid < D) qsrc[tid] = bf16f(p.q[(size_t)bh * D + tid]);
+  __syncthreads();
+  if (tid < 2 * D) {
+    const int row = tid >> 1, half = tid & 1;
+    const float4* hr = reinterpret_cast<const float4*>(p.rotk + ((size_t)h * D + row) * D + half * (D / 2));
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < D / 8; ++j) {
+      const float4 v = hr[j];
+      const int c = half * (D / 2) + 4 * j;
+      acc = fmaf(v.x, qsrc[c], acc);
+      acc = fmaf(v.y, qsrc[c + 1], acc);
+      acc = fmaf(v.z, qsrc[c + 2], acc);
+      acc = fmaf(v.w, qsrc[c + 3], acc);
+    }
+    acc += __shfl_xor(acc, 1, 64);
+    if (half == 0) qr[row] = acc * p.scale_log2;
+  }
+  __syncthreads();
 
   uint32_t QH[16], QL[16];
-  const uint32_t* qp = p.qprep + (size_t)bh * qprep_words(D) + gsel * 33;
+  float qsum = 0.0f;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    QH[k] = qp[k];
-    QL[k] = qp[16 + k];
+    const float a = qr[32 * gsel + k], c = qr[32 * gsel + 16 + k];
+    const _Float16 ah = (_Float16)a, ch = (_Float16)c;
+    QH[k] = pack_h2((float)ah, (float)ch);
+    QL[k] = pack_h2(a - (float)ah, c - (float)ch);
+    qsum += a + c;
   }
-  const float qsum = __uint_as_float(qp[32]);
 
-  float acc[NC][32];
+  float acc[32];
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
-#pragma unroll
-    for (int e = 0; e < 32; ++e) acc[c][e] = 0.0f;
+  for (int e = 0; e < 32; ++e) acc[e] = 0.0f;
   float bias = 0.0f, lsum = 0.0f, m = -INFINITY;
-  const size_t rowbase = (size_t)bh * p.T_max;
-
-  for (int base = start + wave * TILE; base < end; base += kWaves * TILE) {
+  // Each wave keeps DEPTH tiles in flight: tile i is processed while tiles
+  // i+1 .. i+DEPTH-1 load. Loads are issued unconditionally (past the range
+  // they return zeros, masked) so the wait counts are the same on every path and
+  // the compiler does not drain the pipeline early.
+  auto process = [&](Tile<D, NC, CB>& T, int base) {
     const int t0 = base + pi, t1 = t0 + TPW;
     const bool ok0 = lane_on && t0 < end, ok1 = lane_on && t1 < end;
-    const size_t row0 = rowbase + min(t0, p.T_max - 1), row1 = rowbase + min(t1, p.T_max - 1);
-    Tile<D, NC, CB> T;
-    load_tile<D, NC, CB>(T, p, row0, row1, gsel);
 
     // ---- keys: per-component partial scores of this lane's group
     float kp0[NC], kp1[NC];
@@ -264,7 +341,6 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeParams p) {
     if constexpr (NC > 1) kpart(T.c1, 1, std::integral_constant<int, cbits<CB, 1>()>{});
     if constexpr (NC > 2) kpart(T.c2, 2, std::integral_constant<int, cbits<CB, 2>()>{});
     if constexpr (NC > 3) kpart(T.c3, 3, std::integral_constant<int, cbits<CB, 3>()>{});
-    // beta_{NC-1} = 1, beta_c = beta_{c+1} * alpha_{c+1}
     kb0[NC - 1] = kb1[NC - 1] = vb0[NC - 1] = vb1[NC - 1] = 1.0f;
     if constexpr (NC > 3) {
       kb0[2] = f16u(T.c3.ka0); kb1[2] = f16u(T.c3.ka1); vb0[2] = f16u(T.c3.va0); vb1[2] = f16u(T.c3.va1);
@@ -288,21 +364,20 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeParams p) {
     s0 = ok0 ? s0 : -INFINITY;
     s1 = ok1 ? s1 : -INFINITY;
 
-    // ---- online softmax (log2 domain, scores already scaled by log2 e)
-    const float tmax = wave_max(fmaxf(s0, s1));
-    if (tmax == -INFINITY) continue;
+    // ---- online softmax (log2 domain); the max is wave-uniform, so the rare
+    // rescale is a scalar branch
+    const float tmax = __builtin_bit_cast(
+        float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, wave_max(fmaxf(s0, s1)))));
     if (tmax > m) {
-      const float f = exp2f(m - tmax);
+      const float f = __builtin_amdgcn_exp2f(m - tmax);
       m = tmax;
       lsum *= f;
       bias *= f;
 #pragma unroll
-      for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int e = 0; e < 32; ++e) acc[c][e] *= f;
+      for (int e = 0; e < 32; ++e) acc[e] *= f;
     }
-    const float p0 = ok0 ? exp2f(s0 - m) : 0.0f;
-    const float p1 = ok1 ? exp2f(s1 - m) : 0.0f;
+    const float p0 = ok0 ? __builtin_amdgcn_exp2f(s0 - m) : 0.0f;
+    const float p1 = ok1 ? __builtin_amdgcn_exp2f(s1 - m) : 0.0f;
     lsum += p0 + p1;
 
     // ---- values: code part through dot2 with fp16 weights W = 2^6 p beta s, and the
@@ -314,107 +389,136 @@ __global__ __launch_bounds__(kThreads) void decode_main(DecodeParams p) {
     auto vpart = [&](auto& C, int c, auto bits_tag) {
       constexpr int BB = decltype(bits_tag)::value;
       const float pb0 = ok0 ? p0 * vb0[c] : 0.0f, pb1 = ok1 ? p1 * vb1[c] : 0.0f;
-      const float s0 = f16hi(C.vm0), s1 = f16hi(C.vm1), o0 = f16lo(C.vm0), o1 = f16lo(C.vm1);
-      const uint32_t W = pack_h2(fminf(pb0 * s0 * kWScale, 65504.0f), fminf(pb1 * s1 * kWScale, 65504.0f));
+      const float s0v = f16hi(C.vm0), s1v = f16hi(C.vm1), o0v = f16lo(C.vm0), o1v = f16lo(C.vm1);
+      const uint32_t W = pack_h2(fminf(pb0 * s0v * kWScale, kWMax), fminf(pb1 * s1v * kWScale, kWMax));
       const float wb0 = f16lo(W), wb1 = f16hi(W);
-      bias += (wb0 >= kMinNormal) ? wb0 * (o0 * __builtin_amdgcn_rcpf(s0)) * (1.0f / kWScale) : pb0 * o0;
-      bias += (wb1 >= kMinNormal) ? wb1 * (o1 * __builtin_amdgcn_rcpf(s1)) * (1.0f / kWScale) : pb1 * o1;
-      vacc<BB>(C.v0, C.v1, W, acc[c]);
+      bias += (wb0 >= kMinNormal) ? wb0 * (o0v * __builtin_amdgcn_rcpf(s0v)) * (1.0f / kWScale) : pb0 * o0v;
+      bias += (wb1 >= kMinNormal) ? wb1 * (o1v * __builtin_amdgcn_rcpf(s1v)) * (1.0f / kWScale) : pb1 * o1v;
+      vacc<BB, REF>(C.v0, C.v1, W, acc);
     };
     vpart(T.c0, 0, std::integral_constant<int, cbits<CB, 0>()>{});
     if constexpr (NC > 1) vpart(T.c1, 1, std::integral_constant<int, cbits<CB, 1>()>{});
     if constexpr (NC > 2) vpart(T.c2, 2, std::integral_constant<int, cbits<CB, 2>()>{});
     if constexpr (NC > 3) vpart(T.c3, 3, std::integral_constant<int, cbits<CB, 3>()>{});
+
+  };
+  auto fetch = [&](Tile<D, NC, CB>& T, int base) {
+    const uint32_t rel = (uint32_t)(base - start) + (uint32_t)pi;  // row of token t0 in the range
+    Offs o;
+    o.c4 = rel * (D / 2) + gsel * 16;
+    o.c2 = rel * (D / 4) + gsel * 8;
+    o.m = (rel * G + gsel) * 4;
+    o.a = rel * 2;
+    load_tile<D, NC, CB>(T, R, o);
+  };
+
+  constexpr int STRIDE = kWaves * TILE;
+  int base = start + wave * TILE;
+  if constexpr (DEPTH == 2) {
+    Tile<D, NC, CB> A, B;
+    fetch(A, base);
+    for (;;) {
+      if (base >= end) break;
+      fetch(B, base + STRIDE);
+      process(A, base);
+      base += STRIDE;
+      if (base >= end) break;
+      fetch(A, base + STRIDE);
+      process(B, base);
+      base += STRIDE;
+    }
+  } else {
+    Tile<D, NC, CB> A, B, C;
+    fetch(A, base);
+    fetch(B, base + STRIDE);
+    for (;;) {
+      if (base >= end) break;
+      fetch(C, base + 2 * STRIDE);
+      process(A, base);
+      base += STRIDE;
+      if (base >= end) break;
+      fetch(A, base + 2 * STRIDE);
+      process(B, base);
+      base += STRIDE;
+      if (base >= end) break;
+      fetch(B, base + 2 * STRIDE);
+      process(C, base);
+      base += STRIDE;
+    }
   }
 
-  // ---- per-lane group values -> LDS, then merge lanes and waves
-  float out[32];
+  float val[32];
 #pragma unroll
-  for (int e = 0; e < 32; ++e) {
-    float v = bias;
-    constexpr float u = kTwo24 / kWScale;
-    v = fmaf(acc[0][e], u / vclass<cbits<CB, 0>()>(e), v);
-    if constexpr (NC > 1) v = fmaf(acc[1][e], u / vclass<cbits<CB, (NC > 1 ? 1 : 0)>()>(e), v);
-    if constexpr (NC > 2) v = fmaf(acc[2][e], u / vclass<cbits<CB, (NC > 2 ? 2 : 0)>()>(e), v);
-    if constexpr (NC > 3) v = fmaf(acc[3][e], u / vclass<cbits<CB, (NC > 3 ? 3 : 0)>()>(e), v);
-    out[e] = lane_on ? v : 0.0f;
-  }
-#pragma unroll
-  for (int e = 0; e < 32; ++e) red[wave][lane][e] = out[e];
-  const float lw = wave_sum((lane_on && gi == 0) ? lsum : 0.0f);
-  if (lane == 0) {
-    wm[wave] = m;
-    wl[wave] = lw;
-  }
-  __syncthreads();
-  float M = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w]);
-  float f[kWaves];
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) f[w] = (wm[w] == -INFINITY) ? 0.0f : exp2f(wm[w] - M);
-  float* dst = p.part + ((size_t)bh * p.nsplit + split) * part_floats(D);
-  const int d = threadIdx.x;
-  if (d < D) {
-    const int g = d / 32, e = d % 32;
-    float s = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      float sw = 0.0f;
-      for (int i = 0; i < TPW; ++i) sw += red[w][i * G + g][e];
-      s = fmaf(f[w], sw, s);
-    }
-    dst[4 + d] = s;
-  }
-  if (d == 0) {
-    float l = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) l = fmaf(f[w], wl[w], l);
-    dst[0] = M;
-    dst[1] = l;
-  }
+  for (int e = 0; e < 32; ++e) val[e] = fmaf(acc[e], kTwo24 / (kWScale * vclass<REF>(e)), bias);
+  write_partial<D, 32, G, TPW>(val, (lane_on && gi == 0) ? lsum : 0.0f, m, lane_on, red, S,
+                               p.part + ((size_t)bh * p.nsplit + split) * part_floats(D));
 }
 
+
 // ---------------------------------------------------------------- combine
+// Per (b, h): merge the split partials with the current token (scored in the
+// original domain from bf16 q and k_cur) and, for the compressed cache, rotate
+// the value sum back once: out = (H_V^T acc + p_cur v_cur) / l.
 template <int D>
-__global__ __launch_bounds__(D) void combine_kernel(CombineParams p) {
+__global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
+  constexpr int NQ = kThreads / D;    // row slices of the H_V^T product
+  constexpr int RS = D / NQ;          // rows per slice
   __shared__ float acc_s[D];
-  __shared__ float red[D / 32 + 1];
-  const int bh = blockIdx.x, b = bh / p.H, h = bh % p.H, i = threadIdx.x;
+  __shared__ float red_s[kThreads];
+  __shared__ float wsum[kWaves];
+  const int bh = blockIdx.x, b = bh / p.H, h = bh % p.H, tid = threadIdx.x;
   int len = p.past_len[b];
-  if ((len < 0 || len > p.T_max) && i == 0 && h == 0 && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_LENGTH);
+  if ((len < 0 || len > p.T_max) && h == 0 && tid == 0 && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_LENGTH);
   len = len < 0 ? 0 : (len > p.T_max ? p.T_max : len);
-  const int nvalid = (len + p.chunk - 1) / p.chunk;
-  // current token score (original domain, bf16 inputs)
-  float x = bf16f(p.q[(size_t)bh * D + i]) * bf16f(p.kcur[(size_t)bh * D + i]);
-  for (int m = 1; m < 32; m <<= 1) x += __shfl_xor(x, m, 32);
-  if ((i & 31) == 0) red[i / 32] = x;
+  const int nvalid = len > 0 ? (len + p.chunk - 1) / p.chunk : 1;
+
+  float x = tid < D ? bf16f(p.q[(size_t)bh * D + tid]) * bf16f(p.kcur[(size_t)bh * D + tid]) : 0.0f;
+  x = wave_sum(x);
+  if ((tid & 63) == 0) wsum[tid >> 6] = x;
   __syncthreads();
   float scur = 0.0f;
-  for (int w = 0; w < D / 32; ++w) scur += red[w];
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) scur += wsum[w];
   scur *= p.scale_log2;
+
   const float* part = p.part + (size_t)bh * p.nsplit * part_floats(D);
   float M = scur;
-  for (int s = 0; s < nvalid; ++s) M = fmaxf(M, part[s * part_floats(D)]);
-  float l = exp2f(scur - M), a = 0.0f;
+  for (int s = 0; s < nvalid; ++s) M = fmaxf(M, part[(size_t)s * part_floats(D)]);
+  const float pcur = exp2f(scur - M);
+  float l = pcur, a = 0.0f;
   for (int s = 0; s < nvalid; ++s) {
-    const float* ps = part + s * part_floats(D);
-    const float f = exp2f(ps[0] - M);
+    const float* ps = part + (size_t)s * part_floats(D);
+    const float f = (ps[0] == -INFINITY) ? 0.0f : exp2f(ps[0] - M);
     l = fmaf(ps[1], f, l);
-    a = fmaf(ps[4 + i], f, a);
+    if (tid < D) a = fmaf(ps[4 + tid], f, a);
   }
-  float o;
+  if (tid < D) acc_s[tid] = a;
+  __syncthreads();
+  float o = 0.0f;
   if (p.rotv) {
-    acc_s[i] = a;
+    const int j = tid % D, sl = tid / D;
+    if (sl < NQ) {
+      // (H_V^T acc)_j over rows [sl RS, (sl+1) RS); consecutive threads read consecutive j
+      const float* Hm = p.rotv + (size_t)h * D * D + (size_t)sl * RS * D + j;
+      float o0 = 0.0f, o1 = 0.0f, o2 = 0.0f, o3 = 0.0f;
+#pragma unroll 4
+      for (int i = 0; i < RS; i += 4) {
+        o0 = fmaf(Hm[(size_t)(i + 0) * D], acc_s[sl * RS + i + 0], o0);
+        o1 = fmaf(Hm[(size_t)(i + 1) * D], acc_s[sl * RS + i + 1], o1);
+        o2 = fmaf(Hm[(size_t)(i + 2) * D], acc_s[sl * RS + i + 2], o2);
+        o3 = fmaf(Hm[(size_t)(i + 3) * D], acc_s[sl * RS + i + 3], o3);
+      }
+      red_s[tid] = (o0 + o1) + (o2 + o3);
+    }
     __syncthreads();
-    const float* H = p.rotv + (size_t)h * D * D;
-    o = 0.0f;
-    for (int r = 0; r < D; ++r) o = fmaf(H[(size_t)r * D + i], acc_s[r], o);  // (H^T acc)_i
-  } else {
-    o = a;
+    if (tid < D) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) o += red_s[q * D + tid];
+    }
+  } else if (tid < D) {
+    o = acc_s[tid];
   }
-  o = fmaf(exp2f(scur - M), bf16f(p.vcur[(size_t)bh * D + i]), o);
-  p.out[(size_t)bh * D + i] = o / l;
+  if (tid < D) p.out[(size_t)bh * D + tid] = fmaf(pcur, bf16f(p.vcur[(size_t)bh * D + tid]), o) / l;
 }
 
 // ---------------------------------------------------------------- dispatch
@@ -425,7 +529,13 @@ struct Entry {
   MainFn fn;
 };
 
-#define RQ_E(D, NC, CB) {D, NC, CB, decode_main<D, NC, CB, true>}
+#ifndef RQ_DEPTH
+#define RQ_DEPTH 2
+#endif
+#ifndef RQ_HILO
+#define RQ_HILO true
+#endif
+#define RQ_E(D, NC, CB) {D, NC, CB, decode_fused<D, NC, CB, RQ_HILO, RQ_DEPTH>}
 #define RQ_PLANS(D)                                                                                        \
   RQ_E(D, 1, 0x2), RQ_E(D, 1, 0x4), RQ_E(D, 2, 0x22), RQ_E(D, 2, 0x24), RQ_E(D, 2, 0x42), RQ_E(D, 2, 0x44), \
       RQ_E(D, 3, 0x244), RQ_E(D, 3, 0x224), RQ_E(D, 3, 0x222), RQ_E(D, 3, 0x444), RQ_E(D, 4, 0x2244),        \
@@ -450,33 +560,21 @@ const Entry* find(int D, int nc, const int* bits) {
 
 bool have_decode_kernel(int D, int nc, const int* bits) { return find(D, nc, bits) != nullptr; }
 
-int launch_qprep(const QPrepParams& p, int D, void* stream) {
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)(p.B * p.H));
-  switch (D) {
-    case 64: hipLaunchKernelGGL(qprep_kernel<64>, grid, dim3(64), 0, s, p); break;
-    case 96: hipLaunchKernelGGL(qprep_kernel<96>, grid, dim3(96), 0, s, p); break;
-    case 128: hipLaunchKernelGGL(qprep_kernel<128>, grid, dim3(128), 0, s, p); break;
-    default: return -1;
-  }
-  return (int)hipGetLastError();
-}
-
-int launch_decode_main(const DecodeParams& p, int D, int nc, const int* bits, void* stream) {
+int launch_decode(const DecodeParams& p, int D, int nc, const int* bits, int nsplit, void* stream) {
   const Entry* e = find(D, nc, bits);
   if (!e) return -1;
-  const dim3 grid((unsigned)p.nsplit, (unsigned)(p.B * p.H));
+  const dim3 grid((unsigned)nsplit, (unsigned)(p.B * p.H));
   hipLaunchKernelGGL(e->fn, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), p);
   return (int)hipGetLastError();
 }
 
-int launch_combine(const CombineParams& p, int D, void* stream) {
+int launch_combine(const CombineParams& p, int D, int B, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)(p.B * p.H));
+  const dim3 grid((unsigned)(B * p.H));
   switch (D) {
-    case 64: hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(64), 0, s, p); break;
-    case 96: hipLaunchKernelGGL(combine_kernel<96>, grid, dim3(96), 0, s, p); break;
-    case 128: hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(128), 0, s, p); break;
+    case 64: hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(kThreads), 0, s, p); break;
+    case 96: hipLaunchKernelGGL(combine_kernel<96>, grid, dim3(kThreads), 0, s, p); break;
+    case 128: hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(kThreads), 0, s, p); break;
     default: return -1;
   }
   return (int)hipGetLastError();

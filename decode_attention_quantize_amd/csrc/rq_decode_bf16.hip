@@ -1,14 +1,15 @@
 // BF16 decode-attention baseline: split-K flash decoding over an uncompressed
 // bf16 K/V cache, the comparison point of the paper "KV Cache Quantization for
 // Looped Transformers with 2-Bit Residuals" (§5.3 Throughput Improvement). It
-// writes the same per-split partials as the compressed kernel and shares its
-// combine (with no inverse rotation).
+// writes the same split partials as the compressed kernel and shares its
+// combine (without a value rotation).
 //
 // A lane owns 8 channels (16 bytes) of one token row; CPT = D/8 lanes cover a
-// row and a wave covers 64/CPT tokens per step, UNR steps per iteration so that
-// every lane has 2*UNR independent 16-byte loads in flight.
+// row and a wave covers 64/CPT tokens per step, UNR steps per iteration, and
+// the next iteration's rows are loaded while the current ones are processed.
 #include <hip/hip_runtime.h>
 
+#include "rq_combine.hpp"
 #include "rq_device.hpp"
 #include "rq_internal.hpp"
 
@@ -16,21 +17,22 @@ namespace rq {
 namespace {
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void bf16_main(Bf16Params p) {
+__global__ __launch_bounds__(kThreads) void bf16_fused(Bf16Params p) {
   constexpr int CPT = D / 8;
   constexpr int TPW = 64 / CPT;
   constexpr int UNR = 4;
   constexpr int TILE = TPW * UNR;
   __shared__ float red[kWaves][64][9];
-  __shared__ float wm[kWaves], wl[kWaves];
+  __shared__ PartialLds S;
 
   const int split = blockIdx.x, bh = blockIdx.y;
   const int b = bh / p.H;
   int len = p.past_len[b];
   len = len < 0 ? 0 : (len > p.T_max ? p.T_max : len);
+  const int nvalid = len > 0 ? (len + p.chunk - 1) / p.chunk : 1;
+  if (split >= nvalid) return;
   const int start = split * p.chunk;
   const int end = min(start + p.chunk, len);
-  if (start >= end) return;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ts = lane / CPT, ch = lane % CPT;
@@ -53,21 +55,29 @@ __global__ __launch_bounds__(kThreads) void bf16_main(Bf16Params p) {
   float lsum = 0.0f, m = -INFINITY;
   const size_t rowbase = (size_t)bh * p.T_max;
 
-  for (int base = start + wave * TILE; base < end; base += kWaves * TILE) {
-    uint4 kr[UNR], vr[UNR];
-    bool ok[UNR];
+  const int last = end > 0 ? end - 1 : 0;
+  auto load = [&](int base, uint4 (&kr)[UNR], uint4 (&vr)[UNR]) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int t = base + u * TPW + ts;
-      ok[u] = lane_on && t < end;
-      const size_t row = rowbase + min(t, p.T_max - 1);
+      const size_t row = rowbase + min(base + u * TPW + ts, last);  // clamped rows are masked
       kr[u] = *reinterpret_cast<const uint4*>(p.k + row * D + 8 * chs);
       vr[u] = *reinterpret_cast<const uint4*>(p.v + row * D + 8 * chs);
     }
+  };
+
+  int base = start + wave * TILE;
+  uint4 kr[UNR], vr[UNR];
+  if (base < end) load(base, kr, vr);
+  while (base < end) {
+    const int nb = base + kWaves * TILE;
+    uint4 kn[UNR], vn[UNR];
+    load(nb, kn, vn);  // unconditional prefetch (clamped rows on the last pass)
     float s[UNR];
+    bool ok[UNR];
     float tmax = -INFINITY;
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
+      ok[u] = lane_on && base + u * TPW + ts < end;
       const uint32_t w[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w};
       float d = 0.0f;
 #pragma unroll
@@ -79,8 +89,7 @@ __global__ __launch_bounds__(kThreads) void bf16_main(Bf16Params p) {
       s[u] = ok[u] ? d : -INFINITY;
       tmax = fmaxf(tmax, s[u]);
     }
-    tmax = wave_max(tmax);
-    if (tmax == -INFINITY) continue;
+    tmax = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, wave_max(tmax))));
     if (tmax > m) {
       const float f = exp2f(m - tmax);
       m = tmax;
@@ -99,53 +108,26 @@ __global__ __launch_bounds__(kThreads) void bf16_main(Bf16Params p) {
         acc[2 * i + 1] = fmaf(pu, bf16hi(w[i]), acc[2 * i + 1]);
       }
     }
-  }
-
 #pragma unroll
-  for (int e = 0; e < 8; ++e) red[wave][lane][e] = lane_on ? acc[e] : 0.0f;
-  const float lw = wave_sum((lane_on && ch == 0) ? lsum : 0.0f);
-  if (lane == 0) {
-    wm[wave] = m;
-    wl[wave] = lw;
-  }
-  __syncthreads();
-  float M = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w]);
-  float f[kWaves];
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) f[w] = (wm[w] == -INFINITY) ? 0.0f : exp2f(wm[w] - M);
-  float* dst = p.part + ((size_t)bh * p.nsplit + split) * part_floats(D);
-  const int d = threadIdx.x;
-  if (d < D) {
-    const int c = d / 8, e = d % 8;
-    float sacc = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      float sw = 0.0f;
-      for (int i = 0; i < TPW; ++i) sw += red[w][i * CPT + c][e];
-      sacc = fmaf(f[w], sw, sacc);
+    for (int u = 0; u < UNR; ++u) {
+      kr[u] = kn[u];
+      vr[u] = vn[u];
     }
-    dst[4 + d] = sacc;
+    base = nb;
   }
-  if (d == 0) {
-    float l = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) l = fmaf(f[w], wl[w], l);
-    dst[0] = M;
-    dst[1] = l;
-  }
+  write_partial<D, 8, CPT, TPW>(acc, (lane_on && ch == 0) ? lsum : 0.0f, m, lane_on, red, S,
+                                p.part + ((size_t)bh * p.nsplit + split) * part_floats(D));
 }
 
 }  // namespace
 
-int launch_bf16_main(const Bf16Params& p, int D, void* stream) {
-  const dim3 grid((unsigned)p.nsplit, (unsigned)(p.B * p.H));
+int launch_bf16(const Bf16Params& p, int D, int nsplit, void* stream) {
+  const dim3 grid((unsigned)nsplit, (unsigned)(p.B * p.H));
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (D) {
-    case 64: hipLaunchKernelGGL(bf16_main<64>, grid, dim3(kThreads), 0, s, p); break;
-    case 96: hipLaunchKernelGGL(bf16_main<96>, grid, dim3(kThreads), 0, s, p); break;
-    case 128: hipLaunchKernelGGL(bf16_main<128>, grid, dim3(kThreads), 0, s, p); break;
+    case 64: hipLaunchKernelGGL(bf16_fused<64>, grid, dim3(kThreads), 0, s, p); break;
+    case 96: hipLaunchKernelGGL(bf16_fused<96>, grid, dim3(kThreads), 0, s, p); break;
+    case 128: hipLaunchKernelGGL(bf16_fused<128>, grid, dim3(kThreads), 0, s, p); break;
     default: return -1;
   }
   return (int)hipGetLastError();

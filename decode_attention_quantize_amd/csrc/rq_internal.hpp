@@ -21,49 +21,43 @@ constexpr int groups_of(int D) { return D / 32; }
 constexpr int pairs_per_wave(int D) { return 64 / groups_of(D); }
 constexpr int tile_tokens(int D) { return 2 * pairs_per_wave(D); }
 
-// Split of the token axis: every (b, h) has nsplit chunks of `chunk` tokens.
+// Split of the token axis: every (b, h) has nsplit chunks of `chunk` tokens,
+// sized so that the whole call is about two workgroups per compute unit.
 struct SplitPlan {
   int chunk;
   int nsplit;
 };
 SplitPlan split_plan(const rq_desc* d);
 
-// Per-(b,h) prepared query: hi/lo fp16 pairs (q'_k, q'_{k+16}) per group and
-// the per-group sum of q' (fp32), q' = scale * log2(e) * H_K q.
-constexpr size_t qprep_words(int D) { return (size_t)groups_of(D) * 33; }
 constexpr size_t part_floats(int D) { return (size_t)D + 4; }
+
+// Workspace: B*H*nsplit partials of D+4 floats (m, l, -, -, acc[D]).
+
+// What the combine needs to produce the output from the partials.
+struct CombineParams {
+  const float* part;        // split partials
+  const int32_t* past_len;  // device [B]
+  const uint16_t* q;        // bf16 [B][H][D]
+  const uint16_t* kcur;     // bf16 [B][H][D]
+  const uint16_t* vcur;     // bf16 [B][H][D]
+  const float* rotv;        // fp32 [H][D][D], or nullptr (no value rotation)
+  float* out;               // fp32 [B][H][D]
+  int32_t* dev_err;
+  float scale_log2;         // softmax scale * log2(e)
+  int H, T_max, chunk, nsplit;
+};
 
 struct DecodeParams {
   const uint8_t* kcodes[kMaxComp];
   const uint32_t* kmeta[kMaxComp];
-  const uint16_t* kalpha[kMaxComp];   // [c] for c >= 1: the coefficient between c-1 and c
+  const uint16_t* kalpha[kMaxComp];   // [c] for c >= 1: alpha linking component c-1 to c
   const uint8_t* vcodes[kMaxComp];
   const uint32_t* vmeta[kMaxComp];
   const uint16_t* valpha[kMaxComp];
+  const float* rotk;                  // fp32 [H][D][D]
+  const uint16_t* q;                  // bf16 [B][H][D]
   const int32_t* past_len;
-  const uint32_t* qprep;
   float* part;
-  int32_t* dev_err;
-  int B, H, T_max, chunk, nsplit;
-};
-
-struct QPrepParams {
-  const uint16_t* q;        // bf16 [B][H][D]
-  const float* rotk;        // fp32 [H][D][D]
-  uint32_t* qprep;
-  float scale_log2;         // softmax_scale * log2(e)
-  int B, H;
-};
-
-struct CombineParams {
-  const float* part;
-  const int32_t* past_len;
-  const uint16_t* q;
-  const uint16_t* kcur;
-  const uint16_t* vcur;
-  const float* rotv;        // fp32 [H][D][D], nullptr: values are not rotated (BF16 path)
-  float* out;
-  int32_t* dev_err;
   float scale_log2;
   int B, H, T_max, chunk, nsplit;
 };
@@ -74,7 +68,6 @@ struct Bf16Params {
   const uint16_t* q;
   const int32_t* past_len;
   float* part;
-  int32_t* dev_err;
   float scale_log2;
   int B, H, T_max, chunk, nsplit;
 };
@@ -93,11 +86,10 @@ struct AppendParams {
 
 // Launchers (return hipError_t as int; 0 = success). Defined in the .hip files.
 int launch_append(const AppendParams& p, int D, void* stream);
-int launch_qprep(const QPrepParams& p, int D, void* stream);
 // ncomp components with bit widths bits[0..ncomp-1]; returns -1 if no kernel exists.
-int launch_decode_main(const DecodeParams& p, int D, int ncomp, const int* bits, void* stream);
-int launch_combine(const CombineParams& p, int D, void* stream);
-int launch_bf16_main(const Bf16Params& p, int D, void* stream);
+int launch_decode(const DecodeParams& p, int D, int ncomp, const int* bits, int nsplit, void* stream);
+int launch_bf16(const Bf16Params& p, int D, int nsplit, void* stream);
+int launch_combine(const CombineParams& p, int D, int B, void* stream);
 bool have_decode_kernel(int D, int ncomp, const int* bits);
 
 }  // namespace rq

@@ -110,7 +110,9 @@ typedef struct {
  * 1 = meta, 2 = alpha. Returns 0 if the descriptor or arguments are invalid. */
 size_t rq_buffer_bytes(const rq_desc* desc, int kind, int loop);
 
-/* Bytes of device workspace rq_decode_attn / rq_decode_attn_bf16 need (0 if invalid). */
+/* Bytes of device workspace rq_decode_attn / rq_decode_attn_bf16 need (0 if
+ * invalid). The split of the token axis, and so this size, depends on the
+ * compute-unit count of the current device. */
 size_t rq_workspace_bytes(const rq_desc* desc);
 
 /* Host-side check of a descriptor: RQ_OK or the first problem found. */
@@ -139,9 +141,13 @@ rq_status rq_quantize_append(const rq_desc* desc, const rq_layer_cache* cache,
  *   past_len: device int32 [B], cached tokens of each sequence (positions
  *     0 .. past_len[b]-1 are attended, then the current token).
  *   out: fp32 [B][H][D] = softmax(scale [q.k_t ..., q.k_cur]) [v_t ..., v_cur].
- *   workspace: device, >= rq_workspace_bytes(desc) bytes, 256-byte aligned.
- * Keys are scored as (scale * H_K q) . zhat_t; values accumulate in the rotated
- * domain and are rotated back once per (b, h). */
+ *   workspace: device, >= rq_workspace_bytes(desc) bytes, 256-byte aligned; it
+ *     holds the per-split partial results (no initial contents needed). Calls
+ *     that share a workspace must not overlap in time.
+ * Two kernel launches: every workgroup of the first rotates the query
+ * (q' = scale H_K q), scores a contiguous range of cached tokens against the
+ * rotated keys and accumulates the rotated value sum; the second merges the
+ * ranges of each (b, h) with the current token and applies H_V^T once. */
 rq_status rq_decode_attn(const rq_desc* desc, const rq_layer_cache* cache, int32_t loop,
                          const uint16_t* q, const uint16_t* k_cur, const uint16_t* v_cur,
                          const int32_t* past_len, float softmax_scale, float* out,
