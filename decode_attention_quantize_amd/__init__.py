@@ -22,7 +22,8 @@ MAX_LOOPS = 16
 
 OK = 0
 STATUS = {0: "RQ_OK", 1: "RQ_E_NULL", 2: "RQ_E_SHAPE", 3: "RQ_E_BITS", 4: "RQ_E_CAPACITY",
-          5: "RQ_E_WORKSPACE", 6: "RQ_E_UNSUPPORTED", 7: "RQ_E_HIP", 8: "RQ_E_POLICY", 9: "RQ_E_LOOP"}
+          5: "RQ_E_WORKSPACE", 6: "RQ_E_UNSUPPORTED", 7: "RQ_E_HIP", 8: "RQ_E_POLICY", 9: "RQ_E_LOOP",
+          10: "RQ_E_ALIGN"}
 POLICY_LAST_LOOP, POLICY_PREV_LOOP = 0, 1
 DEVERR_CAPACITY, DEVERR_LENGTH = 1, 2
 

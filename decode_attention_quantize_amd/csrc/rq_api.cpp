@@ -49,6 +49,8 @@ namespace {
 
 bool dim_ok(int D) { return D == 64 || D == 96 || D == 128; }
 
+bool al(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
 rq_status check_shape(const rq_desc* d) {
   if (!d) return RQ_E_NULL;
   if (d->batch < 1 || d->heads < 1 || !dim_ok(d->head_dim) || d->loops < 1 || d->loops > RQ_MAX_LOOPS ||
@@ -126,6 +128,7 @@ const char* rq_status_str(rq_status s) {
     case RQ_E_HIP: return "HIP launch failed";
     case RQ_E_POLICY: return "unknown reference policy";
     case RQ_E_LOOP: return "loop index out of range";
+    case RQ_E_ALIGN: return "device array misaligned (codes/rot/kv/q/k/v 16 B, meta/out 4 B, alpha 2 B)";
   }
   return "unknown status";
 }
@@ -159,6 +162,7 @@ rq_status rq_quantize_append(const rq_desc* d, const rq_layer_cache* c, const ui
   if (n > d->max_tokens) return RQ_E_CAPACITY;
   if (n == 0) return RQ_OK;
   if (!kv || !pos || !c->rot[0] || !c->rot[1]) return RQ_E_NULL;
+  if (!al(kv, 16) || !al(pos, 4) || !al(c->rot[0], 16) || !al(c->rot[1], 16)) return RQ_E_ALIGN;
   const int a = anchor_loop(d);
   AppendParams p;
   std::memset(&p, 0, sizeof(p));
@@ -166,6 +170,8 @@ rq_status rq_quantize_append(const rq_desc* d, const rq_layer_cache* c, const ui
     for (int r = 0; r < d->loops; ++r) {
       if (!c->codes[kvi][r] || !c->meta[kvi][r]) return RQ_E_NULL;
       if (r != a && !c->alpha[kvi][r]) return RQ_E_NULL;
+      if (!al(c->codes[kvi][r], 16) || !al(c->meta[kvi][r], 4) || (r != a && !al(c->alpha[kvi][r], 2)))
+        return RQ_E_ALIGN;
       p.codes[kvi][r] = c->codes[kvi][r];
       p.meta[kvi][r] = reinterpret_cast<uint32_t*>(c->meta[kvi][r]);
       p.alpha[kvi][r] = c->alpha[kvi][r];
@@ -194,6 +200,9 @@ rq_status rq_decode_attn(const rq_desc* d, const rq_layer_cache* c, int32_t loop
   if (!c) return RQ_E_NULL;
   if (loop < 0 || loop >= d->loops) return RQ_E_LOOP;
   if (!q || !k_cur || !v_cur || !past_len || !out || !c->rot[0] || !c->rot[1]) return RQ_E_NULL;
+  if (!al(q, 16) || !al(k_cur, 16) || !al(v_cur, 16) || !al(past_len, 4) || !al(out, 4) || !al(c->rot[0], 16) ||
+      !al(c->rot[1], 16))
+    return RQ_E_ALIGN;
   if (!ws || ws_bytes < workspace_for(d) || ((uintptr_t)ws & 255) != 0) return RQ_E_WORKSPACE;
   if (!std::isfinite(softmax_scale)) return RQ_E_SHAPE;
   int loops[RQ_MAX_LOOPS];
@@ -209,12 +218,15 @@ rq_status rq_decode_attn(const rq_desc* d, const rq_layer_cache* c, int32_t loop
   for (int i = 0; i < nc; ++i) {
     const int r = loops[i];
     if (!c->codes[0][r] || !c->meta[0][r] || !c->codes[1][r] || !c->meta[1][r]) return RQ_E_NULL;
+    if (!al(c->codes[0][r], 16) || !al(c->codes[1][r], 16) || !al(c->meta[0][r], 4) || !al(c->meta[1][r], 4))
+      return RQ_E_ALIGN;
     p.kcodes[i] = c->codes[0][r];
     p.kmeta[i] = reinterpret_cast<const uint32_t*>(c->meta[0][r]);
     p.vcodes[i] = c->codes[1][r];
     p.vmeta[i] = reinterpret_cast<const uint32_t*>(c->meta[1][r]);
     if (i > 0) {
       if (!c->alpha[0][r] || !c->alpha[1][r]) return RQ_E_NULL;
+      if (!al(c->alpha[0][r], 2) || !al(c->alpha[1][r], 2)) return RQ_E_ALIGN;
       p.kalpha[i] = c->alpha[0][r];
       p.valpha[i] = c->alpha[1][r];
     }
@@ -242,6 +254,9 @@ rq_status rq_decode_attn_bf16(const rq_desc* d, const uint16_t* k_cache, const u
   rq_status s = check_shape(d);
   if (s != RQ_OK) return s;
   if (!k_cache || !v_cache || !q || !k_cur || !v_cur || !past_len || !out) return RQ_E_NULL;
+  if (!al(k_cache, 16) || !al(v_cache, 16) || !al(q, 16) || !al(k_cur, 16) || !al(v_cur, 16) ||
+      !al(past_len, 4) || !al(out, 4))
+    return RQ_E_ALIGN;
   if (!ws || ws_bytes < workspace_for(d) || ((uintptr_t)ws & 255) != 0) return RQ_E_WORKSPACE;
   if (!std::isfinite(softmax_scale)) return RQ_E_SHAPE;
   const SplitPlan sp = split_plan(d);

@@ -18,6 +18,9 @@
 namespace rq {
 namespace {
 
+// Appends of at most this many tokens per sequence take the per-unit path.
+constexpr int kUnitAppendMaxN = 8;
+
 typedef double d4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ double bf16_to_f64(uint16_t h) {
@@ -209,13 +212,180 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   }
 }
 
+// Few-token path (decode-time store of the current token, short chunks): one
+// workgroup per (sequence, token) unit, head and tensor. The workgroup stages
+// the head's rotation in LDS once; wave w computes Z_r for its loops
+// r = w, w + 4, .. on the fp64 vector units (lane k of group gi holds channels
+// e0 = 32 gi + k and e1 = e0 + 16, the pair quantize_pair takes), so the four
+// waves rotate in parallel and the quantization steps follow the policy's
+// dependency order with one barrier per step.
+__device__ __forceinline__ double pick(const double (&v)[4], int j) {
+  double r = v[0];
+  r = j == 1 ? v[1] : r;
+  r = j == 2 ? v[2] : r;
+  r = j == 3 ? v[3] : r;
+  return r;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void append_unit(AppendParams p) {
+  constexpr int HS = D + 2;                // padded LDS row: 8-byte aligned pairs, 16 rows cover all banks
+  constexpr int NF = D * D / 4 / kThreads; // float4 per thread of the rotation
+  static_assert(NF * 4 * kThreads == D * D, "rotation staging must tile the block");
+  __shared__ float Hs[D * HS];
+  __shared__ float xs[RQ_MAX_LOOPS][D];
+  __shared__ double rec[D];                // current reference (reconstruction)
+  __shared__ double dens;                  // its squared norm
+  const int u = blockIdx.x, h = blockIdx.y, kv = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int L = p.L;
+  const int b = u / p.n, i = u % p.n;
+  const int t = p.pos[b] + i;
+  if (t < 0 || t >= p.T_max) {             // whole block, before any barrier
+    if (tid == 0 && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_CAPACITY);
+    return;
+  }
+
+  // ---- stage H (row-major, padded) and the L input rows
+  {
+    const float4* Hg = reinterpret_cast<const float4*>(p.rot[kv] + (size_t)h * D * D);
+    float4 hv[NF];
+#pragma unroll
+    for (int j = 0; j < NF; ++j) hv[j] = Hg[tid + j * kThreads];
+    uint4 xv = {0u, 0u, 0u, 0u};
+    const int xr = tid / (D / 8), xc = tid % (D / 8);
+    const bool x_on = xr < L;
+    if (x_on) {
+      const uint16_t* row = p.kv + (((((size_t)kv * L + xr) * p.B + b) * p.H + h) * p.n + i) * (size_t)D;
+      xv = reinterpret_cast<const uint4*>(row)[xc];
+    }
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+      const int f = 4 * (tid + j * kThreads), n = f / D, k = f % D;
+      float2* dst = reinterpret_cast<float2*>(&Hs[n * HS + k]);
+      dst[0] = make_float2(hv[j].x, hv[j].y);
+      dst[1] = make_float2(hv[j].z, hv[j].w);
+    }
+    if (x_on) {
+      const uint32_t w[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        xs[xr][8 * xc + 2 * q] = __uint_as_float(w[q] << 16);
+        xs[xr][8 * xc + 2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- Z_r at (e0, e1) for this wave's loops; products of fp32 and bf16 are exact in fp64
+  const int gi = lane >> 4, kk = lane & 15;
+  const bool lane_on = gi < D / 32;
+  const int e0 = lane_on ? 32 * gi + kk : 0, e1 = e0 + 16;
+  double z0[4], z1[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = wave + 4 * j;
+    double a0 = 0.0, a1 = 0.0, c0 = 0.0, c1 = 0.0;
+    if (r < L) {
+      const float* x = xs[r];
+      const float* h0 = &Hs[e0 * HS];
+      const float* h1 = &Hs[e1 * HS];
+      for (int k = 0; k < D; k += 2) {
+        const float2 xv = *reinterpret_cast<const float2*>(&x[k]);
+        const float2 u0 = *reinterpret_cast<const float2*>(&h0[k]);
+        const float2 u1 = *reinterpret_cast<const float2*>(&h1[k]);
+        const double x0 = (double)xv.x, x1 = (double)xv.y;
+        a0 = fma((double)u0.x, x0, a0);
+        c0 = fma((double)u0.y, x1, c0);
+        a1 = fma((double)u1.x, x0, a1);
+        c1 = fma((double)u1.y, x1, c1);
+      }
+    }
+    z0[j] = a0 + c0;
+    z1[j] = a1 + c1;
+  }
+
+  const size_t tok = ((size_t)b * p.H + h) * p.T_max + t;
+  const bool last = p.policy == RQ_POLICY_LAST_LOOP;
+  const int a = last ? L - 1 : 0;
+
+  // ---- anchor
+  if (wave == (a & 3)) {
+    const int j = a >> 2;
+    double r0, r1;
+    quantize_pair<D>(pick(z0, j), pick(z1, j), p.bits[a], lane_on, gi, kk, p.codes[kv][a], p.meta[kv][a],
+                     tok, r0, r1);
+    if (!lane_on) r0 = r1 = 0.0;
+    const double den = wave_sum_f64(r0 * r0 + r1 * r1);
+    if (lane_on) {
+      rec[e0] = r0;
+      rec[e1] = r1;
+    }
+    if (lane == 0) dens = den;
+  }
+  __syncthreads();
+
+  // ---- one residual: alpha against the reference in rec, then Q(Z_r - alpha ref)
+  auto residual = [&](int r, double zz0, double zz1, double& q0, double& q1, double& at, double& r0, double& r1) {
+    r0 = lane_on ? rec[e0] : 0.0;
+    r1 = lane_on ? rec[e1] : 0.0;
+    const double den = dens;
+    const double num = wave_sum_f64((lane_on ? zz0 : 0.0) * r0 + (lane_on ? zz1 : 0.0) * r1);
+    const double alpha = den > 0.0 ? num / den : 0.0;
+    const uint16_t a16 = f64_to_f16(alpha, 0);
+    at = f16_to_f64(a16);
+    if (lane == 0) p.alpha[kv][r][tok] = a16;
+    quantize_pair<D>(zz0 - at * r0, zz1 - at * r1, p.bits[r], lane_on, gi, kk, p.codes[kv][r], p.meta[kv][r], tok,
+                     q0, q1);
+  };
+
+  if (last) {
+    // every residual refers to the anchor: the waves work in parallel
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wave + 4 * j;
+      if (r < L - 1) {
+        double q0, q1, at, r0, r1;
+        residual(r, z0[j], z1[j], q0, q1, at, r0, r1);
+      }
+    }
+  } else {
+    // a chain: loop r refers to the reconstruction of loop r - 1
+    for (int r = 1; r < L; ++r) {
+      if (wave == (r & 3)) {
+        const int j = r >> 2;
+        double q0, q1, at, r0, r1;
+        residual(r, pick(z0, j), pick(z1, j), q0, q1, at, r0, r1);
+        const double n0 = lane_on ? at * r0 + q0 : 0.0, n1 = lane_on ? at * r1 + q1 : 0.0;
+        const double den = wave_sum_f64(n0 * n0 + n1 * n1);
+        if (lane_on) {
+          rec[e0] = n0;
+          rec[e1] = n1;
+        }
+        if (lane == 0) dens = den;
+      }
+      __syncthreads();
+    }
+  }
+}
+
 }  // namespace
 
 int launch_append(const AppendParams& p, int D, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.n <= kUnitAppendMaxN) {
+    const dim3 grid((unsigned)(p.B * p.n), (unsigned)p.H, 2);
+    switch (D) {
+      case 64: hipLaunchKernelGGL(append_unit<64>, grid, dim3(kThreads), 0, s, p); break;
+      case 96: hipLaunchKernelGGL(append_unit<96>, grid, dim3(kThreads), 0, s, p); break;
+      case 128: hipLaunchKernelGGL(append_unit<128>, grid, dim3(kThreads), 0, s, p); break;
+      default: return -1;
+    }
+    return (int)hipGetLastError();
+  }
   const int U = 16 / p.L;
   const long long tiles = ((long long)p.B * p.n + U - 1) / U;
   const dim3 grid((unsigned)((tiles + kWaves - 1) / kWaves), (unsigned)p.H, 2);
-  hipStream_t s = static_cast<hipStream_t>(stream);
   switch (D) {
     case 64: hipLaunchKernelGGL(append_kernel<64>, grid, dim3(kThreads), 0, s, p); break;
     case 96: hipLaunchKernelGGL(append_kernel<96>, grid, dim3(kThreads), 0, s, p); break;

@@ -257,7 +257,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
   constexpr int REF = ref_bits<CB, NC>();
   __shared__ float red[kWaves][64][33];
   __shared__ float qr[D];
-  __shared__ float qsrc[D];
   __shared__ PartialLds S;
 
   const int split = blockIdx.x, bh = blockIdx.y;
@@ -284,26 +283,54 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
   if constexpr (NC > 2) R[2] = comp_rsrc<D, cbits<CB, (NC > 2 ? 2 : 0)>()>(p, 2, row0, ntok);
   if constexpr (NC > 3) R[3] = comp_rsrc<D, cbits<CB, (NC > 3 ? 3 : 0)>()>(p, 3, row0, ntok);
 
-  // ---- q' = scale log2(e) H_K q for this (b, h): two threads per row
-  if (tid < D) qsrc[tid] = bf16f(p.q[(size_t)bh * D + tid]);
-  __syncthreads();
+  auto fetch = [&](Tile<D, NC, CB>& T, int base) {
+    const uint32_t rel = (uint32_t)(base - start) + (uint32_t)pi;  // row of token t0 in the range
+    Offs o;
+    o.c4 = rel * (D / 2) + gsel * 16;
+    o.c2 = rel * (D / 4) + gsel * 8;
+    o.m = (rel * G + gsel) * 4;
+    o.a = rel * 2;
+    load_tile<D, NC, CB>(T, R, o);
+  };
+
+  // Each wave keeps DEPTH tiles in flight: tile i is
+  // processed while tiles i+1 .. i+DEPTH-1 load. Loads are issued
+  // unconditionally (past the range they return zeros, masked) so the wait
+  // counts are the same on every path and the compiler does not drain the
+  // pipeline early.
+  constexpr int STRIDE = kWaves * TILE;
+  int base = start + wave * TILE;
+  Tile<D, NC, CB> A, B, C;
+
+  // ---- q' = scale log2(e) H_K q for this (b, h): two threads per row, each
+  // reading half of the row and half of q straight from memory (one round trip)
   if (tid < 2 * D) {
     const int row = tid >> 1, half = tid & 1;
     const float4* hr = reinterpret_cast<const float4*>(p.rotk + ((size_t)h * D + row) * D + half * (D / 2));
-    float acc = 0.0f;
+    const uint4* qv = reinterpret_cast<const uint4*>(p.q + (size_t)bh * D + half * (D / 2));
+    float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-    for (int j = 0; j < D / 8; ++j) {
-      const float4 v = hr[j];
-      const int c = half * (D / 2) + 4 * j;
-      acc = fmaf(v.x, qsrc[c], acc);
-      acc = fmaf(v.y, qsrc[c + 1], acc);
-      acc = fmaf(v.z, qsrc[c + 2], acc);
-      acc = fmaf(v.w, qsrc[c + 3], acc);
+    for (int j = 0; j < D / 16; ++j) {
+      const uint4 w = qv[j];
+      const float4 u = hr[2 * j], v = hr[2 * j + 1];
+      a0 = fmaf(u.x, bf16lo(w.x), a0);
+      a1 = fmaf(u.y, bf16hi(w.x), a1);
+      a0 = fmaf(u.z, bf16lo(w.y), a0);
+      a1 = fmaf(u.w, bf16hi(w.y), a1);
+      a0 = fmaf(v.x, bf16lo(w.z), a0);
+      a1 = fmaf(v.y, bf16hi(w.z), a1);
+      a0 = fmaf(v.z, bf16lo(w.w), a0);
+      a1 = fmaf(v.w, bf16hi(w.w), a1);
     }
+    float acc = a0 + a1;
     acc += __shfl_xor(acc, 1, 64);
     if (half == 0) qr[row] = acc * p.scale_log2;
   }
   __syncthreads();
+  // (Requesting the first tiles before the rotation would overlap the two
+  // latencies but keeps a tile live across it, which costs register spills.)
+  fetch(A, base);
+  if constexpr (DEPTH == 3) fetch(B, base + STRIDE);
 
   uint32_t QH[16], QL[16];
   float qsum = 0.0f;
@@ -320,10 +347,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
 #pragma unroll
   for (int e = 0; e < 32; ++e) acc[e] = 0.0f;
   float bias = 0.0f, lsum = 0.0f, m = -INFINITY;
-  // Each wave keeps DEPTH tiles in flight: tile i is processed while tiles
-  // i+1 .. i+DEPTH-1 load. Loads are issued unconditionally (past the range
-  // they return zeros, masked) so the wait counts are the same on every path and
-  // the compiler does not drain the pipeline early.
   auto process = [&](Tile<D, NC, CB>& T, int base) {
     const int t0 = base + pi, t1 = t0 + TPW;
     const bool ok0 = lane_on && t0 < end, ok1 = lane_on && t1 < end;
@@ -402,21 +425,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
     if constexpr (NC > 3) vpart(T.c3, 3, std::integral_constant<int, cbits<CB, 3>()>{});
 
   };
-  auto fetch = [&](Tile<D, NC, CB>& T, int base) {
-    const uint32_t rel = (uint32_t)(base - start) + (uint32_t)pi;  // row of token t0 in the range
-    Offs o;
-    o.c4 = rel * (D / 2) + gsel * 16;
-    o.c2 = rel * (D / 4) + gsel * 8;
-    o.m = (rel * G + gsel) * 4;
-    o.a = rel * 2;
-    load_tile<D, NC, CB>(T, R, o);
-  };
-
-  constexpr int STRIDE = kWaves * TILE;
-  int base = start + wave * TILE;
   if constexpr (DEPTH == 2) {
-    Tile<D, NC, CB> A, B;
-    fetch(A, base);
     for (;;) {
       if (base >= end) break;
       fetch(B, base + STRIDE);
@@ -428,9 +437,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
       base += STRIDE;
     }
   } else {
-    Tile<D, NC, CB> A, B, C;
-    fetch(A, base);
-    fetch(B, base + STRIDE);
     for (;;) {
       if (base >= end) break;
       fetch(C, base + 2 * STRIDE);
@@ -459,66 +465,90 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
 // Per (b, h): merge the split partials with the current token (scored in the
 // original domain from bf16 q and k_cur) and, for the compressed cache, rotate
 // the value sum back once: out = (H_V^T acc + p_cur v_cur) / l.
+//
+// Every load is issued up front and none depends on another: the thread's
+// slice of H_V, q/k_cur/v_cur, and the partials of all nsplit slots (slots a
+// shorter sequence did not write are loaded but ignored), so the kernel waits
+// for memory about once.
 template <int D>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
-  constexpr int NQ = kThreads / D;    // row slices of the H_V^T product
-  constexpr int RS = D / NQ;          // rows per slice
+  constexpr int NQ = kThreads / D;  // row slices of the H_V^T product
+  constexpr int RS = D / NQ;        // rows per slice
+  constexpr int PF = (int)part_floats(D);
   __shared__ float acc_s[D];
   __shared__ float red_s[kThreads];
   __shared__ float wsum[kWaves];
   const int bh = blockIdx.x, b = bh / p.H, h = bh % p.H, tid = threadIdx.x;
-  int len = p.past_len[b];
-  if ((len < 0 || len > p.T_max) && h == 0 && tid == 0 && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_LENGTH);
-  len = len < 0 ? 0 : (len > p.T_max ? p.T_max : len);
+  const int j = tid % D, sl = tid / D;
+  const bool rot = p.rotv != nullptr;
+
+  float hv[RS];
+  if (rot && sl < NQ) {
+    const float* Hm = p.rotv + ((size_t)h * D + (size_t)sl * RS) * D + j;
+#pragma unroll
+    for (int i = 0; i < RS; ++i) hv[i] = Hm[(size_t)i * D];
+  }
+  const int raw_len = p.past_len[b];
+  const bool on = tid < D;
+  const size_t qo = (size_t)bh * D + (on ? tid : 0);
+  float x = on ? bf16f(p.q[qo]) * bf16f(p.kcur[qo]) : 0.0f;
+  const float vc = bf16f(p.vcur[qo]);
+
+  if ((raw_len < 0 || raw_len > p.T_max) && h == 0 && tid == 0 && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_LENGTH);
+  const int len = raw_len < 0 ? 0 : (raw_len > p.T_max ? p.T_max : raw_len);
   const int nvalid = len > 0 ? (len + p.chunk - 1) / p.chunk : 1;
 
-  float x = tid < D ? bf16f(p.q[(size_t)bh * D + tid]) * bf16f(p.kcur[(size_t)bh * D + tid]) : 0.0f;
+  // Online merge of the splits' (m, l, acc) relative to their running max M.
+  const float* part = p.part + (size_t)bh * p.nsplit * PF;
+  float M = -INFINITY, l = 0.0f, a = 0.0f;
+#pragma unroll 4
+  for (int s = 0; s < p.nsplit; ++s) {
+    const float* ps = part + (size_t)s * PF;
+    const float ms = ps[0], ls = ps[1], as = ps[4 + (on ? tid : 0)];
+    if (s < nvalid && ms > -INFINITY) {
+      const float Mn = fmaxf(M, ms);
+      const float fo = exp2f(M - Mn), fs = exp2f(ms - Mn);
+      l = fmaf(l, fo, ls * fs);
+      a = fmaf(a, fo, as * fs);
+      M = Mn;
+    }
+  }
+  if (on) acc_s[tid] = a;
   x = wave_sum(x);
   if ((tid & 63) == 0) wsum[tid >> 6] = x;
   __syncthreads();
+
   float scur = 0.0f;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) scur += wsum[w];
   scur *= p.scale_log2;
+  const float Mt = fmaxf(M, scur);
+  const float g = (M == -INFINITY) ? 0.0f : exp2f(M - Mt);
+  const float pcur = exp2f(scur - Mt);
+  const float lt = fmaf(l, g, pcur);
 
-  const float* part = p.part + (size_t)bh * p.nsplit * part_floats(D);
-  float M = scur;
-  for (int s = 0; s < nvalid; ++s) M = fmaxf(M, part[(size_t)s * part_floats(D)]);
-  const float pcur = exp2f(scur - M);
-  float l = pcur, a = 0.0f;
-  for (int s = 0; s < nvalid; ++s) {
-    const float* ps = part + (size_t)s * part_floats(D);
-    const float f = (ps[0] == -INFINITY) ? 0.0f : exp2f(ps[0] - M);
-    l = fmaf(ps[1], f, l);
-    if (tid < D) a = fmaf(ps[4 + tid], f, a);
-  }
-  if (tid < D) acc_s[tid] = a;
-  __syncthreads();
   float o = 0.0f;
-  if (p.rotv) {
-    const int j = tid % D, sl = tid / D;
+  if (rot) {
     if (sl < NQ) {
-      // (H_V^T acc)_j over rows [sl RS, (sl+1) RS); consecutive threads read consecutive j
-      const float* Hm = p.rotv + (size_t)h * D * D + (size_t)sl * RS * D + j;
       float o0 = 0.0f, o1 = 0.0f, o2 = 0.0f, o3 = 0.0f;
-#pragma unroll 4
+#pragma unroll
       for (int i = 0; i < RS; i += 4) {
-        o0 = fmaf(Hm[(size_t)(i + 0) * D], acc_s[sl * RS + i + 0], o0);
-        o1 = fmaf(Hm[(size_t)(i + 1) * D], acc_s[sl * RS + i + 1], o1);
-        o2 = fmaf(Hm[(size_t)(i + 2) * D], acc_s[sl * RS + i + 2], o2);
-        o3 = fmaf(Hm[(size_t)(i + 3) * D], acc_s[sl * RS + i + 3], o3);
+        o0 = fmaf(hv[i + 0], acc_s[sl * RS + i + 0], o0);
+        o1 = fmaf(hv[i + 1], acc_s[sl * RS + i + 1], o1);
+        o2 = fmaf(hv[i + 2], acc_s[sl * RS + i + 2], o2);
+        o3 = fmaf(hv[i + 3], acc_s[sl * RS + i + 3], o3);
       }
       red_s[tid] = (o0 + o1) + (o2 + o3);
     }
     __syncthreads();
-    if (tid < D) {
+    if (on) {
 #pragma unroll
       for (int q = 0; q < NQ; ++q) o += red_s[q * D + tid];
     }
-  } else if (tid < D) {
+  } else if (on) {
     o = acc_s[tid];
   }
-  if (tid < D) p.out[(size_t)bh * D + tid] = fmaf(pcur, bf16f(p.vcur[(size_t)bh * D + tid]), o) / l;
+  if (on) p.out[(size_t)bh * D + tid] = fmaf(g, o, pcur * vc) / lt;
 }
 
 // ---------------------------------------------------------------- dispatch

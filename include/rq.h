@@ -31,6 +31,10 @@
  *     from device memory by the kernels, so a decode step can be captured once
  *     in a hipGraph and replayed. Kernels clamp them to [0, max_tokens] and, if
  *     `dev_err` (device int32, may be NULL) is given, OR an RQ_DEVERR_* bit into it.
+ *   - Alignment of device arrays: codes, rot, kv, q, k_cur, v_cur, k_cache and
+ *     v_cache 16 bytes; meta and out 4 bytes; alpha 2 bytes; the
+ *     workspace 256 bytes. Otherwise the call returns RQ_E_ALIGN (RQ_E_WORKSPACE
+ *     for the workspace). Every allocation of the HIP or torch allocators meets this.
  *   - No C++ exception crosses this interface.
  *
  * Data types: bf16 and fp16 values travel as uint16_t bit patterns.
@@ -57,7 +61,8 @@ typedef enum {
   RQ_E_UNSUPPORTED = 6,  /* valid request this build has no kernel for */
   RQ_E_HIP = 7,          /* a HIP launch failed */
   RQ_E_POLICY = 8,       /* unknown reference policy */
-  RQ_E_LOOP = 9          /* loop index out of range */
+  RQ_E_LOOP = 9,         /* loop index out of range */
+  RQ_E_ALIGN = 10        /* a device array is not aligned as documented below */
 } rq_status;
 
 /* Device-side error bits (OR-ed into *dev_err when given). */

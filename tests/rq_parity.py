@@ -176,9 +176,10 @@ def max_rel_err(gpu_out: torch.Tensor, ref: dict) -> float:
 
 
 def build_gpu_layer(X: torch.Tensor, rot_k, rot_v, bits, policy, T_max: int, T: int,
-                    steps_of_one: int = 0, pos0=None) -> rq.LayerCache:
+                    steps_of_one: int = 0, pos0=None, chunk: int = 1) -> rq.LayerCache:
     """Fill a GPU cache with tokens [0, T) of X (bf16 [2][L][B][H][*][D] on the GPU): one
-    bulk append of the first T - steps_of_one tokens, then single-token appends."""
+    bulk append of the first T - steps_of_one tokens, then appends of `chunk` tokens
+    (the last one shorter) until T."""
     _, L, B, H, _, D = X.shape
     d = rq.make_desc(B, H, D, bits, T_max, policy)
     cache = rq.LayerCache.allocate(d, rot_k, rot_v)
@@ -186,9 +187,11 @@ def build_gpu_layer(X: torch.Tensor, rot_k, rot_v, bits, policy, T_max: int, T: 
     pos = torch.zeros(B, dtype=torch.int32, device="cuda") if pos0 is None else pos0
     if n0 > 0:
         rq.quantize_append(cache, X[..., :n0, :].contiguous(), pos, n0)
-    for i in range(steps_of_one):
-        t = n0 + i
+    t = max(n0, 0)
+    while t < T:
+        n = min(chunk, T - t)
         p = torch.full((B,), t, dtype=torch.int32, device="cuda")
-        rq.quantize_append(cache, X[..., t:t + 1, :].contiguous(), p, 1)
+        rq.quantize_append(cache, X[..., t:t + n, :].contiguous(), p, n)
+        t += n
     torch.cuda.synchronize()
     return cache

@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert "gfx950" in rq.version()
-    for code in range(10):
+    for code in range(11):
         assert rq.status_str(code) and rq.status_str(code) != "unknown status"
 
 
@@ -95,6 +95,10 @@ def test_append_validation():
     assert L.rq_quantize_append(by(d), by(c), None, None, 0, None, 0) == 0      # n == 0: no-op
     cn = _cache(d, null_alpha=True)                                            # residual loops need alpha
     assert L.rq_quantize_append(by(d), by(cn), FAKE, FAKE, 1, None, 0) == 1
+    ca = _cache(d)
+    ca.meta[0][1] = 0x100002                                                   # meta needs 4 bytes
+    assert L.rq_quantize_append(by(d), by(ca), FAKE, FAKE, 1, None, 0) == 10
+    assert L.rq_quantize_append(by(d), by(c), ctypes.c_void_p(0x100001), FAKE, 1, None, 0) == 10
 
 
 def test_decode_validation():
@@ -112,6 +116,11 @@ def test_decode_validation():
     assert L.rq_decode_attn(*args(ws_n=ws - 1)) == 5
     assert L.rq_decode_attn(*args(ws_ptr=ctypes.c_void_p(0x100010))) == 5    # not 256-byte aligned
     assert L.rq_decode_attn(*args(scale=float("nan"))) == 2
+    assert L.rq_decode_attn(*args(q=ctypes.c_void_p(0x100008))) == 10        # q needs 16-byte alignment
+    cm = _cache(d)
+    cm.codes[1][3] = 0x100004                                                  # codes need 16 bytes
+    assert L.rq_decode_attn(by(d), by(cm), 0, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE, ws,
+                            None, 0) == 10
     # chained policy with more components than the fused kernel takes
     d6 = _desc(bits=[4, 4, 2, 2, 2, 2], policy=1)
     c6 = _cache(d6)
@@ -131,3 +140,5 @@ def test_bf16_validation():
                                  ws, None, 0) == 1
     assert L.rq_decode_attn_bf16(by(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE,
                                  ws - 1, None, 0) == 5
+    assert L.rq_decode_attn_bf16(by(d), ctypes.c_void_p(0x100008), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 ctypes.c_float(0.1), FAKE, FAKE, ws, None, 0) == 10

@@ -76,6 +76,25 @@ def test_decode_mode_appends_match_bulk():
     assert_cache_parity(compare_cache(cache, series, T), "decode-mode appends")
 
 
+@pytest.mark.parametrize("wname,D,policy,chunk", [
+    ("huginn_4k", 96, PREV, 3),     # eight loops: two per wave, a chain across waves and barriers
+    ("tiny", 64, LAST, 8),          # the largest few-token append
+    ("tiny", 64, LAST, 9),          # the smallest bulk append
+    ("ouro_16k", 128, PREV, 2),
+])
+def test_few_token_appends(wname, D, policy, chunk):
+    """Appends of a few tokens per call (the per-token store path) against the oracle."""
+    w = synth.WORKLOADS[wname].with_(batch=3, heads=2, D=D)
+    T = 41
+    X, rk, rv = _inputs(w, T, batch=3)
+    bits = w.chained_bits if policy == PREV else w.bits
+    label = f"{wname} D{D} policy={policy} chunks of {chunk}"
+    log(label)
+    cache = build_gpu_layer(X, rk, rv, bits, policy, T_max=T + 3, T=T, steps_of_one=T - 5, chunk=chunk)
+    series = oracle_layer(X, rk, rv, bits, policy, T)
+    assert_cache_parity(compare_cache(cache, series, T), label)
+
+
 def test_ragged_lengths_and_edges():
     """Per-sequence lengths 0, 1, a tile boundary, a split boundary + 1 and a long
     ragged one; every loop; the current token always joins the softmax."""
@@ -167,6 +186,19 @@ def test_device_error_flags():
                             [[None if a is None else a[:, :, 30:40].contiguous() for a in as_] for as_ in cache.alpha],
                             cache.rot)
     assert_cache_parity(compare_cache(shifted, series, 10), "capacity edge")
+    # the few-token path: 5 tokens at position 37, 3 fit
+    err.zero_()
+    pos = torch.tensor([37], dtype=torch.int32, device="cuda")
+    log("device error flags: few-token append past capacity")
+    rq.quantize_append(cache, X[..., 20:25, :].contiguous(), pos, 5, dev_err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & rq.DEVERR_CAPACITY
+    series = oracle_layer(X[..., 20:23, :], rk, rv, w.bits, LAST, 3)
+    tail = rq.LayerCache(d, [[c[:, :, 37:40].contiguous() for c in cs] for cs in cache.codes],
+                         [[m[:, :, 37:40].contiguous() for m in ms] for ms in cache.meta],
+                         [[None if a is None else a[:, :, 37:40].contiguous() for a in as_] for as_ in cache.alpha],
+                         cache.rot)
+    assert_cache_parity(compare_cache(tail, series, 3), "few-token capacity edge")
     err.zero_()
     ws = rq.alloc_workspace(d)
     out = torch.empty(1, 2, 64, device="cuda")
