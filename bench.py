@@ -56,6 +56,113 @@ def call_bytes(D, bits, policy, r):
     return 2 * sum(comp_bytes(D, bits[c], c != a) for c in comps)
 
 
+DOM_KERNEL = "decode_fused<128, 2, 36u, true, 2>"
+COPY_KERNEL = "bitwise_not"
+COPY_KIB = float(1 << 20)            # 1 GiB read and 1 GiB written by the calibration kernel
+PROFILES = os.path.join(ROOT, "profiles")
+FETCH_FILE = os.path.join(PROFILES, "decode_fused_loop1_ouro_16k_fetch_size.txt")
+WRITE_FILE = os.path.join(PROFILES, "decode_fused_loop1_ouro_16k_write_size.txt")
+KERNEL_SOURCES = ["rq_decode.hip", "rq_combine.hpp", "rq_device.hpp", "rq_internal.hpp"]
+
+
+def kernel_source_hash():
+    """sha256 over the sources of the decode kernels and the build flags."""
+    import hashlib
+    h = hashlib.sha256()
+    pkg = os.path.join(ROOT, "decode_attention_quantize_amd")
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(pkg, "csrc", name), "rb") as f:
+            h.update(f.read())
+    with open(os.path.join(pkg, "build.py"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _read_counter_summary(path, counter):
+    """(source hash, {kernel: mean KiB per dispatch}) from a summary this script wrote."""
+    if not os.path.exists(path):
+        return None, {}
+    src, vals = None, {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("# kernel sources sha256:"):
+                src = line.split(":", 1)[1].strip()
+            elif line.startswith("counter\t" + counter + "\t"):
+                _, _, kern, n, mean = line.rstrip("\n").split("\t")
+                vals[kern] = float(mean)
+    return src, vals
+
+
+def profiled_traffic(alg_bytes):
+    """HBM bytes per launch of the dominant kernel from the committed FETCH_SIZE and
+    WRITE_SIZE summaries, each scaled by the copy kernel's reading of its known size;
+    None when a summary is missing or was taken on other kernel sources."""
+    cur = kernel_source_hash()
+    total, used = 0.0, []
+    for path, counter in ((FETCH_FILE, "FETCH_SIZE"), (WRITE_FILE, "WRITE_SIZE")):
+        src, vals = _read_counter_summary(path, counter)
+        if src != cur or DOM_KERNEL not in vals:
+            return None
+        copy = [v for k, v in vals.items() if COPY_KERNEL in k]
+        if not copy or copy[0] <= 0:
+            return None
+        factor = COPY_KIB / copy[0]
+        total += vals[DOM_KERNEL] * factor * 1024.0
+        used.append(f"{os.path.basename(path)} (x{factor:.4f})")
+    return {"bytes": total, "source": ", ".join(used)}
+
+
+def summarize_profile(directory, title, command):
+    """Text summary of rocprofv3 CSV output under `directory`: per-kernel kernel-trace
+    statistics, or per-kernel mean counter values (KiB per dispatch for FETCH_SIZE /
+    WRITE_SIZE), with the command that made it and the kernel-source hash."""
+    import csv
+    import glob
+    import re
+
+    def short(name):
+        m = re.search(r"(decode_fused<[^>]*>|bf16_fused<[^>]*>|combine_kernel<[^>]*>|append_kernel<[^>]*>|"
+                      r"append_unit<[^>]*>)", name)
+        if m:
+            return m.group(1)
+        if COPY_KERNEL in name:
+            return "elementwise " + COPY_KERNEL + " (1 GiB in, 1 GiB out)"
+        return "torch/runtime: " + re.sub(r"\s+", " ", name)[:60]
+
+    lines = [f"# {title}", f"# command: {command}", f"# kernel sources sha256: {kernel_source_hash()}"]
+    stats = glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True)
+    counters = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if stats:
+        agg = {}
+        for row in csv.DictReader(open(stats[0])):
+            k = short(row["Name"])
+            n, tot = int(row["Calls"]), float(row["TotalDurationNs"])
+            a = agg.setdefault(k, [0, 0.0, float("inf"), 0.0])
+            a[0] += n
+            a[1] += tot
+            a[2] = min(a[2], float(row["MinNs"]))
+            a[3] = max(a[3], float(row["MaxNs"]))
+        total = sum(a[1] for a in agg.values())
+        lines.append("kernel\tcalls\tavg_us\tmin_us\tmax_us\ttotal_ms\tpct")
+        for k, (n, tot, mn, mx) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+            lines.append(f"{k}\t{n}\t{tot / n / 1e3:.2f}\t{mn / 1e3:.2f}\t{mx / 1e3:.2f}\t{tot / 1e6:.2f}\t"
+                         f"{100 * tot / total:.1f}")
+    for path in counters:
+        per = {}
+        for row in csv.DictReader(open(path)):
+            k = short(row["Kernel_Name"])
+            key = (row["Counter_Name"], k)
+            d = per.setdefault(key, {})
+            did = row["Dispatch_Id"]
+            d[did] = d.get(did, 0.0) + float(row["Counter_Value"])
+        lines.append("counter\tname\tkernel\tdispatches\tmean_per_dispatch")
+        for (cn, k), d in sorted(per.items()):
+            if k.startswith("torch/runtime"):
+                continue
+            lines.append(f"counter\t{cn}\t{k}\t{len(d)}\t{sum(d.values()) / len(d):.1f}")
+    return "\n".join(lines) + "\n"
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -72,7 +179,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum timed CPU-oracle seconds")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB read + 1 GiB write elementwise kernel (counter scaling)")
+    ap.add_argument("--summarize-profile", nargs=3, metavar=("DIR", "TITLE", "COMMAND"),
+                    help="print a text summary of rocprofv3 CSV output in DIR and exit")
     args = ap.parse_args()
+    if args.summarize_profile:
+        print(summarize_profile(*args.summarize_profile), end="")
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -228,38 +340,55 @@ def main():
                           "rq_speedup_over_bf16": dt_bf / dt_rq}
         log(f"bf16: {K} steps in {dt_bf * 1e3:.2f} ms")
 
-    # ---------------------------------------------------------------- dominant call, HIP events
-    # loops 1-2 (INT4 anchor + INT2 residual) are the most frequent and largest calls
+    # ---------------------------------------------------------------- dominant kernel, HIP events
+    # The streaming kernel (rq_decode_attn_partial's single launch) of loops 1-2
+    # (INT4 anchor + INT2 residual) is the largest share of the step. It is timed
+    # alone, back to back on the stream it is launched on; the combine launch and
+    # whole calls are timed the same way for context.
     reps = args.call_reps
     stream = torch.cuda.current_stream()
+
+    def events(fn):
+        for _ in range(3):
+            fn(0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / reps
+
     percall = {}
     for r in range(L):
         kc = kvcur[0, 0, 0, r, :, :, 0]
         vc = kvcur[0, 0, 1, r, :, :, 0]
-        for _ in range(3):
-            rq.decode_attn(caches[0], r, qs[0, 0, r], kc, vc, past_len, scale, out[0, r], ws, stream=stream)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(reps):
-            rq.decode_attn(caches[i % w.layers], r, qs[0, 0, r], kc, vc, past_len, scale, out[0, r], ws,
-                           stream=stream)
-        e1.record(stream)
-        e1.synchronize()
-        ms = e0.elapsed_time(e1) / reps
         nbytes = call_bytes(D, bits, "last", r) * B * H * T
-        percall[r] = {"ms": ms, "bytes": nbytes, "gbps": nbytes / (ms * 1e-3) / 1e9}
+        ms_k = events(lambda i: rq.decode_attn_partial(caches[i % w.layers], r, qs[0, 0, r], past_len, scale, ws,
+                                                       stream=stream))
+        ms_c = events(lambda i: rq.decode_combine(d_rq, caches[i % w.layers].rot[1], qs[0, 0, r], kc, vc, past_len,
+                                                  scale, out[0, r], ws, stream=stream))
+        ms_call = events(lambda i: rq.decode_attn(caches[i % w.layers], r, qs[0, 0, r], kc, vc, past_len, scale,
+                                                  out[0, r], ws, stream=stream))
+        percall[r] = {"kernel_ms": ms_k, "combine_ms": ms_c, "call_ms": ms_call, "bytes": nbytes,
+                      "kernel_gbps": nbytes / (ms_k * 1e-3) / 1e9}
     dom = percall[0]
-    result["roofline"] = {"bound": "hbm", "achieved": dom["gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                          "frac": dom["gbps"] / HBM_PEAK_GBPS, "traffic": None,
-                          "kernel": "rq_decode_attn loop 1 (INT4 anchor + INT2 residual), one call = "
-                                    "query prep + fused split-K kernel + combine",
-                          "bytes_per_launch": dom["bytes"], "ms_per_launch": dom["ms"]}
+    traffic = profiled_traffic(dom["bytes"])
+    result["roofline"] = {"bound": "hbm", "achieved": dom["kernel_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                          "frac": dom["kernel_gbps"] / HBM_PEAK_GBPS,
+                          "traffic": None if traffic is None else traffic["bytes"],
+                          "kernel": DOM_KERNEL + " (rq_decode_attn_partial, loop 1: INT4 anchor + INT2 residual, "
+                                                 "K and V)",
+                          "bytes_per_launch": dom["bytes"], "ms_per_launch": dom["kernel_ms"],
+                          "traffic_source": None if traffic is None else traffic["source"]}
     result["per_call"] = {f"loop{r + 1}": v for r, v in percall.items()}
 
     if args.calibrate_copy:
-        a = torch.ones(1 << 28, dtype=torch.float32, device=dev)       # 1 GiB
+        # a plain streaming kernel of known size for scaling the HBM counters:
+        # reads 1 GiB and writes 1 GiB
+        a = torch.ones(1 << 28, dtype=torch.int32, device=dev)
         b = torch.empty_like(a)
-        torch.add(a, 0.0, out=b)
+        torch.bitwise_not(a, out=b)
         torch.cuda.synchronize()
         del a, b
 

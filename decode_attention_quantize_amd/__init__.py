@@ -5,8 +5,8 @@ quantization, packing, fused dequantize + attention, combine) runs in the HIP
 kernels of ``librq.so``. PyTorch provides device memory and streams.
 
 Importing this package loads ``librq.so`` from the package directory and fails
-loudly if it is missing; build it with ``python -m
-decode_attention_quantize_amd.build`` (or ``__graft_entry__.build()``).
+loudly if it is missing; build it with ``python
+decode_attention_quantize_amd/build.py`` (or ``__graft_entry__.build()``).
 """
 from __future__ import annotations
 
@@ -48,7 +48,7 @@ class LayerCacheC(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"librq.so not found at {LIB_PATH}; build it first "
-                          "(python -m decode_attention_quantize_amd.build)")
+                          "(python decode_attention_quantize_amd/build.py)")
     L = ctypes.CDLL(LIB_PATH)
     P, I, Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     L.rq_buffer_bytes.restype = Z
@@ -61,6 +61,12 @@ def _load():
     L.rq_quantize_append.argtypes = [P, P, P, P, I, P, P]
     L.rq_decode_attn.restype = ctypes.c_int
     L.rq_decode_attn.argtypes = [P, P, I, P, P, P, P, ctypes.c_float, P, P, Z, P, P]
+    L.rq_split_plan.restype = ctypes.c_int
+    L.rq_split_plan.argtypes = [P, P, P]
+    L.rq_decode_attn_partial.restype = ctypes.c_int
+    L.rq_decode_attn_partial.argtypes = [P, P, I, P, P, ctypes.c_float, P, Z, P]
+    L.rq_decode_combine.restype = ctypes.c_int
+    L.rq_decode_combine.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P, Z, P, P]
     L.rq_decode_attn_bf16.restype = ctypes.c_int
     L.rq_decode_attn_bf16.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, P, P, Z, P, P]
     L.rq_status_str.restype = ctypes.c_char_p
@@ -102,6 +108,13 @@ def buffer_bytes(d: Desc, kind: int, loop: int) -> int:
 
 def workspace_bytes(d: Desc) -> int:
     return lib.rq_workspace_bytes(ctypes.byref(d))
+
+
+def split_plan(d: Desc) -> tuple[int, int]:
+    """(chunk, nsplit): slots of `chunk` cached tokens per (b, h)."""
+    chunk, nsplit = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib.rq_split_plan(ctypes.byref(d), ctypes.byref(chunk), ctypes.byref(nsplit)), "rq_split_plan")
+    return chunk.value, nsplit.value
 
 
 def _ptr(t) -> int | None:
@@ -181,6 +194,22 @@ def decode_attn(cache: LayerCache, loop: int, q, k_cur, v_cur, past_len, scale: 
            "rq_decode_attn")
 
 
+def decode_attn_partial(cache: LayerCache, loop: int, q, past_len, scale: float, workspace, stream=None):
+    """First launch of decode_attn: per-slot partials (m, l, -, -, acc[D]) into the workspace."""
+    cc = cache.c()
+    _check(lib.rq_decode_attn_partial(ctypes.byref(cache.desc), ctypes.byref(cc), loop, _ptr(q), _ptr(past_len),
+                                      scale, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream)), "rq_decode_attn_partial")
+
+
+def decode_combine(d: Desc, rot_v, q, k_cur, v_cur, past_len, scale: float, out, workspace, dev_err=None,
+                   stream=None):
+    """Second launch of decode_attn: merge the workspace partials with the current token."""
+    _check(lib.rq_decode_combine(ctypes.byref(d), _ptr(rot_v), _ptr(q), _ptr(k_cur), _ptr(v_cur), _ptr(past_len),
+                                 scale, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _ptr(dev_err), _stream(stream)), "rq_decode_combine")
+
+
 def decode_attn_bf16(d: Desc, k_cache, v_cache, q, k_cur, v_cur, past_len, scale: float, out, workspace,
                      dev_err=None, stream=None):
     _check(lib.rq_decode_attn_bf16(ctypes.byref(d), _ptr(k_cache), _ptr(v_cache), _ptr(q), _ptr(k_cur),
@@ -190,7 +219,7 @@ def decode_attn_bf16(d: Desc, k_cache, v_cache, q, k_cur, v_cur, past_len, scale
 
 
 def alloc_workspace(d: Desc, device="cuda") -> torch.Tensor:
-    """Zero-filled workspace (the arrival counters in it must start at zero)."""
+    """Workspace for the decode calls (any initial contents; zero-filled here)."""
     n = workspace_bytes(d)
     # torch's caching allocator returns blocks aligned to at least 512 bytes
     return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)

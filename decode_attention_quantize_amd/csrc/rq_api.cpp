@@ -49,6 +49,8 @@ namespace {
 
 bool dim_ok(int D) { return D == 64 || D == 96 || D == 128; }
 
+constexpr float kLog2e = 1.4426950408889634f;
+
 bool al(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 rq_status check_shape(const rq_desc* d) {
@@ -191,18 +193,25 @@ rq_status rq_quantize_append(const rq_desc* d, const rq_layer_cache* c, const ui
   return launch_append(p, d->head_dim, stream) == 0 ? RQ_OK : RQ_E_HIP;
 }
 
-rq_status rq_decode_attn(const rq_desc* d, const rq_layer_cache* c, int32_t loop, const uint16_t* q,
-                         const uint16_t* k_cur, const uint16_t* v_cur, const int32_t* past_len,
-                         float softmax_scale, float* out, void* ws, size_t ws_bytes, int32_t* dev_err,
-                         void* stream) {
+rq_status rq_split_plan(const rq_desc* d, int32_t* chunk, int32_t* nsplit) {
+  const rq_status s = check_shape(d);
+  if (s != RQ_OK) return s;
+  if (!chunk || !nsplit) return RQ_E_NULL;
+  const SplitPlan sp = split_plan(d);
+  *chunk = sp.chunk;
+  *nsplit = sp.nsplit;
+  return RQ_OK;
+}
+
+rq_status rq_decode_attn_partial(const rq_desc* d, const rq_layer_cache* c, int32_t loop, const uint16_t* q,
+                                 const int32_t* past_len, float softmax_scale, void* ws, size_t ws_bytes,
+                                 void* stream) {
   rq_status s = check_plan(d);
   if (s != RQ_OK) return s;
   if (!c) return RQ_E_NULL;
   if (loop < 0 || loop >= d->loops) return RQ_E_LOOP;
-  if (!q || !k_cur || !v_cur || !past_len || !out || !c->rot[0] || !c->rot[1]) return RQ_E_NULL;
-  if (!al(q, 16) || !al(k_cur, 16) || !al(v_cur, 16) || !al(past_len, 4) || !al(out, 4) || !al(c->rot[0], 16) ||
-      !al(c->rot[1], 16))
-    return RQ_E_ALIGN;
+  if (!q || !past_len || !c->rot[0]) return RQ_E_NULL;
+  if (!al(q, 16) || !al(past_len, 4) || !al(c->rot[0], 16)) return RQ_E_ALIGN;
   if (!ws || ws_bytes < workspace_for(d) || ((uintptr_t)ws & 255) != 0) return RQ_E_WORKSPACE;
   if (!std::isfinite(softmax_scale)) return RQ_E_SHAPE;
   int loops[RQ_MAX_LOOPS];
@@ -231,20 +240,53 @@ rq_status rq_decode_attn(const rq_desc* d, const rq_layer_cache* c, int32_t loop
       p.valpha[i] = c->alpha[1][r];
     }
   }
-  const float scale_log2 = softmax_scale * 1.4426950408889634f;
   p.rotk = c->rot[0];
   p.q = q;
   p.past_len = past_len;
   p.part = static_cast<float*>(ws);
-  p.scale_log2 = scale_log2;
+  p.scale_log2 = softmax_scale * kLog2e;
   p.B = d->batch;
   p.H = d->heads;
   p.T_max = d->max_tokens;
   p.chunk = sp.chunk;
   p.nsplit = sp.nsplit;
-  if (launch_decode(p, d->head_dim, nc, bits, sp.nsplit, stream) != 0) return RQ_E_HIP;
-  const CombineParams cp = combine_params(d, ws, q, k_cur, v_cur, past_len, c->rot[1], out, dev_err, scale_log2);
+  return launch_decode(p, d->head_dim, nc, bits, sp.nsplit, stream) == 0 ? RQ_OK : RQ_E_HIP;
+}
+
+rq_status rq_decode_combine(const rq_desc* d, const float* rot_v, const uint16_t* q, const uint16_t* k_cur,
+                            const uint16_t* v_cur, const int32_t* past_len, float softmax_scale, float* out,
+                            const void* ws, size_t ws_bytes, int32_t* dev_err, void* stream) {
+  rq_status s = check_shape(d);
+  if (s != RQ_OK) return s;
+  if (!q || !k_cur || !v_cur || !past_len || !out) return RQ_E_NULL;
+  if (!al(q, 16) || !al(k_cur, 16) || !al(v_cur, 16) || !al(past_len, 4) || !al(out, 4) ||
+      (rot_v && !al(rot_v, 16)))
+    return RQ_E_ALIGN;
+  if (!ws || ws_bytes < workspace_for(d) || ((uintptr_t)ws & 255) != 0) return RQ_E_WORKSPACE;
+  if (!std::isfinite(softmax_scale)) return RQ_E_SHAPE;
+  const CombineParams cp = combine_params(d, const_cast<void*>(ws), q, k_cur, v_cur, past_len, rot_v, out,
+                                          dev_err, softmax_scale * kLog2e);
   return launch_combine(cp, d->head_dim, d->batch, stream) == 0 ? RQ_OK : RQ_E_HIP;
+}
+
+rq_status rq_decode_attn(const rq_desc* d, const rq_layer_cache* c, int32_t loop, const uint16_t* q,
+                         const uint16_t* k_cur, const uint16_t* v_cur, const int32_t* past_len,
+                         float softmax_scale, float* out, void* ws, size_t ws_bytes, int32_t* dev_err,
+                         void* stream) {
+  rq_status s = check_plan(d);
+  if (s != RQ_OK) return s;
+  if (!c) return RQ_E_NULL;
+  if (loop < 0 || loop >= d->loops) return RQ_E_LOOP;
+  if (!q || !k_cur || !v_cur || !past_len || !out || !c->rot[0] || !c->rot[1]) return RQ_E_NULL;
+  if (!al(q, 16) || !al(k_cur, 16) || !al(v_cur, 16) || !al(past_len, 4) || !al(out, 4) || !al(c->rot[0], 16) ||
+      !al(c->rot[1], 16))
+    return RQ_E_ALIGN;
+  // Validate everything the second launch needs before enqueuing the first.
+  if (!ws || ws_bytes < workspace_for(d) || ((uintptr_t)ws & 255) != 0) return RQ_E_WORKSPACE;
+  s = rq_decode_attn_partial(d, c, loop, q, past_len, softmax_scale, ws, ws_bytes, stream);
+  if (s != RQ_OK) return s;
+  return rq_decode_combine(d, c->rot[1], q, k_cur, v_cur, past_len, softmax_scale, out, ws, ws_bytes, dev_err,
+                           stream);
 }
 
 rq_status rq_decode_attn_bf16(const rq_desc* d, const uint16_t* k_cache, const uint16_t* v_cache,
@@ -260,7 +302,7 @@ rq_status rq_decode_attn_bf16(const rq_desc* d, const uint16_t* k_cache, const u
   if (!ws || ws_bytes < workspace_for(d) || ((uintptr_t)ws & 255) != 0) return RQ_E_WORKSPACE;
   if (!std::isfinite(softmax_scale)) return RQ_E_SHAPE;
   const SplitPlan sp = split_plan(d);
-  const float scale_log2 = softmax_scale * 1.4426950408889634f;
+  const float scale_log2 = softmax_scale * kLog2e;
   Bf16Params p;
   p.k = k_cache;
   p.v = v_cache;

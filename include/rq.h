@@ -158,6 +158,40 @@ rq_status rq_decode_attn(const rq_desc* desc, const rq_layer_cache* cache, int32
                          const int32_t* past_len, float softmax_scale, float* out,
                          void* workspace, size_t workspace_bytes, int32_t* dev_err, void* stream);
 
+/* Split of the token axis used by the decode calls (§4.1 "split-K"): every
+ * (b, h) has *nsplit slots of *chunk consecutive cached tokens; slot i covers
+ * tokens [i*chunk, (i+1)*chunk). Depends on the current device's compute-unit
+ * count. */
+rq_status rq_split_plan(const rq_desc* desc, int32_t* chunk, int32_t* nsplit);
+
+/* The two launches of rq_decode_attn as separate calls, for callers that merge
+ * partial results themselves (for instance over a token axis split across
+ * devices, or with partials of another cache) or time the streaming kernel
+ * alone. rq_decode_attn(...) is exactly rq_decode_attn_partial(...) followed by
+ * rq_decode_combine(..., cache->rot[1], ...) on the same stream and workspace.
+ *
+ * rq_decode_attn_partial: rotates q (q' = scale H_K q) and scores the cached
+ *   tokens of each slot that holds any of the past_len[b] tokens (slot 0 always
+ *   counts, even when past_len[b] == 0). For each such (b, h, slot) it writes
+ *   float part[b][h][slot][D + 4] = (m, l, unused, unused, acc[0..D-1]) into
+ *   the workspace, with scores x_t = log2(e) * scale * <q', zhat_K,t> over the
+ *   slot's tokens, m = max_t x_t (-inf for an empty slot), l = sum_t 2^(x_t - m),
+ *   acc = sum_t 2^(x_t - m) zhat_V,t (rotated value domain). Slots past the
+ *   last used one are not written. The current token is not included.
+ * rq_decode_combine: merges the written slots of each (b, h) with the current
+ *   token (score log2(e) * scale * <q, k_cur> in the original domain) and
+ *   writes out = (rot_v^T acc + p_cur v_cur) / l, all slots rescaled to one
+ *   max. rot_v: fp32 [H][D][D] (the cache's value rotation), or NULL when the
+ *   partials are already in the original domain (as rq_decode_attn_bf16's are).
+ *   Only batch, heads, head_dim and max_tokens of desc are used; desc must be
+ *   the one the partials were made with. The workspace is only read. */
+rq_status rq_decode_attn_partial(const rq_desc* desc, const rq_layer_cache* cache, int32_t loop,
+                                 const uint16_t* q, const int32_t* past_len, float softmax_scale,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+rq_status rq_decode_combine(const rq_desc* desc, const float* rot_v, const uint16_t* q, const uint16_t* k_cur,
+                            const uint16_t* v_cur, const int32_t* past_len, float softmax_scale, float* out,
+                            const void* workspace, size_t workspace_bytes, int32_t* dev_err, void* stream);
+
 /* BF16 decode baseline (the paper's comparison point, §5.3): the same attention
  * over an uncompressed cache. k_cache, v_cache: bf16 [B][H][T_max][D]. Only
  * batch, heads, head_dim and max_tokens of desc are used. */

@@ -31,8 +31,12 @@ def _ensure_built():
     """Build the in-tree libraries if they are missing (never rebuilds)."""
     lib = os.path.join(ROOT, "decode_attention_quantize_amd", "librq.so")
     if not os.path.exists(lib):
-        from decode_attention_quantize_amd import build as b
-        b.build()
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_rq_build", os.path.join(ROOT, "decode_attention_quantize_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
 
 
 _ensure_built()

@@ -129,6 +129,29 @@ def test_decode_validation():
                             ws6, None, 0) == 6
 
 
+def test_split_api_validation():
+    L = rq.lib
+    d = _desc()
+    c = _cache(d)
+    by = ctypes.byref
+    ws = rq.workspace_bytes(d)
+    chunk, nsplit = rq.split_plan(d)
+    assert chunk > 0 and nsplit >= 1 and chunk * nsplit >= d.max_tokens
+    assert ws == d.batch * d.heads * nsplit * (d.head_dim + 4) * 4
+    assert L.rq_split_plan(by(d), None, None) == 1
+    f = ctypes.c_float(0.1)
+    assert L.rq_decode_attn_partial(by(d), by(c), 4, FAKE, FAKE, f, FAKE, ws, 0) == 9
+    assert L.rq_decode_attn_partial(by(d), by(c), 0, None, FAKE, f, FAKE, ws, 0) == 1
+    assert L.rq_decode_attn_partial(by(d), by(c), 0, FAKE, FAKE, f, FAKE, ws - 4, 0) == 5
+    assert L.rq_decode_attn_partial(by(d), by(c), 0, ctypes.c_void_p(0x100002), FAKE, f, FAKE, ws, 0) == 10
+    assert L.rq_decode_combine(by(d), None, FAKE, FAKE, FAKE, FAKE, f, None, FAKE, ws, None, 0) == 1
+    assert L.rq_decode_combine(by(d), ctypes.c_void_p(0x100004), FAKE, FAKE, FAKE, FAKE, f, FAKE, FAKE, ws,
+                               None, 0) == 10
+    assert L.rq_decode_combine(by(d), None, FAKE, FAKE, FAKE, FAKE, f, FAKE, FAKE, ws - 1, None, 0) == 5
+    assert L.rq_decode_combine(by(d), None, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(float("inf")), FAKE, FAKE,
+                               ws, None, 0) == 2
+
+
 def test_bf16_validation():
     L = rq.lib
     d = _desc()

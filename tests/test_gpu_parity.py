@@ -111,6 +111,58 @@ def test_ragged_lengths_and_edges():
     _decode_and_compare(w, X, rk, rv, cache, series, lens, range(4), "ragged")
 
 
+def test_partial_and_combine():
+    """The two halves of decode_attn reproduce it exactly, and the documented
+    partial layout, merged in fp64 on the host with the oracle's current-token
+    score, gives the oracle's output."""
+    w = synth.WORKLOADS["tiny"].with_(batch=2, heads=3, D=128, nb=128)
+    T = 900
+    X, rk, rv = _inputs(w, T + 1, batch=2)
+    cache = build_gpu_layer(X, rk, rv, (2, 2, 4, 4), LAST, T_max=T + 1, T=T)
+    series = oracle_layer(X, rk, rv, (2, 2, 4, 4), LAST, T)
+    d = cache.desc
+    B, H, D = 2, 3, 128
+    lens = [T, 0]
+    past = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    chunk, nsplit = rq.split_plan(d)
+    scale = 1.0 / math.sqrt(D)
+    for r in (0, 3):
+        q = synth.query(w, 0, r, 0, device="cuda", batch=B)
+        kc = torch.stack([X[0, r, b, :, lens[b]] for b in range(B)]).contiguous()
+        vc = torch.stack([X[1, r, b, :, lens[b]] for b in range(B)]).contiguous()
+        ws1, ws2 = rq.alloc_workspace(d), rq.alloc_workspace(d)
+        full = torch.empty(B, H, D, device="cuda")
+        split = torch.empty(B, H, D, device="cuda")
+        log(f"partial/combine loop {r}")
+        rq.decode_attn(cache, r, q, kc, vc, past, scale, full, ws1)
+        rq.decode_attn_partial(cache, r, q, past, scale, ws2)
+        torch.cuda.synchronize()
+        part = ws2[:B * H * nsplit * (D + 4) * 4].view(torch.float32).view(B, H, nsplit, D + 4).double().cpu()
+        rq.decode_combine(d, cache.rot[1], q, kc, vc, past, scale, split, ws2)
+        torch.cuda.synchronize()
+        assert torch.equal(full, split)
+        # host merge of the documented partials
+        Hv = rv.double().numpy()
+        qn, kn, vn = u16(q), u16(kc), u16(vc)
+        units = [(b, h) for b in range(B) for h in range(H)]
+        ref = oracle_attention(series, units, r, lens, rk, rv, q, kc, vc, scale)
+        l2e = 1.0 / math.log(2.0)
+        worst = 0.0
+        for b, h in units:
+            used = max(1, -(-lens[b] // chunk))
+            P = part[b, h, :used].numpy()
+            xq, xk, xv = O.bf16_decode(qn[b, h]), O.bf16_decode(kn[b, h]), O.bf16_decode(vn[b, h])
+            xc = float(xq @ xk) * scale * l2e
+            m = max([xc] + [float(v) for v in P[:, 0]])
+            wts = np.where(P[:, 0] == -np.inf, 0.0, np.exp2(P[:, 0] - m))
+            l = float(wts @ P[:, 1]) + 2.0 ** (xc - m)
+            acc = Hv[h].T @ (wts @ P[:, 4:]) + 2.0 ** (xc - m) * xv
+            o = acc / l
+            worst = max(worst, np.abs(o - ref[(b, h)]).max() / np.abs(ref[(b, h)]).max())
+        log(f"partial/combine loop {r}: host merge max rel err {worst:.3e}")
+        assert worst <= TOL_ATTN
+
+
 def test_huginn_shape_d96_eight_loops():
     w = synth.WORKLOADS["huginn_4k"].with_(batch=2, heads=3)
     T = 333
