@@ -83,18 +83,21 @@ def oracle_layer(Xall: torch.Tensor, rot_k: torch.Tensor, rot_v: torch.Tensor, b
         return dict(ex.map(run, jobs))
 
 
-def compare_cache(cache: rq.LayerCache, series: dict, T: int) -> dict:
+def host_copy(cache: rq.LayerCache) -> dict:
+    """Host copies of every cache buffer: {(kv, loop): (codes, meta, alpha)}."""
+    d = cache.desc
+    return {(kv, r): (cache.codes[kv][r].cpu().numpy(), u16(cache.meta[kv][r]),
+                      None if cache.alpha[kv][r] is None else u16(cache.alpha[kv][r]))
+            for kv in range(2) for r in range(d.loops)}
+
+
+def compare_cache(cache: rq.LayerCache, series: dict, T: int, host: dict | None = None) -> dict:
     d = cache.desc
     L, D = d.loops, d.head_dim
     anchor = L - 1 if d.policy == rq.POLICY_LAST_LOOP else 0
     stats = dict(elements=0, exempt_elements=0, meta_exempt=0, alpha_exempt=0, bad=[])
-    host = {}
-    for (kv, b, h) in series:
-        for r in range(L):
-            key = (kv, r)
-            if key not in host:
-                host[key] = (cache.codes[kv][r].cpu().numpy(), u16(cache.meta[kv][r]),
-                             None if cache.alpha[kv][r] is None else u16(cache.alpha[kv][r]))
+    if host is None:
+        host = host_copy(cache)
     for (kv, b, h), s in series.items():
         for r in range(L):
             gc, gm, ga = host[(kv, r)]

@@ -1,0 +1,140 @@
+"""GPU parity at the benchmark's full sizes and launch configuration.
+
+The 16k workload (B8, H16, D128, 4 loops, 16384 cached tokens, 64 decode
+steps, plan [2,2,4,4]; chained comparator [4,4,2,2]) is built exactly as the
+benchmark builds it: the same cache descriptor (token capacity 16384 + 64, so
+the same split plan and grid), a bulk store of the prompt tokens and one
+single-token store per decode step. Decode runs at steps 0 and 63 with the
+benchmark's queries and current tokens.
+
+Layer 0 is checked for every (batch, head): the whole cache (codes, fp16
+metadata and LS coefficients of every loop, 16447 tokens) and every loop's
+attention output. The last layer, the chained comparator and the BF16
+comparator are checked on a sample of (batch, head) series. The oracle works
+on its own quantization of the same bf16 inputs; nothing the HIP path writes
+is fed to it.
+"""
+import math
+import random
+
+import pytest
+import torch
+
+import decode_attention_quantize_amd as rq
+import synth
+from rq_parity import (TOL_ATTN, assert_cache_parity, compare_cache, host_copy, log, max_rel_err,
+                       oracle_attention, oracle_layer, u16)
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS["ouro_16k"]
+STEPS = 64
+LAST, PREV = rq.POLICY_LAST_LOOP, rq.POLICY_PREV_LOOP
+CHECK_STEPS = (0, STEPS - 1)
+
+
+def _sample_units(n, seed):
+    rnd = random.Random(seed)
+    units = {(0, 0), (W.batch - 1, W.heads - 1)}
+    while len(units) < n:
+        units.add((rnd.randrange(W.batch), rnd.randrange(W.heads)))
+    return sorted(units)
+
+
+def _build(layer, policy, bits):
+    """Inputs and a GPU cache holding tokens [0, T + STEPS - 1) of `layer`."""
+    B, H, D, T = W.batch, W.heads, W.D, W.T
+    T_max = T + STEPS
+    X = synth.kv(W, layer, 0, T_max, device="cuda")
+    rk, rv = synth.rotation(W, layer, 0), synth.rotation(W, layer, 1)
+    d = rq.make_desc(B, H, D, list(bits), T_max, policy)
+    cache = rq.LayerCache.allocate(d, rk, rv)
+    log(f"layer {layer} policy {policy}: bulk store of {T} tokens")
+    rq.quantize_append(cache, X[..., :T, :].contiguous(), torch.zeros(B, dtype=torch.int32, device="cuda"), T)
+    for k in range(STEPS - 1):
+        pos = torch.full((B,), T + k, dtype=torch.int32, device="cuda")
+        rq.quantize_append(cache, X[..., T + k:T + k + 1, :].contiguous(), pos, 1)
+    torch.cuda.synchronize()
+    return X, rk, rv, cache
+
+
+def _gpu_outputs(X, cache, layer):
+    """{(step, loop): (out [B][H][D] on the host, q, k_cur, v_cur)} in the benchmark's call order."""
+    B, H, D, T = W.batch, W.heads, W.D, W.T
+    ws = rq.alloc_workspace(cache.desc)
+    res = {}
+    for k in CHECK_STEPS:
+        past = torch.full((B,), T + k, dtype=torch.int32, device="cuda")
+        for r in range(W.L):
+            q = synth.query(W, layer, r, k, device="cuda")
+            kc = X[0, r, :, :, T + k].contiguous()
+            vc = X[1, r, :, :, T + k].contiguous()
+            out = torch.empty(B, H, D, device="cuda")
+            rq.decode_attn(cache, r, q, kc, vc, past, 1.0 / math.sqrt(D), out, ws)
+            res[(k, r)] = (out, q, kc, vc)
+    torch.cuda.synchronize()
+    return res
+
+
+def _check(layer, policy, bits, units, label):
+    X, rk, rv, cache = _build(layer, policy, bits)
+    outs = _gpu_outputs(X, cache, layer)
+    Tc = W.T + STEPS - 1
+    host = host_copy(cache)
+    worst = 0.0
+    for i in range(0, len(units), 16):
+        chunk = units[i:i + 16]
+        log(f"{label}: oracle for units {i}..{i + len(chunk) - 1} of {len(units)}")
+        series = oracle_layer(X, rk, rv, bits, policy, Tc, units=chunk)
+        assert_cache_parity(compare_cache(cache, series, Tc, host=host), f"{label} units {i}+")
+        for (k, r), (out, q, kc, vc) in outs.items():
+            lens = [W.T + k] * W.batch
+            ref = oracle_attention(series, chunk, r, lens, rk, rv, q, kc, vc, 1.0 / math.sqrt(W.D))
+            err = max_rel_err(out, ref)
+            worst = max(worst, err)
+            assert err <= TOL_ATTN, (label, k, r, err)
+        del series
+    log(f"{label}: attention max rel err {worst:.3e} over steps {CHECK_STEPS}, all loops")
+
+
+def test_ouro_16k_layer0_every_series():
+    _check(0, LAST, W.bits, [(b, h) for b in range(W.batch) for h in range(W.heads)], "16k layer 0")
+
+
+def test_ouro_16k_last_layer_sampled():
+    _check(W.layers - 1, LAST, W.bits, _sample_units(8, 23), f"16k layer {W.layers - 1}")
+
+
+def test_ouro_16k_chained_sampled():
+    _check(0, PREV, W.chained_bits, _sample_units(8, 7), "16k chained layer 0")
+
+
+def test_ouro_16k_bf16_sampled():
+    B, H, D, T = W.batch, W.heads, W.D, W.T
+    layer = 0
+    X = synth.kv(W, layer, 0, T + STEPS, device="cuda")
+    d = rq.make_desc(B, H, D, list(W.bits), T + STEPS)
+    ws = rq.alloc_workspace(d)
+    units = _sample_units(8, 11)
+    worst = 0.0
+    for k in CHECK_STEPS:
+        past = torch.full((B,), T + k, dtype=torch.int32, device="cuda")
+        for r in range(W.L):
+            q = synth.query(W, layer, r, k, device="cuda")
+            kc = X[0, r, :, :, T + k].contiguous()
+            vc = X[1, r, :, :, T + k].contiguous()
+            out = torch.empty(B, H, D, device="cuda")
+            log(f"16k bf16 step {k} loop {r}")
+            rq.decode_attn_bf16(d, X[0, r], X[1, r], q, kc, vc, past, 1.0 / math.sqrt(D), out, ws)
+            torch.cuda.synchronize()
+            qn, kn, vn = u16(q), u16(kc), u16(vc)
+            ref = {}
+            for b, h in units:
+                Kh = u16(X[0, r, b, h, :T + k])
+                Vh = u16(X[1, r, b, h, :T + k])
+                ref[(b, h)] = O.attend_bf16(Kh, Vh, qn[b, h], kn[b, h], vn[b, h], 1.0 / math.sqrt(D))
+            err = max_rel_err(out, ref)
+            worst = max(worst, err)
+            assert err <= TOL_ATTN
+    log(f"16k bf16: max rel err {worst:.3e}")
