@@ -175,6 +175,8 @@ def main():
     ap.add_argument("--no-chained", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--call-reps", type=int, default=50)
+    ap.add_argument("--schedule", choices=("overlap", "serial"), default="overlap",
+                    help="overlap: combines and appends on a second stream under the streaming launches")
     ap.add_argument("--cpu-sample-units", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum timed CPU-oracle seconds")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -249,24 +251,76 @@ def main():
         f"{time.time() - t_build:.1f}s")
 
     # ---------------------------------------------------------------- steps as graphs
-    def rq_step(k, cs, workspace):
+    # One step: for each loop r and layer l, the streaming launch (partial) on the
+    # main stream and its combine on a second stream -- plus, after the final
+    # loop, the layer's append of the current token -- so the short,
+    # latency-bound launches run under the next streaming launch. Two
+    # workspaces alternate; a workspace is reused only after its combine ran.
+    # --schedule serial issues the one-call entry points on one stream instead.
+    aux = torch.cuda.Stream()
+    ws_pair = [ws, rq.alloc_workspace(d_rq)]
+    ws_ch_pair = [ws_ch, rq.alloc_workspace(d_ch)]
+
+    def step_overlap(k, partial, combine, append):
+        main = torch.cuda.current_stream()
+        aux.wait_stream(main)
+        done = [None, None]
+        n = 0
         for r in range(L):
             for l in range(w.layers):
-                kc = kvcur[k, l, 0, r, :, :, 0]
-                vc = kvcur[k, l, 1, r, :, :, 0]
-                rq.decode_attn(cs[l], r, qs[k, l, r], kc, vc, past_len, scale, out[l, r], workspace)
-                if r == L - 1:
-                    rq.quantize_append(cs[l], kvcur[k, l], past_len, 1)
+                j = n & 1
+                if done[j] is not None:
+                    main.wait_event(done[j])
+                partial(k, l, r, j, main)
+                ev = torch.cuda.Event()
+                ev.record(main)
+                aux.wait_event(ev)
+                combine(k, l, r, j, aux)
+                if r == L - 1 and append is not None:
+                    append(k, l, aux)
+                done[j] = torch.cuda.Event()
+                done[j].record(aux)
+                n += 1
+        main.wait_stream(aux)
         past_len.add_(1)
 
+    def rq_step(k, cs, d, wsp):
+        if args.schedule == "serial":
+            for r in range(L):
+                for l in range(w.layers):
+                    kc = kvcur[k, l, 0, r, :, :, 0]
+                    vc = kvcur[k, l, 1, r, :, :, 0]
+                    rq.decode_attn(cs[l], r, qs[k, l, r], kc, vc, past_len, scale, out[l, r], wsp[0])
+                    if r == L - 1:
+                        rq.quantize_append(cs[l], kvcur[k, l], past_len, 1)
+            past_len.add_(1)
+            return
+        step_overlap(
+            k,
+            lambda k, l, r, j, st: rq.decode_attn_partial(cs[l], r, qs[k, l, r], past_len, scale, wsp[j], stream=st),
+            lambda k, l, r, j, st: rq.decode_combine(d, cs[l].rot[1], qs[k, l, r], kvcur[k, l, 0, r, :, :, 0],
+                                                     kvcur[k, l, 1, r, :, :, 0], past_len, scale, out[l, r],
+                                                     wsp[j], stream=st),
+            lambda k, l, st: rq.quantize_append(cs[l], kvcur[k, l], past_len, 1, stream=st))
+
     def bf16_step(k):
-        for r in range(L):
-            for l in range(w.layers):
-                kc = kvcur[k, l, 0, r, :, :, 0]
-                vc = kvcur[k, l, 1, r, :, :, 0]
-                rq.decode_attn_bf16(d_rq, bf16[l][0, r], bf16[l][1, r], qs[k, l, r], kc, vc, past_len, scale,
-                                    out[l, r], ws)
-        past_len.add_(1)
+        if args.schedule == "serial":
+            for r in range(L):
+                for l in range(w.layers):
+                    kc = kvcur[k, l, 0, r, :, :, 0]
+                    vc = kvcur[k, l, 1, r, :, :, 0]
+                    rq.decode_attn_bf16(d_rq, bf16[l][0, r], bf16[l][1, r], qs[k, l, r], kc, vc, past_len, scale,
+                                        out[l, r], ws)
+            past_len.add_(1)
+            return
+        step_overlap(
+            k,
+            lambda k, l, r, j, st: rq.decode_attn_bf16_partial(d_rq, bf16[l][0, r], bf16[l][1, r], qs[k, l, r],
+                                                               past_len, scale, ws_pair[j], stream=st),
+            lambda k, l, r, j, st: rq.decode_combine(d_rq, None, qs[k, l, r], kvcur[k, l, 0, r, :, :, 0],
+                                                     kvcur[k, l, 1, r, :, :, 0], past_len, scale, out[l, r],
+                                                     ws_pair[j], stream=st),
+            None)
 
     side = torch.cuda.Stream()
 
@@ -297,7 +351,7 @@ def main():
         return dt
 
     log("capturing RQ steps")
-    g_rq = capture(lambda k: rq_step(k, caches, ws))
+    g_rq = capture(lambda k: rq_step(k, caches, d_rq, ws_pair))
     dt_rq = run(g_rq, args.warmup)
     log(f"RQ: {K} steps in {dt_rq * 1e3:.2f} ms")
     del g_rq
@@ -311,7 +365,7 @@ def main():
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "layers": w.layers, "batch": B, "heads": H, "head_dim": D, "loops": L,
                    "context": T, "bits": bits, "group": w.group, "codes": "int2/int4 + fp16 scale/offset + fp16 alpha",
-                   "arith": "fp16 dot2 products, fp32 accumulation"},
+                   "arith": "fp16 dot2 products, fp32 accumulation", "schedule": args.schedule},
         "hbm_gbps_step": step_bytes / (dt_rq / K) / 1e9,
         "hbm_frac_step": step_bytes / (dt_rq / K) / 1e9 / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": step_bytes,
@@ -319,7 +373,7 @@ def main():
 
     if not args.no_chained:
         log("capturing chained steps")
-        g_ch = capture(lambda k: rq_step(k, chained, ws_ch))
+        g_ch = capture(lambda k: rq_step(k, chained, d_ch, ws_ch_pair))
         dt_ch = run(g_ch, args.warmup)
         del g_ch
         ch_bytes = sum(call_bytes(D, cbits, "prev", r) for r in range(L)) * H * w.layers * B * mean_ctx
@@ -343,33 +397,40 @@ def main():
     # ---------------------------------------------------------------- dominant kernel, HIP events
     # The streaming kernel (rq_decode_attn_partial's single launch) of loops 1-2
     # (INT4 anchor + INT2 residual) is the largest share of the step. It is timed
-    # alone, back to back on the stream it is launched on; the combine launch and
-    # whole calls are timed the same way for context.
+    # alone: `reps` launches (cycling over the layers' caches) captured in a graph,
+    # as the steps are, and replayed between two HIP events on the stream the
+    # graph is launched on. The combine launch and whole calls are timed the same way.
     reps = args.call_reps
     stream = torch.cuda.current_stream()
 
     def events(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for i in range(reps):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        times = []
         for _ in range(3):
-            fn(0)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(reps):
-            fn(i)
-        e1.record(stream)
-        e1.synchronize()
-        return e0.elapsed_time(e1) / reps
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) / reps)
+        del g
+        return sorted(times)[1]          # median of three replays
 
     percall = {}
     for r in range(L):
         kc = kvcur[0, 0, 0, r, :, :, 0]
         vc = kvcur[0, 0, 1, r, :, :, 0]
         nbytes = call_bytes(D, bits, "last", r) * B * H * T
-        ms_k = events(lambda i: rq.decode_attn_partial(caches[i % w.layers], r, qs[0, 0, r], past_len, scale, ws,
-                                                       stream=stream))
+        ms_k = events(lambda i: rq.decode_attn_partial(caches[i % w.layers], r, qs[0, 0, r], past_len, scale, ws))
         ms_c = events(lambda i: rq.decode_combine(d_rq, caches[i % w.layers].rot[1], qs[0, 0, r], kc, vc, past_len,
-                                                  scale, out[0, r], ws, stream=stream))
+                                                  scale, out[0, r], ws))
         ms_call = events(lambda i: rq.decode_attn(caches[i % w.layers], r, qs[0, 0, r], kc, vc, past_len, scale,
-                                                  out[0, r], ws, stream=stream))
+                                                  out[0, r], ws))
         percall[r] = {"kernel_ms": ms_k, "combine_ms": ms_c, "call_ms": ms_call, "bytes": nbytes,
                       "kernel_gbps": nbytes / (ms_k * 1e-3) / 1e9}
     dom = percall[0]

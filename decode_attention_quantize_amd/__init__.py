@@ -67,6 +67,8 @@ def _load():
     L.rq_decode_attn_partial.argtypes = [P, P, I, P, P, ctypes.c_float, P, Z, P]
     L.rq_decode_combine.restype = ctypes.c_int
     L.rq_decode_combine.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, P, Z, P, P]
+    L.rq_decode_attn_bf16_partial.restype = ctypes.c_int
+    L.rq_decode_attn_bf16_partial.argtypes = [P, P, P, P, P, ctypes.c_float, P, Z, P]
     L.rq_decode_attn_bf16.restype = ctypes.c_int
     L.rq_decode_attn_bf16.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, P, P, Z, P, P]
     L.rq_status_str.restype = ctypes.c_char_p
@@ -111,10 +113,18 @@ def workspace_bytes(d: Desc) -> int:
 
 
 def split_plan(d: Desc) -> tuple[int, int]:
-    """(chunk, nsplit): slots of `chunk` cached tokens per (b, h)."""
-    chunk, nsplit = ctypes.c_int32(), ctypes.c_int32()
-    _check(lib.rq_split_plan(ctypes.byref(d), ctypes.byref(chunk), ctypes.byref(nsplit)), "rq_split_plan")
-    return chunk.value, nsplit.value
+    """(unit, nsplit): nsplit slots per (b, h); slot length for a sequence of
+    `n` cached tokens is slot_len(n, nsplit, unit)."""
+    unit, nsplit = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib.rq_split_plan(ctypes.byref(d), ctypes.byref(unit), ctypes.byref(nsplit)), "rq_split_plan")
+    return unit.value, nsplit.value
+
+
+def slot_len(n: int, nsplit: int, unit: int) -> int:
+    """Tokens per slot for a sequence of n cached tokens (the rule stated in rq.h)."""
+    c = -(-n // nsplit)
+    c = -(-c // unit) * unit
+    return max(c, unit)
 
 
 def _ptr(t) -> int | None:
@@ -216,6 +226,13 @@ def decode_attn_bf16(d: Desc, k_cache, v_cache, q, k_cur, v_cur, past_len, scale
                                    _ptr(v_cur), _ptr(past_len), scale, _ptr(out), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _ptr(dev_err),
                                    _stream(stream)), "rq_decode_attn_bf16")
+
+
+def decode_attn_bf16_partial(d: Desc, k_cache, v_cache, q, past_len, scale: float, workspace, stream=None):
+    """First launch of decode_attn_bf16: per-slot partials into the workspace (original domain)."""
+    _check(lib.rq_decode_attn_bf16_partial(ctypes.byref(d), _ptr(k_cache), _ptr(v_cache), _ptr(q), _ptr(past_len),
+                                           scale, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                           _stream(stream)), "rq_decode_attn_bf16_partial")
 
 
 def alloc_workspace(d: Desc, device="cuda") -> torch.Tensor:

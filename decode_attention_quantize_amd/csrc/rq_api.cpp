@@ -21,23 +21,23 @@ static int device_cus() {
 }
 
 #ifndef RQ_WGS_PER_CU
-#define RQ_WGS_PER_CU 2
+#define RQ_WGS_PER_CU 3
 #endif
 
 SplitPlan split_plan(const rq_desc* d) {
-  // About RQ_WGS_PER_CU workgroups per compute unit over the whole call, each a
-  // contiguous run of whole wave tiles of one (b, h), so the per-workgroup query
-  // rotation and partial merge are amortized over many tokens.
-  const long long unit = (long long)kWaves * tile_tokens(d->head_dim);
+  // About RQ_WGS_PER_CU workgroups per compute unit over the whole call, at
+  // most one slot per tile of capacity; slot lengths are set per sequence on
+  // the device (slot_len).
+  const long long unit = tile_tokens(d->head_dim);
   const long long bh = (long long)d->batch * d->heads;
   const long long target = (long long)RQ_WGS_PER_CU * device_cus();
   long long nsplit = (target + bh - 1) / bh;
+  const long long cap = (d->max_tokens + unit - 1) / unit;
+  if (nsplit > cap) nsplit = cap;
   if (nsplit < 1) nsplit = 1;
-  long long chunk = (d->max_tokens + nsplit - 1) / nsplit;
-  chunk = ((chunk + unit - 1) / unit) * unit;
   SplitPlan p;
-  p.chunk = (int)chunk;
-  p.nsplit = (int)((d->max_tokens + chunk - 1) / chunk);
+  p.unit = (int)unit;
+  p.nsplit = (int)nsplit;
   return p;
 }
 
@@ -96,7 +96,7 @@ CombineParams combine_params(const rq_desc* d, void* ws, const uint16_t* q, cons
   a.scale_log2 = scale_log2;
   a.H = d->heads;
   a.T_max = d->max_tokens;
-  a.chunk = sp.chunk;
+  a.unit = sp.unit;
   a.nsplit = sp.nsplit;
   return a;
 }
@@ -193,12 +193,12 @@ rq_status rq_quantize_append(const rq_desc* d, const rq_layer_cache* c, const ui
   return launch_append(p, d->head_dim, stream) == 0 ? RQ_OK : RQ_E_HIP;
 }
 
-rq_status rq_split_plan(const rq_desc* d, int32_t* chunk, int32_t* nsplit) {
+rq_status rq_split_plan(const rq_desc* d, int32_t* unit, int32_t* nsplit) {
   const rq_status s = check_shape(d);
   if (s != RQ_OK) return s;
-  if (!chunk || !nsplit) return RQ_E_NULL;
+  if (!unit || !nsplit) return RQ_E_NULL;
   const SplitPlan sp = split_plan(d);
-  *chunk = sp.chunk;
+  *unit = sp.unit;
   *nsplit = sp.nsplit;
   return RQ_OK;
 }
@@ -248,7 +248,7 @@ rq_status rq_decode_attn_partial(const rq_desc* d, const rq_layer_cache* c, int3
   p.B = d->batch;
   p.H = d->heads;
   p.T_max = d->max_tokens;
-  p.chunk = sp.chunk;
+  p.unit = sp.unit;
   p.nsplit = sp.nsplit;
   return launch_decode(p, d->head_dim, nc, bits, sp.nsplit, stream) == 0 ? RQ_OK : RQ_E_HIP;
 }
@@ -289,6 +289,31 @@ rq_status rq_decode_attn(const rq_desc* d, const rq_layer_cache* c, int32_t loop
                            stream);
 }
 
+rq_status rq_decode_attn_bf16_partial(const rq_desc* d, const uint16_t* k_cache, const uint16_t* v_cache,
+                                      const uint16_t* q, const int32_t* past_len, float softmax_scale, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  rq_status s = check_shape(d);
+  if (s != RQ_OK) return s;
+  if (!k_cache || !v_cache || !q || !past_len) return RQ_E_NULL;
+  if (!al(k_cache, 16) || !al(v_cache, 16) || !al(q, 16) || !al(past_len, 4)) return RQ_E_ALIGN;
+  if (!ws || ws_bytes < workspace_for(d) || ((uintptr_t)ws & 255) != 0) return RQ_E_WORKSPACE;
+  if (!std::isfinite(softmax_scale)) return RQ_E_SHAPE;
+  const SplitPlan sp = split_plan(d);
+  Bf16Params p;
+  p.k = k_cache;
+  p.v = v_cache;
+  p.q = q;
+  p.past_len = past_len;
+  p.part = static_cast<float*>(ws);
+  p.scale_log2 = softmax_scale * kLog2e;
+  p.B = d->batch;
+  p.H = d->heads;
+  p.T_max = d->max_tokens;
+  p.unit = sp.unit;
+  p.nsplit = sp.nsplit;
+  return launch_bf16(p, d->head_dim, sp.nsplit, stream) == 0 ? RQ_OK : RQ_E_HIP;
+}
+
 rq_status rq_decode_attn_bf16(const rq_desc* d, const uint16_t* k_cache, const uint16_t* v_cache,
                               const uint16_t* q, const uint16_t* k_cur, const uint16_t* v_cur,
                               const int32_t* past_len, float softmax_scale, float* out, void* ws,
@@ -301,23 +326,9 @@ rq_status rq_decode_attn_bf16(const rq_desc* d, const uint16_t* k_cache, const u
     return RQ_E_ALIGN;
   if (!ws || ws_bytes < workspace_for(d) || ((uintptr_t)ws & 255) != 0) return RQ_E_WORKSPACE;
   if (!std::isfinite(softmax_scale)) return RQ_E_SHAPE;
-  const SplitPlan sp = split_plan(d);
-  const float scale_log2 = softmax_scale * kLog2e;
-  Bf16Params p;
-  p.k = k_cache;
-  p.v = v_cache;
-  p.q = q;
-  p.past_len = past_len;
-  p.part = static_cast<float*>(ws);
-  p.scale_log2 = scale_log2;
-  p.B = d->batch;
-  p.H = d->heads;
-  p.T_max = d->max_tokens;
-  p.chunk = sp.chunk;
-  p.nsplit = sp.nsplit;
-  if (launch_bf16(p, d->head_dim, sp.nsplit, stream) != 0) return RQ_E_HIP;
-  const CombineParams cp = combine_params(d, ws, q, k_cur, v_cur, past_len, nullptr, out, dev_err, scale_log2);
-  return launch_combine(cp, d->head_dim, d->batch, stream) == 0 ? RQ_OK : RQ_E_HIP;
+  s = rq_decode_attn_bf16_partial(d, k_cache, v_cache, q, past_len, softmax_scale, ws, ws_bytes, stream);
+  if (s != RQ_OK) return s;
+  return rq_decode_combine(d, nullptr, q, k_cur, v_cur, past_len, softmax_scale, out, ws, ws_bytes, dev_err, stream);
 }
 
 }  // extern "C"

@@ -45,6 +45,11 @@ struct Words {
   uint32_t w[BITS];  // one group of 32 codes = BITS 32-bit words
 };
 
+// Cache policy of the streaming loads: non-temporal (the nt bit). Every cache
+// byte is read once per call, so keeping it out of the caches' reuse state
+// leaves L2 and MALL to the rotations and partials; measured ~10% faster.
+constexpr int kAux = 2;
+
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -58,10 +63,10 @@ template <int BITS>
 __device__ __forceinline__ Words<BITS> load_group(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   Words<BITS> w;
   if constexpr (BITS == 4) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAux);
     w.w[0] = v.x; w.w[1] = v.y; w.w[2] = v.z; w.w[3] = v.w;
   } else {
-    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kAux);
     w.w[0] = v.x; w.w[1] = v.y;
   }
   return w;
@@ -209,15 +214,15 @@ __device__ __forceinline__ void load_comp(CompTile<BITS>& T, const CompRsrc& r, 
   T.k1 = load_group<BITS>(r.kc, oc + TPW * RB);
   T.v0 = load_group<BITS>(r.vc, oc);
   T.v1 = load_group<BITS>(r.vc, oc + TPW * RB);
-  T.km0 = __builtin_amdgcn_raw_buffer_load_b32(r.km, o.m, 0, 0);
-  T.km1 = __builtin_amdgcn_raw_buffer_load_b32(r.km, o.m + TPW * G * 4, 0, 0);
-  T.vm0 = __builtin_amdgcn_raw_buffer_load_b32(r.vm, o.m, 0, 0);
-  T.vm1 = __builtin_amdgcn_raw_buffer_load_b32(r.vm, o.m + TPW * G * 4, 0, 0);
+  T.km0 = __builtin_amdgcn_raw_buffer_load_b32(r.km, o.m, 0, kAux);
+  T.km1 = __builtin_amdgcn_raw_buffer_load_b32(r.km, o.m + TPW * G * 4, 0, kAux);
+  T.vm0 = __builtin_amdgcn_raw_buffer_load_b32(r.vm, o.m, 0, kAux);
+  T.vm1 = __builtin_amdgcn_raw_buffer_load_b32(r.vm, o.m + TPW * G * 4, 0, kAux);
   if (has_alpha) {
-    T.ka0 = __builtin_amdgcn_raw_buffer_load_b16(r.ka, o.a, 0, 0);
-    T.ka1 = __builtin_amdgcn_raw_buffer_load_b16(r.ka, o.a + TPW * 2, 0, 0);
-    T.va0 = __builtin_amdgcn_raw_buffer_load_b16(r.va, o.a, 0, 0);
-    T.va1 = __builtin_amdgcn_raw_buffer_load_b16(r.va, o.a + TPW * 2, 0, 0);
+    T.ka0 = __builtin_amdgcn_raw_buffer_load_b16(r.ka, o.a, 0, kAux);
+    T.ka1 = __builtin_amdgcn_raw_buffer_load_b16(r.ka, o.a + TPW * 2, 0, kAux);
+    T.va0 = __builtin_amdgcn_raw_buffer_load_b16(r.va, o.a, 0, kAux);
+    T.va1 = __builtin_amdgcn_raw_buffer_load_b16(r.va, o.a + TPW * 2, 0, kAux);
   } else {
     T.ka0 = T.ka1 = T.va0 = T.va1 = 0x3c00;  // 1.0, unused
   }
@@ -254,19 +259,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
   constexpr int G = D / 32;
   constexpr int TPW = 64 / G;
   constexpr int TILE = 2 * TPW;
+  static_assert(TILE == tile_tokens(D), "slot unit must be the wave tile");
   constexpr int REF = ref_bits<CB, NC>();
   __shared__ float red[kWaves][64][33];
   __shared__ float qr[D];
   __shared__ PartialLds S;
 
-  const int split = blockIdx.x, bh = blockIdx.y;
-  const int b = bh / p.H, h = bh % p.H;
+  int split, b, h;
+  split_item(p.nsplit, p.B, p.H, split, b, h);
+  const int bh = b * p.H + h;
   int len = p.past_len[b];
   len = len < 0 ? 0 : (len > p.T_max ? p.T_max : len);
-  const int nvalid = len > 0 ? (len + p.chunk - 1) / p.chunk : 1;
-  if (split >= nvalid) return;  // whole block, before any barrier
-  const int start = split * p.chunk;
-  const int end = min(start + p.chunk, len);
+  if (split >= slots_used(len, p.nsplit, p.unit)) return;  // whole block, before any barrier
+  const int chunk = slot_len(len, p.nsplit, p.unit);
+  const int start = split * chunk;
+  const int end = min(start + chunk, len);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 
@@ -496,7 +503,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
 
   if ((raw_len < 0 || raw_len > p.T_max) && h == 0 && tid == 0 && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_LENGTH);
   const int len = raw_len < 0 ? 0 : (raw_len > p.T_max ? p.T_max : raw_len);
-  const int nvalid = len > 0 ? (len + p.chunk - 1) / p.chunk : 1;
+  const int nvalid = slots_used(len, p.nsplit, p.unit);
 
   // Online merge of the splits' (m, l, acc) relative to their running max M.
   const float* part = p.part + (size_t)bh * p.nsplit * PF;
@@ -593,7 +600,7 @@ bool have_decode_kernel(int D, int nc, const int* bits) { return find(D, nc, bit
 int launch_decode(const DecodeParams& p, int D, int nc, const int* bits, int nsplit, void* stream) {
   const Entry* e = find(D, nc, bits);
   if (!e) return -1;
-  const dim3 grid((unsigned)nsplit, (unsigned)(p.B * p.H));
+  const dim3 grid((unsigned)(nsplit * p.B * p.H));
   hipLaunchKernelGGL(e->fn, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), p);
   return (int)hipGetLastError();
 }

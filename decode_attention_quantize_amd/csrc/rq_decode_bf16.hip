@@ -16,6 +16,15 @@
 namespace rq {
 namespace {
 
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load of cache rows, non-temporal: each row is read once
+// per call (as in the compressed kernel).
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) {
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void bf16_fused(Bf16Params p) {
   constexpr int CPT = D / 8;
@@ -25,14 +34,15 @@ __global__ __launch_bounds__(kThreads) void bf16_fused(Bf16Params p) {
   __shared__ float red[kWaves][64][9];
   __shared__ PartialLds S;
 
-  const int split = blockIdx.x, bh = blockIdx.y;
-  const int b = bh / p.H;
+  int split, b, h;
+  split_item(p.nsplit, p.B, p.H, split, b, h);
+  const int bh = b * p.H + h;
   int len = p.past_len[b];
   len = len < 0 ? 0 : (len > p.T_max ? p.T_max : len);
-  const int nvalid = len > 0 ? (len + p.chunk - 1) / p.chunk : 1;
-  if (split >= nvalid) return;
-  const int start = split * p.chunk;
-  const int end = min(start + p.chunk, len);
+  if (split >= slots_used(len, p.nsplit, p.unit)) return;  // whole block, before any barrier
+  const int chunk = slot_len(len, p.nsplit, p.unit);
+  const int start = split * chunk;
+  const int end = min(start + chunk, len);
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ts = lane / CPT, ch = lane % CPT;
@@ -60,8 +70,8 @@ __global__ __launch_bounds__(kThreads) void bf16_fused(Bf16Params p) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const size_t row = rowbase + min(base + u * TPW + ts, last);  // clamped rows are masked
-      kr[u] = *reinterpret_cast<const uint4*>(p.k + row * D + 8 * chs);
-      vr[u] = *reinterpret_cast<const uint4*>(p.v + row * D + 8 * chs);
+      kr[u] = ld16(p.k + row * D + 8 * chs);
+      vr[u] = ld16(p.v + row * D + 8 * chs);
     }
   };
 
@@ -122,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void bf16_fused(Bf16Params p) {
 }  // namespace
 
 int launch_bf16(const Bf16Params& p, int D, int nsplit, void* stream) {
-  const dim3 grid((unsigned)nsplit, (unsigned)(p.B * p.H));
+  const dim3 grid((unsigned)(nsplit * p.B * p.H));
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (D) {
     case 64: hipLaunchKernelGGL(bf16_fused<64>, grid, dim3(kThreads), 0, s, p); break;

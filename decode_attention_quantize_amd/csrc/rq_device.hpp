@@ -46,6 +46,21 @@ __device__ __forceinline__ float group_sum(float x) {
   }
 }
 
+// Work item of this workgroup in a 1-D grid of nsplit * B * H workgroups.
+// Consecutive workgroup ids are dispatched round-robin over the 8 XCDs, each
+// with its own L2; the ids are remapped so that every XCD receives one
+// contiguous, head-major range of items (h, b, split), and a head's rotation
+// is fetched into few L2s.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void split_item(int nsplit, int B, int H, int& split, int& b, int& h) {
+  const int i = (int)blockIdx.x, total = nsplit * B * H;
+  const int k = (total % kXcds == 0) ? (i % kXcds) * (total / kXcds) + i / kXcds : i;
+  split = k % nsplit;
+  const int rest = k / nsplit;
+  b = rest % B;
+  h = rest / B;
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));

@@ -21,13 +21,31 @@ constexpr int groups_of(int D) { return D / 32; }
 constexpr int pairs_per_wave(int D) { return 64 / groups_of(D); }
 constexpr int tile_tokens(int D) { return 2 * pairs_per_wave(D); }
 
-// Split of the token axis: every (b, h) has nsplit chunks of `chunk` tokens,
-// sized so that the whole call is about two workgroups per compute unit.
+
+// Split of the token axis: every (b, h) has nsplit slots. The slot length is
+// set on the device from the sequence's own length, so the slots of a ragged
+// batch stay balanced: slot_len = unit * ceil(ceil(len / nsplit) / unit), at
+// least one unit, where unit is the compressed kernel's wave tile (the BF16
+// baseline uses the same slots). nsplit is sized on the host so that the call has about RQ_WGS_PER_CU
+// workgroups per compute unit.
 struct SplitPlan {
-  int chunk;
+  int unit;
   int nsplit;
 };
 SplitPlan split_plan(const rq_desc* d);
+
+__host__ __device__ inline int slot_len(int len, int nsplit, int unit) {
+  int c = (len + nsplit - 1) / nsplit;
+  c = (c + unit - 1) / unit * unit;
+  return c < unit ? unit : c;
+}
+
+// Slots holding any of the len tokens (slot 0 always counts).
+__host__ __device__ inline int slots_used(int len, int nsplit, int unit) {
+  if (len <= 0) return 1;
+  const int c = slot_len(len, nsplit, unit);
+  return (len + c - 1) / c;
+}
 
 constexpr size_t part_floats(int D) { return (size_t)D + 4; }
 
@@ -44,7 +62,7 @@ struct CombineParams {
   float* out;               // fp32 [B][H][D]
   int32_t* dev_err;
   float scale_log2;         // softmax scale * log2(e)
-  int H, T_max, chunk, nsplit;
+  int H, T_max, unit, nsplit;
 };
 
 struct DecodeParams {
@@ -59,7 +77,7 @@ struct DecodeParams {
   const int32_t* past_len;
   float* part;
   float scale_log2;
-  int B, H, T_max, chunk, nsplit;
+  int B, H, T_max, unit, nsplit;
 };
 
 struct Bf16Params {
@@ -69,7 +87,7 @@ struct Bf16Params {
   const int32_t* past_len;
   float* part;
   float scale_log2;
-  int B, H, T_max, chunk, nsplit;
+  int B, H, T_max, unit, nsplit;
 };
 
 struct AppendParams {

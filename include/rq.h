@@ -159,10 +159,13 @@ rq_status rq_decode_attn(const rq_desc* desc, const rq_layer_cache* cache, int32
                          void* workspace, size_t workspace_bytes, int32_t* dev_err, void* stream);
 
 /* Split of the token axis used by the decode calls (§4.1 "split-K"): every
- * (b, h) has *nsplit slots of *chunk consecutive cached tokens; slot i covers
- * tokens [i*chunk, (i+1)*chunk). Depends on the current device's compute-unit
- * count. */
-rq_status rq_split_plan(const rq_desc* desc, int32_t* chunk, int32_t* nsplit);
+ * (b, h) has *nsplit slots (chosen from the current device's compute-unit
+ * count). Slot i of sequence b covers cached tokens [i*c_b, (i+1)*c_b) with
+ * c_b = u * ceil(ceil(past_len[b] / nsplit) / u), at least u, where
+ * u = *unit is the kernel's tile; so the slots of every sequence are equally
+ * long whatever its length, and slots starting at or past past_len[b] are
+ * unused (slot 0 always counts). */
+rq_status rq_split_plan(const rq_desc* desc, int32_t* unit, int32_t* nsplit);
 
 /* The two launches of rq_decode_attn as separate calls, for callers that merge
  * partial results themselves (for instance over a token axis split across
@@ -194,7 +197,13 @@ rq_status rq_decode_combine(const rq_desc* desc, const float* rot_v, const uint1
 
 /* BF16 decode baseline (the paper's comparison point, §5.3): the same attention
  * over an uncompressed cache. k_cache, v_cache: bf16 [B][H][T_max][D]. Only
- * batch, heads, head_dim and max_tokens of desc are used. */
+ * batch, heads, head_dim and max_tokens of desc are used.
+ * rq_decode_attn_bf16 is rq_decode_attn_bf16_partial followed by
+ * rq_decode_combine(desc, NULL, ...); the partial writes the same slots and
+ * layout as rq_decode_attn_partial, in the original (unrotated) domain. */
+rq_status rq_decode_attn_bf16_partial(const rq_desc* desc, const uint16_t* k_cache, const uint16_t* v_cache,
+                                      const uint16_t* q, const int32_t* past_len, float softmax_scale,
+                                      void* workspace, size_t workspace_bytes, void* stream);
 rq_status rq_decode_attn_bf16(const rq_desc* desc, const uint16_t* k_cache, const uint16_t* v_cache,
                               const uint16_t* q, const uint16_t* k_cur, const uint16_t* v_cur,
                               const int32_t* past_len, float softmax_scale, float* out,

@@ -135,8 +135,11 @@ def test_split_api_validation():
     c = _cache(d)
     by = ctypes.byref
     ws = rq.workspace_bytes(d)
-    chunk, nsplit = rq.split_plan(d)
-    assert chunk > 0 and nsplit >= 1 and chunk * nsplit >= d.max_tokens
+    unit, nsplit = rq.split_plan(d)
+    assert unit == 2 * 64 // (d.head_dim // 32) and 1 <= nsplit <= -(-d.max_tokens // unit)
+    for n in (0, 1, unit, d.max_tokens):
+        sl = rq.slot_len(n, nsplit, unit)
+        assert sl % unit == 0 and sl * nsplit >= n and (sl - unit) * nsplit < max(n, 1)
     assert ws == d.batch * d.heads * nsplit * (d.head_dim + 4) * 4
     assert L.rq_split_plan(by(d), None, None) == 1
     f = ctypes.c_float(0.1)
@@ -163,5 +166,9 @@ def test_bf16_validation():
                                  ws, None, 0) == 1
     assert L.rq_decode_attn_bf16(by(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE,
                                  ws - 1, None, 0) == 5
+    f = ctypes.c_float(0.1)
+    assert L.rq_decode_attn_bf16_partial(by(d), None, FAKE, FAKE, FAKE, f, FAKE, ws, 0) == 1
+    assert L.rq_decode_attn_bf16_partial(by(d), FAKE, FAKE, FAKE, FAKE, f, FAKE, ws - 1, 0) == 5
+    assert L.rq_decode_attn_bf16_partial(by(d), FAKE, ctypes.c_void_p(0x100004), FAKE, FAKE, f, FAKE, ws, 0) == 10
     assert L.rq_decode_attn_bf16(by(d), ctypes.c_void_p(0x100008), FAKE, FAKE, FAKE, FAKE, FAKE,
                                  ctypes.c_float(0.1), FAKE, FAKE, ws, None, 0) == 10

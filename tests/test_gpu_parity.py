@@ -124,7 +124,7 @@ def test_partial_and_combine():
     B, H, D = 2, 3, 128
     lens = [T, 0]
     past = torch.tensor(lens, dtype=torch.int32, device="cuda")
-    chunk, nsplit = rq.split_plan(d)
+    unit, nsplit = rq.split_plan(d)
     scale = 1.0 / math.sqrt(D)
     for r in (0, 3):
         q = synth.query(w, 0, r, 0, device="cuda", batch=B)
@@ -149,7 +149,7 @@ def test_partial_and_combine():
         l2e = 1.0 / math.log(2.0)
         worst = 0.0
         for b, h in units:
-            used = max(1, -(-lens[b] // chunk))
+            used = max(1, -(-lens[b] // rq.slot_len(lens[b], nsplit, unit)))
             P = part[b, h, :used].numpy()
             xq, xk, xv = O.bf16_decode(qn[b, h]), O.bf16_decode(kn[b, h]), O.bf16_decode(vn[b, h])
             xc = float(xq @ xk) * scale * l2e
