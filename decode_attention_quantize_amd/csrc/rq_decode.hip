@@ -15,13 +15,16 @@
 // and values accumulate sum_t p_t zhat_V,t in the rotated domain with the same
 // per-group split into a code part (weight p beta s) and an offset part.
 //
-// Code unpacking: a masked code field read as an fp16 bit pattern is the
-// subnormal number code * 2^(shift - 24), exactly, and v_dot2c_f32_f16 keeps
-// fp16 subnormals, so one AND yields two codes ready for the dot product.
-// The packed layout places group elements e and e+16 at the same bit offset of
-// the low and high halves of a word, which is what makes one mask yield a pair
-// for the keys; for the values a byte permute pairs the same element of two
-// tokens.
+// Keys: q' of a lane's group is held as 16-bit fixed point in two signed
+// 8-bit limbs; masking a code word with 0x0F0F0F0F (INT4) or 0x03030303 (INT2)
+// puts four codes in four bytes, and v_dot4c_i32_i8 against each limb gives an
+// exact integer sum of q'_e code_e.
+// Values: a masked code field read as an fp16 bit pattern is the subnormal
+// number code * 2^(shift - 24), exactly, and v_dot2c_f32_f16 keeps fp16
+// subnormals, so one AND yields two codes ready for the dot product. The
+// packed layout places group elements e and e+16 at the same bit offset of the
+// low and high halves of a word; a byte permute pairs the same element of two
+// tokens, and one mask then yields that element of both tokens.
 #include <hip/hip_runtime.h>
 
 #include "rq_combine.hpp"
@@ -72,45 +75,51 @@ __device__ __forceinline__ Words<BITS> load_group(__amdgpu_buffer_rsrc_t r, uint
   return w;
 }
 
-// sum_e q'_e code_e over one group (q' as hi [+ lo] fp16 pairs (e, e+16)).
-template <int BITS, bool HILO>
-__device__ __forceinline__ float kdot(const Words<BITS>& c, const uint32_t (&QH)[16], const uint32_t (&QL)[16]) {
+// q' of one group as 16-bit fixed point, v_e = round(q'_e 2^E) (|v| < 2^14),
+// split into signed 8-bit limbs v = 256 hi + lo (hi in [-64, 64], lo in
+// [-128, 127]) and packed four per register in the order the code bytes of a
+// word come out of one mask (see kdot). Integer dot products of the codes with
+// both limbs are exact.
+struct QFix {
+  uint32_t q4[4][2][2];  // INT4: word j, mask (even / odd nibbles), limb (hi / lo)
+  uint32_t q2[2][4][2];  // INT2: word j, field s, limb
+};
+
+// Elements of the group that byte b (0..3) of a masked word holds.
+//   INT4 word j, mask m (0: bits 0-3 of each byte, 1: bits 4-7):
+//     bytes 0..3 = elements 4j + m, 4j + 2 + m, 16 + 4j + m, 18 + 4j + m.
+//   INT2 word j, field s (bits 2s, 2s+1 of each byte):
+//     bytes 0..3 = elements 8j + s, 8j + 4 + s, 16 + 8j + s, 20 + 8j + s.
+__host__ __device__ constexpr int int4_elem(int j, int m, int b) { return (b >> 1) * 16 + 4 * j + 2 * (b & 1) + m; }
+__host__ __device__ constexpr int int2_elem(int j, int s, int b) { return (b >> 1) * 16 + 8 * j + 4 * (b & 1) + s; }
+
+// sum_e v_e code_e over one group (exact, int32).
+template <int BITS>
+__device__ __forceinline__ int kdot(const Words<BITS>& c, const QFix& Q) {
+  int ah = 0, al = 0;
   if constexpr (BITS == 4) {
-    float a1 = 0.0f, a16 = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t x = c.w[j], y = x >> 8;
-      const uint32_t m0 = x & 0x000F000Fu, m1 = x & 0x00F000F0u, m2 = y & 0x000F000Fu, m3 = y & 0x00F000F0u;
-      a1 = dot2(m0, QH[4 * j], a1);
-      a16 = dot2(m1, QH[4 * j + 1], a16);
-      a1 = dot2(m2, QH[4 * j + 2], a1);
-      a16 = dot2(m3, QH[4 * j + 3], a16);
-      if constexpr (HILO) {
-        a1 = dot2(m0, QL[4 * j], a1);
-        a16 = dot2(m1, QL[4 * j + 1], a16);
-        a1 = dot2(m2, QL[4 * j + 2], a1);
-        a16 = dot2(m3, QL[4 * j + 3], a16);
-      }
+      const uint32_t x = c.w[j];
+      const int m0 = (int)(x & 0x0F0F0F0Fu), m1 = (int)((x >> 4) & 0x0F0F0F0Fu);
+      ah = __builtin_amdgcn_sdot4(m0, (int)Q.q4[j][0][0], ah, false);
+      al = __builtin_amdgcn_sdot4(m0, (int)Q.q4[j][0][1], al, false);
+      ah = __builtin_amdgcn_sdot4(m1, (int)Q.q4[j][1][0], ah, false);
+      al = __builtin_amdgcn_sdot4(m1, (int)Q.q4[j][1][1], al, false);
     }
-    return fmaf(a16, 1.0f / 16.0f, a1);
   } else {
-    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const uint32_t x = c.w[j], y = x >> 8;
+      const uint32_t x = c.w[j];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t mx = x & (0x00030003u << (2 * q)), my = y & (0x00030003u << (2 * q));
-        a[q] = dot2(mx, QH[8 * j + q], a[q]);
-        a[q] = dot2(my, QH[8 * j + 4 + q], a[q]);
-        if constexpr (HILO) {
-          a[q] = dot2(mx, QL[8 * j + q], a[q]);
-          a[q] = dot2(my, QL[8 * j + 4 + q], a[q]);
-        }
+      for (int f = 0; f < 4; ++f) {
+        const int m = (int)((x >> (2 * f)) & 0x03030303u);
+        ah = __builtin_amdgcn_sdot4(m, (int)Q.q2[j][f][0], ah, false);
+        al = __builtin_amdgcn_sdot4(m, (int)Q.q2[j][f][1], al, false);
       }
     }
-    return (a[0] + a[1] * 0.25f) + (a[2] * (1.0f / 16.0f) + a[3] * (1.0f / 64.0f));
   }
+  return ah * 256 + al;
 }
 
 // Field scale 2^shift of element e of a group (index k = e mod 16 in its half)
@@ -253,7 +262,7 @@ constexpr int waves_for() {
   return (NC <= 2 && bits <= 6) ? RQ_WAVES_SMALL : 2;
 }
 
-template <int D, int NC, uint32_t CB, bool HILO, int DEPTH>
+template <int D, int NC, uint32_t CB, int DEPTH>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_for<NC, CB>()))) void decode_fused(
     DecodeParams p) {
   constexpr int G = D / 32;
@@ -339,15 +348,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
   fetch(A, base);
   if constexpr (DEPTH == 3) fetch(B, base + STRIDE);
 
-  uint32_t QH[16], QL[16];
-  float qsum = 0.0f;
+  // This lane's group of q' in fixed point (per-group exponent), and its sum.
+  QFix Q;
+  float qsum = 0.0f, qscale;
+  {
+    float qv[32], mx = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const float a = qr[32 * gsel + k], c = qr[32 * gsel + 16 + k];
-    const _Float16 ah = (_Float16)a, ch = (_Float16)c;
-    QH[k] = pack_h2((float)ah, (float)ch);
-    QL[k] = pack_h2(a - (float)ah, c - (float)ch);
-    qsum += a + c;
+    for (int e = 0; e < 32; ++e) {
+      qv[e] = qr[32 * gsel + e];
+      qsum += qv[e];
+      mx = fmaxf(mx, fabsf(qv[e]));
+    }
+    int ex = 0;
+    (void)frexpf(mx, &ex);                  // mx in [2^(ex-1), 2^ex)
+    const int E = mx > 0.0f ? 14 - ex : 0;  // |q' 2^E| < 2^14
+    qscale = ldexpf(1.0f, -E);
+    int hi[32], lo[32];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const int v = __float2int_rn(ldexpf(qv[e], E));
+      hi[e] = (v + 128) >> 8;
+      lo[e] = v - 256 * hi[e];
+    }
+    auto pack = [](int a, int b, int c, int d) {
+      return (uint32_t)(a & 255) | ((uint32_t)(b & 255) << 8) | ((uint32_t)(c & 255) << 16) | ((uint32_t)d << 24);
+    };
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        Q.q4[j][m][0] = pack(hi[int4_elem(j, m, 0)], hi[int4_elem(j, m, 1)], hi[int4_elem(j, m, 2)], hi[int4_elem(j, m, 3)]);
+        Q.q4[j][m][1] = pack(lo[int4_elem(j, m, 0)], lo[int4_elem(j, m, 1)], lo[int4_elem(j, m, 2)], lo[int4_elem(j, m, 3)]);
+      }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        Q.q2[j][f][0] = pack(hi[int2_elem(j, f, 0)], hi[int2_elem(j, f, 1)], hi[int2_elem(j, f, 2)], hi[int2_elem(j, f, 3)]);
+        Q.q2[j][f][1] = pack(lo[int2_elem(j, f, 0)], lo[int2_elem(j, f, 1)], lo[int2_elem(j, f, 2)], lo[int2_elem(j, f, 3)]);
+      }
   }
 
   float acc[32];
@@ -363,9 +402,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
     float kb0[NC], kb1[NC], vb0[NC], vb1[NC];  // beta weights, K and V
     auto kpart = [&](auto& C, int c, auto bits_tag) {
       constexpr int BB = decltype(bits_tag)::value;
-      const float d0 = kdot<BB, HILO>(C.k0, QH, QL), d1 = kdot<BB, HILO>(C.k1, QH, QL);
-      kp0[c] = fmaf(f16hi(C.km0) * kTwo24, d0, f16lo(C.km0) * qsum);
-      kp1[c] = fmaf(f16hi(C.km1) * kTwo24, d1, f16lo(C.km1) * qsum);
+      const float d0 = (float)kdot<BB>(C.k0, Q), d1 = (float)kdot<BB>(C.k1, Q);
+      kp0[c] = fmaf(f16hi(C.km0) * qscale, d0, f16lo(C.km0) * qsum);
+      kp1[c] = fmaf(f16hi(C.km1) * qscale, d1, f16lo(C.km1) * qsum);
     };
     kpart(T.c0, 0, std::integral_constant<int, cbits<CB, 0>()>{});
     if constexpr (NC > 1) kpart(T.c1, 1, std::integral_constant<int, cbits<CB, 1>()>{});
@@ -569,10 +608,7 @@ struct Entry {
 #ifndef RQ_DEPTH
 #define RQ_DEPTH 2
 #endif
-#ifndef RQ_HILO
-#define RQ_HILO true
-#endif
-#define RQ_E(D, NC, CB) {D, NC, CB, decode_fused<D, NC, CB, RQ_HILO, RQ_DEPTH>}
+#define RQ_E(D, NC, CB) {D, NC, CB, decode_fused<D, NC, CB, RQ_DEPTH>}
 #define RQ_PLANS(D)                                                                                        \
   RQ_E(D, 1, 0x2), RQ_E(D, 1, 0x4), RQ_E(D, 2, 0x22), RQ_E(D, 2, 0x24), RQ_E(D, 2, 0x42), RQ_E(D, 2, 0x44), \
       RQ_E(D, 3, 0x244), RQ_E(D, 3, 0x224), RQ_E(D, 3, 0x222), RQ_E(D, 3, 0x444), RQ_E(D, 4, 0x2244),        \
