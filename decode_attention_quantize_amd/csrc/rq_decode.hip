@@ -435,8 +435,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
 
     // ---- online softmax (log2 domain); the max is wave-uniform, so the rare
     // rescale is a scalar branch
-    const float tmax = __builtin_bit_cast(
-        float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, wave_max(fmaxf(s0, s1)))));
+    const float tmax = wave_max_uniform(fmaxf(s0, s1));
     if (tmax > m) {
       const float f = __builtin_amdgcn_exp2f(m - tmax);
       m = tmax;

@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void bf16_fused(Bf16Params p) {
       s[u] = ok[u] ? d : -INFINITY;
       tmax = fmaxf(tmax, s[u]);
     }
-    tmax = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, wave_max(tmax))));
+    tmax = wave_max_uniform(tmax);
     if (tmax > m) {
       const float f = exp2f(m - tmax);
       m = tmax;

@@ -27,15 +27,40 @@ __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// DPP lane moves (gfx9 data-parallel primitives) on float values.
+enum : int {
+  kQuadSwap1 = 0xB1,      // quad_perm [1,0,3,2]: lane ^ 1
+  kQuadSwap2 = 0x4E,      // quad_perm [2,3,0,1]: lane ^ 2
+  kRowHalfMirror = 0x141, // lane i <- 7 - i within each 8 lanes
+  kRowMirror = 0x140,     // lane i <- 15 - i within each 16-lane row
+  kRowBcast15 = 0x142,    // lane 15 of row r -> every lane of row r + 1
+  kRowBcast31 = 0x143,    // lane 31 -> every lane of rows 2 and 3
+};
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp(float x) {
+  const int v = __builtin_bit_cast(int, x);
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(v, v, CTRL, ROW_MASK, 0xF, false));
+}
+
 // Sum over the G consecutive lanes G*i .. G*i+G-1 (every lane gets the sum).
 template <int G>
 __device__ __forceinline__ float group_sum(float x) {
   if constexpr (G == 1) {
     return x;
-  } else if constexpr ((G & (G - 1)) == 0) {
-#pragma unroll
-    for (int m = 1; m < G; m <<= 1) x += __shfl_xor(x, m, 64);
-    return x;
+  } else if constexpr (G == 2) {
+    return x + dpp<kQuadSwap1>(x);
+  } else if constexpr (G == 4) {
+    x += dpp<kQuadSwap1>(x);
+    return x + dpp<kQuadSwap2>(x);
+  } else if constexpr (G == 8) {
+    x += dpp<kQuadSwap1>(x);
+    x += dpp<kQuadSwap2>(x);
+    return x + dpp<kRowHalfMirror>(x);
+  } else if constexpr (G == 16) {
+    x += dpp<kQuadSwap1>(x);
+    x += dpp<kQuadSwap2>(x);
+    x += dpp<kRowHalfMirror>(x);
+    return x + dpp<kRowMirror>(x);
   } else {
     const int lane = threadIdx.x & 63;
     const int base = lane - lane % G;
@@ -44,6 +69,17 @@ __device__ __forceinline__ float group_sum(float x) {
     for (int j = 0; j < G; ++j) s += __shfl(x, base + j, 64);
     return s;
   }
+}
+
+// Maximum over the wave, returned wave-uniform (from lane 63).
+__device__ __forceinline__ float wave_max_uniform(float x) {
+  x = fmaxf(x, dpp<kQuadSwap1>(x));
+  x = fmaxf(x, dpp<kQuadSwap2>(x));
+  x = fmaxf(x, dpp<kRowHalfMirror>(x));
+  x = fmaxf(x, dpp<kRowMirror>(x));
+  x = fmaxf(x, dpp<kRowBcast15, 0xA>(x));
+  x = fmaxf(x, dpp<kRowBcast31, 0xC>(x));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
 // Work item of this workgroup in a 1-D grid of nsplit * B * H workgroups.
@@ -59,12 +95,6 @@ __device__ __forceinline__ void split_item(int nsplit, int B, int H, int& split,
   const int rest = k / nsplit;
   b = rest % B;
   h = rest / B;
-}
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
-  return x;
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
