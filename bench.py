@@ -175,8 +175,6 @@ def main():
     ap.add_argument("--no-chained", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--call-reps", type=int, default=50)
-    ap.add_argument("--schedule", choices=("overlap", "serial"), default="overlap",
-                    help="overlap: combines and appends on a second stream under the streaming launches")
     ap.add_argument("--cpu-sample-units", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum timed CPU-oracle seconds")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -251,76 +249,28 @@ def main():
         f"{time.time() - t_build:.1f}s")
 
     # ---------------------------------------------------------------- steps as graphs
-    # One step: for each loop r and layer l, the streaming launch (partial) on the
-    # main stream and its combine on a second stream -- plus, after the final
-    # loop, the layer's append of the current token -- so the short,
-    # latency-bound launches run under the next streaming launch. Two
-    # workspaces alternate; a workspace is reused only after its combine ran.
-    # --schedule serial issues the one-call entry points on one stream instead.
-    aux = torch.cuda.Stream()
-    ws_pair = [ws, rq.alloc_workspace(d_rq)]
-    ws_ch_pair = [ws_ch, rq.alloc_workspace(d_ch)]
-
-    def step_overlap(k, partial, combine, append):
-        main = torch.cuda.current_stream()
-        aux.wait_stream(main)
-        done = [None, None]
-        n = 0
+    # One step, in the order a looped decoder runs it: for each loop r and layer
+    # l, the attention call (streaming launch + combine) that the next layer's
+    # query would depend on; after the final loop, each layer's append of the
+    # current token; then past_len += 1. All on one stream.
+    def rq_step(k, cs, d, workspace):
         for r in range(L):
             for l in range(w.layers):
-                j = n & 1
-                if done[j] is not None:
-                    main.wait_event(done[j])
-                partial(k, l, r, j, main)
-                ev = torch.cuda.Event()
-                ev.record(main)
-                aux.wait_event(ev)
-                combine(k, l, r, j, aux)
-                if r == L - 1 and append is not None:
-                    append(k, l, aux)
-                done[j] = torch.cuda.Event()
-                done[j].record(aux)
-                n += 1
-        main.wait_stream(aux)
+                kc = kvcur[k, l, 0, r, :, :, 0]
+                vc = kvcur[k, l, 1, r, :, :, 0]
+                rq.decode_attn(cs[l], r, qs[k, l, r], kc, vc, past_len, scale, out[l, r], workspace)
+                if r == L - 1:
+                    rq.quantize_append(cs[l], kvcur[k, l], past_len, 1)
         past_len.add_(1)
 
-    def rq_step(k, cs, d, wsp):
-        if args.schedule == "serial":
-            for r in range(L):
-                for l in range(w.layers):
-                    kc = kvcur[k, l, 0, r, :, :, 0]
-                    vc = kvcur[k, l, 1, r, :, :, 0]
-                    rq.decode_attn(cs[l], r, qs[k, l, r], kc, vc, past_len, scale, out[l, r], wsp[0])
-                    if r == L - 1:
-                        rq.quantize_append(cs[l], kvcur[k, l], past_len, 1)
-            past_len.add_(1)
-            return
-        step_overlap(
-            k,
-            lambda k, l, r, j, st: rq.decode_attn_partial(cs[l], r, qs[k, l, r], past_len, scale, wsp[j], stream=st),
-            lambda k, l, r, j, st: rq.decode_combine(d, cs[l].rot[1], qs[k, l, r], kvcur[k, l, 0, r, :, :, 0],
-                                                     kvcur[k, l, 1, r, :, :, 0], past_len, scale, out[l, r],
-                                                     wsp[j], stream=st),
-            lambda k, l, st: rq.quantize_append(cs[l], kvcur[k, l], past_len, 1, stream=st))
-
     def bf16_step(k):
-        if args.schedule == "serial":
-            for r in range(L):
-                for l in range(w.layers):
-                    kc = kvcur[k, l, 0, r, :, :, 0]
-                    vc = kvcur[k, l, 1, r, :, :, 0]
-                    rq.decode_attn_bf16(d_rq, bf16[l][0, r], bf16[l][1, r], qs[k, l, r], kc, vc, past_len, scale,
-                                        out[l, r], ws)
-            past_len.add_(1)
-            return
-        step_overlap(
-            k,
-            lambda k, l, r, j, st: rq.decode_attn_bf16_partial(d_rq, bf16[l][0, r], bf16[l][1, r], qs[k, l, r],
-                                                               past_len, scale, ws_pair[j], stream=st),
-            lambda k, l, r, j, st: rq.decode_combine(d_rq, None, qs[k, l, r], kvcur[k, l, 0, r, :, :, 0],
-                                                     kvcur[k, l, 1, r, :, :, 0], past_len, scale, out[l, r],
-                                                     ws_pair[j], stream=st),
-            None)
+        for r in range(L):
+            for l in range(w.layers):
+                kc = kvcur[k, l, 0, r, :, :, 0]
+                vc = kvcur[k, l, 1, r, :, :, 0]
+                rq.decode_attn_bf16(d_rq, bf16[l][0, r], bf16[l][1, r], qs[k, l, r], kc, vc, past_len, scale,
+                                    out[l, r], ws)
+        past_len.add_(1)
 
     side = torch.cuda.Stream()
 
@@ -351,7 +301,7 @@ def main():
         return dt
 
     log("capturing RQ steps")
-    g_rq = capture(lambda k: rq_step(k, caches, d_rq, ws_pair))
+    g_rq = capture(lambda k: rq_step(k, caches, d_rq, ws))
     dt_rq = run(g_rq, args.warmup)
     log(f"RQ: {K} steps in {dt_rq * 1e3:.2f} ms")
     del g_rq
@@ -365,7 +315,7 @@ def main():
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "layers": w.layers, "batch": B, "heads": H, "head_dim": D, "loops": L,
                    "context": T, "bits": bits, "group": w.group, "codes": "int2/int4 + fp16 scale/offset + fp16 alpha",
-                   "arith": "fp16 dot2 products, fp32 accumulation", "schedule": args.schedule},
+                   "arith": "fp16 dot2 products, fp32 accumulation"},
         "hbm_gbps_step": step_bytes / (dt_rq / K) / 1e9,
         "hbm_frac_step": step_bytes / (dt_rq / K) / 1e9 / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": step_bytes,
@@ -373,7 +323,7 @@ def main():
 
     if not args.no_chained:
         log("capturing chained steps")
-        g_ch = capture(lambda k: rq_step(k, chained, d_ch, ws_ch_pair))
+        g_ch = capture(lambda k: rq_step(k, chained, d_ch, ws_ch))
         dt_ch = run(g_ch, args.warmup)
         del g_ch
         ch_bytes = sum(call_bytes(D, cbits, "prev", r) for r in range(L)) * H * w.layers * B * mean_ctx
