@@ -34,20 +34,20 @@ LAST, PREV = rq.POLICY_LAST_LOOP, rq.POLICY_PREV_LOOP
 CHECK_STEPS = (0, STEPS - 1)
 
 
-def _sample_units(n, seed):
+def _sample_units(n, seed, w=W):
     rnd = random.Random(seed)
-    units = {(0, 0), (W.batch - 1, W.heads - 1)}
+    units = {(0, 0), (w.batch - 1, w.heads - 1)}
     while len(units) < n:
-        units.add((rnd.randrange(W.batch), rnd.randrange(W.heads)))
+        units.add((rnd.randrange(w.batch), rnd.randrange(w.heads)))
     return sorted(units)
 
 
-def _build(layer, policy, bits):
+def _build(layer, policy, bits, w=W):
     """Inputs and a GPU cache holding tokens [0, T + STEPS - 1) of `layer`."""
-    B, H, D, T = W.batch, W.heads, W.D, W.T
+    B, H, D, T = w.batch, w.heads, w.D, w.T
     T_max = T + STEPS
-    X = synth.kv(W, layer, 0, T_max, device="cuda")
-    rk, rv = synth.rotation(W, layer, 0), synth.rotation(W, layer, 1)
+    X = synth.kv(w, layer, 0, T_max, device="cuda")
+    rk, rv = synth.rotation(w, layer, 0), synth.rotation(w, layer, 1)
     d = rq.make_desc(B, H, D, list(bits), T_max, policy)
     cache = rq.LayerCache.allocate(d, rk, rv)
     log(f"layer {layer} policy {policy}: bulk store of {T} tokens")
@@ -59,15 +59,15 @@ def _build(layer, policy, bits):
     return X, rk, rv, cache
 
 
-def _gpu_outputs(X, cache, layer):
+def _gpu_outputs(X, cache, layer, w=W):
     """{(step, loop): (out [B][H][D] on the host, q, k_cur, v_cur)} in the benchmark's call order."""
-    B, H, D, T = W.batch, W.heads, W.D, W.T
+    B, H, D, T = w.batch, w.heads, w.D, w.T
     ws = rq.alloc_workspace(cache.desc)
     res = {}
     for k in CHECK_STEPS:
         past = torch.full((B,), T + k, dtype=torch.int32, device="cuda")
-        for r in range(W.L):
-            q = synth.query(W, layer, r, k, device="cuda")
+        for r in range(w.L):
+            q = synth.query(w, layer, r, k, device="cuda")
             kc = X[0, r, :, :, T + k].contiguous()
             vc = X[1, r, :, :, T + k].contiguous()
             out = torch.empty(B, H, D, device="cuda")
@@ -77,10 +77,10 @@ def _gpu_outputs(X, cache, layer):
     return res
 
 
-def _check(layer, policy, bits, units, label):
-    X, rk, rv, cache = _build(layer, policy, bits)
-    outs = _gpu_outputs(X, cache, layer)
-    Tc = W.T + STEPS - 1
+def _check(layer, policy, bits, units, label, w=W):
+    X, rk, rv, cache = _build(layer, policy, bits, w)
+    outs = _gpu_outputs(X, cache, layer, w)
+    Tc = w.T + STEPS - 1
     host = host_copy(cache)
     worst = 0.0
     for i in range(0, len(units), 16):
@@ -89,8 +89,8 @@ def _check(layer, policy, bits, units, label):
         series = oracle_layer(X, rk, rv, bits, policy, Tc, units=chunk)
         assert_cache_parity(compare_cache(cache, series, Tc, host=host), f"{label} units {i}+")
         for (k, r), (out, q, kc, vc) in outs.items():
-            lens = [W.T + k] * W.batch
-            ref = oracle_attention(series, chunk, r, lens, rk, rv, q, kc, vc, 1.0 / math.sqrt(W.D))
+            lens = [w.T + k] * w.batch
+            ref = oracle_attention(series, chunk, r, lens, rk, rv, q, kc, vc, 1.0 / math.sqrt(w.D))
             err = max_rel_err(out, ref)
             worst = max(worst, err)
             assert err <= TOL_ATTN, (label, k, r, err)
@@ -108,6 +108,19 @@ def test_ouro_16k_last_layer_sampled():
 
 def test_ouro_16k_chained_sampled():
     _check(0, PREV, W.chained_bits, _sample_units(8, 7), "16k chained layer 0")
+
+
+def test_huginn_4k_sampled():
+    """Huginn-shaped workload at full size (B4, H55, D96, 8 loops, 4096 tokens): the
+    last layer, sampled series, every loop."""
+    w = synth.WORKLOADS["huginn_4k"]
+    _check(w.layers - 1, LAST, w.bits, _sample_units(8, 5, w), "huginn 4k", w)
+
+
+def test_capacity_8k_batch64_sampled():
+    """Capacity shape (8192 tokens, batch 64): one slot per (batch, head), sampled series."""
+    w = synth.WORKLOADS["ouro_8k_capacity"].with_(batch=64)
+    _check(0, LAST, w.bits, _sample_units(8, 3, w), "8k B64", w)
 
 
 def test_ouro_16k_bf16_sampled():
