@@ -56,7 +56,7 @@ def call_bytes(D, bits, policy, r):
     return 2 * sum(comp_bytes(D, bits[c], c != a) for c in comps)
 
 
-DOM_KERNEL = "decode_fused<128, 2, 36u, true, 2>"
+DOM_KERNEL = "decode_fused<128, 2, 36u, 2>"
 COPY_KERNEL = "bitwise_not"
 COPY_KIB = float(1 << 20)            # 1 GiB read and 1 GiB written by the calibration kernel
 PROFILES = os.path.join(ROOT, "profiles")
