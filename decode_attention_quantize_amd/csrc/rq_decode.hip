@@ -15,8 +15,7 @@
 // and values accumulate sum_t p_t zhat_V,t in the rotated domain with the same
 // per-group split into a code part (weight p beta s) and an offset part.
 //
-// Keys: q' of a lane's group is held as 16-bit fixed point in two signed
-// 8-bit limbs; masking a code word with 0x0F0F0F0F (INT4) or 0x03030303 (INT2)
+// Keys: q' of a lane's group is held as fixed point in signed 8-bit limbs; masking a code word with 0x0F0F0F0F (INT4) or 0x03030303 (INT2)
 // puts four codes in four bytes, and v_dot4c_i32_i8 against each limb gives an
 // exact integer sum of q'_e code_e.
 // Values: a masked code field read as an fp16 bit pattern is the subnormal
@@ -75,14 +74,20 @@ __device__ __forceinline__ Words<BITS> load_group(__amdgpu_buffer_rsrc_t r, uint
   return w;
 }
 
-// q' of one group as 16-bit fixed point, v_e = round(q'_e 2^E) (|v| < 2^14),
-// split into signed 8-bit limbs v = 256 hi + lo (hi in [-64, 64], lo in
-// [-128, 127]) and packed four per register in the order the code bytes of a
-// word come out of one mask (see kdot). Integer dot products of the codes with
-// both limbs are exact.
+// q' of one group as fixed point, v_e = round(q'_e 2^E) with |v| < 2^kFixBits
+// (E per group), written in balanced base 256 as kLimbs signed 8-bit limbs
+// (most significant first) and packed four per register in the order the code
+// bytes of a word come out of one mask (see kdot). Integer dot products of the
+// codes with each limb are exact; the rounding of q' to kFixBits bits is the only
+// error, a relative 2^-kFixBits of the group's largest |q'|. Two limbs (14 bits)
+// keep scores within ~1e-3 (log2 units) of exact at 16k tokens with synthetic
+// outlier keys; three limbs (21 bits) take them to ~1e-6 but cost 16 more VALU
+// instructions per tile and 16 more registers.
+constexpr int kLimbs = 2;
+constexpr int kFixBits = kLimbs == 2 ? 14 : 21;
 struct QFix {
-  uint32_t q4[4][2][2];  // INT4: word j, mask (even / odd nibbles), limb (hi / lo)
-  uint32_t q2[2][4][2];  // INT2: word j, field s, limb
+  uint32_t q4[4][2][kLimbs];  // INT4: word j, mask (low / high nibbles), limb
+  uint32_t q2[2][4][kLimbs];  // INT2: word j, field s, limb
 };
 
 // Elements of the group that byte b (0..3) of a masked word holds.
@@ -93,19 +98,22 @@ struct QFix {
 __host__ __device__ constexpr int int4_elem(int j, int m, int b) { return (b >> 1) * 16 + 4 * j + 2 * (b & 1) + m; }
 __host__ __device__ constexpr int int2_elem(int j, int s, int b) { return (b >> 1) * 16 + 8 * j + 4 * (b & 1) + s; }
 
-// sum_e v_e code_e over one group (exact, int32).
+// sum_e v_e code_e over one group (exact in int32: |v| < 2^21, 32 codes < 16).
 template <int BITS>
 __device__ __forceinline__ int kdot(const Words<BITS>& c, const QFix& Q) {
-  int ah = 0, al = 0;
+  int a[kLimbs];
+#pragma unroll
+  for (int l = 0; l < kLimbs; ++l) a[l] = 0;
   if constexpr (BITS == 4) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t x = c.w[j];
       const int m0 = (int)(x & 0x0F0F0F0Fu), m1 = (int)((x >> 4) & 0x0F0F0F0Fu);
-      ah = __builtin_amdgcn_sdot4(m0, (int)Q.q4[j][0][0], ah, false);
-      al = __builtin_amdgcn_sdot4(m0, (int)Q.q4[j][0][1], al, false);
-      ah = __builtin_amdgcn_sdot4(m1, (int)Q.q4[j][1][0], ah, false);
-      al = __builtin_amdgcn_sdot4(m1, (int)Q.q4[j][1][1], al, false);
+#pragma unroll
+      for (int l = 0; l < kLimbs; ++l) {
+        a[l] = __builtin_amdgcn_sdot4(m0, (int)Q.q4[j][0][l], a[l], false);
+        a[l] = __builtin_amdgcn_sdot4(m1, (int)Q.q4[j][1][l], a[l], false);
+      }
     }
   } else {
 #pragma unroll
@@ -114,16 +122,19 @@ __device__ __forceinline__ int kdot(const Words<BITS>& c, const QFix& Q) {
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
         const int m = (int)((x >> (2 * f)) & 0x03030303u);
-        ah = __builtin_amdgcn_sdot4(m, (int)Q.q2[j][f][0], ah, false);
-        al = __builtin_amdgcn_sdot4(m, (int)Q.q2[j][f][1], al, false);
+#pragma unroll
+        for (int l = 0; l < kLimbs; ++l) a[l] = __builtin_amdgcn_sdot4(m, (int)Q.q2[j][f][l], a[l], false);
       }
     }
   }
-  return ah * 256 + al;
+  int r = a[0];
+#pragma unroll
+  for (int l = 1; l < kLimbs; ++l) r = r * 256 + a[l];
+  return r;
 }
 
 // Field scale 2^shift of element e of a group (index k = e mod 16 in its half)
-// once vacc() has moved it to a byte: INT4 k even 1, odd 16; INT2 4^(k mod 4).
+// as vpairs() presents it: INT4 k even 1, odd 16; INT2 4^(k mod 4).
 template <int BITS>
 __host__ __device__ constexpr float vclass(int e) {
   return BITS == 4 ? (((e & 15) & 1) ? 16.0f : 1.0f) : (float)(1 << (2 * ((e & 15) & 3)));
@@ -132,33 +143,45 @@ __host__ __device__ constexpr float vclass(int e) {
 // acc[e] += W.lo code_{t0,e} + W.hi code_{t1,e} for the 32 elements of a group,
 // accumulated at the field scale of reference width REF (the widest component),
 // so that every component shares one accumulator per element.
+// Code pairs (token t0 in the low half, t1 in the high half, as fp16 subnormal
+// patterns at the reference field class) of elements e = 16 half + 4 blk + q,
+// q = 0..3, of one component, with the weight each pair takes.
+// INT4: half-word blk of each half holds k = 4 blk .. 4 blk + 3; bytes 2 half and
+// 2 half + 1 of word blk carry them, low nibble at class 1, high nibble at 16.
+// INT2: element block blk lies in byte 2 half + (blk & 1) of word blk / 2, fields
+// at classes 1, 4, 16, 64. Under an INT4 reference (classes 1, 16, 1, 16) the
+// upper two fields are shifted down by 4 bits, so every field lands at class 1
+// or 4 and only W and 4W are needed (exact in fp16, W <= kWMax); scaling W down
+// instead would push small weights into fp16 subnormals.
+__device__ __forceinline__ uint32_t pair_byte(uint32_t w0, uint32_t w1, int by) {
+  // [t0 byte `by`, 0, t1 byte `by`, 0]
+  return __builtin_amdgcn_perm(w1, w0, 0x0c000c00u | ((uint32_t)(4 + by) << 16) | (uint32_t)by);
+}
+
 template <int BITS, int REF>
-__device__ __forceinline__ void vacc(const Words<BITS>& c0, const Words<BITS>& c1, uint32_t W, float (&acc)[32]) {
-  uint32_t Wq[4] = {W, W, W, W};
-  if constexpr (BITS == 2 && REF == 4) {
-    // INT2 field scales 1, 4, 16, 64 -> INT4 reference 1, 16, 1, 16: weights x 1, 4, 1/16, 1/4
-    const h2_t w = __builtin_bit_cast(h2_t, W);
-    Wq[1] = __builtin_bit_cast(uint32_t, w * h2_t{(_Float16)4.0f, (_Float16)4.0f});
-    Wq[2] = __builtin_bit_cast(uint32_t, w * h2_t{(_Float16)0.0625f, (_Float16)0.0625f});
-    Wq[3] = __builtin_bit_cast(uint32_t, w * h2_t{(_Float16)0.25f, (_Float16)0.25f});
-  }
+__device__ __forceinline__ void vpairs(const Words<BITS>& c0, const Words<BITS>& c1, int half, int blk, uint32_t W,
+                                       uint32_t W4, uint32_t (&x)[4], uint32_t (&wq)[4]) {
+  if constexpr (BITS == 4) {
+    const uint32_t b0 = pair_byte(c0.w[blk], c1.w[blk], 2 * half), b1 = pair_byte(c0.w[blk], c1.w[blk], 2 * half + 1);
+    x[0] = b0 & 0x000F000Fu;
+    x[1] = b0 & 0x00F000F0u;
+    x[2] = b1 & 0x000F000Fu;
+    x[3] = b1 & 0x00F000F0u;
+    wq[0] = wq[1] = wq[2] = wq[3] = W;
+  } else {
+    const uint32_t b = pair_byte(c0.w[blk >> 1], c1.w[blk >> 1], 2 * half + (blk & 1));
+    if constexpr (REF == 4) {
+      const uint32_t b4 = b >> 4;
+      x[0] = b & 0x00030003u;
+      x[1] = b & 0x000C000Cu;
+      x[2] = b4 & 0x00030003u;
+      x[3] = b4 & 0x000C000Cu;
+      wq[0] = wq[2] = W;
+      wq[1] = wq[3] = W4;
+    } else {
 #pragma unroll
-  for (int j = 0; j < BITS; ++j) {
-#pragma unroll
-    for (int by = 0; by < 4; ++by) {
-      // [t0 byte `by`, 0, t1 byte `by`, 0]
-      const uint32_t sel = 0x0c000c00u | ((uint32_t)(4 + by) << 16) | (uint32_t)by;
-      const uint32_t x = __builtin_amdgcn_perm(c1.w[j], c0.w[j], sel);
-      const int half = by >> 1, hb = by & 1;
-      if constexpr (BITS == 4) {
-        const int e = 16 * half + 4 * j + 2 * hb;
-        acc[e] = dot2(x & 0x000F000Fu, W, acc[e]);
-        acc[e + 1] = dot2(x & 0x00F000F0u, W, acc[e + 1]);
-      } else {
-        const int e = 16 * half + 8 * j + 4 * hb;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[e + q] = dot2(x & (0x00030003u << (2 * q)), Wq[q], acc[e + q]);
-      }
+      for (int q = 0; q < 4; ++q) x[q] = b & (0x00030003u << (2 * q));
+      wq[0] = wq[1] = wq[2] = wq[3] = W;
     }
   }
 }
@@ -348,45 +371,54 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
   fetch(A, base);
   if constexpr (DEPTH == 3) fetch(B, base + STRIDE);
 
-  // This lane's group of q' in fixed point (per-group exponent), and its sum.
+  // This lane's group of q' in fixed point (per-group exponent). qsum, which
+  // multiplies the group offsets, is the sum of the same fixed-point values, so a
+  // stored value o + s c meets one consistent q'.
   QFix Q;
-  float qsum = 0.0f, qscale;
+  float qsum, qscale;
   {
     float qv[32], mx = 0.0f;
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
       qv[e] = qr[32 * gsel + e];
-      qsum += qv[e];
       mx = fmaxf(mx, fabsf(qv[e]));
     }
     int ex = 0;
-    (void)frexpf(mx, &ex);                  // mx in [2^(ex-1), 2^ex)
-    const int E = mx > 0.0f ? 14 - ex : 0;  // |q' 2^E| < 2^14
+    (void)frexpf(mx, &ex);                          // mx in [2^(ex-1), 2^ex)
+    const int E = mx > 0.0f ? kFixBits - ex : 0;    // |q' 2^E| < 2^kFixBits
     qscale = ldexpf(1.0f, -E);
-    int hi[32], lo[32];
+    int lm[kLimbs][32];
+    int vsum = 0;
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
-      const int v = __float2int_rn(ldexpf(qv[e], E));
-      hi[e] = (v + 128) >> 8;
-      lo[e] = v - 256 * hi[e];
+      int v = __float2int_rn(ldexpf(qv[e], E));
+      vsum += v;
+#pragma unroll
+      for (int l = kLimbs - 1; l >= 0; --l) {      // balanced base-256 digits, least significant first
+        const int d = l == 0 ? v : ((v + 128) & 255) - 128;
+        lm[l][e] = d;
+        v = (v - d) >> 8;
+      }
     }
+    qsum = (float)vsum * qscale;
     auto pack = [](int a, int b, int c, int d) {
       return (uint32_t)(a & 255) | ((uint32_t)(b & 255) << 8) | ((uint32_t)(c & 255) << 16) | ((uint32_t)d << 24);
     };
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int l = 0; l < kLimbs; ++l) {
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        Q.q4[j][m][0] = pack(hi[int4_elem(j, m, 0)], hi[int4_elem(j, m, 1)], hi[int4_elem(j, m, 2)], hi[int4_elem(j, m, 3)]);
-        Q.q4[j][m][1] = pack(lo[int4_elem(j, m, 0)], lo[int4_elem(j, m, 1)], lo[int4_elem(j, m, 2)], lo[int4_elem(j, m, 3)]);
-      }
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+        for (int m = 0; m < 2; ++m)
+          Q.q4[j][m][l] = pack(lm[l][int4_elem(j, m, 0)], lm[l][int4_elem(j, m, 1)], lm[l][int4_elem(j, m, 2)],
+                               lm[l][int4_elem(j, m, 3)]);
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        Q.q2[j][f][0] = pack(hi[int2_elem(j, f, 0)], hi[int2_elem(j, f, 1)], hi[int2_elem(j, f, 2)], hi[int2_elem(j, f, 3)]);
-        Q.q2[j][f][1] = pack(lo[int2_elem(j, f, 0)], lo[int2_elem(j, f, 1)], lo[int2_elem(j, f, 2)], lo[int2_elem(j, f, 3)]);
-      }
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+          Q.q2[j][f][l] = pack(lm[l][int2_elem(j, f, 0)], lm[l][int2_elem(j, f, 1)], lm[l][int2_elem(j, f, 2)],
+                               lm[l][int2_elem(j, f, 3)]);
+    }
   }
 
   float acc[32];
@@ -454,7 +486,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
     // by one ptilde (fp16-rounded p), so rounding W costs a relative 2^-11 of the value
     // rather than of its code part s c. Subnormal W (tiny contributions, or s == 0)
     // take the exact p beta o instead.
-    auto vpart = [&](auto& C, int c, auto bits_tag) {
+    uint32_t Wc[NC], W4c[NC];
+    auto vweight = [&](auto& C, int c, auto bits_tag) {
       constexpr int BB = decltype(bits_tag)::value;
       const float pb0 = ok0 ? p0 * vb0[c] : 0.0f, pb1 = ok1 ? p1 * vb1[c] : 0.0f;
       const float s0v = f16hi(C.vm0), s1v = f16hi(C.vm1), o0v = f16lo(C.vm0), o1v = f16lo(C.vm1);
@@ -462,13 +495,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
       const float wb0 = f16lo(W), wb1 = f16hi(W);
       bias += (wb0 >= kMinNormal) ? wb0 * (o0v * __builtin_amdgcn_rcpf(s0v)) * (1.0f / kWScale) : pb0 * o0v;
       bias += (wb1 >= kMinNormal) ? wb1 * (o1v * __builtin_amdgcn_rcpf(s1v)) * (1.0f / kWScale) : pb1 * o1v;
-      vacc<BB, REF>(C.v0, C.v1, W, acc);
+      Wc[c] = W;
+      W4c[c] = W;
+      if constexpr (BB == 2 && REF == 4)
+        W4c[c] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, W) * h2_t{(_Float16)4.0f, (_Float16)4.0f});
     };
-    vpart(T.c0, 0, std::integral_constant<int, cbits<CB, 0>()>{});
-    if constexpr (NC > 1) vpart(T.c1, 1, std::integral_constant<int, cbits<CB, 1>()>{});
-    if constexpr (NC > 2) vpart(T.c2, 2, std::integral_constant<int, cbits<CB, 2>()>{});
-    if constexpr (NC > 3) vpart(T.c3, 3, std::integral_constant<int, cbits<CB, 3>()>{});
+    vweight(T.c0, 0, std::integral_constant<int, cbits<CB, 0>()>{});
+    if constexpr (NC > 1) vweight(T.c1, 1, std::integral_constant<int, cbits<CB, 1>()>{});
+    if constexpr (NC > 2) vweight(T.c2, 2, std::integral_constant<int, cbits<CB, 2>()>{});
+    if constexpr (NC > 3) vweight(T.c3, 3, std::integral_constant<int, cbits<CB, 3>()>{});
 
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        uint32_t x[NC][4], wq[NC][4];
+        vpairs<cbits<CB, 0>(), REF>(T.c0.v0, T.c0.v1, half, blk, Wc[0], W4c[0], x[0], wq[0]);
+        if constexpr (NC > 1) vpairs<cbits<CB, 1>(), REF>(T.c1.v0, T.c1.v1, half, blk, Wc[1], W4c[1], x[1], wq[1]);
+        if constexpr (NC > 2) vpairs<cbits<CB, 2>(), REF>(T.c2.v0, T.c2.v1, half, blk, Wc[2], W4c[2], x[2], wq[2]);
+        if constexpr (NC > 3) vpairs<cbits<CB, 3>(), REF>(T.c3.v0, T.c3.v1, half, blk, Wc[3], W4c[3], x[3], wq[3]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int c = 0; c < NC; ++c) acc[16 * half + 4 * blk + q] = dot2(x[c][q], wq[c][q], acc[16 * half + 4 * blk + q]);
+      }
   };
   if constexpr (DEPTH == 2) {
     for (;;) {
