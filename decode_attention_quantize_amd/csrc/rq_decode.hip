@@ -15,15 +15,16 @@
 // and values accumulate sum_t p_t zhat_V,t in the rotated domain with the same
 // per-group split into a code part (weight p beta s) and an offset part.
 //
-// Keys: q' of a lane's group is held as fixed point in signed 8-bit limbs; masking a code word with 0x0F0F0F0F (INT4) or 0x03030303 (INT2)
-// puts four codes in four bytes, and v_dot4c_i32_i8 against each limb gives an
-// exact integer sum of q'_e code_e.
+// Keys: q' of a lane's group is held as fixed point in signed 8-bit limbs;
+// masking a code word with 0x0F0F0F0F (INT4) or 0x03030303 (INT2) puts four
+// codes in four bytes, and v_dot4c_i32_i8 against each limb gives an exact
+// integer sum of q'_e code_e.
 // Values: a masked code field read as an fp16 bit pattern is the subnormal
-// number code * 2^(shift - 24), exactly, and v_dot2c_f32_f16 keeps fp16
-// subnormals, so one AND yields two codes ready for the dot product. The
-// packed layout places group elements e and e+16 at the same bit offset of the
-// low and high halves of a word; a byte permute pairs the same element of two
-// tokens, and one mask then yields that element of both tokens.
+// number code * 2^(shift - 24), exactly, and the mixed-precision FMA takes fp16
+// subnormal operands exactly. The packed layout places group elements e and
+// e+16 at the same bit offset of the low and high halves of a word; a byte
+// permute pairs the same element of two tokens, and one mask then yields that
+// element of both tokens.
 #include <hip/hip_runtime.h>
 
 #include "rq_combine.hpp"
@@ -37,10 +38,7 @@ namespace {
 #define RQ_WAVES_SMALL 3
 #endif
 
-constexpr float kTwo24 = 16777216.0f;
-constexpr float kWScale = 64.0f;                // value weights are fp16(2^6 p beta s)
-constexpr float kWMax = 16376.0f;               // keeps 4x the weight finite in fp16
-constexpr float kMinNormal = 6.103515625e-05f;  // smallest normal fp16, 2^-14
+constexpr float kTwo24 = 16777216.0f;  // a masked code field reads as code * 2^(shift - 24)
 
 template <int BITS>
 struct Words {
@@ -145,29 +143,27 @@ __host__ __device__ constexpr float vclass(int e) {
 // so that every component shares one accumulator per element.
 // Code pairs (token t0 in the low half, t1 in the high half, as fp16 subnormal
 // patterns at the reference field class) of elements e = 16 half + 4 blk + q,
-// q = 0..3, of one component, with the weight each pair takes.
+// q = 0..3, of one component.
 // INT4: half-word blk of each half holds k = 4 blk .. 4 blk + 3; bytes 2 half and
 // 2 half + 1 of word blk carry them, low nibble at class 1, high nibble at 16.
 // INT2: element block blk lies in byte 2 half + (blk & 1) of word blk / 2, fields
 // at classes 1, 4, 16, 64. Under an INT4 reference (classes 1, 16, 1, 16) the
-// upper two fields are shifted down by 4 bits, so every field lands at class 1
-// or 4 and only W and 4W are needed (exact in fp16, W <= kWMax); scaling W down
-// instead would push small weights into fp16 subnormals.
+// upper two fields are shifted down by 4 bits, so they land at classes 1 and 4
+// and q = 1, 3 take the weight 4W (x4 in vw4()).
 __device__ __forceinline__ uint32_t pair_byte(uint32_t w0, uint32_t w1, int by) {
   // [t0 byte `by`, 0, t1 byte `by`, 0]
   return __builtin_amdgcn_perm(w1, w0, 0x0c000c00u | ((uint32_t)(4 + by) << 16) | (uint32_t)by);
 }
 
 template <int BITS, int REF>
-__device__ __forceinline__ void vpairs(const Words<BITS>& c0, const Words<BITS>& c1, int half, int blk, uint32_t W,
-                                       uint32_t W4, uint32_t (&x)[4], uint32_t (&wq)[4]) {
+__device__ __forceinline__ void vpairs(const Words<BITS>& c0, const Words<BITS>& c1, int half, int blk,
+                                       uint32_t (&x)[4]) {
   if constexpr (BITS == 4) {
     const uint32_t b0 = pair_byte(c0.w[blk], c1.w[blk], 2 * half), b1 = pair_byte(c0.w[blk], c1.w[blk], 2 * half + 1);
     x[0] = b0 & 0x000F000Fu;
     x[1] = b0 & 0x00F000F0u;
     x[2] = b1 & 0x000F000Fu;
     x[3] = b1 & 0x00F000F0u;
-    wq[0] = wq[1] = wq[2] = wq[3] = W;
   } else {
     const uint32_t b = pair_byte(c0.w[blk >> 1], c1.w[blk >> 1], 2 * half + (blk & 1));
     if constexpr (REF == 4) {
@@ -176,14 +172,17 @@ __device__ __forceinline__ void vpairs(const Words<BITS>& c0, const Words<BITS>&
       x[1] = b & 0x000C000Cu;
       x[2] = b4 & 0x00030003u;
       x[3] = b4 & 0x000C000Cu;
-      wq[0] = wq[2] = W;
-      wq[1] = wq[3] = W4;
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q) x[q] = b & (0x00030003u << (2 * q));
-      wq[0] = wq[1] = wq[2] = wq[3] = W;
     }
   }
+}
+
+// Whether field q of a BITS-wide component takes 4W under reference REF.
+template <int BITS, int REF>
+__host__ __device__ constexpr bool vw4(int q) {
+  return BITS == 2 && REF == 4 && (q & 1);
 }
 
 template <uint32_t CB, int c>
@@ -486,38 +485,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
     // by one ptilde (fp16-rounded p), so rounding W costs a relative 2^-11 of the value
     // rather than of its code part s c. Subnormal W (tiny contributions, or s == 0)
     // take the exact p beta o instead.
-    uint32_t Wc[NC], W4c[NC];
-    auto vweight = [&](auto& C, int c, auto bits_tag) {
-      constexpr int BB = decltype(bits_tag)::value;
+    // Weights in fp32: token t of component c contributes p_t beta_c (o + s c) to
+    // every element of the group. The code part goes through the mixed-precision
+    // FMA (fp16 code operand, fp32 weight p beta s, fp32 accumulate, one rounding)
+    // and the offset part into one sum per lane, both exact to fp32 rounding.
+    // (v_dot2c_f32_f16 would take two tokens per instruction with fp16 weights,
+    // but with subnormal operands it rounds a small addend into a large
+    // accumulator low by about two ulps, measured; over a long range that biased
+    // the outputs by 1e-3 at 16k tokens.)
+    float Wa[NC], Wb[NC];
+    auto vweight = [&](auto& C, int c) {
       const float pb0 = ok0 ? p0 * vb0[c] : 0.0f, pb1 = ok1 ? p1 * vb1[c] : 0.0f;
-      const float s0v = f16hi(C.vm0), s1v = f16hi(C.vm1), o0v = f16lo(C.vm0), o1v = f16lo(C.vm1);
-      const uint32_t W = pack_h2(fminf(pb0 * s0v * kWScale, kWMax), fminf(pb1 * s1v * kWScale, kWMax));
-      const float wb0 = f16lo(W), wb1 = f16hi(W);
-      bias += (wb0 >= kMinNormal) ? wb0 * (o0v * __builtin_amdgcn_rcpf(s0v)) * (1.0f / kWScale) : pb0 * o0v;
-      bias += (wb1 >= kMinNormal) ? wb1 * (o1v * __builtin_amdgcn_rcpf(s1v)) * (1.0f / kWScale) : pb1 * o1v;
-      Wc[c] = W;
-      W4c[c] = W;
-      if constexpr (BB == 2 && REF == 4)
-        W4c[c] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, W) * h2_t{(_Float16)4.0f, (_Float16)4.0f});
+      Wa[c] = pb0 * f16hi(C.vm0);
+      Wb[c] = pb1 * f16hi(C.vm1);
+      bias = fmaf(pb0, f16lo(C.vm0), bias);
+      bias = fmaf(pb1, f16lo(C.vm1), bias);
     };
-    vweight(T.c0, 0, std::integral_constant<int, cbits<CB, 0>()>{});
-    if constexpr (NC > 1) vweight(T.c1, 1, std::integral_constant<int, cbits<CB, 1>()>{});
-    if constexpr (NC > 2) vweight(T.c2, 2, std::integral_constant<int, cbits<CB, 2>()>{});
-    if constexpr (NC > 3) vweight(T.c3, 3, std::integral_constant<int, cbits<CB, 3>()>{});
+    vweight(T.c0, 0);
+    if constexpr (NC > 1) vweight(T.c1, 1);
+    if constexpr (NC > 2) vweight(T.c2, 2);
+    if constexpr (NC > 3) vweight(T.c3, 3);
 
 #pragma unroll
     for (int half = 0; half < 2; ++half)
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
-        uint32_t x[NC][4], wq[NC][4];
-        vpairs<cbits<CB, 0>(), REF>(T.c0.v0, T.c0.v1, half, blk, Wc[0], W4c[0], x[0], wq[0]);
-        if constexpr (NC > 1) vpairs<cbits<CB, 1>(), REF>(T.c1.v0, T.c1.v1, half, blk, Wc[1], W4c[1], x[1], wq[1]);
-        if constexpr (NC > 2) vpairs<cbits<CB, 2>(), REF>(T.c2.v0, T.c2.v1, half, blk, Wc[2], W4c[2], x[2], wq[2]);
-        if constexpr (NC > 3) vpairs<cbits<CB, 3>(), REF>(T.c3.v0, T.c3.v1, half, blk, Wc[3], W4c[3], x[3], wq[3]);
+        uint32_t x[NC][4];
+        vpairs<cbits<CB, 0>(), REF>(T.c0.v0, T.c0.v1, half, blk, x[0]);
+        if constexpr (NC > 1) vpairs<cbits<CB, 1>(), REF>(T.c1.v0, T.c1.v1, half, blk, x[1]);
+        if constexpr (NC > 2) vpairs<cbits<CB, 2>(), REF>(T.c2.v0, T.c2.v1, half, blk, x[2]);
+        if constexpr (NC > 3) vpairs<cbits<CB, 3>(), REF>(T.c3.v0, T.c3.v1, half, blk, x[3]);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int c = 0; c < NC; ++c) acc[16 * half + 4 * blk + q] = dot2(x[c][q], wq[c][q], acc[16 * half + 4 * blk + q]);
+        for (int q = 0; q < 4; ++q) {
+          float& a = acc[16 * half + 4 * blk + q];
+          auto comp = [&](int c, bool w4) {
+            a = fmaf(f16lo(x[c][q]), w4 ? 4.0f * Wa[c] : Wa[c], a);
+            a = fmaf(f16hi(x[c][q]), w4 ? 4.0f * Wb[c] : Wb[c], a);
+          };
+          comp(0, vw4<cbits<CB, 0>(), REF>(q));
+          if constexpr (NC > 1) comp(1, vw4<cbits<CB, (NC > 1 ? 1 : 0)>(), REF>(q));
+          if constexpr (NC > 2) comp(2, vw4<cbits<CB, (NC > 2 ? 2 : 0)>(), REF>(q));
+          if constexpr (NC > 3) comp(3, vw4<cbits<CB, (NC > 3 ? 3 : 0)>(), REF>(q));
+        }
       }
   };
   if constexpr (DEPTH == 2) {
@@ -550,7 +559,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
 
   float val[32];
 #pragma unroll
-  for (int e = 0; e < 32; ++e) val[e] = fmaf(acc[e], kTwo24 / (kWScale * vclass<REF>(e)), bias);
+  for (int e = 0; e < 32; ++e) val[e] = fmaf(acc[e], kTwo24 / vclass<REF>(e), bias);
   write_partial<D, 32, G, TPW>(val, (lane_on && gi == 0) ? lsum : 0.0f, m, lane_on, red, S,
                                p.part + ((size_t)bh * p.nsplit + split) * part_floats(D));
 }
