@@ -28,7 +28,7 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 RNE, RD, RU = 0, 1, 2
-LAST_LOOP, PREV_LOOP = 0, 1
+LAST_LOOP, PREV_LOOP, FIRST_LOOP = 0, 1, 2
 
 
 def build(force: bool = True) -> str:
@@ -42,9 +42,13 @@ def build(force: bool = True) -> str:
     return _LIB_PATH
 
 
+MAX_LOOPS = 32
+
+
 class _Cfg(ctypes.Structure):
     _fields_ = [("D", ctypes.c_int32), ("L", ctypes.c_int32), ("policy", ctypes.c_int32),
-                ("bits", ctypes.c_int32 * 16), ("group", ctypes.c_int32 * 16)]
+                ("loop_group", ctypes.c_int32),
+                ("bits", ctypes.c_int32 * MAX_LOOPS), ("group", ctypes.c_int32 * MAX_LOOPS)]
 
 
 def lib():
@@ -160,20 +164,27 @@ class Config:
     bits: list
     group: list | int = 32
     policy: int = LAST_LOOP
+    loop_group: int = 0                 # loops per anchor group; 0 = all loops one group
 
     @property
     def L(self) -> int:
         return len(self.bits)
 
+    @property
+    def G(self) -> int:
+        return self.loop_group or self.L
+
     def groups(self) -> list:
         return list(self.group) if isinstance(self.group, (list, tuple)) else [self.group] * self.L
 
-    def anchor(self) -> int:
-        return self.L - 1 if self.policy == LAST_LOOP else 0
+    def anchor(self, r: int = 0) -> int:
+        """Anchor loop of loop r's group (§3.2, §5 "Models")."""
+        g0 = r // self.G * self.G
+        return g0 + self.G - 1 if self.policy == LAST_LOOP else g0
 
     def c(self) -> _Cfg:
         c = _Cfg()
-        c.D, c.L, c.policy = self.D, self.L, self.policy
+        c.D, c.L, c.policy, c.loop_group = self.D, self.L, self.policy, self.loop_group
         for r, (b, g) in enumerate(zip(self.bits, self.groups())):
             c.bits[r] = b
             c.group[r] = g

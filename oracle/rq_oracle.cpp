@@ -94,8 +94,9 @@ double dot(int n, const double* a, const double* b) {
 bool bits_ok(int b) { return b == 2 || b == 4 || b == 8 || b == 16; }
 
 int check_cfg(const rqo_cfg* c) {
-  if (!c || c->D <= 0 || c->L < 1 || c->L > 16) return -1;
-  if (c->policy != RQO_LAST_LOOP && c->policy != RQO_PREV_LOOP) return -1;
+  if (!c || c->D <= 0 || c->L < 1 || c->L > RQO_MAX_LOOPS) return -1;
+  if (c->policy != RQO_LAST_LOOP && c->policy != RQO_PREV_LOOP && c->policy != RQO_FIRST_LOOP) return -1;
+  if (c->loop_group < 0 || (c->loop_group > 0 && c->L % c->loop_group != 0)) return -1;
   for (int r = 0; r < c->L; ++r) {
     if (!bits_ok(c->bits[r])) return -2;
     const int g = c->group[r];
@@ -104,7 +105,12 @@ int check_cfg(const rqo_cfg* c) {
   return 0;
 }
 
-int anchor_of(const rqo_cfg* c) { return c->policy == RQO_LAST_LOOP ? c->L - 1 : 0; }
+/* Loops per anchor group, the first loop of r's group and its anchor (§3.2, §5 "Models"). */
+int group_len(const rqo_cfg* c) { return c->loop_group > 0 ? c->loop_group : c->L; }
+int group_first(const rqo_cfg* c, int r) { return r / group_len(c) * group_len(c); }
+int anchor_of(const rqo_cfg* c, int r) {
+  return c->policy == RQO_LAST_LOOP ? group_first(c, r) + group_len(c) - 1 : group_first(c, r);
+}
 
 /* Quantize a whole D-vector group by group at loop r; returns the
  * dequantized vector D(c) in deq (§2.1). */
@@ -146,20 +152,20 @@ void dequant_row(const rqo_cfg* c, int r, const uint8_t* code_row, const uint16_
 void reconstruct_token(const rqo_cfg* c, int r, int t, const uint8_t* const* codes,
                        const uint16_t* const* meta, const uint16_t* const* alpha, double* z) {
   const int D = c->D;
-  const int a = anchor_of(c);
+  const int a = anchor_of(c, r);
   std::vector<double> res(D);
   auto row = [&](int loop, double* out) {
     dequant_row(c, loop, codes[loop] + (size_t)t * rqo_row_bytes(c, loop),
                 meta[loop] + (size_t)t * (D / c->group[loop]) * 2, out);
   };
   row(a, z);                                           /* anchor A */
-  if (c->policy == RQO_LAST_LOOP) {
-    if (r == a) return;
+  if (r == a) return;
+  if (c->policy != RQO_PREV_LOOP) {                    /* shared anchor */
     const double al = f16_decode(alpha[r][t]);
     row(r, res.data());
     for (int i = 0; i < D; ++i) z[i] = al * z[i] + res[i];   /* alpha_r A + D(c_r) */
   } else {
-    for (int j = 1; j <= r; ++j) {                     /* zhat_j = alpha_j zhat_{j-1} + D(c_j) */
+    for (int j = a + 1; j <= r; ++j) {                 /* zhat_j = alpha_j zhat_{j-1} + D(c_j) */
       const double al = f16_decode(alpha[j][t]);
       row(j, res.data());
       for (int i = 0; i < D; ++i) z[i] = al * z[i] + res[i];
@@ -298,8 +304,7 @@ int rqo_quantize_series(const rqo_cfg* c, const uint16_t* X, int T, const float*
                         double* delta, double* alpha_pre, double* pre_o, double* pre_s) {
   const int err = check_cfg(c);
   if (err) return err;
-  const int D = c->D, L = c->L;
-  const int a = anchor_of(c);
+  const int D = c->D, L = c->L, G = group_len(c);
   std::vector<double> x(D);
   std::vector<double> Z((size_t)L * D);                /* rotated loops of this token */
   std::vector<double> ref(D), E(D), deq(D);
@@ -316,26 +321,30 @@ int rqo_quantize_series(const rqo_cfg* c, const uint16_t* X, int T, const float*
       *psrow = pre_s ? pre_s + ((size_t)r * T + t) * D : nullptr;
     };
     uint8_t* crow; uint16_t* mrow; double *drow, *porow, *psrow;
-    /* anchor: quantized directly; its reconstruction is the reference (§3.2, App. G.1) */
-    out_ptrs(a, &crow, &mrow, &drow, &porow, &psrow);
-    quantize_vector(c, a, &Z[(size_t)a * D], crow, mrow, drow, porow, psrow, ref.data());
-    if (alpha_pre) alpha_pre[(size_t)a * T + t] = 0.0;
-    /* Last-loop: every other loop refers to the anchor; Previous-loop: loop r
-     * refers to the reconstruction of loop r-1, walking away from loop 1. */
-    for (int step = 1; step < L; ++step) {
-      const int r = (c->policy == RQO_LAST_LOOP) ? step - 1 : step;
-      const double* Zr = &Z[(size_t)r * D];
-      const double den = dot(D, ref.data(), ref.data());
-      const double al = den > 0.0 ? dot(D, Zr, ref.data()) / den : 0.0;   /* LS alpha (§3.2) */
-      const uint16_t al16 = f16_encode(al, RQO_RNE);
-      const double alt = f16_decode(al16);
-      alpha[r][t] = al16;
-      if (alpha_pre) alpha_pre[(size_t)r * T + t] = al;
-      for (int i = 0; i < D; ++i) E[i] = Zr[i] - alt * ref[i];           /* residual */
-      out_ptrs(r, &crow, &mrow, &drow, &porow, &psrow);
-      quantize_vector(c, r, E.data(), crow, mrow, drow, porow, psrow, deq.data());
-      if (c->policy == RQO_PREV_LOOP) {
-        for (int i = 0; i < D; ++i) ref[i] = alt * ref[i] + deq[i];    /* zhat_r, next reference */
+    for (int g0 = 0; g0 < L; g0 += G) {                /* each loop group independently (§5 "Models") */
+      const int a = anchor_of(c, g0);
+      /* anchor: quantized directly; its reconstruction is the reference (§3.2, App. G.1) */
+      out_ptrs(a, &crow, &mrow, &drow, &porow, &psrow);
+      quantize_vector(c, a, &Z[(size_t)a * D], crow, mrow, drow, porow, psrow, ref.data());
+      if (alpha_pre) alpha_pre[(size_t)a * T + t] = 0.0;
+      /* Last-loop / First-loop: every other loop of the group refers to the
+       * anchor; Previous-loop: loop r refers to the reconstruction of loop r-1,
+       * walking away from the group's first loop. */
+      for (int r = g0; r < g0 + G; ++r) {
+        if (r == a) continue;
+        const double* Zr = &Z[(size_t)r * D];
+        const double den = dot(D, ref.data(), ref.data());
+        const double al = den > 0.0 ? dot(D, Zr, ref.data()) / den : 0.0;   /* LS alpha (§3.2) */
+        const uint16_t al16 = f16_encode(al, RQO_RNE);
+        const double alt = f16_decode(al16);
+        alpha[r][t] = al16;
+        if (alpha_pre) alpha_pre[(size_t)r * T + t] = al;
+        for (int i = 0; i < D; ++i) E[i] = Zr[i] - alt * ref[i];           /* residual */
+        out_ptrs(r, &crow, &mrow, &drow, &porow, &psrow);
+        quantize_vector(c, r, E.data(), crow, mrow, drow, porow, psrow, deq.data());
+        if (c->policy == RQO_PREV_LOOP) {
+          for (int i = 0; i < D; ++i) ref[i] = alt * ref[i] + deq[i];    /* zhat_r, next reference */
+        }
       }
     }
   }

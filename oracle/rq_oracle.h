@@ -60,13 +60,21 @@ int rqo_pack_group(const uint16_t* codes, int g, int bits, uint8_t* out);
 int rqo_unpack_group(const uint8_t* in, int g, int bits, uint16_t* codes);
 
 /* ---- configuration of one cache series --------------------------------- */
-enum { RQO_LAST_LOOP = 0, RQO_PREV_LOOP = 1 };
+/* Reference policies (§3.2), applied within each loop group (§5 "Models":
+ * Huginn's 32 loops as eight independent groups of four, App. D):
+ *   RQO_LAST_LOOP:  anchor = last loop of the group, R_r = its reconstruction;
+ *   RQO_PREV_LOOP:  anchor = first loop of the group, R_r = reconstruction of
+ *                   loop r-1 (a chain);
+ *   RQO_FIRST_LOOP: anchor = first loop of the group, R_r = its reconstruction. */
+enum { RQO_LAST_LOOP = 0, RQO_PREV_LOOP = 1, RQO_FIRST_LOOP = 2 };
+#define RQO_MAX_LOOPS 32
 typedef struct {
   int32_t D;          /* head dimension */
-  int32_t L;          /* loops */
-  int32_t policy;     /* RQO_LAST_LOOP (anchor = loop L) or RQO_PREV_LOOP (anchor = loop 1, chained) */
-  int32_t bits[16];   /* bit width per loop (0-based loop index) */
-  int32_t group[16];  /* group size per loop (divides D) */
+  int32_t L;          /* loops, 1 .. RQO_MAX_LOOPS */
+  int32_t policy;     /* RQO_LAST_LOOP, RQO_PREV_LOOP or RQO_FIRST_LOOP */
+  int32_t loop_group; /* loops per anchor group (divides L); 0 = one group of all L loops */
+  int32_t bits[RQO_MAX_LOOPS];   /* bit width per loop (0-based loop index) */
+  int32_t group[RQO_MAX_LOOPS];  /* quantization group size per loop (divides D) */
 } rqo_cfg;
 
 /* Bytes of one token's packed codes for loop r: D * bits[r] / 8. */
@@ -85,8 +93,9 @@ int rqo_quantize_series(const rqo_cfg* c, const uint16_t* X, int T, const float*
                         double* delta, double* alpha_pre, double* pre_o, double* pre_s);
 
 /* Rebuild the rotated-domain reconstruction zhat of loop r for tokens [0, T):
- * out [T][D]. Last-loop: zhat_L = A, zhat_r = alpha_r * A + D(c_r).
- * Previous-loop: zhat_1 = A, zhat_r = alpha_r * zhat_{r-1} + D(c_r). */
+ * out [T][D]. With a the anchor of r's group: Last-loop and First-loop:
+ * zhat_a = A, zhat_r = alpha_r * A + D(c_r); Previous-loop: zhat_a = A,
+ * zhat_r = alpha_r * zhat_{r-1} + D(c_r) back to the group's first loop. */
 int rqo_reconstruct(const rqo_cfg* c, int r, int T, const uint8_t* const* codes,
                     const uint16_t* const* meta, const uint16_t* const* alpha, double* out);
 

@@ -40,23 +40,33 @@ def component_bytes(D: int, bits: int, group: int, meta_bytes_per_group: int = 4
     return D * bits // 8 + (D // group) * meta_bytes_per_group + (alpha_bytes if with_alpha else 0)
 
 
-def components_read(L: int, r: int, policy: str) -> list:
-    """Loops whose stored component loop r's reconstruction reads (App. D).
+def components_read(L: int, r: int, policy: str, loop_group: int = 0) -> list:
+    """Loops whose stored component loop r's reconstruction reads (App. D), within
+    r's loop group of loop_group loops (0: one group of all L loops; §5 "Models").
 
-    'last': the anchor (loop L) plus loop r's own residual; loop L reads the anchor only.
-    'prev': the anchor (loop 1) plus the residuals of loops 2..r (a chain).
+    'last':  the group's last loop is the anchor; loop r reads the anchor plus its
+             own residual; the anchor reads itself only.
+    'first': the same with the group's first loop as the anchor (§3.2).
+    'prev':  the group's first loop is the anchor and loop r reads the chain of
+             residuals back to it.
     Loops are 0-based here.
     """
+    G = loop_group or L
+    g0 = r // G * G
     if policy == "last":
-        return [L - 1] if r == L - 1 else [L - 1, r]
+        a = g0 + G - 1
+        return [a] if r == a else [a, r]
+    if policy == "first":
+        return [g0] if r == g0 else [g0, r]
     if policy == "prev":
-        return list(range(0, r + 1))
+        return list(range(g0, r + 1))
     raise ValueError(policy)
 
 
-def logical_reads(L: int, policy: str) -> int:
-    """Components read to reconstruct every loop once: 2L-1 shared, L(L+1)/2 chained."""
-    return sum(len(components_read(L, r, policy)) for r in range(L))
+def logical_reads(L: int, policy: str, loop_group: int = 0) -> int:
+    """Components read to reconstruct every loop once: 2G-1 shared or G(G+1)/2
+    chained per group of G loops."""
+    return sum(len(components_read(L, r, policy, loop_group)) for r in range(L))
 
 
 def decode_bytes_per_token(D: int, bits, group=32, policy: str = "last", meta_bytes_per_group: int = 4,

@@ -67,6 +67,11 @@ def test_logical_access_counts():
     assert round(S.logical_reads(32, "prev") / S.logical_reads(32, "last"), 2) == G["ratio_L32"]
     assert 8 * S.logical_reads(4, "prev") == G["reads_chain_8x4"]
     assert 8 * S.logical_reads(4, "last") == G["reads_shared_8x4"]
+    # 32 loops in eight groups of four, counted directly by the grouped model
+    assert S.logical_reads(32, "prev", loop_group=4) == G["reads_chain_8x4"]
+    assert S.logical_reads(32, "last", loop_group=4) == G["reads_shared_8x4"]
+    assert S.logical_reads(32, "first", loop_group=4) == G["reads_shared_8x4"]
+    assert S.logical_reads(4, "first") == G["reads_shared_L4"]
 
 
 def test_decode_bytes_closed_form():
