@@ -16,6 +16,11 @@ Reported next to it, in the same process and on the same logical inputs:
   * per-call HIP-event timing of the dominant call for the roofline;
   * the CPU oracle timed on a bounded sample (cpu_baseline).
 
+Other workloads of synth.WORKLOADS run with --workload, e.g. "huginn32_4k"
+(32 recurrences in eight anchor groups of four, D96, 55 heads); per-call
+timings then cover the loops of one group, and the counter-based traffic
+figure (taken for the default workload only) is null.
+
 Prints one JSON line (rank 0). --gpus N > 1 exits: this path runs on one GPU.
 """
 from __future__ import annotations
@@ -43,20 +48,32 @@ def comp_bytes(D, bits, with_alpha, group=32):
     return D * bits // 8 + (D // group) * 4 + (2 if with_alpha else 0)
 
 
-def call_bytes(D, bits, policy, r):
+def call_bytes(D, bits, policy, r, G=0):
     """Algorithmic HBM bytes one decode call of loop r reads per (b, h, cached token):
-    the stored components the reconstruction needs, K and V (fp16 meta and alpha)."""
-    L = len(bits)
+    the stored components the reconstruction needs, K and V (fp16 meta and alpha).
+    Loops form groups of G (0: one group) with an anchor each."""
+    G = G or len(bits)
+    g0 = r // G * G
     if policy == "last":
-        a = L - 1
+        a = g0 + G - 1
         comps = [a] if r == a else [a, r]
     else:
-        a = 0
-        comps = list(range(r + 1))
+        a = g0
+        comps = list(range(g0, r + 1))
     return 2 * sum(comp_bytes(D, bits[c], c != a) for c in comps)
 
 
-DOM_KERNEL = "decode_fused<128, 2, 36u, 2>"
+PROFILED_WORKLOAD = "ouro_16k"       # the workload the committed counter summaries cover
+
+
+def dom_kernel_name(D, bits, G):
+    """Instance name of the streaming kernel decoding loop 1 (anchor + loop-1 residual)."""
+    G = G or len(bits)
+    cb = bits[G - 1] | (bits[0] << 4)
+    return f"decode_fused<{D}, 2, {cb}u, 2>"
+
+
+DOM_KERNEL = dom_kernel_name(128, [2, 2, 4, 4], 0)
 COPY_KERNEL = "bitwise_not"
 COPY_KIB = float(1 << 20)            # 1 GiB read and 1 GiB written by the calibration kernel
 PROFILES = os.path.join(ROOT, "profiles")
@@ -93,10 +110,13 @@ def _read_counter_summary(path, counter):
     return src, vals
 
 
-def profiled_traffic(alg_bytes):
+def profiled_traffic(workload):
     """HBM bytes per launch of the dominant kernel from the committed FETCH_SIZE and
     WRITE_SIZE summaries, each scaled by the copy kernel's reading of its known size;
-    None when a summary is missing or was taken on other kernel sources."""
+    None for another workload, or when a summary is missing or was taken on other
+    kernel sources."""
+    if workload != PROFILED_WORKLOAD:
+        return None
     cur = kernel_source_hash()
     total, used = 0.0, []
     for path, counter in ((FETCH_FILE, "FETCH_SIZE"), (WRITE_FILE, "WRITE_SIZE")):
@@ -211,8 +231,10 @@ def main():
 
     # ---------------------------------------------------------------- build (untimed)
     t_build = time.time()
-    d_rq = rq.make_desc(B, H, D, bits, T_max, rq.POLICY_LAST_LOOP)
-    d_ch = rq.make_desc(B, H, D, cbits, T_max, rq.POLICY_PREV_LOOP)
+    G = w.loop_group
+    run_chained = not args.no_chained and (G or L) <= 4
+    d_rq = rq.make_desc(B, H, D, bits, T_max, rq.POLICY_LAST_LOOP, loop_group=G)
+    d_ch = rq.make_desc(B, H, D, cbits, T_max, rq.POLICY_PREV_LOOP, loop_group=G)
     caches, chained, bf16, rots = [], [], [], []
     kvcur = torch.empty(K, w.layers, 2, L, B, H, 1, D, dtype=torch.bfloat16, device=dev)
     qs = torch.empty(K, w.layers, L, B, H, D, dtype=torch.bfloat16, device=dev)
@@ -224,7 +246,7 @@ def main():
         c = rq.LayerCache.allocate(d_rq, rk, rv)
         rq.quantize_append(c, past, pos0, T)
         caches.append(c)
-        if not args.no_chained:
+        if run_chained:
             cc = rq.LayerCache.allocate(d_ch, rk, rv)
             rq.quantize_append(cc, past, pos0, T)
             chained.append(cc)
@@ -306,7 +328,7 @@ def main():
     log(f"RQ: {K} steps in {dt_rq * 1e3:.2f} ms")
     del g_rq
 
-    per_token_bytes = sum(call_bytes(D, bits, "last", r) for r in range(L)) * H * w.layers
+    per_token_bytes = sum(call_bytes(D, bits, "last", r, G) for r in range(L)) * H * w.layers
     mean_ctx = T + (K - 1) / 2.0
     step_bytes = per_token_bytes * B * mean_ctx
     result = {
@@ -314,19 +336,27 @@ def main():
         "warmup": args.warmup, "ms_per_step": dt_rq * 1e3 / K, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "layers": w.layers, "batch": B, "heads": H, "head_dim": D, "loops": L,
-                   "context": T, "bits": bits, "group": w.group, "codes": "int2/int4 + fp16 scale/offset + fp16 alpha",
-                   "arith": "fp16 dot2 products, fp32 accumulation"},
+                   "loop_group": G or L, "context": T, "bits": bits, "group": w.group,
+                   "codes": "int2/int4 + fp16 scale/offset + fp16 alpha",
+                   "arith": "keys: int8 dot products with a 14-bit fixed-point rotated query; values: fp32 "
+                            "multiply-adds of fp16-exact codes; fp32 softmax and accumulation"},
         "hbm_gbps_step": step_bytes / (dt_rq / K) / 1e9,
         "hbm_frac_step": step_bytes / (dt_rq / K) / 1e9 / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": step_bytes,
     }
 
-    if not args.no_chained:
+    chain_len = G or L
+    if not args.no_chained and chain_len > 4:
+        # the fused decode kernels take at most four stored components per call
+        log(f"chained comparator skipped: chains of {chain_len} components")
+        result["chained"] = {"policy": "previous-loop", "skipped": f"chains of {chain_len} components; the "
+                             "decode kernels read at most 4 per call"}
+    elif run_chained:
         log("capturing chained steps")
         g_ch = capture(lambda k: rq_step(k, chained, d_ch, ws_ch))
         dt_ch = run(g_ch, args.warmup)
         del g_ch
-        ch_bytes = sum(call_bytes(D, cbits, "prev", r) for r in range(L)) * H * w.layers * B * mean_ctx
+        ch_bytes = sum(call_bytes(D, cbits, "prev", r, G) for r in range(L)) * H * w.layers * B * mean_ctx
         result["chained"] = {"policy": "previous-loop", "bits": cbits, "value": B * K / dt_ch,
                              "unit": "tokens/s", "ms_per_step": dt_ch * 1e3 / K,
                              "hbm_gbps_step": ch_bytes / (dt_ch / K) / 1e9,
@@ -373,10 +403,10 @@ def main():
         return sorted(times)[2]          # median of five replays
 
     percall = {}
-    for r in range(L):
+    for r in range(G or L):                       # every loop group has the same shape
         kc = kvcur[0, 0, 0, r, :, :, 0]
         vc = kvcur[0, 0, 1, r, :, :, 0]
-        nbytes = call_bytes(D, bits, "last", r) * B * H * T
+        nbytes = call_bytes(D, bits, "last", r, G) * B * H * T
         ms_k = events(lambda i: rq.decode_attn_partial(caches[i % w.layers], r, qs[0, 0, r], past_len, scale, ws))
         ms_c = events(lambda i: rq.decode_combine(d_rq, caches[i % w.layers].rot[1], qs[0, 0, r], kc, vc, past_len,
                                                   scale, out[0, r], ws))
@@ -385,12 +415,12 @@ def main():
         percall[r] = {"kernel_ms": ms_k, "combine_ms": ms_c, "call_ms": ms_call, "bytes": nbytes,
                       "kernel_gbps": nbytes / (ms_k * 1e-3) / 1e9}
     dom = percall[0]
-    traffic = profiled_traffic(dom["bytes"])
+    traffic = profiled_traffic(w.name)
     result["roofline"] = {"bound": "hbm", "achieved": dom["kernel_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                           "frac": dom["kernel_gbps"] / HBM_PEAK_GBPS,
                           "traffic": None if traffic is None else traffic["bytes"],
-                          "kernel": DOM_KERNEL + " (rq_decode_attn_partial, loop 1: INT4 anchor + INT2 residual, "
-                                                 "K and V)",
+                          "kernel": dom_kernel_name(D, bits, G) + " (rq_decode_attn_partial, loop 1: "
+                                    f"INT{bits[(G or L) - 1]} anchor + INT{bits[0]} residual, K and V)",
                           "bytes_per_launch": dom["bytes"], "ms_per_launch": dom["kernel_ms"],
                           "traffic_source": None if traffic is None else traffic["source"]}
     result["per_call"] = {f"loop{r + 1}": v for r, v in percall.items()}
@@ -431,7 +461,7 @@ def cpu_baseline(w, bits, units, min_seconds, torch, synth, scale):
     u16 = lambda t: t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
     Xh = {p: u16(X[:, :, p[0], p[1]]) for p in pairs}
     qn = [u16(synth.query(w, 0, r, 0, device="cpu")) for r in range(L)]
-    cfg = O.Config(D=D, bits=list(bits))
+    cfg = O.Config(D=D, bits=list(bits), loop_group=w.loop_group)
     t0 = time.time()
 
     def build(p):

@@ -18,13 +18,13 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librq.so")
-MAX_LOOPS = 16
+MAX_LOOPS = 32
 
 OK = 0
 STATUS = {0: "RQ_OK", 1: "RQ_E_NULL", 2: "RQ_E_SHAPE", 3: "RQ_E_BITS", 4: "RQ_E_CAPACITY",
           5: "RQ_E_WORKSPACE", 6: "RQ_E_UNSUPPORTED", 7: "RQ_E_HIP", 8: "RQ_E_POLICY", 9: "RQ_E_LOOP",
           10: "RQ_E_ALIGN"}
-POLICY_LAST_LOOP, POLICY_PREV_LOOP = 0, 1
+POLICY_LAST_LOOP, POLICY_PREV_LOOP, POLICY_FIRST_LOOP = 0, 1, 2
 DEVERR_CAPACITY, DEVERR_LENGTH = 1, 2
 
 
@@ -37,7 +37,7 @@ class RQError(RuntimeError):
 class Desc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("loops", ctypes.c_int32), ("max_tokens", ctypes.c_int32), ("policy", ctypes.c_int32),
-                ("bits", ctypes.c_uint8 * MAX_LOOPS), ("group", ctypes.c_uint8 * MAX_LOOPS)]
+                ("loop_group", ctypes.c_int32), ("bits", ctypes.c_uint8 * MAX_LOOPS), ("group", ctypes.c_uint8 * MAX_LOOPS)]
 
 
 class LayerCacheC(ctypes.Structure):
@@ -90,14 +90,21 @@ def version() -> str:
 
 
 def make_desc(batch: int, heads: int, head_dim: int, bits, max_tokens: int,
-              policy: int = POLICY_LAST_LOOP, group: int = 32) -> Desc:
+              policy: int = POLICY_LAST_LOOP, group: int = 32, loop_group: int = 0) -> Desc:
     d = Desc()
     d.batch, d.heads, d.head_dim = batch, heads, head_dim
-    d.loops, d.max_tokens, d.policy = len(bits), max_tokens, policy
+    d.loops, d.max_tokens, d.policy, d.loop_group = len(bits), max_tokens, policy, loop_group
     for r, b in enumerate(bits):
         d.bits[r] = b
         d.group[r] = group
     return d
+
+
+def anchor_of(d: Desc, r: int) -> int:
+    """Anchor loop of the loop group holding loop r (the rule stated in rq.h)."""
+    G = d.loop_group or d.loops
+    g0 = r // G * G
+    return g0 + G - 1 if d.policy == POLICY_LAST_LOOP else g0
 
 
 def check_desc(d: Desc) -> int:
@@ -145,18 +152,17 @@ class LayerCache:
     desc: Desc
     codes: list      # [2][L] uint8 tensors [B][H][T_max][D*bits/8]
     meta: list       # [2][L] int16 tensors [B][H][T_max][D/32][2] (fp16 bit patterns)
-    alpha: list      # [2][L] int16 tensors [B][H][T_max] or None for the anchor
+    alpha: list      # [2][L] int16 tensors [B][H][T_max] or None for a group's anchor
     rot: list        # [2] float32 [H][D][D]
 
     @staticmethod
     def allocate(d: Desc, rot_k: torch.Tensor, rot_v: torch.Tensor, device="cuda") -> "LayerCache":
         B, H, T, D, L = d.batch, d.heads, d.max_tokens, d.head_dim, d.loops
-        anchor = L - 1 if d.policy == POLICY_LAST_LOOP else 0
         codes = [[torch.empty(B, H, T, D * d.bits[r] // 8, dtype=torch.uint8, device=device)
                   for r in range(L)] for _ in range(2)]
         meta = [[torch.empty(B, H, T, D // d.group[r], 2, dtype=torch.int16, device=device)
                  for r in range(L)] for _ in range(2)]
-        alpha = [[None if r == anchor else torch.empty(B, H, T, dtype=torch.int16, device=device)
+        alpha = [[None if r == anchor_of(d, r) else torch.empty(B, H, T, dtype=torch.int16, device=device)
                   for r in range(L)] for _ in range(2)]
         rot = [rot_k.to(device=device, dtype=torch.float32).contiguous(),
                rot_v.to(device=device, dtype=torch.float32).contiguous()]

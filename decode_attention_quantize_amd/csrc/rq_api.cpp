@@ -64,7 +64,10 @@ rq_status check_shape(const rq_desc* d) {
 rq_status check_plan(const rq_desc* d) {
   rq_status s = check_shape(d);
   if (s != RQ_OK) return s;
-  if (d->policy != RQ_POLICY_LAST_LOOP && d->policy != RQ_POLICY_PREV_LOOP) return RQ_E_POLICY;
+  if (d->policy != RQ_POLICY_LAST_LOOP && d->policy != RQ_POLICY_PREV_LOOP && d->policy != RQ_POLICY_FIRST_LOOP)
+    return RQ_E_POLICY;
+  if (d->loop_group < 0 || d->loop_group > d->loops || (d->loop_group > 0 && d->loops % d->loop_group != 0))
+    return RQ_E_SHAPE;
   for (int r = 0; r < d->loops; ++r) {
     if (d->bits[r] != 2 && d->bits[r] != 4) return RQ_E_BITS;
     if (d->group[r] != 32) return RQ_E_BITS;
@@ -72,7 +75,15 @@ rq_status check_plan(const rq_desc* d) {
   return RQ_OK;
 }
 
-int anchor_loop(const rq_desc* d) { return d->policy == RQ_POLICY_LAST_LOOP ? d->loops - 1 : 0; }
+// Loops per anchor group (loop_group 0 = one group of all loops).
+int group_len(const rq_desc* d) { return d->loop_group > 0 ? d->loop_group : d->loops; }
+
+// Anchor of the group holding loop r (0-based): its last loop under Last-loop,
+// its first under First-loop and Previous-loop (§3.2; §5 "Models").
+int anchor_of(const rq_desc* d, int r) {
+  const int G = group_len(d), g0 = r / G * G;
+  return d->policy == RQ_POLICY_LAST_LOOP ? g0 + G - 1 : g0;
+}
 
 size_t workspace_for(const rq_desc* d) {
   const SplitPlan sp = split_plan(d);
@@ -101,17 +112,18 @@ CombineParams combine_params(const rq_desc* d, void* ws, const uint16_t* q, cons
   return a;
 }
 
-// Components decode loop r reads, in order anchor first (§3.2, App. D).
+// Components decode loop r reads, anchor first (§3.2, App. D): the shared
+// anchor and r itself, or the chain from the group's first loop up to r.
 int components(const rq_desc* d, int r, int* loops) {
-  if (d->policy == RQ_POLICY_LAST_LOOP) {
-    const int a = d->loops - 1;
+  const int a = anchor_of(d, r);
+  if (d->policy != RQ_POLICY_PREV_LOOP) {
     loops[0] = a;
     if (r == a) return 1;
     loops[1] = r;
     return 2;
   }
-  for (int c = 0; c <= r; ++c) loops[c] = c;
-  return r + 1;
+  for (int c = a; c <= r; ++c) loops[c - a] = c;
+  return r - a + 1;
 }
 
 }  // namespace
@@ -122,7 +134,7 @@ const char* rq_status_str(rq_status s) {
   switch (s) {
     case RQ_OK: return "ok";
     case RQ_E_NULL: return "required pointer is NULL";
-    case RQ_E_SHAPE: return "shape out of range (batch, heads, head_dim in {64,96,128}, loops 1..16, max_tokens >= 1, n)";
+    case RQ_E_SHAPE: return "shape out of range (batch, heads, head_dim in {64,96,128}, loops 1..32, loop_group 0 or a divisor of loops, max_tokens >= 1, n)";
     case RQ_E_BITS: return "unsupported bit width or group size (bits 2 or 4, group 32)";
     case RQ_E_CAPACITY: return "size exceeds max_tokens";
     case RQ_E_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
@@ -165,14 +177,14 @@ rq_status rq_quantize_append(const rq_desc* d, const rq_layer_cache* c, const ui
   if (n == 0) return RQ_OK;
   if (!kv || !pos || !c->rot[0] || !c->rot[1]) return RQ_E_NULL;
   if (!al(kv, 16) || !al(pos, 4) || !al(c->rot[0], 16) || !al(c->rot[1], 16)) return RQ_E_ALIGN;
-  const int a = anchor_loop(d);
   AppendParams p;
   std::memset(&p, 0, sizeof(p));
   for (int kvi = 0; kvi < 2; ++kvi) {
     for (int r = 0; r < d->loops; ++r) {
       if (!c->codes[kvi][r] || !c->meta[kvi][r]) return RQ_E_NULL;
-      if (r != a && !c->alpha[kvi][r]) return RQ_E_NULL;
-      if (!al(c->codes[kvi][r], 16) || !al(c->meta[kvi][r], 4) || (r != a && !al(c->alpha[kvi][r], 2)))
+      const bool anchor = r == anchor_of(d, r);
+      if (!anchor && !c->alpha[kvi][r]) return RQ_E_NULL;
+      if (!al(c->codes[kvi][r], 16) || !al(c->meta[kvi][r], 4) || (!anchor && !al(c->alpha[kvi][r], 2)))
         return RQ_E_ALIGN;
       p.codes[kvi][r] = c->codes[kvi][r];
       p.meta[kvi][r] = reinterpret_cast<uint32_t*>(c->meta[kvi][r]);
@@ -189,6 +201,7 @@ rq_status rq_quantize_append(const rq_desc* d, const rq_layer_cache* c, const ui
   p.n = n;
   p.T_max = d->max_tokens;
   p.policy = d->policy;
+  p.G = group_len(d);
   for (int r = 0; r < d->loops; ++r) p.bits[r] = d->bits[r];
   return launch_append(p, d->head_dim, stream) == 0 ? RQ_OK : RQ_E_HIP;
 }

@@ -18,7 +18,8 @@
 namespace rq {
 namespace {
 
-// Appends of at most this many tokens per sequence take the per-unit path.
+// Appends of at most this many tokens per sequence take the per-unit path (as
+// do all appends with more than 16 loops, whose units do not fit a 16-row tile).
 constexpr int kUnitAppendMaxN = 8;
 
 typedef double d4 __attribute__((ext_vector_type(4)));
@@ -185,28 +186,30 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     }
     const size_t tok = ((size_t)b * p.H + h) * p.T_max + t;
     const double(*Z)[D + 1] = &Zs[wave][uu * L];
-    const int a = (p.policy == RQ_POLICY_LAST_LOOP) ? L - 1 : 0;
-    double r0, r1;  // reference (reconstructed anchor, or previous loop) at e0, e1
-    quantize_pair<D>(Z[a][e0], Z[a][e1], p.bits[a], lane_on, gi, k, p.codes[kv][a], p.meta[kv][a], tok, r0,
-                     r1);
-    if (!lane_on) r0 = r1 = 0.0;
-    const double den = wave_sum_f64(r0 * r0 + r1 * r1);
-    double den_cur = den;
-    for (int step = 1; step < L; ++step) {
-      const int r = (p.policy == RQ_POLICY_LAST_LOOP) ? step - 1 : step;
-      const double z0 = lane_on ? Z[r][e0] : 0.0, z1 = lane_on ? Z[r][e1] : 0.0;
-      const double num = wave_sum_f64(z0 * r0 + z1 * r1);
-      const double alpha = den_cur > 0.0 ? num / den_cur : 0.0;
-      const uint16_t a16 = f64_to_f16(alpha, 0);
-      const double at = f16_to_f64(a16);
-      if (lane == 0) p.alpha[kv][r][tok] = a16;
-      double q0, q1;
-      quantize_pair<D>(z0 - at * r0, z1 - at * r1, p.bits[r], lane_on, gi, k, p.codes[kv][r], p.meta[kv][r],
-                       tok, q0, q1);
-      if (p.policy == RQ_POLICY_PREV_LOOP) {    // zhat_r = alpha_r zhat_{r-1} + D(c_r)
-        r0 = lane_on ? at * r0 + q0 : 0.0;
-        r1 = lane_on ? at * r1 + q1 : 0.0;
-        den_cur = wave_sum_f64(r0 * r0 + r1 * r1);
+    // each loop group independently: its anchor, then the other loops of the group
+    for (int g0 = 0; g0 < L; g0 += p.G) {
+      const int a = (p.policy == RQ_POLICY_LAST_LOOP) ? g0 + p.G - 1 : g0;
+      double r0, r1;  // reference (reconstructed anchor, or previous loop) at e0, e1
+      quantize_pair<D>(Z[a][e0], Z[a][e1], p.bits[a], lane_on, gi, k, p.codes[kv][a], p.meta[kv][a], tok, r0,
+                       r1);
+      if (!lane_on) r0 = r1 = 0.0;
+      double den_cur = wave_sum_f64(r0 * r0 + r1 * r1);
+      for (int r = g0; r < g0 + p.G; ++r) {
+        if (r == a) continue;
+        const double z0 = lane_on ? Z[r][e0] : 0.0, z1 = lane_on ? Z[r][e1] : 0.0;
+        const double num = wave_sum_f64(z0 * r0 + z1 * r1);
+        const double alpha = den_cur > 0.0 ? num / den_cur : 0.0;
+        const uint16_t a16 = f64_to_f16(alpha, 0);
+        const double at = f16_to_f64(a16);
+        if (lane == 0) p.alpha[kv][r][tok] = a16;
+        double q0, q1;
+        quantize_pair<D>(z0 - at * r0, z1 - at * r1, p.bits[r], lane_on, gi, k, p.codes[kv][r], p.meta[kv][r],
+                         tok, q0, q1);
+        if (p.policy == RQ_POLICY_PREV_LOOP) {  // zhat_r = alpha_r zhat_{r-1} + D(c_r)
+          r0 = lane_on ? at * r0 + q0 : 0.0;
+          r1 = lane_on ? at * r1 + q1 : 0.0;
+          den_cur = wave_sum_f64(r0 * r0 + r1 * r1);
+        }
       }
     }
   }
@@ -217,28 +220,25 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 // the head's rotation in LDS once; wave w computes Z_r for its loops
 // r = w, w + 4, .. on the fp64 vector units (lane k of group gi holds channels
 // e0 = 32 gi + k and e1 = e0 + 16, the pair quantize_pair takes), so the four
-// waves rotate in parallel and the quantization steps follow the policy's
-// dependency order with one barrier per step.
-__device__ __forceinline__ double pick(const double (&v)[4], int j) {
-  double r = v[0];
-  r = j == 1 ? v[1] : r;
-  r = j == 2 ? v[2] : r;
-  r = j == 3 ? v[3] : r;
-  return r;
-}
-
-template <int D>
+// waves rotate in parallel. Then every loop group's anchor is quantized, and
+// the other loops follow in the policy's dependency order: all at once against
+// the shared anchor (Last-loop, First-loop), or one chain step per barrier
+// (Previous-loop, all groups together). LM bounds the loop count: the LDS
+// footprint grows with it, and at most 8 loops leave room for two workgroups
+// per compute unit at D = 128.
+template <int D, int LM>
 __global__ __launch_bounds__(256) void append_unit(AppendParams p) {
+  constexpr int kLoopsPerWave = LM / kWaves;
   constexpr int HS = D + 2;                // padded LDS row: 8-byte aligned pairs, 16 rows cover all banks
   constexpr int NF = D * D / 4 / kThreads; // float4 per thread of the rotation
   static_assert(NF * 4 * kThreads == D * D, "rotation staging must tile the block");
   __shared__ float Hs[D * HS];
-  __shared__ float xs[RQ_MAX_LOOPS][D];
-  __shared__ double rec[D];                // current reference (reconstruction)
-  __shared__ double dens;                  // its squared norm
+  __shared__ float xs[LM][D];
+  __shared__ double rec[LM][D];            // per loop group: current reference (reconstruction)
+  __shared__ double dens[LM];              // its squared norm
   const int u = blockIdx.x, h = blockIdx.y, kv = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int L = p.L;
+  const int L = p.L, G = p.G;
   const int b = u / p.n, i = u % p.n;
   const int t = p.pos[b] + i;
   if (t < 0 || t >= p.T_max) {             // whole block, before any barrier
@@ -252,13 +252,6 @@ __global__ __launch_bounds__(256) void append_unit(AppendParams p) {
     float4 hv[NF];
 #pragma unroll
     for (int j = 0; j < NF; ++j) hv[j] = Hg[tid + j * kThreads];
-    uint4 xv = {0u, 0u, 0u, 0u};
-    const int xr = tid / (D / 8), xc = tid % (D / 8);
-    const bool x_on = xr < L;
-    if (x_on) {
-      const uint16_t* row = p.kv + (((((size_t)kv * L + xr) * p.B + b) * p.H + h) * p.n + i) * (size_t)D;
-      xv = reinterpret_cast<const uint4*>(row)[xc];
-    }
 #pragma unroll
     for (int j = 0; j < NF; ++j) {
       const int f = 4 * (tid + j * kThreads), n = f / D, k = f % D;
@@ -266,7 +259,10 @@ __global__ __launch_bounds__(256) void append_unit(AppendParams p) {
       dst[0] = make_float2(hv[j].x, hv[j].y);
       dst[1] = make_float2(hv[j].z, hv[j].w);
     }
-    if (x_on) {
+    for (int idx = tid; idx < L * (D / 8); idx += kThreads) {
+      const int xr = idx / (D / 8), xc = idx % (D / 8);
+      const uint16_t* row = p.kv + (((((size_t)kv * L + xr) * p.B + b) * p.H + h) * p.n + i) * (size_t)D;
+      const uint4 xv = reinterpret_cast<const uint4*>(row)[xc];
       const uint32_t w[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -281,15 +277,16 @@ __global__ __launch_bounds__(256) void append_unit(AppendParams p) {
   const int gi = lane >> 4, kk = lane & 15;
   const bool lane_on = gi < D / 32;
   const int e0 = lane_on ? 32 * gi + kk : 0, e1 = e0 + 16;
-  double z0[4], z1[4];
+  double z0[kLoopsPerWave], z1[kLoopsPerWave];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = wave + 4 * j;
+  for (int j = 0; j < kLoopsPerWave; ++j) {
+    const int r = wave + kWaves * j;
     double a0 = 0.0, a1 = 0.0, c0 = 0.0, c1 = 0.0;
     if (r < L) {
       const float* x = xs[r];
       const float* h0 = &Hs[e0 * HS];
       const float* h1 = &Hs[e1 * HS];
+#pragma unroll 4
       for (int k = 0; k < D; k += 2) {
         const float2 xv = *reinterpret_cast<const float2*>(&x[k]);
         const float2 u0 = *reinterpret_cast<const float2*>(&h0[k]);
@@ -306,30 +303,34 @@ __global__ __launch_bounds__(256) void append_unit(AppendParams p) {
   }
 
   const size_t tok = ((size_t)b * p.H + h) * p.T_max + t;
-  const bool last = p.policy == RQ_POLICY_LAST_LOOP;
-  const int a = last ? L - 1 : 0;
+  const bool last = p.policy == RQ_POLICY_LAST_LOOP, chain = p.policy == RQ_POLICY_PREV_LOOP;
+  auto anchor_of = [&](int r) { return last ? r / G * G + G - 1 : r / G * G; };
 
-  // ---- anchor
-  if (wave == (a & 3)) {
-    const int j = a >> 2;
-    double r0, r1;
-    quantize_pair<D>(pick(z0, j), pick(z1, j), p.bits[a], lane_on, gi, kk, p.codes[kv][a], p.meta[kv][a],
-                     tok, r0, r1);
-    if (!lane_on) r0 = r1 = 0.0;
-    const double den = wave_sum_f64(r0 * r0 + r1 * r1);
-    if (lane_on) {
-      rec[e0] = r0;
-      rec[e1] = r1;
+  // ---- anchors of every group (by the waves that own them)
+#pragma unroll
+  for (int j = 0; j < kLoopsPerWave; ++j) {
+    const int r = wave + kWaves * j;
+    if (r < L && r == anchor_of(r)) {
+      double r0, r1;
+      quantize_pair<D>(z0[j], z1[j], p.bits[r], lane_on, gi, kk, p.codes[kv][r], p.meta[kv][r], tok, r0, r1);
+      if (!lane_on) r0 = r1 = 0.0;
+      const double den = wave_sum_f64(r0 * r0 + r1 * r1);
+      if (lane_on) {
+        rec[r / G][e0] = r0;
+        rec[r / G][e1] = r1;
+      }
+      if (lane == 0) dens[r / G] = den;
     }
-    if (lane == 0) dens = den;
   }
   __syncthreads();
 
-  // ---- one residual: alpha against the reference in rec, then Q(Z_r - alpha ref)
-  auto residual = [&](int r, double zz0, double zz1, double& q0, double& q1, double& at, double& r0, double& r1) {
-    r0 = lane_on ? rec[e0] : 0.0;
-    r1 = lane_on ? rec[e1] : 0.0;
-    const double den = dens;
+  // ---- one residual: alpha against the group's reference, then Q(Z_r - alpha ref)
+  auto residual = [&](int r, double zz0, double zz1, double& q0, double& q1, double& at, double& r0,
+                      double& r1) __attribute__((always_inline)) {
+    const int g = r / G;
+    r0 = lane_on ? rec[g][e0] : 0.0;
+    r1 = lane_on ? rec[g][e1] : 0.0;
+    const double den = dens[g];
     const double num = wave_sum_f64((lane_on ? zz0 : 0.0) * r0 + (lane_on ? zz1 : 0.0) * r1);
     const double alpha = den > 0.0 ? num / den : 0.0;
     const uint16_t a16 = f64_to_f16(alpha, 0);
@@ -339,30 +340,33 @@ __global__ __launch_bounds__(256) void append_unit(AppendParams p) {
                      q0, q1);
   };
 
-  if (last) {
-    // every residual refers to the anchor: the waves work in parallel
+  if (!chain) {
+    // shared anchor: the waves work on all their loops at once
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wave + 4 * j;
-      if (r < L - 1) {
+    for (int j = 0; j < kLoopsPerWave; ++j) {
+      const int r = wave + kWaves * j;
+      if (r < L && r != anchor_of(r)) {
         double q0, q1, at, r0, r1;
         residual(r, z0[j], z1[j], q0, q1, at, r0, r1);
       }
     }
   } else {
-    // a chain: loop r refers to the reconstruction of loop r - 1
-    for (int r = 1; r < L; ++r) {
-      if (wave == (r & 3)) {
-        const int j = r >> 2;
-        double q0, q1, at, r0, r1;
-        residual(r, pick(z0, j), pick(z1, j), q0, q1, at, r0, r1);
-        const double n0 = lane_on ? at * r0 + q0 : 0.0, n1 = lane_on ? at * r1 + q1 : 0.0;
-        const double den = wave_sum_f64(n0 * n0 + n1 * n1);
-        if (lane_on) {
-          rec[e0] = n0;
-          rec[e1] = n1;
+    // a chain in every group: step st handles loop g G + st of each group g
+    for (int st = 1; st < G; ++st) {
+#pragma unroll
+      for (int j = 0; j < kLoopsPerWave; ++j) {
+        const int r = wave + kWaves * j;
+        if (r < L && r % G == st) {
+          double q0, q1, at, r0, r1;
+          residual(r, z0[j], z1[j], q0, q1, at, r0, r1);
+          const double n0 = lane_on ? at * r0 + q0 : 0.0, n1 = lane_on ? at * r1 + q1 : 0.0;
+          const double den = wave_sum_f64(n0 * n0 + n1 * n1);
+          if (lane_on) {
+            rec[r / G][e0] = n0;
+            rec[r / G][e1] = n1;
+          }
+          if (lane == 0) dens[r / G] = den;
         }
-        if (lane == 0) dens = den;
       }
       __syncthreads();
     }
@@ -373,12 +377,22 @@ __global__ __launch_bounds__(256) void append_unit(AppendParams p) {
 
 int launch_append(const AppendParams& p, int D, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (p.n <= kUnitAppendMaxN) {
+  if (p.n <= kUnitAppendMaxN || p.L > 16) {
     const dim3 grid((unsigned)(p.B * p.n), (unsigned)p.H, 2);
+    const bool small = p.L <= 8;
     switch (D) {
-      case 64: hipLaunchKernelGGL(append_unit<64>, grid, dim3(kThreads), 0, s, p); break;
-      case 96: hipLaunchKernelGGL(append_unit<96>, grid, dim3(kThreads), 0, s, p); break;
-      case 128: hipLaunchKernelGGL(append_unit<128>, grid, dim3(kThreads), 0, s, p); break;
+      case 64:
+        if (small) hipLaunchKernelGGL((append_unit<64, 8>), grid, dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((append_unit<64, RQ_MAX_LOOPS>), grid, dim3(kThreads), 0, s, p);
+        break;
+      case 96:
+        if (small) hipLaunchKernelGGL((append_unit<96, 8>), grid, dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((append_unit<96, RQ_MAX_LOOPS>), grid, dim3(kThreads), 0, s, p);
+        break;
+      case 128:
+        if (small) hipLaunchKernelGGL((append_unit<128, 8>), grid, dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((append_unit<128, RQ_MAX_LOOPS>), grid, dim3(kThreads), 0, s, p);
+        break;
       default: return -1;
     }
     return (int)hipGetLastError();

@@ -99,6 +99,7 @@ struct AppendParams {
   const int32_t* pos;
   int32_t* dev_err;
   int B, H, L, n, T_max, policy;
+  int G;                    // loops per anchor group (divides L)
   int bits[RQ_MAX_LOOPS];
 };
 

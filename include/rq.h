@@ -5,8 +5,9 @@
  * Transformers with 2-Bit Residuals" (ResidualQuant); section numbers below
  * refer to it. A looped Transformer produces keys/values X_r for every loop
  * r = 1..L. The cache stores
- *   - an anchor (loop L under the Last-loop policy, §3.2), group-quantized in
- *     the rotated domain: A = D(Q(H X_L));
+ *   - an anchor (loop L under the Last-loop policy, §3.2; with loop groups,
+ *     one anchor per group), group-quantized in the rotated domain:
+ *     A = D(Q(H X_L));
  *   - for every other loop r, a least-squares coefficient
  *     alpha_r = <Z_r, A> / |A|^2 (Z_r = H X_r, stored fp16; §3.2 "Scaling
  *     coefficient", App. G.1) and the group-quantized rotated residual
@@ -49,7 +50,7 @@
 extern "C" {
 #endif
 
-#define RQ_MAX_LOOPS 16
+#define RQ_MAX_LOOPS 32
 
 typedef enum {
   RQ_OK = 0,
@@ -69,12 +70,17 @@ typedef enum {
 #define RQ_DEVERR_CAPACITY 1  /* append: pos[b] + n > max_tokens; tokens past capacity were dropped */
 #define RQ_DEVERR_LENGTH 2    /* decode: past_len[b] outside [0, max_tokens]; it was clamped */
 
-/* Reference policy (§3.2, App. D).
- * LAST_LOOP: the anchor is loop L; loop r < L stores Q(Z_r - alpha_r A).
- * PREV_LOOP: the anchor is loop 1; loop r > 1 refers to the reconstruction of
- *   loop r-1 (a chain: zhat_r = alpha_r zhat_{r-1} + D(c_r)), so decoding loop r
- *   reads r stored components. Kept as the comparator the paper measures against. */
-typedef enum { RQ_POLICY_LAST_LOOP = 0, RQ_POLICY_PREV_LOOP = 1 } rq_policy;
+/* Reference policy (§3.2, App. D), applied inside every loop group (see
+ * rq_desc.loop_group; by default all L loops form one group).
+ * LAST_LOOP: the anchor is the group's last loop; every other loop r of the
+ *   group stores Q(Z_r - alpha_r A). Decoding loop r reads two components.
+ * FIRST_LOOP: the same with the group's first loop as anchor (§3.2 "Reference
+ *   KV": the shared-anchor alternative to Previous-loop; ablated in Table 3).
+ * PREV_LOOP: the anchor is the group's first loop; loop r refers to the
+ *   reconstruction of loop r-1 (a chain: zhat_r = alpha_r zhat_{r-1} + D(c_r)),
+ *   so decoding the j-th loop of a group reads j stored components (the decode
+ *   kernels take at most 4). Kept as the comparator the paper measures against. */
+typedef enum { RQ_POLICY_LAST_LOOP = 0, RQ_POLICY_PREV_LOOP = 1, RQ_POLICY_FIRST_LOOP = 2 } rq_policy;
 
 /* Shapes and the quantization plan of one layer's cache. */
 typedef struct {
@@ -84,6 +90,9 @@ typedef struct {
   int32_t loops;       /* L: 1 .. RQ_MAX_LOOPS */
   int32_t max_tokens;  /* T_max >= 1: token capacity of every cache buffer */
   int32_t policy;      /* rq_policy */
+  int32_t loop_group;  /* G: loops per anchor group; 0 = all L loops form one group, else a divisor of L.
+                        * Loops gG .. gG+G-1 (0-based) are quantized against an anchor of their own
+                        * (§5 "Models": a model with many loops, e.g. 32, split into groups of 4). */
   uint8_t bits[RQ_MAX_LOOPS];   /* bit width per loop (0-based), 2 or 4 (§2.1, §3.4) */
   uint8_t group[RQ_MAX_LOOPS];  /* group size per loop along the rotated head_dim: 32 */
 } rq_desc;
@@ -101,7 +110,7 @@ typedef struct {
  *   meta[kv][r]: fp16 [B][H][T_max][D/g][2] = (offset o, scale s) per group;
  *     dequantized value = o + s*code (§2.1).
  *   alpha[kv][r]: fp16 [B][H][T_max], the LS coefficient; unused (may be NULL)
- *     for the anchor loop.
+ *     for the anchor loop of each group.
  *   rot[kv]: fp32 [H][D][D] row-major, z = rot[h] x. Any orthogonal matrix works
  *     (randomized Hadamard, §2.2, or learned rotations such as OptR-H, §3.3). */
 typedef struct {

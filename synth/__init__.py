@@ -12,6 +12,9 @@ keys and values, which are not available here:
   * loop r < L:            X_r[t] = s_r X_L[t] + sigma_r c * eps_{r,t};
     Ouro-shaped: s_r = 0.8 + 0.05 r, sigma_r = 0.4 / r;
     Huginn-shaped: s_r = 0.7 + 0.03 r, sigma_r = 0.5 / r;
+  * with loop groups of G loops (a workload's loop_group), the same law holds
+    inside every group with its own anchor draw (the group's last loop) and r
+    counted within the group;
   * queries q ~ N(0, I); all tensors rounded to bf16 (round to nearest even);
   * the current token of decode step k sits at position T + k and follows the
     same law;
@@ -49,6 +52,11 @@ class Workload:
     family: str = "ouro"        # "ouro" or "huginn"
     nb: int = 0                 # Hadamard block size (0 -> D)
     seed: int = 0
+    loop_group: int = 0         # loops per anchor group (0 -> all L loops)
+
+    @property
+    def G(self) -> int:
+        return self.loop_group or self.L
 
     @property
     def block(self) -> int:
@@ -83,6 +91,10 @@ WORKLOADS = {
     # Huginn-3.5B-shaped: 4 layers, 55 heads, D96 (three 32x32 blocks), 8 recurrences
     "huginn_4k": Workload("huginn_4k", 4, 4, 55, 96, 8, 4096, 1, (2, 2, 2, 2, 2, 2, 4, 4),
                           (4, 4, 2, 2, 2, 2, 2, 2), family="huginn", nb=32),
+    # Huginn-3.5B as the paper runs it: 32 recurrences as 8 independent groups of 4, the
+    # last loop of each group its anchor (INT4), INT2 residuals
+    "huginn32_4k": Workload("huginn32_4k", 4, 4, 55, 96, 32, 4096, 1, (2, 2, 2, 4) * 8, (4, 2, 2, 2) * 8,
+                            family="huginn", nb=32, loop_group=4),
 }
 
 _KIND = {"kscale": 1, "vscale": 2, "kv": 3, "q": 4, "rot": 5, "outl": 6}
@@ -139,17 +151,19 @@ def kv(w: Workload, layer: int, t0: int, n: int, device="cpu", batch=None) -> to
         lo, hi = max(t0, ch * CHUNK), min(t0 + n, (ch + 1) * CHUNK)
         for t in range(2):
             g = _gen(w, layer, "kv", ch, t, device=device)
-            z = torch.randn(B, w.heads, CHUNK, w.D, generator=g, device=device, dtype=torch.float32)
-            eps = torch.randn(w.L - 1, B, w.heads, CHUNK, w.D, generator=g, device=device,
+            ng, G = w.L // w.G, w.G
+            z = torch.randn(ng, B, w.heads, CHUNK, w.D, generator=g, device=device, dtype=torch.float32)
+            eps = torch.randn(ng * (G - 1), B, w.heads, CHUNK, w.D, generator=g, device=device,
                               dtype=torch.float32)
             c = ck if t == 0 else torch.ones_like(ck)
             sl = slice(lo - ch * CHUNK, hi - ch * CHUNK)
-            anchor = c * z[:, :, sl]
             o = slice(lo - t0, hi - t0)
-            out[t, w.L - 1, :, :, o] = anchor.to(torch.bfloat16)
-            for r in range(1, w.L):
-                xr = w.sim(r) * anchor + w.noise(r) * c * eps[r - 1][:, :, sl]
-                out[t, r - 1, :, :, o] = xr.to(torch.bfloat16)
+            for gi in range(ng):
+                anchor = c * z[gi][:, :, sl]
+                out[t, gi * G + G - 1, :, :, o] = anchor.to(torch.bfloat16)
+                for r in range(1, G):
+                    xr = w.sim(r) * anchor + w.noise(r) * c * eps[gi * (G - 1) + r - 1][:, :, sl]
+                    out[t, gi * G + r - 1, :, :, o] = xr.to(torch.bfloat16)
     return out
 
 

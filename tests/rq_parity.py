@@ -15,6 +15,7 @@ ever fed to an oracle computation):
 """
 from __future__ import annotations
 
+import math
 import sys
 from concurrent.futures import ThreadPoolExecutor
 
@@ -60,13 +61,13 @@ def _ambiguous(pre: float, mode: int) -> bool:
     return a[0] != a[1]
 
 
-def oracle_series_for(X: np.ndarray, H: np.ndarray, bits, policy) -> O.Series:
-    cfg = O.Config(D=X.shape[-1], bits=list(bits), policy=policy)
+def oracle_series_for(X: np.ndarray, H: np.ndarray, bits, policy, loop_group: int = 0) -> O.Series:
+    cfg = O.Config(D=X.shape[-1], bits=list(bits), policy=policy, loop_group=loop_group)
     return O.quantize_series(cfg, X, H, diagnostics=True)
 
 
 def oracle_layer(Xall: torch.Tensor, rot_k: torch.Tensor, rot_v: torch.Tensor, bits, policy, T: int,
-                 units=None, threads: int = 16):
+                 units=None, threads: int = 16, loop_group: int = 0):
     """Oracle caches for (kv, b, h) series of tokens [0, T). Xall: bf16 [2][L][B][H][>=T][D]."""
     X = Xall[..., :T, :]
     _, L, B, H, _, D = X.shape
@@ -77,7 +78,7 @@ def oracle_layer(Xall: torch.Tensor, rot_k: torch.Tensor, rot_v: torch.Tensor, b
 
     def run(job):
         kv, b, h = job
-        return job, oracle_series_for(Xc[(b, h)][kv], (Hk if kv == 0 else Hv)[h], bits, policy)
+        return job, oracle_series_for(Xc[(b, h)][kv], (Hk if kv == 0 else Hv)[h], bits, policy, loop_group)
 
     with ThreadPoolExecutor(max_workers=threads) as ex:
         return dict(ex.map(run, jobs))
@@ -94,7 +95,6 @@ def host_copy(cache: rq.LayerCache) -> dict:
 def compare_cache(cache: rq.LayerCache, series: dict, T: int, host: dict | None = None) -> dict:
     d = cache.desc
     L, D = d.loops, d.head_dim
-    anchor = L - 1 if d.policy == rq.POLICY_LAST_LOOP else 0
     stats = dict(elements=0, exempt_elements=0, meta_exempt=0, alpha_exempt=0, bad=[])
     if host is None:
         host = host_copy(cache)
@@ -103,7 +103,7 @@ def compare_cache(cache: rq.LayerCache, series: dict, T: int, host: dict | None 
             gc, gm, ga = host[(kv, r)]
             bits = d.bits[r]
             skip_tok = np.zeros(T, bool)
-            if r != anchor:
+            if r != rq.anchor_of(d, r):
                 oa = s.alpha[r][:T]
                 ga_ = ga[b, h, :T]
                 for t in np.nonzero(oa != ga_)[0]:
@@ -179,12 +179,12 @@ def max_rel_err(gpu_out: torch.Tensor, ref: dict) -> float:
 
 
 def build_gpu_layer(X: torch.Tensor, rot_k, rot_v, bits, policy, T_max: int, T: int,
-                    steps_of_one: int = 0, pos0=None, chunk: int = 1) -> rq.LayerCache:
+                    steps_of_one: int = 0, pos0=None, chunk: int = 1, loop_group: int = 0) -> rq.LayerCache:
     """Fill a GPU cache with tokens [0, T) of X (bf16 [2][L][B][H][*][D] on the GPU): one
     bulk append of the first T - steps_of_one tokens, then appends of `chunk` tokens
     (the last one shorter) until T."""
     _, L, B, H, _, D = X.shape
-    d = rq.make_desc(B, H, D, bits, T_max, policy)
+    d = rq.make_desc(B, H, D, bits, T_max, policy, loop_group=loop_group)
     cache = rq.LayerCache.allocate(d, rot_k, rot_v)
     n0 = T - steps_of_one
     pos = torch.zeros(B, dtype=torch.int32, device="cuda") if pos0 is None else pos0
@@ -198,3 +198,35 @@ def build_gpu_layer(X: torch.Tensor, rot_k, rot_v, bits, policy, T_max: int, T: 
         t += n
     torch.cuda.synchronize()
     return cache
+
+
+def inputs(w, T_total, layer=0, batch=None):
+    X = synth.kv(w, layer, 0, T_total, device="cuda", batch=batch)
+    rk = synth.rotation(w, layer, 0)
+    rv = synth.rotation(w, layer, 1)
+    return X, rk, rv
+
+
+def decode_and_compare(w, X, rk, rv, cache, series, lens, loops, label, batch=None):
+    B, H, D = X.shape[2], X.shape[3], X.shape[5]
+    d = cache.desc
+    ws = rq.alloc_workspace(d)
+    past = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    scale = 1.0 / math.sqrt(D)
+    worst = 0.0
+    for r in loops:
+        q = synth.query(w, 0, r, 0, device="cuda", batch=B)
+        # current token: position lens[b] of sequence b, loop r
+        kc = torch.stack([X[0, r, b, :, lens[b]] for b in range(B)]).contiguous()
+        vc = torch.stack([X[1, r, b, :, lens[b]] for b in range(B)]).contiguous()
+        out = torch.empty(B, H, D, dtype=torch.float32, device="cuda")
+        log(f"{label}: decode loop {r}")
+        rq.decode_attn(cache, r, q, kc, vc, past, scale, out, ws)
+        torch.cuda.synchronize()
+        units = [(b, h) for b in range(B) for h in range(H)]
+        ref = oracle_attention(series, units, r, lens, rk, rv, q, kc, vc, scale)
+        err = max_rel_err(out, ref)
+        worst = max(worst, err)
+        log(f"{label}: loop {r} max rel err {err:.3e}")
+        assert err <= TOL_ATTN, (label, r, err)
+    return worst

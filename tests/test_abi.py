@@ -41,7 +41,10 @@ def _desc(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(head_dim=80), 2), (dict(batch=0), 2), (dict(max_tokens=0), 2), (dict(bits=[2, 3, 4]), 3),
-    (dict(bits=[2] * 17), None), (dict(policy=5), 8),
+    (dict(bits=[2] * 33), None), (dict(policy=5), 8), (dict(policy=3), 8), (dict(policy=2), 0),
+    (dict(bits=[2] * 32), 0), (dict(loop_group=2), 0), (dict(loop_group=4), 0), (dict(loop_group=1), 0),
+    (dict(loop_group=3), 2), (dict(loop_group=5), 2), (dict(loop_group=-1), 2),
+    (dict(bits=[2] * 32, loop_group=4), 0), (dict(bits=[2] * 32, loop_group=12), 2),
 ])
 def test_check_desc(kw, code):
     if code is None:
@@ -49,6 +52,24 @@ def test_check_desc(kw, code):
             _desc(**kw)
         return
     assert rq.check_desc(_desc(**kw)) == code
+
+
+def test_desc_layout_matches_header():
+    """The ctypes mirror of rq_desc: six int32 fields, then 32 bit widths and 32 group sizes."""
+    assert rq.MAX_LOOPS == 32
+    assert ctypes.sizeof(rq.Desc) == 7 * 4 + 2 * 32
+    assert rq.Desc.loop_group.offset == 6 * 4
+    assert rq.Desc.bits.offset == 7 * 4
+
+
+@pytest.mark.parametrize("policy,G,L,expect", [
+    (0, 0, 4, [3, 3, 3, 3]), (2, 0, 4, [0, 0, 0, 0]), (1, 0, 4, [0, 0, 0, 0]),
+    (0, 4, 8, [3, 3, 3, 3, 7, 7, 7, 7]), (2, 4, 8, [0, 0, 0, 0, 4, 4, 4, 4]), (1, 2, 4, [0, 0, 2, 2]),
+    (0, 1, 3, [0, 1, 2]),
+])
+def test_anchor_of(policy, G, L, expect):
+    d = _desc(bits=[2] * L, policy=policy, loop_group=G)
+    assert [rq.anchor_of(d, r) for r in range(L)] == expect
 
 
 def test_group_must_be_32():
@@ -101,6 +122,26 @@ def test_append_validation():
     assert L.rq_quantize_append(by(d), by(c), ctypes.c_void_p(0x100001), FAKE, 1, None, 0) == 10
 
 
+@pytest.mark.parametrize("policy", [0, 1, 2])
+def test_append_validation_groups(policy):
+    """With loop groups only each group's anchor may go without an alpha buffer. A
+    misaligned buffer in the last loop of the value tensor shows that the checks got
+    past every alpha pointer (no call here reaches a launch)."""
+    L, by = rq.lib, ctypes.byref
+    d = _desc(bits=[2] * 8, policy=policy, loop_group=4)
+    anchors = {rq.anchor_of(d, r) for r in range(8)}
+    assert len(anchors) == 2
+    c = _cache(d)
+    for kv in range(2):
+        for r in anchors:
+            c.alpha[kv][r] = None
+    c.codes[1][7] = 0x100004
+    assert L.rq_quantize_append(by(d), by(c), FAKE, FAKE, 1, None, 0) == 10
+    r_res = next(r for r in range(8) if r not in anchors)
+    c.alpha[0][r_res] = None
+    assert L.rq_quantize_append(by(d), by(c), FAKE, FAKE, 1, None, 0) == 1
+
+
 def test_decode_validation():
     L = rq.lib
     d = _desc()
@@ -127,6 +168,25 @@ def test_decode_validation():
     ws6 = rq.workspace_bytes(d6)
     assert L.rq_decode_attn(by(d6), by(c6), 5, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE,
                             ws6, None, 0) == 6
+    # chains restart in every loop group: loop 13 of 16 in groups of 8 reads loops 8..13
+    d16 = _desc(bits=[2] * 16, policy=1, loop_group=8)
+    c16 = _cache(d16)
+    assert L.rq_decode_attn(by(d16), by(c16), 13, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE,
+                            rq.workspace_bytes(d16), None, 0) == 6
+    # a shared-anchor read of loop 13 in groups of 8 takes the group's anchor, then loop 13:
+    # a misaligned anchor buffer is reported before loop 13's missing meta, and loop 0 (NULL
+    # codes) is never read; every call ends in an error before any launch
+    for policy, anchor in ((0, 15), (2, 8)):
+        dg = _desc(bits=[2] * 16, policy=policy, loop_group=8)
+        cg = _cache(dg)
+        cg.codes[0][0] = None
+        cg.meta[1][13] = None
+        cg.codes[1][anchor] = 0x100004
+        assert L.rq_decode_attn(by(dg), by(cg), 13, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE,
+                                rq.workspace_bytes(dg), None, 0) == 10
+        cg.codes[1][anchor] = 0x100000
+        assert L.rq_decode_attn(by(dg), by(cg), 13, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE,
+                                rq.workspace_bytes(dg), None, 0) == 1
 
 
 def test_split_api_validation():

@@ -9,8 +9,10 @@ benchmark's queries and current tokens.
 
 Layer 0 is checked for every (batch, head): the whole cache (codes, fp16
 metadata and LS coefficients of every loop, 16447 tokens) and every loop's
-attention output. The last layer, the chained comparator and the BF16
-comparator are checked on a sample of (batch, head) series. The oracle works
+attention output. The last layer, the chained comparator, the BF16
+comparator, the Huginn-shaped workloads (8 loops in one group; 32 loops in
+eight anchor groups) and the capacity shape are checked on a sample of
+(batch, head) series. The oracle works
 on its own quantization of the same bf16 inputs; nothing the HIP path writes
 is fed to it.
 """
@@ -48,7 +50,7 @@ def _build(layer, policy, bits, w=W):
     T_max = T + STEPS
     X = synth.kv(w, layer, 0, T_max, device="cuda")
     rk, rv = synth.rotation(w, layer, 0), synth.rotation(w, layer, 1)
-    d = rq.make_desc(B, H, D, list(bits), T_max, policy)
+    d = rq.make_desc(B, H, D, list(bits), T_max, policy, loop_group=w.loop_group)
     cache = rq.LayerCache.allocate(d, rk, rv)
     log(f"layer {layer} policy {policy}: bulk store of {T} tokens")
     rq.quantize_append(cache, X[..., :T, :].contiguous(), torch.zeros(B, dtype=torch.int32, device="cuda"), T)
@@ -86,7 +88,7 @@ def _check(layer, policy, bits, units, label, w=W):
     for i in range(0, len(units), 16):
         chunk = units[i:i + 16]
         log(f"{label}: oracle for units {i}..{i + len(chunk) - 1} of {len(units)}")
-        series = oracle_layer(X, rk, rv, bits, policy, Tc, units=chunk)
+        series = oracle_layer(X, rk, rv, bits, policy, Tc, units=chunk, loop_group=w.loop_group)
         assert_cache_parity(compare_cache(cache, series, Tc, host=host), f"{label} units {i}+")
         for (k, r), (out, q, kc, vc) in outs.items():
             lens = [w.T + k] * w.batch
@@ -115,6 +117,16 @@ def test_huginn_4k_sampled():
     last layer, sampled series, every loop."""
     w = synth.WORKLOADS["huginn_4k"]
     _check(w.layers - 1, LAST, w.bits, _sample_units(8, 5, w), "huginn 4k", w)
+
+
+@pytest.mark.parametrize("policy", [LAST, PREV])
+def test_huginn32_groups_sampled(policy):
+    """Huginn-3.5B as the paper groups it (B4, H55, D96, 32 loops in eight anchor
+    groups of four, 4096 tokens): layer 0, sampled series, every loop, both the
+    shared-anchor and the chained policy."""
+    w = synth.WORKLOADS["huginn32_4k"]
+    bits = w.bits if policy == LAST else w.chained_bits
+    _check(0, policy, bits, _sample_units(6, 13 + policy, w), f"huginn32 G4 policy={policy}", w)
 
 
 def test_capacity_8k_batch64_sampled():

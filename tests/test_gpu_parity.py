@@ -12,64 +12,32 @@ import torch
 import decode_attention_quantize_amd as rq
 import oracle as O
 import synth
-from rq_parity import (TOL_ATTN, assert_cache_parity, build_gpu_layer, compare_cache, log, max_rel_err,
-                       oracle_attention, oracle_layer, u16)
+from rq_parity import (TOL_ATTN, assert_cache_parity, build_gpu_layer, compare_cache, decode_and_compare,
+                       inputs, log, max_rel_err, oracle_attention, oracle_layer, u16)
 
 pytestmark = pytest.mark.gpu
 
 LAST, PREV = rq.POLICY_LAST_LOOP, rq.POLICY_PREV_LOOP
 
 
-def _inputs(w, T_total, layer=0, batch=None):
-    X = synth.kv(w, layer, 0, T_total, device="cuda", batch=batch)
-    rk = synth.rotation(w, layer, 0)
-    rv = synth.rotation(w, layer, 1)
-    return X, rk, rv
-
-
-def _decode_and_compare(w, X, rk, rv, cache, series, lens, loops, label, batch=None):
-    B, H, D = X.shape[2], X.shape[3], X.shape[5]
-    d = cache.desc
-    ws = rq.alloc_workspace(d)
-    past = torch.tensor(lens, dtype=torch.int32, device="cuda")
-    scale = 1.0 / math.sqrt(D)
-    worst = 0.0
-    for r in loops:
-        q = synth.query(w, 0, r, 0, device="cuda", batch=B)
-        # current token: position lens[b] of sequence b, loop r
-        kc = torch.stack([X[0, r, b, :, lens[b]] for b in range(B)]).contiguous()
-        vc = torch.stack([X[1, r, b, :, lens[b]] for b in range(B)]).contiguous()
-        out = torch.empty(B, H, D, dtype=torch.float32, device="cuda")
-        log(f"{label}: decode loop {r}")
-        rq.decode_attn(cache, r, q, kc, vc, past, scale, out, ws)
-        torch.cuda.synchronize()
-        units = [(b, h) for b in range(B) for h in range(H)]
-        ref = oracle_attention(series, units, r, lens, rk, rv, q, kc, vc, scale)
-        err = max_rel_err(out, ref)
-        worst = max(worst, err)
-        log(f"{label}: loop {r} max rel err {err:.3e}")
-        assert err <= TOL_ATTN, (label, r, err)
-    return worst
-
-
 @pytest.mark.parametrize("policy,bits", [(LAST, (2, 2, 2, 4)), (LAST, (2, 2, 4, 4)), (PREV, (4, 4, 2, 2))])
 def test_tiny_append_and_decode(policy, bits):
     w = synth.WORKLOADS["tiny"]
     T = w.T
-    X, rk, rv = _inputs(w, T + 1)
+    X, rk, rv = inputs(w, T + 1)
     label = f"tiny policy={policy} bits={bits}"
     log(f"{label}: append {T} tokens")
     cache = build_gpu_layer(X, rk, rv, bits, policy, T_max=T + 1, T=T)
     series = oracle_layer(X, rk, rv, bits, policy, T)
     assert_cache_parity(compare_cache(cache, series, T), label)
-    _decode_and_compare(w, X, rk, rv, cache, series, [T], range(4), label)
+    decode_and_compare(w, X, rk, rv, cache, series, [T], range(4), label)
 
 
 def test_decode_mode_appends_match_bulk():
     """Token-by-token appends at increasing positions give the same cache as the oracle."""
     w = synth.WORKLOADS["tiny"].with_(batch=2)
     T = 70
-    X, rk, rv = _inputs(w, T + 1, batch=2)
+    X, rk, rv = inputs(w, T + 1, batch=2)
     log("decode-mode appends")
     cache = build_gpu_layer(X, rk, rv, w.bits, LAST, T_max=T + 5, T=T, steps_of_one=9)
     series = oracle_layer(X, rk, rv, w.bits, LAST, T)
@@ -86,7 +54,7 @@ def test_few_token_appends(wname, D, policy, chunk):
     """Appends of a few tokens per call (the per-token store path) against the oracle."""
     w = synth.WORKLOADS[wname].with_(batch=3, heads=2, D=D)
     T = 41
-    X, rk, rv = _inputs(w, T, batch=3)
+    X, rk, rv = inputs(w, T, batch=3)
     bits = w.chained_bits if policy == PREV else w.bits
     label = f"{wname} D{D} policy={policy} chunks of {chunk}"
     log(label)
@@ -100,7 +68,7 @@ def test_ragged_lengths_and_edges():
     ragged one; every loop; the current token always joins the softmax."""
     w = synth.WORKLOADS["tiny"].with_(batch=5, heads=3, D=128, nb=128, outliers=4)
     T = 700
-    X, rk, rv = _inputs(w, T + 1, batch=5)
+    X, rk, rv = inputs(w, T + 1, batch=5)
     cache = build_gpu_layer(X, rk, rv, (2, 2, 4, 4), LAST, T_max=T + 1, T=T)
     series = oracle_layer(X, rk, rv, (2, 2, 4, 4), LAST, T)
     assert_cache_parity(compare_cache(cache, series, T), "ragged cache")
@@ -108,7 +76,7 @@ def test_ragged_lengths_and_edges():
     from_plan = rq.workspace_bytes(d)
     assert from_plan > 0
     lens = [0, 1, 32, 129, 699]
-    _decode_and_compare(w, X, rk, rv, cache, series, lens, range(4), "ragged")
+    decode_and_compare(w, X, rk, rv, cache, series, lens, range(4), "ragged")
 
 
 def test_partial_and_combine():
@@ -117,7 +85,7 @@ def test_partial_and_combine():
     score, gives the oracle's output."""
     w = synth.WORKLOADS["tiny"].with_(batch=2, heads=3, D=128, nb=128)
     T = 900
-    X, rk, rv = _inputs(w, T + 1, batch=2)
+    X, rk, rv = inputs(w, T + 1, batch=2)
     cache = build_gpu_layer(X, rk, rv, (2, 2, 4, 4), LAST, T_max=T + 1, T=T)
     series = oracle_layer(X, rk, rv, (2, 2, 4, 4), LAST, T)
     d = cache.desc
@@ -166,27 +134,27 @@ def test_partial_and_combine():
 def test_huginn_shape_d96_eight_loops():
     w = synth.WORKLOADS["huginn_4k"].with_(batch=2, heads=3)
     T = 333
-    X, rk, rv = _inputs(w, T + 1, batch=2)
+    X, rk, rv = inputs(w, T + 1, batch=2)
     cache = build_gpu_layer(X, rk, rv, w.bits, LAST, T_max=T + 1, T=T)
     series = oracle_layer(X, rk, rv, w.bits, LAST, T)
     assert_cache_parity(compare_cache(cache, series, T), "d96 L8")
-    _decode_and_compare(w, X, rk, rv, cache, series, [T, 200], range(8), "d96 L8")
+    decode_and_compare(w, X, rk, rv, cache, series, [T, 200], range(8), "d96 L8")
 
 
 def test_uniform_int2_d128():
     w = synth.WORKLOADS["ouro_int2_4k"].with_(heads=4)
     T = 515
-    X, rk, rv = _inputs(w, T + 1)
+    X, rk, rv = inputs(w, T + 1)
     cache = build_gpu_layer(X, rk, rv, w.bits, LAST, T_max=T + 1, T=T)
     series = oracle_layer(X, rk, rv, w.bits, LAST, T)
     assert_cache_parity(compare_cache(cache, series, T), "int2 d128")
-    _decode_and_compare(w, X, rk, rv, cache, series, [T], range(4), "int2 d128")
+    decode_and_compare(w, X, rk, rv, cache, series, [T], range(4), "int2 d128")
 
 
 def test_bf16_decode_ragged():
     w = synth.WORKLOADS["tiny"].with_(batch=3, heads=2, D=128, nb=128)
     T = 600
-    X, rk, rv = _inputs(w, T + 1, batch=3)
+    X, rk, rv = inputs(w, T + 1, batch=3)
     B, H, D = 3, 2, 128
     lens = [0, 77, 600]
     scale = 1.0 / math.sqrt(D)
@@ -216,7 +184,7 @@ def test_device_error_flags():
     """Appends past capacity are dropped and flagged; lengths beyond capacity are clamped and flagged."""
     w = synth.WORKLOADS["tiny"]
     T_max = 40
-    X, rk, rv = _inputs(w, 64)
+    X, rk, rv = inputs(w, 64)
     d = rq.make_desc(1, 2, 64, w.bits, T_max)
     cache = rq.LayerCache.allocate(d, rk, rv)
     for kv in range(2):                       # never-written positions hold zeros, not garbage
