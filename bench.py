@@ -48,11 +48,17 @@ def comp_bytes(D, bits, with_alpha, group=32):
     return D * bits // 8 + (D // group) * 4 + (2 if with_alpha else 0)
 
 
-def call_bytes(D, bits, policy, r, G=0):
+def _groups(bits, groups):
+    return list(groups) if groups else [32] * len(bits)
+
+
+def call_bytes(D, bits, policy, r, G=0, groups=None):
     """Algorithmic HBM bytes one decode call of loop r reads per (b, h, cached token):
     the stored components the reconstruction needs, K and V (fp16 meta and alpha).
-    Loops form groups of G (0: one group) with an anchor each."""
+    Loops form groups of G (0: one group) with an anchor each; `groups` gives each
+    loop's channel group size (default 32)."""
     G = G or len(bits)
+    gs = _groups(bits, groups)
     g0 = r // G * G
     if policy == "last":
         a = g0 + G - 1
@@ -60,16 +66,19 @@ def call_bytes(D, bits, policy, r, G=0):
     else:
         a = g0
         comps = list(range(g0, r + 1))
-    return 2 * sum(comp_bytes(D, bits[c], c != a) for c in comps)
+    return 2 * sum(comp_bytes(D, bits[c], c != a, gs[c]) for c in comps)
 
 
 PROFILED_WORKLOAD = "ouro_16k"       # the workload the committed counter summaries cover
 
 
-def dom_kernel_name(D, bits, G):
-    """Instance name of the streaming kernel decoding loop 1 (anchor + loop-1 residual)."""
+def dom_kernel_name(D, bits, G, groups=None):
+    """Instance name of the streaming kernel decoding loop 1 (anchor + loop-1 residual);
+    a component's nibble is its bit width, plus 8 for groups of 16 channels."""
     G = G or len(bits)
-    cb = bits[G - 1] | (bits[0] << 4)
+    gs = _groups(bits, groups)
+    kind = [b | (8 if g == 16 else 0) for b, g in zip(bits, gs)]
+    cb = kind[G - 1] | (kind[0] << 4)
     return f"decode_fused<{D}, 2, {cb}u, 2>"
 
 
@@ -232,9 +241,10 @@ def main():
     # ---------------------------------------------------------------- build (untimed)
     t_build = time.time()
     G = w.loop_group
+    gr, cgr = w.groups_for(bits), w.groups_for(cbits)
     run_chained = not args.no_chained and (G or L) <= 4
-    d_rq = rq.make_desc(B, H, D, bits, T_max, rq.POLICY_LAST_LOOP, loop_group=G)
-    d_ch = rq.make_desc(B, H, D, cbits, T_max, rq.POLICY_PREV_LOOP, loop_group=G)
+    d_rq = rq.make_desc(B, H, D, bits, T_max, rq.POLICY_LAST_LOOP, group=gr, loop_group=G)
+    d_ch = rq.make_desc(B, H, D, cbits, T_max, rq.POLICY_PREV_LOOP, group=cgr, loop_group=G)
     caches, chained, bf16, rots = [], [], [], []
     kvcur = torch.empty(K, w.layers, 2, L, B, H, 1, D, dtype=torch.bfloat16, device=dev)
     qs = torch.empty(K, w.layers, L, B, H, D, dtype=torch.bfloat16, device=dev)
@@ -328,7 +338,7 @@ def main():
     log(f"RQ: {K} steps in {dt_rq * 1e3:.2f} ms")
     del g_rq
 
-    per_token_bytes = sum(call_bytes(D, bits, "last", r, G) for r in range(L)) * H * w.layers
+    per_token_bytes = sum(call_bytes(D, bits, "last", r, G, gr) for r in range(L)) * H * w.layers
     mean_ctx = T + (K - 1) / 2.0
     step_bytes = per_token_bytes * B * mean_ctx
     result = {
@@ -336,7 +346,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": dt_rq * 1e3 / K, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "layers": w.layers, "batch": B, "heads": H, "head_dim": D, "loops": L,
-                   "loop_group": G or L, "context": T, "bits": bits, "group": w.group,
+                   "loop_group": G or L, "context": T, "bits": bits, "group": gr,
                    "codes": "int2/int4 + fp16 scale/offset + fp16 alpha",
                    "arith": "keys: int8 dot products with a 14-bit fixed-point rotated query; values: fp32 "
                             "multiply-adds of fp16-exact codes; fp32 softmax and accumulation"},
@@ -356,7 +366,7 @@ def main():
         g_ch = capture(lambda k: rq_step(k, chained, d_ch, ws_ch))
         dt_ch = run(g_ch, args.warmup)
         del g_ch
-        ch_bytes = sum(call_bytes(D, cbits, "prev", r, G) for r in range(L)) * H * w.layers * B * mean_ctx
+        ch_bytes = sum(call_bytes(D, cbits, "prev", r, G, cgr) for r in range(L)) * H * w.layers * B * mean_ctx
         result["chained"] = {"policy": "previous-loop", "bits": cbits, "value": B * K / dt_ch,
                              "unit": "tokens/s", "ms_per_step": dt_ch * 1e3 / K,
                              "hbm_gbps_step": ch_bytes / (dt_ch / K) / 1e9,
@@ -406,7 +416,7 @@ def main():
     for r in range(G or L):                       # every loop group has the same shape
         kc = kvcur[0, 0, 0, r, :, :, 0]
         vc = kvcur[0, 0, 1, r, :, :, 0]
-        nbytes = call_bytes(D, bits, "last", r, G) * B * H * T
+        nbytes = call_bytes(D, bits, "last", r, G, gr) * B * H * T
         ms_k = events(lambda i: rq.decode_attn_partial(caches[i % w.layers], r, qs[0, 0, r], past_len, scale, ws))
         ms_c = events(lambda i: rq.decode_combine(d_rq, caches[i % w.layers].rot[1], qs[0, 0, r], kc, vc, past_len,
                                                   scale, out[0, r], ws))
@@ -419,7 +429,7 @@ def main():
     result["roofline"] = {"bound": "hbm", "achieved": dom["kernel_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                           "frac": dom["kernel_gbps"] / HBM_PEAK_GBPS,
                           "traffic": None if traffic is None else traffic["bytes"],
-                          "kernel": dom_kernel_name(D, bits, G) + " (rq_decode_attn_partial, loop 1: "
+                          "kernel": dom_kernel_name(D, bits, G, gr) + " (rq_decode_attn_partial, loop 1: "
                                     f"INT{bits[(G or L) - 1]} anchor + INT{bits[0]} residual, K and V)",
                           "bytes_per_launch": dom["bytes"], "ms_per_launch": dom["kernel_ms"],
                           "traffic_source": None if traffic is None else traffic["source"]}
@@ -461,7 +471,7 @@ def cpu_baseline(w, bits, units, min_seconds, torch, synth, scale):
     u16 = lambda t: t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
     Xh = {p: u16(X[:, :, p[0], p[1]]) for p in pairs}
     qn = [u16(synth.query(w, 0, r, 0, device="cpu")) for r in range(L)]
-    cfg = O.Config(D=D, bits=list(bits), loop_group=w.loop_group)
+    cfg = O.Config(D=D, bits=list(bits), group=w.groups_for(bits), loop_group=w.loop_group)
     t0 = time.time()
 
     def build(p):

@@ -90,13 +90,17 @@ def version() -> str:
 
 
 def make_desc(batch: int, heads: int, head_dim: int, bits, max_tokens: int,
-              policy: int = POLICY_LAST_LOOP, group: int = 32, loop_group: int = 0) -> Desc:
+              policy: int = POLICY_LAST_LOOP, group=32, loop_group: int = 0) -> Desc:
+    """Descriptor of one layer's cache; `group` is one size for all loops or one per loop."""
     d = Desc()
     d.batch, d.heads, d.head_dim = batch, heads, head_dim
     d.loops, d.max_tokens, d.policy, d.loop_group = len(bits), max_tokens, policy, loop_group
-    for r, b in enumerate(bits):
+    groups = list(group) if isinstance(group, (list, tuple)) else [group] * len(bits)
+    if len(groups) != len(bits):
+        raise ValueError("one group size per loop")
+    for r, (b, g) in enumerate(zip(bits, groups)):
         d.bits[r] = b
-        d.group[r] = group
+        d.group[r] = g
     return d
 
 

@@ -70,7 +70,7 @@ rq_status check_plan(const rq_desc* d) {
     return RQ_E_SHAPE;
   for (int r = 0; r < d->loops; ++r) {
     if (d->bits[r] != 2 && d->bits[r] != 4) return RQ_E_BITS;
-    if (d->group[r] != 32) return RQ_E_BITS;
+    if (d->group[r] != 32 && !(d->group[r] == 16 && d->bits[r] == 2)) return RQ_E_BITS;
   }
   return RQ_OK;
 }
@@ -135,14 +135,14 @@ const char* rq_status_str(rq_status s) {
     case RQ_OK: return "ok";
     case RQ_E_NULL: return "required pointer is NULL";
     case RQ_E_SHAPE: return "shape out of range (batch, heads, head_dim in {64,96,128}, loops 1..32, loop_group 0 or a divisor of loops, max_tokens >= 1, n)";
-    case RQ_E_BITS: return "unsupported bit width or group size (bits 2 or 4, group 32)";
+    case RQ_E_BITS: return "unsupported bit width or group size (bits 2 or 4; group 32, or 16 for 2 bits)";
     case RQ_E_CAPACITY: return "size exceeds max_tokens";
     case RQ_E_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
     case RQ_E_UNSUPPORTED: return "no kernel for this combination (e.g. more than 4 chained components)";
     case RQ_E_HIP: return "HIP launch failed";
     case RQ_E_POLICY: return "unknown reference policy";
     case RQ_E_LOOP: return "loop index out of range";
-    case RQ_E_ALIGN: return "device array misaligned (codes/rot/kv/q/k/v 16 B, meta/out 4 B, alpha 2 B)";
+    case RQ_E_ALIGN: return "device array misaligned (codes/rot/kv/q/k/v 16 B, meta 4 B (8 B for groups of 16), out 4 B, alpha 2 B)";
   }
   return "unknown status";
 }
@@ -184,7 +184,8 @@ rq_status rq_quantize_append(const rq_desc* d, const rq_layer_cache* c, const ui
       if (!c->codes[kvi][r] || !c->meta[kvi][r]) return RQ_E_NULL;
       const bool anchor = r == anchor_of(d, r);
       if (!anchor && !c->alpha[kvi][r]) return RQ_E_NULL;
-      if (!al(c->codes[kvi][r], 16) || !al(c->meta[kvi][r], 4) || (!anchor && !al(c->alpha[kvi][r], 2)))
+      const uintptr_t ma = d->group[r] == 16 ? 8 : 4;
+      if (!al(c->codes[kvi][r], 16) || !al(c->meta[kvi][r], ma) || (!anchor && !al(c->alpha[kvi][r], 2)))
         return RQ_E_ALIGN;
       p.codes[kvi][r] = c->codes[kvi][r];
       p.meta[kvi][r] = reinterpret_cast<uint32_t*>(c->meta[kvi][r]);
@@ -202,7 +203,10 @@ rq_status rq_quantize_append(const rq_desc* d, const rq_layer_cache* c, const ui
   p.T_max = d->max_tokens;
   p.policy = d->policy;
   p.G = group_len(d);
-  for (int r = 0; r < d->loops; ++r) p.bits[r] = d->bits[r];
+  for (int r = 0; r < d->loops; ++r) {
+    p.bits[r] = d->bits[r];
+    if (d->group[r] == 16) p.g16 |= 1u << r;
+  }
   return launch_append(p, d->head_dim, stream) == 0 ? RQ_OK : RQ_E_HIP;
 }
 
@@ -230,8 +234,8 @@ rq_status rq_decode_attn_partial(const rq_desc* d, const rq_layer_cache* c, int3
   int loops[RQ_MAX_LOOPS];
   const int nc = components(d, loop, loops);
   if (nc > kMaxComp) return RQ_E_UNSUPPORTED;
-  int bits[kMaxComp];
-  for (int i = 0; i < nc; ++i) bits[i] = d->bits[loops[i]];
+  int bits[kMaxComp];  // component kinds: bit width, plus 8 for INT2 in groups of 16
+  for (int i = 0; i < nc; ++i) bits[i] = d->bits[loops[i]] | (d->group[loops[i]] == 16 ? 8 : 0);
   if (!have_decode_kernel(d->head_dim, nc, bits)) return RQ_E_UNSUPPORTED;
 
   const SplitPlan sp = split_plan(d);
@@ -240,7 +244,8 @@ rq_status rq_decode_attn_partial(const rq_desc* d, const rq_layer_cache* c, int3
   for (int i = 0; i < nc; ++i) {
     const int r = loops[i];
     if (!c->codes[0][r] || !c->meta[0][r] || !c->codes[1][r] || !c->meta[1][r]) return RQ_E_NULL;
-    if (!al(c->codes[0][r], 16) || !al(c->codes[1][r], 16) || !al(c->meta[0][r], 4) || !al(c->meta[1][r], 4))
+    const uintptr_t ma = d->group[r] == 16 ? 8 : 4;  // metadata of a 32-channel block: 4 or 8 bytes
+    if (!al(c->codes[0][r], 16) || !al(c->codes[1][r], 16) || !al(c->meta[0][r], ma) || !al(c->meta[1][r], ma))
       return RQ_E_ALIGN;
     p.kcodes[i] = c->codes[0][r];
     p.kmeta[i] = reinterpret_cast<const uint32_t*>(c->meta[0][r]);

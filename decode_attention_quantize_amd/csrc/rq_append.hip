@@ -85,40 +85,79 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
-// Quantize one row's group pair (elements e0 = 32 gi + k, e1 = e0 + 16 held by
-// lane k of group gi), store codes and metadata, return the dequantized pair.
+// Quantize one row's pair of elements e0 = 32 gi + k, e1 = e0 + 16 (held by
+// lane k of lane group gi) in one group of 32 channels, or, with g16, e0 in
+// group 2 gi and e1 in group 2 gi + 1 of 16 channels each (INT2 only); store
+// codes and metadata, return the dequantized pair.
 template <int D>
-__device__ void quantize_pair(double v0, double v1, int bits, bool lane_on, int gi, int k,
+__device__ void quantize_pair(double v0, double v1, int bits, bool g16, bool lane_on, int gi, int k,
                               uint8_t* codes, uint32_t* meta, size_t tok, double& d0, double& d1) {
-  constexpr int G = D / 32;
-  double mn = lane_on ? fmin(v0, v1) : 0.0, mx = lane_on ? fmax(v0, v1) : 0.0;
-  for (int m = 1; m < 16; m <<= 1) {            // the 16 lanes of one group
-    mn = fmin(mn, shfl_xor_f64(mn, m));
-    mx = fmax(mx, shfl_xor_f64(mx, m));
+  double mn0, mx0, mn1, mx1;
+  if (g16) {
+    mn0 = lane_on ? v0 : 0.0;
+    mx0 = mn0;
+    mn1 = lane_on ? v1 : 0.0;
+    mx1 = mn1;
+  } else {
+    mn0 = mn1 = lane_on ? fmin(v0, v1) : 0.0;
+    mx0 = mx1 = lane_on ? fmax(v0, v1) : 0.0;
   }
-  const uint16_t o16 = f64_to_f16(mn, 1);
-  const double od = f16_to_f64(o16);
+  for (int m = 1; m < 16; m <<= 1) {            // the 16 lanes of one lane group
+    mn0 = fmin(mn0, shfl_xor_f64(mn0, m));
+    mx0 = fmax(mx0, shfl_xor_f64(mx0, m));
+    if (g16) {
+      mn1 = fmin(mn1, shfl_xor_f64(mn1, m));
+      mx1 = fmax(mx1, shfl_xor_f64(mx1, m));
+    }
+  }
+  if (!g16) {
+    mn1 = mn0;
+    mx1 = mx0;
+  }
   const double qmax = (double)((1 << bits) - 1);
-  const double sp = (mx - od) / qmax;
-  const uint16_t s16 = f64_to_f16(sp, 2);
-  const double sd = f16_to_f64(s16);
-  uint32_t c0 = 0, c1 = 0;
-  if (sd != 0.0) {
-    c0 = (uint32_t)fmin(fmax(rint((v0 - od) / sd), 0.0), qmax);
-    c1 = (uint32_t)fmin(fmax(rint((v1 - od) / sd), 0.0), qmax);
+  uint16_t o16[2], s16[2];
+  double od[2], sd[2];
+  for (int i = 0; i < (g16 ? 2 : 1); ++i) {
+    o16[i] = f64_to_f16(i ? mn1 : mn0, 1);
+    od[i] = f16_to_f64(o16[i]);
+    s16[i] = f64_to_f16(((i ? mx1 : mx0) - od[i]) / qmax, 2);
+    sd[i] = f16_to_f64(s16[i]);
   }
-  d0 = od + sd * (double)c0;
-  d1 = od + sd * (double)c1;
+  if (!g16) {
+    o16[1] = o16[0]; s16[1] = s16[0];
+    od[1] = od[0]; sd[1] = sd[0];
+  }
+  uint32_t c0 = 0, c1 = 0;
+  if (sd[0] != 0.0) c0 = (uint32_t)fmin(fmax(rint((v0 - od[0]) / sd[0]), 0.0), qmax);
+  if (sd[1] != 0.0) c1 = (uint32_t)fmin(fmax(rint((v1 - od[1]) / sd[1]), 0.0), qmax);
+  d0 = od[0] + sd[0] * (double)c0;
+  d1 = od[1] + sd[1] * (double)c1;
+  uint8_t* row = codes + tok * (size_t)(D * bits / 8);
+  if (g16) {
+    // one 32-bit word per group: element k at bit 16 (k / 8) + 2 (k mod 8)
+    const int sh = 16 * (k >> 3) + 2 * (k & 7);
+    uint32_t wa = c0 << sh, wb = c1 << sh;
+    for (int m = 1; m < 16; m <<= 1) {
+      wa |= (uint32_t)__shfl_xor((int)wa, m, 64);
+      wb |= (uint32_t)__shfl_xor((int)wb, m, 64);
+    }
+    if (lane_on && k == 0) {
+      *reinterpret_cast<uint2*>(row + gi * 8) = make_uint2(wa, wb);
+      *reinterpret_cast<uint2*>(meta + tok * (D / 16) + 2 * gi) =
+          make_uint2((uint32_t)o16[0] | ((uint32_t)s16[0] << 16), (uint32_t)o16[1] | ((uint32_t)s16[1] << 16));
+    }
+    return;
+  }
   const int per = 16 / bits;                    // codes per 16-bit half-word
   const int sh = bits * (k % per);
   uint32_t word = (c0 << sh) | (c1 << (16 + sh));
   for (int m = 1; m < per; m <<= 1) word |= (uint32_t)__shfl_xor((int)word, m, 64);
   if (lane_on) {
     if (k % per == 0) {
-      uint32_t* dst = reinterpret_cast<uint32_t*>(codes + tok * (size_t)(D * bits / 8) + gi * 4 * bits);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(row + gi * 4 * bits);
       dst[k / per] = word;
     }
-    if (k == 0) meta[tok * G + gi] = (uint32_t)o16 | ((uint32_t)s16 << 16);
+    if (k == 0) meta[tok * (D / 32) + gi] = (uint32_t)o16[0] | ((uint32_t)s16[0] << 16);
   }
 }
 
@@ -190,8 +229,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
     for (int g0 = 0; g0 < L; g0 += p.G) {
       const int a = (p.policy == RQ_POLICY_LAST_LOOP) ? g0 + p.G - 1 : g0;
       double r0, r1;  // reference (reconstructed anchor, or previous loop) at e0, e1
-      quantize_pair<D>(Z[a][e0], Z[a][e1], p.bits[a], lane_on, gi, k, p.codes[kv][a], p.meta[kv][a], tok, r0,
-                       r1);
+      quantize_pair<D>(Z[a][e0], Z[a][e1], p.bits[a], (p.g16 >> a) & 1, lane_on, gi, k, p.codes[kv][a],
+                       p.meta[kv][a], tok, r0, r1);
       if (!lane_on) r0 = r1 = 0.0;
       double den_cur = wave_sum_f64(r0 * r0 + r1 * r1);
       for (int r = g0; r < g0 + p.G; ++r) {
@@ -203,8 +242,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
         const double at = f16_to_f64(a16);
         if (lane == 0) p.alpha[kv][r][tok] = a16;
         double q0, q1;
-        quantize_pair<D>(z0 - at * r0, z1 - at * r1, p.bits[r], lane_on, gi, k, p.codes[kv][r], p.meta[kv][r],
-                         tok, q0, q1);
+        quantize_pair<D>(z0 - at * r0, z1 - at * r1, p.bits[r], (p.g16 >> r) & 1, lane_on, gi, k, p.codes[kv][r],
+                         p.meta[kv][r], tok, q0, q1);
         if (p.policy == RQ_POLICY_PREV_LOOP) {  // zhat_r = alpha_r zhat_{r-1} + D(c_r)
           r0 = lane_on ? at * r0 + q0 : 0.0;
           r1 = lane_on ? at * r1 + q1 : 0.0;
@@ -312,7 +351,8 @@ __global__ __launch_bounds__(256) void append_unit(AppendParams p) {
     const int r = wave + kWaves * j;
     if (r < L && r == anchor_of(r)) {
       double r0, r1;
-      quantize_pair<D>(z0[j], z1[j], p.bits[r], lane_on, gi, kk, p.codes[kv][r], p.meta[kv][r], tok, r0, r1);
+      quantize_pair<D>(z0[j], z1[j], p.bits[r], (p.g16 >> r) & 1, lane_on, gi, kk, p.codes[kv][r], p.meta[kv][r],
+                       tok, r0, r1);
       if (!lane_on) r0 = r1 = 0.0;
       const double den = wave_sum_f64(r0 * r0 + r1 * r1);
       if (lane_on) {
@@ -336,8 +376,8 @@ __global__ __launch_bounds__(256) void append_unit(AppendParams p) {
     const uint16_t a16 = f64_to_f16(alpha, 0);
     at = f16_to_f64(a16);
     if (lane == 0) p.alpha[kv][r][tok] = a16;
-    quantize_pair<D>(zz0 - at * r0, zz1 - at * r1, p.bits[r], lane_on, gi, kk, p.codes[kv][r], p.meta[kv][r], tok,
-                     q0, q1);
+    quantize_pair<D>(zz0 - at * r0, zz1 - at * r1, p.bits[r], (p.g16 >> r) & 1, lane_on, gi, kk, p.codes[kv][r],
+                     p.meta[kv][r], tok, q0, q1);
   };
 
   if (!chain) {

@@ -21,10 +21,14 @@
 // integer sum of q'_e code_e.
 // Values: a masked code field read as an fp16 bit pattern is the subnormal
 // number code * 2^(shift - 24), exactly, and the mixed-precision FMA takes fp16
-// subnormal operands exactly. The packed layout places group elements e and
-// e+16 at the same bit offset of the low and high halves of a word; a byte
-// permute pairs the same element of two tokens, and one mask then yields that
-// element of both tokens.
+// subnormal operands exactly. A byte permute pairs the same code byte of two
+// tokens, and one mask then yields that element of both tokens.
+//
+// A lane always owns a block of 32 channels. A component is INT4 or INT2 in one
+// group of 32 (offset, scale) per block, or INT2 in two groups of 16 (§5
+// "Quantization setup": g = 16 for INT2): then word j of the block's codes is
+// group j, the block carries two metadata words, and the key and value sums
+// keep the two halves of the block apart.
 #include <hip/hip_runtime.h>
 
 #include "rq_combine.hpp"
@@ -84,8 +88,9 @@ __device__ __forceinline__ Words<BITS> load_group(__amdgpu_buffer_rsrc_t r, uint
 constexpr int kLimbs = 2;
 constexpr int kFixBits = kLimbs == 2 ? 14 : 21;
 struct QFix {
-  uint32_t q4[4][2][kLimbs];  // INT4: word j, mask (low / high nibbles), limb
-  uint32_t q2[2][4][kLimbs];  // INT2: word j, field s, limb
+  uint32_t q4[4][2][kLimbs];   // INT4: word j, mask (low / high nibbles), limb
+  uint32_t q2[2][4][kLimbs];   // INT2, one group of 32: word j, field s, limb
+  uint32_t q2h[2][4][kLimbs];  // INT2, two groups of 16: word j (= group j), field s, limb
 };
 
 // Elements of the group that byte b (0..3) of a masked word holds.
@@ -93,8 +98,40 @@ struct QFix {
 //     bytes 0..3 = elements 4j + m, 4j + 2 + m, 16 + 4j + m, 18 + 4j + m.
 //   INT2 word j, field s (bits 2s, 2s+1 of each byte):
 //     bytes 0..3 = elements 8j + s, 8j + 4 + s, 16 + 8j + s, 20 + 8j + s.
+//   INT2 in groups of 16, word j = group j, field s:
+//     bytes 0..3 = elements 16j + s, 16j + 4 + s, 16j + 8 + s, 16j + 12 + s.
 __host__ __device__ constexpr int int4_elem(int j, int m, int b) { return (b >> 1) * 16 + 4 * j + 2 * (b & 1) + m; }
 __host__ __device__ constexpr int int2_elem(int j, int s, int b) { return (b >> 1) * 16 + 8 * j + 4 * (b & 1) + s; }
+__host__ __device__ constexpr int int2h_elem(int j, int s, int b) { return 16 * j + 4 * b + s; }
+
+// Component kind, one nibble of a plan: the bit width in bits 0-2, and
+// kGroup16 for INT2 in groups of 16 channels (else one group of 32).
+constexpr int kGroup16 = 8;
+__host__ __device__ constexpr int kbits(int k) { return k & 7; }
+__host__ __device__ constexpr bool kg16(int k) { return (k & kGroup16) != 0; }
+
+// sum_e v_e code_e over each group of 16 of an INT2 block (exact in int32).
+__device__ __forceinline__ void kdot16(const Words<2>& c, const QFix& Q, int& d0, int& d1) {
+  int r[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    int a[kLimbs];
+#pragma unroll
+    for (int l = 0; l < kLimbs; ++l) a[l] = 0;
+    const uint32_t x = c.w[j];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int m = (int)((x >> (2 * f)) & 0x03030303u);
+#pragma unroll
+      for (int l = 0; l < kLimbs; ++l) a[l] = __builtin_amdgcn_sdot4(m, (int)Q.q2h[j][f][l], a[l], false);
+    }
+    r[j] = a[0];
+#pragma unroll
+    for (int l = 1; l < kLimbs; ++l) r[j] = r[j] * 256 + a[l];
+  }
+  d0 = r[0];
+  d1 = r[1];
+}
 
 // sum_e v_e code_e over one group (exact in int32: |v| < 2^21, 32 codes < 16).
 template <int BITS>
@@ -155,9 +192,12 @@ __device__ __forceinline__ uint32_t pair_byte(uint32_t w0, uint32_t w1, int by) 
   return __builtin_amdgcn_perm(w1, w0, 0x0c000c00u | ((uint32_t)(4 + by) << 16) | (uint32_t)by);
 }
 
-template <int BITS, int REF>
-__device__ __forceinline__ void vpairs(const Words<BITS>& c0, const Words<BITS>& c1, int half, int blk,
+// INT2 in groups of 16: elements 16 half + 4 blk + q are field q of byte blk of
+// word half (group `half`), at the same classes as above.
+template <int K, int REF>
+__device__ __forceinline__ void vpairs(const Words<kbits(K)>& c0, const Words<kbits(K)>& c1, int half, int blk,
                                        uint32_t (&x)[4]) {
+  constexpr int BITS = kbits(K);
   if constexpr (BITS == 4) {
     const uint32_t b0 = pair_byte(c0.w[blk], c1.w[blk], 2 * half), b1 = pair_byte(c0.w[blk], c1.w[blk], 2 * half + 1);
     x[0] = b0 & 0x000F000Fu;
@@ -165,7 +205,8 @@ __device__ __forceinline__ void vpairs(const Words<BITS>& c0, const Words<BITS>&
     x[2] = b1 & 0x000F000Fu;
     x[3] = b1 & 0x00F000F0u;
   } else {
-    const uint32_t b = pair_byte(c0.w[blk >> 1], c1.w[blk >> 1], 2 * half + (blk & 1));
+    const uint32_t b = kg16(K) ? pair_byte(c0.w[half], c1.w[half], blk)
+                               : pair_byte(c0.w[blk >> 1], c1.w[blk >> 1], 2 * half + (blk & 1));
     if constexpr (REF == 4) {
       const uint32_t b4 = b >> 4;
       x[0] = b & 0x00030003u;
@@ -186,7 +227,7 @@ __host__ __device__ constexpr bool vw4(int q) {
 }
 
 template <uint32_t CB, int c>
-constexpr int cbits() {
+constexpr int ckind() {
   return (int)((CB >> (4 * c)) & 0xF);
 }
 
@@ -194,15 +235,24 @@ template <uint32_t CB, int NC>
 constexpr int ref_bits() {
   int r = 2;
   for (int c = 0; c < NC; ++c)
-    if (((CB >> (4 * c)) & 0xF) == 4) r = 4;
+    if (kbits((int)((CB >> (4 * c)) & 0xF)) == 4) r = 4;
   return r;
 }
 
-// Per-component tile data of one lane: codes of tokens t0, t1 for K and V, metadata, alpha.
-template <int BITS>
+template <uint32_t CB, int NC>
+constexpr bool any_g16() {
+  bool r = false;
+  for (int c = 0; c < NC; ++c) r = r || kg16((int)((CB >> (4 * c)) & 0xF));
+  return r;
+}
+
+// Per-component tile data of one lane: codes of tokens t0, t1 for K and V,
+// metadata (one word per group of the lane's block), alpha.
+template <int K>
 struct CompTile {
-  Words<BITS> k0, k1, v0, v1;
-  uint32_t km0, km1, vm0, vm1;
+  static constexpr int NM = kg16(K) ? 2 : 1;
+  Words<kbits(K)> k0, k1, v0, v1;
+  uint32_t km0[NM], km1[NM], vm0[NM], vm1[NM];
   uint16_t ka0, ka1, va0, va1;
 };
 
@@ -211,10 +261,10 @@ struct CompRsrc {
   __amdgpu_buffer_rsrc_t kc, vc, km, vm, ka, va;
 };
 
-template <int D, int BITS>
+template <int D, int K>
 __device__ __forceinline__ CompRsrc comp_rsrc(const DecodeParams& p, int c, size_t row0, uint32_t ntok) {
-  constexpr int G = D / 32;
-  constexpr uint32_t RB = D * BITS / 8;
+  constexpr int G = kg16(K) ? D / 16 : D / 32;  // metadata words per token
+  constexpr uint32_t RB = D * kbits(K) / 8;
   CompRsrc r;
   r.kc = make_rsrc(p.kcodes[c] + row0 * RB, ntok * RB);
   r.vc = make_rsrc(p.vcodes[c] + row0 * RB, ntok * RB);
@@ -235,8 +285,9 @@ struct Offs {
   uint32_t c4, c2, m, a;
 };
 
-template <int D, int BITS>
-__device__ __forceinline__ void load_comp(CompTile<BITS>& T, const CompRsrc& r, bool has_alpha, const Offs& o) {
+template <int D, int K>
+__device__ __forceinline__ void load_comp(CompTile<K>& T, const CompRsrc& r, bool has_alpha, const Offs& o) {
+  constexpr int BITS = kbits(K);
   constexpr int G = D / 32;
   constexpr int TPW = 64 / G;
   constexpr uint32_t RB = D * BITS / 8;
@@ -245,10 +296,20 @@ __device__ __forceinline__ void load_comp(CompTile<BITS>& T, const CompRsrc& r, 
   T.k1 = load_group<BITS>(r.kc, oc + TPW * RB);
   T.v0 = load_group<BITS>(r.vc, oc);
   T.v1 = load_group<BITS>(r.vc, oc + TPW * RB);
-  T.km0 = __builtin_amdgcn_raw_buffer_load_b32(r.km, o.m, 0, kAux);
-  T.km1 = __builtin_amdgcn_raw_buffer_load_b32(r.km, o.m + TPW * G * 4, 0, kAux);
-  T.vm0 = __builtin_amdgcn_raw_buffer_load_b32(r.vm, o.m, 0, kAux);
-  T.vm1 = __builtin_amdgcn_raw_buffer_load_b32(r.vm, o.m + TPW * G * 4, 0, kAux);
+  if constexpr (kg16(K)) {               // two groups of 16 per block: 8 bytes of metadata
+    const uint32_t m0 = 2 * o.m, m1 = 2 * (o.m + TPW * G * 4);
+    const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(r.km, m0, 0, kAux);
+    const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(r.km, m1, 0, kAux);
+    const u32x2 c = __builtin_amdgcn_raw_buffer_load_b64(r.vm, m0, 0, kAux);
+    const u32x2 d = __builtin_amdgcn_raw_buffer_load_b64(r.vm, m1, 0, kAux);
+    T.km0[0] = a.x; T.km0[1] = a.y; T.km1[0] = b.x; T.km1[1] = b.y;
+    T.vm0[0] = c.x; T.vm0[1] = c.y; T.vm1[0] = d.x; T.vm1[1] = d.y;
+  } else {
+    T.km0[0] = __builtin_amdgcn_raw_buffer_load_b32(r.km, o.m, 0, kAux);
+    T.km1[0] = __builtin_amdgcn_raw_buffer_load_b32(r.km, o.m + TPW * G * 4, 0, kAux);
+    T.vm0[0] = __builtin_amdgcn_raw_buffer_load_b32(r.vm, o.m, 0, kAux);
+    T.vm1[0] = __builtin_amdgcn_raw_buffer_load_b32(r.vm, o.m + TPW * G * 4, 0, kAux);
+  }
   if (has_alpha) {
     T.ka0 = __builtin_amdgcn_raw_buffer_load_b16(r.ka, o.a, 0, kAux);
     T.ka1 = __builtin_amdgcn_raw_buffer_load_b16(r.ka, o.a + TPW * 2, 0, kAux);
@@ -261,18 +322,18 @@ __device__ __forceinline__ void load_comp(CompTile<BITS>& T, const CompRsrc& r, 
 
 template <int D, int NC, uint32_t CB>
 struct Tile {
-  CompTile<cbits<CB, 0>()> c0;
-  CompTile<cbits<CB, (NC > 1 ? 1 : 0)>()> c1;
-  CompTile<cbits<CB, (NC > 2 ? 2 : 0)>()> c2;
-  CompTile<cbits<CB, (NC > 3 ? 3 : 0)>()> c3;
+  CompTile<ckind<CB, 0>()> c0;
+  CompTile<ckind<CB, (NC > 1 ? 1 : 0)>()> c1;
+  CompTile<ckind<CB, (NC > 2 ? 2 : 0)>()> c2;
+  CompTile<ckind<CB, (NC > 3 ? 3 : 0)>()> c3;
 };
 
 template <int D, int NC, uint32_t CB>
 __device__ __forceinline__ void load_tile(Tile<D, NC, CB>& T, const CompRsrc (&R)[NC], const Offs& o) {
-  load_comp<D, cbits<CB, 0>()>(T.c0, R[0], false, o);
-  if constexpr (NC > 1) load_comp<D, cbits<CB, 1>()>(T.c1, R[1], true, o);
-  if constexpr (NC > 2) load_comp<D, cbits<CB, 2>()>(T.c2, R[2], true, o);
-  if constexpr (NC > 3) load_comp<D, cbits<CB, 3>()>(T.c3, R[3], true, o);
+  load_comp<D, ckind<CB, 0>()>(T.c0, R[0], false, o);
+  if constexpr (NC > 1) load_comp<D, ckind<CB, 1>()>(T.c1, R[1], true, o);
+  if constexpr (NC > 2) load_comp<D, ckind<CB, 2>()>(T.c2, R[2], true, o);
+  if constexpr (NC > 3) load_comp<D, ckind<CB, 3>()>(T.c3, R[3], true, o);
 }
 
 // Waves per SIMD the register budget is tuned for: three for plans whose tile
@@ -280,7 +341,7 @@ __device__ __forceinline__ void load_tile(Tile<D, NC, CB>& T, const CompRsrc (&R
 template <int NC, uint32_t CB>
 constexpr int waves_for() {
   int bits = 0;
-  for (int c = 0; c < NC; ++c) bits += (int)((CB >> (4 * c)) & 0xF);
+  for (int c = 0; c < NC; ++c) bits += kbits((int)((CB >> (4 * c)) & 0xF));
   return (NC <= 2 && bits <= 6) ? RQ_WAVES_SMALL : 2;
 }
 
@@ -316,10 +377,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
   const bool lane_on = pi < TPW;
   const int gsel = lane_on ? gi : 0;
   CompRsrc R[NC];
-  R[0] = comp_rsrc<D, cbits<CB, 0>()>(p, 0, row0, ntok);
-  if constexpr (NC > 1) R[1] = comp_rsrc<D, cbits<CB, (NC > 1 ? 1 : 0)>()>(p, 1, row0, ntok);
-  if constexpr (NC > 2) R[2] = comp_rsrc<D, cbits<CB, (NC > 2 ? 2 : 0)>()>(p, 2, row0, ntok);
-  if constexpr (NC > 3) R[3] = comp_rsrc<D, cbits<CB, (NC > 3 ? 3 : 0)>()>(p, 3, row0, ntok);
+  R[0] = comp_rsrc<D, ckind<CB, 0>()>(p, 0, row0, ntok);
+  if constexpr (NC > 1) R[1] = comp_rsrc<D, ckind<CB, (NC > 1 ? 1 : 0)>()>(p, 1, row0, ntok);
+  if constexpr (NC > 2) R[2] = comp_rsrc<D, ckind<CB, (NC > 2 ? 2 : 0)>()>(p, 2, row0, ntok);
+  if constexpr (NC > 3) R[3] = comp_rsrc<D, ckind<CB, (NC > 3 ? 3 : 0)>()>(p, 3, row0, ntok);
 
   auto fetch = [&](Tile<D, NC, CB>& T, int base) {
     const uint32_t rel = (uint32_t)(base - start) + (uint32_t)pi;  // row of token t0 in the range
@@ -374,7 +435,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
   // multiplies the group offsets, is the sum of the same fixed-point values, so a
   // stored value o + s c meets one consistent q'.
   QFix Q;
-  float qsum, qscale;
+  float qsum, qscale, qsum_h[2];  // qsum_h: the two 16-channel halves of the lane's block
   {
     float qv[32], mx = 0.0f;
 #pragma unroll
@@ -387,11 +448,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
     const int E = mx > 0.0f ? kFixBits - ex : 0;    // |q' 2^E| < 2^kFixBits
     qscale = ldexpf(1.0f, -E);
     int lm[kLimbs][32];
-    int vsum = 0;
+    int vsum = 0, vsum_h[2] = {0, 0};
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
       int v = __float2int_rn(ldexpf(qv[e], E));
       vsum += v;
+      vsum_h[e >> 4] += v;
 #pragma unroll
       for (int l = kLimbs - 1; l >= 0; --l) {      // balanced base-256 digits, least significant first
         const int d = l == 0 ? v : ((v + 128) & 255) - 128;
@@ -400,6 +462,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
       }
     }
     qsum = (float)vsum * qscale;
+    qsum_h[0] = (float)vsum_h[0] * qscale;
+    qsum_h[1] = (float)vsum_h[1] * qscale;
     auto pack = [](int a, int b, int c, int d) {
       return (uint32_t)(a & 255) | ((uint32_t)(b & 255) << 8) | ((uint32_t)(c & 255) << 16) | ((uint32_t)d << 24);
     };
@@ -417,13 +481,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
         for (int f = 0; f < 4; ++f)
           Q.q2[j][f][l] = pack(lm[l][int2_elem(j, f, 0)], lm[l][int2_elem(j, f, 1)], lm[l][int2_elem(j, f, 2)],
                                lm[l][int2_elem(j, f, 3)]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+          Q.q2h[j][f][l] = pack(lm[l][int2h_elem(j, f, 0)], lm[l][int2h_elem(j, f, 1)],
+                                lm[l][int2h_elem(j, f, 2)], lm[l][int2h_elem(j, f, 3)]);
     }
   }
 
   float acc[32];
 #pragma unroll
   for (int e = 0; e < 32; ++e) acc[e] = 0.0f;
-  float bias = 0.0f, lsum = 0.0f, m = -INFINITY;
+  // Offsets enter one sum per 16-channel half of the block; with groups of 32
+  // only, both halves share bias[0].
+  constexpr bool G16 = any_g16<CB, NC>();
+  float bias[2] = {0.0f, 0.0f};
+  float lsum = 0.0f, m = -INFINITY;
   auto process = [&](Tile<D, NC, CB>& T, int base) {
     const int t0 = base + pi, t1 = t0 + TPW;
     const bool ok0 = lane_on && t0 < end, ok1 = lane_on && t1 < end;
@@ -431,16 +505,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
     // ---- keys: per-component partial scores of this lane's group
     float kp0[NC], kp1[NC];
     float kb0[NC], kb1[NC], vb0[NC], vb1[NC];  // beta weights, K and V
-    auto kpart = [&](auto& C, int c, auto bits_tag) {
-      constexpr int BB = decltype(bits_tag)::value;
-      const float d0 = (float)kdot<BB>(C.k0, Q), d1 = (float)kdot<BB>(C.k1, Q);
-      kp0[c] = fmaf(f16hi(C.km0) * qscale, d0, f16lo(C.km0) * qsum);
-      kp1[c] = fmaf(f16hi(C.km1) * qscale, d1, f16lo(C.km1) * qsum);
+    auto kpart = [&](auto& C, int c, auto kind_tag) {
+      constexpr int KK = decltype(kind_tag)::value;
+      if constexpr (kg16(KK)) {
+        int a0, b0, a1, b1;
+        kdot16(C.k0, Q, a0, b0);
+        kdot16(C.k1, Q, a1, b1);
+        kp0[c] = fmaf(f16hi(C.km0[0]) * qscale, (float)a0, f16lo(C.km0[0]) * qsum_h[0]) +
+                 fmaf(f16hi(C.km0[1]) * qscale, (float)b0, f16lo(C.km0[1]) * qsum_h[1]);
+        kp1[c] = fmaf(f16hi(C.km1[0]) * qscale, (float)a1, f16lo(C.km1[0]) * qsum_h[0]) +
+                 fmaf(f16hi(C.km1[1]) * qscale, (float)b1, f16lo(C.km1[1]) * qsum_h[1]);
+      } else {
+        const float d0 = (float)kdot<kbits(KK)>(C.k0, Q), d1 = (float)kdot<kbits(KK)>(C.k1, Q);
+        kp0[c] = fmaf(f16hi(C.km0[0]) * qscale, d0, f16lo(C.km0[0]) * qsum);
+        kp1[c] = fmaf(f16hi(C.km1[0]) * qscale, d1, f16lo(C.km1[0]) * qsum);
+      }
     };
-    kpart(T.c0, 0, std::integral_constant<int, cbits<CB, 0>()>{});
-    if constexpr (NC > 1) kpart(T.c1, 1, std::integral_constant<int, cbits<CB, 1>()>{});
-    if constexpr (NC > 2) kpart(T.c2, 2, std::integral_constant<int, cbits<CB, 2>()>{});
-    if constexpr (NC > 3) kpart(T.c3, 3, std::integral_constant<int, cbits<CB, 3>()>{});
+    kpart(T.c0, 0, std::integral_constant<int, ckind<CB, 0>()>{});
+    if constexpr (NC > 1) kpart(T.c1, 1, std::integral_constant<int, ckind<CB, 1>()>{});
+    if constexpr (NC > 2) kpart(T.c2, 2, std::integral_constant<int, ckind<CB, 2>()>{});
+    if constexpr (NC > 3) kpart(T.c3, 3, std::integral_constant<int, ckind<CB, 3>()>{});
     kb0[NC - 1] = kb1[NC - 1] = vb0[NC - 1] = vb1[NC - 1] = 1.0f;
     if constexpr (NC > 3) {
       kb0[2] = f16u(T.c3.ka0); kb1[2] = f16u(T.c3.ka1); vb0[2] = f16u(T.c3.va0); vb1[2] = f16u(T.c3.va1);
@@ -471,7 +555,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
       const float f = __builtin_amdgcn_exp2f(m - tmax);
       m = tmax;
       lsum *= f;
-      bias *= f;
+      bias[0] *= f;
+      if constexpr (G16) bias[1] *= f;
 #pragma unroll
       for (int e = 0; e < 32; ++e) acc[e] *= f;
     }
@@ -479,53 +564,60 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
     const float p1 = ok1 ? __builtin_amdgcn_exp2f(s1 - m) : 0.0f;
     lsum += p0 + p1;
 
-    // ---- values: code part through dot2 with fp16 weights W = 2^6 p beta s, and the
-    // offset part from the same rounded W: bias += W (o/s) 2^-6 = ptilde beta o with
-    // ptilde = W / (2^6 beta s). Every stored value o + s c of a token is thus weighted
-    // by one ptilde (fp16-rounded p), so rounding W costs a relative 2^-11 of the value
-    // rather than of its code part s c. Subnormal W (tiny contributions, or s == 0)
-    // take the exact p beta o instead.
-    // Weights in fp32: token t of component c contributes p_t beta_c (o + s c) to
-    // every element of the group. The code part goes through the mixed-precision
+    // ---- values. Token t of component c contributes p_t beta_c (o + s c) to
+    // every element of a group. The code part goes through the mixed-precision
     // FMA (fp16 code operand, fp32 weight p beta s, fp32 accumulate, one rounding)
-    // and the offset part into one sum per lane, both exact to fp32 rounding.
-    // (v_dot2c_f32_f16 would take two tokens per instruction with fp16 weights,
-    // but with subnormal operands it rounds a small addend into a large
-    // accumulator low by about two ulps, measured; over a long range that biased
-    // the outputs by 1e-3 at 16k tokens.)
-    float Wa[NC], Wb[NC];
-    auto vweight = [&](auto& C, int c) {
+    // and the offset part into one sum per lane (per half with groups of 16),
+    // both exact to fp32 rounding. (v_dot2c_f32_f16 would take two tokens per
+    // instruction with fp16 weights, but with subnormal operands it rounds a small
+    // addend into a large accumulator low by about two ulps, measured; over a long
+    // range that biased the outputs by 1e-3 at 16k tokens.)
+    float Wa[NC][2], Wb[NC][2];  // [component][half of the block]
+    auto vweight = [&](auto& C, int c, auto kind_tag) {
+      constexpr int KK = decltype(kind_tag)::value;
       const float pb0 = ok0 ? p0 * vb0[c] : 0.0f, pb1 = ok1 ? p1 * vb1[c] : 0.0f;
-      Wa[c] = pb0 * f16hi(C.vm0);
-      Wb[c] = pb1 * f16hi(C.vm1);
-      bias = fmaf(pb0, f16lo(C.vm0), bias);
-      bias = fmaf(pb1, f16lo(C.vm1), bias);
+#pragma unroll
+      for (int hh = 0; hh < (kg16(KK) ? 2 : 1); ++hh) {
+        Wa[c][hh] = pb0 * f16hi(C.vm0[hh]);
+        Wb[c][hh] = pb1 * f16hi(C.vm1[hh]);
+        const float ob = fmaf(pb0, f16lo(C.vm0[hh]), pb1 * f16lo(C.vm1[hh]));
+        if constexpr (kg16(KK)) {
+          bias[hh] += ob;
+        } else {
+          bias[0] += ob;
+          if constexpr (G16) bias[1] += ob;
+        }
+      }
+      if constexpr (!kg16(KK)) {
+        Wa[c][1] = Wa[c][0];
+        Wb[c][1] = Wb[c][0];
+      }
     };
-    vweight(T.c0, 0);
-    if constexpr (NC > 1) vweight(T.c1, 1);
-    if constexpr (NC > 2) vweight(T.c2, 2);
-    if constexpr (NC > 3) vweight(T.c3, 3);
+    vweight(T.c0, 0, std::integral_constant<int, ckind<CB, 0>()>{});
+    if constexpr (NC > 1) vweight(T.c1, 1, std::integral_constant<int, ckind<CB, 1>()>{});
+    if constexpr (NC > 2) vweight(T.c2, 2, std::integral_constant<int, ckind<CB, 2>()>{});
+    if constexpr (NC > 3) vweight(T.c3, 3, std::integral_constant<int, ckind<CB, 3>()>{});
 
 #pragma unroll
     for (int half = 0; half < 2; ++half)
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
         uint32_t x[NC][4];
-        vpairs<cbits<CB, 0>(), REF>(T.c0.v0, T.c0.v1, half, blk, x[0]);
-        if constexpr (NC > 1) vpairs<cbits<CB, 1>(), REF>(T.c1.v0, T.c1.v1, half, blk, x[1]);
-        if constexpr (NC > 2) vpairs<cbits<CB, 2>(), REF>(T.c2.v0, T.c2.v1, half, blk, x[2]);
-        if constexpr (NC > 3) vpairs<cbits<CB, 3>(), REF>(T.c3.v0, T.c3.v1, half, blk, x[3]);
+        vpairs<ckind<CB, 0>(), REF>(T.c0.v0, T.c0.v1, half, blk, x[0]);
+        if constexpr (NC > 1) vpairs<ckind<CB, 1>(), REF>(T.c1.v0, T.c1.v1, half, blk, x[1]);
+        if constexpr (NC > 2) vpairs<ckind<CB, 2>(), REF>(T.c2.v0, T.c2.v1, half, blk, x[2]);
+        if constexpr (NC > 3) vpairs<ckind<CB, 3>(), REF>(T.c3.v0, T.c3.v1, half, blk, x[3]);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float& a = acc[16 * half + 4 * blk + q];
           auto comp = [&](int c, bool w4) {
-            a = fmaf(f16lo(x[c][q]), w4 ? 4.0f * Wa[c] : Wa[c], a);
-            a = fmaf(f16hi(x[c][q]), w4 ? 4.0f * Wb[c] : Wb[c], a);
+            a = fmaf(f16lo(x[c][q]), w4 ? 4.0f * Wa[c][half] : Wa[c][half], a);
+            a = fmaf(f16hi(x[c][q]), w4 ? 4.0f * Wb[c][half] : Wb[c][half], a);
           };
-          comp(0, vw4<cbits<CB, 0>(), REF>(q));
-          if constexpr (NC > 1) comp(1, vw4<cbits<CB, (NC > 1 ? 1 : 0)>(), REF>(q));
-          if constexpr (NC > 2) comp(2, vw4<cbits<CB, (NC > 2 ? 2 : 0)>(), REF>(q));
-          if constexpr (NC > 3) comp(3, vw4<cbits<CB, (NC > 3 ? 3 : 0)>(), REF>(q));
+          comp(0, vw4<kbits(ckind<CB, 0>()), REF>(q));
+          if constexpr (NC > 1) comp(1, vw4<kbits(ckind<CB, (NC > 1 ? 1 : 0)>()), REF>(q));
+          if constexpr (NC > 2) comp(2, vw4<kbits(ckind<CB, (NC > 2 ? 2 : 0)>()), REF>(q));
+          if constexpr (NC > 3) comp(3, vw4<kbits(ckind<CB, (NC > 3 ? 3 : 0)>()), REF>(q));
         }
       }
   };
@@ -559,7 +651,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
 
   float val[32];
 #pragma unroll
-  for (int e = 0; e < 32; ++e) val[e] = fmaf(acc[e], kTwo24 / vclass<REF>(e), bias);
+  for (int e = 0; e < 32; ++e) val[e] = fmaf(acc[e], kTwo24 / vclass<REF>(e), bias[G16 ? (e >> 4) : 0]);
   write_partial<D, 32, G, TPW>(val, (lane_on && gi == 0) ? lsum : 0.0f, m, lane_on, red, S,
                                p.part + ((size_t)bh * p.nsplit + split) * part_floats(D));
 }
@@ -667,10 +759,13 @@ struct Entry {
 #define RQ_DEPTH 2
 #endif
 #define RQ_E(D, NC, CB) {D, NC, CB, decode_fused<D, NC, CB, RQ_DEPTH>}
+// Plans: one nibble per component, anchor first (0xA = INT2 in groups of 16).
 #define RQ_PLANS(D)                                                                                        \
   RQ_E(D, 1, 0x2), RQ_E(D, 1, 0x4), RQ_E(D, 2, 0x22), RQ_E(D, 2, 0x24), RQ_E(D, 2, 0x42), RQ_E(D, 2, 0x44), \
       RQ_E(D, 3, 0x244), RQ_E(D, 3, 0x224), RQ_E(D, 3, 0x222), RQ_E(D, 3, 0x444), RQ_E(D, 4, 0x2244),        \
-      RQ_E(D, 4, 0x2224), RQ_E(D, 4, 0x2222), RQ_E(D, 4, 0x4444)
+      RQ_E(D, 4, 0x2224), RQ_E(D, 4, 0x2222), RQ_E(D, 4, 0x4444),                                           \
+      RQ_E(D, 1, 0xA), RQ_E(D, 2, 0xAA), RQ_E(D, 2, 0xA4), RQ_E(D, 3, 0xAA4), RQ_E(D, 4, 0xAAA4),          \
+      RQ_E(D, 3, 0xAAA), RQ_E(D, 4, 0xAAAA)
 
 const Entry kTable[] = {RQ_PLANS(64), RQ_PLANS(96), RQ_PLANS(128)};
 

@@ -100,6 +100,7 @@ struct AppendParams {
   int32_t* dev_err;
   int B, H, L, n, T_max, policy;
   int G;                    // loops per anchor group (divides L)
+  uint32_t g16;             // bit r: loop r is INT2 in groups of 16 channels (else groups of 32)
   int bits[RQ_MAX_LOOPS];
 };
 

@@ -33,9 +33,9 @@
  *     in a hipGraph and replayed. Kernels clamp them to [0, max_tokens] and, if
  *     `dev_err` (device int32, may be NULL) is given, OR an RQ_DEVERR_* bit into it.
  *   - Alignment of device arrays: codes, rot, kv, q, k_cur, v_cur, k_cache and
- *     v_cache 16 bytes; meta and out 4 bytes; alpha 2 bytes; the
- *     workspace 256 bytes. Otherwise the call returns RQ_E_ALIGN (RQ_E_WORKSPACE
- *     for the workspace). Every allocation of the HIP or torch allocators meets this.
+ *     v_cache 16 bytes; meta 4 bytes (8 for loops in groups of 16); out 4
+ *     bytes; alpha 2 bytes; the workspace 256 bytes. Otherwise the call
+ *     returns RQ_E_ALIGN (RQ_E_WORKSPACE for the workspace). Every allocation of the HIP or torch allocators meets this.
  *   - No C++ exception crosses this interface.
  *
  * Data types: bf16 and fp16 values travel as uint16_t bit patterns.
@@ -94,7 +94,8 @@ typedef struct {
                         * Loops gG .. gG+G-1 (0-based) are quantized against an anchor of their own
                         * (§5 "Models": a model with many loops, e.g. 32, split into groups of 4). */
   uint8_t bits[RQ_MAX_LOOPS];   /* bit width per loop (0-based), 2 or 4 (§2.1, §3.4) */
-  uint8_t group[RQ_MAX_LOOPS];  /* group size per loop along the rotated head_dim: 32 */
+  uint8_t group[RQ_MAX_LOOPS];  /* group size per loop along the rotated head_dim: 32, or 16 for
+                                 * 2-bit loops (§5 "Quantization setup": g = 16 for INT2) */
 } rq_desc;
 
 /* Device buffers of one layer's compressed cache. kv index 0 = keys, 1 = values;

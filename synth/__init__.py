@@ -53,10 +53,15 @@ class Workload:
     nb: int = 0                 # Hadamard block size (0 -> D)
     seed: int = 0
     loop_group: int = 0         # loops per anchor group (0 -> all L loops)
+    int2_group: int = 32        # group size of the 2-bit loops (16 or 32); 4-bit loops use `group`
 
     @property
     def G(self) -> int:
         return self.loop_group or self.L
+
+    def groups_for(self, bits) -> list:
+        """Group size of every loop of a bit plan."""
+        return [self.int2_group if b == 2 else self.group for b in bits]
 
     @property
     def block(self) -> int:
@@ -87,6 +92,9 @@ WORKLOADS = {
     # Ouro-1.4B-shaped fixed batch, 16k context, 64 decode steps, [2,2,4,4]
     "ouro_16k": Workload("ouro_16k", 24, 8, 16, 128, 4, 16384, 64, (2, 2, 4, 4), (4, 4, 2, 2)),
     # Ouro-1.4B-shaped capacity sweep at 8k context (batch set per run)
+    # the 16k workload with the 2-bit residual loops in groups of 16 channels
+    "ouro_16k_g16": Workload("ouro_16k_g16", 24, 8, 16, 128, 4, 16384, 64, (2, 2, 4, 4), (4, 4, 2, 2),
+                             int2_group=16),
     "ouro_8k_capacity": Workload("ouro_8k_capacity", 24, 16, 16, 128, 4, 8192, 8, (2, 2, 4, 4), (4, 4, 2, 2)),
     # Huginn-3.5B-shaped: 4 layers, 55 heads, D96 (three 32x32 blocks), 8 recurrences
     "huginn_4k": Workload("huginn_4k", 4, 4, 55, 96, 8, 4096, 1, (2, 2, 2, 2, 2, 2, 4, 4),

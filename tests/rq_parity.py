@@ -61,13 +61,14 @@ def _ambiguous(pre: float, mode: int) -> bool:
     return a[0] != a[1]
 
 
-def oracle_series_for(X: np.ndarray, H: np.ndarray, bits, policy, loop_group: int = 0) -> O.Series:
-    cfg = O.Config(D=X.shape[-1], bits=list(bits), policy=policy, loop_group=loop_group)
+def oracle_series_for(X: np.ndarray, H: np.ndarray, bits, policy, loop_group: int = 0, groups=32) -> O.Series:
+    groups = list(groups) if isinstance(groups, (list, tuple)) else groups
+    cfg = O.Config(D=X.shape[-1], bits=list(bits), group=groups, policy=policy, loop_group=loop_group)
     return O.quantize_series(cfg, X, H, diagnostics=True)
 
 
 def oracle_layer(Xall: torch.Tensor, rot_k: torch.Tensor, rot_v: torch.Tensor, bits, policy, T: int,
-                 units=None, threads: int = 16, loop_group: int = 0):
+                 units=None, threads: int = 16, loop_group: int = 0, groups=32):
     """Oracle caches for (kv, b, h) series of tokens [0, T). Xall: bf16 [2][L][B][H][>=T][D]."""
     X = Xall[..., :T, :]
     _, L, B, H, _, D = X.shape
@@ -78,7 +79,8 @@ def oracle_layer(Xall: torch.Tensor, rot_k: torch.Tensor, rot_v: torch.Tensor, b
 
     def run(job):
         kv, b, h = job
-        return job, oracle_series_for(Xc[(b, h)][kv], (Hk if kv == 0 else Hv)[h], bits, policy, loop_group)
+        return job, oracle_series_for(Xc[(b, h)][kv], (Hk if kv == 0 else Hv)[h], bits, policy, loop_group,
+                                      groups)
 
     with ThreadPoolExecutor(max_workers=threads) as ex:
         return dict(ex.map(run, jobs))
@@ -101,7 +103,7 @@ def compare_cache(cache: rq.LayerCache, series: dict, T: int, host: dict | None 
     for (kv, b, h), s in series.items():
         for r in range(L):
             gc, gm, ga = host[(kv, r)]
-            bits = d.bits[r]
+            bits, g = d.bits[r], d.group[r]
             skip_tok = np.zeros(T, bool)
             if r != rq.anchor_of(d, r):
                 oa = s.alpha[r][:T]
@@ -128,21 +130,20 @@ def compare_cache(cache: rq.LayerCache, series: dict, T: int, host: dict | None 
             oc = s.codes[r][:T]
             gcc = gc[b, h, :T]
             rows = np.nonzero(np.any(oc != gcc, axis=1))[0]
-            G = D // 32
             stats["elements"] += T * D
-            stats["exempt_elements"] += int(skip_tok.sum()) * D + int(grp_skip.sum()) * 32
+            stats["exempt_elements"] += int(skip_tok.sum()) * D + int(grp_skip.sum()) * g
             for t in rows:
                 if skip_tok[t]:
                     continue
-                a = unpack_np(oc[t], D, bits)
-                g = unpack_np(gcc[t], D, bits)
-                for e in np.nonzero(a != g)[0]:
-                    if grp_skip[t, e // 32]:
+                a = unpack_np(oc[t], D, bits, g)
+                gg = unpack_np(gcc[t], D, bits, g)
+                for e in np.nonzero(a != gg)[0]:
+                    if grp_skip[t, e // g]:
                         continue
                     if s.delta[r, t, e] < CODE_DELTA:
                         stats["exempt_elements"] += 1
                     else:
-                        stats["bad"].append(("code", kv, b, h, r, int(t), int(e), int(a[e]), int(g[e])))
+                        stats["bad"].append(("code", kv, b, h, r, int(t), int(e), int(a[e]), int(gg[e])))
     return stats
 
 
@@ -179,12 +180,13 @@ def max_rel_err(gpu_out: torch.Tensor, ref: dict) -> float:
 
 
 def build_gpu_layer(X: torch.Tensor, rot_k, rot_v, bits, policy, T_max: int, T: int,
-                    steps_of_one: int = 0, pos0=None, chunk: int = 1, loop_group: int = 0) -> rq.LayerCache:
+                    steps_of_one: int = 0, pos0=None, chunk: int = 1, loop_group: int = 0,
+                    groups=32) -> rq.LayerCache:
     """Fill a GPU cache with tokens [0, T) of X (bf16 [2][L][B][H][*][D] on the GPU): one
     bulk append of the first T - steps_of_one tokens, then appends of `chunk` tokens
     (the last one shorter) until T."""
     _, L, B, H, _, D = X.shape
-    d = rq.make_desc(B, H, D, bits, T_max, policy, loop_group=loop_group)
+    d = rq.make_desc(B, H, D, bits, T_max, policy, group=groups, loop_group=loop_group)
     cache = rq.LayerCache.allocate(d, rot_k, rot_v)
     n0 = T - steps_of_one
     pos = torch.zeros(B, dtype=torch.int32, device="cuda") if pos0 is None else pos0

@@ -72,10 +72,38 @@ def test_anchor_of(policy, G, L, expect):
     assert [rq.anchor_of(d, r) for r in range(L)] == expect
 
 
-def test_group_must_be_32():
-    d = _desc()
+def test_group_sizes():
+    """Groups of 32 everywhere, or 16 for 2-bit loops (INT4 stays at 32)."""
+    d = _desc()                                   # bits [2, 2, 4, 4]
     d.group[1] = 16
+    assert rq.check_desc(d) == 0
+    d.group[2] = 16
     assert rq.check_desc(d) == 3
+    d.group[2] = 32
+    d.group[0] = 64
+    assert rq.check_desc(d) == 3
+    d.group[0] = 8
+    assert rq.check_desc(d) == 3
+    assert rq.check_desc(_desc(group=[16, 16, 32, 32])) == 0
+    assert rq.buffer_bytes(_desc(group=[16, 16, 32, 32]), 1, 0) == 2 * 3 * 100 * 8 * 4
+    with pytest.raises(ValueError):
+        _desc(group=[16, 32])
+
+
+def test_group16_meta_alignment():
+    """Metadata of a loop in groups of 16 is read 8 bytes at a time: 8-byte alignment."""
+    L, by = rq.lib, ctypes.byref
+    d = _desc(group=[16, 16, 32, 32])
+    c = _cache(d)
+    c.meta[1][0] = 0x100004                       # 4-byte aligned only
+    assert L.rq_quantize_append(by(d), by(c), FAKE, FAKE, 1, None, 0) == 10
+    ws = rq.workspace_bytes(d)
+    assert L.rq_decode_attn(by(d), by(c), 0, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE, ws,
+                            None, 0) == 10
+    c.meta[1][0] = 0x100000
+    c.meta[1][2] = 0x100004                       # groups of 32: 4 bytes suffice, the next check fails
+    c.codes[1][3] = 0x100004
+    assert L.rq_quantize_append(by(d), by(c), FAKE, FAKE, 1, None, 0) == 10
 
 
 def test_buffer_and_workspace_sizes():

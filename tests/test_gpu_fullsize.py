@@ -50,7 +50,7 @@ def _build(layer, policy, bits, w=W):
     T_max = T + STEPS
     X = synth.kv(w, layer, 0, T_max, device="cuda")
     rk, rv = synth.rotation(w, layer, 0), synth.rotation(w, layer, 1)
-    d = rq.make_desc(B, H, D, list(bits), T_max, policy, loop_group=w.loop_group)
+    d = rq.make_desc(B, H, D, list(bits), T_max, policy, group=w.groups_for(bits), loop_group=w.loop_group)
     cache = rq.LayerCache.allocate(d, rk, rv)
     log(f"layer {layer} policy {policy}: bulk store of {T} tokens")
     rq.quantize_append(cache, X[..., :T, :].contiguous(), torch.zeros(B, dtype=torch.int32, device="cuda"), T)
@@ -88,7 +88,8 @@ def _check(layer, policy, bits, units, label, w=W):
     for i in range(0, len(units), 16):
         chunk = units[i:i + 16]
         log(f"{label}: oracle for units {i}..{i + len(chunk) - 1} of {len(units)}")
-        series = oracle_layer(X, rk, rv, bits, policy, Tc, units=chunk, loop_group=w.loop_group)
+        series = oracle_layer(X, rk, rv, bits, policy, Tc, units=chunk, loop_group=w.loop_group,
+                              groups=w.groups_for(bits))
         assert_cache_parity(compare_cache(cache, series, Tc, host=host), f"{label} units {i}+")
         for (k, r), (out, q, kc, vc) in outs.items():
             lens = [w.T + k] * w.batch
@@ -127,6 +128,13 @@ def test_huginn32_groups_sampled(policy):
     w = synth.WORKLOADS["huginn32_4k"]
     bits = w.bits if policy == LAST else w.chained_bits
     _check(0, policy, bits, _sample_units(6, 13 + policy, w), f"huginn32 G4 policy={policy}", w)
+
+
+def test_ouro_16k_group16_sampled():
+    """The 16k workload with its 2-bit loops in groups of 16 channels: layer 0, sampled
+    series, every loop."""
+    w = synth.WORKLOADS["ouro_16k_g16"]
+    _check(0, LAST, w.bits, _sample_units(8, 17, w), "16k g16", w)
 
 
 def test_capacity_8k_batch64_sampled():
