@@ -88,7 +88,7 @@ COPY_KIB = float(1 << 20)            # 1 GiB read and 1 GiB written by the calib
 PROFILES = os.path.join(ROOT, "profiles")
 FETCH_FILE = os.path.join(PROFILES, "decode_fused_loop1_ouro_16k_fetch_size.txt")
 WRITE_FILE = os.path.join(PROFILES, "decode_fused_loop1_ouro_16k_write_size.txt")
-KERNEL_SOURCES = ["rq_decode.hip", "rq_combine.hpp", "rq_device.hpp", "rq_internal.hpp"]
+KERNEL_SOURCES = ["rq_decode.hip", "rq_decode_kernel.hpp", "rq_combine.hpp", "rq_device.hpp", "rq_internal.hpp"]
 
 
 def kernel_source_hash():
@@ -200,6 +200,8 @@ def main():
     ap.add_argument("--workload", default="ouro_16k")
     ap.add_argument("--layers", type=int, default=0, help="override layer count (0: workload's)")
     ap.add_argument("--batch", type=int, default=0, help="override batch (0: workload's)")
+    ap.add_argument("--block-size", type=int, default=0,
+                    help="paged compressed caches with blocks of this many tokens over a shuffled pool (0: contiguous)")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-chained", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -233,6 +235,9 @@ def main():
         w = w.with_(batch=args.batch)
     B, H, D, L, T, K = w.batch, w.heads, w.D, w.L, w.T, args.steps
     T_max = T + max(K, args.warmup)
+    BS = args.block_size
+    if BS:
+        T_max = -(-T_max // BS) * BS
     dev = "cuda"
     torch.cuda.set_device(0)
     scale = 1.0 / math.sqrt(D)
@@ -243,8 +248,16 @@ def main():
     G = w.loop_group
     gr, cgr = w.groups_for(bits), w.groups_for(cbits)
     run_chained = not args.no_chained and (G or L) <= 4
-    d_rq = rq.make_desc(B, H, D, bits, T_max, rq.POLICY_LAST_LOOP, group=gr, loop_group=G)
-    d_ch = rq.make_desc(B, H, D, cbits, T_max, rq.POLICY_PREV_LOOP, group=cgr, loop_group=G)
+    table, nblocks = None, 0
+    if BS:
+        # a serving engine's block table: every sequence's blocks scattered over one pool
+        nblocks = B * (T_max // BS)
+        perm = torch.randperm(nblocks, generator=torch.Generator().manual_seed(1234)).to(torch.int32)
+        table = perm.view(B, T_max // BS).to(dev)
+    d_rq = rq.make_desc(B, H, D, bits, T_max, rq.POLICY_LAST_LOOP, group=gr, loop_group=G, block_size=BS,
+                        num_blocks=nblocks)
+    d_ch = rq.make_desc(B, H, D, cbits, T_max, rq.POLICY_PREV_LOOP, group=cgr, loop_group=G, block_size=BS,
+                        num_blocks=nblocks)
     caches, chained, bf16, rots = [], [], [], []
     kvcur = torch.empty(K, w.layers, 2, L, B, H, 1, D, dtype=torch.bfloat16, device=dev)
     qs = torch.empty(K, w.layers, L, B, H, D, dtype=torch.bfloat16, device=dev)
@@ -253,11 +266,11 @@ def main():
         X = synth.kv(w, l, 0, T_max, device=dev)                      # [2][L][B][H][T_max][D]
         rk, rv = synth.rotation(w, l, 0), synth.rotation(w, l, 1)
         past = X[..., :T, :].contiguous()
-        c = rq.LayerCache.allocate(d_rq, rk, rv)
+        c = rq.LayerCache.allocate(d_rq, rk, rv, block_table=table)
         rq.quantize_append(c, past, pos0, T)
         caches.append(c)
         if run_chained:
-            cc = rq.LayerCache.allocate(d_ch, rk, rv)
+            cc = rq.LayerCache.allocate(d_ch, rk, rv, block_table=table)
             rq.quantize_append(cc, past, pos0, T)
             chained.append(cc)
         del past
@@ -346,7 +359,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": dt_rq * 1e3 / K, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "layers": w.layers, "batch": B, "heads": H, "head_dim": D, "loops": L,
-                   "loop_group": G or L, "context": T, "bits": bits, "group": gr,
+                   "loop_group": G or L, "context": T, "bits": bits, "group": gr, "block_size": BS,
                    "codes": "int2/int4 + fp16 scale/offset + fp16 alpha",
                    "arith": "keys: int8 dot products with a 14-bit fixed-point rotated query; values: fp32 "
                             "multiply-adds of fp16-exact codes; fp32 softmax and accumulation"},
@@ -425,11 +438,12 @@ def main():
         percall[r] = {"kernel_ms": ms_k, "combine_ms": ms_c, "call_ms": ms_call, "bytes": nbytes,
                       "kernel_gbps": nbytes / (ms_k * 1e-3) / 1e9}
     dom = percall[0]
-    traffic = profiled_traffic(w.name)
+    traffic = None if BS else profiled_traffic(w.name)
     result["roofline"] = {"bound": "hbm", "achieved": dom["kernel_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                           "frac": dom["kernel_gbps"] / HBM_PEAK_GBPS,
                           "traffic": None if traffic is None else traffic["bytes"],
-                          "kernel": dom_kernel_name(D, bits, G, gr) + " (rq_decode_attn_partial, loop 1: "
+                          "kernel": dom_kernel_name(D, bits, G, gr).replace("fused", "fused_paged" if BS else "fused")
+                                    + " (rq_decode_attn_partial, loop 1: "
                                     f"INT{bits[(G or L) - 1]} anchor + INT{bits[0]} residual, K and V)",
                           "bytes_per_launch": dom["bytes"], "ms_per_launch": dom["kernel_ms"],
                           "traffic_source": None if traffic is None else traffic["source"]}

@@ -25,7 +25,7 @@ STATUS = {0: "RQ_OK", 1: "RQ_E_NULL", 2: "RQ_E_SHAPE", 3: "RQ_E_BITS", 4: "RQ_E_
           5: "RQ_E_WORKSPACE", 6: "RQ_E_UNSUPPORTED", 7: "RQ_E_HIP", 8: "RQ_E_POLICY", 9: "RQ_E_LOOP",
           10: "RQ_E_ALIGN"}
 POLICY_LAST_LOOP, POLICY_PREV_LOOP, POLICY_FIRST_LOOP = 0, 1, 2
-DEVERR_CAPACITY, DEVERR_LENGTH = 1, 2
+DEVERR_CAPACITY, DEVERR_LENGTH, DEVERR_BLOCK = 1, 2, 4
 
 
 class RQError(RuntimeError):
@@ -37,12 +37,14 @@ class RQError(RuntimeError):
 class Desc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("loops", ctypes.c_int32), ("max_tokens", ctypes.c_int32), ("policy", ctypes.c_int32),
-                ("loop_group", ctypes.c_int32), ("bits", ctypes.c_uint8 * MAX_LOOPS), ("group", ctypes.c_uint8 * MAX_LOOPS)]
+                ("loop_group", ctypes.c_int32), ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("bits", ctypes.c_uint8 * MAX_LOOPS), ("group", ctypes.c_uint8 * MAX_LOOPS)]
 
 
 class LayerCacheC(ctypes.Structure):
     _fields_ = [("codes", (ctypes.c_void_p * MAX_LOOPS) * 2), ("meta", (ctypes.c_void_p * MAX_LOOPS) * 2),
-                ("alpha", (ctypes.c_void_p * MAX_LOOPS) * 2), ("rot", ctypes.c_void_p * 2)]
+                ("alpha", (ctypes.c_void_p * MAX_LOOPS) * 2), ("rot", ctypes.c_void_p * 2),
+                ("block_table", ctypes.c_void_p)]
 
 
 def _load():
@@ -90,11 +92,14 @@ def version() -> str:
 
 
 def make_desc(batch: int, heads: int, head_dim: int, bits, max_tokens: int,
-              policy: int = POLICY_LAST_LOOP, group=32, loop_group: int = 0) -> Desc:
-    """Descriptor of one layer's cache; `group` is one size for all loops or one per loop."""
+              policy: int = POLICY_LAST_LOOP, group=32, loop_group: int = 0, block_size: int = 0,
+              num_blocks: int = 0) -> Desc:
+    """Descriptor of one layer's cache; `group` is one size for all loops or one per loop;
+    block_size > 0 makes it a paged cache of num_blocks blocks (see rq.h)."""
     d = Desc()
     d.batch, d.heads, d.head_dim = batch, heads, head_dim
     d.loops, d.max_tokens, d.policy, d.loop_group = len(bits), max_tokens, policy, loop_group
+    d.block_size, d.num_blocks = block_size, num_blocks
     groups = list(group) if isinstance(group, (list, tuple)) else [group] * len(bits)
     if len(groups) != len(bits):
         raise ValueError("one group size per loop")
@@ -154,23 +159,32 @@ def _stream(stream) -> int | None:
 class LayerCache:
     """Device buffers of one layer's compressed cache (caller-owned, allocated by torch)."""
     desc: Desc
-    codes: list      # [2][L] uint8 tensors [B][H][T_max][D*bits/8]
-    meta: list       # [2][L] int16 tensors [B][H][T_max][D/32][2] (fp16 bit patterns)
+    codes: list      # [2][L] uint8 tensors [B][H][T_max][D*bits/8]  (paged: [NB][H][BS][..])
+    meta: list       # [2][L] int16 tensors [B][H][T_max][D/g][2] (fp16 bit patterns)
     alpha: list      # [2][L] int16 tensors [B][H][T_max] or None for a group's anchor
     rot: list        # [2] float32 [H][D][D]
+    block_table: torch.Tensor | None = None   # paged: int32 [B][T_max / BS]
 
     @staticmethod
-    def allocate(d: Desc, rot_k: torch.Tensor, rot_v: torch.Tensor, device="cuda") -> "LayerCache":
-        B, H, T, D, L = d.batch, d.heads, d.max_tokens, d.head_dim, d.loops
-        codes = [[torch.empty(B, H, T, D * d.bits[r] // 8, dtype=torch.uint8, device=device)
+    def allocate(d: Desc, rot_k: torch.Tensor, rot_v: torch.Tensor, device="cuda",
+                 block_table: torch.Tensor | None = None) -> "LayerCache":
+        H, D, L = d.heads, d.head_dim, d.loops
+        if d.block_size:
+            if block_table is None or block_table.dtype != torch.int32:
+                raise ValueError("a paged cache needs an int32 block table [B][max_tokens / block_size]")
+            lead = (d.num_blocks, H, d.block_size)
+        else:
+            lead = (d.batch, H, d.max_tokens)
+        codes = [[torch.empty(*lead, D * d.bits[r] // 8, dtype=torch.uint8, device=device)
                   for r in range(L)] for _ in range(2)]
-        meta = [[torch.empty(B, H, T, D // d.group[r], 2, dtype=torch.int16, device=device)
+        meta = [[torch.empty(*lead, D // d.group[r], 2, dtype=torch.int16, device=device)
                  for r in range(L)] for _ in range(2)]
-        alpha = [[None if r == anchor_of(d, r) else torch.empty(B, H, T, dtype=torch.int16, device=device)
+        alpha = [[None if r == anchor_of(d, r) else torch.empty(*lead, dtype=torch.int16, device=device)
                   for r in range(L)] for _ in range(2)]
         rot = [rot_k.to(device=device, dtype=torch.float32).contiguous(),
                rot_v.to(device=device, dtype=torch.float32).contiguous()]
-        return LayerCache(d, codes, meta, alpha, rot)
+        table = None if not d.block_size else block_table.to(device).contiguous()
+        return LayerCache(d, codes, meta, alpha, rot, table)
 
     def c(self) -> LayerCacheC:
         c = LayerCacheC()
@@ -180,6 +194,7 @@ class LayerCache:
                 c.meta[kv][r] = _ptr(self.meta[kv][r])
                 c.alpha[kv][r] = _ptr(self.alpha[kv][r])
             c.rot[kv] = _ptr(self.rot[kv])
+        c.block_table = _ptr(self.block_table)
         return c
 
     def nbytes(self) -> int:

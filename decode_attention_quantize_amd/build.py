@@ -18,6 +18,8 @@ SOURCES = {
     "rq_api.cpp": ["-x", "hip"],
     "rq_append.hip": ["-ffp-contract=off"],
     "rq_decode.hip": [],
+    "rq_decode_paged.hip": [],
+    "rq_decode_paged_tile.hip": [],
     "rq_decode_bf16.hip": [],
 }
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -53,6 +53,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 bool al(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
+int log2_of(int x) {
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
+}
+
 rq_status check_shape(const rq_desc* d) {
   if (!d) return RQ_E_NULL;
   if (d->batch < 1 || d->heads < 1 || !dim_ok(d->head_dim) || d->loops < 1 || d->loops > RQ_MAX_LOOPS ||
@@ -68,6 +74,15 @@ rq_status check_plan(const rq_desc* d) {
     return RQ_E_POLICY;
   if (d->loop_group < 0 || d->loop_group > d->loops || (d->loop_group > 0 && d->loops % d->loop_group != 0))
     return RQ_E_SHAPE;
+  if (d->block_size != 0) {  // paged cache
+    const int bs = d->block_size;
+    if (bs < 16 || bs > 4096 || (bs & (bs - 1)) != 0 || d->max_tokens % bs != 0 || d->num_blocks < 1)
+      return RQ_E_SHAPE;
+    // every pool buffer (the largest: INT4 codes, D/2 bytes per row) stays addressable by
+    // the 32-bit offsets of the decode kernel's buffer loads
+    const uint64_t rows = (uint64_t)d->num_blocks * (uint64_t)d->heads * (uint64_t)bs;
+    if (rows * (uint64_t)(d->head_dim / 2) > 0xFFFF0000ull) return RQ_E_SHAPE;
+  }
   for (int r = 0; r < d->loops; ++r) {
     if (d->bits[r] != 2 && d->bits[r] != 4) return RQ_E_BITS;
     if (d->group[r] != 32 && !(d->group[r] == 16 && d->bits[r] == 2)) return RQ_E_BITS;
@@ -153,7 +168,8 @@ rq_status rq_check_desc(const rq_desc* d) { return check_plan(d); }
 
 size_t rq_buffer_bytes(const rq_desc* d, int kind, int loop) {
   if (check_plan(d) != RQ_OK || loop < 0 || loop >= d->loops) return 0;
-  const size_t toks = (size_t)d->batch * d->heads * d->max_tokens;
+  const size_t toks = d->block_size ? (size_t)d->num_blocks * d->heads * d->block_size
+                                    : (size_t)d->batch * d->heads * d->max_tokens;
   switch (kind) {
     case 0: return toks * d->head_dim * d->bits[loop] / 8;
     case 1: return toks * (d->head_dim / d->group[loop]) * 4;
@@ -203,6 +219,14 @@ rq_status rq_quantize_append(const rq_desc* d, const rq_layer_cache* c, const ui
   p.T_max = d->max_tokens;
   p.policy = d->policy;
   p.G = group_len(d);
+  if (d->block_size) {
+    if (!c->block_table) return RQ_E_NULL;
+    if (!al(c->block_table, 4)) return RQ_E_ALIGN;
+    p.table = c->block_table;
+    p.maxblk = d->max_tokens / d->block_size;
+    p.lbs = log2_of(d->block_size);
+    p.num_blocks = d->num_blocks;
+  }
   for (int r = 0; r < d->loops; ++r) {
     p.bits[r] = d->bits[r];
     if (d->group[r] == 16) p.g16 |= 1u << r;
@@ -220,9 +244,13 @@ rq_status rq_split_plan(const rq_desc* d, int32_t* unit, int32_t* nsplit) {
   return RQ_OK;
 }
 
-rq_status rq_decode_attn_partial(const rq_desc* d, const rq_layer_cache* c, int32_t loop, const uint16_t* q,
-                                 const int32_t* past_len, float softmax_scale, void* ws, size_t ws_bytes,
-                                 void* stream) {
+}  // extern "C"
+
+namespace {
+
+rq_status decode_partial(const rq_desc* d, const rq_layer_cache* c, int32_t loop, const uint16_t* q,
+                         const int32_t* past_len, float softmax_scale, void* ws, size_t ws_bytes, int32_t* dev_err,
+                         void* stream) {
   rq_status s = check_plan(d);
   if (s != RQ_OK) return s;
   if (!c) return RQ_E_NULL;
@@ -268,7 +296,27 @@ rq_status rq_decode_attn_partial(const rq_desc* d, const rq_layer_cache* c, int3
   p.T_max = d->max_tokens;
   p.unit = sp.unit;
   p.nsplit = sp.nsplit;
+  p.dev_err = dev_err;
+  if (d->block_size) {
+    if (!c->block_table) return RQ_E_NULL;
+    if (!al(c->block_table, 4)) return RQ_E_ALIGN;
+    p.table = c->block_table;
+    p.maxblk = d->max_tokens / d->block_size;
+    p.lbs = log2_of(d->block_size);
+    p.num_blocks = d->num_blocks;
+    p.pool_rows = (uint32_t)((size_t)d->num_blocks * d->heads * d->block_size);
+  }
   return launch_decode(p, d->head_dim, nc, bits, sp.nsplit, stream) == 0 ? RQ_OK : RQ_E_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+rq_status rq_decode_attn_partial(const rq_desc* d, const rq_layer_cache* c, int32_t loop, const uint16_t* q,
+                                 const int32_t* past_len, float softmax_scale, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  return decode_partial(d, c, loop, q, past_len, softmax_scale, ws, ws_bytes, nullptr, stream);
 }
 
 rq_status rq_decode_combine(const rq_desc* d, const float* rot_v, const uint16_t* q, const uint16_t* k_cur,
@@ -301,7 +349,7 @@ rq_status rq_decode_attn(const rq_desc* d, const rq_layer_cache* c, int32_t loop
     return RQ_E_ALIGN;
   // Validate everything the second launch needs before enqueuing the first.
   if (!ws || ws_bytes < workspace_for(d) || ((uintptr_t)ws & 255) != 0) return RQ_E_WORKSPACE;
-  s = rq_decode_attn_partial(d, c, loop, q, past_len, softmax_scale, ws, ws_bytes, stream);
+  s = decode_partial(d, c, loop, q, past_len, softmax_scale, ws, ws_bytes, dev_err, stream);
   if (s != RQ_OK) return s;
   return rq_decode_combine(d, c->rot[1], q, k_cur, v_cur, past_len, softmax_scale, out, ws, ws_bytes, dev_err,
                            stream);

@@ -89,6 +89,19 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
 // lane k of lane group gi) in one group of 32 channels, or, with g16, e0 in
 // group 2 gi and e1 in group 2 gi + 1 of 16 channels each (INT2 only); store
 // codes and metadata, return the dequantized pair.
+// Row of token t of (b, h) in every cache buffer: contiguous [B][H][T_max], or
+// through the block table of a paged cache. False for an invalid block id.
+__device__ __forceinline__ bool cache_row(const AppendParams& p, int b, int h, int t, size_t& row) {
+  if (!p.table) {
+    row = ((size_t)b * p.H + h) * p.T_max + t;
+    return true;
+  }
+  const int32_t blk = p.table[(size_t)b * p.maxblk + (t >> p.lbs)];
+  if ((uint32_t)blk >= (uint32_t)p.num_blocks) return false;
+  row = (((size_t)blk * p.H + h) << p.lbs) + (size_t)(t & ((1 << p.lbs) - 1));
+  return true;
+}
+
 template <int D>
 __device__ void quantize_pair(double v0, double v1, int bits, bool g16, bool lane_on, int gi, int k,
                               uint8_t* codes, uint32_t* meta, size_t tok, double& d0, double& d1) {
@@ -223,7 +236,11 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
       if (lane == 0 && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_CAPACITY);
       continue;
     }
-    const size_t tok = ((size_t)b * p.H + h) * p.T_max + t;
+    size_t tok;
+    if (!cache_row(p, b, h, t, tok)) {
+      if (lane == 0 && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_BLOCK);
+      continue;
+    }
     const double(*Z)[D + 1] = &Zs[wave][uu * L];
     // each loop group independently: its anchor, then the other loops of the group
     for (int g0 = 0; g0 < L; g0 += p.G) {
@@ -284,6 +301,11 @@ __global__ __launch_bounds__(256) void append_unit(AppendParams p) {
     if (tid == 0 && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_CAPACITY);
     return;
   }
+  size_t tok;
+  if (!cache_row(p, b, h, t, tok)) {       // likewise
+    if (tid == 0 && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_BLOCK);
+    return;
+  }
 
   // ---- stage H (row-major, padded) and the L input rows
   {
@@ -341,7 +363,6 @@ __global__ __launch_bounds__(256) void append_unit(AppendParams p) {
     z1[j] = a1 + c1;
   }
 
-  const size_t tok = ((size_t)b * p.H + h) * p.T_max + t;
   const bool last = p.policy == RQ_POLICY_LAST_LOOP, chain = p.policy == RQ_POLICY_PREV_LOOP;
   auto anchor_of = [&](int r) { return last ? r / G * G + G - 1 : r / G * G; };
 

@@ -78,6 +78,12 @@ struct DecodeParams {
   float* part;
   float scale_log2;
   int B, H, T_max, unit, nsplit;
+  // paged cache (table == nullptr: contiguous): block table [B][maxblk], block
+  // size 2^lbs tokens, pool of num_blocks blocks = pool_rows rows per buffer
+  const int32_t* table;
+  int maxblk, lbs, num_blocks;
+  uint32_t pool_rows;
+  int32_t* dev_err;                   // may be null
 };
 
 struct Bf16Params {
@@ -101,6 +107,8 @@ struct AppendParams {
   int B, H, L, n, T_max, policy;
   int G;                    // loops per anchor group (divides L)
   uint32_t g16;             // bit r: loop r is INT2 in groups of 16 channels (else groups of 32)
+  const int32_t* table;     // paged cache: block table [B][maxblk], blocks of 2^lbs tokens; else null
+  int maxblk, lbs, num_blocks;
   int bits[RQ_MAX_LOOPS];
 };
 
@@ -108,6 +116,8 @@ struct AppendParams {
 int launch_append(const AppendParams& p, int D, void* stream);
 // ncomp components with bit widths bits[0..ncomp-1]; returns -1 if no kernel exists.
 int launch_decode(const DecodeParams& p, int D, int ncomp, const int* bits, int nsplit, void* stream);
+int launch_decode_paged(const DecodeParams& p, int D, int ncomp, const int* bits, int nsplit, void* stream);
+int launch_decode_paged_tile(const DecodeParams& p, int D, int ncomp, const int* bits, int nsplit, void* stream);
 int launch_bf16(const Bf16Params& p, int D, int nsplit, void* stream);
 int launch_combine(const CombineParams& p, int D, int B, void* stream);
 bool have_decode_kernel(int D, int ncomp, const int* bits);

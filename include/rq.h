@@ -69,6 +69,8 @@ typedef enum {
 /* Device-side error bits (OR-ed into *dev_err when given). */
 #define RQ_DEVERR_CAPACITY 1  /* append: pos[b] + n > max_tokens; tokens past capacity were dropped */
 #define RQ_DEVERR_LENGTH 2    /* decode: past_len[b] outside [0, max_tokens]; it was clamped */
+#define RQ_DEVERR_BLOCK 4     /* paged cache: a block-table entry a token needs is outside [0, num_blocks);
+                               * append dropped the token, decode read it as zeros */
 
 /* Reference policy (§3.2, App. D), applied inside every loop group (see
  * rq_desc.loop_group; by default all L loops form one group).
@@ -93,6 +95,10 @@ typedef struct {
   int32_t loop_group;  /* G: loops per anchor group; 0 = all L loops form one group, else a divisor of L.
                         * Loops gG .. gG+G-1 (0-based) are quantized against an anchor of their own
                         * (§5 "Models": a model with many loops, e.g. 32, split into groups of 4). */
+  int32_t block_size;  /* 0: contiguous cache. Else a paged cache (§4.2: the cache lives in the
+                        * serving engine's paged KV blocks): tokens per block, a power of two in
+                        * [16, 4096] dividing max_tokens; see rq_layer_cache.block_table */
+  int32_t num_blocks;  /* paged cache: blocks in every buffer's pool (>= 1) */
   uint8_t bits[RQ_MAX_LOOPS];   /* bit width per loop (0-based), 2 or 4 (§2.1, §3.4) */
   uint8_t group[RQ_MAX_LOOPS];  /* group size per loop along the rotated head_dim: 32, or 16 for
                                  * 2-bit loops (§5 "Quantization setup": g = 16 for INT2) */
@@ -113,12 +119,22 @@ typedef struct {
  *   alpha[kv][r]: fp16 [B][H][T_max], the LS coefficient; unused (may be NULL)
  *     for the anchor loop of each group.
  *   rot[kv]: fp32 [H][D][D] row-major, z = rot[h] x. Any orthogonal matrix works
- *     (randomized Hadamard, §2.2, or learned rotations such as OptR-H, §3.3). */
+ *     (randomized Hadamard, §2.2, or learned rotations such as OptR-H, §3.3).
+ * Paged cache (desc.block_size = BS > 0): every codes, meta and alpha buffer is
+ *   a pool [num_blocks][H][BS][row] with the rows above; token t of sequence b,
+ *   head h, is row (block_table[b][t / BS] * H + h) * BS + t % BS. Each of a
+ *   block's heads thus holds BS consecutive tokens. Every pool buffer must stay
+ *   below 4 GiB - 64 KiB (RQ_E_SHAPE otherwise). */
 typedef struct {
   uint8_t* codes[2][RQ_MAX_LOOPS];
   uint16_t* meta[2][RQ_MAX_LOOPS];
   uint16_t* alpha[2][RQ_MAX_LOOPS];
   const float* rot[2];
+  const int32_t* block_table;  /* paged cache only (else ignored, may be NULL): device int32
+                                * [B][max_tokens / block_size]; entry [b][j] is the pool block
+                                * holding tokens j*BS .. j*BS+BS-1 of sequence b. Entries covering
+                                * tokens an append writes or a decode reads must lie in
+                                * [0, num_blocks); others are never read. */
 } rq_layer_cache;
 
 /* Bytes of one cache buffer of `loop` for one tensor (K or V): kind 0 = codes,

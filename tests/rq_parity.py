@@ -86,11 +86,27 @@ def oracle_layer(Xall: torch.Tensor, rot_k: torch.Tensor, rot_v: torch.Tensor, b
         return dict(ex.map(run, jobs))
 
 
-def host_copy(cache: rq.LayerCache) -> dict:
-    """Host copies of every cache buffer: {(kv, loop): (codes, meta, alpha)}."""
+def logical_rows(cache: rq.LayerCache, pool: np.ndarray) -> np.ndarray:
+    """A paged pool [NB][H][BS][...] gathered into logical order [B][H][T_max][...]
+    through the block table (rq.h); tokens whose entry is not a valid block are zero."""
     d = cache.desc
-    return {(kv, r): (cache.codes[kv][r].cpu().numpy(), u16(cache.meta[kv][r]),
-                      None if cache.alpha[kv][r] is None else u16(cache.alpha[kv][r]))
+    BS, NB = d.block_size, d.num_blocks
+    table = cache.block_table.cpu().numpy()                       # [B][T_max / BS]
+    t = np.arange(d.max_tokens)
+    blk = table[:, t // BS]                                       # [B][T_max]
+    ok = (blk >= 0) & (blk < NB)
+    g = pool[np.where(ok, blk, 0), :, (t % BS)[None, :]]          # [B][T_max][H][...]
+    g = np.where(ok.reshape(ok.shape + (1,) * (g.ndim - 2)), g, 0)
+    return np.ascontiguousarray(np.swapaxes(g, 1, 2))
+
+
+def host_copy(cache: rq.LayerCache) -> dict:
+    """Host copies of every cache buffer in logical order [B][H][T_max][...]:
+    {(kv, loop): (codes, meta, alpha)}."""
+    d = cache.desc
+    view = (lambda a: logical_rows(cache, a)) if d.block_size else (lambda a: a)
+    return {(kv, r): (view(cache.codes[kv][r].cpu().numpy()), view(u16(cache.meta[kv][r])),
+                      None if cache.alpha[kv][r] is None else view(u16(cache.alpha[kv][r])))
             for kv in range(2) for r in range(d.loops)}
 
 
@@ -181,13 +197,16 @@ def max_rel_err(gpu_out: torch.Tensor, ref: dict) -> float:
 
 def build_gpu_layer(X: torch.Tensor, rot_k, rot_v, bits, policy, T_max: int, T: int,
                     steps_of_one: int = 0, pos0=None, chunk: int = 1, loop_group: int = 0,
-                    groups=32) -> rq.LayerCache:
+                    groups=32, paging=None) -> rq.LayerCache:
     """Fill a GPU cache with tokens [0, T) of X (bf16 [2][L][B][H][*][D] on the GPU): one
     bulk append of the first T - steps_of_one tokens, then appends of `chunk` tokens
-    (the last one shorter) until T."""
+    (the last one shorter) until T. paging = (block_size, num_blocks, block table) makes
+    it a paged cache."""
     _, L, B, H, _, D = X.shape
-    d = rq.make_desc(B, H, D, bits, T_max, policy, group=groups, loop_group=loop_group)
-    cache = rq.LayerCache.allocate(d, rot_k, rot_v)
+    bs, nb, table = paging if paging else (0, 0, None)
+    d = rq.make_desc(B, H, D, bits, T_max, policy, group=groups, loop_group=loop_group, block_size=bs,
+                     num_blocks=nb)
+    cache = rq.LayerCache.allocate(d, rot_k, rot_v, block_table=table)
     n0 = T - steps_of_one
     pos = torch.zeros(B, dtype=torch.int32, device="cuda") if pos0 is None else pos0
     if n0 > 0:
@@ -232,3 +251,19 @@ def decode_and_compare(w, X, rk, rv, cache, series, lens, loops, label, batch=No
         log(f"{label}: loop {r} max rel err {err:.3e}")
         assert err <= TOL_ATTN, (label, r, err)
     return worst
+
+
+def shuffled_table(B: int, T_max: int, BS: int, lens, extra: int = 3, seed: int = 0):
+    """A block table that scatters every sequence's blocks over a pool with `extra`
+    unused blocks, in a seeded random order; entries past ceil(lens[b] / BS) are -1
+    (never read). Returns (num_blocks, int32 table [B][T_max / BS] on the GPU)."""
+    nbt = T_max // BS
+    need = [-(-n // BS) for n in lens]
+    nb = sum(need) + extra
+    perm = np.random.default_rng(seed).permutation(nb)
+    table = np.full((B, nbt), -1, np.int32)
+    k = 0
+    for b in range(B):
+        table[b, :need[b]] = perm[k:k + need[b]]
+        k += need[b]
+    return nb, torch.from_numpy(table).cuda()

@@ -55,11 +55,58 @@ def test_check_desc(kw, code):
 
 
 def test_desc_layout_matches_header():
-    """The ctypes mirror of rq_desc: six int32 fields, then 32 bit widths and 32 group sizes."""
+    """The ctypes mirrors of rq_desc (nine int32 fields, then 32 bit widths and 32 group
+    sizes) and rq_layer_cache (block_table after the rotations)."""
     assert rq.MAX_LOOPS == 32
-    assert ctypes.sizeof(rq.Desc) == 7 * 4 + 2 * 32
+    assert ctypes.sizeof(rq.Desc) == 9 * 4 + 2 * 32
     assert rq.Desc.loop_group.offset == 6 * 4
-    assert rq.Desc.bits.offset == 7 * 4
+    assert rq.Desc.block_size.offset == 7 * 4 and rq.Desc.num_blocks.offset == 8 * 4
+    assert rq.Desc.bits.offset == 9 * 4
+    assert rq.LayerCacheC.block_table.offset == 8 * (3 * 2 * 32 + 2)
+
+
+@pytest.mark.parametrize("bs,nb,code", [
+    (16, 10, 0), (64, 1, 0), (4096, 3, 0), (0, 0, 0), (8, 10, 2), (48, 10, 2), (8192, 1, 2), (16, 0, 2),
+    (-16, 4, 2),
+])
+def test_paged_desc_validation(bs, nb, code):
+    assert rq.check_desc(_desc(max_tokens=8192, block_size=bs, num_blocks=nb)) == code
+
+
+def test_paged_block_size_divides_max_tokens():
+    assert rq.check_desc(_desc(max_tokens=1056, block_size=32, num_blocks=4)) == 0      # 33 blocks
+    assert rq.check_desc(_desc(max_tokens=1048, block_size=32, num_blocks=4)) == 2
+
+
+def test_paged_pool_size_limit():
+    """Every pool buffer must stay addressable by 32-bit offsets (INT4 codes are the largest)."""
+    ok = _desc(block_size=16, num_blocks=(0xFFFF0000 // (64 * 3 * 16)), max_tokens=1024)
+    assert rq.check_desc(ok) == 0
+    big = _desc(block_size=16, num_blocks=(0xFFFF0000 // (64 * 3 * 16)) + 1, max_tokens=1024)
+    assert rq.check_desc(big) == 2
+
+
+def test_paged_buffer_bytes():
+    d = _desc(block_size=64, num_blocks=7, max_tokens=1024)     # bits [2, 2, 4, 4], H3, D128
+    rows = 7 * 3 * 64
+    assert rq.buffer_bytes(d, 0, 0) == rows * 32
+    assert rq.buffer_bytes(d, 0, 3) == rows * 64
+    assert rq.buffer_bytes(d, 1, 1) == rows * 4 * 4
+    assert rq.buffer_bytes(d, 2, 0) == rows * 2
+
+
+def test_paged_calls_need_the_table():
+    L, by = rq.lib, ctypes.byref
+    d = _desc(block_size=16, num_blocks=40, max_tokens=1024)
+    c = _cache(d)
+    assert L.rq_quantize_append(by(d), by(c), FAKE, FAKE, 1, None, 0) == 1         # no table
+    ws = rq.workspace_bytes(d)
+    assert L.rq_decode_attn(by(d), by(c), 0, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE, ws,
+                            None, 0) == 1
+    c.block_table = 0x100002
+    assert L.rq_quantize_append(by(d), by(c), FAKE, FAKE, 1, None, 0) == 10
+    assert L.rq_decode_attn(by(d), by(c), 0, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE, ws,
+                            None, 0) == 10
 
 
 @pytest.mark.parametrize("policy,G,L,expect", [

@@ -11,8 +11,8 @@ Layer 0 is checked for every (batch, head): the whole cache (codes, fp16
 metadata and LS coefficients of every loop, 16447 tokens) and every loop's
 attention output. The last layer, the chained comparator, the BF16
 comparator, the Huginn-shaped workloads (8 loops in one group; 32 loops in
-eight anchor groups) and the capacity shape are checked on a sample of
-(batch, head) series. The oracle works
+eight anchor groups), the 2-bit loops in groups of 16, the paged cache and
+the capacity shape are checked on a sample of (batch, head) series. The oracle works
 on its own quantization of the same bf16 inputs; nothing the HIP path writes
 is fed to it.
 """
@@ -25,7 +25,7 @@ import torch
 import decode_attention_quantize_amd as rq
 import synth
 from rq_parity import (TOL_ATTN, assert_cache_parity, compare_cache, host_copy, log, max_rel_err,
-                       oracle_attention, oracle_layer, u16)
+                       oracle_attention, oracle_layer, shuffled_table, u16)
 import oracle as O
 
 pytestmark = pytest.mark.gpu
@@ -44,14 +44,17 @@ def _sample_units(n, seed, w=W):
     return sorted(units)
 
 
-def _build(layer, policy, bits, w=W):
-    """Inputs and a GPU cache holding tokens [0, T + STEPS - 1) of `layer`."""
+def _build(layer, policy, bits, w=W, block_size=0):
+    """Inputs and a GPU cache holding tokens [0, T + STEPS - 1) of `layer`; block_size > 0
+    makes it a paged cache over a shuffled pool."""
     B, H, D, T = w.batch, w.heads, w.D, w.T
     T_max = T + STEPS
     X = synth.kv(w, layer, 0, T_max, device="cuda")
     rk, rv = synth.rotation(w, layer, 0), synth.rotation(w, layer, 1)
-    d = rq.make_desc(B, H, D, list(bits), T_max, policy, group=w.groups_for(bits), loop_group=w.loop_group)
-    cache = rq.LayerCache.allocate(d, rk, rv)
+    nb, table = shuffled_table(B, T_max, block_size, [T_max] * B, seed=layer) if block_size else (0, None)
+    d = rq.make_desc(B, H, D, list(bits), T_max, policy, group=w.groups_for(bits), loop_group=w.loop_group,
+                     block_size=block_size, num_blocks=nb)
+    cache = rq.LayerCache.allocate(d, rk, rv, block_table=table)
     log(f"layer {layer} policy {policy}: bulk store of {T} tokens")
     rq.quantize_append(cache, X[..., :T, :].contiguous(), torch.zeros(B, dtype=torch.int32, device="cuda"), T)
     for k in range(STEPS - 1):
@@ -79,8 +82,8 @@ def _gpu_outputs(X, cache, layer, w=W):
     return res
 
 
-def _check(layer, policy, bits, units, label, w=W):
-    X, rk, rv, cache = _build(layer, policy, bits, w)
+def _check(layer, policy, bits, units, label, w=W, block_size=0):
+    X, rk, rv, cache = _build(layer, policy, bits, w, block_size)
     outs = _gpu_outputs(X, cache, layer, w)
     Tc = w.T + STEPS - 1
     host = host_copy(cache)
@@ -135,6 +138,12 @@ def test_ouro_16k_group16_sampled():
     series, every loop."""
     w = synth.WORKLOADS["ouro_16k_g16"]
     _check(0, LAST, w.bits, _sample_units(8, 17, w), "16k g16", w)
+
+
+def test_ouro_16k_paged_sampled():
+    """The 16k workload in a paged cache (16-token blocks over a shuffled pool, the
+    benchmark's paged configuration): layer 0, sampled series, every loop."""
+    _check(0, LAST, W.bits, _sample_units(8, 29), "16k paged BS16", W, block_size=16)
 
 
 def test_capacity_8k_batch64_sampled():
