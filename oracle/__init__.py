@@ -80,6 +80,7 @@ def lib():
         L.rqo_attend.argtypes = att
         L.rqo_attend_bruteforce.argtypes = att
         L.rqo_attend_bf16.argtypes = [I, I, P, P, P, P, P, ctypes.c_double, P]
+        L.rqo_prefill_attend.argtypes = [I, I, P, P, P, ctypes.c_double, P]
         _lib = L
     return _lib
 
@@ -292,6 +293,20 @@ def attend(ks: Series, vs: Series, r: int, T: int, HK, HV, q, kcur, vcur, scale:
 
 def attend_bruteforce(ks: Series, vs: Series, r: int, T: int, HK, HV, q, kcur, vcur, scale: float) -> np.ndarray:
     return _attend(lib().rqo_attend_bruteforce, ks, vs, r, T, HK, HV, q, kcur, vcur, scale)
+
+
+def prefill_attend(Q, K, V, scale: float) -> np.ndarray:
+    """Causal attention of one loop over its bf16 prompt (§4.2 "Prefill"): Q, K, V uint16
+    [T][D] bf16 bit patterns of one (sequence, head); returns fp64 [T][D]."""
+    Q = np.ascontiguousarray(Q, np.uint16)
+    K = np.ascontiguousarray(K, np.uint16)
+    V = np.ascontiguousarray(V, np.uint16)
+    T, D = Q.shape
+    assert K.shape == (T, D) and V.shape == (T, D)
+    out = np.zeros((T, D))
+    if lib().rqo_prefill_attend(D, T, _p(Q), _p(K), _p(V), ctypes.c_double(scale), _p(out)) != 0:
+        raise ValueError("rqo_prefill_attend failed")
+    return out
 
 
 def attend_bf16(K, V, q, kcur, vcur, scale: float) -> np.ndarray:

@@ -463,4 +463,30 @@ int rqo_attend_bf16(int D, int T, const uint16_t* K, const uint16_t* V, const ui
   return 0;
 }
 
+int rqo_prefill_attend(int D, int T, const uint16_t* Q, const uint16_t* K, const uint16_t* V, double scale,
+                       double* out) {
+  if (D <= 0 || T < 0) return -1;
+  std::vector<double> q(D), k(D), v(D), s(T);
+  for (int i = 0; i < T; ++i) {                 /* query i sees keys 0..i (causal) */
+    decode_bf16_vec(D, Q + (size_t)i * D, q.data());
+    double m = -INFINITY;
+    for (int j = 0; j <= i; ++j) {
+      decode_bf16_vec(D, K + (size_t)j * D, k.data());
+      s[j] = scale * dot(D, q.data(), k.data());
+      if (s[j] > m) m = s[j];
+    }
+    double l = 0.0;
+    double* o = out + (size_t)i * D;
+    for (int c = 0; c < D; ++c) o[c] = 0.0;
+    for (int j = 0; j <= i; ++j) {
+      const double p = std::exp(s[j] - m);
+      l += p;
+      decode_bf16_vec(D, V + (size_t)j * D, v.data());
+      for (int c = 0; c < D; ++c) o[c] += p * v[c];
+    }
+    for (int c = 0; c < D; ++c) o[c] /= l;
+  }
+  return 0;
+}
+
 }  // extern "C"

@@ -122,6 +122,13 @@ int rqo_attend_bruteforce(const rqo_cfg* c, int r, int T,
 int rqo_attend_bf16(int D, int T, const uint16_t* K, const uint16_t* V, const uint16_t* q,
                     const uint16_t* kcur, const uint16_t* vcur, double scale, double* out);
 
+/* Prefill attention of one loop (§4.2 "Prefill": every loop attends causally
+ * over its own BF16 prompt K/V before the prompt is quantized). Q, K, V are
+ * bf16 [T][D] of one (sequence, head); row i of out (fp64 [T][D]) is the
+ * softmax(scale q_i . k_j) weighted sum of v_j over j <= i. */
+int rqo_prefill_attend(int D, int T, const uint16_t* Q, const uint16_t* K, const uint16_t* V, double scale,
+                       double* out);
+
 #ifdef __cplusplus
 }
 #endif
