@@ -73,6 +73,8 @@ def _load():
     L.rq_decode_attn_bf16_partial.argtypes = [P, P, P, P, P, ctypes.c_float, P, Z, P]
     L.rq_decode_attn_bf16.restype = ctypes.c_int
     L.rq_decode_attn_bf16.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, P, P, Z, P, P]
+    L.rq_prefill_attn.restype = ctypes.c_int
+    L.rq_prefill_attn.argtypes = [P, P, P, P, P, I, ctypes.c_float, P, P, P]
     L.rq_status_str.restype = ctypes.c_char_p
     L.rq_status_str.argtypes = [ctypes.c_int]
     L.rq_version.restype = ctypes.c_char_p
@@ -218,6 +220,15 @@ def quantize_append(cache: LayerCache, kv: torch.Tensor, pos: torch.Tensor, n: i
     cc = cache.c()
     _check(lib.rq_quantize_append(ctypes.byref(cache.desc), ctypes.byref(cc), _ptr(kv), _ptr(pos), n,
                                   _ptr(dev_err), _stream(stream)), "rq_quantize_append")
+
+
+def prefill_attn(d: Desc, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lens: torch.Tensor, scale: float,
+                 out: torch.Tensor, dev_err: torch.Tensor | None = None, stream=None):
+    """Causal prefill attention of one loop: q, k, v bf16 [B][H][n][D]; lens int32 [B];
+    out fp32 [B][H][n][D] (rows past lens[b] not written)."""
+    n = q.shape[2]
+    _check(lib.rq_prefill_attn(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(lens), n, scale, _ptr(out),
+                               _ptr(dev_err), _stream(stream)), "rq_prefill_attn")
 
 
 def decode_attn(cache: LayerCache, loop: int, q, k_cur, v_cur, past_len, scale: float, out, workspace,

@@ -21,6 +21,7 @@ SOURCES = {
     "rq_decode_paged.hip": [],
     "rq_decode_paged_tile.hip": [],
     "rq_decode_bf16.hip": [],
+    "rq_prefill.hip": [],
 }
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           # packed fp32 arithmetic is disabled on purpose for every kernel

@@ -397,4 +397,30 @@ rq_status rq_decode_attn_bf16(const rq_desc* d, const uint16_t* k_cache, const u
   return rq_decode_combine(d, nullptr, q, k_cur, v_cur, past_len, softmax_scale, out, ws, ws_bytes, dev_err, stream);
 }
 
+rq_status rq_prefill_attn(const rq_desc* d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          const int32_t* lens, int32_t n, float softmax_scale, float* out, int32_t* dev_err,
+                          void* stream) {
+  rq_status s = check_shape(d);
+  if (s != RQ_OK) return s;
+  if (n < 0) return RQ_E_SHAPE;
+  if (n == 0) return RQ_OK;
+  if (!q || !k || !v || !lens || !out) return RQ_E_NULL;
+  if (!al(q, 16) || !al(k, 16) || !al(v, 16) || !al(out, 16) || !al(lens, 4)) return RQ_E_ALIGN;
+  if (!std::isfinite(softmax_scale)) return RQ_E_SHAPE;
+  const long long blocks = ((long long)n + 127) / 128 * d->batch * d->heads;
+  if (blocks > 0x7FFFFFFFLL) return RQ_E_SHAPE;
+  PrefillParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.lens = lens;
+  p.out = out;
+  p.dev_err = dev_err;
+  p.scale_log2 = softmax_scale * kLog2e;
+  p.B = d->batch;
+  p.H = d->heads;
+  p.T = n;
+  return launch_prefill(p, d->head_dim, stream) == 0 ? RQ_OK : RQ_E_HIP;
+}
+
 }  // extern "C"

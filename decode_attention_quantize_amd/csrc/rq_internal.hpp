@@ -112,6 +112,17 @@ struct AppendParams {
   int bits[RQ_MAX_LOOPS];
 };
 
+struct PrefillParams {
+  const uint16_t* q;        // bf16 [B][H][T][D]
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* lens;      // [B], clamped to [0, T]
+  float* out;               // fp32 [B][H][T][D]
+  int32_t* dev_err;         // may be null
+  float scale_log2;
+  int B, H, T;
+};
+
 // Launchers (return hipError_t as int; 0 = success). Defined in the .hip files.
 int launch_append(const AppendParams& p, int D, void* stream);
 // ncomp components with bit widths bits[0..ncomp-1]; returns -1 if no kernel exists.
@@ -120,6 +131,7 @@ int launch_decode_paged(const DecodeParams& p, int D, int ncomp, const int* bits
 int launch_decode_paged_tile(const DecodeParams& p, int D, int ncomp, const int* bits, int nsplit, void* stream);
 int launch_bf16(const Bf16Params& p, int D, int nsplit, void* stream);
 int launch_combine(const CombineParams& p, int D, int B, void* stream);
+int launch_prefill(const PrefillParams& p, int D, void* stream);
 bool have_decode_kernel(int D, int ncomp, const int* bits);
 
 }  // namespace rq

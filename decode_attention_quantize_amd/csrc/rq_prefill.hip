@@ -1,0 +1,224 @@
+// Prefill attention of one loop (paper "KV Cache Quantization for Looped
+// Transformers with 2-Bit Residuals", §4.2 "Prefill": every loop attends
+// causally over its own BF16 prompt K/V; after the final loop the prompt is
+// quantized into the cache, which rq_quantize_append does).
+//
+// A flash-attention forward pass on the matrix cores of gfx950. One workgroup
+// owns 128 queries of one (b, h); each of its four waves owns 32 of them and
+// walks the key tiles of 64 tokens that causality lets it see. Per tile:
+//   S^T = K Q^T    v_mfma_f32_16x16x32_bf16: K rows (A operand) from LDS, the
+//                  wave's queries (B operand) held in registers for the whole
+//                  pass; bf16 products are exact, sums in fp32;
+//   online softmax in the log2 domain, per query column (a lane's column is
+//                  lane % 16, so the rescale of its accumulators is lane-local);
+//   O^T += V^T P^T v_mfma_f32_16x16x32_f16: P in fp16 (2^-11 relative
+//                  rounding; bf16 would cost 2^-9) and V converted to fp16 when
+//                  staged, V^T (A operand) from a transposed LDS tile.
+// The key rows of each 16-row S tile are permuted (rows 4i..4i+3 of tile 2c+h
+// are keys 32c + 8i + 4h + 0..3) so that the S accumulators a lane holds are
+// exactly the eight consecutive keys its P operand needs: no lane exchange
+// between the two products.
+#include <hip/hip_runtime.h>
+
+#include "rq_device.hpp"
+#include "rq_internal.hpp"
+
+namespace rq {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBQ = 128;          // queries per workgroup (32 per wave)
+constexpr int kBK = 64;           // keys per tile
+
+// Key of row r (0..15) of S tile mt (0..3) within a key tile.
+__host__ __device__ constexpr int tile_key(int mt, int r) { return 32 * (mt >> 1) + 8 * (r >> 2) + 4 * (mt & 1) + (r & 3); }
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p) {
+  constexpr int KS = D / 32;      // k-steps of S (32 channels each)
+  constexpr int MD = D / 16;      // 16-channel tiles of O^T
+  constexpr int KP = D + 8;       // padded LDS row of K (bf16)
+  constexpr int VP = kBK + 8;     // padded LDS row of V^T (fp16)
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBK * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
+
+  // heaviest query blocks (most keys under the causal mask) are dispatched first
+  const int nqb = (p.T + kBQ - 1) / kBQ;
+  const int BH = p.B * p.H;
+  const int qb = nqb - 1 - (int)blockIdx.x / BH;
+  const int bh = (int)blockIdx.x % BH;
+  const int b = bh / p.H;
+  int len = p.lens[b];
+  // flagged once per sequence: by its head-0 block of the first dispatched query block
+  if ((len < 0 || len > p.T) && threadIdx.x == 0 && (int)blockIdx.x < BH && bh % p.H == 0 && p.dev_err)
+    atomicOr(p.dev_err, RQ_DEVERR_LENGTH);
+  len = len < 0 ? 0 : (len > p.T ? p.T : len);
+  const int q0 = qb * kBQ;
+  if (q0 >= len) return;                               // whole block, before any barrier
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int qw = q0 + 32 * wave;                       // this wave's first query
+  const size_t head = (size_t)bh * p.T * D;            // element offset of (b, h) in q, k, v, out
+
+  // ---- the wave's queries as B operands: query qw + 16 nt + col, channels 32 ks + 8 grp ..
+  bf16x8 qreg[2][KS];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int qi = min(qw + 16 * nt + col, p.T - 1);
+    const uint4* src = reinterpret_cast<const uint4*>(p.q + head + (size_t)qi * D);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qreg[nt][ks] = __builtin_bit_cast(bf16x8, src[4 * ks + grp]);
+  }
+
+  f32x4 o[2][MD];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int md = 0; md < MD; ++md) o[nt][md] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};   // per query column, lane-partial l
+
+  const int kend = min(len, q0 + kBQ);                 // keys any query of the block may see
+  const int nkt = (kend + kBK - 1) / kBK;
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int k0 = kt * kBK;
+    __syncthreads();                                   // the previous tile is consumed
+    // ---- stage K (row-major) and V^T (fp16), zeros past the sequence
+    for (int c = tid; c < kBK * (D / 8); c += kThreads) {
+      const int key = c / (D / 8), d0 = 8 * (c % (D / 8));
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (k0 + key < len) w = *reinterpret_cast<const uint4*>(p.k + head + (size_t)(k0 + key) * D + d0);
+      *reinterpret_cast<uint4*>(&Ks[key * KP + d0]) = w;
+    }
+    for (int c = tid; c < (kBK / 2) * (D / 8); c += kThreads) {
+      const int kp = c % (kBK / 2), dc = c / (kBK / 2);
+      const int key = 2 * kp;
+      uint4 w0 = make_uint4(0, 0, 0, 0), w1 = make_uint4(0, 0, 0, 0);
+      if (k0 + key < len) w0 = *reinterpret_cast<const uint4*>(p.v + head + (size_t)(k0 + key) * D + 8 * dc);
+      if (k0 + key + 1 < len) w1 = *reinterpret_cast<const uint4*>(p.v + head + (size_t)(k0 + key + 1) * D + 8 * dc);
+      const uint32_t a[4] = {w0.x, w0.y, w0.z, w0.w}, bb[4] = {w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = (uint32_t)f32_to_f16_bits(bf16lo(a[j])) | ((uint32_t)f32_to_f16_bits(bf16lo(bb[j])) << 16);
+        const uint32_t hi = (uint32_t)f32_to_f16_bits(bf16hi(a[j])) | ((uint32_t)f32_to_f16_bits(bf16hi(bb[j])) << 16);
+        *reinterpret_cast<uint32_t*>(&Vt[(8 * dc + 2 * j) * VP + key]) = lo;
+        *reinterpret_cast<uint32_t*>(&Vt[(8 * dc + 2 * j + 1) * VP + key]) = hi;
+      }
+    }
+    __syncthreads();
+    if (qw >= len || k0 > qw + 31) continue;           // nothing of this tile is visible to the wave
+
+    // ---- S^T tiles: [mt][nt], rows = keys tile_key(mt, 4 grp + i), column = query
+    f32x4 s[4][2];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      bf16x8 ka[KS];
+      const uint16_t* kr = &Ks[tile_key(mt, col) * KP + 8 * grp];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) ka[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kr + 32 * ks));
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks], qreg[nt][ks], acc, 0, 0, 0);
+        s[mt][nt] = acc;
+      }
+    }
+
+    // ---- causal and length mask, online softmax per query column (log2 domain)
+    const bool diag = k0 + kBK - 1 > qw || k0 + kBK > len;
+    f16x8 pb[2][2];                                    // [nt][32-key chunk]: P^T as B operands
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int qi = qw + 16 * nt + col;
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float x = s[mt][nt][i] * p.scale_log2;
+          if (diag) {
+            const int key = k0 + tile_key(mt, 4 * grp + i);
+            x = (key <= qi && key < len) ? x : -INFINITY;
+          }
+          s[mt][nt][i] = x;
+          tmax = fmaxf(tmax, x);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mnew = fmaxf(mrow[nt], tmax);
+      const float base = mnew == -INFINITY ? 0.f : mnew;          // a column with nothing visible yet
+      const float f = __builtin_amdgcn_exp2f(mrow[nt] - base);
+      mrow[nt] = mnew;
+      float ls = 0.f;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(s[2 * c + h][nt][i] - base);
+            ls += (float)ph;                           // l sums the rounded weights the product uses
+            pb[nt][c][4 * h + i] = ph;
+          }
+      lrow[nt] = fmaf(lrow[nt], f, ls);
+#pragma unroll
+      for (int md = 0; md < MD; ++md) o[nt][md] *= f;
+    }
+
+    // ---- O^T += V^T P^T: A = V^T rows (channel 16 md + col), keys 32 c + 8 grp ..
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+      const uint16_t* vr = &Vt[(16 * md + col) * VP + 8 * grp];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const f16x8 va = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(vr + 32 * c));
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) o[nt][md] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[nt][c], o[nt][md], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- normalize and store: lane holds O^T[16 md + 4 grp + i][query col of tile nt]
+  if (qw >= len) return;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    float l = lrow[nt];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const int qi = qw + 16 * nt + col;
+    if (qi >= len) continue;
+    const float inv = 1.0f / l;
+    float* dst = p.out + head + (size_t)qi * D + 4 * grp;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+      const f32x4 v = o[nt][md] * inv;
+      *reinterpret_cast<float4*>(dst + 16 * md) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
+}  // namespace
+
+int launch_prefill(const PrefillParams& p, int D, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int nqb = (p.T + kBQ - 1) / kBQ;
+  const dim3 grid((unsigned)(nqb * p.B * p.H));
+  switch (D) {
+    case 64: hipLaunchKernelGGL(prefill_attn_kernel<64>, grid, dim3(kThreads), 0, s, p); break;
+    case 96: hipLaunchKernelGGL(prefill_attn_kernel<96>, grid, dim3(kThreads), 0, s, p); break;
+    case 128: hipLaunchKernelGGL(prefill_attn_kernel<128>, grid, dim3(kThreads), 0, s, p); break;
+    default: return -1;
+  }
+  return (int)hipGetLastError();
+}
+
+}  // namespace rq

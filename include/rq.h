@@ -235,6 +235,23 @@ rq_status rq_decode_attn_bf16(const rq_desc* desc, const uint16_t* k_cache, cons
                               const int32_t* past_len, float softmax_scale, float* out,
                               void* workspace, size_t workspace_bytes, int32_t* dev_err, void* stream);
 
+/* Prefill attention of one loop (§4.2 "Prefill"): every prompt token attends
+ * causally over the prompt's own BF16 K/V of that loop, before anything is
+ * quantized; after the final loop the caller stores the prompt with
+ * rq_quantize_append (all loops at once). Row i of a sequence's output is
+ * sum_{j <= i} softmax_j(scale <q_i, k_j>) v_j.
+ *   q, k, v: bf16 [B][H][n][D] (one loop's prompt), 16-byte aligned;
+ *   lens: device int32 [B], the prompt length of each sequence (clamped to
+ *     [0, n]; RQ_DEVERR_LENGTH if outside); rows past it are not written;
+ *   out: fp32 [B][H][n][D], 16-byte aligned.
+ * Only batch, heads and head_dim of desc are used (n is the prompt capacity,
+ * independent of max_tokens). The matrix products run in bf16 (scores) and fp16
+ * (probabilities times values) with fp32 accumulation; values must lie within
+ * the fp16 range (|v| < 65504). n == 0 is a no-op. */
+rq_status rq_prefill_attn(const rq_desc* desc, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          const int32_t* lens, int32_t n, float softmax_scale, float* out, int32_t* dev_err,
+                          void* stream);
+
 /* Static description of a status code. */
 const char* rq_status_str(rq_status status);
 

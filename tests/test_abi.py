@@ -264,6 +264,22 @@ def test_decode_validation():
                                 rq.workspace_bytes(dg), None, 0) == 1
 
 
+def test_prefill_validation():
+    L, by = rq.lib, ctypes.byref
+    d = _desc()
+    f = ctypes.c_float(0.1)
+    assert L.rq_prefill_attn(None, FAKE, FAKE, FAKE, FAKE, 8, f, FAKE, None, 0) == 1
+    assert L.rq_prefill_attn(by(d), FAKE, FAKE, FAKE, FAKE, -1, f, FAKE, None, 0) == 2
+    assert L.rq_prefill_attn(by(d), None, None, None, None, 0, f, None, None, 0) == 0     # n == 0: no-op
+    assert L.rq_prefill_attn(by(d), None, FAKE, FAKE, FAKE, 8, f, FAKE, None, 0) == 1
+    assert L.rq_prefill_attn(by(d), FAKE, FAKE, FAKE, None, 8, f, FAKE, None, 0) == 1
+    assert L.rq_prefill_attn(by(d), FAKE, FAKE, FAKE, FAKE, 8, f, None, None, 0) == 1
+    assert L.rq_prefill_attn(by(d), FAKE, ctypes.c_void_p(0x100008), FAKE, FAKE, 8, f, FAKE, None, 0) == 10
+    assert L.rq_prefill_attn(by(d), FAKE, FAKE, FAKE, FAKE, 8, f, ctypes.c_void_p(0x100004), None, 0) == 10
+    assert L.rq_prefill_attn(by(d), FAKE, FAKE, FAKE, FAKE, 8, ctypes.c_float(float("inf")), FAKE, None, 0) == 2
+    assert L.rq_prefill_attn(by(_desc(head_dim=80)), FAKE, FAKE, FAKE, FAKE, 8, f, FAKE, None, 0) == 2
+
+
 def test_split_api_validation():
     L = rq.lib
     d = _desc()
