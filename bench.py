@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode-attn tokens/s + achieved HBM GB/s (% of peak) at 16k ctx, 4 loops"
 HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0            # dense bf16 matrix-core peak of the MI355X
 
 
 def log(msg):
@@ -203,6 +204,7 @@ def main():
     ap.add_argument("--block-size", type=int, default=0,
                     help="paged compressed caches with blocks of this many tokens over a shuffled pool (0: contiguous)")
     ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-chained", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--call-reps", type=int, default=50)
@@ -448,6 +450,43 @@ def main():
                           "bytes_per_launch": dom["bytes"], "ms_per_launch": dom["kernel_ms"],
                           "traffic_source": None if traffic is None else traffic["source"]}
     result["per_call"] = {f"loop{r + 1}": v for r, v in percall.items()}
+
+    # ---------------------------------------------------------------- prefill attention
+    # rq_prefill_attn over the workload's prompt (B x H x T tokens, one loop): the
+    # step that precedes decode (§4.2 "Prefill"). Algorithmic flops: 2 D per
+    # (query, visible key) for the scores and 2 D for the value sum, T (T + 1) / 2
+    # visible pairs per (b, h) under the causal mask.
+    if not args.no_prefill:
+        del caches, chained, bf16
+        torch.cuda.empty_cache()
+        g = torch.Generator(device=dev).manual_seed(7)
+        pq = torch.randn(B, H, T, D, generator=g, device=dev).to(torch.bfloat16)
+        Xp = synth.kv(w, 0, 0, T, device=dev)
+        pk, pv = Xp[0, 0].contiguous(), Xp[1, 0].contiguous()
+        del Xp
+        pout = torch.empty(B, H, T, D, dtype=torch.float32, device=dev)
+        plens = torch.full((B,), T, dtype=torch.int32, device=dev)
+        preps = 5
+        for _ in range(2):
+            rq.prefill_attn(d_rq, pq, pk, pv, plens, scale, pout)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(preps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rq.prefill_attn(d_rq, pq, pk, pv, plens, scale, pout)
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1))
+        ms = sorted(times)[preps // 2]
+        flops = 4.0 * D * (T * (T + 1) / 2) * B * H
+        result["prefill"] = {"kernel": f"prefill_attn_kernel<{D}> (rq_prefill_attn, one loop, causal)",
+                             "tokens": B * T, "ms_per_launch": ms, "flops_per_launch": flops,
+                             "tflops": flops / (ms * 1e-3) / 1e12, "bound": "mfma", "peak_tflops": BF16_PEAK_TFLOPS,
+                             "frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                             "prompt_tokens_per_s": B * T / (ms * 1e-3)}
+        log(f"prefill: {ms:.2f} ms per loop-layer, {result['prefill']['tflops']:.0f} TFLOP/s")
+        del pq, pk, pv, pout
 
     if args.calibrate_copy:
         # a plain streaming kernel of known size for scaling the HBM counters:

@@ -41,11 +41,17 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_attn_kernel(
+    PrefillParams p) {
   constexpr int KS = D / 32;      // k-steps of S (32 channels each)
   constexpr int MD = D / 16;      // 16-channel tiles of O^T
-  constexpr int KP = D + 8;       // padded LDS row of K (bf16)
+  constexpr int KP = D + 8;       // padded LDS row of K and Q (bf16)
   constexpr int VP = kBK + 8;     // padded LDS row of V^T (fp16)
+  constexpr int KC = kBK * (D / 8);                       // 16-byte chunks of a K tile
+  constexpr int VC = (kBK / 2) * (D / 8);                 // (key pair, 8 channels) items of a V tile
+  constexpr int KPF = (KC + kThreads - 1) / kThreads;     // per thread
+  constexpr int VPF = (VC + kThreads - 1) / kThreads;
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[kBQ * KP];
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kBK * KP];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
 
@@ -69,15 +75,55 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
   const int qw = q0 + 32 * wave;                       // this wave's first query
   const size_t head = (size_t)bh * p.T * D;            // element offset of (b, h) in q, k, v, out
 
-  // ---- the wave's queries as B operands: query qw + 16 nt + col, channels 32 ks + 8 grp ..
-  bf16x8 qreg[2][KS];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int qi = min(qw + 16 * nt + col, p.T - 1);
-    const uint4* src = reinterpret_cast<const uint4*>(p.q + head + (size_t)qi * D);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qreg[nt][ks] = __builtin_bit_cast(bf16x8, src[4 * ks + grp]);
+  // ---- the block's queries in LDS (rows past the tensor clamp to its last row)
+  for (int c = tid; c < kBQ * (D / 8); c += kThreads) {
+    const int r = c / (D / 8), d0 = 8 * (c % (D / 8));
+    const int qi = min(q0 + r, p.T - 1);
+    *reinterpret_cast<uint4*>(&Qs[r * KP + d0]) = *reinterpret_cast<const uint4*>(p.q + head + (size_t)qi * D + d0);
   }
+
+  // ---- next tile's K and V, held in registers while the current tile is computed
+  uint4 kpf[KPF], vpf[VPF][2];
+  auto prefetch = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < KPF; ++j) {
+      const int c = tid + j * kThreads;
+      const int key = c / (D / 8), d0 = 8 * (c % (D / 8));
+      kpf[j] = make_uint4(0, 0, 0, 0);
+      if (c < KC && k0 + key < len) kpf[j] = *reinterpret_cast<const uint4*>(p.k + head + (size_t)(k0 + key) * D + d0);
+    }
+#pragma unroll
+    for (int j = 0; j < VPF; ++j) {
+      const int c = tid + j * kThreads;
+      const int key = 2 * (c % (kBK / 2)), dc = c / (kBK / 2);
+      vpf[j][0] = vpf[j][1] = make_uint4(0, 0, 0, 0);
+      if (c < VC && k0 + key < len) vpf[j][0] = *reinterpret_cast<const uint4*>(p.v + head + (size_t)(k0 + key) * D + 8 * dc);
+      if (c < VC && k0 + key + 1 < len)
+        vpf[j][1] = *reinterpret_cast<const uint4*>(p.v + head + (size_t)(k0 + key + 1) * D + 8 * dc);
+    }
+  };
+  auto stage = [&]() {                                 // K row-major; V transposed, in fp16
+#pragma unroll
+    for (int j = 0; j < KPF; ++j) {
+      const int c = tid + j * kThreads;
+      if (c < KC) *reinterpret_cast<uint4*>(&Ks[(c / (D / 8)) * KP + 8 * (c % (D / 8))]) = kpf[j];
+    }
+#pragma unroll
+    for (int j = 0; j < VPF; ++j) {
+      const int c = tid + j * kThreads;
+      if (c >= VC) continue;
+      const int key = 2 * (c % (kBK / 2)), dc = c / (kBK / 2);
+      const uint32_t a[4] = {vpf[j][0].x, vpf[j][0].y, vpf[j][0].z, vpf[j][0].w};
+      const uint32_t bb[4] = {vpf[j][1].x, vpf[j][1].y, vpf[j][1].z, vpf[j][1].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = (uint32_t)f32_to_f16_bits(bf16lo(a[i])) | ((uint32_t)f32_to_f16_bits(bf16lo(bb[i])) << 16);
+        const uint32_t hi = (uint32_t)f32_to_f16_bits(bf16hi(a[i])) | ((uint32_t)f32_to_f16_bits(bf16hi(bb[i])) << 16);
+        *reinterpret_cast<uint32_t*>(&Vt[(8 * dc + 2 * i) * VP + key]) = lo;
+        *reinterpret_cast<uint32_t*>(&Vt[(8 * dc + 2 * i + 1) * VP + key]) = hi;
+      }
+    }
+  };
 
   f32x4 o[2][MD];
 #pragma unroll
@@ -88,35 +134,24 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
 
   const int kend = min(len, q0 + kBQ);                 // keys any query of the block may see
   const int nkt = (kend + kBK - 1) / kBK;
+  prefetch(0);
   for (int kt = 0; kt < nkt; ++kt) {
     const int k0 = kt * kBK;
     __syncthreads();                                   // the previous tile is consumed
-    // ---- stage K (row-major) and V^T (fp16), zeros past the sequence
-    for (int c = tid; c < kBK * (D / 8); c += kThreads) {
-      const int key = c / (D / 8), d0 = 8 * (c % (D / 8));
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (k0 + key < len) w = *reinterpret_cast<const uint4*>(p.k + head + (size_t)(k0 + key) * D + d0);
-      *reinterpret_cast<uint4*>(&Ks[key * KP + d0]) = w;
-    }
-    for (int c = tid; c < (kBK / 2) * (D / 8); c += kThreads) {
-      const int kp = c % (kBK / 2), dc = c / (kBK / 2);
-      const int key = 2 * kp;
-      uint4 w0 = make_uint4(0, 0, 0, 0), w1 = make_uint4(0, 0, 0, 0);
-      if (k0 + key < len) w0 = *reinterpret_cast<const uint4*>(p.v + head + (size_t)(k0 + key) * D + 8 * dc);
-      if (k0 + key + 1 < len) w1 = *reinterpret_cast<const uint4*>(p.v + head + (size_t)(k0 + key + 1) * D + 8 * dc);
-      const uint32_t a[4] = {w0.x, w0.y, w0.z, w0.w}, bb[4] = {w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t lo = (uint32_t)f32_to_f16_bits(bf16lo(a[j])) | ((uint32_t)f32_to_f16_bits(bf16lo(bb[j])) << 16);
-        const uint32_t hi = (uint32_t)f32_to_f16_bits(bf16hi(a[j])) | ((uint32_t)f32_to_f16_bits(bf16hi(bb[j])) << 16);
-        *reinterpret_cast<uint32_t*>(&Vt[(8 * dc + 2 * j) * VP + key]) = lo;
-        *reinterpret_cast<uint32_t*>(&Vt[(8 * dc + 2 * j + 1) * VP + key]) = hi;
-      }
-    }
+    stage();
     __syncthreads();
+    if (kt + 1 < nkt) prefetch(k0 + kBK);              // lands while this tile is computed
     if (qw >= len || k0 > qw + 31) continue;           // nothing of this tile is visible to the wave
 
-    // ---- S^T tiles: [mt][nt], rows = keys tile_key(mt, 4 grp + i), column = query
+    // ---- S^T tiles: [mt][nt], rows = keys tile_key(mt, 4 grp + i), column = query.
+    // B operands: query qw + 16 nt + col, channels 32 ks + 8 grp .. + 7
+    bf16x8 qb[2][KS];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qb[nt][ks] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(&Qs[(32 * wave + 16 * nt + col) * KP + 32 * ks + 8 * grp]));
     f32x4 s[4][2];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -128,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
       for (int nt = 0; nt < 2; ++nt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks], qreg[nt][ks], acc, 0, 0, 0);
+        for (int ks = 0; ks < KS; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks], qb[nt][ks], acc, 0, 0, 0);
         s[mt][nt] = acc;
       }
     }
