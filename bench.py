@@ -151,8 +151,8 @@ def summarize_profile(directory, title, command):
     import re
 
     def short(name):
-        m = re.search(r"(decode_fused<[^>]*>|bf16_fused<[^>]*>|combine_kernel<[^>]*>|append_kernel<[^>]*>|"
-                      r"append_unit<[^>]*>)", name)
+        m = re.search(r"((?:decode_fused|decode_fused_paged|decode_fused_paged_tile|bf16_fused|combine_kernel|"
+                      r"append_kernel|append_unit|prefill_attn_kernel)<[^>]*>)", name)
         if m:
             return m.group(1)
         if COPY_KERNEL in name:
