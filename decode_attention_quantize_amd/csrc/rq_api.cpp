@@ -406,7 +406,7 @@ rq_status rq_prefill_attn(const rq_desc* d, const uint16_t* q, const uint16_t* k
   if (n == 0) return RQ_OK;
   if (!q || !k || !v || !lens || !out) return RQ_E_NULL;
   if (!al(q, 16) || !al(k, 16) || !al(v, 16) || !al(out, 16) || !al(lens, 4)) return RQ_E_ALIGN;
-  if (!std::isfinite(softmax_scale)) return RQ_E_SHAPE;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f)) return RQ_E_SHAPE;
   const long long blocks = ((long long)n + 127) / 128 * d->batch * d->heads;
   if (blocks > 0x7FFFFFFFLL) return RQ_E_SHAPE;
   PrefillParams p;

@@ -35,6 +35,9 @@ constexpr int kBK = 64;           // keys per tile
 
 // Key of row r (0..15) of S tile mt (0..3) within a key tile.
 __host__ __device__ constexpr int tile_key(int mt, int r) { return 32 * (mt >> 1) + 8 * (r >> 2) + 4 * (mt & 1) + (r & 3); }
+// LDS row of key k of the tile: the tile's rows read together (one 16-row S
+// tile) are stored consecutively, so the A-operand reads do not collide on banks.
+__host__ __device__ constexpr int k_row(int k) { return (k & 32) | ((k & 4) << 2) | ((k >> 1) & 12) | (k & 3); }
 
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (_Float16)x);
@@ -72,6 +75,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
+  const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;   // byte addresses of the lanes of a column
   const int qw = q0 + 32 * wave;                       // this wave's first query
   const size_t head = (size_t)bh * p.T * D;            // element offset of (b, h) in q, k, v, out
 
@@ -83,30 +87,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 
   // ---- next tile's K and V, held in registers while the current tile is computed
+  // Raw buffer loads over the sequence's own rows [0, len) of K and V: rows past
+  // the end (and items past the tile) read as zeros through the hardware range
+  // check, so the loads need no branches.
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.k + head), (short)0, (int)((uint32_t)len * D * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.v + head), (short)0, (int)((uint32_t)len * D * 2), 0x00020000);
+  constexpr uint32_t kOut = 0x80000000u;               // an offset past any sequence
   uint4 kpf[KPF], vpf[VPF][2];
+  auto ld16 = [](__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+  };
   auto prefetch = [&](int k0) {
 #pragma unroll
     for (int j = 0; j < KPF; ++j) {
       const int c = tid + j * kThreads;
       const int key = c / (D / 8), d0 = 8 * (c % (D / 8));
-      kpf[j] = make_uint4(0, 0, 0, 0);
-      if (c < KC && k0 + key < len) kpf[j] = *reinterpret_cast<const uint4*>(p.k + head + (size_t)(k0 + key) * D + d0);
+      kpf[j] = ld16(krs, c < KC ? (uint32_t)((k0 + key) * D + d0) * 2u : kOut);
     }
 #pragma unroll
     for (int j = 0; j < VPF; ++j) {
       const int c = tid + j * kThreads;
       const int key = 2 * (c % (kBK / 2)), dc = c / (kBK / 2);
-      vpf[j][0] = vpf[j][1] = make_uint4(0, 0, 0, 0);
-      if (c < VC && k0 + key < len) vpf[j][0] = *reinterpret_cast<const uint4*>(p.v + head + (size_t)(k0 + key) * D + 8 * dc);
-      if (c < VC && k0 + key + 1 < len)
-        vpf[j][1] = *reinterpret_cast<const uint4*>(p.v + head + (size_t)(k0 + key + 1) * D + 8 * dc);
+      const uint32_t off = c < VC ? (uint32_t)((k0 + key) * D + 8 * dc) * 2u : kOut;
+      vpf[j][0] = ld16(vrs, off);
+      vpf[j][1] = ld16(vrs, c < VC ? off + D * 2 : kOut);
     }
   };
   auto stage = [&]() {                                 // K row-major; V transposed, in fp16
 #pragma unroll
     for (int j = 0; j < KPF; ++j) {
       const int c = tid + j * kThreads;
-      if (c < KC) *reinterpret_cast<uint4*>(&Ks[(c / (D / 8)) * KP + 8 * (c % (D / 8))]) = kpf[j];
+      if (c < KC) *reinterpret_cast<uint4*>(&Ks[k_row(c / (D / 8)) * KP + 8 * (c % (D / 8))]) = kpf[j];
     }
 #pragma unroll
     for (int j = 0; j < VPF; ++j) {
@@ -141,7 +156,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     stage();
     __syncthreads();
     if (kt + 1 < nkt) prefetch(k0 + kBK);              // lands while this tile is computed
-    if (qw >= len || k0 > qw + 31) continue;           // nothing of this tile is visible to the wave
+    // (A wave whose queries see nothing of this tile, at most the last one or two
+    // tiles of a block, still runs it fully masked: a skip would split the
+    // accumulators' live ranges into two paths and cost register copies on every tile.)
 
     // ---- S^T tiles: [mt][nt], rows = keys tile_key(mt, 4 grp + i), column = query.
     // B operands: query qw + 16 nt + col, channels 32 ks + 8 grp .. + 7
@@ -156,7 +173,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       bf16x8 ka[KS];
-      const uint16_t* kr = &Ks[tile_key(mt, col) * KP + 8 * grp];
+      const uint16_t* kr = &Ks[k_row(tile_key(mt, col)) * KP + 8 * grp];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) ka[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kr + 32 * ks));
 #pragma unroll
@@ -168,30 +185,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
     }
 
-    // ---- causal and length mask, online softmax per query column (log2 domain)
-    const bool diag = k0 + kBK - 1 > qw || k0 + kBK > len;
+    // ---- causal and length mask (tiles that reach past a query or the sequence)
+    if (k0 + kBK - 1 > qw || k0 + kBK > len) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int lim = min(qw + 16 * nt + col, len - 1) - (k0 + 8 * grp);   // last visible key, relative
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (32 * (mt >> 1) + 4 * (mt & 1) + i > lim) s[mt][nt][i] = -INFINITY;
+      }
+    }
+
+    // ---- online softmax per query column (log2 domain; the scale is positive, so the
+    // column max of the raw scores gives the max of the scaled ones)
     f16x8 pb[2][2];                                    // [nt][32-key chunk]: P^T as B operands
+    float fcol[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const int qi = qw + 16 * nt + col;
       float tmax = -INFINITY;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float x = s[mt][nt][i] * p.scale_log2;
-          if (diag) {
-            const int key = k0 + tile_key(mt, 4 * grp + i);
-            x = (key <= qi && key < len) ? x : -INFINITY;
-          }
-          s[mt][nt][i] = x;
-          tmax = fmaxf(tmax, x);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float mnew = fmaxf(mrow[nt], tmax);
+        tmax = fmaxf(fmaxf(tmax, fmaxf(s[mt][nt][0], s[mt][nt][1])), fmaxf(s[mt][nt][2], s[mt][nt][3]));
+      tmax = fmaxf(tmax, __int_as_float(__builtin_amdgcn_ds_bpermute(x16, __float_as_int(tmax))));
+      tmax = fmaxf(tmax, __int_as_float(__builtin_amdgcn_ds_bpermute(x32, __float_as_int(tmax))));
+      const float mnew = fmaxf(mrow[nt], tmax * p.scale_log2);
       const float base = mnew == -INFINITY ? 0.f : mnew;          // a column with nothing visible yet
-      const float f = __builtin_amdgcn_exp2f(mrow[nt] - base);
+      fcol[nt] = __builtin_amdgcn_exp2f(mrow[nt] - base);
       mrow[nt] = mnew;
       float ls = 0.f;
 #pragma unroll
@@ -200,13 +221,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const _Float16 ph = (_Float16)__builtin_amdgcn_exp2f(s[2 * c + h][nt][i] - base);
-            ls += (float)ph;                           // l sums the rounded weights the product uses
-            pb[nt][c][4 * h + i] = ph;
+            const float pv = __builtin_amdgcn_exp2f(fmaf(s[2 * c + h][nt][i], p.scale_log2, -base));
+            ls += pv;
+            pb[nt][c][4 * h + i] = (_Float16)pv;
           }
-      lrow[nt] = fmaf(lrow[nt], f, ls);
+      lrow[nt] = fmaf(lrow[nt], fcol[nt], ls);
+    }
+    // the accumulators are rescaled only when some column's max moved (rare after
+    // the first tiles)
+    if (__builtin_amdgcn_ballot_w64(fcol[0] != 1.0f || fcol[1] != 1.0f)) {
 #pragma unroll
-      for (int md = 0; md < MD; ++md) o[nt][md] *= f;
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int md = 0; md < MD; ++md) o[nt][md] *= fcol[nt];
     }
 
     // ---- O^T += V^T P^T: A = V^T rows (channel 16 md + col), keys 32 c + 8 grp ..

@@ -245,7 +245,7 @@ rq_status rq_decode_attn_bf16(const rq_desc* desc, const uint16_t* k_cache, cons
  *     [0, n]; RQ_DEVERR_LENGTH if outside); rows past it are not written;
  *   out: fp32 [B][H][n][D], 16-byte aligned.
  * Only batch, heads and head_dim of desc are used (n is the prompt capacity,
- * independent of max_tokens). The matrix products run in bf16 (scores) and fp16
+ * independent of max_tokens). softmax_scale must be positive (RQ_E_SHAPE). The matrix products run in bf16 (scores) and fp16
  * (probabilities times values) with fp32 accumulation; values must lie within
  * the fp16 range (|v| < 65504). n == 0 is a no-op. */
 rq_status rq_prefill_attn(const rq_desc* desc, const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -277,6 +277,8 @@ def test_prefill_validation():
     assert L.rq_prefill_attn(by(d), FAKE, ctypes.c_void_p(0x100008), FAKE, FAKE, 8, f, FAKE, None, 0) == 10
     assert L.rq_prefill_attn(by(d), FAKE, FAKE, FAKE, FAKE, 8, f, ctypes.c_void_p(0x100004), None, 0) == 10
     assert L.rq_prefill_attn(by(d), FAKE, FAKE, FAKE, FAKE, 8, ctypes.c_float(float("inf")), FAKE, None, 0) == 2
+    assert L.rq_prefill_attn(by(d), FAKE, FAKE, FAKE, FAKE, 8, ctypes.c_float(0.0), FAKE, None, 0) == 2
+    assert L.rq_prefill_attn(by(d), FAKE, FAKE, FAKE, FAKE, 8, ctypes.c_float(-0.1), FAKE, None, 0) == 2
     assert L.rq_prefill_attn(by(_desc(head_dim=80)), FAKE, FAKE, FAKE, FAKE, 8, f, FAKE, None, 0) == 2
 
 
