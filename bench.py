@@ -466,27 +466,29 @@ def main():
         del Xp
         pout = torch.empty(B, H, T, D, dtype=torch.float32, device=dev)
         plens = torch.full((B,), T, dtype=torch.int32, device=dev)
+        pws = rq.alloc_prefill_workspace(d_rq, T)
         preps = 5
         for _ in range(2):
-            rq.prefill_attn(d_rq, pq, pk, pv, plens, scale, pout)
+            rq.prefill_attn(d_rq, pq, pk, pv, plens, scale, pout, pws)
         torch.cuda.synchronize()
         times = []
         for _ in range(preps):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            rq.prefill_attn(d_rq, pq, pk, pv, plens, scale, pout)
+            rq.prefill_attn(d_rq, pq, pk, pv, plens, scale, pout, pws)
             e1.record(stream)
             e1.synchronize()
             times.append(e0.elapsed_time(e1))
         ms = sorted(times)[preps // 2]
         flops = 4.0 * D * (T * (T + 1) / 2) * B * H
-        result["prefill"] = {"kernel": f"prefill_attn_kernel<{D}> (rq_prefill_attn, one loop, causal)",
+        result["prefill"] = {"kernel": f"prefill_vt_kernel<{D}> + prefill_attn_kernel<{D}> (rq_prefill_attn, "
+                                       "one loop, causal; time of both launches)",
                              "tokens": B * T, "ms_per_launch": ms, "flops_per_launch": flops,
                              "tflops": flops / (ms * 1e-3) / 1e12, "bound": "mfma", "peak_tflops": BF16_PEAK_TFLOPS,
                              "frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                              "prompt_tokens_per_s": B * T / (ms * 1e-3)}
         log(f"prefill: {ms:.2f} ms per loop-layer, {result['prefill']['tflops']:.0f} TFLOP/s")
-        del pq, pk, pv, pout
+        del pq, pk, pv, pout, pws
 
     if args.calibrate_copy:
         # a plain streaming kernel of known size for scaling the HBM counters:

@@ -74,7 +74,9 @@ def _load():
     L.rq_decode_attn_bf16.restype = ctypes.c_int
     L.rq_decode_attn_bf16.argtypes = [P, P, P, P, P, P, P, ctypes.c_float, P, P, Z, P, P]
     L.rq_prefill_attn.restype = ctypes.c_int
-    L.rq_prefill_attn.argtypes = [P, P, P, P, P, I, ctypes.c_float, P, P, P]
+    L.rq_prefill_attn.argtypes = [P, P, P, P, P, I, ctypes.c_float, P, P, Z, P, P]
+    L.rq_prefill_workspace_bytes.restype = Z
+    L.rq_prefill_workspace_bytes.argtypes = [P, I]
     L.rq_status_str.restype = ctypes.c_char_p
     L.rq_status_str.argtypes = [ctypes.c_int]
     L.rq_version.restype = ctypes.c_char_p
@@ -222,13 +224,26 @@ def quantize_append(cache: LayerCache, kv: torch.Tensor, pos: torch.Tensor, n: i
                                   _ptr(dev_err), _stream(stream)), "rq_quantize_append")
 
 
+def prefill_workspace_bytes(d: Desc, n: int) -> int:
+    return lib.rq_prefill_workspace_bytes(ctypes.byref(d), n)
+
+
+def alloc_prefill_workspace(d: Desc, n: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(prefill_workspace_bytes(d, n), 1), dtype=torch.uint8, device=device)
+
+
 def prefill_attn(d: Desc, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lens: torch.Tensor, scale: float,
-                 out: torch.Tensor, dev_err: torch.Tensor | None = None, stream=None):
+                 out: torch.Tensor, workspace: torch.Tensor | None = None, dev_err: torch.Tensor | None = None,
+                 stream=None):
     """Causal prefill attention of one loop: q, k, v bf16 [B][H][n][D]; lens int32 [B];
-    out fp32 [B][H][n][D] (rows past lens[b] not written)."""
+    out fp32 [B][H][n][D] (rows past lens[b] not written). The workspace is allocated
+    here when not given."""
     n = q.shape[2]
+    if workspace is None:
+        workspace = alloc_prefill_workspace(d, n, q.device)
     _check(lib.rq_prefill_attn(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(lens), n, scale, _ptr(out),
-                               _ptr(dev_err), _stream(stream)), "rq_prefill_attn")
+                               _ptr(workspace), workspace.numel(), _ptr(dev_err), _stream(stream)),
+           "rq_prefill_attn")
 
 
 def decode_attn(cache: LayerCache, loop: int, q, k_cur, v_cur, past_len, scale: float, out, workspace,

@@ -397,9 +397,14 @@ rq_status rq_decode_attn_bf16(const rq_desc* d, const uint16_t* k_cache, const u
   return rq_decode_combine(d, nullptr, q, k_cur, v_cur, past_len, softmax_scale, out, ws, ws_bytes, dev_err, stream);
 }
 
+size_t rq_prefill_workspace_bytes(const rq_desc* d, int32_t n) {
+  if (check_shape(d) != RQ_OK || n < 0) return 0;
+  return prefill_workspace_bytes(d->batch, d->heads, d->head_dim, n);
+}
+
 rq_status rq_prefill_attn(const rq_desc* d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                          const int32_t* lens, int32_t n, float softmax_scale, float* out, int32_t* dev_err,
-                          void* stream) {
+                          const int32_t* lens, int32_t n, float softmax_scale, float* out, void* ws,
+                          size_t ws_bytes, int32_t* dev_err, void* stream) {
   rq_status s = check_shape(d);
   if (s != RQ_OK) return s;
   if (n < 0) return RQ_E_SHAPE;
@@ -409,17 +414,23 @@ rq_status rq_prefill_attn(const rq_desc* d, const uint16_t* q, const uint16_t* k
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f)) return RQ_E_SHAPE;
   const long long blocks = ((long long)n + 127) / 128 * d->batch * d->heads;
   if (blocks > 0x7FFFFFFFLL) return RQ_E_SHAPE;
+  // 32-bit byte offsets of the range-checked loads: one (b, h) of K, V and V^T
+  if ((unsigned long long)(n + 64) * d->head_dim * 2 > 0x7FFFFFFFull) return RQ_E_SHAPE;
+  if (!ws || ws_bytes < prefill_workspace_bytes(d->batch, d->heads, d->head_dim, n) || ((uintptr_t)ws & 255) != 0)
+    return RQ_E_WORKSPACE;
   PrefillParams p;
   p.q = q;
   p.k = k;
   p.v = v;
   p.lens = lens;
   p.out = out;
+  p.vt = static_cast<uint16_t*>(ws);
   p.dev_err = dev_err;
   p.scale_log2 = softmax_scale * kLog2e;
   p.B = d->batch;
   p.H = d->heads;
   p.T = n;
+  p.Tp = (n + 63) / 64 * 64;
   return launch_prefill(p, d->head_dim, stream) == 0 ? RQ_OK : RQ_E_HIP;
 }
 

@@ -118,9 +118,10 @@ struct PrefillParams {
   const uint16_t* v;
   const int32_t* lens;      // [B], clamped to [0, T]
   float* out;               // fp32 [B][H][T][D]
+  uint16_t* vt;             // workspace: fp16 V^T [B][H][D][Tp]
   int32_t* dev_err;         // may be null
   float scale_log2;
-  int B, H, T;
+  int B, H, T, Tp;          // Tp: T rounded up to the key tile
 };
 
 // Launchers (return hipError_t as int; 0 = success). Defined in the .hip files.
@@ -132,6 +133,7 @@ int launch_decode_paged_tile(const DecodeParams& p, int D, int ncomp, const int*
 int launch_bf16(const Bf16Params& p, int D, int nsplit, void* stream);
 int launch_combine(const CombineParams& p, int D, int B, void* stream);
 int launch_prefill(const PrefillParams& p, int D, void* stream);
+size_t prefill_workspace_bytes(int B, int H, int D, int T);
 bool have_decode_kernel(int D, int ncomp, const int* bits);
 
 }  // namespace rq

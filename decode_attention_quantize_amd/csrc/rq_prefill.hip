@@ -12,8 +12,11 @@
 //   online softmax in the log2 domain, per query column (a lane's column is
 //                  lane % 16, so the rescale of its accumulators is lane-local);
 //   O^T += V^T P^T v_mfma_f32_16x16x32_f16: P in fp16 (2^-11 relative
-//                  rounding; bf16 would cost 2^-9) and V converted to fp16 when
-//                  staged, V^T (A operand) from a transposed LDS tile.
+//                  rounding; bf16 would cost 2^-9) and V^T (A operand) in fp16,
+//                  transposed and converted once per call by a first pass
+//                  (prefill_vt_kernel) into the caller's workspace, so the
+//                  workgroups that read a key tile (up to T / 128 of them) only
+//                  copy it into LDS.
 // The key rows of each 16-row S tile are permuted (rows 4i..4i+3 of tile 2c+h
 // are keys 32c + 8i + 4h + 0..3) so that the S accumulators a lane holds are
 // exactly the eight consecutive keys its P operand needs: no lane exchange
@@ -29,6 +32,16 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// LDS row paddings (elements): 32 bytes keep the 16-byte operand reads of a
+// 16-row tile free of bank conflicts (measured: 16 bytes left half the LDS
+// cycles in conflicts, none with 32).
+#ifndef RQ_PF_KPAD
+#define RQ_PF_KPAD 16
+#endif
+#ifndef RQ_PF_VPAD
+#define RQ_PF_VPAD 16
+#endif
 
 constexpr int kBQ = 128;          // queries per workgroup (32 per wave)
 constexpr int kBK = 64;           // keys per tile
@@ -48,20 +61,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     PrefillParams p) {
   constexpr int KS = D / 32;      // k-steps of S (32 channels each)
   constexpr int MD = D / 16;      // 16-channel tiles of O^T
-  constexpr int KP = D + 8;       // padded LDS row of K and Q (bf16)
-  constexpr int VP = kBK + 8;     // padded LDS row of V^T (fp16)
+  constexpr int KP = D + RQ_PF_KPAD;   // padded LDS row of K (bf16)
+  constexpr int VP = kBK + RQ_PF_VPAD; // padded LDS row of V^T (fp16)
   constexpr int KC = kBK * (D / 8);                       // 16-byte chunks of a K tile
-  constexpr int VC = (kBK / 2) * (D / 8);                 // (key pair, 8 channels) items of a V tile
+  constexpr int VC = D * (kBK / 8);                       // 16-byte chunks (8 keys of a channel) of a V^T tile
   constexpr int KPF = (KC + kThreads - 1) / kThreads;     // per thread
   constexpr int VPF = (VC + kThreads - 1) / kThreads;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[kBQ * KP];
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kBK * KP];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
 
   // heaviest query blocks (most keys under the causal mask) are dispatched first
   const int nqb = (p.T + kBQ - 1) / kBQ;
   const int BH = p.B * p.H;
-  const int qb = nqb - 1 - (int)blockIdx.x / BH;
+  const int qblk = nqb - 1 - (int)blockIdx.x / BH;
   const int bh = (int)blockIdx.x % BH;
   const int b = bh / p.H;
   int len = p.lens[b];
@@ -69,7 +81,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   if ((len < 0 || len > p.T) && threadIdx.x == 0 && (int)blockIdx.x < BH && bh % p.H == 0 && p.dev_err)
     atomicOr(p.dev_err, RQ_DEVERR_LENGTH);
   len = len < 0 ? 0 : (len > p.T ? p.T : len);
-  const int q0 = qb * kBQ;
+  const int q0 = qblk * kBQ;
   if (q0 >= len) return;                               // whole block, before any barrier
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -79,11 +91,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int qw = q0 + 32 * wave;                       // this wave's first query
   const size_t head = (size_t)bh * p.T * D;            // element offset of (b, h) in q, k, v, out
 
-  // ---- the block's queries in LDS (rows past the tensor clamp to its last row)
-  for (int c = tid; c < kBQ * (D / 8); c += kThreads) {
-    const int r = c / (D / 8), d0 = 8 * (c % (D / 8));
-    const int qi = min(q0 + r, p.T - 1);
-    *reinterpret_cast<uint4*>(&Qs[r * KP + d0]) = *reinterpret_cast<const uint4*>(p.q + head + (size_t)qi * D + d0);
+  // ---- the wave's queries as B operands, held for the whole pass: query
+  // qw + 16 nt + col (rows past the tensor clamp to its last row), channels
+  // 32 ks + 8 grp ..
+  bf16x8 qb[2][KS];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const uint4* src = reinterpret_cast<const uint4*>(p.q + head + (size_t)min(qw + 16 * nt + col, p.T - 1) * D);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qb[nt][ks] = __builtin_bit_cast(bf16x8, src[4 * ks + grp]);
   }
 
   // ---- next tile's K and V, held in registers while the current tile is computed
@@ -93,9 +109,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(p.k + head), (short)0, (int)((uint32_t)len * D * 2), 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(p.v + head), (short)0, (int)((uint32_t)len * D * 2), 0x00020000);
+      p.vt + (size_t)bh * D * p.Tp, (short)0, (int)((uint32_t)p.Tp * D * 2), 0x00020000);
   constexpr uint32_t kOut = 0x80000000u;               // an offset past any sequence
-  uint4 kpf[KPF], vpf[VPF][2];
+  uint4 kpf[KPF], vpf[VPF];
   auto ld16 = [](__amdgpu_buffer_rsrc_t r, uint32_t off) {
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
@@ -111,13 +127,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int j = 0; j < VPF; ++j) {
       const int c = tid + j * kThreads;
-      const int key = 2 * (c % (kBK / 2)), dc = c / (kBK / 2);
-      const uint32_t off = c < VC ? (uint32_t)((k0 + key) * D + 8 * dc) * 2u : kOut;
-      vpf[j][0] = ld16(vrs, off);
-      vpf[j][1] = ld16(vrs, c < VC ? off + D * 2 : kOut);
+      const int d = c / (kBK / 8), kc = c % (kBK / 8);
+      vpf[j] = ld16(vrs, c < VC ? (uint32_t)(d * p.Tp + k0 + 8 * kc) * 2u : kOut);
     }
   };
-  auto stage = [&]() {                                 // K row-major; V transposed, in fp16
+  auto stage = [&]() {                                 // K row-major (rows in read order); V^T
 #pragma unroll
     for (int j = 0; j < KPF; ++j) {
       const int c = tid + j * kThreads;
@@ -126,17 +140,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int j = 0; j < VPF; ++j) {
       const int c = tid + j * kThreads;
-      if (c >= VC) continue;
-      const int key = 2 * (c % (kBK / 2)), dc = c / (kBK / 2);
-      const uint32_t a[4] = {vpf[j][0].x, vpf[j][0].y, vpf[j][0].z, vpf[j][0].w};
-      const uint32_t bb[4] = {vpf[j][1].x, vpf[j][1].y, vpf[j][1].z, vpf[j][1].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = (uint32_t)f32_to_f16_bits(bf16lo(a[i])) | ((uint32_t)f32_to_f16_bits(bf16lo(bb[i])) << 16);
-        const uint32_t hi = (uint32_t)f32_to_f16_bits(bf16hi(a[i])) | ((uint32_t)f32_to_f16_bits(bf16hi(bb[i])) << 16);
-        *reinterpret_cast<uint32_t*>(&Vt[(8 * dc + 2 * i) * VP + key]) = lo;
-        *reinterpret_cast<uint32_t*>(&Vt[(8 * dc + 2 * i + 1) * VP + key]) = hi;
-      }
+      if (c < VC) *reinterpret_cast<uint4*>(&Vt[(c / (kBK / 8)) * VP + 8 * (c % (kBK / 8))]) = vpf[j];
     }
   };
 
@@ -162,13 +166,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
     // ---- S^T tiles: [mt][nt], rows = keys tile_key(mt, 4 grp + i), column = query.
     // B operands: query qw + 16 nt + col, channels 32 ks + 8 grp .. + 7
-    bf16x8 qb[2][KS];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qb[nt][ks] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const uint4*>(&Qs[(32 * wave + 16 * nt + col) * KP + 32 * ks + 8 * grp]));
     f32x4 s[4][2];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -268,16 +265,67 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 }
 
+// First pass: V^T in fp16, vt[b][h][d][key] with keys padded to Tp (a
+// multiple of the key tile); keys at or past the sequence's length are zero,
+// so the attention pass reads whole tiles without checks. One workgroup per
+// (key tile, b, h): rows are read coalesced, transposed through LDS, and
+// written as 128-byte channel rows.
+template <int D>
+__global__ __launch_bounds__(kThreads) void prefill_vt_kernel(PrefillParams p) {
+  constexpr int VP = kBK + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
+  const int k0 = (int)blockIdx.x * kBK, bh = (int)blockIdx.y, b = bh / p.H, tid = threadIdx.x;
+  int len = p.lens[b];
+  len = len < 0 ? 0 : (len > p.T ? p.T : len);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.v + (size_t)bh * p.T * D), (short)0, (int)((uint32_t)len * D * 2), 0x00020000);
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  for (int c = tid; c < (kBK / 2) * (D / 8); c += kThreads) {
+    const int key = 2 * (c % (kBK / 2)), dc = c / (kBK / 2);
+    const uint32_t off = (uint32_t)((k0 + key) * D + 8 * dc) * 2u;
+    const u32x4 w0 = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
+    const u32x4 w1 = __builtin_amdgcn_raw_buffer_load_b128(vrs, off + D * 2, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = (uint32_t)f32_to_f16_bits(bf16lo(w0[i])) | ((uint32_t)f32_to_f16_bits(bf16lo(w1[i])) << 16);
+      const uint32_t hi = (uint32_t)f32_to_f16_bits(bf16hi(w0[i])) | ((uint32_t)f32_to_f16_bits(bf16hi(w1[i])) << 16);
+      *reinterpret_cast<uint32_t*>(&Vt[(8 * dc + 2 * i) * VP + key]) = lo;
+      *reinterpret_cast<uint32_t*>(&Vt[(8 * dc + 2 * i + 1) * VP + key]) = hi;
+    }
+  }
+  __syncthreads();
+  uint16_t* dst = p.vt + (size_t)bh * D * p.Tp + k0;
+  for (int c = tid; c < D * (kBK / 8); c += kThreads) {
+    const int d = c / (kBK / 8), kc = c % (kBK / 8);
+    *reinterpret_cast<uint4*>(dst + (size_t)d * p.Tp + 8 * kc) = *reinterpret_cast<const uint4*>(&Vt[d * VP + 8 * kc]);
+  }
+}
+
 }  // namespace
+
+size_t prefill_workspace_bytes(int B, int H, int D, int T) {
+  const size_t Tp = (size_t)(T + kBK - 1) / kBK * kBK;
+  return (size_t)B * H * D * Tp * 2;
+}
 
 int launch_prefill(const PrefillParams& p, int D, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int nqb = (p.T + kBQ - 1) / kBQ;
   const dim3 grid((unsigned)(nqb * p.B * p.H));
+  const dim3 vgrid((unsigned)(p.Tp / kBK), (unsigned)(p.B * p.H));
   switch (D) {
-    case 64: hipLaunchKernelGGL(prefill_attn_kernel<64>, grid, dim3(kThreads), 0, s, p); break;
-    case 96: hipLaunchKernelGGL(prefill_attn_kernel<96>, grid, dim3(kThreads), 0, s, p); break;
-    case 128: hipLaunchKernelGGL(prefill_attn_kernel<128>, grid, dim3(kThreads), 0, s, p); break;
+    case 64:
+      hipLaunchKernelGGL(prefill_vt_kernel<64>, vgrid, dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL(prefill_attn_kernel<64>, grid, dim3(kThreads), 0, s, p);
+      break;
+    case 96:
+      hipLaunchKernelGGL(prefill_vt_kernel<96>, vgrid, dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL(prefill_attn_kernel<96>, grid, dim3(kThreads), 0, s, p);
+      break;
+    case 128:
+      hipLaunchKernelGGL(prefill_vt_kernel<128>, vgrid, dim3(kThreads), 0, s, p);
+      hipLaunchKernelGGL(prefill_attn_kernel<128>, grid, dim3(kThreads), 0, s, p);
+      break;
     default: return -1;
   }
   return (int)hipGetLastError();

@@ -243,14 +243,18 @@ rq_status rq_decode_attn_bf16(const rq_desc* desc, const uint16_t* k_cache, cons
  *   q, k, v: bf16 [B][H][n][D] (one loop's prompt), 16-byte aligned;
  *   lens: device int32 [B], the prompt length of each sequence (clamped to
  *     [0, n]; RQ_DEVERR_LENGTH if outside); rows past it are not written;
- *   out: fp32 [B][H][n][D], 16-byte aligned.
+ *   out: fp32 [B][H][n][D], 16-byte aligned;
+ *   workspace: device memory of rq_prefill_workspace_bytes(desc, n) bytes,
+ *     256-byte aligned (a first pass writes V transposed in fp16 there).
  * Only batch, heads and head_dim of desc are used (n is the prompt capacity,
- * independent of max_tokens). softmax_scale must be positive (RQ_E_SHAPE). The matrix products run in bf16 (scores) and fp16
- * (probabilities times values) with fp32 accumulation; values must lie within
- * the fp16 range (|v| < 65504). n == 0 is a no-op. */
+ * independent of max_tokens). softmax_scale must be positive (RQ_E_SHAPE).
+ * The matrix products run in bf16 (scores) and fp16 (probabilities times
+ * values) with fp32 accumulation; values must lie within the fp16 range
+ * (|v| < 65504). n == 0 is a no-op. */
+size_t rq_prefill_workspace_bytes(const rq_desc* desc, int32_t n);
 rq_status rq_prefill_attn(const rq_desc* desc, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                          const int32_t* lens, int32_t n, float softmax_scale, float* out, int32_t* dev_err,
-                          void* stream);
+                          const int32_t* lens, int32_t n, float softmax_scale, float* out, void* workspace,
+                          size_t workspace_bytes, int32_t* dev_err, void* stream);
 
 /* Static description of a status code. */
 const char* rq_status_str(rq_status status);

@@ -268,18 +268,26 @@ def test_prefill_validation():
     L, by = rq.lib, ctypes.byref
     d = _desc()
     f = ctypes.c_float(0.1)
-    assert L.rq_prefill_attn(None, FAKE, FAKE, FAKE, FAKE, 8, f, FAKE, None, 0) == 1
-    assert L.rq_prefill_attn(by(d), FAKE, FAKE, FAKE, FAKE, -1, f, FAKE, None, 0) == 2
-    assert L.rq_prefill_attn(by(d), None, None, None, None, 0, f, None, None, 0) == 0     # n == 0: no-op
-    assert L.rq_prefill_attn(by(d), None, FAKE, FAKE, FAKE, 8, f, FAKE, None, 0) == 1
-    assert L.rq_prefill_attn(by(d), FAKE, FAKE, FAKE, None, 8, f, FAKE, None, 0) == 1
-    assert L.rq_prefill_attn(by(d), FAKE, FAKE, FAKE, FAKE, 8, f, None, None, 0) == 1
-    assert L.rq_prefill_attn(by(d), FAKE, ctypes.c_void_p(0x100008), FAKE, FAKE, 8, f, FAKE, None, 0) == 10
-    assert L.rq_prefill_attn(by(d), FAKE, FAKE, FAKE, FAKE, 8, f, ctypes.c_void_p(0x100004), None, 0) == 10
-    assert L.rq_prefill_attn(by(d), FAKE, FAKE, FAKE, FAKE, 8, ctypes.c_float(float("inf")), FAKE, None, 0) == 2
-    assert L.rq_prefill_attn(by(d), FAKE, FAKE, FAKE, FAKE, 8, ctypes.c_float(0.0), FAKE, None, 0) == 2
-    assert L.rq_prefill_attn(by(d), FAKE, FAKE, FAKE, FAKE, 8, ctypes.c_float(-0.1), FAKE, None, 0) == 2
-    assert L.rq_prefill_attn(by(_desc(head_dim=80)), FAKE, FAKE, FAKE, FAKE, 8, f, FAKE, None, 0) == 2
+    ws = rq.prefill_workspace_bytes(d, 8)
+    assert ws == 2 * 3 * 128 * 64 * 2                     # B H D x 8 keys padded to one 64-key tile, fp16
+    assert rq.prefill_workspace_bytes(d, 65) == 2 * 3 * 128 * 128 * 2
+    args = lambda n=8, q=FAKE, k=FAKE, lens=FAKE, out=FAKE, scale=f, ws_ptr=FAKE, ws_n=ws: (
+        by(d), q, k, FAKE, lens, n, scale, out, ws_ptr, ws_n, None, 0)
+    assert L.rq_prefill_attn(None, FAKE, FAKE, FAKE, FAKE, 8, f, FAKE, FAKE, ws, None, 0) == 1
+    assert L.rq_prefill_attn(*args(n=-1)) == 2
+    assert L.rq_prefill_attn(by(d), None, None, None, None, 0, f, None, None, 0, None, 0) == 0   # n == 0: no-op
+    assert L.rq_prefill_attn(*args(q=None)) == 1
+    assert L.rq_prefill_attn(*args(lens=None)) == 1
+    assert L.rq_prefill_attn(*args(out=None)) == 1
+    assert L.rq_prefill_attn(*args(k=ctypes.c_void_p(0x100008))) == 10
+    assert L.rq_prefill_attn(*args(out=ctypes.c_void_p(0x100004))) == 10
+    assert L.rq_prefill_attn(*args(scale=ctypes.c_float(float("inf")))) == 2
+    assert L.rq_prefill_attn(*args(scale=ctypes.c_float(0.0))) == 2
+    assert L.rq_prefill_attn(*args(scale=ctypes.c_float(-0.1))) == 2
+    assert L.rq_prefill_attn(*args(ws_ptr=None)) == 5
+    assert L.rq_prefill_attn(*args(ws_n=ws - 1)) == 5
+    assert L.rq_prefill_attn(*args(ws_ptr=ctypes.c_void_p(0x100010))) == 5
+    assert L.rq_prefill_attn(by(_desc(head_dim=80)), FAKE, FAKE, FAKE, FAKE, 8, f, FAKE, FAKE, ws, None, 0) == 2
 
 
 def test_split_api_validation():
