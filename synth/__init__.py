@@ -92,6 +92,8 @@ WORKLOADS = {
     # Ouro-1.4B-shaped fixed batch, 16k context, 64 decode steps, [2,2,4,4]
     "ouro_16k": Workload("ouro_16k", 24, 8, 16, 128, 4, 16384, 64, (2, 2, 4, 4), (4, 4, 2, 2)),
     # Ouro-1.4B-shaped capacity sweep at 8k context (batch set per run)
+    # the 16k workload with the paper's main mixed plan: INT2 residuals, INT4 anchor only
+    "ouro_16k_2224": Workload("ouro_16k_2224", 24, 8, 16, 128, 4, 16384, 64, (2, 2, 2, 4), (4, 2, 2, 2)),
     # the 16k workload with the 2-bit residual loops in groups of 16 channels
     "ouro_16k_g16": Workload("ouro_16k_g16", 24, 8, 16, 128, 4, 16384, 64, (2, 2, 4, 4), (4, 4, 2, 2),
                              int2_group=16),
