@@ -382,16 +382,42 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   int split, b, h;
   split_item(p.nsplit, p.B, p.H, split, b, h);
   const int bh = b * p.H + h;
-  int len = p.past_len[b];
-  len = len < 0 ? 0 : (len > p.T_max ? p.T_max : len);
-  if (split >= slots_used(len, p.nsplit, p.unit)) return;  // whole block, before any barrier
-  const int chunk = slot_len(len, p.nsplit, p.unit);
-  const int start = split * chunk;
-  const int end = min(start + chunk, len);
-
   // the wave index is uniform across the wave: say so, so that tile positions and
   // everything derived from them (paged descriptors) live in scalar registers
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+
+  // The prologue overlaps its memory round trips: the sequence length (a scalar
+  // load, issued before anything that could be taken to write memory), q (once
+  // per workgroup, into LDS) and the query rotation's rows of H_K (half a row
+  // per thread) are requested together, then the first tile of the cache; only
+  // then does the rotation wait for its operands. What bounds the prologue is
+  // the data the compute unit's loads return (64 KB of H_K per workgroup), so q
+  // is not loaded per thread.
+  int len = p.past_len[b];
+  constexpr int RJ = D / 16;
+  const bool rot_on = tid < 2 * D;
+  __shared__ uint4 qs[D / 8];
+  uint4 qg = make_uint4(0, 0, 0, 0);
+  if (tid < D / 8) qg = reinterpret_cast<const uint4*>(p.q + (size_t)bh * D)[tid];
+  float4 hu[RJ], hw[RJ];
+  if (rot_on) {
+    const int row = tid >> 1, half = tid & 1;
+    const float4* hr = reinterpret_cast<const float4*>(p.rotk + ((size_t)h * D + row) * D + half * (D / 2));
+#pragma unroll
+    for (int j = 0; j < RJ; ++j) {
+      hu[j] = hr[2 * j];
+      hw[j] = hr[2 * j + 1];
+    }
+  }
+  asm volatile("" ::: "memory");  // those loads are issued here, ahead of the ones below
+
+  // A slot past the sequence's last used one streams nothing and stores no
+  // partial; its workgroup still runs to the end (no return with loads in flight).
+  len = len < 0 ? 0 : (len > p.T_max ? p.T_max : len);
+  const bool active = split < slots_used(len, p.nsplit, p.unit);  // uniform over the workgroup
+  const int chunk = slot_len(len, p.nsplit, p.unit);
+  const int start = active ? split * chunk : 0;
+  const int end = active ? min(start + chunk, len) : 0;
 
   // This workgroup reads rows [start, end) of its (b, h); the descriptors cover
   // exactly that range, so tiles running past its end load zeros (masked). A
@@ -492,17 +518,26 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   int base = start + wave * TILE;
   Tile<D, NC, CB> A, B, C;
 
+  // first tile(s) (and paged block ids) requested before the rotation waits
+  if constexpr (MODE != kContig) {
+#pragma unroll
+    for (int k = 0; k < TAHEAD; ++k) table_load(base + k * STRIDE, tq[k]);
+  }
+  fetch(A, base);
+  if constexpr (DEPTH == 3) fetch(B, base + STRIDE);
+  asm volatile("" ::: "memory");
+  if (tid < D / 8) qs[tid] = qg;
+  __syncthreads();
+
   // ---- q' = scale log2(e) H_K q for this (b, h): two threads per row, each
-  // reading half of the row and half of q straight from memory (one round trip)
-  if (tid < 2 * D) {
+  // with half of the row and half of q
+  if (rot_on) {
     const int row = tid >> 1, half = tid & 1;
-    const float4* hr = reinterpret_cast<const float4*>(p.rotk + ((size_t)h * D + row) * D + half * (D / 2));
-    const uint4* qv = reinterpret_cast<const uint4*>(p.q + (size_t)bh * D + half * (D / 2));
     float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) {
-      const uint4 w = qv[j];
-      const float4 u = hr[2 * j], v = hr[2 * j + 1];
+    for (int j = 0; j < RJ; ++j) {
+      const uint4 w = qs[half * RJ + j];
+      const float4 u = hu[j], v = hw[j];
       a0 = fmaf(u.x, bf16lo(w.x), a0);
       a1 = fmaf(u.y, bf16hi(w.x), a1);
       a0 = fmaf(u.z, bf16lo(w.y), a0);
@@ -517,14 +552,6 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     if (half == 0) qr[row] = acc * p.scale_log2;
   }
   __syncthreads();
-  // (Requesting the first tiles before the rotation would overlap the two
-  // latencies but keeps a tile live across it, which costs register spills.)
-  if constexpr (MODE != kContig) {
-#pragma unroll
-    for (int k = 0; k < TAHEAD; ++k) table_load(base + k * STRIDE, tq[k]);
-  }
-  fetch(A, base);
-  if constexpr (DEPTH == 3) fetch(B, base + STRIDE);
 
   // This lane's group of q' in fixed point (per-group exponent). qsum, which
   // multiplies the group offsets, is the sum of the same fixed-point values, so a
@@ -744,6 +771,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     }
   }
 
+  if (!active) return;
   float val[32];
 #pragma unroll
   for (int e = 0; e < 32; ++e) val[e] = fmaf(acc[e], kTwo24 / vclass<REF>(e), bias[G16 ? (e >> 4) : 0]);
