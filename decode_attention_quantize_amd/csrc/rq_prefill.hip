@@ -52,6 +52,21 @@ __host__ __device__ constexpr int tile_key(int mt, int r) { return 32 * (mt >> 1
 // tile) are stored consecutively, so the A-operand reads do not collide on banks.
 __host__ __device__ constexpr int k_row(int k) { return (k & 32) | ((k & 4) << 2) | ((k >> 1) & 12) | (k & 3); }
 
+// IEEE 754-2019 maximum (NaN-propagating): unlike fmaxf it needs no quieting
+// of its operands in the kernel's IEEE mode, and chains of it fold into
+// three-input instructions. Scores are finite or -inf.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// Maximum over the four lanes of a query column (lanes l, l ^ 16, l ^ 32,
+// l ^ 48): the lane-swap instructions exchange half-waves and 16-lane rows in
+// the vector unit, without a round trip through LDS.
+__device__ __forceinline__ float col_max(float t) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_int(t), __float_as_int(t), false, false);
+  t = vmax(__int_as_float(a[0]), __int_as_float(a[1]));           // max(x[l], x[l ^ 32])
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_int(t), __float_as_int(t), false, false);
+  return vmax(__int_as_float(b[0]), __int_as_float(b[1]));        // and of l ^ 16
+}
+
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
@@ -87,7 +102,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
-  const int x16 = (lane ^ 16) << 2, x32 = (lane ^ 32) << 2;   // byte addresses of the lanes of a column
   const int qw = q0 + 32 * wave;                       // this wave's first query
   const size_t head = (size_t)bh * p.T * D;            // element offset of (b, h) in q, k, v, out
 
@@ -122,25 +136,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int j = 0; j < KPF; ++j) {
       const int c = tid + j * kThreads;
       const int key = c / (D / 8), d0 = 8 * (c % (D / 8));
-      kpf[j] = ld16(krs, c < KC ? (uint32_t)((k0 + key) * D + d0) * 2u : kOut);
+      kpf[j] = ld16(krs, (KC % kThreads == 0 || c < KC) ? (uint32_t)((k0 + key) * D + d0) * 2u : kOut);
     }
 #pragma unroll
     for (int j = 0; j < VPF; ++j) {
       const int c = tid + j * kThreads;
       const int d = c / (kBK / 8), kc = c % (kBK / 8);
-      vpf[j] = ld16(vrs, c < VC ? (uint32_t)(d * p.Tp + k0 + 8 * kc) * 2u : kOut);
+      vpf[j] = ld16(vrs, (VC % kThreads == 0 || c < VC) ? (uint32_t)(d * p.Tp + k0 + 8 * kc) * 2u : kOut);
     }
   };
   auto stage = [&]() {                                 // K row-major (rows in read order); V^T
 #pragma unroll
     for (int j = 0; j < KPF; ++j) {
       const int c = tid + j * kThreads;
-      if (c < KC) *reinterpret_cast<uint4*>(&Ks[k_row(c / (D / 8)) * KP + 8 * (c % (D / 8))]) = kpf[j];
+      if (KC % kThreads == 0 || c < KC) *reinterpret_cast<uint4*>(&Ks[k_row(c / (D / 8)) * KP + 8 * (c % (D / 8))]) = kpf[j];
     }
 #pragma unroll
     for (int j = 0; j < VPF; ++j) {
       const int c = tid + j * kThreads;
-      if (c < VC) *reinterpret_cast<uint4*>(&Vt[(c / (kBK / 8)) * VP + 8 * (c % (kBK / 8))]) = vpf[j];
+      if (VC % kThreads == 0 || c < VC) *reinterpret_cast<uint4*>(&Vt[(c / (kBK / 8)) * VP + 8 * (c % (kBK / 8))]) = vpf[j];
     }
   };
 
@@ -149,7 +163,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
     for (int md = 0; md < MD; ++md) o[nt][md] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};   // per query column, lane-partial l
+  float mrow[2] = {-INFINITY, -INFINITY};             // per query column (log2 domain)
+  // Column sums of P^T on the matrix cores: an all-ones A operand gives, in every
+  // row of the 16x16 result, sum_k P[k][query]: the softmax denominator of the
+  // same fp16 P the value product uses, with no lane reduction.
+  f32x4 lsum[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  const f16x8 ones = {(_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f,
+                      (_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f};
 
   const int kend = min(len, q0 + kBQ);                 // keys any query of the block may see
   const int nkt = (kend + kBK - 1) / kBK;
@@ -198,61 +218,78 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // ---- online softmax per query column (log2 domain; the scale is positive, so the
     // column max of the raw scores gives the max of the scaled ones)
     f16x8 pb[2][2];                                    // [nt][32-key chunk]: P^T as B operands
-    float fcol[2];
+    float fcol[2], bases[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      float tmax = -INFINITY;
+      float tmax = s[0][nt][0];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        tmax = fmaxf(fmaxf(tmax, fmaxf(s[mt][nt][0], s[mt][nt][1])), fmaxf(s[mt][nt][2], s[mt][nt][3]));
-      tmax = fmaxf(tmax, __int_as_float(__builtin_amdgcn_ds_bpermute(x16, __float_as_int(tmax))));
-      tmax = fmaxf(tmax, __int_as_float(__builtin_amdgcn_ds_bpermute(x32, __float_as_int(tmax))));
-      const float mnew = fmaxf(mrow[nt], tmax * p.scale_log2);
+#pragma unroll
+        for (int i = (mt == 0 ? 1 : 0); i < 4; ++i) tmax = vmax(tmax, s[mt][nt][i]);
+      tmax = col_max(tmax);
+      const float mnew = vmax(mrow[nt], tmax * p.scale_log2);
       const float base = mnew == -INFINITY ? 0.f : mnew;          // a column with nothing visible yet
       fcol[nt] = __builtin_amdgcn_exp2f(mrow[nt] - base);
       mrow[nt] = mnew;
-      float ls = 0.f;
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float pv = __builtin_amdgcn_exp2f(fmaf(s[2 * c + h][nt][i], p.scale_log2, -base));
-            ls += pv;
-            pb[nt][c][4 * h + i] = (_Float16)pv;
-          }
-      lrow[nt] = fmaf(lrow[nt], fcol[nt], ls);
+      bases[nt] = base;
     }
     // the accumulators are rescaled only when some column's max moved (rare after
     // the first tiles)
     if (__builtin_amdgcn_ballot_w64(fcol[0] != 1.0f || fcol[1] != 1.0f)) {
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
         for (int md = 0; md < MD; ++md) o[nt][md] *= fcol[nt];
+        lsum[nt] *= fcol[nt];
+      }
     }
 
-    // ---- O^T += V^T P^T: A = V^T rows (channel 16 md + col), keys 32 c + 8 grp ..
+    // ---- per 32-key chunk c: P^T (exponentials, fp16) and O^T += V^T P^T with
+    // A = V^T rows (channel 16 md + col), keys 32 c + 8 grp ... The matrix-core
+    // products of chunk 0 are issued interleaved with the exponentials of chunk 1
+    // (independent work for the vector unit while each product runs).
+    auto exps = [&](int c) {
 #pragma unroll
-    for (int md = 0; md < MD; ++md) {
-      const uint16_t* vr = &Vt[(16 * md + col) * VP + 8 * grp];
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const f16x8 va = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(vr + 32 * c));
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            pb[nt][c][4 * h + i] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[2 * c + h][nt][i], p.scale_log2, -bases[nt]));
+    };
+    auto pv = [&](int c) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) lsum[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb[nt][c], lsum[nt], 0, 0, 0);
+#pragma unroll
+      for (int md = 0; md < MD; ++md) {
+        const f16x8 va =
+            __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(&Vt[(16 * md + col) * VP + 8 * grp + 32 * c]));
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) o[nt][md] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[nt][c], o[nt][md], 0, 0, 0);
       }
+    };
+    exps(0);
+    __builtin_amdgcn_sched_barrier(0);
+    pv(0);
+    exps(1);
+#ifndef RQ_PF_NO_INTERLEAVE
+    // 2 + 2 MD products, MD reads of V^T, 16 exponentials with their fma and 8 packs
+    __builtin_amdgcn_sched_group_barrier(0x100, MD, 0);   // V^T operand reads first
+#pragma unroll
+    for (int k = 0; k < 2 + 2 * MD; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three vector instructions
     }
+#endif
+    __builtin_amdgcn_sched_barrier(0);
+    pv(1);
   }
 
   // ---- normalize and store: lane holds O^T[16 md + 4 grp + i][query col of tile nt]
   if (qw >= len) return;
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
-    float l = lrow[nt];
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    const float l = lsum[nt][0];
     const int qi = qw + 16 * nt + col;
     if (qi >= len) continue;
     const float inv = 1.0f / l;
