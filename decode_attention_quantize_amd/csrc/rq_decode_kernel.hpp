@@ -356,6 +356,14 @@ constexpr int waves_for() {
   return (NC <= 2 && bits <= 6) ? RQ_WAVES_SMALL : 2;
 }
 
+// The paged instances keep block ids and row offsets (lane mode) or per-tile
+// descriptors (tile mode) live as well; with groups of 16 that no longer fits
+// three waves' registers without spilling.
+template <int NC, uint32_t CB>
+constexpr int waves_for_paged() {
+  return any_g16<CB, NC>() ? 2 : waves_for<NC, CB>();
+}
+
 // Cache addressing of the streaming kernel.
 //   kContig: the (b, h) series is contiguous; the descriptors cover the slot.
 //   kPagedLane: rows through the block table (token t of sequence b lives in row
@@ -786,13 +794,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
 }
 
 template <int D, int NC, uint32_t CB, int DEPTH>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_for<NC, CB>()))) void
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_for_paged<NC, CB>()))) void
 decode_fused_paged(DecodeParams p) {
   decode_body<D, NC, CB, DEPTH, kPagedLane>(p);
 }
 
 template <int D, int NC, uint32_t CB, int DEPTH>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_for<NC, CB>()))) void
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_for_paged<NC, CB>()))) void
 decode_fused_paged_tile(DecodeParams p) {
   decode_body<D, NC, CB, DEPTH, kPagedTile>(p);
 }
@@ -810,12 +818,15 @@ struct PlanEntry {
 #endif
 // Plans with kernels: one nibble per component, anchor first (0xA = INT2 in
 // groups of 16). RQ_E(D, NC, CB) names the instance a table entry takes.
-#define RQ_PLANS(D)                                                                                        \
+// RQ_PLANS_UP3: one to three components; RQ_PLANS_4: four (chained loops).
+#define RQ_PLANS_UP3(D)                                                                                    \
   RQ_E(D, 1, 0x2), RQ_E(D, 1, 0x4), RQ_E(D, 2, 0x22), RQ_E(D, 2, 0x24), RQ_E(D, 2, 0x42), RQ_E(D, 2, 0x44), \
-      RQ_E(D, 3, 0x244), RQ_E(D, 3, 0x224), RQ_E(D, 3, 0x222), RQ_E(D, 3, 0x444), RQ_E(D, 4, 0x2244),        \
-      RQ_E(D, 4, 0x2224), RQ_E(D, 4, 0x2222), RQ_E(D, 4, 0x4444),                                           \
-      RQ_E(D, 1, 0xA), RQ_E(D, 2, 0xAA), RQ_E(D, 2, 0xA4), RQ_E(D, 3, 0xAA4), RQ_E(D, 4, 0xAAA4),          \
-      RQ_E(D, 3, 0xAAA), RQ_E(D, 4, 0xAAAA)
+      RQ_E(D, 3, 0x244), RQ_E(D, 3, 0x224), RQ_E(D, 3, 0x222), RQ_E(D, 3, 0x444), RQ_E(D, 1, 0xA),          \
+      RQ_E(D, 2, 0xAA), RQ_E(D, 2, 0xA4), RQ_E(D, 3, 0xAA4), RQ_E(D, 3, 0xAAA)
+#define RQ_PLANS_4(D)                                                                                     \
+  RQ_E(D, 4, 0x2244), RQ_E(D, 4, 0x2224), RQ_E(D, 4, 0x2222), RQ_E(D, 4, 0x4444), RQ_E(D, 4, 0xAAA4),     \
+      RQ_E(D, 4, 0xAAAA)
+#define RQ_PLANS(D) RQ_PLANS_UP3(D), RQ_PLANS_4(D)
 
 template <size_t N>
 const PlanEntry* find_plan(const PlanEntry (&table)[N], int D, int nc, const int* kinds) {

@@ -3,14 +3,15 @@
 // one block, so the kernel takes one block id per tile and addresses the
 // tile's rows through per-tile buffer descriptors (rq_decode_kernel.hpp,
 // kPagedTile). D = 96 tiles (42 tokens) never align; that size takes the
-// lane-by-lane path.
+// lane-by-lane path, and so do four-component plans, whose per-tile
+// descriptors (24 scalar registers per component) would spill.
 #include "rq_decode_kernel.hpp"
 
 namespace rq {
 namespace {
 
 #define RQ_E(D, NC, CB) {D, NC, CB, decode_fused_paged_tile<D, NC, CB, RQ_DEPTH>}
-const PlanEntry kTileTable[] = {RQ_PLANS(64), RQ_PLANS(128)};
+const PlanEntry kTileTable[] = {RQ_PLANS_UP3(64), RQ_PLANS_UP3(128)};
 #undef RQ_E
 
 }  // namespace
