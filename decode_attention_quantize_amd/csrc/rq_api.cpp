@@ -24,15 +24,21 @@ static int device_cus() {
 #define RQ_WGS_PER_CU 3
 #endif
 
+#ifndef RQ_MIN_SLOT_TILES
+#define RQ_MIN_SLOT_TILES 8
+#endif
+
 SplitPlan split_plan(const rq_desc* d) {
-  // About RQ_WGS_PER_CU workgroups per compute unit over the whole call, at
-  // most one slot per tile of capacity; slot lengths are set per sequence on
-  // the device (slot_len).
+  // About RQ_WGS_PER_CU workgroups per compute unit over the whole call, but
+  // no more slots than leave each at least RQ_MIN_SLOT_TILES tiles of the
+  // cache's capacity: a workgroup's fixed work (the query rotation, its partial)
+  // costs about as much as streaming that many tiles. Slot lengths are set per
+  // sequence on the device (slot_len).
   const long long unit = tile_tokens(d->head_dim);
   const long long bh = (long long)d->batch * d->heads;
   const long long target = (long long)RQ_WGS_PER_CU * device_cus();
   long long nsplit = (target + bh - 1) / bh;
-  const long long cap = (d->max_tokens + unit - 1) / unit;
+  const long long cap = d->max_tokens / (unit * RQ_MIN_SLOT_TILES);
   if (nsplit > cap) nsplit = cap;
   if (nsplit < 1) nsplit = 1;
   SplitPlan p;

@@ -12,10 +12,7 @@ namespace {
 // original domain from bf16 q and k_cur) and, for the compressed cache, rotate
 // the value sum back once: out = (H_V^T acc + p_cur v_cur) / l.
 //
-// Every load is issued up front and none depends on another: the thread's
-// slice of H_V, q/k_cur/v_cur, and the partials of all nsplit slots (slots a
-// shorter sequence did not write are loaded but ignored), so the kernel waits
-// for memory about once.
+// Its reads are latency-bound; they are ordered and batched as described below.
 template <int D>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   constexpr int NQ = kThreads / D;  // row slices of the H_V^T product
@@ -28,37 +25,57 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   const int j = tid % D, sl = tid / D;
   const bool rot = p.rotv != nullptr;
 
+  // Loads in the order their values are needed: the partials of the first CH
+  // slots, q/k_cur/v_cur, then the thread's slice of H_V. A round's loads are all
+  // issued before the first is used, so a call waits for memory about once per
+  // CH slots (slots past the last one are loaded clamped and ignored).
+  constexpr int CH = 16;
+  const bool on = tid < D;
+  const float* part = p.part + (size_t)bh * p.nsplit * PF;
+  float ms[CH], ls[CH], as[CH];
+  auto load_slots = [&](int s0) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const float* ps = part + (size_t)min(s0 + i, p.nsplit - 1) * PF;
+      ms[i] = ps[0];
+      ls[i] = ps[1];
+      as[i] = ps[4 + (on ? tid : 0)];
+    }
+  };
+  load_slots(0);
+  const int raw_len = p.past_len[b];
+  const size_t qo = (size_t)bh * D + (on ? tid : 0);
+  const uint16_t qh = p.q[qo], kh = p.kcur[qo], vh = p.vcur[qo];
   float hv[RS];
   if (rot && sl < NQ) {
     const float* Hm = p.rotv + ((size_t)h * D + (size_t)sl * RS) * D + j;
 #pragma unroll
     for (int i = 0; i < RS; ++i) hv[i] = Hm[(size_t)i * D];
   }
-  const int raw_len = p.past_len[b];
-  const bool on = tid < D;
-  const size_t qo = (size_t)bh * D + (on ? tid : 0);
-  float x = on ? bf16f(p.q[qo]) * bf16f(p.kcur[qo]) : 0.0f;
-  const float vc = bf16f(p.vcur[qo]);
 
   if ((raw_len < 0 || raw_len > p.T_max) && h == 0 && tid == 0 && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_LENGTH);
   const int len = raw_len < 0 ? 0 : (raw_len > p.T_max ? p.T_max : raw_len);
   const int nvalid = slots_used(len, p.nsplit, p.unit);
 
   // Online merge of the splits' (m, l, acc) relative to their running max M.
-  const float* part = p.part + (size_t)bh * p.nsplit * PF;
   float M = -INFINITY, l = 0.0f, a = 0.0f;
-#pragma unroll 4
-  for (int s = 0; s < p.nsplit; ++s) {
-    const float* ps = part + (size_t)s * PF;
-    const float ms = ps[0], ls = ps[1], as = ps[4 + (on ? tid : 0)];
-    if (s < nvalid && ms > -INFINITY) {
-      const float Mn = fmaxf(M, ms);
-      const float fo = exp2f(M - Mn), fs = exp2f(ms - Mn);
-      l = fmaf(l, fo, ls * fs);
-      a = fmaf(a, fo, as * fs);
-      M = Mn;
+  for (int s0 = 0;;) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      if (s0 + i < nvalid && ms[i] > -INFINITY) {
+        const float Mn = fmaxf(M, ms[i]);
+        const float fo = exp2f(M - Mn), fs = exp2f(ms[i] - Mn);
+        l = fmaf(l, fo, ls[i] * fs);
+        a = fmaf(a, fo, as[i] * fs);
+        M = Mn;
+      }
     }
+    s0 += CH;
+    if (s0 >= nvalid) break;
+    load_slots(s0);
   }
+  float x = on ? bf16f(qh) * bf16f(kh) : 0.0f;
+  const float vc = bf16f(vh);
   if (on) acc_s[tid] = a;
   x = wave_sum(x);
   if ((tid & 63) == 0) wsum[tid >> 6] = x;
