@@ -310,13 +310,22 @@ def main():
                     rq.quantize_append(cs[l], kvcur[k, l], past_len, 1)
         past_len.add_(1)
 
+    # The BF16 comparator's step pays for its cache store as the RQ step pays for
+    # its append: after the final loop, each layer's current K/V of every loop is
+    # written at position past_len (a torch index copy; same values as the
+    # prefilled rows, so the attention reads are unchanged).
+    bf16_pos = torch.empty(1, dtype=torch.long, device=dev)
+
     def bf16_step(k):
+        bf16_pos.copy_(past_len[:1])
         for r in range(L):
             for l in range(w.layers):
                 kc = kvcur[k, l, 0, r, :, :, 0]
                 vc = kvcur[k, l, 1, r, :, :, 0]
                 rq.decode_attn_bf16(d_rq, bf16[l][0, r], bf16[l][1, r], qs[k, l, r], kc, vc, past_len, scale,
                                     out[l, r], ws)
+                if r == L - 1:
+                    bf16[l].index_copy_(4, bf16_pos, kvcur[k, l])
         past_len.add_(1)
 
     side = torch.cuda.Stream()

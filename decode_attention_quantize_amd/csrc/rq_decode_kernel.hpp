@@ -401,23 +401,31 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   // then does the rotation wait for its operands. What bounds the prologue is
   // the data the compute unit's loads return (64 KB of H_K per workgroup), so q
   // is not loaded per thread.
+  // (A paged cache first requests the block ids of its first tiles: the tile
+  // loads wait for them, and vector loads complete in issue order.)
   int len = p.past_len[b];
   constexpr int RJ = D / 16;
   const bool rot_on = tid < 2 * D;
   __shared__ uint4 qs[D / 8];
   uint4 qg = make_uint4(0, 0, 0, 0);
-  if (tid < D / 8) qg = reinterpret_cast<const uint4*>(p.q + (size_t)bh * D)[tid];
   float4 hu[RJ], hw[RJ];
-  if (rot_on) {
-    const int row = tid >> 1, half = tid & 1;
+  // Loaded by every thread, with clamped indices (only the threads that need
+  // them use the values): loads outside branches keep the waits for later
+  // loads exact.
+  auto load_rotation = [&]() {
+    qg = reinterpret_cast<const uint4*>(p.q + (size_t)bh * D)[tid % (D / 8)];
+    const int row = min(tid >> 1, D - 1), half = tid & 1;
     const float4* hr = reinterpret_cast<const float4*>(p.rotk + ((size_t)h * D + row) * D + half * (D / 2));
 #pragma unroll
     for (int j = 0; j < RJ; ++j) {
       hu[j] = hr[2 * j];
       hw[j] = hr[2 * j + 1];
     }
+  };
+  if constexpr (MODE == kContig) {
+    load_rotation();
+    asm volatile("" ::: "memory");  // those loads are issued here, ahead of the ones below
   }
-  asm volatile("" ::: "memory");  // those loads are issued here, ahead of the ones below
 
   // A slot past the sequence's last used one streams nothing and stores no
   // partial; its workgroup still runs to the end (no return with loads in flight).
@@ -449,14 +457,21 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   const int32_t* table = MODE != kContig ? p.table + (size_t)b * p.maxblk : nullptr;
   constexpr int TAHEAD = DEPTH;
   int32_t tq[TAHEAD][2];                 // block ids for the next TAHEAD fetches, oldest first
+  // The ids are loaded unconditionally, from an index clamped into the
+  // sequence's table row, and replaced by -1 past the range: with no branch
+  // around the loads, the waits for them stay exact and do not also wait for
+  // loads issued after them.
+  const int last_tok = max(end - 1, 0);
   auto table_load = [&](int base, int32_t (&e)[2]) {
     if constexpr (MODE == kPagedTile) {  // one id per tile (the same in every lane)
-      e[0] = base < end ? table[base >> p.lbs] : -1;
+      const int32_t v = table[min(base, last_tok) >> p.lbs];
+      e[0] = base < end ? v : -1;
       e[1] = e[0];
     } else {
       const int t0 = base + pi, t1 = t0 + TPW;
-      e[0] = (lane_on && t0 < end) ? table[t0 >> p.lbs] : -1;
-      e[1] = (lane_on && t1 < end) ? table[t1 >> p.lbs] : -1;
+      const int32_t v0 = table[min(t0, last_tok) >> p.lbs], v1 = table[min(t1, last_tok) >> p.lbs];
+      e[0] = (lane_on && t0 < end) ? v0 : -1;
+      e[1] = (lane_on && t1 < end) ? v1 : -1;
     }
   };
   auto page_row = [&](int t, int32_t blk) -> uint32_t {
@@ -530,6 +545,9 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   if constexpr (MODE != kContig) {
 #pragma unroll
     for (int k = 0; k < TAHEAD; ++k) table_load(base + k * STRIDE, tq[k]);
+    asm volatile("" ::: "memory");
+    load_rotation();
+    asm volatile("" ::: "memory");
   }
   fetch(A, base);
   if constexpr (DEPTH == 3) fetch(B, base + STRIDE);
