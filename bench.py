@@ -151,7 +151,7 @@ def summarize_profile(directory, title, command):
     import re
 
     def short(name):
-        m = re.search(r"((?:decode_fused|decode_fused_paged|decode_fused_paged_tile|bf16_fused|combine_kernel|"
+        m = re.search(r"((?:decode_fused|decode_fused_paged|bf16_fused|combine_kernel|"
                       r"append_kernel|append_unit|prefill_attn_kernel|prefill_vt_kernel)<[^>]*>)", name)
         if m:
             return m.group(1)

@@ -19,7 +19,6 @@ SOURCES = {
     "rq_append.hip": ["-ffp-contract=off"],
     "rq_decode.hip": [],
     "rq_decode_paged.hip": [],
-    "rq_decode_paged_tile.hip": [],
     "rq_decode_bf16.hip": [],
     "rq_prefill.hip": [],
 }

@@ -356,9 +356,9 @@ constexpr int waves_for() {
   return (NC <= 2 && bits <= 6) ? RQ_WAVES_SMALL : 2;
 }
 
-// The paged instances keep block ids and row offsets (lane mode) or per-tile
-// descriptors (tile mode) live as well; with groups of 16 that no longer fits
-// three waves' registers without spilling.
+// The paged instances keep block ids and per-lane row offsets live as well;
+// with groups of 16 that no longer fits three waves' registers without
+// spilling.
 template <int NC, uint32_t CB>
 constexpr int waves_for_paged() {
   return any_g16<CB, NC>() ? 2 : waves_for<NC, CB>();
@@ -369,10 +369,12 @@ constexpr int waves_for_paged() {
 //   kPagedLane: rows through the block table (token t of sequence b lives in row
 //     (blk H + h) BS + t mod BS of the pool, blk = table[b][t / BS]), looked up
 //     per lane; descriptors cover the pool. Any block size.
-//   kPagedTile: block size a multiple of the wave tile, so a tile lies in one
-//     block: one block id per tile, and per-tile descriptors that cover exactly
-//     the tile's valid rows (no per-lane address arithmetic).
-enum : int { kContig = 0, kPagedLane = 1, kPagedTile = 2 };
+// (A mode with one block id per tile and per-tile descriptors covering exactly
+// the tile's rows, for block sizes that are multiples of the tile, measured no
+// faster for one plan and 5-9 % slower for the others: its descriptors took
+// more scalar registers than a wave has, and the overflow went through vector
+// registers.)
+enum : int { kContig = 0, kPagedLane = 1 };
 
 // One (b, h, slot) work item: stream the slot's tokens of the compressed
 // cache and store the slot's partial.
@@ -463,16 +465,10 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   // loads issued after them.
   const int last_tok = max(end - 1, 0);
   auto table_load = [&](int base, int32_t (&e)[2]) {
-    if constexpr (MODE == kPagedTile) {  // one id per tile (the same in every lane)
-      const int32_t v = table[min(base, last_tok) >> p.lbs];
-      e[0] = base < end ? v : -1;
-      e[1] = e[0];
-    } else {
-      const int t0 = base + pi, t1 = t0 + TPW;
-      const int32_t v0 = table[min(t0, last_tok) >> p.lbs], v1 = table[min(t1, last_tok) >> p.lbs];
-      e[0] = (lane_on && t0 < end) ? v0 : -1;
-      e[1] = (lane_on && t1 < end) ? v1 : -1;
-    }
+    const int t0 = base + pi, t1 = t0 + TPW;
+    const int32_t v0 = table[min(t0, last_tok) >> p.lbs], v1 = table[min(t1, last_tok) >> p.lbs];
+    e[0] = (lane_on && t0 < end) ? v0 : -1;
+    e[1] = (lane_on && t1 < end) ? v1 : -1;
   };
   auto page_row = [&](int t, int32_t blk) -> uint32_t {
     if (!lane_on || t >= end) return p.pool_rows;
@@ -484,29 +480,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   };
   auto fetch = [&](Tile<D, NC, CB>& T, int base) {
     Offs o;
-    if constexpr (MODE == kPagedTile) {
-      const int32_t blk = __builtin_amdgcn_readfirstlane(tq[0][0]);
-#pragma unroll
-      for (int k = 0; k + 1 < TAHEAD; ++k) tq[k][0] = tq[k + 1][0];
-      table_load(base + TAHEAD * STRIDE, tq[TAHEAD - 1]);
-      const int nvalid = max(0, min(end - base, TILE));
-      const bool good = (uint32_t)blk < (uint32_t)p.num_blocks;
-      if (!good && nvalid > 0 && lane == 0 && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_BLOCK);
-      const size_t rb = good ? (((size_t)blk * p.H + h) << p.lbs) + (size_t)(base & ((1 << p.lbs) - 1)) : 0;
-      const uint32_t nt = good ? (uint32_t)nvalid : 0u;
-      CompRsrc RT[NC];
-      RT[0] = comp_rsrc<D, ckind<CB, 0>()>(p, 0, rb, nt);
-      if constexpr (NC > 1) RT[1] = comp_rsrc<D, ckind<CB, (NC > 1 ? 1 : 0)>()>(p, 1, rb, nt);
-      if constexpr (NC > 2) RT[2] = comp_rsrc<D, ckind<CB, (NC > 2 ? 2 : 0)>()>(p, 2, rb, nt);
-      if constexpr (NC > 3) RT[3] = comp_rsrc<D, ckind<CB, (NC > 3 ? 3 : 0)>()>(p, 3, rb, nt);
-      const uint32_t rel = (uint32_t)pi;  // row of token t0 in the tile
-      o.c4 = rel * (D / 2) + gsel * 16;
-      o.c2 = rel * (D / 4) + gsel * 8;
-      o.m = (rel * G + gsel) * 4;
-      o.a = rel * 2;
-      load_tile<D, NC, CB, false>(T, RT, o);
-      return;
-    } else if constexpr (MODE == kPagedLane) {
+    if constexpr (MODE == kPagedLane) {
       const int32_t b0 = tq[0][0], b1 = tq[0][1];
 #pragma unroll
       for (int k = 0; k + 1 < TAHEAD; ++k) {
@@ -817,11 +791,6 @@ decode_fused_paged(DecodeParams p) {
   decode_body<D, NC, CB, DEPTH, kPagedLane>(p);
 }
 
-template <int D, int NC, uint32_t CB, int DEPTH>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_for_paged<NC, CB>()))) void
-decode_fused_paged_tile(DecodeParams p) {
-  decode_body<D, NC, CB, DEPTH, kPagedTile>(p);
-}
 
 // ---------------------------------------------------------------- plan tables
 typedef void (*MainFn)(DecodeParams);
@@ -836,15 +805,12 @@ struct PlanEntry {
 #endif
 // Plans with kernels: one nibble per component, anchor first (0xA = INT2 in
 // groups of 16). RQ_E(D, NC, CB) names the instance a table entry takes.
-// RQ_PLANS_UP3: one to three components; RQ_PLANS_4: four (chained loops).
-#define RQ_PLANS_UP3(D)                                                                                    \
+#define RQ_PLANS(D)                                                                                        \
   RQ_E(D, 1, 0x2), RQ_E(D, 1, 0x4), RQ_E(D, 2, 0x22), RQ_E(D, 2, 0x24), RQ_E(D, 2, 0x42), RQ_E(D, 2, 0x44), \
-      RQ_E(D, 3, 0x244), RQ_E(D, 3, 0x224), RQ_E(D, 3, 0x222), RQ_E(D, 3, 0x444), RQ_E(D, 1, 0xA),          \
-      RQ_E(D, 2, 0xAA), RQ_E(D, 2, 0xA4), RQ_E(D, 3, 0xAA4), RQ_E(D, 3, 0xAAA)
-#define RQ_PLANS_4(D)                                                                                     \
-  RQ_E(D, 4, 0x2244), RQ_E(D, 4, 0x2224), RQ_E(D, 4, 0x2222), RQ_E(D, 4, 0x4444), RQ_E(D, 4, 0xAAA4),     \
-      RQ_E(D, 4, 0xAAAA)
-#define RQ_PLANS(D) RQ_PLANS_UP3(D), RQ_PLANS_4(D)
+      RQ_E(D, 3, 0x244), RQ_E(D, 3, 0x224), RQ_E(D, 3, 0x222), RQ_E(D, 3, 0x444), RQ_E(D, 4, 0x2244),        \
+      RQ_E(D, 4, 0x2224), RQ_E(D, 4, 0x2222), RQ_E(D, 4, 0x4444),                                           \
+      RQ_E(D, 1, 0xA), RQ_E(D, 2, 0xAA), RQ_E(D, 2, 0xA4), RQ_E(D, 3, 0xAA4), RQ_E(D, 4, 0xAAA4),          \
+      RQ_E(D, 3, 0xAAA), RQ_E(D, 4, 0xAAAA)
 
 template <size_t N>
 const PlanEntry* find_plan(const PlanEntry (&table)[N], int D, int nc, const int* kinds) {

@@ -1,8 +1,7 @@
-// Decode launches of librq over a paged cache whose block size is not a
-// multiple of the wave tile, or whose plan has four components: the streaming
-// kernel instances that find each token's row through a block table, lane by
-// lane (rq.h: token t of sequence b lives in row (table[b][t / BS] H + h) BS +
-// t mod BS of every buffer's block pool). The kernel is the one of
+// Decode launches of librq over a paged cache: the streaming kernel instances
+// that find each token's row through a block table, lane by lane (rq.h: token t
+// of sequence b lives in row (table[b][t / BS] H + h) BS + t mod BS of every
+// buffer's block pool), for any block size. The kernel is the one of
 // rq_decode_kernel.hpp; the combine launch is shared with the contiguous cache.
 #include "rq_decode_kernel.hpp"
 
@@ -16,7 +15,6 @@ const PlanEntry kPagedTable[] = {RQ_PLANS(64), RQ_PLANS(96), RQ_PLANS(128)};
 }  // namespace
 
 int launch_decode_paged(const DecodeParams& p, int D, int nc, const int* bits, int nsplit, void* stream) {
-  if ((1 << p.lbs) % tile_tokens(D) == 0 && nc <= 3) return launch_decode_paged_tile(p, D, nc, bits, nsplit, stream);
   const PlanEntry* e = find_plan(kPagedTable, D, nc, bits);
   if (!e) return -1;
   const dim3 grid((unsigned)(nsplit * p.B * p.H));

@@ -129,7 +129,6 @@ int launch_append(const AppendParams& p, int D, void* stream);
 // ncomp components with bit widths bits[0..ncomp-1]; returns -1 if no kernel exists.
 int launch_decode(const DecodeParams& p, int D, int ncomp, const int* bits, int nsplit, void* stream);
 int launch_decode_paged(const DecodeParams& p, int D, int ncomp, const int* bits, int nsplit, void* stream);
-int launch_decode_paged_tile(const DecodeParams& p, int D, int ncomp, const int* bits, int nsplit, void* stream);
 int launch_bf16(const Bf16Params& p, int D, int nsplit, void* stream);
 int launch_combine(const CombineParams& p, int D, int B, void* stream);
 int launch_prefill(const PrefillParams& p, int D, void* stream);
