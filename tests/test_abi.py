@@ -290,6 +290,35 @@ def test_prefill_validation():
     assert L.rq_prefill_attn(by(_desc(head_dim=80)), FAKE, FAKE, FAKE, FAKE, 8, f, FAKE, FAKE, ws, None, 0) == 2
 
 
+@pytest.mark.parametrize("B,H,D,T,expect", [
+    (2, 3, 128, 100, 1),          # shorter than 8 tiles: one slot
+    (1, 16, 128, 4160, 16),       # 4160 // (32 * 8): capped below the 48 slots three per CU would give
+    (8, 16, 128, 16448, 6),       # ceil(3 * 256 / 128): the 16k benchmark shape
+    (4, 55, 96, 4160, 4),         # ceil(3 * 256 / 220), under the cap 4160 // (42 * 8) = 12
+    (128, 16, 128, 8256, 1),      # more series than workgroup slots
+])
+def test_split_plan_rule(B, H, D, T, expect):
+    """Split plan: about three workgroups per compute unit (256 CUs here, the
+    count the library assumes without a device), but every slot at least 8
+    tiles of the capacity."""
+    d = rq.make_desc(B, H, D, [2, 2, 4, 4], T)
+    unit, nsplit = rq.split_plan(d)
+    assert unit == 2 * 64 // (D // 32)
+    if rq_cus() == 256:
+        assert nsplit == expect
+    assert 1 <= nsplit <= max(1, T // (unit * 8))
+
+
+def rq_cus():
+    try:
+        import torch
+        if torch.cuda.is_available():
+            return torch.cuda.get_device_properties(0).multi_processor_count
+    except Exception:
+        pass
+    return 256
+
+
 def test_split_api_validation():
     L = rq.lib
     d = _desc()
