@@ -190,7 +190,37 @@ class LayerCache:
         table = None if not d.block_size else block_table.to(device).contiguous()
         return LayerCache(d, codes, meta, alpha, rot, table)
 
+    def validate(self):
+        """Every buffer's size, dtype and layout against the descriptor (once)."""
+        if getattr(self, "_valid", False):
+            return
+        d = self.desc
+        if check_desc(d) != OK:
+            raise ValueError(f"cache descriptor invalid (status {check_desc(d)})")
+        for kv in range(2):
+            for r in range(d.loops):
+                for kind, t, dt, name in ((0, self.codes[kv][r], torch.uint8, "codes"),
+                                          (1, self.meta[kv][r], torch.int16, "meta"),
+                                          (2, self.alpha[kv][r], torch.int16, "alpha")):
+                    want = buffer_bytes(d, kind, r)
+                    if kind == 2 and r == anchor_of(d, r):
+                        continue
+                    _need(t, None, dt, f"cache {name}[{kv}][{r}]")
+                    if t.numel() * t.element_size() != want:
+                        raise ValueError(f"cache {name}[{kv}][{r}]: {t.numel() * t.element_size()} bytes, "
+                                         f"the descriptor needs {want}")
+            _need(self.rot[kv], (d.heads, d.head_dim, d.head_dim), torch.float32, f"cache rot[{kv}]")
+        if d.block_size:
+            _need(self.block_table, (d.batch, d.max_tokens // d.block_size), torch.int32, "block_table")
+        bufs = {f"cache codes[{kv}][{r}]": self.codes[kv][r] for kv in range(2) for r in range(d.loops)}
+        bufs.update({f"cache meta[{kv}][{r}]": self.meta[kv][r] for kv in range(2) for r in range(d.loops)})
+        bufs.update({f"cache alpha[{kv}][{r}]": self.alpha[kv][r] for kv in range(2) for r in range(d.loops)})
+        bufs.update({"cache rot[0]": self.rot[0], "cache rot[1]": self.rot[1], "block_table": self.block_table})
+        _on_gpu(**bufs)
+        self._valid = True
+
     def c(self) -> LayerCacheC:
+        self.validate()
         c = LayerCacheC()
         for kv in range(2):
             for r in range(self.desc.loops):
@@ -211,6 +241,45 @@ class LayerCache:
         return n
 
 
+def _need(t, shape, dtype, what: str, optional: bool = False):
+    """The C ABI takes raw pointers and cannot see sizes: every tensor handed to
+    it is checked here, before the call, for its shape, dtype and layout (a wrong
+    size would make a kernel read or write past the tensor); _on_gpu then checks
+    the devices."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{what}: missing")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch.Tensor, got {type(t).__name__}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{what}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous")
+
+
+def _on_gpu(**tensors):
+    for what, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{what}: must be on a GPU device")
+
+
+def _need_err(dev_err):
+    if dev_err is not None:
+        _need(dev_err, None, torch.int32, "dev_err")
+        if dev_err.numel() < 1:
+            raise ValueError("dev_err: needs one int32")
+
+
+def _need_bytes(t, nbytes: int, what: str):
+    if not isinstance(t, torch.Tensor) or not t.is_contiguous():
+        raise ValueError(f"{what}: must be a contiguous tensor")
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{what}: {t.numel() * t.element_size()} bytes, needs {nbytes}")
+
+
 def _check(code: int, where: str):
     if code != OK:
         raise RQError(code, where)
@@ -219,6 +288,11 @@ def _check(code: int, where: str):
 def quantize_append(cache: LayerCache, kv: torch.Tensor, pos: torch.Tensor, n: int,
                     dev_err: torch.Tensor | None = None, stream=None):
     """kv: bf16 [2][L][B][H][n][D]; pos: int32 [B] on the device."""
+    d = cache.desc
+    _need(kv, (2, d.loops, d.batch, d.heads, n, d.head_dim), torch.bfloat16, "kv")
+    _need(pos, (d.batch,), torch.int32, "pos")
+    _need_err(dev_err)
+    _on_gpu(kv=kv, pos=pos, dev_err=dev_err)
     cc = cache.c()
     _check(lib.rq_quantize_append(ctypes.byref(cache.desc), ctypes.byref(cc), _ptr(kv), _ptr(pos), n,
                                   _ptr(dev_err), _stream(stream)), "rq_quantize_append")
@@ -238,16 +312,38 @@ def prefill_attn(d: Desc, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, len
     """Causal prefill attention of one loop: q, k, v bf16 [B][H][n][D]; lens int32 [B];
     out fp32 [B][H][n][D] (rows past lens[b] not written). The workspace is allocated
     here when not given."""
-    n = q.shape[2]
+    n = q.shape[2] if isinstance(q, torch.Tensor) and q.dim() == 4 else -1
+    shape = (d.batch, d.heads, n, d.head_dim)
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, shape, torch.bfloat16, name)
+    _need(lens, (d.batch,), torch.int32, "lens")
+    _need(out, shape, torch.float32, "out")
+    _need_err(dev_err)
     if workspace is None:
         workspace = alloc_prefill_workspace(d, n, q.device)
+    _need_bytes(workspace, prefill_workspace_bytes(d, n), "workspace")
+    _on_gpu(q=q, k=k, v=v, lens=lens, out=out, workspace=workspace, dev_err=dev_err)
     _check(lib.rq_prefill_attn(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(lens), n, scale, _ptr(out),
                                _ptr(workspace), workspace.numel(), _ptr(dev_err), _stream(stream)),
            "rq_prefill_attn")
 
 
+def _need_step(d: Desc, q, past_len, k_cur=None, v_cur=None, out=None, full=True):
+    bhd = (d.batch, d.heads, d.head_dim)
+    _need(q, bhd, torch.bfloat16, "q")
+    _need(past_len, (d.batch,), torch.int32, "past_len")
+    if full:
+        _need(k_cur, bhd, torch.bfloat16, "k_cur")
+        _need(v_cur, bhd, torch.bfloat16, "v_cur")
+        _need(out, bhd, torch.float32, "out")
+
+
 def decode_attn(cache: LayerCache, loop: int, q, k_cur, v_cur, past_len, scale: float, out, workspace,
                 dev_err=None, stream=None):
+    _need_step(cache.desc, q, past_len, k_cur, v_cur, out)
+    _need_err(dev_err)
+    _need_bytes(workspace, 1, "workspace")
+    _on_gpu(q=q, k_cur=k_cur, v_cur=v_cur, past_len=past_len, out=out, workspace=workspace, dev_err=dev_err)
     cc = cache.c()
     _check(lib.rq_decode_attn(ctypes.byref(cache.desc), ctypes.byref(cc), loop, _ptr(q), _ptr(k_cur),
                               _ptr(v_cur), _ptr(past_len), scale, _ptr(out), _ptr(workspace),
@@ -257,6 +353,9 @@ def decode_attn(cache: LayerCache, loop: int, q, k_cur, v_cur, past_len, scale: 
 
 def decode_attn_partial(cache: LayerCache, loop: int, q, past_len, scale: float, workspace, stream=None):
     """First launch of decode_attn: per-slot partials (m, l, -, -, acc[D]) into the workspace."""
+    _need_step(cache.desc, q, past_len, full=False)
+    _need_bytes(workspace, 1, "workspace")
+    _on_gpu(q=q, past_len=past_len, workspace=workspace)
     cc = cache.c()
     _check(lib.rq_decode_attn_partial(ctypes.byref(cache.desc), ctypes.byref(cc), loop, _ptr(q), _ptr(past_len),
                                       scale, _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -266,13 +365,31 @@ def decode_attn_partial(cache: LayerCache, loop: int, q, past_len, scale: float,
 def decode_combine(d: Desc, rot_v, q, k_cur, v_cur, past_len, scale: float, out, workspace, dev_err=None,
                    stream=None):
     """Second launch of decode_attn: merge the workspace partials with the current token."""
+    _need_step(d, q, past_len, k_cur, v_cur, out)
+    _need(rot_v, (d.heads, d.head_dim, d.head_dim), torch.float32, "rot_v", optional=True)
+    _need_err(dev_err)
+    _need_bytes(workspace, 1, "workspace")
+    _on_gpu(rot_v=rot_v, q=q, k_cur=k_cur, v_cur=v_cur, past_len=past_len, out=out, workspace=workspace,
+            dev_err=dev_err)
     _check(lib.rq_decode_combine(ctypes.byref(d), _ptr(rot_v), _ptr(q), _ptr(k_cur), _ptr(v_cur), _ptr(past_len),
                                  scale, _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                  _ptr(dev_err), _stream(stream)), "rq_decode_combine")
 
 
+def _need_bf16_cache(d: Desc, k_cache, v_cache):
+    shape = (d.batch, d.heads, d.max_tokens, d.head_dim)
+    _need(k_cache, shape, torch.bfloat16, "k_cache")
+    _need(v_cache, shape, torch.bfloat16, "v_cache")
+
+
 def decode_attn_bf16(d: Desc, k_cache, v_cache, q, k_cur, v_cur, past_len, scale: float, out, workspace,
                      dev_err=None, stream=None):
+    _need_bf16_cache(d, k_cache, v_cache)
+    _need_step(d, q, past_len, k_cur, v_cur, out)
+    _need_err(dev_err)
+    _need_bytes(workspace, 1, "workspace")
+    _on_gpu(k_cache=k_cache, v_cache=v_cache, q=q, k_cur=k_cur, v_cur=v_cur, past_len=past_len, out=out,
+            workspace=workspace, dev_err=dev_err)
     _check(lib.rq_decode_attn_bf16(ctypes.byref(d), _ptr(k_cache), _ptr(v_cache), _ptr(q), _ptr(k_cur),
                                    _ptr(v_cur), _ptr(past_len), scale, _ptr(out), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _ptr(dev_err),
@@ -281,6 +398,10 @@ def decode_attn_bf16(d: Desc, k_cache, v_cache, q, k_cur, v_cur, past_len, scale
 
 def decode_attn_bf16_partial(d: Desc, k_cache, v_cache, q, past_len, scale: float, workspace, stream=None):
     """First launch of decode_attn_bf16: per-slot partials into the workspace (original domain)."""
+    _need_bf16_cache(d, k_cache, v_cache)
+    _need_step(d, q, past_len, full=False)
+    _need_bytes(workspace, 1, "workspace")
+    _on_gpu(k_cache=k_cache, v_cache=v_cache, q=q, past_len=past_len, workspace=workspace)
     _check(lib.rq_decode_attn_bf16_partial(ctypes.byref(d), _ptr(k_cache), _ptr(v_cache), _ptr(q), _ptr(past_len),
                                            scale, _ptr(workspace), workspace.numel() * workspace.element_size(),
                                            _stream(stream)), "rq_decode_attn_bf16_partial")

@@ -13,6 +13,7 @@
 // and sum below is rounded on its own.
 #include <hip/hip_runtime.h>
 
+#include "rq_device.hpp"
 #include "rq_internal.hpp"
 
 namespace rq {
@@ -73,16 +74,61 @@ __device__ uint16_t f64_to_f16(double x, int mode) {
   return (uint16_t)(sign | (uint16_t)((EE + 15) << 10) | (uint16_t)(n - 1024));
 }
 
-__device__ __forceinline__ double shfl_xor_f64(double v, int m) {
+// Lane exchanges of the reductions below, in the vector unit (no LDS round
+// trip). Within a row of 16 lanes, DPP: the quad permutations give lane l ^ 1
+// and l ^ 2; after those, every lane of a quad holds the same value, so the
+// half-row mirror (lane i <- 7 - i) and the row mirror (i <- 15 - i) give the
+// value of lane l ^ 4 and then l ^ 8. Across rows, the gfx950 swaps of odd and
+// even 16-lane rows and of the two half-waves. A reduction therefore combines
+// exactly the pairs a xor butterfly combines, and its fp64 sums are the same.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int x) {
+  return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
   const long long b = __double_as_longlong(v);
-  const int lo = __shfl_xor((int)(b & 0xffffffff), m, 64);
-  const int hi = __shfl_xor((int)(b >> 32), m, 64);
+  const int lo = dpp_i32<CTRL>((int)(b & 0xffffffff)), hi = dpp_i32<CTRL>((int)(b >> 32));
   return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+// Sum over lanes l and l ^ 16 (W = 16) or l ^ 32 (W = 32).
+template <int W>
+__device__ __forceinline__ double swap_add_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = (int)(b & 0xffffffff), hi = (int)(b >> 32);
+  const auto l = W == 16 ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
+                         : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  const auto h = W == 16 ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                         : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  const double a = __longlong_as_double(((long long)h[0] << 32) | (unsigned int)l[0]);
+  const double c = __longlong_as_double(((long long)h[1] << 32) | (unsigned int)l[1]);
+  return a + c;                                   // own and partner value, in either order
+}
+
+// op over the 16 lanes of a row, the result in every lane of it.
+template <typename Op>
+__device__ __forceinline__ double row16_f64(double v, Op op) {
+  v = op(v, dpp_f64<kQuadSwap1>(v));
+  v = op(v, dpp_f64<kQuadSwap2>(v));
+  v = op(v, dpp_f64<kRowHalfMirror>(v));
+  return op(v, dpp_f64<kRowMirror>(v));
 }
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
-  for (int m = 1; m < 64; m <<= 1) v += shfl_xor_f64(v, m);
-  return v;
+  v = row16_f64(v, [](double a, double b) { return a + b; });
+  v = swap_add_f64<16>(v);
+  return swap_add_f64<32>(v);
+}
+
+// Bitwise or over the N consecutive lanes N i .. N i + N - 1 (N = 2, 4, 8, 16).
+template <int N>
+__device__ __forceinline__ uint32_t group_or(uint32_t x) {
+  int v = (int)x;
+  v |= dpp_i32<kQuadSwap1>(v);
+  if constexpr (N > 2) v |= dpp_i32<kQuadSwap2>(v);
+  if constexpr (N > 4) v |= dpp_i32<kRowHalfMirror>(v);
+  if constexpr (N > 8) v |= dpp_i32<kRowMirror>(v);
+  return (uint32_t)v;
 }
 
 // Quantize one row's pair of elements e0 = 32 gi + k, e1 = e0 + 16 (held by
@@ -115,12 +161,14 @@ __device__ void quantize_pair(double v0, double v1, int bits, bool g16, bool lan
     mn0 = mn1 = lane_on ? fmin(v0, v1) : 0.0;
     mx0 = mx1 = lane_on ? fmax(v0, v1) : 0.0;
   }
-  for (int m = 1; m < 16; m <<= 1) {            // the 16 lanes of one lane group
-    mn0 = fmin(mn0, shfl_xor_f64(mn0, m));
-    mx0 = fmax(mx0, shfl_xor_f64(mx0, m));
+  {                                             // the 16 lanes of one lane group
+    auto mn = [](double a, double b) { return fmin(a, b); };
+    auto mx = [](double a, double b) { return fmax(a, b); };
+    mn0 = row16_f64(mn0, mn);
+    mx0 = row16_f64(mx0, mx);
     if (g16) {
-      mn1 = fmin(mn1, shfl_xor_f64(mn1, m));
-      mx1 = fmax(mx1, shfl_xor_f64(mx1, m));
+      mn1 = row16_f64(mn1, mn);
+      mx1 = row16_f64(mx1, mx);
     }
   }
   if (!g16) {
@@ -150,10 +198,8 @@ __device__ void quantize_pair(double v0, double v1, int bits, bool g16, bool lan
     // one 32-bit word per group: element k at bit 16 (k / 8) + 2 (k mod 8)
     const int sh = 16 * (k >> 3) + 2 * (k & 7);
     uint32_t wa = c0 << sh, wb = c1 << sh;
-    for (int m = 1; m < 16; m <<= 1) {
-      wa |= (uint32_t)__shfl_xor((int)wa, m, 64);
-      wb |= (uint32_t)__shfl_xor((int)wb, m, 64);
-    }
+    wa = group_or<16>(wa);
+    wb = group_or<16>(wb);
     if (lane_on && k == 0) {
       *reinterpret_cast<uint2*>(row + gi * 8) = make_uint2(wa, wb);
       *reinterpret_cast<uint2*>(meta + tok * (D / 16) + 2 * gi) =
@@ -164,7 +210,7 @@ __device__ void quantize_pair(double v0, double v1, int bits, bool g16, bool lan
   const int per = 16 / bits;                    // codes per 16-bit half-word
   const int sh = bits * (k % per);
   uint32_t word = (c0 << sh) | (c1 << (16 + sh));
-  for (int m = 1; m < per; m <<= 1) word |= (uint32_t)__shfl_xor((int)word, m, 64);
+  word = per == 8 ? group_or<8>(word) : group_or<4>(word);
   if (lane_on) {
     if (k % per == 0) {
       uint32_t* dst = reinterpret_cast<uint32_t*>(row + gi * 4 * bits);

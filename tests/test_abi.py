@@ -362,3 +362,41 @@ def test_bf16_validation():
     assert L.rq_decode_attn_bf16_partial(by(d), FAKE, ctypes.c_void_p(0x100004), FAKE, FAKE, f, FAKE, ws, 0) == 10
     assert L.rq_decode_attn_bf16(by(d), ctypes.c_void_p(0x100008), FAKE, FAKE, FAKE, FAKE, FAKE,
                                  ctypes.c_float(0.1), FAKE, FAKE, ws, None, 0) == 10
+
+
+def test_binding_checks_tensors_before_the_call():
+    """The binding checks every tensor against the descriptor before calling the
+    library (raw pointers carry no sizes): a K/V input with too few loops, a wrong
+    dtype, a non-contiguous view or a host tensor is refused with an error."""
+    import torch
+    d = _desc(batch=2, heads=3, head_dim=64, bits=[2, 2, 2, 4], max_tokens=64)
+    rk = torch.eye(64).expand(3, 64, 64).contiguous()
+    c = rq.LayerCache.allocate(d, rk, rk, device="cpu")
+    pos = torch.zeros(2, dtype=torch.int32)
+    good = torch.zeros(2, 4, 2, 3, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="kv: expected shape"):
+        rq.quantize_append(c, torch.zeros(2, 2, 2, 3, 1, 64, dtype=torch.bfloat16), pos, 1)   # 2 loops, not 4
+    with pytest.raises(ValueError, match="kv: expected torch.bfloat16"):
+        rq.quantize_append(c, good.float(), pos, 1)
+    with pytest.raises(ValueError, match="kv: must be contiguous"):
+        rq.quantize_append(c, torch.zeros(2, 4, 2, 3, 1, 128, dtype=torch.bfloat16)[..., ::2], pos, 1)
+    with pytest.raises(ValueError, match="pos: expected torch.int32"):
+        rq.quantize_append(c, good, pos.long(), 1)
+    with pytest.raises(ValueError, match="must be on a GPU device"):
+        rq.quantize_append(c, good, pos, 1)
+    q = torch.zeros(2, 3, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="out: expected shape"):
+        rq.decode_attn(c, 0, q, q, q, pos, 0.1, torch.zeros(2, 3, 32), torch.zeros(256, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="k_cache: expected shape"):
+        rq.decode_attn_bf16(d, torch.zeros(2, 3, 63, 64, dtype=torch.bfloat16), None, q, q, q, pos, 0.1,
+                            torch.zeros(2, 3, 64), torch.zeros(256, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="v: expected shape"):
+        rq.prefill_attn(d, torch.zeros(2, 3, 8, 64, dtype=torch.bfloat16), torch.zeros(2, 3, 8, 64, dtype=torch.bfloat16),
+                        torch.zeros(2, 3, 9, 64, dtype=torch.bfloat16), torch.zeros(2, dtype=torch.int32), 0.1,
+                        torch.zeros(2, 3, 8, 64))
+    bad = rq.LayerCache.allocate(d, rk, rk, device="cpu")
+    bad.codes[0][1] = torch.zeros(5, dtype=torch.uint8)
+    with pytest.raises(ValueError, match=r"cache codes\[0\]\[1\]: 5 bytes"):
+        bad.validate()
+    with pytest.raises(ValueError, match=r"cache codes\[0\]\[0\]: must be on a GPU device"):
+        c.validate()
