@@ -180,3 +180,16 @@ def test_ouro_16k_bf16_sampled():
             worst = max(worst, err)
             assert err <= TOL_ATTN
     log(f"16k bf16: max rel err {worst:.3e}")
+
+
+def test_long_context_many_slots():
+    """One sequence of 65536 cached tokens over two heads (D128, plan [2,2,4,4]): the
+    split plan gives 256 slots of 8 tiles per (b, h), so every launch streams short
+    slots and the combine merges 256 partials in sixteen rounds of loads. Both
+    series, the whole cache and every loop's output at the first and last step."""
+    w = W.with_(batch=1, heads=2, T=65536, layers=1)
+    d = rq.make_desc(w.batch, w.heads, w.D, list(w.bits), w.T + STEPS)
+    unit, nsplit = rq.split_plan(d)
+    log(f"64k B1 H2: {nsplit} slots of {rq.slot_len(w.T, nsplit, unit)} tokens")
+    assert nsplit >= 64
+    _check(0, LAST, w.bits, [(0, 0), (0, 1)], "64k B1 H2", w)
