@@ -8,12 +8,6 @@
 
 namespace rq {
 
-typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-
-// v_dot2c_f32_f16: c + a.lo * b.lo + a.hi * b.hi (fp16 inputs, fp32 accumulate).
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, a), __builtin_bit_cast(h2_t, b), c, false);
-}
 __device__ __forceinline__ float f16lo(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
 }
@@ -22,10 +16,6 @@ __device__ __forceinline__ float f16u(uint16_t h) { return (float)__builtin_bit_
 __device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
-  h2_t v = {(_Float16)a, (_Float16)b};
-  return __builtin_bit_cast(uint32_t, v);
-}
 
 // DPP lane moves (gfx9 data-parallel primitives) on float values.
 enum : int {

@@ -15,8 +15,8 @@ constexpr int kWaves = 4;            // waves per decode workgroup
 constexpr int kThreads = 64 * kWaves;
 
 // Token-pair tile of one wave: G = D/32 lanes cover one token's groups, and a
-// lane holds two tokens (t, t + TPW) so that value codes pair up for the
-// fp16 dot-2 instruction.
+// lane holds two tokens (t, t + TPW), whose value codes a byte permute pairs in
+// one register.
 constexpr int groups_of(int D) { return D / 32; }
 constexpr int pairs_per_wave(int D) { return 64 / groups_of(D); }
 constexpr int tile_tokens(int D) { return 2 * pairs_per_wave(D); }
