@@ -68,6 +68,13 @@ def test_prefill_ragged(D):
     _run(w, 300, [300, 128, 65, 1, 0], f"prefill D{D}")
 
 
+def test_prefill_ragged_grouped_order():
+    """B8 H2 (B H a multiple of 8): workgroups take the XCD-grouped order, series by
+    series; ragged lengths, including empty and one-token sequences."""
+    w = synth.WORKLOADS["tiny"].with_(batch=8, heads=2, D=128, outliers=4)
+    _run(w, 300, [300, 0, 1, 65, 128, 299, 200, 17], "prefill grouped order")
+
+
 def test_prefill_long_rows():
     w = synth.WORKLOADS["tiny"].with_(batch=1, heads=2, D=128, outliers=4)
     _run(w, 1500, [1500], "prefill 1500")
