@@ -6,9 +6,10 @@ batch 8, 16 MHA heads, head_dim 128, 4 loops, 16384 cached tokens, INT2/4
 plan [2,2,4,4] (loops 1-2 INT2 residuals, loop 3 INT4 residual, INT4 anchor),
 group 32, synthetic seeded inputs (synth/). One step = one decoded token per
 sequence: for each loop r and layer l, rq_decode_attn over the compressed
-cache with the current token's bf16 K/V; after the final loop, each layer's
-rq_quantize_append of the current token (all loops) at position past_len; then
-past_len += 1 on the device. Each step is one captured hipGraph.
+cache with the current token's bf16 K/V; after the final loop, one
+rq_quantize_append_layers call stores the current token (all loops) of every
+layer at position past_len; then past_len += 1 on the device. Each step is one
+captured hipGraph.
 
 Reported next to it, in the same process and on the same logical inputs:
   * the BF16 decode baseline (rq_decode_attn_bf16 over the uncompressed cache);
@@ -261,6 +262,10 @@ def main():
     d_ch = rq.make_desc(B, H, D, cbits, T_max, rq.POLICY_PREV_LOOP, group=cgr, loop_group=G, block_size=BS,
                         num_blocks=nblocks)
     caches, chained, bf16, rots = [], [], [], []
+    # the BF16 caches of all layers in one tensor, so that one index copy stores a
+    # step's current K/V of every layer
+    bf16_all = None if args.no_bf16 else torch.empty(w.layers, 2, L, B, H, T_max, D, dtype=torch.bfloat16,
+                                                     device=dev)
     kvcur = torch.empty(K, w.layers, 2, L, B, H, 1, D, dtype=torch.bfloat16, device=dev)
     qs = torch.empty(K, w.layers, L, B, H, D, dtype=torch.bfloat16, device=dev)
     pos0 = torch.zeros(B, dtype=torch.int32, device=dev)
@@ -280,10 +285,10 @@ def main():
             kvcur[k, l] = X[..., T + k:T + k + 1, :]
             for r in range(L):
                 qs[k, l, r] = synth.query(w, l, r, k, device=dev)
-        if args.no_bf16:
-            del X
-        else:
-            bf16.append(X)
+        if not args.no_bf16:
+            bf16_all[l].copy_(X)
+            bf16.append(bf16_all[l])
+        del X
         torch.cuda.synchronize()
         if l % 6 == 5 or l == w.layers - 1:
             log(f"built layer {l + 1}/{w.layers} ({time.time() - t_build:.1f}s)")
@@ -298,22 +303,22 @@ def main():
     # ---------------------------------------------------------------- steps as graphs
     # One step, in the order a looped decoder runs it: for each loop r and layer
     # l, the attention call (streaming launch + combine) that the next layer's
-    # query would depend on; after the final loop, each layer's append of the
-    # current token; then past_len += 1. All on one stream.
+    # query would depend on; after the final loop, the append of the current
+    # token to every layer's cache (one call, shared launches); then
+    # past_len += 1. All on one stream.
     def rq_step(k, cs, d, workspace):
         for r in range(L):
             for l in range(w.layers):
                 kc = kvcur[k, l, 0, r, :, :, 0]
                 vc = kvcur[k, l, 1, r, :, :, 0]
                 rq.decode_attn(cs[l], r, qs[k, l, r], kc, vc, past_len, scale, out[l, r], workspace)
-                if r == L - 1:
-                    rq.quantize_append(cs[l], kvcur[k, l], past_len, 1)
+        rq.quantize_append_layers(cs, kvcur[k], past_len, 1)
         past_len.add_(1)
 
     # The BF16 comparator's step pays for its cache store as the RQ step pays for
-    # its append: after the final loop, each layer's current K/V of every loop is
-    # written at position past_len (a torch index copy; same values as the
-    # prefilled rows, so the attention reads are unchanged).
+    # its append: after the final loop, every layer's current K/V of every loop is
+    # written at position past_len (one torch index copy over all layers; same
+    # values as the prefilled rows, so the attention reads are unchanged).
     bf16_pos = torch.empty(1, dtype=torch.long, device=dev)
 
     def bf16_step(k):
@@ -324,8 +329,7 @@ def main():
                 vc = kvcur[k, l, 1, r, :, :, 0]
                 rq.decode_attn_bf16(d_rq, bf16[l][0, r], bf16[l][1, r], qs[k, l, r], kc, vc, past_len, scale,
                                     out[l, r], ws)
-                if r == L - 1:
-                    bf16[l].index_copy_(4, bf16_pos, kvcur[k, l])
+        bf16_all.index_copy_(5, bf16_pos, kvcur[k])
         past_len.add_(1)
 
     side = torch.cuda.Stream()
@@ -466,7 +470,7 @@ def main():
     # (query, visible key) for the scores and 2 D for the value sum, T (T + 1) / 2
     # visible pairs per (b, h) under the causal mask.
     if not args.no_prefill:
-        del caches, chained, bf16
+        del caches, chained, bf16, bf16_all
         torch.cuda.empty_cache()
         g = torch.Generator(device=dev).manual_seed(7)
         pq = torch.randn(B, H, T, D, generator=g, device=dev).to(torch.bfloat16)

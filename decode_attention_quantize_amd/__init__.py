@@ -61,6 +61,8 @@ def _load():
     L.rq_check_desc.argtypes = [P]
     L.rq_quantize_append.restype = ctypes.c_int
     L.rq_quantize_append.argtypes = [P, P, P, P, I, P, P]
+    L.rq_quantize_append_layers.restype = ctypes.c_int
+    L.rq_quantize_append_layers.argtypes = [P, P, I, P, P, I, P, P]
     L.rq_decode_attn.restype = ctypes.c_int
     L.rq_decode_attn.argtypes = [P, P, I, P, P, P, P, ctypes.c_float, P, P, Z, P, P]
     L.rq_split_plan.restype = ctypes.c_int
@@ -296,6 +298,25 @@ def quantize_append(cache: LayerCache, kv: torch.Tensor, pos: torch.Tensor, n: i
     cc = cache.c()
     _check(lib.rq_quantize_append(ctypes.byref(cache.desc), ctypes.byref(cc), _ptr(kv), _ptr(pos), n,
                                   _ptr(dev_err), _stream(stream)), "rq_quantize_append")
+
+
+def quantize_append_layers(caches: list, kv: torch.Tensor, pos: torch.Tensor, n: int,
+                           dev_err: torch.Tensor | None = None, stream=None):
+    """quantize_append for several layers in one call (the layers share launches):
+    kv bf16 [nlayers][2][L][B][H][n][D], layer l's input at kv[l]; pos int32 [B]."""
+    if len(caches) == 0:
+        return
+    d = caches[0].desc
+    for l, c in enumerate(caches):
+        if bytes(c.desc) != bytes(d):
+            raise ValueError(f"caches[{l}]: descriptor differs from caches[0]")
+    _need(kv, (len(caches), 2, d.loops, d.batch, d.heads, n, d.head_dim), torch.bfloat16, "kv")
+    _need(pos, (d.batch,), torch.int32, "pos")
+    _need_err(dev_err)
+    _on_gpu(kv=kv, pos=pos, dev_err=dev_err)
+    arr = (LayerCacheC * len(caches))(*[c.c() for c in caches])
+    _check(lib.rq_quantize_append_layers(ctypes.byref(d), arr, len(caches), _ptr(kv), _ptr(pos), n,
+                                         _ptr(dev_err), _stream(stream)), "rq_quantize_append_layers")
 
 
 def prefill_workspace_bytes(d: Desc, n: int) -> int:

@@ -189,18 +189,14 @@ size_t rq_workspace_bytes(const rq_desc* d) {
   return workspace_for(d);
 }
 
-rq_status rq_quantize_append(const rq_desc* d, const rq_layer_cache* c, const uint16_t* kv,
-                             const int32_t* pos, int32_t n, int32_t* dev_err, void* stream) {
-  rq_status s = check_plan(d);
-  if (s != RQ_OK) return s;
-  if (!c) return RQ_E_NULL;
-  if (n < 0) return RQ_E_SHAPE;
-  if (n > d->max_tokens) return RQ_E_CAPACITY;
-  if (n == 0) return RQ_OK;
-  if (!kv || !pos || !c->rot[0] || !c->rot[1]) return RQ_E_NULL;
-  if (!al(kv, 16) || !al(pos, 4) || !al(c->rot[0], 16) || !al(c->rot[1], 16)) return RQ_E_ALIGN;
-  AppendParams p;
-  std::memset(&p, 0, sizeof(p));
+}  // extern "C"
+
+namespace {
+
+// Pointer and alignment checks of one layer's cache for an append.
+rq_status check_append_cache(const rq_desc* d, const rq_layer_cache* c) {
+  if (!c->rot[0] || !c->rot[1]) return RQ_E_NULL;
+  if (!al(c->rot[0], 16) || !al(c->rot[1], 16)) return RQ_E_ALIGN;
   for (int kvi = 0; kvi < 2; ++kvi) {
     for (int r = 0; r < d->loops; ++r) {
       if (!c->codes[kvi][r] || !c->meta[kvi][r]) return RQ_E_NULL;
@@ -209,35 +205,127 @@ rq_status rq_quantize_append(const rq_desc* d, const rq_layer_cache* c, const ui
       const uintptr_t ma = d->group[r] == 16 ? 8 : 4;
       if (!al(c->codes[kvi][r], 16) || !al(c->meta[kvi][r], ma) || (!anchor && !al(c->alpha[kvi][r], 2)))
         return RQ_E_ALIGN;
-      p.codes[kvi][r] = c->codes[kvi][r];
-      p.meta[kvi][r] = reinterpret_cast<uint32_t*>(c->meta[kvi][r]);
-      p.alpha[kvi][r] = c->alpha[kvi][r];
     }
-    p.rot[kvi] = c->rot[kvi];
   }
-  p.kv = kv;
-  p.pos = pos;
-  p.dev_err = dev_err;
-  p.B = d->batch;
-  p.H = d->heads;
-  p.L = d->loops;
-  p.n = n;
-  p.T_max = d->max_tokens;
-  p.policy = d->policy;
-  p.G = group_len(d);
   if (d->block_size) {
     if (!c->block_table) return RQ_E_NULL;
     if (!al(c->block_table, 4)) return RQ_E_ALIGN;
-    p.table = c->block_table;
-    p.maxblk = d->max_tokens / d->block_size;
-    p.lbs = log2_of(d->block_size);
+  }
+  return RQ_OK;
+}
+
+// Appends n tokens to nl layers (caches[0..nl-1]); kv holds the layers' inputs
+// back to back. Every check runs before the first launch.
+rq_status append_layers(const rq_desc* d, const rq_layer_cache* caches, int32_t nl, const uint16_t* kv,
+                        const int32_t* pos, int32_t n, int32_t* dev_err, void* stream) {
+  rq_status s = check_plan(d);
+  if (s != RQ_OK) return s;
+  if (!caches) return RQ_E_NULL;
+  if (n < 0 || nl < 0) return RQ_E_SHAPE;
+  if (n > d->max_tokens) return RQ_E_CAPACITY;
+  if (n == 0 || nl == 0) return RQ_OK;
+  if (!kv || !pos) return RQ_E_NULL;
+  if (!al(kv, 16) || !al(pos, 4)) return RQ_E_ALIGN;
+  for (int l = 0; l < nl; ++l)
+    if ((s = check_append_cache(d, &caches[l])) != RQ_OK) return s;
+  const size_t layer_elems = (size_t)2 * d->loops * d->batch * d->heads * n * d->head_dim;
+  const int lbs = d->block_size ? log2_of(d->block_size) : 0;
+  const int maxblk = d->block_size ? d->max_tokens / d->block_size : 0;
+  uint32_t g16 = 0;
+  for (int r = 0; r < d->loops; ++r)
+    if (d->group[r] == 16) g16 |= 1u << r;
+
+  if (n <= kUnitAppendMax || d->loops > 16) {
+    // per-unit kernel, as many layers per launch as the argument slots hold
+    UnitParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.pos = pos;
+    p.dev_err = dev_err;
+    p.B = d->batch;
+    p.H = d->heads;
+    p.L = d->loops;
+    p.n = n;
+    p.T_max = d->max_tokens;
+    p.policy = d->policy;
+    p.G = group_len(d);
+    p.g16 = g16;
+    p.maxblk = maxblk;
+    p.lbs = lbs;
     p.num_blocks = d->num_blocks;
+    for (int r = 0; r < d->loops; ++r) p.bits[r] = d->bits[r];
+    const int stride = unit_stride(d->loops);
+    const int per = kUnitSlots / stride;
+    for (int l0 = 0; l0 < nl; l0 += per) {
+      p.nl = nl - l0 < per ? nl - l0 : per;
+      p.kv = kv + (size_t)l0 * layer_elems;
+      for (int i = 0; i < p.nl; ++i) {
+        const rq_layer_cache* c = &caches[l0 + i];
+        const void** sl = p.slot + (size_t)i * stride;
+        sl[0] = d->block_size ? c->block_table : nullptr;
+        for (int kvi = 0; kvi < 2; ++kvi) {
+          const void** st = sl + 1 + kvi * (1 + 3 * d->loops);
+          st[0] = c->rot[kvi];
+          for (int r = 0; r < d->loops; ++r) {
+            st[1 + r] = c->codes[kvi][r];
+            st[1 + d->loops + r] = c->meta[kvi][r];
+            st[1 + 2 * d->loops + r] = c->alpha[kvi][r];
+          }
+        }
+      }
+      if (launch_append_unit(p, d->head_dim, stream) != 0) return RQ_E_HIP;
+    }
+    return RQ_OK;
   }
-  for (int r = 0; r < d->loops; ++r) {
-    p.bits[r] = d->bits[r];
-    if (d->group[r] == 16) p.g16 |= 1u << r;
+
+  // bulk kernel (fp64 matrix cores), one launch per layer
+  for (int l = 0; l < nl; ++l) {
+    const rq_layer_cache* c = &caches[l];
+    AppendParams p;
+    std::memset(&p, 0, sizeof(p));
+    for (int kvi = 0; kvi < 2; ++kvi) {
+      for (int r = 0; r < d->loops; ++r) {
+        p.codes[kvi][r] = c->codes[kvi][r];
+        p.meta[kvi][r] = reinterpret_cast<uint32_t*>(c->meta[kvi][r]);
+        p.alpha[kvi][r] = c->alpha[kvi][r];
+      }
+      p.rot[kvi] = c->rot[kvi];
+    }
+    p.kv = kv + (size_t)l * layer_elems;
+    p.pos = pos;
+    p.dev_err = dev_err;
+    p.B = d->batch;
+    p.H = d->heads;
+    p.L = d->loops;
+    p.n = n;
+    p.T_max = d->max_tokens;
+    p.policy = d->policy;
+    p.G = group_len(d);
+    p.g16 = g16;
+    if (d->block_size) {
+      p.table = c->block_table;
+      p.maxblk = maxblk;
+      p.lbs = lbs;
+      p.num_blocks = d->num_blocks;
+    }
+    for (int r = 0; r < d->loops; ++r) p.bits[r] = d->bits[r];
+    if (launch_append(p, d->head_dim, stream) != 0) return RQ_E_HIP;
   }
-  return launch_append(p, d->head_dim, stream) == 0 ? RQ_OK : RQ_E_HIP;
+  return RQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rq_status rq_quantize_append(const rq_desc* d, const rq_layer_cache* c, const uint16_t* kv,
+                             const int32_t* pos, int32_t n, int32_t* dev_err, void* stream) {
+  return append_layers(d, c, 1, kv, pos, n, dev_err, stream);
+}
+
+rq_status rq_quantize_append_layers(const rq_desc* d, const rq_layer_cache* caches, int32_t nlayers,
+                                    const uint16_t* kv, const int32_t* pos, int32_t n, int32_t* dev_err,
+                                    void* stream) {
+  return append_layers(d, caches, nlayers, kv, pos, n, dev_err, stream);
 }
 
 rq_status rq_split_plan(const rq_desc* d, int32_t* unit, int32_t* nsplit) {

@@ -19,10 +19,6 @@
 namespace rq {
 namespace {
 
-// Appends of at most this many tokens per sequence take the per-unit path (as
-// do all appends with more than 16 loops, whose units do not fit a 16-row tile).
-constexpr int kUnitAppendMaxN = 8;
-
 typedef double d4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ double bf16_to_f64(uint16_t h) {
@@ -137,14 +133,15 @@ __device__ __forceinline__ uint32_t group_or(uint32_t x) {
 // codes and metadata, return the dequantized pair.
 // Row of token t of (b, h) in every cache buffer: contiguous [B][H][T_max], or
 // through the block table of a paged cache. False for an invalid block id.
-__device__ __forceinline__ bool cache_row(const AppendParams& p, int b, int h, int t, size_t& row) {
-  if (!p.table) {
-    row = ((size_t)b * p.H + h) * p.T_max + t;
+__device__ __forceinline__ bool cache_row(const int32_t* table, int maxblk, int lbs, int num_blocks, int H, int T_max,
+                                          int b, int h, int t, size_t& row) {
+  if (!table) {
+    row = ((size_t)b * H + h) * T_max + t;
     return true;
   }
-  const int32_t blk = p.table[(size_t)b * p.maxblk + (t >> p.lbs)];
-  if ((uint32_t)blk >= (uint32_t)p.num_blocks) return false;
-  row = (((size_t)blk * p.H + h) << p.lbs) + (size_t)(t & ((1 << p.lbs) - 1));
+  const int32_t blk = table[(size_t)b * maxblk + (t >> lbs)];
+  if ((uint32_t)blk >= (uint32_t)num_blocks) return false;
+  row = (((size_t)blk * H + h) << lbs) + (size_t)(t & ((1 << lbs) - 1));
   return true;
 }
 
@@ -283,7 +280,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
       continue;
     }
     size_t tok;
-    if (!cache_row(p, b, h, t, tok)) {
+    if (!cache_row(p.table, p.maxblk, p.lbs, p.num_blocks, p.H, p.T_max, b, h, t, tok)) {
       if (lane == 0 && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_BLOCK);
       continue;
     }
@@ -328,8 +325,10 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 // (Previous-loop, all groups together). LM bounds the loop count: the LDS
 // footprint grows with it, and at most 8 loops leave room for two workgroups
 // per compute unit at D = 128.
+// blockIdx.z = 2 layer + tensor: one launch appends to the p.nl layers whose
+// cache pointers are in p.slot; layer i reads its inputs at kv + i * 2 L B H n D.
 template <int D, int LM>
-__global__ __launch_bounds__(256) void append_unit(AppendParams p) {
+__global__ __launch_bounds__(256) void append_unit(UnitParams p) {
   constexpr int kLoopsPerWave = LM / kWaves;
   constexpr int HS = D + 2;                // padded LDS row: 8-byte aligned pairs, 16 rows cover all banks
   constexpr int NF = D * D / 4 / kThreads; // float4 per thread of the rotation
@@ -338,9 +337,18 @@ __global__ __launch_bounds__(256) void append_unit(AppendParams p) {
   __shared__ float xs[LM][D];
   __shared__ double rec[LM][D];            // per loop group: current reference (reconstruction)
   __shared__ double dens[LM];              // its squared norm
-  const int u = blockIdx.x, h = blockIdx.y, kv = blockIdx.z;
+  const int u = blockIdx.x, h = blockIdx.y, kv = blockIdx.z & 1, layer = blockIdx.z >> 1;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int L = p.L, G = p.G;
+  // this layer's and tensor's pointers
+  const void* const* sl = p.slot + (size_t)layer * unit_stride(L);
+  const int32_t* table = p.maxblk ? static_cast<const int32_t*>(sl[0]) : nullptr;
+  const void* const* st = sl + 1 + kv * (1 + 3 * L);
+  const float* rot = static_cast<const float*>(st[0]);
+  auto codes_of = [&](int r) { return static_cast<uint8_t*>(const_cast<void*>(st[1 + r])); };
+  auto meta_of = [&](int r) { return static_cast<uint32_t*>(const_cast<void*>(st[1 + L + r])); };
+  auto alpha_of = [&](int r) { return static_cast<uint16_t*>(const_cast<void*>(st[1 + 2 * L + r])); };
+  const uint16_t* kvin = p.kv + (size_t)layer * 2 * L * p.B * p.H * p.n * D;
   const int b = u / p.n, i = u % p.n;
   const int t = p.pos[b] + i;
   if (t < 0 || t >= p.T_max) {             // whole block, before any barrier
@@ -348,14 +356,14 @@ __global__ __launch_bounds__(256) void append_unit(AppendParams p) {
     return;
   }
   size_t tok;
-  if (!cache_row(p, b, h, t, tok)) {       // likewise
+  if (!cache_row(table, p.maxblk, p.lbs, p.num_blocks, p.H, p.T_max, b, h, t, tok)) {  // likewise
     if (tid == 0 && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_BLOCK);
     return;
   }
 
   // ---- stage H (row-major, padded) and the L input rows
   {
-    const float4* Hg = reinterpret_cast<const float4*>(p.rot[kv] + (size_t)h * D * D);
+    const float4* Hg = reinterpret_cast<const float4*>(rot + (size_t)h * D * D);
     float4 hv[NF];
 #pragma unroll
     for (int j = 0; j < NF; ++j) hv[j] = Hg[tid + j * kThreads];
@@ -368,7 +376,7 @@ __global__ __launch_bounds__(256) void append_unit(AppendParams p) {
     }
     for (int idx = tid; idx < L * (D / 8); idx += kThreads) {
       const int xr = idx / (D / 8), xc = idx % (D / 8);
-      const uint16_t* row = p.kv + (((((size_t)kv * L + xr) * p.B + b) * p.H + h) * p.n + i) * (size_t)D;
+      const uint16_t* row = kvin + (((((size_t)kv * L + xr) * p.B + b) * p.H + h) * p.n + i) * (size_t)D;
       const uint4 xv = reinterpret_cast<const uint4*>(row)[xc];
       const uint32_t w[4] = {xv.x, xv.y, xv.z, xv.w};
 #pragma unroll
@@ -418,8 +426,8 @@ __global__ __launch_bounds__(256) void append_unit(AppendParams p) {
     const int r = wave + kWaves * j;
     if (r < L && r == anchor_of(r)) {
       double r0, r1;
-      quantize_pair<D>(z0[j], z1[j], p.bits[r], (p.g16 >> r) & 1, lane_on, gi, kk, p.codes[kv][r], p.meta[kv][r],
-                       tok, r0, r1);
+      quantize_pair<D>(z0[j], z1[j], p.bits[r], (p.g16 >> r) & 1, lane_on, gi, kk, codes_of(r), meta_of(r), tok, r0,
+                       r1);
       if (!lane_on) r0 = r1 = 0.0;
       const double den = wave_sum_f64(r0 * r0 + r1 * r1);
       if (lane_on) {
@@ -442,9 +450,9 @@ __global__ __launch_bounds__(256) void append_unit(AppendParams p) {
     const double alpha = den > 0.0 ? num / den : 0.0;
     const uint16_t a16 = f64_to_f16(alpha, 0);
     at = f16_to_f64(a16);
-    if (lane == 0) p.alpha[kv][r][tok] = a16;
-    quantize_pair<D>(zz0 - at * r0, zz1 - at * r1, p.bits[r], (p.g16 >> r) & 1, lane_on, gi, kk, p.codes[kv][r],
-                     p.meta[kv][r], tok, q0, q1);
+    if (lane == 0) alpha_of(r)[tok] = a16;
+    quantize_pair<D>(zz0 - at * r0, zz1 - at * r1, p.bits[r], (p.g16 >> r) & 1, lane_on, gi, kk, codes_of(r),
+                     meta_of(r), tok, q0, q1);
   };
 
   if (!chain) {
@@ -482,28 +490,30 @@ __global__ __launch_bounds__(256) void append_unit(AppendParams p) {
 
 }  // namespace
 
+int launch_append_unit(const UnitParams& p, int D, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)(p.B * p.n), (unsigned)p.H, (unsigned)(2 * p.nl));
+  const bool small = p.L <= 8;
+  switch (D) {
+    case 64:
+      if (small) hipLaunchKernelGGL((append_unit<64, 8>), grid, dim3(kThreads), 0, s, p);
+      else hipLaunchKernelGGL((append_unit<64, RQ_MAX_LOOPS>), grid, dim3(kThreads), 0, s, p);
+      break;
+    case 96:
+      if (small) hipLaunchKernelGGL((append_unit<96, 8>), grid, dim3(kThreads), 0, s, p);
+      else hipLaunchKernelGGL((append_unit<96, RQ_MAX_LOOPS>), grid, dim3(kThreads), 0, s, p);
+      break;
+    case 128:
+      if (small) hipLaunchKernelGGL((append_unit<128, 8>), grid, dim3(kThreads), 0, s, p);
+      else hipLaunchKernelGGL((append_unit<128, RQ_MAX_LOOPS>), grid, dim3(kThreads), 0, s, p);
+      break;
+    default: return -1;
+  }
+  return (int)hipGetLastError();
+}
+
 int launch_append(const AppendParams& p, int D, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (p.n <= kUnitAppendMaxN || p.L > 16) {
-    const dim3 grid((unsigned)(p.B * p.n), (unsigned)p.H, 2);
-    const bool small = p.L <= 8;
-    switch (D) {
-      case 64:
-        if (small) hipLaunchKernelGGL((append_unit<64, 8>), grid, dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((append_unit<64, RQ_MAX_LOOPS>), grid, dim3(kThreads), 0, s, p);
-        break;
-      case 96:
-        if (small) hipLaunchKernelGGL((append_unit<96, 8>), grid, dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((append_unit<96, RQ_MAX_LOOPS>), grid, dim3(kThreads), 0, s, p);
-        break;
-      case 128:
-        if (small) hipLaunchKernelGGL((append_unit<128, 8>), grid, dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((append_unit<128, RQ_MAX_LOOPS>), grid, dim3(kThreads), 0, s, p);
-        break;
-      default: return -1;
-    }
-    return (int)hipGetLastError();
-  }
   const int U = 16 / p.L;
   const long long tiles = ((long long)p.B * p.n + U - 1) / U;
   const dim3 grid((unsigned)((tiles + kWaves - 1) / kWaves), (unsigned)p.H, 2);

@@ -112,6 +112,29 @@ struct AppendParams {
   int bits[RQ_MAX_LOOPS];
 };
 
+// One-token (or few-token) appends, one workgroup per (token, head, tensor,
+// layer). The cache pointers of the launch's layers travel in the kernel
+// arguments, so one launch serves many layers without a table in device memory:
+// layer i's pointers start at slot i * stride, as
+//   [block table, then per tensor (K, V): rotation, codes[0..L-1], meta[0..L-1],
+//    alpha[0..L-1]], stride = 1 + 2 (1 + 3 L).
+// kUnitSlots keeps the whole argument block below 4 KB.
+constexpr int kUnitSlots = 440;
+constexpr int unit_stride(int L) { return 1 + 2 * (1 + 3 * L); }
+struct UnitParams {
+  const uint16_t* kv;       // bf16 [nl][2][L][B][H][n][D]
+  const int32_t* pos;
+  int32_t* dev_err;
+  int B, H, L, n, T_max, policy;
+  int G;                    // loops per anchor group (divides L)
+  uint32_t g16;             // bit r: loop r is INT2 in groups of 16 channels
+  int maxblk, lbs, num_blocks;  // paged cache (block size 2^lbs); maxblk = 0: contiguous
+  int nl;                   // layers in this launch
+  int bits[RQ_MAX_LOOPS];
+  const void* slot[kUnitSlots];
+};
+static_assert(sizeof(UnitParams) <= 4096, "kernel arguments must stay within 4 KB");
+
 struct PrefillParams {
   const uint16_t* q;        // bf16 [B][H][T][D]
   const uint16_t* k;
@@ -126,6 +149,9 @@ struct PrefillParams {
 
 // Launchers (return hipError_t as int; 0 = success). Defined in the .hip files.
 int launch_append(const AppendParams& p, int D, void* stream);
+// n <= kUnitAppendMax tokens per sequence, or more than 16 loops.
+constexpr int kUnitAppendMax = 8;
+int launch_append_unit(const UnitParams& p, int D, void* stream);
 // ncomp components with bit widths bits[0..ncomp-1]; returns -1 if no kernel exists.
 int launch_decode(const DecodeParams& p, int D, int ncomp, const int* bits, int nsplit, void* stream);
 int launch_decode_paged(const DecodeParams& p, int D, int ncomp, const int* bits, int nsplit, void* stream);

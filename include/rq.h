@@ -165,6 +165,25 @@ rq_status rq_quantize_append(const rq_desc* desc, const rq_layer_cache* cache,
                              const uint16_t* kv, const int32_t* pos, int32_t n,
                              int32_t* dev_err, void* stream);
 
+/* rq_quantize_append for nlayers layers that share one descriptor (§4.2
+ * "Decode": the store of the current token is deferred until after the final
+ * loop, when every layer's keys and values of all loops are known, so one call
+ * can store them for the whole layer stack).
+ *   caches: host array of nlayers layer caches (copied during the call).
+ *   kv:     bf16 [nlayers][2][L][B][H][n][D], layer l's input as in
+ *           rq_quantize_append, the layers back to back.
+ *   pos:    as in rq_quantize_append, the same positions for every layer.
+ * Each layer's buffers receive exactly the bytes rq_quantize_append(desc,
+ * &caches[l], kv + l*2*L*B*H*n*D, pos, n, ...) would write. For n <= 8 (or
+ * more than 16 loops) the layers share launches: their cache pointers travel in
+ * the kernel arguments, as many layers per launch as fit (16 at 4 loops, 8 at
+ * 8 loops); larger n takes one bulk launch per layer. Every cache is checked
+ * before the first launch, so an error status means nothing was launched.
+ * nlayers == 0 or n == 0 is a no-op; nlayers < 0 is RQ_E_SHAPE. */
+rq_status rq_quantize_append_layers(const rq_desc* desc, const rq_layer_cache* caches,
+                                    int32_t nlayers, const uint16_t* kv, const int32_t* pos,
+                                    int32_t n, int32_t* dev_err, void* stream);
+
 /* Decode attention of loop `loop` (0-based) over the compressed cache plus the
  * current token held in bf16 (§4.1, §4.2 "Decode", App. G.2).
  *   q, k_cur, v_cur: bf16 [B][H][D], original domain (current token's q/k/v of

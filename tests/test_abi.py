@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import decode_attention_quantize_amd as rq
 
@@ -195,6 +196,37 @@ def test_append_validation():
     ca.meta[0][1] = 0x100002                                                   # meta needs 4 bytes
     assert L.rq_quantize_append(by(d), by(ca), FAKE, FAKE, 1, None, 0) == 10
     assert L.rq_quantize_append(by(d), by(c), ctypes.c_void_p(0x100001), FAKE, 1, None, 0) == 10
+
+
+def test_append_layers_validation():
+    """Every layer is checked before the first launch (no call here reaches one)."""
+    L, by = rq.lib, ctypes.byref
+    d = _desc()
+    arr = (rq.LayerCacheC * 3)(_cache(d), _cache(d), _cache(d))
+    assert L.rq_quantize_append_layers(by(d), None, 3, FAKE, FAKE, 1, None, 0) == 1
+    assert L.rq_quantize_append_layers(by(d), arr, -1, FAKE, FAKE, 1, None, 0) == 2
+    assert L.rq_quantize_append_layers(by(d), arr, 0, FAKE, FAKE, 1, None, 0) == 0     # no layers: no-op
+    assert L.rq_quantize_append_layers(by(d), arr, 3, None, None, 0, None, 0) == 0     # n == 0: no-op
+    assert L.rq_quantize_append_layers(by(d), arr, 3, FAKE, FAKE, 101, None, 0) == 4
+    assert L.rq_quantize_append_layers(by(d), arr, 3, None, FAKE, 1, None, 0) == 1
+    arr[2].meta[1][1] = 0x100002                                                     # last layer misaligned
+    assert L.rq_quantize_append_layers(by(d), arr, 3, FAKE, FAKE, 1, None, 0) == 10
+    arr[2].meta[1][1] = 0x100000
+    arr[1].alpha[0][2] = None                                                        # a residual without alpha
+    assert L.rq_quantize_append_layers(by(d), arr, 3, FAKE, FAKE, 1, None, 0) == 1
+
+
+def test_append_layers_binding_checks():
+    """The binding refuses caches with different descriptors and a kv of the wrong shape."""
+    d1, d2 = _desc(), _desc(max_tokens=200)
+    a = rq.LayerCache(d1, [], [], [], [])
+    b = rq.LayerCache(d2, [], [], [], [])
+    kv = torch.zeros(2, 2, d1.loops, d1.batch, d1.heads, 1, d1.head_dim, dtype=torch.bfloat16)
+    pos = torch.zeros(d1.batch, dtype=torch.int32)
+    with pytest.raises(ValueError, match="descriptor differs"):
+        rq.quantize_append_layers([a, b], kv, pos, 1)
+    with pytest.raises(ValueError, match="kv"):
+        rq.quantize_append_layers([a, a, a], kv, pos, 1)
 
 
 @pytest.mark.parametrize("policy", [0, 1, 2])
