@@ -315,7 +315,9 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 }
 
 // Few-token path (decode-time store of the current token, short chunks): one
-// workgroup per (sequence, token) unit, head and tensor. The workgroup stages
+// workgroup per (sequence, token) unit, head, tensor and layer (blockIdx.z =
+// 2 layer + tensor; the launch's p.nl layers find their cache pointers in
+// p.slot, and layer i reads its inputs at kv + i * 2 L B H n D). The workgroup stages
 // the head's rotation in LDS once; wave w computes Z_r for its loops
 // r = w, w + 4, .. on the fp64 vector units (lane k of group gi holds channels
 // e0 = 32 gi + k and e1 = e0 + 16, the pair quantize_pair takes), so the four
@@ -325,8 +327,6 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 // (Previous-loop, all groups together). LM bounds the loop count: the LDS
 // footprint grows with it, and at most 8 loops leave room for two workgroups
 // per compute unit at D = 128.
-// blockIdx.z = 2 layer + tensor: one launch appends to the p.nl layers whose
-// cache pointers are in p.slot; layer i reads its inputs at kv + i * 2 L B H n D.
 template <int D, int LM>
 __global__ __launch_bounds__(256) void append_unit(UnitParams p) {
   constexpr int kLoopsPerWave = LM / kWaves;
