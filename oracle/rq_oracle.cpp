@@ -59,6 +59,14 @@ uint16_t f16_encode(double x, int mode) {
   return (uint16_t)(sign | (uint16_t)((lead2 + 15) << 10) | mant);
 }
 
+/* The cache holds o, s and alpha as finite fp16 numbers. A value whose rounding
+ * leaves the fp16 range (rotated inputs or residuals beyond +-65504, or an LS
+ * coefficient of that size) is held at the largest finite magnitude of its
+ * sign; the pages do not discuss overflow. */
+uint16_t f16_saturate(uint16_t h) {
+  return (h & 0x7fff) == 0x7c00 ? (uint16_t)((h & 0x8000) | 0x7bff) : h;
+}
+
 double f16_decode(uint16_t h) {
   const int e = (h >> 10) & 31;
   const int m = h & 1023;
@@ -236,10 +244,10 @@ void rqo_group_quant(const double* v, int g, int bits, uint16_t* o16, uint16_t* 
     if (v[i] > mx) mx = v[i];
   }
   const double qmax = (double)((1 << bits) - 1);
-  const uint16_t o = f16_encode(mn, RQO_RD);
+  const uint16_t o = f16_saturate(f16_encode(mn, RQO_RD));
   const double od = f16_decode(o);
   const double sp = (mx - od) / qmax;
-  const uint16_t s = f16_encode(sp, RQO_RU);
+  const uint16_t s = f16_saturate(f16_encode(sp, RQO_RU));
   const double sd = f16_decode(s);
   *o16 = o;
   *s16 = s;
@@ -335,7 +343,7 @@ int rqo_quantize_series(const rqo_cfg* c, const uint16_t* X, int T, const float*
         const double* Zr = &Z[(size_t)r * D];
         const double den = dot(D, ref.data(), ref.data());
         const double al = den > 0.0 ? dot(D, Zr, ref.data()) / den : 0.0;   /* LS alpha (§3.2) */
-        const uint16_t al16 = f16_encode(al, RQO_RNE);
+        const uint16_t al16 = f16_saturate(f16_encode(al, RQO_RNE));
         const double alt = f16_decode(al16);
         alpha[r][t] = al16;
         if (alpha_pre) alpha_pre[(size_t)r * T + t] = al;

@@ -42,7 +42,9 @@ int rqo_rotation(int D, int nb, const int8_t* sign, double* H);
 /* One group of g values -> fp16 offset o, fp16 scale s, integer codes.
  *   o = fp16 round-toward--inf of min(v); s = fp16 round-toward-+inf of
  *   (max(v) - o) / (2^bits - 1); code_i = clamp(rne((v_i - o) / s), 0, 2^bits - 1);
- *   s == 0 (all values equal o) gives code 0 everywhere.
+ *   s == 0 (all values equal o) gives code 0 everywhere. An o or s whose fp16
+ *   rounding overflows is held at +-65504 (the largest finite fp16 magnitude of
+ *   its sign), so values outside [o, o + (2^bits - 1) s] clip to the end codes.
  * Optional outputs (may be NULL): delta[i] = distance, in code units, of
  * (v_i - o)/s from the nearest rounding boundary k + 1/2; pre_o = min(v);
  * pre_s = (max(v) - o)/(2^bits - 1) before fp16 rounding. */
@@ -83,7 +85,8 @@ int rqo_row_bytes(const rqo_cfg* c, int r);
 /* Quantize one (tensor, batch, head) series of T tokens.
  * X: bf16 [L][T][D] (original domain). H: fp32 [D][D], z = H x.
  * codes[r]: [T][row_bytes(r)]; meta[r]: fp16 [T][D/group[r]][2] as (o, s);
- * alpha[r]: fp16 [T] for every non-anchor loop (ignored for the anchor; may be NULL there).
+ * alpha[r]: fp16 [T] for every non-anchor loop (ignored for the anchor; may be NULL there);
+ *   an LS coefficient whose fp16 rounding overflows is held at +-65504.
  * Diagnostics (each may be NULL): delta [L][T][D]; alpha_pre [L][T];
  * pre_o, pre_s [L][T][D], of which entry [r][t][j] for j < D/group[r] holds
  * group j's value before fp16 rounding.

@@ -113,3 +113,42 @@ def test_pack_layout_single_bit_probe(bits, g):
         j, p = divmod(k, per)
         expect = 32 * j + 16 * h + bits * p
         assert bitpos.tolist() == [expect], (e, bitpos, expect)
+
+
+def _f16_up(x):
+    """Smallest float16 >= x (numpy's conversion rounds to nearest; step up if below)."""
+    h = np.float16(x)
+    if float(h) < x:
+        h = np.nextafter(h, np.float16(np.inf))
+    return h
+
+
+def test_offset_beyond_fp16_range_saturates():
+    """A group whose minimum is below -65504 keeps the most negative finite fp16
+    offset; values below it clip to code 0 and the rest follow the usual rule."""
+    v = np.linspace(-70000.0, 1000.0, 32)
+    for bits in (2, 4):
+        qmax = 2 ** bits - 1
+        o16, s16, codes, _, pre_o, pre_s = O.group_quant(v, bits)
+        assert np.isneginf(np.float16(v.min()))              # plain fp16 rounding would overflow
+        assert o16 == int(np.float16(-65504.0).view(np.uint16))
+        s = _f16(s16)
+        assert s == float(_f16_up((v.max() + 65504.0) / qmax))
+        assert pre_s == (v.max() + 65504.0) / qmax
+        levels = -65504.0 + s * np.arange(qmax + 1)
+        best = np.abs(v[:, None] - levels[None, :]).argmin(axis=1)   # nearest level, clipping included
+        assert np.array_equal(codes, best)
+        assert codes[0] == 0 and codes[-1] == qmax
+
+
+def test_scale_beyond_fp16_range_saturates():
+    """(max - o)/(2^b - 1) above 65504 keeps the largest finite fp16 scale; values past
+    o + (2^b - 1) * 65504 clip to the top code."""
+    v = np.concatenate([[0.0, 250000.0], np.linspace(1.0, 240000.0, 30)])
+    o16, s16, codes, _, pre_o, pre_s = O.group_quant(v, 2)
+    assert _f16(o16) == 0.0 and pre_s == 250000.0 / 3
+    assert np.isinf(np.float16(pre_s))
+    assert s16 == int(np.float16(65504.0).view(np.uint16))
+    expect = np.clip(np.round(v / 65504.0), 0, 3)            # no exact ties in these values
+    assert np.array_equal(codes, expect.astype(np.uint16))
+    assert codes[1] == 3 and codes[0] == 0

@@ -192,3 +192,31 @@ def test_alpha_tracks_generator_similarity():
         s = O.quantize_series(O.Config(D=64, bits=[2, 2, 2, 4]), X, H)
         for r in range(3):
             assert abs(s.alpha_pre[r].mean() / w.sim(r + 1) - 1) < 0.03
+
+
+def test_alpha_beyond_fp16_range_saturates():
+    """A loop about 1e6 times its (small) anchor along the same direction: the exact LS
+    coefficient overflows fp16, the stored one is 65504 and the residual is taken with it."""
+    rng = np.random.default_rng(3)
+    T, D = 6, 64
+    base = rng.normal(size=(T, D)).astype(np.float32)
+    anchor = _bf16(1e-4 * base)
+    loop = _bf16(1e2 * O.bf16_decode(anchor).astype(np.float32) * 1e4)   # ~1e6 x the anchor
+    X = np.stack([loop, anchor])
+    H = np.eye(D, dtype=np.float32)
+    s = O.quantize_series(O.Config(D=D, bits=[4, 4]), X, H)
+    A = O.reconstruct(s, 1)
+    Z = O.bf16_decode(loop)
+    exact = np.einsum("td,td->t", Z, A) / np.einsum("td,td->t", A, A)      # numpy LS, no fp16
+    assert np.all(np.abs(exact) > 65520.0)                                # fp16 would round to inf
+    assert np.all(s.alpha[0] == np.float16(65504.0).view(np.uint16))
+    assert np.allclose(s.alpha_pre[0], exact, rtol=1e-12)
+    # the residual is quantized against alpha = 65504: reconstruction = 65504 A + D(c)
+    o, sc = _meta_scales(s, 0)
+    codes = np.stack([np.concatenate([O.unpack_group(s.codes[0][t, j * 16:(j + 1) * 16], 32, 4)
+                                      for j in range(2)]) for t in range(T)])
+    deq = np.repeat(o, 32, axis=1) + np.repeat(sc, 32, axis=1) * codes
+    assert np.array_equal(O.reconstruct(s, 0), 65504.0 * A + deq)
+    E = Z - 65504.0 * A
+    assert np.all(np.abs(O.reconstruct(s, 0) - Z) <= np.repeat(sc, 32, axis=1) / 2 * (1 + 2 ** -20)
+                  + 1e-9 * np.abs(E).max())
