@@ -81,7 +81,7 @@ def dom_kernel_name(D, bits, G, groups=None):
     gs = _groups(bits, groups)
     kind = [b | (8 if g == 16 else 0) for b, g in zip(bits, gs)]
     cb = kind[G - 1] | (kind[0] << 4)
-    return f"decode_fused<{D}, 2, {cb}u, 2>"
+    return f"decode_fused<{D}, 2, {cb}u, 2, 2>"
 
 
 DOM_KERNEL = dom_kernel_name(128, [2, 2, 4, 4], 0)

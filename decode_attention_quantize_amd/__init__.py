@@ -25,7 +25,8 @@ STATUS = {0: "RQ_OK", 1: "RQ_E_NULL", 2: "RQ_E_SHAPE", 3: "RQ_E_BITS", 4: "RQ_E_
           5: "RQ_E_WORKSPACE", 6: "RQ_E_UNSUPPORTED", 7: "RQ_E_HIP", 8: "RQ_E_POLICY", 9: "RQ_E_LOOP",
           10: "RQ_E_ALIGN"}
 POLICY_LAST_LOOP, POLICY_PREV_LOOP, POLICY_FIRST_LOOP = 0, 1, 2
-DEVERR_CAPACITY, DEVERR_LENGTH, DEVERR_BLOCK = 1, 2, 4
+DEVERR_CAPACITY, DEVERR_LENGTH, DEVERR_BLOCK, DEVERR_RANGE = 1, 2, 4, 8
+FLAG_PRECISE_QUERY = 1
 
 
 class RQError(RuntimeError):
@@ -38,6 +39,7 @@ class Desc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("loops", ctypes.c_int32), ("max_tokens", ctypes.c_int32), ("policy", ctypes.c_int32),
                 ("loop_group", ctypes.c_int32), ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("flags", ctypes.c_int32),
                 ("bits", ctypes.c_uint8 * MAX_LOOPS), ("group", ctypes.c_uint8 * MAX_LOOPS)]
 
 
@@ -99,13 +101,14 @@ def version() -> str:
 
 def make_desc(batch: int, heads: int, head_dim: int, bits, max_tokens: int,
               policy: int = POLICY_LAST_LOOP, group=32, loop_group: int = 0, block_size: int = 0,
-              num_blocks: int = 0) -> Desc:
+              num_blocks: int = 0, flags: int = 0) -> Desc:
     """Descriptor of one layer's cache; `group` is one size for all loops or one per loop;
-    block_size > 0 makes it a paged cache of num_blocks blocks (see rq.h)."""
+    block_size > 0 makes it a paged cache of num_blocks blocks; flags: FLAG_PRECISE_QUERY
+    (see rq.h)."""
     d = Desc()
     d.batch, d.heads, d.head_dim = batch, heads, head_dim
     d.loops, d.max_tokens, d.policy, d.loop_group = len(bits), max_tokens, policy, loop_group
-    d.block_size, d.num_blocks = block_size, num_blocks
+    d.block_size, d.num_blocks, d.flags = block_size, num_blocks, flags
     groups = list(group) if isinstance(group, (list, tuple)) else [group] * len(bits)
     if len(groups) != len(bits):
         raise ValueError("one group size per loop")
@@ -359,26 +362,38 @@ def _need_step(d: Desc, q, past_len, k_cur=None, v_cur=None, out=None, full=True
         _need(out, bhd, torch.float32, "out")
 
 
+def _with_flags(d: Desc, flags) -> Desc:
+    """The descriptor as passed to a decode call: flags=None keeps the cache's own."""
+    if flags is None or flags == d.flags:
+        return d
+    c = Desc.from_buffer_copy(d)
+    c.flags = flags
+    return c
+
+
 def decode_attn(cache: LayerCache, loop: int, q, k_cur, v_cur, past_len, scale: float, out, workspace,
-                dev_err=None, stream=None):
+                dev_err=None, stream=None, flags=None):
+    """flags (e.g. FLAG_PRECISE_QUERY) override the cache descriptor's for this call."""
     _need_step(cache.desc, q, past_len, k_cur, v_cur, out)
     _need_err(dev_err)
     _need_bytes(workspace, 1, "workspace")
     _on_gpu(q=q, k_cur=k_cur, v_cur=v_cur, past_len=past_len, out=out, workspace=workspace, dev_err=dev_err)
     cc = cache.c()
-    _check(lib.rq_decode_attn(ctypes.byref(cache.desc), ctypes.byref(cc), loop, _ptr(q), _ptr(k_cur),
+    _check(lib.rq_decode_attn(ctypes.byref(_with_flags(cache.desc, flags)), ctypes.byref(cc), loop, _ptr(q), _ptr(k_cur),
                               _ptr(v_cur), _ptr(past_len), scale, _ptr(out), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _ptr(dev_err), _stream(stream)),
            "rq_decode_attn")
 
 
-def decode_attn_partial(cache: LayerCache, loop: int, q, past_len, scale: float, workspace, stream=None):
+def decode_attn_partial(cache: LayerCache, loop: int, q, past_len, scale: float, workspace, stream=None,
+                        flags=None):
     """First launch of decode_attn: per-slot partials (m, l, -, -, acc[D]) into the workspace."""
     _need_step(cache.desc, q, past_len, full=False)
     _need_bytes(workspace, 1, "workspace")
     _on_gpu(q=q, past_len=past_len, workspace=workspace)
     cc = cache.c()
-    _check(lib.rq_decode_attn_partial(ctypes.byref(cache.desc), ctypes.byref(cc), loop, _ptr(q), _ptr(past_len),
+    _check(lib.rq_decode_attn_partial(ctypes.byref(_with_flags(cache.desc, flags)), ctypes.byref(cc), loop, _ptr(q),
+                                      _ptr(past_len),
                                       scale, _ptr(workspace), workspace.numel() * workspace.element_size(),
                                       _stream(stream)), "rq_decode_attn_partial")
 

@@ -68,7 +68,7 @@ int log2_of(int x) {
 rq_status check_shape(const rq_desc* d) {
   if (!d) return RQ_E_NULL;
   if (d->batch < 1 || d->heads < 1 || !dim_ok(d->head_dim) || d->loops < 1 || d->loops > RQ_MAX_LOOPS ||
-      d->max_tokens < 1)
+      d->max_tokens < 1 || (d->flags & ~RQ_FLAG_PRECISE_QUERY) != 0)
     return RQ_E_SHAPE;
   return RQ_OK;
 }
@@ -155,7 +155,7 @@ const char* rq_status_str(rq_status s) {
   switch (s) {
     case RQ_OK: return "ok";
     case RQ_E_NULL: return "required pointer is NULL";
-    case RQ_E_SHAPE: return "shape out of range (batch, heads, head_dim in {64,96,128}, loops 1..32, loop_group 0 or a divisor of loops, max_tokens >= 1, n)";
+    case RQ_E_SHAPE: return "shape out of range (batch, heads, head_dim in {64,96,128}, loops 1..32, loop_group 0 or a divisor of loops, max_tokens >= 1, n, known flags)";
     case RQ_E_BITS: return "unsupported bit width or group size (bits 2 or 4; group 32, or 16 for 2 bits)";
     case RQ_E_CAPACITY: return "size exceeds max_tokens";
     case RQ_E_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
@@ -358,7 +358,8 @@ rq_status decode_partial(const rq_desc* d, const rq_layer_cache* c, int32_t loop
   if (nc > kMaxComp) return RQ_E_UNSUPPORTED;
   int bits[kMaxComp];  // component kinds: bit width, plus 8 for INT2 in groups of 16
   for (int i = 0; i < nc; ++i) bits[i] = d->bits[loops[i]] | (d->group[loops[i]] == 16 ? 8 : 0);
-  if (!have_decode_kernel(d->head_dim, nc, bits)) return RQ_E_UNSUPPORTED;
+  const int limbs = (d->flags & RQ_FLAG_PRECISE_QUERY) ? 3 : 2;
+  if (!have_decode_kernel(d->head_dim, nc, bits, limbs)) return RQ_E_UNSUPPORTED;
 
   const SplitPlan sp = split_plan(d);
   DecodeParams p;
@@ -400,7 +401,7 @@ rq_status decode_partial(const rq_desc* d, const rq_layer_cache* c, int32_t loop
     p.num_blocks = d->num_blocks;
     p.pool_rows = (uint32_t)((size_t)d->num_blocks * d->heads * d->block_size);
   }
-  return launch_decode(p, d->head_dim, nc, bits, sp.nsplit, stream) == 0 ? RQ_OK : RQ_E_HIP;
+  return launch_decode(p, d->head_dim, nc, bits, limbs, sp.nsplit, stream) == 0 ? RQ_OK : RQ_E_HIP;
 }
 
 }  // namespace
@@ -429,10 +430,13 @@ rq_status rq_decode_combine(const rq_desc* d, const float* rot_v, const uint16_t
   return launch_combine(cp, d->head_dim, d->batch, stream) == 0 ? RQ_OK : RQ_E_HIP;
 }
 
-rq_status rq_decode_attn(const rq_desc* d, const rq_layer_cache* c, int32_t loop, const uint16_t* q,
-                         const uint16_t* k_cur, const uint16_t* v_cur, const int32_t* past_len,
-                         float softmax_scale, float* out, void* ws, size_t ws_bytes, int32_t* dev_err,
-                         void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of a whole decode call that come before its workspace.
+rq_status check_decode_call(const rq_desc* d, const rq_layer_cache* c, int32_t loop, const uint16_t* q,
+                            const uint16_t* k_cur, const uint16_t* v_cur, const int32_t* past_len, const float* out) {
   rq_status s = check_plan(d);
   if (s != RQ_OK) return s;
   if (!c) return RQ_E_NULL;
@@ -441,6 +445,19 @@ rq_status rq_decode_attn(const rq_desc* d, const rq_layer_cache* c, int32_t loop
   if (!al(q, 16) || !al(k_cur, 16) || !al(v_cur, 16) || !al(past_len, 4) || !al(out, 4) || !al(c->rot[0], 16) ||
       !al(c->rot[1], 16))
     return RQ_E_ALIGN;
+  return RQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rq_status rq_decode_attn(const rq_desc* d, const rq_layer_cache* c, int32_t loop, const uint16_t* q,
+                         const uint16_t* k_cur, const uint16_t* v_cur, const int32_t* past_len,
+                         float softmax_scale, float* out, void* ws, size_t ws_bytes, int32_t* dev_err,
+                         void* stream) {
+  rq_status s = check_decode_call(d, c, loop, q, k_cur, v_cur, past_len, out);
+  if (s != RQ_OK) return s;
   // Validate everything the second launch needs before enqueuing the first.
   if (!ws || ws_bytes < workspace_for(d) || ((uintptr_t)ws & 255) != 0) return RQ_E_WORKSPACE;
   s = decode_partial(d, c, loop, q, past_len, softmax_scale, ws, ws_bytes, dev_err, stream);

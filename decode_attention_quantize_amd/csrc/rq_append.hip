@@ -70,6 +70,17 @@ __device__ uint16_t f64_to_f16(double x, int mode) {
   return (uint16_t)(sign | (uint16_t)((EE + 15) << 10) | (uint16_t)(n - 1024));
 }
 
+// The cache holds offsets, scales and LS coefficients as finite fp16 numbers:
+// a rounding that overflows (inputs or residuals beyond the fp16 range) is held
+// at the largest finite magnitude of its sign and reported through `sat`.
+__device__ __forceinline__ uint16_t f16_sat(uint16_t h, bool& sat) {
+  if ((h & 0x7fff) == 0x7c00) {
+    sat = true;
+    return (uint16_t)((h & 0x8000) | 0x7bff);
+  }
+  return h;
+}
+
 // Lane exchanges of the reductions below, in the vector unit (no LDS round
 // trip). Within a row of 16 lanes, DPP: the quad permutations give lane l ^ 1
 // and l ^ 2; after those, every lane of a quad holds the same value, so the
@@ -147,7 +158,7 @@ __device__ __forceinline__ bool cache_row(const int32_t* table, int maxblk, int 
 
 template <int D>
 __device__ void quantize_pair(double v0, double v1, int bits, bool g16, bool lane_on, int gi, int k,
-                              uint8_t* codes, uint32_t* meta, size_t tok, double& d0, double& d1) {
+                              uint8_t* codes, uint32_t* meta, size_t tok, double& d0, double& d1, bool& sat) {
   double mn0, mx0, mn1, mx1;
   if (g16) {
     mn0 = lane_on ? v0 : 0.0;
@@ -176,9 +187,9 @@ __device__ void quantize_pair(double v0, double v1, int bits, bool g16, bool lan
   uint16_t o16[2], s16[2];
   double od[2], sd[2];
   for (int i = 0; i < (g16 ? 2 : 1); ++i) {
-    o16[i] = f64_to_f16(i ? mn1 : mn0, 1);
+    o16[i] = f16_sat(f64_to_f16(i ? mn1 : mn0, 1), sat);
     od[i] = f16_to_f64(o16[i]);
-    s16[i] = f64_to_f16(((i ? mx1 : mx0) - od[i]) / qmax, 2);
+    s16[i] = f16_sat(f64_to_f16(((i ? mx1 : mx0) - od[i]) / qmax, 2), sat);
     sd[i] = f16_to_f64(s16[i]);
   }
   if (!g16) {
@@ -285,12 +296,13 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
       continue;
     }
     const double(*Z)[D + 1] = &Zs[wave][uu * L];
+    bool sat = false;
     // each loop group independently: its anchor, then the other loops of the group
     for (int g0 = 0; g0 < L; g0 += p.G) {
       const int a = (p.policy == RQ_POLICY_LAST_LOOP) ? g0 + p.G - 1 : g0;
       double r0, r1;  // reference (reconstructed anchor, or previous loop) at e0, e1
       quantize_pair<D>(Z[a][e0], Z[a][e1], p.bits[a], (p.g16 >> a) & 1, lane_on, gi, k, p.codes[kv][a],
-                       p.meta[kv][a], tok, r0, r1);
+                       p.meta[kv][a], tok, r0, r1, sat);
       if (!lane_on) r0 = r1 = 0.0;
       double den_cur = wave_sum_f64(r0 * r0 + r1 * r1);
       for (int r = g0; r < g0 + p.G; ++r) {
@@ -298,12 +310,12 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
         const double z0 = lane_on ? Z[r][e0] : 0.0, z1 = lane_on ? Z[r][e1] : 0.0;
         const double num = wave_sum_f64(z0 * r0 + z1 * r1);
         const double alpha = den_cur > 0.0 ? num / den_cur : 0.0;
-        const uint16_t a16 = f64_to_f16(alpha, 0);
+        const uint16_t a16 = f16_sat(f64_to_f16(alpha, 0), sat);
         const double at = f16_to_f64(a16);
         if (lane == 0) p.alpha[kv][r][tok] = a16;
         double q0, q1;
         quantize_pair<D>(z0 - at * r0, z1 - at * r1, p.bits[r], (p.g16 >> r) & 1, lane_on, gi, k, p.codes[kv][r],
-                         p.meta[kv][r], tok, q0, q1);
+                         p.meta[kv][r], tok, q0, q1, sat);
         if (p.policy == RQ_POLICY_PREV_LOOP) {  // zhat_r = alpha_r zhat_{r-1} + D(c_r)
           r0 = lane_on ? at * r0 + q0 : 0.0;
           r1 = lane_on ? at * r1 + q1 : 0.0;
@@ -311,6 +323,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
         }
       }
     }
+    if (sat && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_RANGE);
   }
 }
 
@@ -420,6 +433,7 @@ __global__ __launch_bounds__(256) void append_unit(UnitParams p) {
   const bool last = p.policy == RQ_POLICY_LAST_LOOP, chain = p.policy == RQ_POLICY_PREV_LOOP;
   auto anchor_of = [&](int r) { return last ? r / G * G + G - 1 : r / G * G; };
 
+  bool sat = false;                        // an fp16 offset, scale or alpha was saturated
   // ---- anchors of every group (by the waves that own them)
 #pragma unroll
   for (int j = 0; j < kLoopsPerWave; ++j) {
@@ -427,7 +441,7 @@ __global__ __launch_bounds__(256) void append_unit(UnitParams p) {
     if (r < L && r == anchor_of(r)) {
       double r0, r1;
       quantize_pair<D>(z0[j], z1[j], p.bits[r], (p.g16 >> r) & 1, lane_on, gi, kk, codes_of(r), meta_of(r), tok, r0,
-                       r1);
+                       r1, sat);
       if (!lane_on) r0 = r1 = 0.0;
       const double den = wave_sum_f64(r0 * r0 + r1 * r1);
       if (lane_on) {
@@ -448,11 +462,11 @@ __global__ __launch_bounds__(256) void append_unit(UnitParams p) {
     const double den = dens[g];
     const double num = wave_sum_f64((lane_on ? zz0 : 0.0) * r0 + (lane_on ? zz1 : 0.0) * r1);
     const double alpha = den > 0.0 ? num / den : 0.0;
-    const uint16_t a16 = f64_to_f16(alpha, 0);
+    const uint16_t a16 = f16_sat(f64_to_f16(alpha, 0), sat);
     at = f16_to_f64(a16);
     if (lane == 0) alpha_of(r)[tok] = a16;
     quantize_pair<D>(zz0 - at * r0, zz1 - at * r1, p.bits[r], (p.g16 >> r) & 1, lane_on, gi, kk, codes_of(r),
-                     meta_of(r), tok, q0, q1);
+                     meta_of(r), tok, q0, q1, sat);
   };
 
   if (!chain) {
@@ -486,6 +500,7 @@ __global__ __launch_bounds__(256) void append_unit(UnitParams p) {
       __syncthreads();
     }
   }
+  if (sat && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_RANGE);
 }
 
 }  // namespace

@@ -115,17 +115,19 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
 }
 
 // ---------------------------------------------------------------- dispatch
-#define RQ_E(D, NC, CB) {D, NC, CB, decode_fused<D, NC, CB, RQ_DEPTH>}
+#define RQ_E(D, NC, CB, LB) {D, NC, CB, LB, decode_fused<D, NC, CB, RQ_DEPTH, LB>}
 const PlanEntry kTable[] = {RQ_PLANS(64), RQ_PLANS(96), RQ_PLANS(128)};
 #undef RQ_E
 
 }  // namespace
 
-bool have_decode_kernel(int D, int nc, const int* bits) { return find_plan(kTable, D, nc, bits) != nullptr; }
+bool have_decode_kernel(int D, int nc, const int* bits, int limbs) {
+  return find_plan(kTable, D, nc, bits, limbs) != nullptr;
+}
 
-int launch_decode(const DecodeParams& p, int D, int nc, const int* bits, int nsplit, void* stream) {
-  if (p.table) return launch_decode_paged(p, D, nc, bits, nsplit, stream);
-  const PlanEntry* e = find_plan(kTable, D, nc, bits);
+int launch_decode(const DecodeParams& p, int D, int nc, const int* bits, int limbs, int nsplit, void* stream) {
+  if (p.table) return launch_decode_paged(p, D, nc, bits, limbs, nsplit, stream);
+  const PlanEntry* e = find_plan(kTable, D, nc, bits, limbs);
   if (!e) return -1;
   const dim3 grid((unsigned)(nsplit * p.B * p.H));
   hipLaunchKernelGGL(e->fn, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), p);

@@ -78,21 +78,24 @@ __device__ __forceinline__ Words<BITS> load_group(__amdgpu_buffer_rsrc_t r, uint
   return w;
 }
 
-// q' of one group as fixed point, v_e = round(q'_e 2^E) with |v| < 2^kFixBits
-// (E per group), written in balanced base 256 as kLimbs signed 8-bit limbs
-// (most significant first) and packed four per register in the order the code
-// bytes of a word come out of one mask (see kdot). Integer dot products of the
-// codes with each limb are exact; the rounding of q' to kFixBits bits is the only
-// error, a relative 2^-kFixBits of the group's largest |q'|. Two limbs (14 bits)
-// keep scores within ~1e-3 (log2 units) of exact at 16k tokens with synthetic
-// outlier keys; three limbs (21 bits) take them to ~1e-6 but cost 16 more VALU
+// q' of one group as fixed point, v_e = round(q'_e 2^E) with |v| < 2^FIX
+// (E per group, FIX = 7 LIMBS), written in balanced base 256 as LIMBS signed
+// 8-bit limbs (most significant first) and packed four per register in the
+// order the code bytes of a word come out of one mask (see kdot). Integer dot
+// products of the codes with each limb are exact; the rounding of q' to FIX
+// bits is the only error, a relative 2^-FIX of the group's largest |q'|, and the
+// score error it causes grows with the size of the scores. Two limbs (14 bits,
+// the default) keep scores within ~1e-3 (log2 units) of exact at 16k tokens with
+// synthetic outlier keys; three limbs (21 bits, RQ_FLAG_PRECISE_QUERY) take
+// them to ~1e-5 for sharper softmax distributions, for 16 more VALU
 // instructions per tile and 16 more registers.
-constexpr int kLimbs = 2;
-constexpr int kFixBits = kLimbs == 2 ? 14 : 21;
+template <int LIMBS>
+constexpr int fix_bits() { return 7 * LIMBS; }
+template <int LIMBS>
 struct QFix {
-  uint32_t q4[4][2][kLimbs];   // INT4: word j, mask (low / high nibbles), limb
-  uint32_t q2[2][4][kLimbs];   // INT2, one group of 32: word j, field s, limb
-  uint32_t q2h[2][4][kLimbs];  // INT2, two groups of 16: word j (= group j), field s, limb
+  uint32_t q4[4][2][LIMBS];   // INT4: word j, mask (low / high nibbles), limb
+  uint32_t q2[2][4][LIMBS];   // INT2, one group of 32: word j, field s, limb
+  uint32_t q2h[2][4][LIMBS];  // INT2, two groups of 16: word j (= group j), field s, limb
 };
 
 // Elements of the group that byte b (0..3) of a masked word holds.
@@ -113,41 +116,42 @@ __host__ __device__ constexpr int kbits(int k) { return k & 7; }
 __host__ __device__ constexpr bool kg16(int k) { return (k & kGroup16) != 0; }
 
 // sum_e v_e code_e over each group of 16 of an INT2 block (exact in int32).
-__device__ __forceinline__ void kdot16(const Words<2>& c, const QFix& Q, int& d0, int& d1) {
+template <int LIMBS>
+__device__ __forceinline__ void kdot16(const Words<2>& c, const QFix<LIMBS>& Q, int& d0, int& d1) {
   int r[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    int a[kLimbs];
+    int a[LIMBS];
 #pragma unroll
-    for (int l = 0; l < kLimbs; ++l) a[l] = 0;
+    for (int l = 0; l < LIMBS; ++l) a[l] = 0;
     const uint32_t x = c.w[j];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       const int m = (int)((x >> (2 * f)) & 0x03030303u);
 #pragma unroll
-      for (int l = 0; l < kLimbs; ++l) a[l] = __builtin_amdgcn_sdot4(m, (int)Q.q2h[j][f][l], a[l], false);
+      for (int l = 0; l < LIMBS; ++l) a[l] = __builtin_amdgcn_sdot4(m, (int)Q.q2h[j][f][l], a[l], false);
     }
     r[j] = a[0];
 #pragma unroll
-    for (int l = 1; l < kLimbs; ++l) r[j] = r[j] * 256 + a[l];
+    for (int l = 1; l < LIMBS; ++l) r[j] = r[j] * 256 + a[l];
   }
   d0 = r[0];
   d1 = r[1];
 }
 
 // sum_e v_e code_e over one group (exact in int32: |v| < 2^21, 32 codes < 16).
-template <int BITS>
-__device__ __forceinline__ int kdot(const Words<BITS>& c, const QFix& Q) {
-  int a[kLimbs];
+template <int BITS, int LIMBS>
+__device__ __forceinline__ int kdot(const Words<BITS>& c, const QFix<LIMBS>& Q) {
+  int a[LIMBS];
 #pragma unroll
-  for (int l = 0; l < kLimbs; ++l) a[l] = 0;
+  for (int l = 0; l < LIMBS; ++l) a[l] = 0;
   if constexpr (BITS == 4) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t x = c.w[j];
       const int m0 = (int)(x & 0x0F0F0F0Fu), m1 = (int)((x >> 4) & 0x0F0F0F0Fu);
 #pragma unroll
-      for (int l = 0; l < kLimbs; ++l) {
+      for (int l = 0; l < LIMBS; ++l) {
         a[l] = __builtin_amdgcn_sdot4(m0, (int)Q.q4[j][0][l], a[l], false);
         a[l] = __builtin_amdgcn_sdot4(m1, (int)Q.q4[j][1][l], a[l], false);
       }
@@ -160,13 +164,13 @@ __device__ __forceinline__ int kdot(const Words<BITS>& c, const QFix& Q) {
       for (int f = 0; f < 4; ++f) {
         const int m = (int)((x >> (2 * f)) & 0x03030303u);
 #pragma unroll
-        for (int l = 0; l < kLimbs; ++l) a[l] = __builtin_amdgcn_sdot4(m, (int)Q.q2[j][f][l], a[l], false);
+        for (int l = 0; l < LIMBS; ++l) a[l] = __builtin_amdgcn_sdot4(m, (int)Q.q2[j][f][l], a[l], false);
       }
     }
   }
   int r = a[0];
 #pragma unroll
-  for (int l = 1; l < kLimbs; ++l) r = r * 256 + a[l];
+  for (int l = 1; l < LIMBS; ++l) r = r * 256 + a[l];
   return r;
 }
 
@@ -349,19 +353,22 @@ __device__ __forceinline__ void load_tile(Tile<D, NC, CB>& T, const CompRsrc (&R
 
 // Waves per SIMD the register budget is tuned for: three for plans whose tile
 // data is small enough (one INT4 and one INT2 component at most), two otherwise.
-template <int NC, uint32_t CB>
+// The 21-bit query (a third of its registers more) does not fit three waves'
+// registers without spilling.
+template <int NC, uint32_t CB, int LIMBS>
 constexpr int waves_for() {
   int bits = 0;
   for (int c = 0; c < NC; ++c) bits += kbits((int)((CB >> (4 * c)) & 0xF));
+  if (LIMBS > 2) return 2;
   return (NC <= 2 && bits <= 6) ? RQ_WAVES_SMALL : 2;
 }
 
 // The paged instances keep block ids and per-lane row offsets live as well;
 // with groups of 16 that no longer fits three waves' registers without
 // spilling.
-template <int NC, uint32_t CB>
+template <int NC, uint32_t CB, int LIMBS>
 constexpr int waves_for_paged() {
-  return any_g16<CB, NC>() ? 2 : waves_for<NC, CB>();
+  return any_g16<CB, NC>() ? 2 : waves_for<NC, CB, LIMBS>();
 }
 
 // Cache addressing of the streaming kernel.
@@ -378,7 +385,7 @@ enum : int { kContig = 0, kPagedLane = 1 };
 
 // One (b, h, slot) work item: stream the slot's tokens of the compressed
 // cache and store the slot's partial.
-template <int D, int NC, uint32_t CB, int DEPTH, int MODE>
+template <int D, int NC, uint32_t CB, int DEPTH, int MODE, int LIMBS>
 __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   constexpr int G = D / 32;
   constexpr int TPW = 64 / G;
@@ -556,7 +563,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   // This lane's group of q' in fixed point (per-group exponent). qsum, which
   // multiplies the group offsets, is the sum of the same fixed-point values, so a
   // stored value o + s c meets one consistent q'.
-  QFix Q;
+  QFix<LIMBS> Q;
   float qsum, qscale, qsum_h[2];  // qsum_h: the two 16-channel halves of the lane's block
   {
     float qv[32], mx = 0.0f;
@@ -567,9 +574,9 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     }
     int ex = 0;
     (void)frexpf(mx, &ex);                          // mx in [2^(ex-1), 2^ex)
-    const int E = mx > 0.0f ? kFixBits - ex : 0;    // |q' 2^E| < 2^kFixBits
+    const int E = mx > 0.0f ? fix_bits<LIMBS>() - ex : 0;  // |q' 2^E| < 2^FIX
     qscale = ldexpf(1.0f, -E);
-    int lm[kLimbs][32];
+    int lm[LIMBS][32];
     int vsum = 0, vsum_h[2] = {0, 0};
 #pragma unroll
     for (int e = 0; e < 32; ++e) {
@@ -577,7 +584,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
       vsum += v;
       vsum_h[e >> 4] += v;
 #pragma unroll
-      for (int l = kLimbs - 1; l >= 0; --l) {      // balanced base-256 digits, least significant first
+      for (int l = LIMBS - 1; l >= 0; --l) {       // balanced base-256 digits, least significant first
         const int d = l == 0 ? v : ((v + 128) & 255) - 128;
         lm[l][e] = d;
         v = (v - d) >> 8;
@@ -590,7 +597,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
       return (uint32_t)(a & 255) | ((uint32_t)(b & 255) << 8) | ((uint32_t)(c & 255) << 16) | ((uint32_t)d << 24);
     };
 #pragma unroll
-    for (int l = 0; l < kLimbs; ++l) {
+    for (int l = 0; l < LIMBS; ++l) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -638,7 +645,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
         kp1[c] = fmaf(f16hi(C.km1[0]) * qscale, (float)a1, f16lo(C.km1[0]) * qsum_h[0]) +
                  fmaf(f16hi(C.km1[1]) * qscale, (float)b1, f16lo(C.km1[1]) * qsum_h[1]);
       } else {
-        const float d0 = (float)kdot<kbits(KK)>(C.k0, Q), d1 = (float)kdot<kbits(KK)>(C.k1, Q);
+        const float d0 = (float)kdot<kbits(KK), LIMBS>(C.k0, Q), d1 = (float)kdot<kbits(KK), LIMBS>(C.k1, Q);
         kp0[c] = fmaf(f16hi(C.km0[0]) * qscale, d0, f16lo(C.km0[0]) * qsum);
         kp1[c] = fmaf(f16hi(C.km1[0]) * qscale, d1, f16lo(C.km1[0]) * qsum);
       }
@@ -779,16 +786,16 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
                                p.part + ((size_t)bh * p.nsplit + split) * part_floats(D));
 }
 
-template <int D, int NC, uint32_t CB, int DEPTH>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_for<NC, CB>()))) void decode_fused(
+template <int D, int NC, uint32_t CB, int DEPTH, int LIMBS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_for<NC, CB, LIMBS>()))) void decode_fused(
     DecodeParams p) {
-  decode_body<D, NC, CB, DEPTH, kContig>(p);
+  decode_body<D, NC, CB, DEPTH, kContig, LIMBS>(p);
 }
 
-template <int D, int NC, uint32_t CB, int DEPTH>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_for_paged<NC, CB>()))) void
+template <int D, int NC, uint32_t CB, int DEPTH, int LIMBS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_for_paged<NC, CB, LIMBS>()))) void
 decode_fused_paged(DecodeParams p) {
-  decode_body<D, NC, CB, DEPTH, kPagedLane>(p);
+  decode_body<D, NC, CB, DEPTH, kPagedLane, LIMBS>(p);
 }
 
 
@@ -797,6 +804,7 @@ typedef void (*MainFn)(DecodeParams);
 struct PlanEntry {
   int D, nc;
   uint32_t cb;
+  int limbs;
   MainFn fn;
 };
 
@@ -804,20 +812,22 @@ struct PlanEntry {
 #define RQ_DEPTH 2
 #endif
 // Plans with kernels: one nibble per component, anchor first (0xA = INT2 in
-// groups of 16). RQ_E(D, NC, CB) names the instance a table entry takes.
-#define RQ_PLANS(D)                                                                                        \
-  RQ_E(D, 1, 0x2), RQ_E(D, 1, 0x4), RQ_E(D, 2, 0x22), RQ_E(D, 2, 0x24), RQ_E(D, 2, 0x42), RQ_E(D, 2, 0x44), \
-      RQ_E(D, 3, 0x244), RQ_E(D, 3, 0x224), RQ_E(D, 3, 0x222), RQ_E(D, 3, 0x444), RQ_E(D, 4, 0x2244),        \
-      RQ_E(D, 4, 0x2224), RQ_E(D, 4, 0x2222), RQ_E(D, 4, 0x4444),                                           \
-      RQ_E(D, 1, 0xA), RQ_E(D, 2, 0xAA), RQ_E(D, 2, 0xA4), RQ_E(D, 3, 0xAA4), RQ_E(D, 4, 0xAAA4),          \
-      RQ_E(D, 3, 0xAAA), RQ_E(D, 4, 0xAAAA)
+// groups of 16). RQ_E(D, NC, CB, LIMBS) names the instance a table entry takes;
+// every plan has a 14-bit (2 limbs) and a 21-bit (3 limbs) query instance.
+#define RQ_PLANS_L(D, LB)                                                                                   \
+  RQ_E(D, 1, 0x2, LB), RQ_E(D, 1, 0x4, LB), RQ_E(D, 2, 0x22, LB), RQ_E(D, 2, 0x24, LB), RQ_E(D, 2, 0x42, LB), \
+      RQ_E(D, 2, 0x44, LB), RQ_E(D, 3, 0x244, LB), RQ_E(D, 3, 0x224, LB), RQ_E(D, 3, 0x222, LB),               \
+      RQ_E(D, 3, 0x444, LB), RQ_E(D, 4, 0x2244, LB), RQ_E(D, 4, 0x2224, LB), RQ_E(D, 4, 0x2222, LB),           \
+      RQ_E(D, 4, 0x4444, LB), RQ_E(D, 1, 0xA, LB), RQ_E(D, 2, 0xAA, LB), RQ_E(D, 2, 0xA4, LB),                 \
+      RQ_E(D, 3, 0xAA4, LB), RQ_E(D, 4, 0xAAA4, LB), RQ_E(D, 3, 0xAAA, LB), RQ_E(D, 4, 0xAAAA, LB)
+#define RQ_PLANS(D) RQ_PLANS_L(D, 2), RQ_PLANS_L(D, 3)
 
 template <size_t N>
-const PlanEntry* find_plan(const PlanEntry (&table)[N], int D, int nc, const int* kinds) {
+const PlanEntry* find_plan(const PlanEntry (&table)[N], int D, int nc, const int* kinds, int limbs) {
   uint32_t cb = 0;
   for (int c = 0; c < nc; ++c) cb |= (uint32_t)kinds[c] << (4 * c);
   for (const PlanEntry& e : table)
-    if (e.D == D && e.nc == nc && e.cb == cb) return &e;
+    if (e.D == D && e.nc == nc && e.cb == cb && e.limbs == limbs) return &e;
   return nullptr;
 }
 

@@ -8,14 +8,15 @@
 namespace rq {
 namespace {
 
-#define RQ_E(D, NC, CB) {D, NC, CB, decode_fused_paged<D, NC, CB, RQ_DEPTH>}
+#define RQ_E(D, NC, CB, LB) {D, NC, CB, LB, decode_fused_paged<D, NC, CB, RQ_DEPTH, LB>}
 const PlanEntry kPagedTable[] = {RQ_PLANS(64), RQ_PLANS(96), RQ_PLANS(128)};
 #undef RQ_E
 
 }  // namespace
 
-int launch_decode_paged(const DecodeParams& p, int D, int nc, const int* bits, int nsplit, void* stream) {
-  const PlanEntry* e = find_plan(kPagedTable, D, nc, bits);
+int launch_decode_paged(const DecodeParams& p, int D, int nc, const int* bits, int limbs, int nsplit,
+                        void* stream) {
+  const PlanEntry* e = find_plan(kPagedTable, D, nc, bits, limbs);
   if (!e) return -1;
   const dim3 grid((unsigned)(nsplit * p.B * p.H));
   hipLaunchKernelGGL(e->fn, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), p);

@@ -152,13 +152,15 @@ int launch_append(const AppendParams& p, int D, void* stream);
 // n <= kUnitAppendMax tokens per sequence, or more than 16 loops.
 constexpr int kUnitAppendMax = 8;
 int launch_append_unit(const UnitParams& p, int D, void* stream);
-// ncomp components with bit widths bits[0..ncomp-1]; returns -1 if no kernel exists.
-int launch_decode(const DecodeParams& p, int D, int ncomp, const int* bits, int nsplit, void* stream);
-int launch_decode_paged(const DecodeParams& p, int D, int ncomp, const int* bits, int nsplit, void* stream);
+// ncomp components of kinds bits[0..ncomp-1], the rotated query in `limbs` 7-bit
+// limbs (2 or 3); returns -1 if no kernel exists.
+int launch_decode(const DecodeParams& p, int D, int ncomp, const int* bits, int limbs, int nsplit, void* stream);
+int launch_decode_paged(const DecodeParams& p, int D, int ncomp, const int* bits, int limbs, int nsplit,
+                        void* stream);
 int launch_bf16(const Bf16Params& p, int D, int nsplit, void* stream);
 int launch_combine(const CombineParams& p, int D, int B, void* stream);
 int launch_prefill(const PrefillParams& p, int D, void* stream);
 size_t prefill_workspace_bytes(int B, int H, int D, int T);
-bool have_decode_kernel(int D, int ncomp, const int* bits);
+bool have_decode_kernel(int D, int ncomp, const int* bits, int limbs);
 
 }  // namespace rq

@@ -71,6 +71,8 @@ typedef enum {
 #define RQ_DEVERR_LENGTH 2    /* decode: past_len[b] outside [0, max_tokens]; it was clamped */
 #define RQ_DEVERR_BLOCK 4     /* paged cache: a block-table entry a token needs is outside [0, num_blocks);
                                * append dropped the token, decode read it as zeros */
+#define RQ_DEVERR_RANGE 8     /* append: an offset, scale or LS coefficient fell outside the fp16 range and
+                               * was stored as +-65504 (see rq_quantize_append) */
 
 /* Reference policy (§3.2, App. D), applied inside every loop group (see
  * rq_desc.loop_group; by default all L loops form one group).
@@ -83,6 +85,14 @@ typedef enum {
  *   so decoding the j-th loop of a group reads j stored components (the decode
  *   kernels take at most 4). Kept as the comparator the paper measures against. */
 typedef enum { RQ_POLICY_LAST_LOOP = 0, RQ_POLICY_PREV_LOOP = 1, RQ_POLICY_FIRST_LOOP = 2 } rq_policy;
+
+/* Decode flag: score the cached keys against the rotated query held in 21-bit
+ * instead of 14-bit fixed point (§4.1 keeps softmax in FP32; App. G.2). The
+ * query's rounding is the only error of the key path, relative 2^-15 (default)
+ * or 2^-22 of each 32-channel group's largest |q'|, so the score error grows
+ * with the size of the logits; set the flag for sharp softmax distributions. It
+ * costs a few percent of the streaming kernel's time. Decode calls only. */
+#define RQ_FLAG_PRECISE_QUERY 1
 
 /* Shapes and the quantization plan of one layer's cache. */
 typedef struct {
@@ -99,6 +109,7 @@ typedef struct {
                         * serving engine's paged KV blocks): tokens per block, a power of two in
                         * [16, 4096] dividing max_tokens; see rq_layer_cache.block_table */
   int32_t num_blocks;  /* paged cache: blocks in every buffer's pool (>= 1) */
+  int32_t flags;       /* 0 or RQ_FLAG_PRECISE_QUERY (other bits: RQ_E_SHAPE) */
   uint8_t bits[RQ_MAX_LOOPS];   /* bit width per loop (0-based), 2 or 4 (§2.1, §3.4) */
   uint8_t group[RQ_MAX_LOOPS];  /* group size per loop along the rotated head_dim: 32, or 16 for
                                  * 2-bit loops (§5 "Quantization setup": g = 16 for INT2) */
@@ -160,7 +171,14 @@ rq_status rq_check_desc(const rq_desc* desc);
  * E_r = Z_r - alpha_r * ref, group quantization of E_r, packing. Offsets are
  * rounded toward -inf and scales toward +inf to fp16, codes to nearest-even,
  * so every group's range is covered. Tokens at positions >= max_tokens are
- * dropped (RQ_DEVERR_CAPACITY). n == 0 is a no-op. */
+ * dropped (RQ_DEVERR_CAPACITY). n == 0 is a no-op.
+ * Accepted range: the metadata are fp16, so every rotated value (and every
+ * residual E_r) must lie within +-65504 and every group's range within
+ * (2^bits - 1) * 65504; LS coefficients must stay below 65504 in magnitude.
+ * Outside it, an offset, scale or coefficient whose fp16 rounding overflows is
+ * stored as the largest finite fp16 magnitude of its sign (values beyond the
+ * group's covered range then clip to the end codes) and RQ_DEVERR_RANGE is set;
+ * the cache stays finite. Inputs must be finite bf16. */
 rq_status rq_quantize_append(const rq_desc* desc, const rq_layer_cache* cache,
                              const uint16_t* kv, const int32_t* pos, int32_t n,
                              int32_t* dev_err, void* stream);

@@ -16,6 +16,7 @@ ever fed to an oracle computation):
 from __future__ import annotations
 
 import math
+import os
 import sys
 from concurrent.futures import ThreadPoolExecutor
 
@@ -31,9 +32,18 @@ CODE_DELTA = 1e-6
 TOL_ATTN = 2e-3
 
 
+_LOG_FILE = os.environ.get("RQ_PARITY_LOG")
+
+
 def log(msg: str):
+    """Print a parity record; with RQ_PARITY_LOG set, also append it to that file, so a
+    run leaves every logged error and exemption count behind."""
     print(f"[parity] {msg}", flush=True)
     sys.stdout.flush()
+    if _LOG_FILE:
+        test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+        with open(_LOG_FILE, "a") as f:
+            f.write(f"{test}\t{msg}\n")
 
 
 def u16(t: torch.Tensor) -> np.ndarray:

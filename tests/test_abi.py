@@ -46,6 +46,7 @@ def _desc(**kw):
     (dict(bits=[2] * 32), 0), (dict(loop_group=2), 0), (dict(loop_group=4), 0), (dict(loop_group=1), 0),
     (dict(loop_group=3), 2), (dict(loop_group=5), 2), (dict(loop_group=-1), 2),
     (dict(bits=[2] * 32, loop_group=4), 0), (dict(bits=[2] * 32, loop_group=12), 2),
+    (dict(flags=1), 0), (dict(flags=2), 2), (dict(flags=-1), 2),
 ])
 def test_check_desc(kw, code):
     if code is None:
@@ -55,15 +56,32 @@ def test_check_desc(kw, code):
     assert rq.check_desc(_desc(**kw)) == code
 
 
-def test_desc_layout_matches_header():
-    """The ctypes mirrors of rq_desc (nine int32 fields, then 32 bit widths and 32 group
-    sizes) and rq_layer_cache (block_table after the rotations)."""
+def test_desc_layout_matches_header(tmp_path):
+    """The ctypes mirrors of rq_desc and rq_layer_cache have the sizes and field offsets
+    a C compiler gives the structs of include/rq.h."""
+    import subprocess
+    fields = {"rq_desc": [f for f, _ in rq.Desc._fields_], "rq_layer_cache": [f for f, _ in rq.LayerCacheC._fields_]}
+    prog = ["#include <stdio.h>", "#include <stddef.h>", '#include "rq.h"', "int main(void) {"]
+    for st, fs in fields.items():
+        prog.append(f'  printf("{st} size %zu\\n", sizeof({st}));')
+        for f in fs:
+            prog.append(f'  printf("{st} {f} %zu\\n", offsetof({st}, {f}));')
+    prog += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(prog) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.splitlines():
+        st, f, v = line.split()
+        got[(st, f)] = int(v)
+    assert got[("rq_desc", "size")] == ctypes.sizeof(rq.Desc)
+    assert got[("rq_layer_cache", "size")] == ctypes.sizeof(rq.LayerCacheC)
+    for f in fields["rq_desc"]:
+        assert got[("rq_desc", f)] == getattr(rq.Desc, f).offset, f
+    for f in fields["rq_layer_cache"]:
+        assert got[("rq_layer_cache", f)] == getattr(rq.LayerCacheC, f).offset, f
     assert rq.MAX_LOOPS == 32
-    assert ctypes.sizeof(rq.Desc) == 9 * 4 + 2 * 32
-    assert rq.Desc.loop_group.offset == 6 * 4
-    assert rq.Desc.block_size.offset == 7 * 4 and rq.Desc.num_blocks.offset == 8 * 4
-    assert rq.Desc.bits.offset == 9 * 4
-    assert rq.LayerCacheC.block_table.offset == 8 * (3 * 2 * 32 + 2)
 
 
 @pytest.mark.parametrize("bs,nb,code", [

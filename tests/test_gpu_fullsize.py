@@ -152,6 +152,18 @@ def test_capacity_8k_batch64_sampled():
     _check(0, LAST, w.bits, _sample_units(8, 3, w), "8k B64", w)
 
 
+def test_ouro_int2_4k_every_series():
+    """Uniform-INT2 Ouro shape at its full size (B1, H16, D128, 4 loops, 4096 cached
+    tokens, plan [2,2,2,2]; capacity 4096 + 64, so the benchmark's split plan of 16 slots
+    per series): layer 0, every (batch, head) series, the whole cache and every loop's
+    output at the first and last step."""
+    w = synth.WORKLOADS["ouro_int2_4k"]
+    d = rq.make_desc(w.batch, w.heads, w.D, list(w.bits), w.T + STEPS)
+    unit, nsplit = rq.split_plan(d)
+    log(f"int2 4k: {nsplit} slots of {rq.slot_len(w.T, nsplit, unit)} tokens per series")
+    _check(0, LAST, w.bits, [(b, h) for b in range(w.batch) for h in range(w.heads)], "int2 4k layer 0", w)
+
+
 def test_ouro_16k_bf16_sampled():
     B, H, D, T = W.batch, W.heads, W.D, W.T
     layer = 0
