@@ -23,7 +23,8 @@ MAX_LOOPS = 32
 OK = 0
 STATUS = {0: "RQ_OK", 1: "RQ_E_NULL", 2: "RQ_E_SHAPE", 3: "RQ_E_BITS", 4: "RQ_E_CAPACITY",
           5: "RQ_E_WORKSPACE", 6: "RQ_E_UNSUPPORTED", 7: "RQ_E_HIP", 8: "RQ_E_POLICY", 9: "RQ_E_LOOP",
-          10: "RQ_E_ALIGN"}
+          10: "RQ_E_ALIGN", 11: "RQ_E_SCRATCH"}
+SCRATCH_BYTES = 8 << 20                  # RQ_SCRATCH_BYTES of rq.h
 POLICY_LAST_LOOP, POLICY_PREV_LOOP, POLICY_FIRST_LOOP = 0, 1, 2
 DEVERR_CAPACITY, DEVERR_LENGTH, DEVERR_BLOCK, DEVERR_RANGE = 1, 2, 4, 8
 FLAG_PRECISE_QUERY = 1
@@ -67,6 +68,8 @@ def _load():
     L.rq_quantize_append_layers.argtypes = [P, P, I, P, P, I, P, P]
     L.rq_decode_attn.restype = ctypes.c_int
     L.rq_decode_attn.argtypes = [P, P, I, P, P, P, P, ctypes.c_float, P, P, Z, P, P]
+    L.rq_decode_attn_noalloc.restype = ctypes.c_int
+    L.rq_decode_attn_noalloc.argtypes = [P, P, I, P, P, P, P, ctypes.c_float, P, P, P]
     L.rq_split_plan.restype = ctypes.c_int
     L.rq_split_plan.argtypes = [P, P, P]
     L.rq_decode_attn_partial.restype = ctypes.c_int
@@ -383,6 +386,19 @@ def decode_attn(cache: LayerCache, loop: int, q, k_cur, v_cur, past_len, scale: 
                               _ptr(v_cur), _ptr(past_len), scale, _ptr(out), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _ptr(dev_err), _stream(stream)),
            "rq_decode_attn")
+
+
+def decode_attn_noalloc(cache: LayerCache, loop: int, q, k_cur, v_cur, past_len, scale: float, out,
+                        dev_err=None, stream=None, flags=None):
+    """decode_attn without a workspace: the library's static per-device scratch holds the
+    partials (calls on one GPU must not overlap)."""
+    _need_step(cache.desc, q, past_len, k_cur, v_cur, out)
+    _need_err(dev_err)
+    _on_gpu(q=q, k_cur=k_cur, v_cur=v_cur, past_len=past_len, out=out, dev_err=dev_err)
+    cc = cache.c()
+    _check(lib.rq_decode_attn_noalloc(ctypes.byref(_with_flags(cache.desc, flags)), ctypes.byref(cc), loop, _ptr(q),
+                                      _ptr(k_cur), _ptr(v_cur), _ptr(past_len), scale, _ptr(out), _ptr(dev_err),
+                                      _stream(stream)), "rq_decode_attn_noalloc")
 
 
 def decode_attn_partial(cache: LayerCache, loop: int, q, past_len, scale: float, workspace, stream=None,

@@ -2,6 +2,7 @@
 // kernel dispatch for the C ABI declared in include/rq.h.
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include <hip/hip_runtime.h>
 
@@ -164,6 +165,7 @@ const char* rq_status_str(rq_status s) {
     case RQ_E_POLICY: return "unknown reference policy";
     case RQ_E_LOOP: return "loop index out of range";
     case RQ_E_ALIGN: return "device array misaligned (codes/rot/kv/q/k/v 16 B, meta 4 B (8 B for groups of 16), out 4 B, alpha 2 B)";
+    case RQ_E_SCRATCH: return "the call's split partials exceed the library's static scratch (RQ_SCRATCH_BYTES); use rq_decode_attn with a workspace";
   }
   return "unknown status";
 }
@@ -464,6 +466,53 @@ rq_status rq_decode_attn(const rq_desc* d, const rq_layer_cache* c, int32_t loop
   if (s != RQ_OK) return s;
   return rq_decode_combine(d, c->rot[1], q, k_cur, v_cur, past_len, softmax_scale, out, ws, ws_bytes, dev_err,
                            stream);
+}
+
+}  // extern "C"
+
+// ---- decode without a caller workspace -------------------------------------
+// The split partials live in a file-scope device array instead: every GPU the
+// library runs on holds its own copy for the life of the process, and its
+// address on each device is looked up once, with that device current.
+static __device__ __align__(256) unsigned char scratch[RQ_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Address of the current device's scratch (nullptr if it cannot be found).
+void* scratch_of_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch[dev] = p;
+  }
+  return g_scratch[dev];
+}
+}  // namespace
+
+extern "C" {
+
+rq_status rq_decode_attn_noalloc(const rq_desc* d, const rq_layer_cache* c, int32_t loop, const uint16_t* q,
+                                 const uint16_t* k_cur, const uint16_t* v_cur, const int32_t* past_len,
+                                 float softmax_scale, float* out, int32_t* dev_err, void* stream) {
+  const rq_status s = check_decode_call(d, c, loop, q, k_cur, v_cur, past_len, out);
+  if (s != RQ_OK) return s;
+  if (workspace_for(d) > (size_t)RQ_SCRATCH_BYTES) return RQ_E_SCRATCH;
+  void* ws = scratch_of_current_device();
+  if (!ws) return RQ_E_HIP;
+  return rq_decode_attn(d, c, loop, q, k_cur, v_cur, past_len, softmax_scale, out, ws, (size_t)RQ_SCRATCH_BYTES,
+                        dev_err, stream);
 }
 
 rq_status rq_decode_attn_bf16_partial(const rq_desc* d, const uint16_t* k_cache, const uint16_t* v_cache,

@@ -63,7 +63,8 @@ typedef enum {
   RQ_E_HIP = 7,          /* a HIP launch failed */
   RQ_E_POLICY = 8,       /* unknown reference policy */
   RQ_E_LOOP = 9,         /* loop index out of range */
-  RQ_E_ALIGN = 10        /* a device array is not aligned as documented below */
+  RQ_E_ALIGN = 10,       /* a device array is not aligned as documented below */
+  RQ_E_SCRATCH = 11      /* rq_decode_attn_noalloc: the request needs more than RQ_SCRATCH_BYTES */
 } rq_status;
 
 /* Device-side error bits (OR-ed into *dev_err when given). */
@@ -257,6 +258,25 @@ rq_status rq_decode_attn_partial(const rq_desc* desc, const rq_layer_cache* cach
 rq_status rq_decode_combine(const rq_desc* desc, const float* rot_v, const uint16_t* q, const uint16_t* k_cur,
                             const uint16_t* v_cur, const int32_t* past_len, float softmax_scale, float* out,
                             const void* workspace, size_t workspace_bytes, int32_t* dev_err, void* stream);
+
+/* rq_decode_attn for callers that cannot allocate device memory (code under
+ * hipGraph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and results, bit for bit, with the split partials kept in a
+ * static device array of RQ_SCRATCH_BYTES that the library holds on every GPU
+ * it runs on until the process ends, instead of a caller workspace. The call
+ * allocates nothing. Its first call on a device looks up that device's array
+ * (hipGetSymbolAddress, with the device current); make that first call outside
+ * stream capture. Requests whose partials, rq_workspace_bytes(desc), exceed
+ * RQ_SCRATCH_BYTES return RQ_E_SCRATCH and enqueue nothing. All calls on one
+ * GPU share its array and it keeps the last call's contents (nothing in it needs
+ * to start at zero): calls that overlap in time on one GPU, from any stream or
+ * thread, race and must be ordered by the caller. Other arguments and errors as
+ * rq_decode_attn. */
+#define RQ_SCRATCH_BYTES (8u << 20)
+rq_status rq_decode_attn_noalloc(const rq_desc* desc, const rq_layer_cache* cache, int32_t loop,
+                                 const uint16_t* q, const uint16_t* k_cur, const uint16_t* v_cur,
+                                 const int32_t* past_len, float softmax_scale, float* out, int32_t* dev_err,
+                                 void* stream);
 
 /* BF16 decode baseline (the paper's comparison point, §5.3): the same attention
  * over an uncompressed cache. k_cache, v_cache: bf16 [B][H][T_max][D]. Only

@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert "gfx950" in rq.version()
-    for code in range(11):
+    for code in range(12):
         assert rq.status_str(code) and rq.status_str(code) != "unknown status"
 
 
