@@ -13,10 +13,12 @@ LIB = os.path.join(PKG, "librq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # per-source extra flags: the append kernel takes its rounding decisions in fp64
-# and must not contract products and sums into fused multiply-adds
+# and must not contract products and sums into fused multiply-adds; its inputs
+# are finite (rq.h), so min/max need not quiet NaN operands (IEEE mode off: one
+# v_max_f64 instead of three)
 SOURCES = {
     "rq_api.cpp": ["-x", "hip"],
-    "rq_append.hip": ["-ffp-contract=off"],
+    "rq_append.hip": ["-ffp-contract=off", "-fno-honor-nans", "-mno-amdgpu-ieee"],
     "rq_decode.hip": [],
     "rq_decode_paged.hip": [],
     "rq_decode_bf16.hip": [],

@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include "rq_device.hpp"
+#include "rq_fp16.hpp"
 #include "rq_internal.hpp"
 
 namespace rq {
@@ -27,47 +28,6 @@ __device__ __forceinline__ double bf16_to_f64(uint16_t h) {
 
 __device__ __forceinline__ double f16_to_f64(uint16_t h) {
   return (double)(float)__builtin_bit_cast(_Float16, h);
-}
-
-// binary64 -> binary16 bits. mode 0: nearest-even, 1: toward -inf, 2: toward +inf.
-// The magnitude M * 2^(E-52) is cut at the fp16 spacing of its binade
-// (2^(E-10), or 2^-24 below the normal range); the dropped bits decide rounding.
-__device__ uint16_t f64_to_f16(double x, int mode) {
-  const uint64_t bits = (uint64_t)__double_as_longlong(x);
-  const bool neg = (bits >> 63) != 0;
-  const uint16_t sign = neg ? 0x8000 : 0;
-  const int e = (int)((bits >> 52) & 0x7ff);
-  const uint64_t frac = bits & 0xFFFFFFFFFFFFFull;
-  if (e == 0x7ff) return frac ? (uint16_t)0x7e00 : (uint16_t)(sign | 0x7c00);
-  if (e == 0 && frac == 0) return sign;
-  const int E = (e == 0) ? -1022 : e - 1023;
-  const uint64_t M = (e == 0) ? frac : (frac | (1ull << 52));
-  const int qexp = (E < -14) ? -24 : E - 10;
-  const int shift = qexp - (E - 52);  // >= 42
-  uint64_t n = 0;
-  bool up;
-  if (shift >= 64) {
-    up = (mode == 1 && neg) || (mode == 2 && !neg);  // nonzero remainder below half a spacing
-  } else {
-    n = M >> shift;
-    const uint64_t rem = M & ((1ull << shift) - 1);
-    const uint64_t half = 1ull << (shift - 1);
-    if (mode == 0) up = rem > half || (rem == half && (n & 1));
-    else if (mode == 1) up = neg && rem != 0;
-    else up = !neg && rem != 0;
-  }
-  n += up ? 1 : 0;
-  if (qexp == -24) return (uint16_t)(sign | (uint16_t)n);  // n <= 1024; 1024 is 2^-14
-  int EE = E;
-  if (n == 2048) {
-    n = 1024;
-    EE += 1;
-  }
-  if (EE > 15) {
-    const bool toward_zero = (mode == 1 && !neg) || (mode == 2 && neg);
-    return (uint16_t)(sign | (toward_zero ? 0x7bff : 0x7c00));
-  }
-  return (uint16_t)(sign | (uint16_t)((EE + 15) << 10) | (uint16_t)(n - 1024));
 }
 
 // The cache holds offsets, scales and LS coefficients as finite fp16 numbers:
@@ -156,175 +116,284 @@ __device__ __forceinline__ bool cache_row(const int32_t* table, int maxblk, int 
   return true;
 }
 
-template <int D>
-__device__ void quantize_pair(double v0, double v1, int bits, bool g16, bool lane_on, int gi, int k,
-                              uint8_t* codes, uint32_t* meta, size_t tok, double& d0, double& d1, bool& sat) {
+// Code of value v in a group with fp16 offset od and scale sd (§2.1): nearest
+// level, ties to even, clamped to [0, 2^BITS - 1]; 0 when sd = 0 (a constant group).
+template <int BITS>
+__device__ __forceinline__ uint32_t code_of(double v, double od, double sd) {
+  constexpr double qmax = (double)((1 << BITS) - 1);
+  const double t = rint((v - od) / (sd != 0.0 ? sd : 1.0));
+  return sd != 0.0 ? (uint32_t)fmin(fmax(t, 0.0), qmax) : 0u;
+}
+
+// Quantize one row's pair of elements e0 = 32 gi + k, e1 = e0 + 16 (held by
+// lane k of a 16-lane row) in one group of 32 channels, or, with G16, e0 in
+// group 2 gi and e1 in group 2 gi + 1 of 16 channels each (INT2 only); store
+// codes into the token's code row and metadata into its metadata row, and
+// return the dequantized pair. A row with lane_on false (the same for its 16
+// lanes) stores nothing.
+template <int D, int BITS, bool G16>
+__device__ __forceinline__ void quantize_pair_t(double v0, double v1, bool lane_on, int gi, int k, uint8_t* row,
+                                                uint32_t* mrow, double& d0, double& d1, bool& sat) {
+  constexpr double qmax = (double)((1 << BITS) - 1);
+  if (!lane_on) {
+    v0 = 0.0;
+    v1 = 0.0;
+  }
+  auto mn = [](double a, double b) { return fmin(a, b); };
+  auto mx = [](double a, double b) { return fmax(a, b); };
   double mn0, mx0, mn1, mx1;
-  if (g16) {
-    mn0 = lane_on ? v0 : 0.0;
-    mx0 = mn0;
-    mn1 = lane_on ? v1 : 0.0;
-    mx1 = mn1;
+  if constexpr (G16) {
+    mn0 = row16_f64(v0, mn);
+    mx0 = row16_f64(v0, mx);
+    mn1 = row16_f64(v1, mn);
+    mx1 = row16_f64(v1, mx);
   } else {
-    mn0 = mn1 = lane_on ? fmin(v0, v1) : 0.0;
-    mx0 = mx1 = lane_on ? fmax(v0, v1) : 0.0;
+    mn0 = mn1 = row16_f64(fmin(v0, v1), mn);
+    mx0 = mx1 = row16_f64(fmax(v0, v1), mx);
   }
-  {                                             // the 16 lanes of one lane group
-    auto mn = [](double a, double b) { return fmin(a, b); };
-    auto mx = [](double a, double b) { return fmax(a, b); };
-    mn0 = row16_f64(mn0, mn);
-    mx0 = row16_f64(mx0, mx);
-    if (g16) {
-      mn1 = row16_f64(mn1, mn);
-      mx1 = row16_f64(mx1, mx);
-    }
+  const uint16_t oa = f16_sat(f64_to_f16<kRoundDown>(mn0), sat);
+  const double oda = f16_to_f64(oa);
+  const uint16_t sa = f16_sat(f64_to_f16<kRoundUp>((mx0 - oda) / qmax), sat);
+  const double sda = f16_to_f64(sa);
+  uint16_t ob = oa, sb = sa;
+  double odb = oda, sdb = sda;
+  if constexpr (G16) {
+    ob = f16_sat(f64_to_f16<kRoundDown>(mn1), sat);
+    odb = f16_to_f64(ob);
+    sb = f16_sat(f64_to_f16<kRoundUp>((mx1 - odb) / qmax), sat);
+    sdb = f16_to_f64(sb);
   }
-  if (!g16) {
-    mn1 = mn0;
-    mx1 = mx0;
-  }
-  const double qmax = (double)((1 << bits) - 1);
-  uint16_t o16[2], s16[2];
-  double od[2], sd[2];
-  for (int i = 0; i < (g16 ? 2 : 1); ++i) {
-    o16[i] = f16_sat(f64_to_f16(i ? mn1 : mn0, 1), sat);
-    od[i] = f16_to_f64(o16[i]);
-    s16[i] = f16_sat(f64_to_f16(((i ? mx1 : mx0) - od[i]) / qmax, 2), sat);
-    sd[i] = f16_to_f64(s16[i]);
-  }
-  if (!g16) {
-    o16[1] = o16[0]; s16[1] = s16[0];
-    od[1] = od[0]; sd[1] = sd[0];
-  }
-  uint32_t c0 = 0, c1 = 0;
-  if (sd[0] != 0.0) c0 = (uint32_t)fmin(fmax(rint((v0 - od[0]) / sd[0]), 0.0), qmax);
-  if (sd[1] != 0.0) c1 = (uint32_t)fmin(fmax(rint((v1 - od[1]) / sd[1]), 0.0), qmax);
-  d0 = od[0] + sd[0] * (double)c0;
-  d1 = od[1] + sd[1] * (double)c1;
-  uint8_t* row = codes + tok * (size_t)(D * bits / 8);
-  if (g16) {
+  const uint32_t c0 = code_of<BITS>(v0, oda, sda), c1 = code_of<BITS>(v1, odb, sdb);
+  d0 = oda + sda * (double)c0;
+  d1 = odb + sdb * (double)c1;
+  if constexpr (G16) {
     // one 32-bit word per group: element k at bit 16 (k / 8) + 2 (k mod 8)
     const int sh = 16 * (k >> 3) + 2 * (k & 7);
-    uint32_t wa = c0 << sh, wb = c1 << sh;
-    wa = group_or<16>(wa);
-    wb = group_or<16>(wb);
+    const uint32_t wa = group_or<16>(c0 << sh), wb = group_or<16>(c1 << sh);
     if (lane_on && k == 0) {
       *reinterpret_cast<uint2*>(row + gi * 8) = make_uint2(wa, wb);
-      *reinterpret_cast<uint2*>(meta + tok * (D / 16) + 2 * gi) =
-          make_uint2((uint32_t)o16[0] | ((uint32_t)s16[0] << 16), (uint32_t)o16[1] | ((uint32_t)s16[1] << 16));
+      *reinterpret_cast<uint2*>(mrow + 2 * gi) =
+          make_uint2((uint32_t)oa | ((uint32_t)sa << 16), (uint32_t)ob | ((uint32_t)sb << 16));
     }
-    return;
-  }
-  const int per = 16 / bits;                    // codes per 16-bit half-word
-  const int sh = bits * (k % per);
-  uint32_t word = (c0 << sh) | (c1 << (16 + sh));
-  word = per == 8 ? group_or<8>(word) : group_or<4>(word);
-  if (lane_on) {
-    if (k % per == 0) {
-      uint32_t* dst = reinterpret_cast<uint32_t*>(row + gi * 4 * bits);
-      dst[k / per] = word;
+  } else {
+    constexpr int per = 16 / BITS;             // codes per 16-bit half-word
+    const int sh = BITS * (k % per);
+    uint32_t word = (c0 << sh) | (c1 << (16 + sh));
+    word = group_or<per>(word);
+    if (lane_on) {
+      if (k % per == 0) reinterpret_cast<uint32_t*>(row + gi * 4 * BITS)[k / per] = word;
+      if (k == 0) mrow[gi] = (uint32_t)oa | ((uint32_t)sa << 16);
     }
-    if (k == 0) meta[tok * (D / 32) + gi] = (uint32_t)o16[0] | ((uint32_t)s16[0] << 16);
   }
 }
 
+// Component kinds of the append: INT2 or INT4 in groups of 32, INT2 in groups of 16.
+enum : int { kKind2 = 0, kKind4 = 1, kKind2h = 2 };
+__device__ __forceinline__ int kind_of(int bits, bool g16) { return g16 ? kKind2h : (bits == 4 ? kKind4 : kKind2); }
+
+// quantize_pair_t for a loop's kind known at run time (uniform over the wave);
+// codes and meta are the loop's buffers, tok the token's row in them.
 template <int D>
-__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
-  constexpr int NT = D / 16;   // 16-wide output column tiles
-  constexpr int NK = D / 4;    // k steps of the 16x16x4 instruction
-  constexpr int HP = D + 16;   // padded row of the transposed rotation in LDS
-  __shared__ float Ht[D * HP];                 // Ht[k][n] = H[n][k]
-  __shared__ double Zs[kWaves][16][D + 1];
+__device__ __forceinline__ void quantize_pair(double v0, double v1, int bits, bool g16, bool lane_on, int gi, int k,
+                                              uint8_t* codes, uint32_t* meta, size_t tok, double& d0, double& d1,
+                                              bool& sat) {
+  uint8_t* row = codes + tok * (size_t)(D * bits / 8);
+  uint32_t* mrow = meta + tok * (size_t)(g16 ? D / 16 : D / 32);
+  switch (kind_of(bits, g16)) {
+    case kKind4: quantize_pair_t<D, 4, false>(v0, v1, lane_on, gi, k, row, mrow, d0, d1, sat); break;
+    case kKind2h: quantize_pair_t<D, 2, true>(v0, v1, lane_on, gi, k, row, mrow, d0, d1, sat); break;
+    default: quantize_pair_t<D, 2, false>(v0, v1, lane_on, gi, k, row, mrow, d0, d1, sat); break;
+  }
+}
+
+// All NG 32-channel groups of one row: the row's pairs (z0[gi], z1[gi]) -> dequantized (d0, d1).
+template <int D, int BITS, bool G16>
+__device__ __forceinline__ void quantize_row_t(const double (&z0)[D / 32], const double (&z1)[D / 32], bool on, int k,
+                                               uint8_t* row, uint32_t* mrow, double (&d0)[D / 32], double (&d1)[D / 32],
+                                               bool& sat) {
+#pragma unroll
+  for (int gi = 0; gi < D / 32; ++gi) quantize_pair_t<D, BITS, G16>(z0[gi], z1[gi], on, gi, k, row, mrow, d0[gi], d1[gi], sat);
+}
+
+constexpr long long kAppendWorkgroups = 512;
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void append_kernel(AppendParams p) {
+  constexpr int NT = D / 16;        // 16-column tiles of the product
+  constexpr int NG = D / 32;        // 32-channel groups
+  constexpr int KB = D / 16;        // 4-step blocks of the contraction per lane row
+  constexpr int HS = D + 4;         // padded LDS row of the rotation (16-byte aligned)
+  constexpr int XW = D / 8;         // 32-bit words of a lane's D/4 bf16 operands
+  __shared__ float Hs[D * HS];      // Hs[n][k] = H[n][k]
   const int kv = blockIdx.z, h = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const float* Hg = p.rot[kv] + (size_t)h * D * D;
-  for (int idx = threadIdx.x; idx < D * D; idx += blockDim.x) {
-    const int n = idx / D, k = idx % D;
-    Ht[k * HP + n] = Hg[idx];
+  {
+    const float4* Hg = reinterpret_cast<const float4*>(p.rot[kv] + (size_t)h * D * D);
+    for (int idx = threadIdx.x; idx < D * D / 4; idx += kThreads) {
+      const int n = idx / (D / 4), c4 = idx % (D / 4);
+      *reinterpret_cast<float4*>(&Hs[n * HS + 4 * c4]) = Hg[idx];
+    }
   }
   __syncthreads();
 
-  const int L = p.L;
-  const int U = 16 / L;                        // (sequence, token) units per tile
-  const int units = p.B * p.n;
-  const int u0 = (blockIdx.x * kWaves + wave) * U;
-  if (u0 >= units) return;                     // no block-wide barrier follows
+  const int L = p.L, G = p.G, n = p.n;
+  const int units = p.B * n;
+  const int quads = (units + 3) / 4;
+  const int per_wg = (quads + gridDim.x - 1) / gridDim.x;
+  const int q_begin = blockIdx.x * per_wg;
+  const int q_end = min(q_begin + per_wg, quads);
+  const int npiece = (G + 3) / 4;   // pieces of at most 4 loops per loop group
+  const int tiles_per_quad = (L / G) * npiece;
+  const bool last = p.policy == RQ_POLICY_LAST_LOOP, chain = p.policy == RQ_POLICY_PREV_LOOP;
 
-  // ---- Z = X H^T on the matrix cores ----------------------------------------
-  const int m = lane & 15;
-  const int mu = m / L, mr = m % L;
-  const bool row_ok = mu < U && u0 + mu < units;
-  const int urow = row_ok ? u0 + mu : 0;
-  const int b_row = urow / p.n, i_row = urow % p.n;
-  const uint16_t* xrow =
-      p.kv + (((((size_t)kv * L + mr) * p.B + b_row) * p.H + h) * p.n + i_row) * (size_t)D;
-  d4 acc[NT];
-  for (int ct = 0; ct < NT; ++ct) acc[ct] = d4{0.0, 0.0, 0.0, 0.0};
-  for (int kk = 0; kk < NK; ++kk) {
-    const int k = kk * 4 + (lane >> 4);
-    const double a = row_ok ? bf16_to_f64(xrow[k]) : 0.0;
-    const float* hk = &Ht[k * HP + (lane & 15)];
-#pragma unroll
-    for (int ct = 0; ct < NT; ++ct)
-      acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)hk[ct * 16], acc[ct], 0, 0, 0);
-  }
-  // lane l, register j of column tile ct holds Z[4j + l/16][16 ct + l%16]
-#pragma unroll
-  for (int ct = 0; ct < NT; ++ct)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) Zs[wave][4 * j + (lane >> 4)][ct * 16 + (lane & 15)] = acc[ct][j];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  const int rsel = lane >> 4, k = lane & 15;   // unit within the quad; lane within its row
+  // operand row of this lane: unit l % 4, loop l % 16 / 4 of the piece, contraction block l / 16
+  const int a_unit = lane & 3, a_loop = (lane & 15) >> 2, a_blk = lane >> 4;
+  bool sat = false;
 
-  // ---- per unit: anchor, LS alpha, residuals ---------------------------------
-  const int gi = lane >> 4, k = lane & 15;
-  const bool lane_on = gi < D / 32;
-  const int e0 = lane_on ? 32 * gi + k : 0, e1 = e0 + 16;
-  for (int uu = 0; uu < U; ++uu) {
-    const int u = u0 + uu;
-    if (u >= units) break;
-    const int b = u / p.n, i = u % p.n;
-    const int t = p.pos[b] + i;
-    if (t < 0 || t >= p.T_max) {
-      if (lane == 0 && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_CAPACITY);
-      continue;
+  // tile tau of this wave's stream -> (quad, group start, first loop of the piece, loops in it)
+  // (tiles tau of a wave's stream: quad q_begin + wave + 4 (tau / tiles_per_quad))
+  auto tile_of = [&](int tau, int& quad, int& g0, int& l0, int& nl) {
+    quad = q_begin + wave + kWaves * (tau / tiles_per_quad);
+    const int rest = tau % tiles_per_quad;
+    const int g = rest / npiece, i = rest % npiece;
+    const int pc = last ? (i == 0 ? npiece - 1 : i - 1) : i;  // anchor piece first
+    g0 = g * G;
+    l0 = g0 + 4 * pc;
+    nl = min(4, g0 + G - l0);
+  };
+  auto load_x = [&](int tau, uint4 (&x)[XW / 4]) {
+    int quad, g0, l0, nl;
+    tile_of(tau, quad, g0, l0, nl);
+    const int u = quad * 4 + a_unit;
+    const bool ok = a_loop < nl && u < units;
+    const int uu = ok ? u : 0;
+    const int b = uu / n, i = uu % n;
+    const uint4* src = reinterpret_cast<const uint4*>(
+        p.kv + (((((size_t)kv * L + (ok ? l0 + a_loop : 0)) * p.B + b) * p.H + h) * n + i) * (size_t)D +
+        a_blk * (D / 4));
+#pragma unroll
+    for (int w = 0; w < XW / 4; ++w) x[w] = ok ? src[w] : make_uint4(0, 0, 0, 0);
+  };
+
+  const int my_quads = q_end - q_begin > wave ? (q_end - q_begin - wave + kWaves - 1) / kWaves : 0;
+  const int tiles = my_quads * tiles_per_quad;
+  double rf0[NG], rf1[NG], den = 0.0;   // reference of the current loop group (this lane's unit)
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) rf0[gi] = rf1[gi] = 0.0;
+  uint4 xa[XW / 4];
+  if (tiles > 0) load_x(0, xa);
+  for (int tau = 0; tau < tiles; ++tau) {
+    int quad, g0, l0, nl;
+    tile_of(tau, quad, g0, l0, nl);
+    // ---- Z of the piece on the matrix cores; the next tile's operands load meanwhile
+    d4 acc[NT];
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) acc[ct] = d4{0.0, 0.0, 0.0, 0.0};
+    uint32_t xw[XW];
+#pragma unroll
+    for (int w = 0; w < XW / 4; ++w) {
+      xw[4 * w] = xa[w].x; xw[4 * w + 1] = xa[w].y; xw[4 * w + 2] = xa[w].z; xw[4 * w + 3] = xa[w].w;
     }
-    size_t tok;
-    if (!cache_row(p.table, p.maxblk, p.lbs, p.num_blocks, p.H, p.T_max, b, h, t, tok)) {
-      if (lane == 0 && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_BLOCK);
-      continue;
-    }
-    const double(*Z)[D + 1] = &Zs[wave][uu * L];
-    bool sat = false;
-    // each loop group independently: its anchor, then the other loops of the group
-    for (int g0 = 0; g0 < L; g0 += p.G) {
-      const int a = (p.policy == RQ_POLICY_LAST_LOOP) ? g0 + p.G - 1 : g0;
-      double r0, r1;  // reference (reconstructed anchor, or previous loop) at e0, e1
-      quantize_pair<D>(Z[a][e0], Z[a][e1], p.bits[a], (p.g16 >> a) & 1, lane_on, gi, k, p.codes[kv][a],
-                       p.meta[kv][a], tok, r0, r1, sat);
-      if (!lane_on) r0 = r1 = 0.0;
-      double den_cur = wave_sum_f64(r0 * r0 + r1 * r1);
-      for (int r = g0; r < g0 + p.G; ++r) {
-        if (r == a) continue;
-        const double z0 = lane_on ? Z[r][e0] : 0.0, z1 = lane_on ? Z[r][e1] : 0.0;
-        const double num = wave_sum_f64(z0 * r0 + z1 * r1);
-        const double alpha = den_cur > 0.0 ? num / den_cur : 0.0;
-        const uint16_t a16 = f16_sat(f64_to_f16(alpha, 0), sat);
-        const double at = f16_to_f64(a16);
-        if (lane == 0) p.alpha[kv][r][tok] = a16;
-        double q0, q1;
-        quantize_pair<D>(z0 - at * r0, z1 - at * r1, p.bits[r], (p.g16 >> r) & 1, lane_on, gi, k, p.codes[kv][r],
-                         p.meta[kv][r], tok, q0, q1, sat);
-        if (p.policy == RQ_POLICY_PREV_LOOP) {  // zhat_r = alpha_r zhat_{r-1} + D(c_r)
-          r0 = lane_on ? at * r0 + q0 : 0.0;
-          r1 = lane_on ? at * r1 + q1 : 0.0;
-          den_cur = wave_sum_f64(r0 * r0 + r1 * r1);
+    if (tau + 1 < tiles) load_x(tau + 1, xa);
+    // rotation operands of contraction block kb + 1 are read from LDS while the
+    // products of block kb run; the scheduling barrier keeps the compiler from
+    // hoisting all blocks' reads (their registers would spill)
+    auto read_h = [&](int kb, float4 (&hb)[NT]) {
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct)
+        hb[ct] = *reinterpret_cast<const float4*>(&Hs[(16 * ct + k) * HS + a_blk * (D / 4) + 4 * kb]);
+    };
+    float4 hbuf[2][NT];
+    read_h(0, hbuf[0]);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      if (kb + 1 < KB) read_h(kb + 1, hbuf[(kb + 1) & 1]);
+      const float4(&hb)[NT] = hbuf[kb & 1];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t wv = xw[2 * kb + (q >> 1)];
+        const double a = (double)__uint_as_float((q & 1) ? (wv & 0xffff0000u) : (wv << 16));
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+          const float bq = q == 0 ? hb[ct].x : q == 1 ? hb[ct].y : q == 2 ? hb[ct].z : hb[ct].w;
+          acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)bq, acc[ct], 0, 0, 0);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (sat && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_RANGE);
+
+    // ---- this lane's unit and its cache row
+    const int u = quad * 4 + rsel;
+    bool on = u < units;
+    size_t tok = 0;
+    if (on) {
+      const int b = u / n, i = u % n;
+      const int t = p.pos[b] + i;
+      if (t < 0 || t >= p.T_max) {
+        on = false;
+        if (k == 0 && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_CAPACITY);
+      } else if (!cache_row(p.table, p.maxblk, p.lbs, p.num_blocks, p.H, p.T_max, b, h, t, tok)) {
+        on = false;
+        if (k == 0 && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_BLOCK);
+      }
+    }
+
+    // ---- quantization: the anchor first (when the piece holds it), then the
+    // other loops in order; one step per loop, the loop's column j of acc
+    // picked at run time so that the quantizer is instantiated once per kind
+    const int a = last ? g0 + G - 1 : g0;
+    const int ja = (a >= l0 && a < l0 + nl) ? a - l0 : -1;
+#pragma unroll 1
+    for (int st = 0; st < nl; ++st) {
+      const int j = ja < 0 ? st : (st == 0 ? ja : (st - 1 < ja ? st - 1 : st));
+      const int r = l0 + j;
+      double z0[NG], z1[NG];
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        z0[gi] = j == 0 ? acc[2 * gi][0] : j == 1 ? acc[2 * gi][1] : j == 2 ? acc[2 * gi][2] : acc[2 * gi][3];
+        z1[gi] = j == 0 ? acc[2 * gi + 1][0] : j == 1 ? acc[2 * gi + 1][1] : j == 2 ? acc[2 * gi + 1][2]
+                                                                                   : acc[2 * gi + 1][3];
+      }
+      const bool is_anchor = r == a;
+      double at = 0.0;
+      if (!is_anchor) {                          // LS alpha against the reference, residual
+        double s = 0.0;
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) s += z0[gi] * rf0[gi] + z1[gi] * rf1[gi];
+        const double num = row16_f64(on ? s : 0.0, [](double x, double y) { return x + y; });
+        const double alpha = den > 0.0 ? num / den : 0.0;
+        const uint16_t a16 = f16_sat(f64_to_f16<kRoundNearest>(alpha), sat);
+        at = f16_to_f64(a16);
+        if (on && k == 0) p.alpha[kv][r][tok] = a16;
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          z0[gi] = z0[gi] - at * rf0[gi];
+          z1[gi] = z1[gi] - at * rf1[gi];
+        }
+      }
+      const bool g16 = (p.g16 >> r) & 1;
+      uint8_t* row = p.codes[kv][r] + tok * (size_t)(D * p.bits[r] / 8);
+      uint32_t* mrow = p.meta[kv][r] + tok * (size_t)(g16 ? D / 16 : D / 32);
+      double q0[NG], q1[NG];
+      switch (kind_of(p.bits[r], g16)) {
+        case kKind4: quantize_row_t<D, 4, false>(z0, z1, on, k, row, mrow, q0, q1, sat); break;
+        case kKind2h: quantize_row_t<D, 2, true>(z0, z1, on, k, row, mrow, q0, q1, sat); break;
+        default: quantize_row_t<D, 2, false>(z0, z1, on, k, row, mrow, q0, q1, sat); break;
+      }
+      if (is_anchor || chain) {                  // the reference: A, or zhat_r = alpha_r zhat_{r-1} + D(c_r)
+        double s2 = 0.0;
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          rf0[gi] = on ? (is_anchor ? q0[gi] : at * rf0[gi] + q0[gi]) : 0.0;
+          rf1[gi] = on ? (is_anchor ? q1[gi] : at * rf1[gi] + q1[gi]) : 0.0;
+          s2 += rf0[gi] * rf0[gi] + rf1[gi] * rf1[gi];
+        }
+        den = row16_f64(s2, [](double x, double y) { return x + y; });
+      }
+    }
   }
+  if (sat && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_RANGE);
 }
 
 // Few-token path (decode-time store of the current token, short chunks): one
@@ -462,7 +531,7 @@ __global__ __launch_bounds__(256) void append_unit(UnitParams p) {
     const double den = dens[g];
     const double num = wave_sum_f64((lane_on ? zz0 : 0.0) * r0 + (lane_on ? zz1 : 0.0) * r1);
     const double alpha = den > 0.0 ? num / den : 0.0;
-    const uint16_t a16 = f16_sat(f64_to_f16(alpha, 0), sat);
+    const uint16_t a16 = f16_sat(f64_to_f16<kRoundNearest>(alpha), sat);
     at = f16_to_f64(a16);
     if (lane == 0) alpha_of(r)[tok] = a16;
     quantize_pair<D>(zz0 - at * r0, zz1 - at * r1, p.bits[r], (p.g16 >> r) & 1, lane_on, gi, kk, codes_of(r),
@@ -529,9 +598,14 @@ int launch_append_unit(const UnitParams& p, int D, void* stream) {
 
 int launch_append(const AppendParams& p, int D, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int U = 16 / p.L;
-  const long long tiles = ((long long)p.B * p.n + U - 1) / U;
-  const dim3 grid((unsigned)((tiles + kWaves - 1) / kWaves), (unsigned)p.H, 2);
+  // About two resident workgroups per compute unit in one round (the rotation
+  // takes 34-68 KB of LDS), each at least one quad per wave.
+  const long long quads = ((long long)p.B * p.n + 3) / 4;
+  long long chunks = kAppendWorkgroups / (2LL * p.H);
+  const long long most = (quads + kWaves - 1) / kWaves;
+  if (chunks > most) chunks = most;
+  if (chunks < 1) chunks = 1;
+  const dim3 grid((unsigned)chunks, (unsigned)p.H, 2);
   switch (D) {
     case 64: hipLaunchKernelGGL(append_kernel<64>, grid, dim3(kThreads), 0, s, p); break;
     case 96: hipLaunchKernelGGL(append_kernel<96>, grid, dim3(kThreads), 0, s, p); break;
