@@ -14,7 +14,13 @@ captured hipGraph.
 Reported next to it, in the same process and on the same logical inputs:
   * the BF16 decode baseline (rq_decode_attn_bf16 over the uncompressed cache);
   * the chained Previous-loop reference policy ([4,4,2,2], anchor on loop 1);
-  * per-call HIP-event timing of the dominant call for the roofline;
+  * per-call HIP-event timing of the dominant call for the roofline (and of the
+    same launch with the 21-bit rotated query);
+  * the prefill attention of one loop and the bulk store of the prompt;
+  * "configs": compact records of the other workload shapes (uniform INT2 at
+    4k, B1; the Huginn-shaped recurrence, B4, 4k; the 8k capacity shape with
+    RQ at batch 128 against BF16 at batch 32, its largest that fits), each with
+    16 decode steps;
   * the CPU oracle timed on a bounded sample (cpu_baseline).
 
 Other workloads of synth.WORKLOADS run with --workload, e.g. "huginn32_4k"
@@ -39,6 +45,7 @@ sys.path.insert(0, ROOT)
 METRIC = "decode-attn tokens/s + achieved HBM GB/s (% of peak) at 16k ctx, 4 loops"
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0            # dense bf16 matrix-core peak of the MI355X
+FP64_PEAK_TFLOPS = 78.6             # fp64 matrix-core peak of the MI355X
 
 
 def log(msg):
@@ -194,63 +201,28 @@ def summarize_profile(directory, title, command):
     return "\n".join(lines) + "\n"
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=64)
-    ap.add_argument("--warmup", type=int, default=4)
-    ap.add_argument("--workload", default="ouro_16k")
-    ap.add_argument("--layers", type=int, default=0, help="override layer count (0: workload's)")
-    ap.add_argument("--batch", type=int, default=0, help="override batch (0: workload's)")
-    ap.add_argument("--block-size", type=int, default=0,
-                    help="paged compressed caches with blocks of this many tokens over a shuffled pool (0: contiguous)")
-    ap.add_argument("--no-bf16", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--no-chained", action="store_true")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--call-reps", type=int, default=50)
-    ap.add_argument("--cpu-sample-units", type=int, default=0)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum timed CPU-oracle seconds")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run one plain 1 GiB read + 1 GiB write elementwise kernel (counter scaling)")
-    ap.add_argument("--summarize-profile", nargs=3, metavar=("DIR", "TITLE", "COMMAND"),
-                    help="print a text summary of rocprofv3 CSV output in DIR and exit")
-    args = ap.parse_args()
-    if args.summarize_profile:
-        print(summarize_profile(*args.summarize_profile), end="")
-        return
-
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py: this decode path runs on one GPU; --gpus {args.gpus} (WORLD_SIZE {world}) is "
-              "not supported (multi-GPU sharding is a design note, not built)", file=sys.stderr)
-        sys.exit(2)
-
+def measure(w, K, warmup, BS=0, want_rq=True, want_chained=True, want_bf16=True, want_percall=False,
+            call_reps=50):
+    """Build workload w's caches (untimed) and time K decode steps of the enabled
+    paths, each step captured as one HIP graph. Returns a dict of timings; every
+    device buffer is released when it returns."""
     import torch
 
     import decode_attention_quantize_amd as rq
     import synth
 
-    w = synth.WORKLOADS[args.workload]
-    if args.layers:
-        w = w.with_(layers=args.layers)
-    if args.batch:
-        w = w.with_(batch=args.batch)
-    B, H, D, L, T, K = w.batch, w.heads, w.D, w.L, w.T, args.steps
-    T_max = T + max(K, args.warmup)
-    BS = args.block_size
+    B, H, D, L, T = w.batch, w.heads, w.D, w.L, w.T
+    T_max = T + max(K, warmup)
     if BS:
         T_max = -(-T_max // BS) * BS
     dev = "cuda"
-    torch.cuda.set_device(0)
     scale = 1.0 / math.sqrt(D)
     bits, cbits = list(w.bits), list(w.chained_bits)
-
-    # ---------------------------------------------------------------- build (untimed)
-    t_build = time.time()
     G = w.loop_group
     gr, cgr = w.groups_for(bits), w.groups_for(cbits)
-    run_chained = not args.no_chained and (G or L) <= 4
+    chain_len = G or L
+    run_chained = want_chained and chain_len <= 4
+    t_build = time.time()
     table, nblocks = None, 0
     if BS:
         # a serving engine's block table: every sequence's blocks scattered over one pool
@@ -261,52 +233,54 @@ def main():
                         num_blocks=nblocks)
     d_ch = rq.make_desc(B, H, D, cbits, T_max, rq.POLICY_PREV_LOOP, group=cgr, loop_group=G, block_size=BS,
                         num_blocks=nblocks)
-    caches, chained, bf16, rots = [], [], [], []
+    caches, chained, bf16 = [], [], []
     # the BF16 caches of all layers in one tensor, so that one index copy stores a
     # step's current K/V of every layer
-    bf16_all = None if args.no_bf16 else torch.empty(w.layers, 2, L, B, H, T_max, D, dtype=torch.bfloat16,
-                                                     device=dev)
+    bf16_all = torch.empty(w.layers, 2, L, B, H, T_max, D, dtype=torch.bfloat16, device=dev) if want_bf16 else None
     kvcur = torch.empty(K, w.layers, 2, L, B, H, 1, D, dtype=torch.bfloat16, device=dev)
     qs = torch.empty(K, w.layers, L, B, H, D, dtype=torch.bfloat16, device=dev)
     pos0 = torch.zeros(B, dtype=torch.int32, device=dev)
+    n_cur = T_max - T
     for l in range(w.layers):
-        X = synth.kv(w, l, 0, T_max, device=dev)                      # [2][L][B][H][T_max][D]
+        # the prompt [0, T) and the decode steps' tokens [T, T_max), generated apart
+        # (the generator is seeded per 256-token chunk, so the values are those of one
+        # draw over [0, T_max)) to halve the temporary memory at the capacity shape
+        past = synth.kv(w, l, 0, T, device=dev)                       # [2][L][B][H][T][D]
+        cur = synth.kv(w, l, T, n_cur, device=dev)
         rk, rv = synth.rotation(w, l, 0), synth.rotation(w, l, 1)
-        past = X[..., :T, :].contiguous()
-        c = rq.LayerCache.allocate(d_rq, rk, rv, block_table=table)
-        rq.quantize_append(c, past, pos0, T)
-        caches.append(c)
+        if want_rq:
+            c = rq.LayerCache.allocate(d_rq, rk, rv, block_table=table)
+            rq.quantize_append(c, past, pos0, T)
+            caches.append(c)
         if run_chained:
             cc = rq.LayerCache.allocate(d_ch, rk, rv, block_table=table)
             rq.quantize_append(cc, past, pos0, T)
             chained.append(cc)
-        del past
         for k in range(K):
-            kvcur[k, l] = X[..., T + k:T + k + 1, :]
+            kvcur[k, l] = cur[..., k:k + 1, :]
             for r in range(L):
                 qs[k, l, r] = synth.query(w, l, r, k, device=dev)
-        if not args.no_bf16:
-            bf16_all[l].copy_(X)
+        if want_bf16:
+            bf16_all[l][..., :T, :].copy_(past)
+            bf16_all[l][..., T:, :].copy_(cur)
             bf16.append(bf16_all[l])
-        del X
+        del past, cur
         torch.cuda.synchronize()
         if l % 6 == 5 or l == w.layers - 1:
-            log(f"built layer {l + 1}/{w.layers} ({time.time() - t_build:.1f}s)")
+            log(f"{w.name} B{B}: built layer {l + 1}/{w.layers} ({time.time() - t_build:.1f}s)")
     ws = rq.alloc_workspace(d_rq)
     ws_ch = rq.alloc_workspace(d_ch)
     out = torch.empty(w.layers, L, B, H, D, dtype=torch.float32, device=dev)
     past_len = torch.full((B,), T, dtype=torch.int32, device=dev)
-    rq_bytes_gb = sum(c.nbytes() for c in caches) / 1e9
-    log(f"caches built: RQ {rq_bytes_gb:.2f} GB, BF16 {sum(x.numel() * 2 for x in bf16) / 1e9:.2f} GB, "
-        f"{time.time() - t_build:.1f}s")
+    log(f"{w.name} B{B}: caches built: RQ {sum(c.nbytes() for c in caches) / 1e9:.2f} GB, BF16 "
+        f"{sum(x.numel() * 2 for x in bf16) / 1e9:.2f} GB, {time.time() - t_build:.1f}s")
 
-    # ---------------------------------------------------------------- steps as graphs
     # One step, in the order a looped decoder runs it: for each loop r and layer
     # l, the attention call (streaming launch + combine) that the next layer's
     # query would depend on; after the final loop, the append of the current
     # token to every layer's cache (one call, shared launches); then
     # past_len += 1. All on one stream.
-    def rq_step(k, cs, d, workspace):
+    def rq_step(k, cs, workspace):
         for r in range(L):
             for l in range(w.layers):
                 kc = kvcur[k, l, 0, r, :, :, 0]
@@ -345,8 +319,8 @@ def main():
         torch.cuda.synchronize()
         return graphs
 
-    def run(graphs, warm):
-        for k in range(min(warm, K)):
+    def run(graphs):
+        for k in range(min(warmup, K)):
             graphs[k].replay()
         torch.cuda.synchronize()
         past_len.fill_(T)
@@ -360,19 +334,170 @@ def main():
         torch.cuda.synchronize()
         return dt
 
-    log("capturing RQ steps")
-    g_rq = capture(lambda k: rq_step(k, caches, d_rq, ws))
-    dt_rq = run(g_rq, args.warmup)
-    log(f"RQ: {K} steps in {dt_rq * 1e3:.2f} ms")
-    del g_rq
-
-    per_token_bytes = sum(call_bytes(D, bits, "last", r, G, gr) for r in range(L)) * H * w.layers
     mean_ctx = T + (K - 1) / 2.0
-    step_bytes = per_token_bytes * B * mean_ctx
+    res = {"w": w, "K": K, "mean_ctx": mean_ctx}
+    if want_rq:
+        log(f"{w.name} B{B}: capturing RQ steps")
+        g_rq = capture(lambda k: rq_step(k, caches, ws))
+        res["rq_s"] = run(g_rq)
+        del g_rq
+        res["rq_bytes"] = sum(call_bytes(D, bits, "last", r, G, gr) for r in range(L)) * H * w.layers * B * mean_ctx
+        log(f"{w.name} B{B}: RQ {K} steps in {res['rq_s'] * 1e3:.2f} ms")
+    if want_chained and chain_len > 4:
+        res["chained_skipped"] = f"chains of {chain_len} components; the decode kernels read at most 4 per call"
+    elif run_chained:
+        log(f"{w.name} B{B}: capturing chained steps")
+        g_ch = capture(lambda k: rq_step(k, chained, ws_ch))
+        res["ch_s"] = run(g_ch)
+        del g_ch
+        res["ch_bytes"] = sum(call_bytes(D, cbits, "prev", r, G, cgr) for r in range(L)) * H * w.layers * B * mean_ctx
+        log(f"{w.name} B{B}: chained {K} steps in {res['ch_s'] * 1e3:.2f} ms")
+    if want_bf16:
+        log(f"{w.name} B{B}: capturing BF16 steps")
+        g_bf = capture(bf16_step)
+        res["bf_s"] = run(g_bf)
+        del g_bf
+        res["bf_bytes"] = 2 * L * D * 2 * H * w.layers * B * mean_ctx
+        log(f"{w.name} B{B}: bf16 {K} steps in {res['bf_s'] * 1e3:.2f} ms")
+
+    if want_percall and want_rq:
+        # The streaming kernel (rq_decode_attn_partial's single launch) of each loop
+        # of the first group is timed alone: `call_reps` launches (cycling over the
+        # layers' caches) captured in a graph, as the steps are, and replayed between
+        # two HIP events on the stream the graph is launched on. The combine launch
+        # and whole calls are timed the same way.
+        stream = torch.cuda.current_stream()
+
+        def events(fn):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                for i in range(call_reps):
+                    fn(i)
+            for _ in range(3):               # warm the clocks after the host-side capture
+                g.replay()
+            torch.cuda.synchronize()
+            times = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+                e1.synchronize()
+                times.append(e0.elapsed_time(e1) / call_reps)
+            del g
+            return sorted(times)[2]          # median of five replays
+
+        percall = {}
+        for r in range(G or L):                       # every loop group has the same shape
+            kc = kvcur[0, 0, 0, r, :, :, 0]
+            vc = kvcur[0, 0, 1, r, :, :, 0]
+            nbytes = call_bytes(D, bits, "last", r, G, gr) * B * H * T
+            ms_k = events(lambda i: rq.decode_attn_partial(caches[i % w.layers], r, qs[0, 0, r], past_len, scale,
+                                                           ws))
+            ms_c = events(lambda i: rq.decode_combine(d_rq, caches[i % w.layers].rot[1], qs[0, 0, r], kc, vc,
+                                                      past_len, scale, out[0, r], ws))
+            ms_call = events(lambda i: rq.decode_attn(caches[i % w.layers], r, qs[0, 0, r], kc, vc, past_len, scale,
+                                                      out[0, r], ws))
+            entry = {"kernel_ms": ms_k, "combine_ms": ms_c, "call_ms": ms_call, "bytes": nbytes,
+                     "kernel_gbps": nbytes / (ms_k * 1e-3) / 1e9}
+            if r == 0:
+                # the same launch with the 21-bit rotated query (RQ_FLAG_PRECISE_QUERY)
+                ms_p = events(lambda i: rq.decode_attn_partial(caches[i % w.layers], r, qs[0, 0, r], past_len,
+                                                               scale, ws, flags=rq.FLAG_PRECISE_QUERY))
+                entry["precise_query_kernel_ms"] = ms_p
+            percall[r] = entry
+        res["percall"] = percall
+    del caches, chained, bf16, bf16_all, kvcur, qs, ws, ws_ch, out
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def sub_record(res, label):
+    """Compact record of one workload's measure(): tokens/s, the step's algorithmic
+    HBM rate and fraction of peak, and the comparators."""
+    w, K = res["w"], res["K"]
+    rec = {"workload": w.name, "label": label, "layers": w.layers, "batch": w.batch, "heads": w.heads,
+           "head_dim": w.D, "loops": w.L, "loop_group": w.loop_group or w.L, "context": w.T, "bits": list(w.bits),
+           "steps": K}
+    if "rq_s" in res:
+        t = res["rq_s"] / K
+        rec.update({"value": w.batch * K / res["rq_s"], "unit": "tokens/s", "ms_per_step": t * 1e3,
+                    "hbm_gbps_step": res["rq_bytes"] / t / 1e9, "hbm_frac_step": res["rq_bytes"] / t / 1e9 / HBM_PEAK_GBPS})
+    if "ch_s" in res:
+        rec["chained"] = {"value": w.batch * K / res["ch_s"], "ms_per_step": res["ch_s"] / K * 1e3,
+                          "rq_speedup_over_chained": res["ch_s"] / res["rq_s"]}
+    if "chained_skipped" in res:
+        rec["chained"] = {"skipped": res["chained_skipped"]}
+    if "bf_s" in res:
+        t = res["bf_s"] / K
+        rec["bf16"] = {"value": w.batch * K / res["bf_s"], "ms_per_step": t * 1e3,
+                       "hbm_frac_step": res["bf_bytes"] / t / 1e9 / HBM_PEAK_GBPS}
+        if "rq_s" in res:
+            rec["bf16"]["rq_speedup_over_bf16"] = res["bf_s"] / res["rq_s"]
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--workload", default="ouro_16k")
+    ap.add_argument("--layers", type=int, default=0, help="override layer count (0: workload's)")
+    ap.add_argument("--batch", type=int, default=0, help="override batch (0: workload's)")
+    ap.add_argument("--block-size", type=int, default=0,
+                    help="paged compressed caches with blocks of this many tokens over a shuffled pool (0: contiguous)")
+    ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-chained", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workload shapes (uniform INT2 4k, Huginn-shaped 4k, capacity 8k)")
+    ap.add_argument("--config-steps", type=int, default=16, help="decode steps of each other workload shape")
+    ap.add_argument("--call-reps", type=int, default=50)
+    ap.add_argument("--cpu-sample-units", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum timed CPU-oracle seconds")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 1 GiB read + 1 GiB write elementwise kernel (counter scaling)")
+    ap.add_argument("--summarize-profile", nargs=3, metavar=("DIR", "TITLE", "COMMAND"),
+                    help="print a text summary of rocprofv3 CSV output in DIR and exit")
+    args = ap.parse_args()
+    if args.summarize_profile:
+        print(summarize_profile(*args.summarize_profile), end="")
+        return
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this decode path runs on one GPU; --gpus {args.gpus} (WORLD_SIZE {world}) is "
+              "not supported (multi-GPU sharding is a design note, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import decode_attention_quantize_amd as rq
+    import synth
+
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[args.workload]
+    if args.layers:
+        w = w.with_(layers=args.layers)
+    if args.batch:
+        w = w.with_(batch=args.batch)
+    B, H, D, L, T, K = w.batch, w.heads, w.D, w.L, w.T, args.steps
+    BS = args.block_size
+    bits = list(w.bits)
+    G = w.loop_group
+    gr = w.groups_for(bits)
+
+    res = measure(w, K, args.warmup, BS, want_rq=True, want_chained=not args.no_chained,
+                  want_bf16=not args.no_bf16, want_percall=True, call_reps=args.call_reps)
+    dt_rq = res["rq_s"]
+    step_bytes = res["rq_bytes"]
     result = {
         "metric": METRIC, "value": B * K / dt_rq, "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": dt_rq * 1e3 / K, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "vs_baseline": None, "dtype": "int8+fp32", "data": "synthetic",
         "config": {"workload": w.name, "layers": w.layers, "batch": B, "heads": H, "head_dim": D, "loops": L,
                    "loop_group": G or L, "context": T, "bits": bits, "group": gr, "block_size": BS,
                    "codes": "int2/int4 + fp16 scale/offset + fp16 alpha",
@@ -382,76 +507,22 @@ def main():
         "hbm_frac_step": step_bytes / (dt_rq / K) / 1e9 / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": step_bytes,
     }
-
-    chain_len = G or L
-    if not args.no_chained and chain_len > 4:
-        # the fused decode kernels take at most four stored components per call
-        log(f"chained comparator skipped: chains of {chain_len} components")
-        result["chained"] = {"policy": "previous-loop", "skipped": f"chains of {chain_len} components; the "
-                             "decode kernels read at most 4 per call"}
-    elif run_chained:
-        log("capturing chained steps")
-        g_ch = capture(lambda k: rq_step(k, chained, d_ch, ws_ch))
-        dt_ch = run(g_ch, args.warmup)
-        del g_ch
-        ch_bytes = sum(call_bytes(D, cbits, "prev", r, G, cgr) for r in range(L)) * H * w.layers * B * mean_ctx
-        result["chained"] = {"policy": "previous-loop", "bits": cbits, "value": B * K / dt_ch,
+    if "chained_skipped" in res:
+        log(f"chained comparator skipped: {res['chained_skipped']}")
+        result["chained"] = {"policy": "previous-loop", "skipped": res["chained_skipped"]}
+    elif "ch_s" in res:
+        dt_ch = res["ch_s"]
+        result["chained"] = {"policy": "previous-loop", "bits": list(w.chained_bits), "value": B * K / dt_ch,
                              "unit": "tokens/s", "ms_per_step": dt_ch * 1e3 / K,
-                             "hbm_gbps_step": ch_bytes / (dt_ch / K) / 1e9,
+                             "hbm_gbps_step": res["ch_bytes"] / (dt_ch / K) / 1e9,
                              "rq_speedup_over_chained": dt_ch / dt_rq}
-        log(f"chained: {K} steps in {dt_ch * 1e3:.2f} ms")
-
-    if not args.no_bf16:
-        log("capturing BF16 steps")
-        g_bf = capture(bf16_step)
-        dt_bf = run(g_bf, args.warmup)
-        del g_bf
-        bf_bytes = 2 * L * D * 2 * H * w.layers * B * mean_ctx
+    if "bf_s" in res:
+        dt_bf = res["bf_s"]
         result["bf16"] = {"value": B * K / dt_bf, "unit": "tokens/s", "ms_per_step": dt_bf * 1e3 / K,
-                          "hbm_gbps_step": bf_bytes / (dt_bf / K) / 1e9,
+                          "hbm_gbps_step": res["bf_bytes"] / (dt_bf / K) / 1e9,
                           "rq_speedup_over_bf16": dt_bf / dt_rq}
-        log(f"bf16: {K} steps in {dt_bf * 1e3:.2f} ms")
 
-    # ---------------------------------------------------------------- dominant kernel, HIP events
-    # The streaming kernel (rq_decode_attn_partial's single launch) of loops 1-2
-    # (INT4 anchor + INT2 residual) is the largest share of the step. It is timed
-    # alone: `reps` launches (cycling over the layers' caches) captured in a graph,
-    # as the steps are, and replayed between two HIP events on the stream the
-    # graph is launched on. The combine launch and whole calls are timed the same way.
-    reps = args.call_reps
-    stream = torch.cuda.current_stream()
-
-    def events(fn):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=side):
-            for i in range(reps):
-                fn(i)
-        for _ in range(3):               # warm the clocks after the host-side capture
-            g.replay()
-        torch.cuda.synchronize()
-        times = []
-        for _ in range(5):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-            e1.synchronize()
-            times.append(e0.elapsed_time(e1) / reps)
-        del g
-        return sorted(times)[2]          # median of five replays
-
-    percall = {}
-    for r in range(G or L):                       # every loop group has the same shape
-        kc = kvcur[0, 0, 0, r, :, :, 0]
-        vc = kvcur[0, 0, 1, r, :, :, 0]
-        nbytes = call_bytes(D, bits, "last", r, G, gr) * B * H * T
-        ms_k = events(lambda i: rq.decode_attn_partial(caches[i % w.layers], r, qs[0, 0, r], past_len, scale, ws))
-        ms_c = events(lambda i: rq.decode_combine(d_rq, caches[i % w.layers].rot[1], qs[0, 0, r], kc, vc, past_len,
-                                                  scale, out[0, r], ws))
-        ms_call = events(lambda i: rq.decode_attn(caches[i % w.layers], r, qs[0, 0, r], kc, vc, past_len, scale,
-                                                  out[0, r], ws))
-        percall[r] = {"kernel_ms": ms_k, "combine_ms": ms_c, "call_ms": ms_call, "bytes": nbytes,
-                      "kernel_gbps": nbytes / (ms_k * 1e-3) / 1e9}
+    percall = res["percall"]
     dom = percall[0]
     traffic = None if BS else profiled_traffic(w.name)
     result["roofline"] = {"bound": "hbm", "achieved": dom["kernel_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -468,31 +539,38 @@ def main():
     # rq_prefill_attn over the workload's prompt (B x H x T tokens, one loop): the
     # step that precedes decode (§4.2 "Prefill"). Algorithmic flops: 2 D per
     # (query, visible key) for the scores and 2 D for the value sum, T (T + 1) / 2
-    # visible pairs per (b, h) under the causal mask.
+    # visible pairs per (b, h) under the causal mask. The bulk store of the prompt
+    # after the final loop (rq_quantize_append of T tokens, one layer) is timed
+    # beside it against the fp64 matrix-core peak (algorithmic flops: 2 D^2 per
+    # rotated row, 2 L B H T rows).
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
     if not args.no_prefill:
-        del caches, chained, bf16, bf16_all
-        torch.cuda.empty_cache()
         g = torch.Generator(device=dev).manual_seed(7)
         pq = torch.randn(B, H, T, D, generator=g, device=dev).to(torch.bfloat16)
         Xp = synth.kv(w, 0, 0, T, device=dev)
         pk, pv = Xp[0, 0].contiguous(), Xp[1, 0].contiguous()
-        del Xp
         pout = torch.empty(B, H, T, D, dtype=torch.float32, device=dev)
         plens = torch.full((B,), T, dtype=torch.int32, device=dev)
-        pws = rq.alloc_prefill_workspace(d_rq, T)
-        preps = 5
-        for _ in range(2):
-            rq.prefill_attn(d_rq, pq, pk, pv, plens, scale, pout, pws)
-        torch.cuda.synchronize()
-        times = []
-        for _ in range(preps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            rq.prefill_attn(d_rq, pq, pk, pv, plens, scale, pout, pws)
-            e1.record(stream)
-            e1.synchronize()
-            times.append(e0.elapsed_time(e1))
-        ms = sorted(times)[preps // 2]
+        d_p = rq.make_desc(B, H, D, bits, T, rq.POLICY_LAST_LOOP, group=gr, loop_group=G)
+        pws = rq.alloc_prefill_workspace(d_p, T)
+        scale = 1.0 / math.sqrt(D)
+
+        def timed(fn, reps=5, warm=2):
+            for _ in range(warm):
+                fn()
+            torch.cuda.synchronize()
+            times = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                e1.synchronize()
+                times.append(e0.elapsed_time(e1))
+            return sorted(times)[reps // 2]
+
+        ms = timed(lambda: rq.prefill_attn(d_p, pq, pk, pv, plens, scale, pout, pws))
         flops = 4.0 * D * (T * (T + 1) / 2) * B * H
         result["prefill"] = {"kernel": f"prefill_vt_kernel<{D}> + prefill_attn_kernel<{D}> (rq_prefill_attn, "
                                        "one loop, causal; time of both launches)",
@@ -502,6 +580,40 @@ def main():
                              "prompt_tokens_per_s": B * T / (ms * 1e-3)}
         log(f"prefill: {ms:.2f} ms per loop-layer, {result['prefill']['tflops']:.0f} TFLOP/s")
         del pq, pk, pv, pout, pws
+        cache = rq.LayerCache.allocate(d_p, synth.rotation(w, 0, 0), synth.rotation(w, 0, 1))
+        pos0 = torch.zeros(B, dtype=torch.int32, device=dev)
+        ms_a = timed(lambda: rq.quantize_append(cache, Xp, pos0, T), reps=3, warm=1)
+        aflops = 2.0 * D * D * 2 * L * B * H * T
+        result["prompt_store"] = {"kernel": f"append_kernel<{D}> (rq_quantize_append of the {T}-token prompt, one "
+                                            "layer, all loops, K and V)",
+                                  "ms_per_launch": ms_a, "flops_per_launch": aflops,
+                                  "tflops": aflops / (ms_a * 1e-3) / 1e12, "bound": "mfma",
+                                  "peak_tflops": FP64_PEAK_TFLOPS, "frac": aflops / (ms_a * 1e-3) / 1e12 / FP64_PEAK_TFLOPS}
+        log(f"prompt store: {ms_a:.2f} ms per layer, {result['prompt_store']['tflops']:.1f} TFLOP/s fp64")
+        del cache, Xp
+        torch.cuda.empty_cache()
+
+    # ---------------------------------------------------------------- the other workload shapes
+    # Uniform INT2 at 4k (B1: fixed per-call costs dominate), the Huginn-shaped
+    # recurrence (8 loops in one group, D96, 55 heads) and the 8k capacity shape:
+    # RQ at the largest batch the sweep runs (128) against BF16 at the largest
+    # batch whose cache fits (32), each with fewer steps than the headline.
+    if not args.no_configs and not (args.layers or args.batch or BS):
+        cs = args.config_steps
+        configs = {}
+        for name, label in (("ouro_int2_4k", "uniform INT2, B1, 4k"), ("huginn_4k", "Huginn-shaped, B4, 4k")):
+            r = measure(synth.WORKLOADS[name], cs, 2, 0, want_rq=True, want_chained=True, want_bf16=True)
+            configs[name] = sub_record(r, label)
+        cap = synth.WORKLOADS["ouro_8k_capacity"]
+        r_rq = measure(cap.with_(batch=128), cs, 2, 0, want_rq=True, want_chained=False, want_bf16=False)
+        r_bf = measure(cap.with_(batch=32), cs, 2, 0, want_rq=False, want_chained=False, want_bf16=True)
+        rec = sub_record(r_rq, "capacity 8k: RQ at batch 128")
+        bf = sub_record(r_bf, "capacity 8k: BF16 at batch 32")["bf16"]
+        bf["batch"] = 32
+        rec["bf16_at_its_largest_batch"] = bf
+        rec["rq_peak_over_bf16_peak"] = rec["value"] / bf["value"]
+        configs["ouro_8k_capacity"] = rec
+        result["configs"] = configs
 
     if args.calibrate_copy:
         # a plain streaming kernel of known size for scaling the HBM counters:
@@ -515,7 +627,7 @@ def main():
     # ---------------------------------------------------------------- CPU oracle baseline
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, bits, args.cpu_sample_units, args.cpu_seconds, torch, synth,
-                                              scale)
+                                              1.0 / math.sqrt(D))
 
     print(json.dumps(result), flush=True)
 
@@ -530,7 +642,11 @@ def cpu_baseline(w, bits, units, min_seconds, torch, synth, scale):
 
     import oracle as O
 
-    cores = min(16, os.cpu_count() or 1)
+    # every host core this process may run on, within the CPU share the host grants
+    # it (OMP_NUM_THREADS where the host sets one)
+    visible = len(os.sched_getaffinity(0))
+    share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    cores = min(visible, share) if share > 0 else visible
     units = units or w.batch * w.heads
     T, L, D = w.T, w.L, w.D
     pairs = [(u // w.heads % w.batch, u % w.heads) for u in range(units)]
@@ -569,7 +685,8 @@ def cpu_baseline(w, bits, units, min_seconds, torch, synth, scale):
     per_pass = dt / passes
     full = per_pass * (w.batch * w.heads * w.layers) / units
     log(f"cpu baseline: {units} (b,h) series x {L} loops, {passes} passes in {dt:.2f}s on {cores} threads")
-    return {"value": w.batch / full, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": w.batch / full, "unit": "tokens/s", "cores": cores, "cores_visible": visible,
+            "cores_share": share or None, "kind": "oracle",
             "sample": f"{units} (batch, head) series of layer 0 at {T} cached tokens: all {L} loops of "
                       f"fp64 oracle attention plus one-token quantize-append, on {cores} threads, "
                       f"{passes} passes; per-pass time scaled by {w.batch * w.heads * w.layers}/{units}",
