@@ -46,6 +46,7 @@ METRIC = "decode-attn tokens/s + achieved HBM GB/s (% of peak) at 16k ctx, 4 loo
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0            # dense bf16 matrix-core peak of the MI355X
 FP64_PEAK_TFLOPS = 78.6             # fp64 matrix-core peak of the MI355X
+MAX_CHAIN = 8                        # stored components one decode call reads at most
 
 
 def log(msg):
@@ -221,7 +222,7 @@ def measure(w, K, warmup, BS=0, want_rq=True, want_chained=True, want_bf16=True,
     G = w.loop_group
     gr, cgr = w.groups_for(bits), w.groups_for(cbits)
     chain_len = G or L
-    run_chained = want_chained and chain_len <= 4
+    run_chained = want_chained and chain_len <= MAX_CHAIN
     t_build = time.time()
     table, nblocks = None, 0
     if BS:
@@ -343,8 +344,9 @@ def measure(w, K, warmup, BS=0, want_rq=True, want_chained=True, want_bf16=True,
         del g_rq
         res["rq_bytes"] = sum(call_bytes(D, bits, "last", r, G, gr) for r in range(L)) * H * w.layers * B * mean_ctx
         log(f"{w.name} B{B}: RQ {K} steps in {res['rq_s'] * 1e3:.2f} ms")
-    if want_chained and chain_len > 4:
-        res["chained_skipped"] = f"chains of {chain_len} components; the decode kernels read at most 4 per call"
+    if want_chained and chain_len > MAX_CHAIN:
+        res["chained_skipped"] = (f"chains of {chain_len} components; the decode kernels read at most {MAX_CHAIN} "
+                                  "per call")
     elif run_chained:
         log(f"{w.name} B{B}: capturing chained steps")
         g_ch = capture(lambda k: rq_step(k, chained, ws_ch))

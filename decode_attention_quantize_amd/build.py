@@ -21,6 +21,7 @@ SOURCES = {
     "rq_append.hip": ["-ffp-contract=off", "-fno-honor-nans", "-mno-amdgpu-ieee"],
     "rq_decode.hip": [],
     "rq_decode_paged.hip": [],
+    "rq_decode_long.hip": [],
     "rq_decode_bf16.hip": [],
     "rq_prefill.hip": [],
 }
@@ -39,7 +40,7 @@ def _compile(src: str, build_dir: str, extra: tuple) -> str:
     return obj
 
 
-def build(jobs: int = 4, out: str = LIB, extra_flags=(), build_dir: str = BUILD) -> str:
+def build(jobs: int = 6, out: str = LIB, extra_flags=(), build_dir: str = BUILD) -> str:
     """Compile every source and link `out` (default: the in-tree librq.so)."""
     os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=jobs) as ex:

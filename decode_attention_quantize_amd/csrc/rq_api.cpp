@@ -160,7 +160,7 @@ const char* rq_status_str(rq_status s) {
     case RQ_E_BITS: return "unsupported bit width or group size (bits 2 or 4; group 32, or 16 for 2 bits)";
     case RQ_E_CAPACITY: return "size exceeds max_tokens";
     case RQ_E_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
-    case RQ_E_UNSUPPORTED: return "no kernel for this combination (e.g. more than 4 chained components)";
+    case RQ_E_UNSUPPORTED: return "no kernel for this combination (e.g. a chain of more than 8 components, or of more than 4 in a paged cache)";
     case RQ_E_HIP: return "HIP launch failed";
     case RQ_E_POLICY: return "unknown reference policy";
     case RQ_E_LOOP: return "loop index out of range";
@@ -361,7 +361,7 @@ rq_status decode_partial(const rq_desc* d, const rq_layer_cache* c, int32_t loop
   int bits[kMaxComp];  // component kinds: bit width, plus 8 for INT2 in groups of 16
   for (int i = 0; i < nc; ++i) bits[i] = d->bits[loops[i]] | (d->group[loops[i]] == 16 ? 8 : 0);
   const int limbs = (d->flags & RQ_FLAG_PRECISE_QUERY) ? 3 : 2;
-  if (!have_decode_kernel(d->head_dim, nc, bits, limbs)) return RQ_E_UNSUPPORTED;
+  if (!have_decode_kernel(d->head_dim, nc, bits, limbs, d->block_size != 0)) return RQ_E_UNSUPPORTED;
 
   const SplitPlan sp = split_plan(d);
   DecodeParams p;

@@ -121,11 +121,13 @@ const PlanEntry kTable[] = {RQ_PLANS(64), RQ_PLANS(96), RQ_PLANS(128)};
 
 }  // namespace
 
-bool have_decode_kernel(int D, int nc, const int* bits, int limbs) {
+bool have_decode_kernel(int D, int nc, const int* bits, int limbs, bool paged) {
+  if (nc > 4) return !paged && have_decode_kernel_long(D, nc, bits, limbs);
   return find_plan(kTable, D, nc, bits, limbs) != nullptr;
 }
 
 int launch_decode(const DecodeParams& p, int D, int nc, const int* bits, int limbs, int nsplit, void* stream) {
+  if (nc > 4) return launch_decode_long(p, D, nc, bits, limbs, nsplit, stream);
   if (p.table) return launch_decode_paged(p, D, nc, bits, limbs, nsplit, stream);
   const PlanEntry* e = find_plan(kTable, D, nc, bits, limbs);
   if (!e) return -1;

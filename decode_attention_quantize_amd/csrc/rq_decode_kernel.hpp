@@ -335,20 +335,48 @@ __device__ __forceinline__ void load_comp(CompTile<K>& T, const CompRsrc& r, boo
   }
 }
 
+// Calls f(integral_constant<int, I>) for I = B .. E-1.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Tile data of up to kMaxComp components (members past NC are never used).
 template <int D, int NC, uint32_t CB>
 struct Tile {
   CompTile<ckind<CB, 0>()> c0;
   CompTile<ckind<CB, (NC > 1 ? 1 : 0)>()> c1;
   CompTile<ckind<CB, (NC > 2 ? 2 : 0)>()> c2;
   CompTile<ckind<CB, (NC > 3 ? 3 : 0)>()> c3;
+  CompTile<ckind<CB, (NC > 4 ? 4 : 0)>()> c4;
+  CompTile<ckind<CB, (NC > 5 ? 5 : 0)>()> c5;
+  CompTile<ckind<CB, (NC > 6 ? 6 : 0)>()> c6;
+  CompTile<ckind<CB, (NC > 7 ? 7 : 0)>()> c7;
 };
+static_assert(kMaxComp == 8, "Tile holds eight components");
+
+// Component I of a tile.
+template <int I, class T>
+__device__ __forceinline__ auto& tc(T& t) {
+  if constexpr (I == 0) return t.c0;
+  else if constexpr (I == 1) return t.c1;
+  else if constexpr (I == 2) return t.c2;
+  else if constexpr (I == 3) return t.c3;
+  else if constexpr (I == 4) return t.c4;
+  else if constexpr (I == 5) return t.c5;
+  else if constexpr (I == 6) return t.c6;
+  else return t.c7;
+}
 
 template <int D, int NC, uint32_t CB, bool SEP1>
 __device__ __forceinline__ void load_tile(Tile<D, NC, CB>& T, const CompRsrc (&R)[NC], const Offs& o) {
-  load_comp<D, ckind<CB, 0>(), SEP1>(T.c0, R[0], false, o);
-  if constexpr (NC > 1) load_comp<D, ckind<CB, 1>(), SEP1>(T.c1, R[1], true, o);
-  if constexpr (NC > 2) load_comp<D, ckind<CB, 2>(), SEP1>(T.c2, R[2], true, o);
-  if constexpr (NC > 3) load_comp<D, ckind<CB, 3>(), SEP1>(T.c3, R[3], true, o);
+  static_for<0, NC>([&](auto ic) {
+    constexpr int c = decltype(ic)::value;
+    load_comp<D, ckind<CB, c>(), SEP1>(tc<c>(T), R[c], c > 0, o);
+  });
 }
 
 // Waves per SIMD the register budget is tuned for: three for plans whose tile
@@ -359,6 +387,7 @@ template <int NC, uint32_t CB, int LIMBS>
 constexpr int waves_for() {
   int bits = 0;
   for (int c = 0; c < NC; ++c) bits += kbits((int)((CB >> (4 * c)) & 0xF));
+  if (NC > 4) return 1;                        // long chains: two tiles of up to eight components
   if (LIMBS > 2) return 2;
   return (NC <= 2 && bits <= 6) ? RQ_WAVES_SMALL : 2;
 }
@@ -455,10 +484,10 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   const bool lane_on = pi < TPW;
   const int gsel = lane_on ? gi : 0;
   CompRsrc R[NC];
-  R[0] = comp_rsrc<D, ckind<CB, 0>()>(p, 0, row0, ntok);
-  if constexpr (NC > 1) R[1] = comp_rsrc<D, ckind<CB, (NC > 1 ? 1 : 0)>()>(p, 1, row0, ntok);
-  if constexpr (NC > 2) R[2] = comp_rsrc<D, ckind<CB, (NC > 2 ? 2 : 0)>()>(p, 2, row0, ntok);
-  if constexpr (NC > 3) R[3] = comp_rsrc<D, ckind<CB, (NC > 3 ? 3 : 0)>()>(p, 3, row0, ntok);
+  static_for<0, NC>([&](auto ic) {
+    constexpr int c = decltype(ic)::value;
+    R[c] = comp_rsrc<D, ckind<CB, c>()>(p, c, row0, ntok);
+  });
 
   constexpr int STRIDE = kWaves * TILE;  // tokens between a wave's consecutive tiles
   // Paged: the block ids of a tile's two tokens are loaded DEPTH fetches ahead
@@ -650,22 +679,19 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
         kp1[c] = fmaf(f16hi(C.km1[0]) * qscale, d1, f16lo(C.km1[0]) * qsum);
       }
     };
-    kpart(T.c0, 0, std::integral_constant<int, ckind<CB, 0>()>{});
-    if constexpr (NC > 1) kpart(T.c1, 1, std::integral_constant<int, ckind<CB, 1>()>{});
-    if constexpr (NC > 2) kpart(T.c2, 2, std::integral_constant<int, ckind<CB, 2>()>{});
-    if constexpr (NC > 3) kpart(T.c3, 3, std::integral_constant<int, ckind<CB, 3>()>{});
+    static_for<0, NC>([&](auto ic) {
+      constexpr int c = decltype(ic)::value;
+      kpart(tc<c>(T), c, std::integral_constant<int, ckind<CB, c>()>{});
+    });
+    // beta_c = prod_{j > c} alpha_j, from the last component down (the product
+    // starts with alpha_{NC-1} itself: multiplying by 1.0f first is exact)
     kb0[NC - 1] = kb1[NC - 1] = vb0[NC - 1] = vb1[NC - 1] = 1.0f;
-    if constexpr (NC > 3) {
-      kb0[2] = f16u(T.c3.ka0); kb1[2] = f16u(T.c3.ka1); vb0[2] = f16u(T.c3.va0); vb1[2] = f16u(T.c3.va1);
-    }
-    if constexpr (NC > 2) {
-      kb0[1] = kb0[2] * f16u(T.c2.ka0); kb1[1] = kb1[2] * f16u(T.c2.ka1);
-      vb0[1] = vb0[2] * f16u(T.c2.va0); vb1[1] = vb1[2] * f16u(T.c2.va1);
-    }
-    if constexpr (NC > 1) {
-      kb0[0] = kb0[1] * f16u(T.c1.ka0); kb1[0] = kb1[1] * f16u(T.c1.ka1);
-      vb0[0] = vb0[1] * f16u(T.c1.va0); vb1[0] = vb1[1] * f16u(T.c1.va1);
-    }
+    static_for<0, NC - 1>([&](auto ic) {
+      constexpr int c = NC - 2 - decltype(ic)::value;
+      const auto& C = tc<c + 1>(T);
+      kb0[c] = kb0[c + 1] * f16u(C.ka0); kb1[c] = kb1[c + 1] * f16u(C.ka1);
+      vb0[c] = vb0[c + 1] * f16u(C.va0); vb1[c] = vb1[c + 1] * f16u(C.va1);
+    });
     float s0 = 0.0f, s1 = 0.0f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -722,20 +748,20 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
         Wb[c][1] = Wb[c][0];
       }
     };
-    vweight(T.c0, 0, std::integral_constant<int, ckind<CB, 0>()>{});
-    if constexpr (NC > 1) vweight(T.c1, 1, std::integral_constant<int, ckind<CB, 1>()>{});
-    if constexpr (NC > 2) vweight(T.c2, 2, std::integral_constant<int, ckind<CB, 2>()>{});
-    if constexpr (NC > 3) vweight(T.c3, 3, std::integral_constant<int, ckind<CB, 3>()>{});
+    static_for<0, NC>([&](auto ic) {
+      constexpr int c = decltype(ic)::value;
+      vweight(tc<c>(T), c, std::integral_constant<int, ckind<CB, c>()>{});
+    });
 
 #pragma unroll
     for (int half = 0; half < 2; ++half)
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
         uint32_t x[NC][4];
-        vpairs<ckind<CB, 0>(), REF>(T.c0.v0, T.c0.v1, half, blk, x[0]);
-        if constexpr (NC > 1) vpairs<ckind<CB, 1>(), REF>(T.c1.v0, T.c1.v1, half, blk, x[1]);
-        if constexpr (NC > 2) vpairs<ckind<CB, 2>(), REF>(T.c2.v0, T.c2.v1, half, blk, x[2]);
-        if constexpr (NC > 3) vpairs<ckind<CB, 3>(), REF>(T.c3.v0, T.c3.v1, half, blk, x[3]);
+        static_for<0, NC>([&](auto ic) {
+          constexpr int c = decltype(ic)::value;
+          vpairs<ckind<CB, c>(), REF>(tc<c>(T).v0, tc<c>(T).v1, half, blk, x[c]);
+        });
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float& a = acc[16 * half + 4 * blk + q];
@@ -743,10 +769,10 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
             a = fmaf(f16lo(x[c][q]), w4 ? 4.0f * Wa[c][half] : Wa[c][half], a);
             a = fmaf(f16hi(x[c][q]), w4 ? 4.0f * Wb[c][half] : Wb[c][half], a);
           };
-          comp(0, vw4<kbits(ckind<CB, 0>()), REF>(q));
-          if constexpr (NC > 1) comp(1, vw4<kbits(ckind<CB, (NC > 1 ? 1 : 0)>()), REF>(q));
-          if constexpr (NC > 2) comp(2, vw4<kbits(ckind<CB, (NC > 2 ? 2 : 0)>()), REF>(q));
-          if constexpr (NC > 3) comp(3, vw4<kbits(ckind<CB, (NC > 3 ? 3 : 0)>()), REF>(q));
+          static_for<0, NC>([&](auto ic) {
+            constexpr int c = decltype(ic)::value;
+            comp(c, vw4<kbits(ckind<CB, c>()), REF>(q));
+          });
         }
       }
   };

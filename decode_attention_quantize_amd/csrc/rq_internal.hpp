@@ -10,7 +10,7 @@
 
 namespace rq {
 
-constexpr int kMaxComp = 4;          // stored components one decode call may read
+constexpr int kMaxComp = 8;          // stored components one decode call may read
 constexpr int kWaves = 4;            // waves per decode workgroup
 constexpr int kThreads = 64 * kWaves;
 
@@ -161,6 +161,10 @@ int launch_bf16(const Bf16Params& p, int D, int nsplit, void* stream);
 int launch_combine(const CombineParams& p, int D, int B, void* stream);
 int launch_prefill(const PrefillParams& p, int D, void* stream);
 size_t prefill_workspace_bytes(int B, int H, int D, int T);
-bool have_decode_kernel(int D, int ncomp, const int* bits, int limbs);
+// paged: a paged cache (chains of more than four components have contiguous instances only)
+bool have_decode_kernel(int D, int ncomp, const int* bits, int limbs, bool paged);
+bool have_decode_kernel_long(int D, int ncomp, const int* bits, int limbs);
+int launch_decode_long(const DecodeParams& p, int D, int ncomp, const int* bits, int limbs, int nsplit,
+                       void* stream);
 
 }  // namespace rq

@@ -83,8 +83,11 @@ typedef enum {
  *   KV": the shared-anchor alternative to Previous-loop; ablated in Table 3).
  * PREV_LOOP: the anchor is the group's first loop; loop r refers to the
  *   reconstruction of loop r-1 (a chain: zhat_r = alpha_r zhat_{r-1} + D(c_r)),
- *   so decoding the j-th loop of a group reads j stored components (the decode
- *   kernels take at most 4). Kept as the comparator the paper measures against. */
+ *   so decoding the j-th loop of a group reads j stored components (App. D).
+ *   Kept as the comparator the paper measures against. The decode kernels take
+ *   up to 8 components per call; chains of 5 to 8 have kernels for a contiguous
+ *   cache whose first one or two loops may be INT4 and the others INT2 (groups
+ *   of 32); other long chains return RQ_E_UNSUPPORTED. */
 typedef enum { RQ_POLICY_LAST_LOOP = 0, RQ_POLICY_PREV_LOOP = 1, RQ_POLICY_FIRST_LOOP = 2 } rq_policy;
 
 /* Decode flag: score the cached keys against the rotated query held in 21-bit

@@ -238,7 +238,7 @@ def inputs(w, T_total, layer=0, batch=None):
     return X, rk, rv
 
 
-def decode_and_compare(w, X, rk, rv, cache, series, lens, loops, label, batch=None):
+def decode_and_compare(w, X, rk, rv, cache, series, lens, loops, label, batch=None, flags=None):
     B, H, D = X.shape[2], X.shape[3], X.shape[5]
     d = cache.desc
     ws = rq.alloc_workspace(d)
@@ -252,7 +252,7 @@ def decode_and_compare(w, X, rk, rv, cache, series, lens, loops, label, batch=No
         vc = torch.stack([X[1, r, b, :, lens[b]] for b in range(B)]).contiguous()
         out = torch.empty(B, H, D, dtype=torch.float32, device="cuda")
         log(f"{label}: decode loop {r}")
-        rq.decode_attn(cache, r, q, kc, vc, past, scale, out, ws)
+        rq.decode_attn(cache, r, q, kc, vc, past, scale, out, ws, flags=flags)
         torch.cuda.synchronize()
         units = [(b, h) for b in range(B) for h in range(H)]
         ref = oracle_attention(series, units, r, lens, rk, rv, q, kc, vc, scale)

@@ -287,14 +287,18 @@ def test_decode_validation():
     cm.codes[1][3] = 0x100004                                                  # codes need 16 bytes
     assert L.rq_decode_attn(by(d), by(cm), 0, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE, ws,
                             None, 0) == 10
-    # chained policy with more components than the fused kernel takes
-    d6 = _desc(bits=[4, 4, 2, 2, 2, 2], policy=1)
-    c6 = _cache(d6)
-    ws6 = rq.workspace_bytes(d6)
-    assert L.rq_decode_attn(by(d6), by(c6), 5, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE,
-                            ws6, None, 0) == 6
-    # chains restart in every loop group: loop 13 of 16 in groups of 8 reads loops 8..13
-    d16 = _desc(bits=[2] * 16, policy=1, loop_group=8)
+    # chained policy with more components than the fused kernel takes (9), a long chain of
+    # an order without an instance (INT2 anchor, then INT4), and a long chain in a paged cache
+    for bits, loop, kw in (([2] * 9, 8, {}), ([2, 4, 2, 4, 2, 4], 5, {}),
+                           ([4, 2, 2, 2, 2], 4, dict(block_size=16, num_blocks=40, max_tokens=1024))):
+        dl = _desc(bits=bits, policy=1, **kw)
+        cl = _cache(dl)
+        if kw:
+            cl.block_table = 0x100000
+        assert L.rq_decode_attn(by(dl), by(cl), loop, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE,
+                                rq.workspace_bytes(dl), None, 0) == 6, (bits, kw)
+    # chains restart in every loop group: loop 13 of 32 in groups of 16 reads loops 0..13
+    d16 = _desc(bits=[2] * 32, policy=1, loop_group=16)
     c16 = _cache(d16)
     assert L.rq_decode_attn(by(d16), by(c16), 13, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE,
                             rq.workspace_bytes(d16), None, 0) == 6

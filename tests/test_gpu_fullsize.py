@@ -123,6 +123,14 @@ def test_huginn_4k_sampled():
     _check(w.layers - 1, LAST, w.bits, _sample_units(8, 5, w), "huginn 4k", w)
 
 
+def test_huginn_4k_chained_sampled():
+    """The Huginn-shaped workload's chained comparator at full size (one group of 8
+    loops, plan [4,4,2,2,2,2,2,2]: decoding loop j reads j stored components, up to
+    8): the last layer, sampled series, every loop."""
+    w = synth.WORKLOADS["huginn_4k"]
+    _check(w.layers - 1, PREV, w.chained_bits, _sample_units(6, 9, w), "huginn 4k chained", w)
+
+
 @pytest.mark.parametrize("policy", [LAST, PREV])
 def test_huginn32_groups_sampled(policy):
     """Huginn-3.5B as the paper groups it (B4, H55, D96, 32 loops in eight anchor
