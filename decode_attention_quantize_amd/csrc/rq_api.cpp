@@ -127,6 +127,7 @@ CombineParams combine_params(const rq_desc* d, void* ws, const uint16_t* q, cons
   a.out = out;
   a.dev_err = dev_err;
   a.scale_log2 = scale_log2;
+  a.B = d->batch;
   a.H = d->heads;
   a.T_max = d->max_tokens;
   a.unit = sp.unit;
@@ -429,7 +430,11 @@ rq_status rq_decode_combine(const rq_desc* d, const float* rot_v, const uint16_t
   if (!std::isfinite(softmax_scale)) return RQ_E_SHAPE;
   const CombineParams cp = combine_params(d, const_cast<void*>(ws), q, k_cur, v_cur, past_len, rot_v, out,
                                           dev_err, softmax_scale * kLog2e);
-  return launch_combine(cp, d->head_dim, d->batch, stream) == 0 ? RQ_OK : RQ_E_HIP;
+  // the value rotation's product spread over D/32 workgroups per (b, h) while
+  // that leaves no more workgroups than compute units
+  const long long narrow = (long long)d->batch * d->heads * (d->head_dim / 32);
+  const int cols = (rot_v && narrow <= device_cus()) ? 32 : d->head_dim;
+  return launch_combine(cp, d->head_dim, cols, stream) == 0 ? RQ_OK : RQ_E_HIP;
 }
 
 }  // extern "C"

@@ -12,23 +12,36 @@ namespace {
 // original domain from bf16 q and k_cur) and, for the compressed cache, rotate
 // the value sum back once: out = (H_V^T acc + p_cur v_cur) / l.
 //
-// Its reads are latency-bound; they are ordered and batched as described below.
-template <int D>
+// Its reads are latency-bound. With few (b, h), the H_V^T product of each is
+// spread over D / COLS workgroups (COLS = 32), each producing COLS output
+// columns from a D x COLS block of H_V (16 KB at D = 128), so that no compute
+// unit waits for a whole matrix; each merges all D elements of the partials (a
+// few hundred bytes per slot). With many (b, h), or no rotation, one workgroup
+// per (b, h) (COLS = D) costs less: more workgroups than compute units only add
+// to the launch. split_item places a (b, h)'s workgroups on the XCD whose
+// workgroups wrote its partials (both launches map consecutive (b, h) blocks to
+// XCDs in proportion, when their workgroup counts are multiples of the XCD
+// count), where the partials are still in L2.
+template <int D, int COLS>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
-  constexpr int NQ = kThreads / D;  // row slices of the H_V^T product
-  constexpr int RS = D / NQ;        // rows per slice
+  constexpr int NS = D / COLS;               // workgroups per (b, h)
+  constexpr int NR = kThreads / COLS;        // row parts of the product
+  constexpr int RPT = D / NR;                // rows per thread
   constexpr int PF = (int)part_floats(D);
+  static_assert(D % COLS == 0 && D % NR == 0 && RPT % 4 == 0, "product layout");
   __shared__ float acc_s[D];
-  __shared__ float red_s[kThreads];
+  __shared__ float red_s[NR][COLS];
   __shared__ float wsum[kWaves];
-  const int bh = blockIdx.x, b = bh / p.H, h = bh % p.H, tid = threadIdx.x;
-  const int j = tid % D, sl = tid / D;
-  const bool rot = p.rotv != nullptr;
+  int slice, b, h;
+  split_item(NS, p.B, p.H, slice, b, h);
+  const int bh = b * p.H + h, tid = threadIdx.x;
+  const int c = tid % COLS, r = tid / COLS, col = slice * COLS + c;
+  const bool rot = p.rotv != nullptr, prod = r < NR;  // threads past NR * COLS only merge
 
   // Loads in the order their values are needed: the partials of the first CH
-  // slots, q/k_cur/v_cur, then the thread's slice of H_V. A round's loads are all
-  // issued before the first is used, so a call waits for memory about once per
-  // CH slots (slots past the last one are loaded clamped and ignored).
+  // slots, q/k_cur/v_cur, then the thread's block of H_V. A round's loads are
+  // all issued before the first is used, so a call waits for memory about once
+  // per CH slots (slots past the last one are loaded clamped and ignored).
   constexpr int CH = 16;
   const bool on = tid < D;
   const float* part = p.part + (size_t)bh * p.nsplit * PF;
@@ -45,19 +58,21 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   load_slots(0);
   const int raw_len = p.past_len[b];
   const size_t qo = (size_t)bh * D + (on ? tid : 0);
-  const uint16_t qh = p.q[qo], kh = p.kcur[qo], vh = p.vcur[qo];
-  float hv[RS];
-  if (rot && sl < NQ) {
-    const float* Hm = p.rotv + ((size_t)h * D + (size_t)sl * RS) * D + j;
+  const uint16_t qh = p.q[qo], kh = p.kcur[qo], vh = p.vcur[(size_t)bh * D + col];
+  float hv[RPT];
+  if (rot && prod) {
+    const float* Hm = p.rotv + ((size_t)h * D + (size_t)r * RPT) * D + col;
 #pragma unroll
-    for (int i = 0; i < RS; ++i) hv[i] = Hm[(size_t)i * D];
+    for (int i = 0; i < RPT; ++i) hv[i] = Hm[(size_t)i * D];
   }
 
-  if ((raw_len < 0 || raw_len > p.T_max) && h == 0 && tid == 0 && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_LENGTH);
+  if ((raw_len < 0 || raw_len > p.T_max) && h == 0 && slice == 0 && tid == 0 && p.dev_err)
+    atomicOr(p.dev_err, RQ_DEVERR_LENGTH);
   const int len = raw_len < 0 ? 0 : (raw_len > p.T_max ? p.T_max : raw_len);
   const int nvalid = slots_used(len, p.nsplit, p.unit);
 
-  // Online merge of the splits' (m, l, acc) relative to their running max M.
+  // Online merge of the splits' (m, l, acc) relative to their running max M
+  // (the same M and l in every thread).
   float M = -INFINITY, l = 0.0f, a = 0.0f;
   for (int s0 = 0;;) {
 #pragma unroll
@@ -92,26 +107,24 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
 
   float o = 0.0f;
   if (rot) {
-    if (sl < NQ) {
-      float o0 = 0.0f, o1 = 0.0f, o2 = 0.0f, o3 = 0.0f;
+    float o0 = 0.0f, o1 = 0.0f, o2 = 0.0f, o3 = 0.0f;
 #pragma unroll
-      for (int i = 0; i < RS; i += 4) {
-        o0 = fmaf(hv[i + 0], acc_s[sl * RS + i + 0], o0);
-        o1 = fmaf(hv[i + 1], acc_s[sl * RS + i + 1], o1);
-        o2 = fmaf(hv[i + 2], acc_s[sl * RS + i + 2], o2);
-        o3 = fmaf(hv[i + 3], acc_s[sl * RS + i + 3], o3);
-      }
-      red_s[tid] = (o0 + o1) + (o2 + o3);
+    for (int i = 0; i < RPT; i += 4) {
+      o0 = fmaf(hv[i + 0], acc_s[r * RPT + i + 0], o0);
+      o1 = fmaf(hv[i + 1], acc_s[r * RPT + i + 1], o1);
+      o2 = fmaf(hv[i + 2], acc_s[r * RPT + i + 2], o2);
+      o3 = fmaf(hv[i + 3], acc_s[r * RPT + i + 3], o3);
     }
+    if (prod) red_s[r][c] = (o0 + o1) + (o2 + o3);
     __syncthreads();
-    if (on) {
+    if (tid < COLS) {
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) o += red_s[q * D + tid];
+      for (int q = 0; q < NR; ++q) o += red_s[q][tid];
     }
-  } else if (on) {
-    o = acc_s[tid];
+  } else if (tid < COLS) {
+    o = acc_s[col];
   }
-  if (on) p.out[(size_t)bh * D + tid] = fmaf(g, o, pcur * vc) / lt;
+  if (tid < COLS) p.out[(size_t)bh * D + col] = fmaf(g, o, pcur * vc) / lt;
 }
 
 // ---------------------------------------------------------------- dispatch
@@ -136,13 +149,23 @@ int launch_decode(const DecodeParams& p, int D, int nc, const int* bits, int lim
   return (int)hipGetLastError();
 }
 
-int launch_combine(const CombineParams& p, int D, int B, void* stream) {
+int launch_combine(const CombineParams& p, int D, int cols, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)(B * p.H));
+  const dim3 grid((unsigned)(p.B * p.H * (D / cols)));
+  const bool narrow = cols != D;
   switch (D) {
-    case 64: hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(kThreads), 0, s, p); break;
-    case 96: hipLaunchKernelGGL(combine_kernel<96>, grid, dim3(kThreads), 0, s, p); break;
-    case 128: hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(kThreads), 0, s, p); break;
+    case 64:
+      if (narrow) hipLaunchKernelGGL((combine_kernel<64, 32>), grid, dim3(kThreads), 0, s, p);
+      else hipLaunchKernelGGL((combine_kernel<64, 64>), grid, dim3(kThreads), 0, s, p);
+      break;
+    case 96:
+      if (narrow) hipLaunchKernelGGL((combine_kernel<96, 32>), grid, dim3(kThreads), 0, s, p);
+      else hipLaunchKernelGGL((combine_kernel<96, 96>), grid, dim3(kThreads), 0, s, p);
+      break;
+    case 128:
+      if (narrow) hipLaunchKernelGGL((combine_kernel<128, 32>), grid, dim3(kThreads), 0, s, p);
+      else hipLaunchKernelGGL((combine_kernel<128, 128>), grid, dim3(kThreads), 0, s, p);
+      break;
     default: return -1;
   }
   return (int)hipGetLastError();

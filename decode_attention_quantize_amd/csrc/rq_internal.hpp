@@ -62,7 +62,7 @@ struct CombineParams {
   float* out;               // fp32 [B][H][D]
   int32_t* dev_err;
   float scale_log2;         // softmax scale * log2(e)
-  int H, T_max, unit, nsplit;
+  int B, H, T_max, unit, nsplit;
 };
 
 struct DecodeParams {
@@ -158,7 +158,8 @@ int launch_decode(const DecodeParams& p, int D, int ncomp, const int* bits, int 
 int launch_decode_paged(const DecodeParams& p, int D, int ncomp, const int* bits, int limbs, int nsplit,
                         void* stream);
 int launch_bf16(const Bf16Params& p, int D, int nsplit, void* stream);
-int launch_combine(const CombineParams& p, int D, int B, void* stream);
+// cols: output columns per workgroup, 32 or D
+int launch_combine(const CombineParams& p, int D, int cols, void* stream);
 int launch_prefill(const PrefillParams& p, int D, void* stream);
 size_t prefill_workspace_bytes(int B, int H, int D, int T);
 // paged: a paged cache (chains of more than four components have contiguous instances only)
