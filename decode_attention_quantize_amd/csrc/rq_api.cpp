@@ -260,6 +260,14 @@ rq_status append_layers(const rq_desc* d, const rq_layer_cache* caches, int32_t 
     const int per = kUnitSlots / stride;
     for (int l0 = 0; l0 < nl; l0 += per) {
       p.nl = nl - l0 < per ? nl - l0 : per;
+      // Units share a workgroup (and its staging of the rotation) while that
+      // still leaves about two workgroups per compute unit.
+      const long long units = (long long)d->batch * n;
+      long long upw = units * d->heads * 2 * p.nl / (2LL * device_cus());
+      if (upw < 1) upw = 1;
+      if (upw > units) upw = units;
+      const long long runs = (units + upw - 1) / upw;
+      p.upw = (int)((units + runs - 1) / runs);
       p.kv = kv + (size_t)l0 * layer_elems;
       for (int i = 0; i < p.nl; ++i) {
         const rq_layer_cache* c = &caches[l0 + i];

@@ -397,10 +397,11 @@ __global__ __launch_bounds__(kThreads, 2) void append_kernel(AppendParams p) {
 }
 
 // Few-token path (decode-time store of the current token, short chunks): one
-// workgroup per (sequence, token) unit, head, tensor and layer (blockIdx.z =
-// 2 layer + tensor; the launch's p.nl layers find their cache pointers in
-// p.slot, and layer i reads its inputs at kv + i * 2 L B H n D). The workgroup stages
-// the head's rotation in LDS once; wave w computes Z_r for its loops
+// workgroup per run of p.upw consecutive (sequence, token) units, head, tensor
+// and layer (blockIdx.z = 2 layer + tensor; the launch's p.nl layers find their
+// cache pointers in p.slot, and layer i reads its inputs at kv + i * 2 L B H n
+// D). The workgroup stages the head's rotation in LDS once for all its units;
+// for each unit, wave w computes Z_r for its loops
 // r = w, w + 4, .. on the fp64 vector units (lane k of group gi holds channels
 // e0 = 32 gi + k and e1 = e0 + 16, the pair quantize_pair takes), so the four
 // waves rotate in parallel. Then every loop group's anchor is quantized, and
@@ -419,7 +420,7 @@ __global__ __launch_bounds__(256) void append_unit(UnitParams p) {
   __shared__ float xs[LM][D];
   __shared__ double rec[LM][D];            // per loop group: current reference (reconstruction)
   __shared__ double dens[LM];              // its squared norm
-  const int u = blockIdx.x, h = blockIdx.y, kv = blockIdx.z & 1, layer = blockIdx.z >> 1;
+  const int u0 = blockIdx.x * p.upw, h = blockIdx.y, kv = blockIdx.z & 1, layer = blockIdx.z >> 1;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int L = p.L, G = p.G;
   // this layer's and tensor's pointers
@@ -431,19 +432,8 @@ __global__ __launch_bounds__(256) void append_unit(UnitParams p) {
   auto meta_of = [&](int r) { return static_cast<uint32_t*>(const_cast<void*>(st[1 + L + r])); };
   auto alpha_of = [&](int r) { return static_cast<uint16_t*>(const_cast<void*>(st[1 + 2 * L + r])); };
   const uint16_t* kvin = p.kv + (size_t)layer * 2 * L * p.B * p.H * p.n * D;
-  const int b = u / p.n, i = u % p.n;
-  const int t = p.pos[b] + i;
-  if (t < 0 || t >= p.T_max) {             // whole block, before any barrier
-    if (tid == 0 && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_CAPACITY);
-    return;
-  }
-  size_t tok;
-  if (!cache_row(table, p.maxblk, p.lbs, p.num_blocks, p.H, p.T_max, b, h, t, tok)) {  // likewise
-    if (tid == 0 && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_BLOCK);
-    return;
-  }
 
-  // ---- stage H (row-major, padded) and the L input rows
+  // ---- stage H (row-major, padded) once for all of the workgroup's units
   {
     const float4* Hg = reinterpret_cast<const float4*>(rot + (size_t)h * D * D);
     float4 hv[NF];
@@ -456,119 +446,157 @@ __global__ __launch_bounds__(256) void append_unit(UnitParams p) {
       dst[0] = make_float2(hv[j].x, hv[j].y);
       dst[1] = make_float2(hv[j].z, hv[j].w);
     }
-    for (int idx = tid; idx < L * (D / 8); idx += kThreads) {
-      const int xr = idx / (D / 8), xc = idx % (D / 8);
-      const uint16_t* row = kvin + (((((size_t)kv * L + xr) * p.B + b) * p.H + h) * p.n + i) * (size_t)D;
-      const uint4 xv = reinterpret_cast<const uint4*>(row)[xc];
-      const uint32_t w[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        xs[xr][8 * xc + 2 * q] = __uint_as_float(w[q] << 16);
-        xs[xr][8 * xc + 2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
-      }
-    }
   }
-  __syncthreads();
-
-  // ---- Z_r at (e0, e1) for this wave's loops; products of fp32 and bf16 are exact in fp64
-  const int gi = lane >> 4, kk = lane & 15;
-  const bool lane_on = gi < D / 32;
-  const int e0 = lane_on ? 32 * gi + kk : 0, e1 = e0 + 16;
-  double z0[kLoopsPerWave], z1[kLoopsPerWave];
-#pragma unroll
-  for (int j = 0; j < kLoopsPerWave; ++j) {
-    const int r = wave + kWaves * j;
-    double a0 = 0.0, a1 = 0.0, c0 = 0.0, c1 = 0.0;
-    if (r < L) {
-      const float* x = xs[r];
-      const float* h0 = &Hs[e0 * HS];
-      const float* h1 = &Hs[e1 * HS];
-#pragma unroll 4
-      for (int k = 0; k < D; k += 2) {
-        const float2 xv = *reinterpret_cast<const float2*>(&x[k]);
-        const float2 u0 = *reinterpret_cast<const float2*>(&h0[k]);
-        const float2 u1 = *reinterpret_cast<const float2*>(&h1[k]);
-        const double x0 = (double)xv.x, x1 = (double)xv.y;
-        a0 = fma((double)u0.x, x0, a0);
-        c0 = fma((double)u0.y, x1, c0);
-        a1 = fma((double)u1.x, x0, a1);
-        c1 = fma((double)u1.y, x1, c1);
-      }
-    }
-    z0[j] = a0 + c0;
-    z1[j] = a1 + c1;
-  }
-
-  const bool last = p.policy == RQ_POLICY_LAST_LOOP, chain = p.policy == RQ_POLICY_PREV_LOOP;
-  auto anchor_of = [&](int r) { return last ? r / G * G + G - 1 : r / G * G; };
 
   bool sat = false;                        // an fp16 offset, scale or alpha was saturated
-  // ---- anchors of every group (by the waves that own them)
+  const int u_end = min(u0 + p.upw, p.B * p.n);
+  // The input rows of unit u + 1 load while unit u is processed: XI 16-byte
+  // pieces per thread hold the L rows of a unit.
+  constexpr int XI = (LM * (D / 8) + kThreads - 1) / kThreads;
+  uint4 xn[XI];
+  auto load_x = [&](int uu) {
+    const int bb = uu / p.n, ii = uu % p.n;
 #pragma unroll
-  for (int j = 0; j < kLoopsPerWave; ++j) {
-    const int r = wave + kWaves * j;
-    if (r < L && r == anchor_of(r)) {
-      double r0, r1;
-      quantize_pair<D>(z0[j], z1[j], p.bits[r], (p.g16 >> r) & 1, lane_on, gi, kk, codes_of(r), meta_of(r), tok, r0,
-                       r1, sat);
-      if (!lane_on) r0 = r1 = 0.0;
-      const double den = wave_sum_f64(r0 * r0 + r1 * r1);
-      if (lane_on) {
-        rec[r / G][e0] = r0;
-        rec[r / G][e1] = r1;
-      }
-      if (lane == 0) dens[r / G] = den;
+    for (int q = 0; q < XI; ++q) {
+      const int idx = tid + q * kThreads, xr = idx / (D / 8), xc = idx % (D / 8);
+      const uint4* row = reinterpret_cast<const uint4*>(
+          kvin + (((((size_t)kv * L + (xr < L ? xr : 0)) * p.B + bb) * p.H + h) * p.n + ii) * (size_t)D);
+      xn[q] = xr < L ? row[xc] : make_uint4(0, 0, 0, 0);
     }
-  }
-  __syncthreads();
-
-  // ---- one residual: alpha against the group's reference, then Q(Z_r - alpha ref)
-  auto residual = [&](int r, double zz0, double zz1, double& q0, double& q1, double& at, double& r0,
-                      double& r1) __attribute__((always_inline)) {
-    const int g = r / G;
-    r0 = lane_on ? rec[g][e0] : 0.0;
-    r1 = lane_on ? rec[g][e1] : 0.0;
-    const double den = dens[g];
-    const double num = wave_sum_f64((lane_on ? zz0 : 0.0) * r0 + (lane_on ? zz1 : 0.0) * r1);
-    const double alpha = den > 0.0 ? num / den : 0.0;
-    const uint16_t a16 = f16_sat(f64_to_f16<kRoundNearest>(alpha), sat);
-    at = f16_to_f64(a16);
-    if (lane == 0) alpha_of(r)[tok] = a16;
-    quantize_pair<D>(zz0 - at * r0, zz1 - at * r1, p.bits[r], (p.g16 >> r) & 1, lane_on, gi, kk, codes_of(r),
-                     meta_of(r), tok, q0, q1, sat);
   };
+  if (u0 < u_end) load_x(u0);
+  for (int u = u0; u < u_end; ++u) {       // uniform over the workgroup
+    uint4 xc[XI];
+#pragma unroll
+    for (int q = 0; q < XI; ++q) xc[q] = xn[q];
+    if (u + 1 < u_end) load_x(u + 1);
+    const int b = u / p.n, i = u % p.n;
+    const int t = p.pos[b] + i;
+    if (t < 0 || t >= p.T_max) {             // the whole unit, before any barrier
+      if (tid == 0 && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_CAPACITY);
+      continue;
+    }
+    size_t tok;
+    if (!cache_row(table, p.maxblk, p.lbs, p.num_blocks, p.H, p.T_max, b, h, t, tok)) {  // likewise
+      if (tid == 0 && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_BLOCK);
+      continue;
+    }
+    __syncthreads();                         // the previous unit is done with xs, rec and dens
 
-  if (!chain) {
-    // shared anchor: the waves work on all their loops at once
+    // ---- stage the L input rows (bf16 -> fp32)
+#pragma unroll
+    for (int q = 0; q < XI; ++q) {
+      const int idx = tid + q * kThreads, xr = idx / (D / 8), xcol = idx % (D / 8);
+      if (xr < L) {
+        const uint32_t w[4] = {xc[q].x, xc[q].y, xc[q].z, xc[q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xs[xr][8 * xcol + 2 * e] = __uint_as_float(w[e] << 16);
+          xs[xr][8 * xcol + 2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- Z_r at (e0, e1) for this wave's loops; products of fp32 and bf16 are exact in fp64
+    const int gi = lane >> 4, kk = lane & 15;
+    const bool lane_on = gi < D / 32;
+    const int e0 = lane_on ? 32 * gi + kk : 0, e1 = e0 + 16;
+    double z0[kLoopsPerWave], z1[kLoopsPerWave];
 #pragma unroll
     for (int j = 0; j < kLoopsPerWave; ++j) {
       const int r = wave + kWaves * j;
-      if (r < L && r != anchor_of(r)) {
-        double q0, q1, at, r0, r1;
-        residual(r, z0[j], z1[j], q0, q1, at, r0, r1);
+      double a0 = 0.0, a1 = 0.0, c0 = 0.0, c1 = 0.0;
+      if (r < L) {
+        const float* x = xs[r];
+        const float* h0 = &Hs[e0 * HS];
+        const float* h1 = &Hs[e1 * HS];
+#pragma unroll 4
+        for (int k = 0; k < D; k += 2) {
+          const float2 xv = *reinterpret_cast<const float2*>(&x[k]);
+          const float2 u0 = *reinterpret_cast<const float2*>(&h0[k]);
+          const float2 u1 = *reinterpret_cast<const float2*>(&h1[k]);
+          const double x0 = (double)xv.x, x1 = (double)xv.y;
+          a0 = fma((double)u0.x, x0, a0);
+          c0 = fma((double)u0.y, x1, c0);
+          a1 = fma((double)u1.x, x0, a1);
+          c1 = fma((double)u1.y, x1, c1);
+        }
+      }
+      z0[j] = a0 + c0;
+      z1[j] = a1 + c1;
+    }
+
+    const bool last = p.policy == RQ_POLICY_LAST_LOOP, chain = p.policy == RQ_POLICY_PREV_LOOP;
+    auto anchor_of = [&](int r) { return last ? r / G * G + G - 1 : r / G * G; };
+
+    // ---- anchors of every group (by the waves that own them)
+#pragma unroll
+    for (int j = 0; j < kLoopsPerWave; ++j) {
+      const int r = wave + kWaves * j;
+      if (r < L && r == anchor_of(r)) {
+        double r0, r1;
+        quantize_pair<D>(z0[j], z1[j], p.bits[r], (p.g16 >> r) & 1, lane_on, gi, kk, codes_of(r), meta_of(r), tok, r0,
+                         r1, sat);
+        if (!lane_on) r0 = r1 = 0.0;
+        const double den = wave_sum_f64(r0 * r0 + r1 * r1);
+        if (lane_on) {
+          rec[r / G][e0] = r0;
+          rec[r / G][e1] = r1;
+        }
+        if (lane == 0) dens[r / G] = den;
       }
     }
-  } else {
-    // a chain in every group: step st handles loop g G + st of each group g
-    for (int st = 1; st < G; ++st) {
+    __syncthreads();
+
+    // ---- one residual: alpha against the group's reference, then Q(Z_r - alpha ref)
+    auto residual = [&](int r, double zz0, double zz1, double& q0, double& q1, double& at, double& r0,
+                        double& r1) __attribute__((always_inline)) {
+      const int g = r / G;
+      r0 = lane_on ? rec[g][e0] : 0.0;
+      r1 = lane_on ? rec[g][e1] : 0.0;
+      const double den = dens[g];
+      const double num = wave_sum_f64((lane_on ? zz0 : 0.0) * r0 + (lane_on ? zz1 : 0.0) * r1);
+      const double alpha = den > 0.0 ? num / den : 0.0;
+      const uint16_t a16 = f16_sat(f64_to_f16<kRoundNearest>(alpha), sat);
+      at = f16_to_f64(a16);
+      if (lane == 0) alpha_of(r)[tok] = a16;
+      quantize_pair<D>(zz0 - at * r0, zz1 - at * r1, p.bits[r], (p.g16 >> r) & 1, lane_on, gi, kk, codes_of(r),
+                       meta_of(r), tok, q0, q1, sat);
+    };
+
+    if (!chain) {
+      // shared anchor: the waves work on all their loops at once
 #pragma unroll
       for (int j = 0; j < kLoopsPerWave; ++j) {
         const int r = wave + kWaves * j;
-        if (r < L && r % G == st) {
+        if (r < L && r != anchor_of(r)) {
           double q0, q1, at, r0, r1;
           residual(r, z0[j], z1[j], q0, q1, at, r0, r1);
-          const double n0 = lane_on ? at * r0 + q0 : 0.0, n1 = lane_on ? at * r1 + q1 : 0.0;
-          const double den = wave_sum_f64(n0 * n0 + n1 * n1);
-          if (lane_on) {
-            rec[r / G][e0] = n0;
-            rec[r / G][e1] = n1;
-          }
-          if (lane == 0) dens[r / G] = den;
         }
       }
-      __syncthreads();
+    } else {
+      // a chain in every group: step st handles loop g G + st of each group g
+      for (int st = 1; st < G; ++st) {
+#pragma unroll
+        for (int j = 0; j < kLoopsPerWave; ++j) {
+          const int r = wave + kWaves * j;
+          if (r < L && r % G == st) {
+            double q0, q1, at, r0, r1;
+            residual(r, z0[j], z1[j], q0, q1, at, r0, r1);
+            const double n0 = lane_on ? at * r0 + q0 : 0.0, n1 = lane_on ? at * r1 + q1 : 0.0;
+            const double den = wave_sum_f64(n0 * n0 + n1 * n1);
+            if (lane_on) {
+              rec[r / G][e0] = n0;
+              rec[r / G][e1] = n1;
+            }
+            if (lane == 0) dens[r / G] = den;
+          }
+        }
+        __syncthreads();
+      }
     }
-  }
+  }                                        // units
   if (sat && p.dev_err) atomicOr(p.dev_err, RQ_DEVERR_RANGE);
 }
 
@@ -576,7 +604,7 @@ __global__ __launch_bounds__(256) void append_unit(UnitParams p) {
 
 int launch_append_unit(const UnitParams& p, int D, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)(p.B * p.n), (unsigned)p.H, (unsigned)(2 * p.nl));
+  const dim3 grid((unsigned)((p.B * p.n + p.upw - 1) / p.upw), (unsigned)p.H, (unsigned)(2 * p.nl));
   const bool small = p.L <= 8;
   switch (D) {
     case 64:

@@ -130,6 +130,7 @@ struct UnitParams {
   uint32_t g16;             // bit r: loop r is INT2 in groups of 16 channels
   int maxblk, lbs, num_blocks;  // paged cache (block size 2^lbs); maxblk = 0: contiguous
   int nl;                   // layers in this launch
+  int upw;                  // (sequence, token) units per workgroup
   int bits[RQ_MAX_LOOPS];
   const void* slot[kUnitSlots];
 };
