@@ -116,13 +116,25 @@ __device__ __forceinline__ bool cache_row(const int32_t* table, int maxblk, int 
   return true;
 }
 
-// Code of value v in a group with fp16 offset od and scale sd (§2.1): nearest
-// level, ties to even, clamped to [0, 2^BITS - 1]; 0 when sd = 0 (a constant group).
+// Code of value v in a group with fp16 offset od and scale sd (§2.1): the
+// nearest level to fl((v - od) / sd), ties to even, clamped to [0, 2^BITS - 1];
+// 0 when sd = 0 (a constant group).
+// The quotient is formed with rs, sd's single-precision reciprocal (v_rcp_f32,
+// within one ulp): t is within |t| 2^-22.9 of the exact quotient, which is
+// below 2^-18.9 wherever the clamp leaves a choice (|t| <= 16). So t and the
+// correctly rounded quotient have the same nearest integer unless t lies within
+// 2^-16 of a half-integer; there (rarely) the division itself decides.
+__device__ __forceinline__ double recip_of(double sd) {
+  return sd != 0.0 ? (double)__builtin_amdgcn_rcpf((float)sd) : 0.0;   // sd is an fp16 value: exact in fp32
+}
 template <int BITS>
-__device__ __forceinline__ uint32_t code_of(double v, double od, double sd) {
+__device__ __forceinline__ uint32_t code_of(double v, double od, double sd, double rs) {
   constexpr double qmax = (double)((1 << BITS) - 1);
-  const double t = rint((v - od) / (sd != 0.0 ? sd : 1.0));
-  return sd != 0.0 ? (uint32_t)fmin(fmax(t, 0.0), qmax) : 0u;
+  const double u = v - od;
+  const double t = u * rs;
+  double c = rint(t);
+  if (fabs(fabs(t - c) - 0.5) < 0x1p-16) c = rint(u / (sd != 0.0 ? sd : 1.0));
+  return sd != 0.0 ? (uint32_t)fmin(fmax(c, 0.0), qmax) : 0u;
 }
 
 // Quantize one row's pair of elements e0 = 32 gi + k, e1 = e0 + 16 (held by
@@ -163,7 +175,8 @@ __device__ __forceinline__ void quantize_pair_t(double v0, double v1, bool lane_
     sb = f16_sat(f64_to_f16<kRoundUp>((mx1 - odb) / qmax), sat);
     sdb = f16_to_f64(sb);
   }
-  const uint32_t c0 = code_of<BITS>(v0, oda, sda), c1 = code_of<BITS>(v1, odb, sdb);
+  const double rsa = recip_of(sda), rsb = G16 ? recip_of(sdb) : rsa;
+  const uint32_t c0 = code_of<BITS>(v0, oda, sda, rsa), c1 = code_of<BITS>(v1, odb, sdb, rsb);
   d0 = oda + sda * (double)c0;
   d1 = odb + sdb * (double)c1;
   if constexpr (G16) {
