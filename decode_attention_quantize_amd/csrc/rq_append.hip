@@ -228,23 +228,31 @@ __device__ __forceinline__ void quantize_row_t(const double (&z0)[D / 32], const
   for (int gi = 0; gi < D / 32; ++gi) quantize_pair_t<D, BITS, G16>(z0[gi], z1[gi], on, gi, k, row, mrow, d0[gi], d1[gi], sat);
 }
 
-constexpr long long kAppendWorkgroups = 512;
+// The bulk kernel's workgroup: eight waves, one workgroup per compute unit,
+// sharing one copy of the rotation in LDS, held in fp64 (up to 133 KB at
+// D = 128) so that the matrix-core operands need no conversion.
+constexpr int kAppendWaves = 8;
+constexpr int kAppendThreads = 64 * kAppendWaves;
+constexpr long long kAppendWorkgroups = 256;
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void append_kernel(AppendParams p) {
+__global__ __launch_bounds__(kAppendThreads, 1) void append_kernel(AppendParams p) {
   constexpr int NT = D / 16;        // 16-column tiles of the product
   constexpr int NG = D / 32;        // 32-channel groups
   constexpr int KB = D / 16;        // 4-step blocks of the contraction per lane row
-  constexpr int HS = D + 4;         // padded LDS row of the rotation (16-byte aligned)
+  constexpr int HS = D + 2;         // padded LDS row of the rotation (16-byte aligned, conflict-free rows)
   constexpr int XW = D / 8;         // 32-bit words of a lane's D/4 bf16 operands
-  __shared__ float Hs[D * HS];      // Hs[n][k] = H[n][k]
+  __shared__ double Hs[D * HS];     // Hs[n][k] = H[n][k], exact in fp64
   const int kv = blockIdx.z, h = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   {
     const float4* Hg = reinterpret_cast<const float4*>(p.rot[kv] + (size_t)h * D * D);
-    for (int idx = threadIdx.x; idx < D * D / 4; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < D * D / 4; idx += kAppendThreads) {
       const int n = idx / (D / 4), c4 = idx % (D / 4);
-      *reinterpret_cast<float4*>(&Hs[n * HS + 4 * c4]) = Hg[idx];
+      const float4 v = Hg[idx];
+      double2* dst = reinterpret_cast<double2*>(&Hs[n * HS + 4 * c4]);
+      dst[0] = make_double2((double)v.x, (double)v.y);
+      dst[1] = make_double2((double)v.z, (double)v.w);
     }
   }
   __syncthreads();
@@ -265,9 +273,9 @@ __global__ __launch_bounds__(kThreads, 2) void append_kernel(AppendParams p) {
   bool sat = false;
 
   // tile tau of this wave's stream -> (quad, group start, first loop of the piece, loops in it)
-  // (tiles tau of a wave's stream: quad q_begin + wave + 4 (tau / tiles_per_quad))
+  // (tiles tau of a wave's stream: quad q_begin + wave + kAppendWaves (tau / tiles_per_quad))
   auto tile_of = [&](int tau, int& quad, int& g0, int& l0, int& nl) {
-    quad = q_begin + wave + kWaves * (tau / tiles_per_quad);
+    quad = q_begin + wave + kAppendWaves * (tau / tiles_per_quad);
     const int rest = tau % tiles_per_quad;
     const int g = rest / npiece, i = rest % npiece;
     const int pc = last ? (i == 0 ? npiece - 1 : i - 1) : i;  // anchor piece first
@@ -289,7 +297,7 @@ __global__ __launch_bounds__(kThreads, 2) void append_kernel(AppendParams p) {
     for (int w = 0; w < XW / 4; ++w) x[w] = ok ? src[w] : make_uint4(0, 0, 0, 0);
   };
 
-  const int my_quads = q_end - q_begin > wave ? (q_end - q_begin - wave + kWaves - 1) / kWaves : 0;
+  const int my_quads = q_end - q_begin > wave ? (q_end - q_begin - wave + kAppendWaves - 1) / kAppendWaves : 0;
   const int tiles = my_quads * tiles_per_quad;
   double rf0[NG], rf1[NG], den = 0.0;   // reference of the current loop group (this lane's unit)
 #pragma unroll
@@ -309,29 +317,28 @@ __global__ __launch_bounds__(kThreads, 2) void append_kernel(AppendParams p) {
       xw[4 * w] = xa[w].x; xw[4 * w + 1] = xa[w].y; xw[4 * w + 2] = xa[w].z; xw[4 * w + 3] = xa[w].w;
     }
     if (tau + 1 < tiles) load_x(tau + 1, xa);
-    // rotation operands of contraction block kb + 1 are read from LDS while the
-    // products of block kb run; the scheduling barrier keeps the compiler from
-    // hoisting all blocks' reads (their registers would spill)
-    auto read_h = [&](int kb, float4 (&hb)[NT]) {
+    // rotation operands of the next half-block (two contraction steps) are read
+    // from LDS while the products of the current one run; the scheduling barrier
+    // keeps the compiler from hoisting all blocks' reads (their registers would
+    // spill)
+    auto read_h = [&](int hk, double2 (&hb)[NT]) {  // half-block hk: steps 2 hk, 2 hk + 1
 #pragma unroll
       for (int ct = 0; ct < NT; ++ct)
-        hb[ct] = *reinterpret_cast<const float4*>(&Hs[(16 * ct + k) * HS + a_blk * (D / 4) + 4 * kb]);
+        hb[ct] = *reinterpret_cast<const double2*>(&Hs[(16 * ct + k) * HS + a_blk * (D / 4) + 2 * hk]);
     };
-    float4 hbuf[2][NT];
+    double2 hbuf[2][NT];
     read_h(0, hbuf[0]);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      if (kb + 1 < KB) read_h(kb + 1, hbuf[(kb + 1) & 1]);
-      const float4(&hb)[NT] = hbuf[kb & 1];
+    for (int hk = 0; hk < 2 * KB; ++hk) {
+      if (hk + 1 < 2 * KB) read_h(hk + 1, hbuf[(hk + 1) & 1]);
+      const double2(&hb)[NT] = hbuf[hk & 1];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t wv = xw[2 * kb + (q >> 1)];
-        const double a = (double)__uint_as_float((q & 1) ? (wv & 0xffff0000u) : (wv << 16));
+      for (int q2 = 0; q2 < 2; ++q2) {
+        const uint32_t wv = xw[hk];
+        const double a = (double)__uint_as_float(q2 ? (wv & 0xffff0000u) : (wv << 16));
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct) {
-          const float bq = q == 0 ? hb[ct].x : q == 1 ? hb[ct].y : q == 2 ? hb[ct].z : hb[ct].w;
-          acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, (double)bq, acc[ct], 0, 0, 0);
-        }
+        for (int ct = 0; ct < NT; ++ct)
+          acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, q2 ? hb[ct].y : hb[ct].x, acc[ct], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -639,18 +646,18 @@ int launch_append_unit(const UnitParams& p, int D, void* stream) {
 
 int launch_append(const AppendParams& p, int D, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // About two resident workgroups per compute unit in one round (the rotation
-  // takes 34-68 KB of LDS), each at least one quad per wave.
+  // About one resident workgroup per compute unit in one round (the rotation
+  // takes 33-133 KB of LDS), each at least one quad per wave.
   const long long quads = ((long long)p.B * p.n + 3) / 4;
   long long chunks = kAppendWorkgroups / (2LL * p.H);
-  const long long most = (quads + kWaves - 1) / kWaves;
+  const long long most = (quads + kAppendWaves - 1) / kAppendWaves;
   if (chunks > most) chunks = most;
   if (chunks < 1) chunks = 1;
   const dim3 grid((unsigned)chunks, (unsigned)p.H, 2);
   switch (D) {
-    case 64: hipLaunchKernelGGL(append_kernel<64>, grid, dim3(kThreads), 0, s, p); break;
-    case 96: hipLaunchKernelGGL(append_kernel<96>, grid, dim3(kThreads), 0, s, p); break;
-    case 128: hipLaunchKernelGGL(append_kernel<128>, grid, dim3(kThreads), 0, s, p); break;
+    case 64: hipLaunchKernelGGL(append_kernel<64>, grid, dim3(kAppendThreads), 0, s, p); break;
+    case 96: hipLaunchKernelGGL(append_kernel<96>, grid, dim3(kAppendThreads), 0, s, p); break;
+    case 128: hipLaunchKernelGGL(append_kernel<128>, grid, dim3(kAppendThreads), 0, s, p); break;
     default: return -1;
   }
   return (int)hipGetLastError();
