@@ -84,6 +84,33 @@ def test_layers_equal_one_layer_calls(case):
     log(f"append layers {label}: {nl} layers x {n} tokens equal to the one-layer calls")
 
 
+@pytest.mark.parametrize("bs", [0, 16], ids=["contiguous", "paged"])
+def test_layers_multi_unit_workgroups(bs):
+    """Enough (sequence, token) units, heads and layers that the shared launch
+    gives each workgroup several units in turn (the rotation staged once for
+    them); positions drop a token past capacity partway through a workgroup's
+    units. Every layer equals its one-layer call (which has one unit per
+    workgroup) and the drop is flagged by both."""
+    B, H, T_max, nl, n = 8, 16, 64, 4, 2
+    units = B * n
+    assert units * H * 2 * nl >= 4 * 2 * 256        # several units per workgroup on any device of <= 256 CUs
+    d, one, many = two_stacks(128, [2, 2, 4, 4], LAST, 0, 32, nl, B, H, T_max, bs)
+    g = torch.Generator(device="cuda").manual_seed(11)
+    kv = (2.0 * torch.randn(nl, 2, 4, B, H, n, 128, generator=g, device="cuda")).to(torch.bfloat16)
+    pos = torch.tensor([0, 7, 30, T_max - 1, 12, T_max - 2, 3, 50], dtype=torch.int32, device="cuda")
+    e1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    e2 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for l in range(nl):
+        rq.quantize_append(one[l], kv[l].contiguous(), pos, n, dev_err=e1)
+    rq.quantize_append_layers(many, kv, pos, n, dev_err=e2)
+    torch.cuda.synchronize()
+    assert int(e1.item()) == int(e2.item()) == rq.DEVERR_CAPACITY
+    for l in range(nl):
+        for x, y in zip(buffers(one[l]), buffers(many[l])):
+            assert torch.equal(x, y), f"layer {l} differs from the one-layer call"
+    log(f"append layers multi-unit ({'paged' if bs else 'contiguous'}): {nl} layers x {units} units equal")
+
+
 def test_layers_capacity_flag():
     """A token past max_tokens is dropped and flagged, by both calls alike."""
     B, H, T_max, nl = 3, 2, 64, 4
