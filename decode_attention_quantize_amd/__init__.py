@@ -62,6 +62,8 @@ def _load():
     L.rq_workspace_bytes.argtypes = [P]
     L.rq_check_desc.restype = ctypes.c_int
     L.rq_check_desc.argtypes = [P]
+    L.rq_check_decode.restype = ctypes.c_int
+    L.rq_check_decode.argtypes = [P, ctypes.c_int32]
     L.rq_quantize_append.restype = ctypes.c_int
     L.rq_quantize_append.argtypes = [P, P, P, P, I, P, P]
     L.rq_quantize_append_layers.restype = ctypes.c_int
@@ -130,6 +132,11 @@ def anchor_of(d: Desc, r: int) -> int:
 
 def check_desc(d: Desc) -> int:
     return lib.rq_check_desc(ctypes.byref(d))
+
+
+def check_decode(d: Desc, loop: int) -> int:
+    """0 when a decode kernel exists for `loop` under d (and its flags), else the status."""
+    return lib.rq_check_decode(ctypes.byref(d), loop)
 
 
 def buffer_bytes(d: Desc, kind: int, loop: int) -> int:

@@ -353,6 +353,18 @@ rq_status rq_split_plan(const rq_desc* d, int32_t* unit, int32_t* nsplit) {
 
 namespace {
 
+// Whether a streaming kernel exists for the components decode of `loop` reads
+// under d (their kinds, the head size, the query precision, the cache mode).
+bool decode_supported(const rq_desc* d, int32_t loop) {
+  int loops[RQ_MAX_LOOPS];
+  const int nc = components(d, loop, loops);
+  if (nc > kMaxComp) return false;
+  int kinds[kMaxComp];
+  for (int i = 0; i < nc; ++i) kinds[i] = d->bits[loops[i]] | (d->group[loops[i]] == 16 ? 8 : 0);
+  const int limbs = (d->flags & RQ_FLAG_PRECISE_QUERY) ? 3 : 2;
+  return have_decode_kernel(d->head_dim, nc, kinds, limbs, d->block_size != 0);
+}
+
 rq_status decode_partial(const rq_desc* d, const rq_layer_cache* c, int32_t loop, const uint16_t* q,
                          const int32_t* past_len, float softmax_scale, void* ws, size_t ws_bytes, int32_t* dev_err,
                          void* stream) {
@@ -366,11 +378,10 @@ rq_status decode_partial(const rq_desc* d, const rq_layer_cache* c, int32_t loop
   if (!std::isfinite(softmax_scale)) return RQ_E_SHAPE;
   int loops[RQ_MAX_LOOPS];
   const int nc = components(d, loop, loops);
-  if (nc > kMaxComp) return RQ_E_UNSUPPORTED;
   int bits[kMaxComp];  // component kinds: bit width, plus 8 for INT2 in groups of 16
-  for (int i = 0; i < nc; ++i) bits[i] = d->bits[loops[i]] | (d->group[loops[i]] == 16 ? 8 : 0);
   const int limbs = (d->flags & RQ_FLAG_PRECISE_QUERY) ? 3 : 2;
-  if (!have_decode_kernel(d->head_dim, nc, bits, limbs, d->block_size != 0)) return RQ_E_UNSUPPORTED;
+  if (!decode_supported(d, loop)) return RQ_E_UNSUPPORTED;
+  for (int i = 0; i < nc; ++i) bits[i] = d->bits[loops[i]] | (d->group[loops[i]] == 16 ? 8 : 0);
 
   const SplitPlan sp = split_plan(d);
   DecodeParams p;
@@ -418,6 +429,13 @@ rq_status decode_partial(const rq_desc* d, const rq_layer_cache* c, int32_t loop
 }  // namespace
 
 extern "C" {
+
+rq_status rq_check_decode(const rq_desc* d, int32_t loop) {
+  const rq_status s = check_plan(d);
+  if (s != RQ_OK) return s;
+  if (loop < 0 || loop >= d->loops) return RQ_E_LOOP;
+  return decode_supported(d, loop) ? RQ_OK : RQ_E_UNSUPPORTED;
+}
 
 rq_status rq_decode_attn_partial(const rq_desc* d, const rq_layer_cache* c, int32_t loop, const uint16_t* q,
                                  const int32_t* past_len, float softmax_scale, void* ws, size_t ws_bytes,

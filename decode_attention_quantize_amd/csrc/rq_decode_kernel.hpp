@@ -840,12 +840,17 @@ struct PlanEntry {
 // Plans with kernels: one nibble per component, anchor first (0xA = INT2 in
 // groups of 16). RQ_E(D, NC, CB, LIMBS) names the instance a table entry takes;
 // every plan has a 14-bit (2 limbs) and a 21-bit (3 limbs) query instance.
+// Covered: one or two components of any kinds (every Last-loop and First-loop
+// plan), and chains of three or four whose INT4 components all precede their
+// INT2 ones, the INT2 ones in one group size (the descending Previous-loop plans).
 #define RQ_PLANS_L(D, LB)                                                                                   \
   RQ_E(D, 1, 0x2, LB), RQ_E(D, 1, 0x4, LB), RQ_E(D, 2, 0x22, LB), RQ_E(D, 2, 0x24, LB), RQ_E(D, 2, 0x42, LB), \
       RQ_E(D, 2, 0x44, LB), RQ_E(D, 3, 0x244, LB), RQ_E(D, 3, 0x224, LB), RQ_E(D, 3, 0x222, LB),               \
       RQ_E(D, 3, 0x444, LB), RQ_E(D, 4, 0x2244, LB), RQ_E(D, 4, 0x2224, LB), RQ_E(D, 4, 0x2222, LB),           \
       RQ_E(D, 4, 0x4444, LB), RQ_E(D, 1, 0xA, LB), RQ_E(D, 2, 0xAA, LB), RQ_E(D, 2, 0xA4, LB),                 \
-      RQ_E(D, 3, 0xAA4, LB), RQ_E(D, 4, 0xAAA4, LB), RQ_E(D, 3, 0xAAA, LB), RQ_E(D, 4, 0xAAAA, LB)
+      RQ_E(D, 3, 0xAA4, LB), RQ_E(D, 4, 0xAAA4, LB), RQ_E(D, 3, 0xAAA, LB), RQ_E(D, 4, 0xAAAA, LB),          \
+      RQ_E(D, 3, 0xA44, LB), RQ_E(D, 4, 0xAA44, LB), RQ_E(D, 4, 0x2444, LB), RQ_E(D, 4, 0xA444, LB),           \
+      RQ_E(D, 2, 0x2A, LB), RQ_E(D, 2, 0x4A, LB), RQ_E(D, 2, 0xA2, LB)
 #define RQ_PLANS(D) RQ_PLANS_L(D, 2), RQ_PLANS_L(D, 3)
 
 template <size_t N>

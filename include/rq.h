@@ -85,9 +85,8 @@ typedef enum {
  *   reconstruction of loop r-1 (a chain: zhat_r = alpha_r zhat_{r-1} + D(c_r)),
  *   so decoding the j-th loop of a group reads j stored components (App. D).
  *   Kept as the comparator the paper measures against. The decode kernels take
- *   up to 8 components per call; chains of 5 to 8 have kernels for a contiguous
- *   cache whose first one or two loops may be INT4 and the others INT2 (groups
- *   of 32); other long chains return RQ_E_UNSUPPORTED. */
+ *   up to 8 components per call, for the chains rq_check_decode describes;
+ *   other chains return RQ_E_UNSUPPORTED at decode (their append works). */
 typedef enum { RQ_POLICY_LAST_LOOP = 0, RQ_POLICY_PREV_LOOP = 1, RQ_POLICY_FIRST_LOOP = 2 } rq_policy;
 
 /* Decode flag: score the cached keys against the rotated query held in 21-bit
@@ -163,6 +162,17 @@ size_t rq_workspace_bytes(const rq_desc* desc);
 
 /* Host-side check of a descriptor: RQ_OK or the first problem found. */
 rq_status rq_check_desc(const rq_desc* desc);
+
+/* Host-side check that rq_decode_attn / rq_decode_attn_partial have a kernel for
+ * decoding loop `loop` (0-based) under desc, its flags included: RQ_OK, a
+ * descriptor error as rq_check_desc, RQ_E_LOOP, or RQ_E_UNSUPPORTED. Touches no
+ * device. Kernels exist for every decode that reads one or two stored
+ * components (every Last-loop and First-loop plan, any widths and group sizes)
+ * and for Previous-loop chains of three to eight components whose INT4 loops
+ * all come before their INT2 loops, the INT2 loops in one group size (§3.2,
+ * §3.4: the descending plans); chains of five to eight need a contiguous cache,
+ * at most two INT4 loops and groups of 32. */
+rq_status rq_check_decode(const rq_desc* desc, int32_t loop);
 
 /* Quantize and store n tokens per sequence (§4.2 "Prefill" bulk store and
  * "Decode" deferred store; App. G.1 recipe).

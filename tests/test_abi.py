@@ -172,6 +172,42 @@ def test_group16_meta_alignment():
     assert L.rq_quantize_append(by(d), by(c), FAKE, FAKE, 1, None, 0) == 10
 
 
+def test_decode_support_rule():
+    """rq_check_decode (host only) against the documented rule, over every 4-loop plan of
+    widths and group sizes, all three policies, contiguous and paged: one or two
+    components always; chains whose INT4 loops precede their INT2 loops, the INT2 loops
+    in one group size. Chains of 5-8: contiguous, at most two INT4 loops first, groups of 32."""
+    import itertools
+    kinds = [(2, 32), (2, 16), (4, 32)]
+    for pol in (rq.POLICY_LAST_LOOP, rq.POLICY_FIRST_LOOP, rq.POLICY_PREV_LOOP):
+        for bs in (0, 16):
+            for combo in itertools.product(kinds, repeat=4):
+                kw = dict(block_size=bs, num_blocks=64, max_tokens=128) if bs else {}
+                d = _desc(bits=[k[0] for k in combo], group=[k[1] for k in combo], policy=pol, **kw)
+                assert rq.check_desc(d) == 0
+                for r in range(4):
+                    if pol == rq.POLICY_PREV_LOOP:
+                        ks = combo[:r + 1]
+                        wide = [k[0] == 4 for k in ks]
+                        ok = len(ks) <= 2 or (wide == sorted(wide, reverse=True)
+                                              and len({k[1] for k in ks if k[0] == 2}) <= 1)
+                    else:
+                        ok = True
+                    assert rq.check_decode(d, r) == (0 if ok else 6), (pol, bs, combo, r)
+    for bits, ok in (([4, 4] + [2] * 6, True), ([4] + [2] * 7, True), ([2] * 8, True), ([4, 4, 4] + [2] * 5, False),
+                     ([2, 4] + [2] * 6, False)):
+        d = _desc(bits=bits, policy=rq.POLICY_PREV_LOOP)
+        assert rq.check_decode(d, 7) == (0 if ok else 6), bits
+        d16 = _desc(bits=bits, group=[16 if b == 2 else 32 for b in bits], policy=rq.POLICY_PREV_LOOP)
+        assert rq.check_decode(d16, 7) == 6
+        dp = _desc(bits=bits, policy=rq.POLICY_PREV_LOOP, block_size=16, num_blocks=64, max_tokens=128)
+        head = [b == 4 for b in bits[:4]]
+        assert rq.check_decode(dp, 4) == 6 and rq.check_decode(dp, 3) == (0 if head == sorted(head, reverse=True) else 6)
+    d = _desc()
+    assert rq.check_decode(d, 4) == 9 and rq.check_decode(d, -1) == 9
+    assert rq.check_decode(_desc(head_dim=80), 0) == 2
+
+
 def test_buffer_and_workspace_sizes():
     d = _desc()
     toks = 2 * 3 * 100

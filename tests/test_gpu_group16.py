@@ -31,6 +31,7 @@ def _run(w, bits, policy, T, lens, steps_of_one, chunk, label, loops=None, group
     (LAST, (2, 2, 2, 4)),          # INT4 g32 anchor, INT2 g16 residuals
     (LAST, (2, 2, 2, 2)),          # uniform INT2 g16
     (PREV, (4, 2, 2, 2)),          # chained, mixed group sizes in one chain
+    (PREV, (4, 4, 2, 2)),          # chained, two INT4 g32 loops before the g16 ones (the 16k chained plan)
     (PREV, (2, 2, 2, 2)),
     (FIRST, (4, 2, 2, 2)),
 ])
