@@ -107,15 +107,17 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
 
   float o = 0.0f;
   if (rot) {
-    float o0 = 0.0f, o1 = 0.0f, o2 = 0.0f, o3 = 0.0f;
+    if (prod) {
+      float o0 = 0.0f, o1 = 0.0f, o2 = 0.0f, o3 = 0.0f;
 #pragma unroll
-    for (int i = 0; i < RPT; i += 4) {
-      o0 = fmaf(hv[i + 0], acc_s[r * RPT + i + 0], o0);
-      o1 = fmaf(hv[i + 1], acc_s[r * RPT + i + 1], o1);
-      o2 = fmaf(hv[i + 2], acc_s[r * RPT + i + 2], o2);
-      o3 = fmaf(hv[i + 3], acc_s[r * RPT + i + 3], o3);
+      for (int i = 0; i < RPT; i += 4) {
+        o0 = fmaf(hv[i + 0], acc_s[r * RPT + i + 0], o0);
+        o1 = fmaf(hv[i + 1], acc_s[r * RPT + i + 1], o1);
+        o2 = fmaf(hv[i + 2], acc_s[r * RPT + i + 2], o2);
+        o3 = fmaf(hv[i + 3], acc_s[r * RPT + i + 3], o3);
+      }
+      red_s[r][c] = (o0 + o1) + (o2 + o3);
     }
-    if (prod) red_s[r][c] = (o0 + o1) + (o2 + o3);
     __syncthreads();
     if (tid < COLS) {
 #pragma unroll
