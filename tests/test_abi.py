@@ -384,13 +384,15 @@ def test_prefill_validation():
     (2, 3, 128, 100, 1),          # shorter than 8 tiles: one slot
     (1, 16, 128, 4160, 16),       # 4160 // (32 * 8): capped below the 48 slots three per CU would give
     (8, 16, 128, 16448, 6),       # ceil(3 * 256 / 128): the 16k benchmark shape
-    (4, 55, 96, 4160, 4),         # ceil(3 * 256 / 220), under the cap 4160 // (42 * 8) = 12
+    (4, 55, 96, 4160, 2),         # ceil(3 * 256 / 220) = 4 overshoots 768: floor(2 * 256 / 220)
+    (2, 3, 128, 65600, 128),      # ceil(768 / 6) = 128 fits exactly
+    (2, 7, 128, 65600, 36),       # ceil(768 / 14) = 55 overshoots: floor(512 / 14)
     (128, 16, 128, 8256, 1),      # more series than workgroup slots
 ])
 def test_split_plan_rule(B, H, D, T, expect):
     """Split plan: about three workgroups per compute unit (256 CUs here, the
-    count the library assumes without a device), but every slot at least 8
-    tiles of the capacity."""
+    count the library assumes without a device), or two where rounding up would
+    overshoot three, but every slot at least 8 tiles of the capacity."""
     d = rq.make_desc(B, H, D, [2, 2, 4, 4], T)
     unit, nsplit = rq.split_plan(d)
     assert unit == 2 * 64 // (D // 32)
