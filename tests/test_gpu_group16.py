@@ -40,6 +40,21 @@ def test_tiny_group16(policy, bits):
     _run(w, bits, policy, 300, [300, 77], steps_of_one=6, chunk=1, label=f"tiny g16 policy={policy}")
 
 
+@pytest.mark.parametrize("policy,bits,groups", [
+    (LAST, (4, 4, 4, 2), (32, 32, 32, 16)),     # INT2 g16 anchor, INT4 residuals (plan 0x4A)
+    (FIRST, (2, 2, 2, 2), (16, 32, 32, 32)),    # g16 anchor, g32 residuals (0x2A)
+    (LAST, (2, 2, 2, 2), (16, 16, 16, 32)),     # g32 anchor, g16 residuals (0xA2)
+    (PREV, (4, 4, 4, 2), (32, 32, 32, 32)),     # chain with three INT4 loops first (0x2444)
+    (PREV, (4, 4, 4, 2), (32, 32, 32, 16)),     # the same, last loop in groups of 16 (0xA444)
+])
+def test_mixed_group_plans(policy, bits, groups):
+    """Plans that mix group sizes between the anchor and the residuals, and chains
+    with three INT4 loops before an INT2 one: every loop decoded against the oracle."""
+    w = synth.WORKLOADS["tiny"].with_(batch=2, heads=2, D=128, nb=128, outliers=4)
+    _run(w, bits, policy, 260, [260, 45], steps_of_one=3, chunk=1,
+         label=f"mixed groups policy={policy} bits={bits} groups={groups}", groups=list(groups))
+
+
 @pytest.mark.parametrize("D", [96, 128])
 def test_group16_ragged(D):
     """D96 (three blocks) and D128, ragged lengths including 0 and a tile edge, chunked appends."""
