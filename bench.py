@@ -407,12 +407,79 @@ def measure(w, K, warmup, BS=0, want_rq=True, want_chained=True, want_bf16=True,
                 ms_p = events(lambda i: rq.decode_attn_partial(caches[i % w.layers], r, qs[0, 0, r], past_len,
                                                                scale, ws, flags=rq.FLAG_PRECISE_QUERY))
                 entry["precise_query_kernel_ms"] = ms_p
+                entry["read_ceiling"] = read_ceiling(caches, d_rq, r, G or L, bits, gr, T, events, ms_k)
             percall[r] = entry
         res["percall"] = percall
     del caches, chained, bf16, bf16_all, kvcur, qs, ws, ws_ch, out
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
+
+
+def _calib_lib():
+    """librq_calib.so (the read-rate calibration kernel, built beside librq.so), or None."""
+    import ctypes
+    path = os.path.join(ROOT, "decode_attention_quantize_amd", "librq_calib.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.rqc_read_slots.restype = ctypes.c_int
+    lib.rqc_read_slots.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_int)] + \
+        [ctypes.c_int] * 7 + [ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
+def read_ceiling(caches, d, r, G, bits, gr, T, events, kernel_ms):
+    """The practical read ceiling of loop r's decode traffic: a plain streaming read
+    (rqc_read_slots: non-temporal 16-byte loads, no arithmetic) of exactly the
+    buffers and per-(b, h) slot ranges the decode call reads, with the same
+    workgroup count, timed like the kernel (graphs of launches cycling over the
+    layers' caches). Contiguous caches, loops in groups of G, Last-loop."""
+    import ctypes
+    import torch
+    import decode_attention_quantize_amd as rq
+    lib = _calib_lib()
+    if lib is None:
+        log("read ceiling: librq_calib.so not built")
+        return None
+    if d.block_size or T % 8:
+        return None
+    unit, nsplit = rq.split_plan(d)
+    a = r // G * G + G - 1
+    comps = [a] if r == a else [a, r]
+    D, B, H = d.head_dim, d.batch, d.heads
+    arrays = []
+    for c in caches:
+        ptrs, bpt = [], []
+        for kv in range(2):
+            for comp in comps:
+                ptrs.append(c.codes[kv][comp].data_ptr())
+                bpt.append(D * bits[comp] // 8)
+                ptrs.append(c.meta[kv][comp].data_ptr())
+                bpt.append(D // gr[comp] * 4)
+                if comp != a:
+                    ptrs.append(c.alpha[kv][comp].data_ptr())
+                    bpt.append(2)
+        arrays.append(((ctypes.c_void_p * len(ptrs))(*ptrs), (ctypes.c_int * len(bpt))(*bpt), len(ptrs)))
+    row = sum(bpt)
+    sink = torch.empty(nsplit * B * H, dtype=torch.int32, device="cuda")
+
+    def launch(i):
+        p, b, n = arrays[i % len(arrays)]
+        st = lib.rqc_read_slots(p, b, n, B, H, d.max_tokens, T, nsplit, unit, ctypes.c_void_p(sink.data_ptr()),
+                                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"rqc_read_slots failed ({st})")
+
+    ms = events(launch)
+    nbytes = row * B * H * T
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    log(f"read ceiling of loop {r + 1}'s traffic: {ms * 1e3:.1f} us, {gbps:.0f} GB/s; kernel/ceiling "
+        f"{kernel_ms / ms:.3f}")
+    return {"kernel": "read_slots (librq_calib.so): plain non-temporal reads of the call's buffers and slots, same "
+                      "workgroup count, no arithmetic",
+            "ms_per_launch": ms, "bytes_per_launch": nbytes, "gbps": gbps, "frac_of_peak": gbps / HBM_PEAK_GBPS,
+            "decode_kernel_over_ceiling_time": kernel_ms / ms}
 
 
 def sub_record(res, label):
@@ -535,6 +602,10 @@ def main():
                                     f"INT{bits[(G or L) - 1]} anchor + INT{bits[0]} residual, K and V)",
                           "bytes_per_launch": dom["bytes"], "ms_per_launch": dom["kernel_ms"],
                           "traffic_source": None if traffic is None else traffic["source"]}
+    ceiling = dom.pop("read_ceiling", None)
+    if ceiling:
+        # context for the roofline: the same bytes, slots and grid with no arithmetic
+        result["read_ceiling"] = ceiling
     result["per_call"] = {f"loop{r + 1}": v for r, v in percall.items()}
 
     # ---------------------------------------------------------------- prefill attention

@@ -10,6 +10,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librq.so")
+# the benchmark's read-rate calibration kernel, a library of its own (not librq's interface)
+CALIB_SRC = os.path.join(CSRC, "calib", "rq_calib_read.hip")
+CALIB_LIB = os.path.join(PKG, "librq_calib.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # per-source extra flags: the append kernel takes its rounding decisions in fp64
@@ -50,6 +53,19 @@ def build(jobs: int = 6, out: str = LIB, extra_flags=(), build_dir: str = BUILD)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, out)
+    if out == LIB:
+        build_calib()
+    return out
+
+
+def build_calib(out: str = CALIB_LIB) -> str:
+    """Compile and link the read-rate calibration library (used by bench.py only)."""
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = [HIPCC, *COMMON, "-shared", CALIB_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {CALIB_SRC}:\n{r.stderr}")
     os.replace(tmp, out)
     return out
 

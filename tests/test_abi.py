@@ -492,3 +492,24 @@ def test_binding_checks_tensors_before_the_call():
         bad.validate()
     with pytest.raises(ValueError, match=r"cache codes\[0\]\[0\]: must be on a GPU device"):
         c.validate()
+
+
+def test_read_calibration_library_validation():
+    """The benchmark's read-rate calibration (librq_calib.so) loads, exports its one
+    call and rejects arguments outside its limits without a launch."""
+    import bench
+    lib = bench._calib_lib()
+    assert lib is not None, "librq_calib.so is built beside librq.so"
+    bufs = (ctypes.c_void_p * 2)(0x100000, 0x200000)
+
+    def call(bpt, n=2, B=8, H=16, T_max=16448, length=16384, nsplit=6, unit=32, sink=FAKE, b=bufs):
+        return lib.rqc_read_slots(b, (ctypes.c_int * 2)(*bpt), n, B, H, T_max, length, nsplit, unit, sink, None)
+    assert call((0, 16)) == -1
+    assert call((1 << 20, 16)) == -1               # a buffer of 2^31 bytes or more per (b, h)
+    assert call((32, 16), length=16500) == -1      # longer than T_max
+    assert call((32, 16), n=0) == -1
+    assert call((32, 16), n=25) == -1              # more buffers than it takes
+    assert call((32, 16), nsplit=0) == -1
+    assert call((32, 16), unit=0) == -1
+    assert call((32, 16), sink=None) == -1
+    assert call((32, 16), b=(ctypes.c_void_p * 2)(0x100000, None)) == -1
