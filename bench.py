@@ -81,15 +81,14 @@ def call_bytes(D, bits, policy, r, G=0, groups=None):
 PROFILED_WORKLOAD = "ouro_16k"       # the workload the committed counter summaries cover
 
 
-def dom_kernel_name(D, bits, G, groups=None, blocked=True):
+def dom_kernel_name(D, bits, G, groups=None):
     """Instance name of the streaming kernel decoding loop 1 (anchor + loop-1 residual);
-    a component's nibble is its bit width, plus 8 for groups of 16 channels; the last
-    template argument says whether the cache is in the blocked layout."""
+    a component's nibble is its bit width, plus 8 for groups of 16 channels."""
     G = G or len(bits)
     gs = _groups(bits, groups)
     kind = [b | (8 if g == 16 else 0) for b, g in zip(bits, gs)]
     cb = kind[G - 1] | (kind[0] << 4)
-    return f"decode_fused<{D}, 2, {cb}u, 2, 2, {'true' if blocked else 'false'}>"
+    return f"decode_fused<{D}, 2, {cb}u, 2, 2>"
 
 
 DOM_KERNEL = dom_kernel_name(128, [2, 2, 4, 4], 0)
@@ -98,8 +97,7 @@ COPY_KIB = float(1 << 20)            # 1 GiB read and 1 GiB written by the calib
 PROFILES = os.path.join(ROOT, "profiles")
 FETCH_FILE = os.path.join(PROFILES, "decode_fused_loop1_ouro_16k_fetch_size.txt")
 WRITE_FILE = os.path.join(PROFILES, "decode_fused_loop1_ouro_16k_write_size.txt")
-KERNEL_SOURCES = ["rq_decode.hip", "rq_decode_blocked.hip", "rq_decode_kernel.hpp", "rq_combine.hpp", "rq_device.hpp",
-                  "rq_internal.hpp"]
+KERNEL_SOURCES = ["rq_decode.hip", "rq_decode_kernel.hpp", "rq_combine.hpp", "rq_device.hpp", "rq_internal.hpp"]
 
 
 def kernel_source_hash():
@@ -130,7 +128,7 @@ def _read_counter_summary(path, counter):
     return src, vals
 
 
-def profiled_traffic(workload, kernel=DOM_KERNEL):
+def profiled_traffic(workload):
     """HBM bytes per launch of the dominant kernel from the committed FETCH_SIZE and
     WRITE_SIZE summaries, each scaled by the copy kernel's reading of its known size;
     None for another workload, or when a summary is missing or was taken on other
@@ -141,13 +139,13 @@ def profiled_traffic(workload, kernel=DOM_KERNEL):
     total, used = 0.0, []
     for path, counter in ((FETCH_FILE, "FETCH_SIZE"), (WRITE_FILE, "WRITE_SIZE")):
         src, vals = _read_counter_summary(path, counter)
-        if src != cur or kernel not in vals:
+        if src != cur or DOM_KERNEL not in vals:
             return None
         copy = [v for k, v in vals.items() if COPY_KERNEL in k]
         if not copy or copy[0] <= 0:
             return None
         factor = COPY_KIB / copy[0]
-        total += vals[kernel] * factor * 1024.0
+        total += vals[DOM_KERNEL] * factor * 1024.0
         used.append(f"{os.path.basename(path)} (x{factor:.4f})")
     return {"bytes": total, "source": ", ".join(used)}
 
@@ -204,7 +202,7 @@ def summarize_profile(directory, title, command):
 
 
 def measure(w, K, warmup, BS=0, want_rq=True, want_chained=True, want_bf16=True, want_percall=False,
-            call_reps=50, blocked=True):
+            call_reps=50):
     """Build workload w's caches (untimed) and time K decode steps of the enabled
     paths, each step captured as one HIP graph. Returns a dict of timings; every
     device buffer is released when it returns."""
@@ -215,13 +213,8 @@ def measure(w, K, warmup, BS=0, want_rq=True, want_chained=True, want_bf16=True,
 
     B, H, D, L, T = w.batch, w.heads, w.D, w.L, w.T
     T_max = T + max(K, warmup)
-    if blocked and BS and BS < 32:
-        log(f"blocked layout needs pages of at least 32 rows; block size {BS}: separate buffers")
-        blocked = False
     if BS:
         T_max = -(-T_max // BS) * BS
-    if blocked:
-        T_max = -(-T_max // 32) * 32       # whole 32-row blocks per series
     dev = "cuda"
     scale = 1.0 / math.sqrt(D)
     bits, cbits = list(w.bits), list(w.chained_bits)
@@ -257,11 +250,11 @@ def measure(w, K, warmup, BS=0, want_rq=True, want_chained=True, want_bf16=True,
         cur = synth.kv(w, l, T, n_cur, device=dev)
         rk, rv = synth.rotation(w, l, 0), synth.rotation(w, l, 1)
         if want_rq:
-            c = rq.LayerCache.allocate(d_rq, rk, rv, block_table=table, blocked=blocked)
+            c = rq.LayerCache.allocate(d_rq, rk, rv, block_table=table)
             rq.quantize_append(c, past, pos0, T)
             caches.append(c)
         if run_chained:
-            cc = rq.LayerCache.allocate(d_ch, rk, rv, block_table=table, blocked=blocked)
+            cc = rq.LayerCache.allocate(d_ch, rk, rv, block_table=table)
             rq.quantize_append(cc, past, pos0, T)
             chained.append(cc)
         for k in range(K):
@@ -458,20 +451,15 @@ def read_ceiling(caches, d, r, G, bits, gr, T, events, kernel_ms):
     arrays = []
     for c in caches:
         ptrs, bpt = [], []
-        if c.blocks is not None:               # blocked layout: one buffer per stored loop
+        for kv in range(2):
             for comp in comps:
-                ptrs.append(c.blocks[comp].data_ptr())
-                bpt.append(rq.loop_row_bytes(d, comp))
-        else:
-            for kv in range(2):
-                for comp in comps:
-                    ptrs.append(c.codes[kv][comp].data_ptr())
-                    bpt.append(D * bits[comp] // 8)
-                    ptrs.append(c.meta[kv][comp].data_ptr())
-                    bpt.append(D // gr[comp] * 4)
-                    if comp != a:
-                        ptrs.append(c.alpha[kv][comp].data_ptr())
-                        bpt.append(2)
+                ptrs.append(c.codes[kv][comp].data_ptr())
+                bpt.append(D * bits[comp] // 8)
+                ptrs.append(c.meta[kv][comp].data_ptr())
+                bpt.append(D // gr[comp] * 4)
+                if comp != a:
+                    ptrs.append(c.alpha[kv][comp].data_ptr())
+                    bpt.append(2)
         arrays.append(((ctypes.c_void_p * len(ptrs))(*ptrs), (ctypes.c_int * len(bpt))(*bpt), len(ptrs)))
     row = sum(bpt)
     sink = torch.empty(nsplit * B * H, dtype=torch.int32, device="cuda")
@@ -489,7 +477,7 @@ def read_ceiling(caches, d, r, G, bits, gr, T, events, kernel_ms):
     log(f"read ceiling of loop {r + 1}'s traffic: {ms * 1e3:.1f} us, {gbps:.0f} GB/s; kernel/ceiling "
         f"{kernel_ms / ms:.3f}")
     return {"kernel": "read_slots (librq_calib.so): plain non-temporal reads of the call's buffers and slots, same "
-                      "workgroup count, no arithmetic", "buffers": len(bpt),
+                      "workgroup count, no arithmetic",
             "ms_per_launch": ms, "bytes_per_launch": nbytes, "gbps": gbps, "frac_of_peak": gbps / HBM_PEAK_GBPS,
             "decode_kernel_over_ceiling_time": kernel_ms / ms}
 
@@ -529,9 +517,6 @@ def main():
     ap.add_argument("--batch", type=int, default=0, help="override batch (0: workload's)")
     ap.add_argument("--block-size", type=int, default=0,
                     help="paged compressed caches with blocks of this many tokens over a shuffled pool (0: contiguous)")
-    ap.add_argument("--layout", choices=("blocked", "separate"), default="blocked",
-                    help="compressed cache layout: each loop's K/V codes, metadata and alpha in shared blocks "
-                         "of 32 token rows, or one buffer per array (rq.h, rq_layer_cache.block_bytes)")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-chained", action="store_true")
@@ -574,9 +559,8 @@ def main():
     G = w.loop_group
     gr = w.groups_for(bits)
 
-    blocked = args.layout == "blocked"
     res = measure(w, K, args.warmup, BS, want_rq=True, want_chained=not args.no_chained,
-                  want_bf16=not args.no_bf16, want_percall=True, call_reps=args.call_reps, blocked=blocked)
+                  want_bf16=not args.no_bf16, want_percall=True, call_reps=args.call_reps)
     dt_rq = res["rq_s"]
     step_bytes = res["rq_bytes"]
     result = {
@@ -585,7 +569,6 @@ def main():
         "vs_baseline": None, "dtype": "int8+fp32", "data": "synthetic",
         "config": {"workload": w.name, "layers": w.layers, "batch": B, "heads": H, "head_dim": D, "loops": L,
                    "loop_group": G or L, "context": T, "bits": bits, "group": gr, "block_size": BS,
-                   "layout": "blocked (32-row blocks, one buffer per loop)" if blocked else "separate buffers",
                    "codes": "int2/int4 + fp16 scale/offset + fp16 alpha",
                    "arith": "keys: int8 dot products with a 14-bit fixed-point rotated query; values: fp32 "
                             "multiply-adds of fp16-exact codes; fp32 softmax and accumulation"},
@@ -610,11 +593,11 @@ def main():
 
     percall = res["percall"]
     dom = percall[0]
-    traffic = None if BS else profiled_traffic(w.name, dom_kernel_name(D, bits, G, gr, blocked))
+    traffic = None if BS else profiled_traffic(w.name)
     result["roofline"] = {"bound": "hbm", "achieved": dom["kernel_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                           "frac": dom["kernel_gbps"] / HBM_PEAK_GBPS,
                           "traffic": None if traffic is None else traffic["bytes"],
-                          "kernel": dom_kernel_name(D, bits, G, gr, blocked).replace("fused", "fused_paged" if BS else "fused")
+                          "kernel": dom_kernel_name(D, bits, G, gr).replace("fused", "fused_paged" if BS else "fused")
                                     + " (rq_decode_attn_partial, loop 1: "
                                     f"INT{bits[(G or L) - 1]} anchor + INT{bits[0]} residual, K and V)",
                           "bytes_per_launch": dom["bytes"], "ms_per_launch": dom["kernel_ms"],
@@ -692,12 +675,10 @@ def main():
         cs = args.config_steps
         configs = {}
         for name, label in (("ouro_int2_4k", "uniform INT2, B1, 4k"), ("huginn_4k", "Huginn-shaped, B4, 4k")):
-            r = measure(synth.WORKLOADS[name], cs, 2, 0, want_rq=True, want_chained=True, want_bf16=True,
-                        blocked=blocked)
+            r = measure(synth.WORKLOADS[name], cs, 2, 0, want_rq=True, want_chained=True, want_bf16=True)
             configs[name] = sub_record(r, label)
         cap = synth.WORKLOADS["ouro_8k_capacity"]
-        r_rq = measure(cap.with_(batch=128), cs, 2, 0, want_rq=True, want_chained=False, want_bf16=False,
-                       blocked=blocked)
+        r_rq = measure(cap.with_(batch=128), cs, 2, 0, want_rq=True, want_chained=False, want_bf16=False)
         r_bf = measure(cap.with_(batch=32), cs, 2, 0, want_rq=False, want_chained=False, want_bf16=True)
         rec = sub_record(r_rq, "capacity 8k: RQ at batch 128")
         bf = sub_record(r_bf, "capacity 8k: BF16 at batch 32")["bf16"]

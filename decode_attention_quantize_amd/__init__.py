@@ -47,7 +47,7 @@ class Desc(ctypes.Structure):
 class LayerCacheC(ctypes.Structure):
     _fields_ = [("codes", (ctypes.c_void_p * MAX_LOOPS) * 2), ("meta", (ctypes.c_void_p * MAX_LOOPS) * 2),
                 ("alpha", (ctypes.c_void_p * MAX_LOOPS) * 2), ("rot", ctypes.c_void_p * 2),
-                ("block_table", ctypes.c_void_p), ("block_bytes", ctypes.c_int32 * MAX_LOOPS)]
+                ("block_table", ctypes.c_void_p)]
 
 
 def _load():
@@ -58,8 +58,6 @@ def _load():
     P, I, Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     L.rq_buffer_bytes.restype = Z
     L.rq_buffer_bytes.argtypes = [P, ctypes.c_int, ctypes.c_int]
-    L.rq_loop_row_bytes.restype = Z
-    L.rq_loop_row_bytes.argtypes = [P, ctypes.c_int]
     L.rq_workspace_bytes.restype = Z
     L.rq_workspace_bytes.argtypes = [P]
     L.rq_check_desc.restype = ctypes.c_int
@@ -145,12 +143,6 @@ def buffer_bytes(d: Desc, kind: int, loop: int) -> int:
     return lib.rq_buffer_bytes(ctypes.byref(d), kind, loop)
 
 
-def loop_row_bytes(d: Desc, loop: int) -> int:
-    """Bytes of one token row of `loop` over its K and V codes, metadata and alpha;
-    32 times this is one block of the blocked layout (rq.h, rq_layer_cache.block_bytes)."""
-    return lib.rq_loop_row_bytes(ctypes.byref(d), loop)
-
-
 def workspace_bytes(d: Desc) -> int:
     return lib.rq_workspace_bytes(ctypes.byref(d))
 
@@ -182,31 +174,19 @@ def _stream(stream) -> int | None:
     return stream.cuda_stream
 
 
-ROW_BLOCK = 32          # rows per block of the blocked layout (rq.h)
-
-
 @dataclass
 class LayerCache:
-    """Device buffers of one layer's compressed cache (caller-owned, allocated by torch).
-
-    Separate layout (blocked=False): one contiguous tensor per (tensor, loop,
-    array), rows back to back. Blocked layout: one uint8 allocation per loop,
-    `blocks[r]` [rows / 32][32 * loop_row_bytes], each block holding 32 rows of
-    K codes, V codes, K meta, V meta, K alpha, V alpha in turn; codes, meta and
-    alpha are then views [..][T_max / 32][32][...] into it, and the library is
-    told the block size (rq.h, rq_layer_cache.block_bytes). logical() gives any
-    array in row order."""
+    """Device buffers of one layer's compressed cache (caller-owned, allocated by torch)."""
     desc: Desc
     codes: list      # [2][L] uint8 tensors [B][H][T_max][D*bits/8]  (paged: [NB][H][BS][..])
     meta: list       # [2][L] int16 tensors [B][H][T_max][D/g][2] (fp16 bit patterns)
     alpha: list      # [2][L] int16 tensors [B][H][T_max] or None for a group's anchor
     rot: list        # [2] float32 [H][D][D]
     block_table: torch.Tensor | None = None   # paged: int32 [B][T_max / BS]
-    blocks: list | None = None                # blocked layout: [L] uint8 [rows / 32][32 * loop row bytes]
 
     @staticmethod
     def allocate(d: Desc, rot_k: torch.Tensor, rot_v: torch.Tensor, device="cuda",
-                 block_table: torch.Tensor | None = None, blocked: bool = False) -> "LayerCache":
+                 block_table: torch.Tensor | None = None) -> "LayerCache":
         H, D, L = d.heads, d.head_dim, d.loops
         if d.block_size:
             if block_table is None or block_table.dtype != torch.int32:
@@ -214,52 +194,16 @@ class LayerCache:
             lead = (d.num_blocks, H, d.block_size)
         else:
             lead = (d.batch, H, d.max_tokens)
-        blocks = None
-        if blocked:
-            if lead[2] % ROW_BLOCK:
-                raise ValueError("the blocked layout needs max_tokens (or block_size) a multiple of 32")
-            nblk = lead[0] * lead[1] * lead[2] // ROW_BLOCK
-            bl = lead[:2] + (lead[2] // ROW_BLOCK,)
-            blocks = [torch.empty(nblk, ROW_BLOCK * loop_row_bytes(d, r), dtype=torch.uint8, device=device)
-                      for r in range(L)]
-            codes, meta, alpha = [[None] * L for _ in range(2)], [[None] * L for _ in range(2)], \
-                [[None] * L for _ in range(2)]
-            for r in range(L):
-                rb, mb, R = D * d.bits[r] // 8, D // d.group[r] * 4, ROW_BLOCK
-                for kv in range(2):
-                    c0 = kv * R * rb
-                    codes[kv][r] = blocks[r][:, c0:c0 + R * rb].unflatten(1, (R, rb)).unflatten(0, bl)
-                    m0 = 2 * R * rb + kv * R * mb
-                    meta[kv][r] = blocks[r][:, m0:m0 + R * mb].view(torch.int16).unflatten(
-                        1, (R, D // d.group[r], 2)).unflatten(0, bl)
-                    if r != anchor_of(d, r):
-                        a0 = 2 * R * (rb + mb) + kv * 2 * R
-                        alpha[kv][r] = blocks[r][:, a0:a0 + 2 * R].view(torch.int16).unflatten(0, bl)
-        else:
-            codes = [[torch.empty(*lead, D * d.bits[r] // 8, dtype=torch.uint8, device=device)
-                      for r in range(L)] for _ in range(2)]
-            meta = [[torch.empty(*lead, D // d.group[r], 2, dtype=torch.int16, device=device)
-                     for r in range(L)] for _ in range(2)]
-            alpha = [[None if r == anchor_of(d, r) else torch.empty(*lead, dtype=torch.int16, device=device)
-                      for r in range(L)] for _ in range(2)]
+        codes = [[torch.empty(*lead, D * d.bits[r] // 8, dtype=torch.uint8, device=device)
+                  for r in range(L)] for _ in range(2)]
+        meta = [[torch.empty(*lead, D // d.group[r], 2, dtype=torch.int16, device=device)
+                 for r in range(L)] for _ in range(2)]
+        alpha = [[None if r == anchor_of(d, r) else torch.empty(*lead, dtype=torch.int16, device=device)
+                  for r in range(L)] for _ in range(2)]
         rot = [rot_k.to(device=device, dtype=torch.float32).contiguous(),
                rot_v.to(device=device, dtype=torch.float32).contiguous()]
         table = None if not d.block_size else block_table.to(device).contiguous()
-        return LayerCache(d, codes, meta, alpha, rot, table, blocks)
-
-    def logical(self, which: str, kv: int, r: int) -> torch.Tensor | None:
-        """Array `which` ("codes", "meta" or "alpha") of tensor kv, loop r, in row
-        order [B][H][T_max][...] (paged: [NB][H][BS][...]): the array itself in the
-        separate layout, a row-ordered copy in the blocked one."""
-        t = getattr(self, which)[kv][r]
-        if t is None or self.blocks is None:
-            return t
-        lead = self._lead()
-        return t.reshape(lead + tuple(t.shape[4:]))
-
-    def _lead(self):
-        d = self.desc
-        return (d.num_blocks, d.heads, d.block_size) if d.block_size else (d.batch, d.heads, d.max_tokens)
+        return LayerCache(d, codes, meta, alpha, rot, table)
 
     def validate(self):
         """Every buffer's size, dtype and layout against the descriptor (once)."""
@@ -268,8 +212,6 @@ class LayerCache:
         d = self.desc
         if check_desc(d) != OK:
             raise ValueError(f"cache descriptor invalid (status {check_desc(d)})")
-        if self.blocks is not None:
-            self._validate_blocked()
         for kv in range(2):
             for r in range(d.loops):
                 for kind, t, dt, name in ((0, self.codes[kv][r], torch.uint8, "codes"),
@@ -278,8 +220,6 @@ class LayerCache:
                     want = buffer_bytes(d, kind, r)
                     if kind == 2 and r == anchor_of(d, r):
                         continue
-                    if self.blocks is not None:
-                        continue                     # views checked against their loop's blocks above
                     _need(t, None, dt, f"cache {name}[{kv}][{r}]")
                     if t.numel() * t.element_size() != want:
                         raise ValueError(f"cache {name}[{kv}][{r}]: {t.numel() * t.element_size()} bytes, "
@@ -294,49 +234,6 @@ class LayerCache:
         _on_gpu(**bufs)
         self._valid = True
 
-    def _validate_blocked(self):
-        """Blocked layout: each loop's block buffer, and every view into it lying in
-        its own byte range of every block (the rule rq.h states for block_bytes)."""
-        d = self.desc
-        lead = self._lead()
-        R = ROW_BLOCK
-        if lead[2] % R:
-            raise ValueError("the blocked layout needs max_tokens (or block_size) a multiple of 32")
-        bl = lead[:2] + (lead[2] // R,)
-        for r in range(d.loops):
-            blk = self.blocks[r]
-            BB = R * loop_row_bytes(d, r)
-            _need(blk, (bl[0] * bl[1] * bl[2], BB), torch.uint8, f"cache blocks[{r}]")
-            base = blk.data_ptr()
-            spans = []
-            ng = d.head_dim // d.group[r]
-            rb = d.head_dim * d.bits[r] // 8
-            for kv in range(2):
-                for t, width, name, dt, inner, istr in (
-                        (self.codes[kv][r], R * rb, "codes", torch.uint8, (R, rb), (rb, 1)),
-                        (self.meta[kv][r], R * ng * 4, "meta", torch.int16, (R, ng, 2), (2 * ng, 2, 1)),
-                        (self.alpha[kv][r], 2 * R, "alpha", torch.int16, (R,), (1,))):
-                    if t is None:
-                        if name == "alpha" and r == anchor_of(d, r):
-                            continue
-                        raise ValueError(f"cache {name}[{kv}][{r}]: missing")
-                    what = f"cache {name}[{kv}][{r}]"
-                    if not isinstance(t, torch.Tensor) or t.dtype != dt or tuple(t.shape) != bl + inner:
-                        raise ValueError(f"{what}: expected a {dt} view of shape {bl + inner}")
-                    off = t.data_ptr() - base
-                    es = t.element_size()
-                    lead_str = (bl[1] * bl[2] * BB, bl[2] * BB, BB)
-                    if t.untyped_storage().data_ptr() != blk.untyped_storage().data_ptr() or off < 0 \
-                            or off + width > BB \
-                            or any(bl[k] > 1 and t.stride(k) * es != lead_str[k] for k in range(3)) \
-                            or tuple(t.stride()[3:]) != istr:
-                        raise ValueError(f"{what}: not a view of blocks[{r}] within one block")
-                    spans.append((off, off + width, f"{name}[{kv}]"))
-            spans.sort()
-            for (a0, a1, n0), (b0, b1, n1) in zip(spans, spans[1:]):
-                if b0 < a1:
-                    raise ValueError(f"cache blocks[{r}]: {n0} and {n1} overlap")
-
     def c(self) -> LayerCacheC:
         self.validate()
         c = LayerCacheC()
@@ -347,14 +244,9 @@ class LayerCache:
                 c.alpha[kv][r] = _ptr(self.alpha[kv][r])
             c.rot[kv] = _ptr(self.rot[kv])
         c.block_table = _ptr(self.block_table)
-        if self.blocks is not None:
-            for r in range(self.desc.loops):
-                c.block_bytes[r] = self.blocks[r].shape[-1]
         return c
 
     def nbytes(self) -> int:
-        if self.blocks is not None:
-            return sum(t.numel() for t in self.blocks)
         n = 0
         for kv in range(2):
             for r in range(self.desc.loops):

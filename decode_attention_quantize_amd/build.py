@@ -24,8 +24,6 @@ SOURCES = {
     "rq_append.hip": ["-ffp-contract=off", "-fno-honor-nans", "-mno-amdgpu-ieee"],
     "rq_decode.hip": [],
     "rq_decode_paged.hip": [],
-    "rq_decode_blocked.hip": [],
-    "rq_decode_paged_blocked.hip": [],
     "rq_decode_long.hip": [],
     "rq_decode_bf16.hip": [],
     "rq_prefill.hip": [],

@@ -154,36 +154,6 @@ int components(const rq_desc* d, int r, int* loops) {
   return r - a + 1;
 }
 
-// Row widths of loop r's buffers (bytes) and of its six arrays side by side.
-uint32_t code_row_bytes(const rq_desc* d, int r) { return (uint32_t)(d->head_dim * d->bits[r] / 8); }
-uint32_t meta_row_bytes(const rq_desc* d, int r) { return (uint32_t)(d->head_dim / d->group[r] * 4); }
-uint32_t loop_row_bytes(const rq_desc* d, int r) {
-  return 2 * (code_row_bytes(d, r) + meta_row_bytes(d, r)) + (r == anchor_of(d, r) ? 0u : 4u);
-}
-
-// Loop r's layout in a cache: separate arrays (block_bytes 0), or blocks of
-// kRowBlock rows that hold the loop's arrays (a multiple of 16 bytes, at least
-// kRowBlock rows of all six), with whole blocks per (b, h) series or pool page
-// and every block addressable by the decode's 32-bit offsets.
-rq_status check_blocks(const rq_desc* d, const rq_layer_cache* c, int r) {
-  const int32_t BB = c->block_bytes[r];
-  if (BB == 0) return RQ_OK;
-  if (BB < 0 || BB % 16 != 0 || (uint64_t)BB < (uint64_t)kRowBlock * loop_row_bytes(d, r)) return RQ_E_SHAPE;
-  const uint64_t rows = d->block_size ? (uint64_t)d->num_blocks * d->heads * d->block_size : (uint64_t)d->max_tokens;
-  if (d->block_size ? d->block_size % kRowBlock != 0 : d->max_tokens % kRowBlock != 0) return RQ_E_SHAPE;
-  // (a wave's prefetch may address up to eight blocks past the last one; those
-  // loads fall outside the descriptors and return zeros)
-  if ((rows / kRowBlock + 8) * (uint64_t)BB > 0xFFFF0000ull) return RQ_E_SHAPE;
-  return RQ_OK;
-}
-
-// Alignment of loop r's arrays (both layouts): codes 16 bytes, metadata 4 (8
-// for groups of 16), alpha 2.
-bool aligned_loop(const rq_desc* d, const rq_layer_cache* c, int kvi, int r, bool with_alpha) {
-  const uintptr_t ma = d->group[r] == 16 ? 8 : 4;
-  return al(c->codes[kvi][r], 16) && al(c->meta[kvi][r], ma) && (!with_alpha || al(c->alpha[kvi][r], 2));
-}
-
 }  // namespace
 
 extern "C" {
@@ -218,14 +188,8 @@ size_t rq_buffer_bytes(const rq_desc* d, int kind, int loop) {
     case 0: return toks * d->head_dim * d->bits[loop] / 8;
     case 1: return toks * (d->head_dim / d->group[loop]) * 4;
     case 2: return toks * 2;
-    case 3: return toks * loop_row_bytes(d, loop);
   }
   return 0;
-}
-
-size_t rq_loop_row_bytes(const rq_desc* d, int loop) {
-  if (check_plan(d) != RQ_OK || loop < 0 || loop >= d->loops) return 0;
-  return loop_row_bytes(d, loop);
 }
 
 size_t rq_workspace_bytes(const rq_desc* d) {
@@ -246,8 +210,9 @@ rq_status check_append_cache(const rq_desc* d, const rq_layer_cache* c) {
       if (!c->codes[kvi][r] || !c->meta[kvi][r]) return RQ_E_NULL;
       const bool anchor = r == anchor_of(d, r);
       if (!anchor && !c->alpha[kvi][r]) return RQ_E_NULL;
-      if (check_blocks(d, c, r) != RQ_OK) return RQ_E_SHAPE;
-      if (!aligned_loop(d, c, kvi, r, !anchor)) return RQ_E_ALIGN;
+      const uintptr_t ma = d->group[r] == 16 ? 8 : 4;
+      if (!al(c->codes[kvi][r], 16) || !al(c->meta[kvi][r], ma) || (!anchor && !al(c->alpha[kvi][r], 2)))
+        return RQ_E_ALIGN;
     }
   }
   if (d->block_size) {
@@ -271,10 +236,6 @@ rq_status append_layers(const rq_desc* d, const rq_layer_cache* caches, int32_t 
   if (!al(kv, 16) || !al(pos, 4)) return RQ_E_ALIGN;
   for (int l = 0; l < nl; ++l)
     if ((s = check_append_cache(d, &caches[l])) != RQ_OK) return s;
-  // one launch of the per-unit kernel serves many layers with one layout
-  for (int l = 1; l < nl; ++l)
-    for (int r = 0; r < d->loops; ++r)
-      if (caches[l].block_bytes[r] != caches[0].block_bytes[r]) return RQ_E_SHAPE;
   const size_t layer_elems = (size_t)2 * d->loops * d->batch * d->heads * n * d->head_dim;
   const int lbs = d->block_size ? log2_of(d->block_size) : 0;
   const int maxblk = d->block_size ? d->max_tokens / d->block_size : 0;
@@ -299,10 +260,7 @@ rq_status append_layers(const rq_desc* d, const rq_layer_cache* caches, int32_t 
     p.maxblk = maxblk;
     p.lbs = lbs;
     p.num_blocks = d->num_blocks;
-    for (int r = 0; r < d->loops; ++r) {
-      p.bits[r] = d->bits[r];
-      p.blockb[r] = (uint32_t)caches[0].block_bytes[r];
-    }
+    for (int r = 0; r < d->loops; ++r) p.bits[r] = d->bits[r];
     const int stride = unit_stride(d->loops);
     const int per = kUnitSlots / stride;
     for (int l0 = 0; l0 < nl; l0 += per) {
@@ -365,10 +323,7 @@ rq_status append_layers(const rq_desc* d, const rq_layer_cache* caches, int32_t 
       p.lbs = lbs;
       p.num_blocks = d->num_blocks;
     }
-    for (int r = 0; r < d->loops; ++r) {
-      p.bits[r] = d->bits[r];
-      p.blockb[r] = (uint32_t)c->block_bytes[r];
-    }
+    for (int r = 0; r < d->loops; ++r) p.bits[r] = d->bits[r];
     if (launch_append(p, d->head_dim, stream) != 0) return RQ_E_HIP;
   }
   return RQ_OK;
@@ -439,21 +394,19 @@ rq_status decode_partial(const rq_desc* d, const rq_layer_cache* c, int32_t loop
   for (int i = 0; i < nc; ++i) {
     const int r = loops[i];
     if (!c->codes[0][r] || !c->meta[0][r] || !c->codes[1][r] || !c->meta[1][r]) return RQ_E_NULL;
-    if (i > 0 && (!c->alpha[0][r] || !c->alpha[1][r])) return RQ_E_NULL;
-    if (check_blocks(d, c, r) != RQ_OK) return RQ_E_SHAPE;
-    if (!aligned_loop(d, c, 0, r, i > 0) || !aligned_loop(d, c, 1, r, i > 0)) return RQ_E_ALIGN;
+    const uintptr_t ma = d->group[r] == 16 ? 8 : 4;  // metadata of a 32-channel block: 4 or 8 bytes
+    if (!al(c->codes[0][r], 16) || !al(c->codes[1][r], 16) || !al(c->meta[0][r], ma) || !al(c->meta[1][r], ma))
+      return RQ_E_ALIGN;
     p.kcodes[i] = c->codes[0][r];
     p.kmeta[i] = reinterpret_cast<const uint32_t*>(c->meta[0][r]);
     p.vcodes[i] = c->codes[1][r];
     p.vmeta[i] = reinterpret_cast<const uint32_t*>(c->meta[1][r]);
     if (i > 0) {
+      if (!c->alpha[0][r] || !c->alpha[1][r]) return RQ_E_NULL;
+      if (!al(c->alpha[0][r], 2) || !al(c->alpha[1][r], 2)) return RQ_E_ALIGN;
       p.kalpha[i] = c->alpha[0][r];
       p.valpha[i] = c->alpha[1][r];
     }
-    // a call's stored loops are all blocked or none is
-    if ((c->block_bytes[r] != 0) != (c->block_bytes[loops[0]] != 0)) return RQ_E_SHAPE;
-    p.blockb[i] = (uint32_t)c->block_bytes[r];
-    p.blocked = c->block_bytes[r] != 0;
   }
   p.rotk = c->rot[0];
   p.q = q;

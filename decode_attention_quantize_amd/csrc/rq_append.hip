@@ -204,33 +204,14 @@ __device__ __forceinline__ void quantize_pair_t(double v0, double v1, bool lane_
 enum : int { kKind2 = 0, kKind4 = 1, kKind2h = 2 };
 __device__ __forceinline__ int kind_of(int bits, bool g16) { return g16 ? kKind2h : (bits == 4 ? kKind4 : kKind2); }
 
-// Token row `tok` of a loop's codes, metadata and alpha: back to back in each
-// array (bb = 0), or in the blocked layout, rows grouped in blocks of kRowBlock
-// that are bb bytes apart: row tok at (tok / kRowBlock) bb + (tok % kRowBlock)
-// times the array's row width (rq.h, rq_layer_cache.block_bytes).
-__device__ __forceinline__ size_t row_byte(size_t tok, uint32_t width, uint32_t bb) {
-  return bb ? tok / kRowBlock * bb + tok % kRowBlock * width : tok * width;
-}
-template <int D>
-__device__ __forceinline__ uint8_t* code_row(uint8_t* codes, size_t tok, int bits, uint32_t bb) {
-  return codes + row_byte(tok, D * bits / 8, bb);
-}
-template <int D>
-__device__ __forceinline__ uint32_t* meta_row(uint32_t* meta, size_t tok, bool g16, uint32_t bb) {
-  return reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(meta) + row_byte(tok, (g16 ? D / 16 : D / 32) * 4, bb));
-}
-__device__ __forceinline__ uint16_t* alpha_at(uint16_t* alpha, size_t tok, uint32_t bb) {
-  return reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(alpha) + row_byte(tok, 2, bb));
-}
-
 // quantize_pair_t for a loop's kind known at run time (uniform over the wave);
 // codes and meta are the loop's buffers, tok the token's row in them.
 template <int D>
 __device__ __forceinline__ void quantize_pair(double v0, double v1, int bits, bool g16, bool lane_on, int gi, int k,
-                                              uint8_t* codes, uint32_t* meta, size_t tok, uint32_t bb, double& d0,
-                                              double& d1, bool& sat) {
-  uint8_t* row = code_row<D>(codes, tok, bits, bb);
-  uint32_t* mrow = meta_row<D>(meta, tok, g16, bb);
+                                              uint8_t* codes, uint32_t* meta, size_t tok, double& d0, double& d1,
+                                              bool& sat) {
+  uint8_t* row = codes + tok * (size_t)(D * bits / 8);
+  uint32_t* mrow = meta + tok * (size_t)(g16 ? D / 16 : D / 32);
   switch (kind_of(bits, g16)) {
     case kKind4: quantize_pair_t<D, 4, false>(v0, v1, lane_on, gi, k, row, mrow, d0, d1, sat); break;
     case kKind2h: quantize_pair_t<D, 2, true>(v0, v1, lane_on, gi, k, row, mrow, d0, d1, sat); break;
@@ -404,7 +385,7 @@ __global__ __launch_bounds__(kAppendThreads, 1) void append_kernel(AppendParams 
         const double alpha = den > 0.0 ? num / den : 0.0;
         const uint16_t a16 = f16_sat(f64_to_f16<kRoundNearest>(alpha), sat);
         at = f16_to_f64(a16);
-        if (on && k == 0) *alpha_at(p.alpha[kv][r], tok, p.blockb[r]) = a16;
+        if (on && k == 0) p.alpha[kv][r][tok] = a16;
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
           z0[gi] = z0[gi] - at * rf0[gi];
@@ -412,8 +393,8 @@ __global__ __launch_bounds__(kAppendThreads, 1) void append_kernel(AppendParams 
         }
       }
       const bool g16 = (p.g16 >> r) & 1;
-      uint8_t* row = code_row<D>(p.codes[kv][r], tok, p.bits[r], p.blockb[r]);
-      uint32_t* mrow = meta_row<D>(p.meta[kv][r], tok, g16, p.blockb[r]);
+      uint8_t* row = p.codes[kv][r] + tok * (size_t)(D * p.bits[r] / 8);
+      uint32_t* mrow = p.meta[kv][r] + tok * (size_t)(g16 ? D / 16 : D / 32);
       double q0[NG], q1[NG];
       switch (kind_of(p.bits[r], g16)) {
         case kKind4: quantize_row_t<D, 4, false>(z0, z1, on, k, row, mrow, q0, q1, sat); break;
@@ -575,8 +556,8 @@ __global__ __launch_bounds__(256) void append_unit(UnitParams p) {
       const int r = wave + kWaves * j;
       if (r < L && r == anchor_of(r)) {
         double r0, r1;
-        quantize_pair<D>(z0[j], z1[j], p.bits[r], (p.g16 >> r) & 1, lane_on, gi, kk, codes_of(r), meta_of(r), tok,
-                         p.blockb[r], r0, r1, sat);
+        quantize_pair<D>(z0[j], z1[j], p.bits[r], (p.g16 >> r) & 1, lane_on, gi, kk, codes_of(r), meta_of(r), tok, r0,
+                         r1, sat);
         if (!lane_on) r0 = r1 = 0.0;
         const double den = wave_sum_f64(r0 * r0 + r1 * r1);
         if (lane_on) {
@@ -599,9 +580,9 @@ __global__ __launch_bounds__(256) void append_unit(UnitParams p) {
       const double alpha = den > 0.0 ? num / den : 0.0;
       const uint16_t a16 = f16_sat(f64_to_f16<kRoundNearest>(alpha), sat);
       at = f16_to_f64(a16);
-      if (lane == 0) *alpha_at(alpha_of(r), tok, p.blockb[r]) = a16;
+      if (lane == 0) alpha_of(r)[tok] = a16;
       quantize_pair<D>(zz0 - at * r0, zz1 - at * r1, p.bits[r], (p.g16 >> r) & 1, lane_on, gi, kk, codes_of(r),
-                       meta_of(r), tok, p.blockb[r], q0, q1, sat);
+                       meta_of(r), tok, q0, q1, sat);
     };
 
     if (!chain) {

@@ -143,10 +143,7 @@ bool have_decode_kernel(int D, int nc, const int* bits, int limbs, bool paged) {
 
 int launch_decode(const DecodeParams& p, int D, int nc, const int* bits, int limbs, int nsplit, void* stream) {
   if (nc > 4) return launch_decode_long(p, D, nc, bits, limbs, nsplit, stream);
-  if (p.table)
-    return p.blocked ? launch_decode_paged_blocked(p, D, nc, bits, limbs, nsplit, stream)
-                     : launch_decode_paged(p, D, nc, bits, limbs, nsplit, stream);
-  if (p.blocked) return launch_decode_blocked(p, D, nc, bits, limbs, nsplit, stream);
+  if (p.table) return launch_decode_paged(p, D, nc, bits, limbs, nsplit, stream);
   const PlanEntry* e = find_plan(kTable, D, nc, bits, limbs);
   if (!e) return -1;
   const dim3 grid((unsigned)(nsplit * p.B * p.H));

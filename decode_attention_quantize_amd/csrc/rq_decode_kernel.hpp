@@ -268,31 +268,12 @@ struct CompRsrc {
 };
 
 // Contiguous cache: rows [row0, row0 + ntok) of the (b, h) series. Paged cache:
-// row0 = 0 and ntok = every row of the block pool. BLOCKED (rq.h,
-// rq_layer_cache.block_bytes): the component's arrays share blocks of
-// kRowBlock rows, p.blockb[c] bytes each; row0 and ntok are then whole blocks
-// (the series' first row and its capacity, or the pool).
-template <int D, int K, bool BLOCKED>
+// row0 = 0 and ntok = every row of the block pool.
+template <int D, int K>
 __device__ __forceinline__ CompRsrc comp_rsrc(const DecodeParams& p, int c, size_t row0, uint32_t ntok) {
   constexpr int G = kg16(K) ? D / 16 : D / 32;  // metadata words per token
   constexpr uint32_t RB = D * kbits(K) / 8;
   CompRsrc r;
-  if constexpr (BLOCKED) {
-    const uint32_t BB = p.blockb[c];
-    const size_t o = row0 / kRowBlock * BB;
-    const uint32_t n = ntok / kRowBlock * BB;
-    r.kc = make_rsrc(p.kcodes[c] + o, n);
-    r.vc = make_rsrc(p.vcodes[c] + o, n);
-    r.km = make_rsrc(reinterpret_cast<const uint8_t*>(p.kmeta[c]) + o, n);
-    r.vm = make_rsrc(reinterpret_cast<const uint8_t*>(p.vmeta[c]) + o, n);
-    if (c > 0) {
-      r.ka = make_rsrc(reinterpret_cast<const uint8_t*>(p.kalpha[c]) + o, n);
-      r.va = make_rsrc(reinterpret_cast<const uint8_t*>(p.valpha[c]) + o, n);
-    } else {
-      r.ka = r.va = r.kc;
-    }
-    return r;
-  }
   r.kc = make_rsrc(p.kcodes[c] + row0 * RB, ntok * RB);
   r.vc = make_rsrc(p.vcodes[c] + row0 * RB, ntok * RB);
   r.km = make_rsrc(p.kmeta[c] + row0 * G, ntok * G * 4);
@@ -354,75 +335,6 @@ __device__ __forceinline__ void load_comp(CompTile<K>& T, const CompRsrc& r, boo
   }
 }
 
-// Blocked layout: byte offsets, from the descriptors' first block, of this
-// lane's two tokens in one component's codes, metadata and alpha arrays
-// (row i: (i / kRowBlock) BB + (i % kRowBlock) width + the lane block's offset),
-// with scalar parts where they are uniform over the wave.
-struct BlkOffs {
-  uint32_t c0, m0, a0, c1, m1, a1;  // per lane
-  uint32_t s0, s1;                  // uniform: added to token t0's / t1's offsets
-};
-
-template <int D, int K>
-__device__ __forceinline__ void load_comp_blocked(CompTile<K>& T, const CompRsrc& r, bool has_alpha,
-                                                  const BlkOffs& o) {
-  constexpr int BITS = kbits(K);
-  auto ld_codes = [&](__amdgpu_buffer_rsrc_t rs, uint32_t off, uint32_t so) {
-    Words<BITS> x;
-    if constexpr (BITS == 4) {
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, so, kAux);
-      x.w[0] = v.x; x.w[1] = v.y; x.w[2] = v.z; x.w[3] = v.w;
-    } else {
-      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, so, kAux);
-      x.w[0] = v.x; x.w[1] = v.y;
-    }
-    return x;
-  };
-  T.k0 = ld_codes(r.kc, o.c0, o.s0);
-  T.k1 = ld_codes(r.kc, o.c1, o.s1);
-  T.v0 = ld_codes(r.vc, o.c0, o.s0);
-  T.v1 = ld_codes(r.vc, o.c1, o.s1);
-  if constexpr (kg16(K)) {
-    const u32x2 a = __builtin_amdgcn_raw_buffer_load_b64(r.km, o.m0, o.s0, kAux);
-    const u32x2 b = __builtin_amdgcn_raw_buffer_load_b64(r.km, o.m1, o.s1, kAux);
-    const u32x2 c = __builtin_amdgcn_raw_buffer_load_b64(r.vm, o.m0, o.s0, kAux);
-    const u32x2 d = __builtin_amdgcn_raw_buffer_load_b64(r.vm, o.m1, o.s1, kAux);
-    T.km0[0] = a.x; T.km0[1] = a.y; T.km1[0] = b.x; T.km1[1] = b.y;
-    T.vm0[0] = c.x; T.vm0[1] = c.y; T.vm1[0] = d.x; T.vm1[1] = d.y;
-  } else {
-    T.km0[0] = __builtin_amdgcn_raw_buffer_load_b32(r.km, o.m0, o.s0, kAux);
-    T.km1[0] = __builtin_amdgcn_raw_buffer_load_b32(r.km, o.m1, o.s1, kAux);
-    T.vm0[0] = __builtin_amdgcn_raw_buffer_load_b32(r.vm, o.m0, o.s0, kAux);
-    T.vm1[0] = __builtin_amdgcn_raw_buffer_load_b32(r.vm, o.m1, o.s1, kAux);
-  }
-  if (has_alpha) {
-    T.ka0 = __builtin_amdgcn_raw_buffer_load_b16(r.ka, o.a0, o.s0, kAux);
-    T.ka1 = __builtin_amdgcn_raw_buffer_load_b16(r.ka, o.a1, o.s1, kAux);
-    T.va0 = __builtin_amdgcn_raw_buffer_load_b16(r.va, o.a0, o.s0, kAux);
-    T.va1 = __builtin_amdgcn_raw_buffer_load_b16(r.va, o.a1, o.s1, kAux);
-  } else {
-    T.ka0 = T.ka1 = T.va0 = T.va1 = 0x3c00;  // 1.0, unused
-  }
-}
-
-// Offsets of rows i0, i1 (per lane) in a blocked component of kind K.
-template <int D, int K>
-__device__ __forceinline__ BlkOffs blk_offs(uint32_t BB, uint32_t i0, uint32_t i1, uint32_t blk) {
-  constexpr uint32_t RB = D * kbits(K) / 8, MB = (kg16(K) ? D / 16 : D / 32) * 4;
-  constexpr uint32_t CW = 32 * kbits(K) / 8, MW = kg16(K) ? 8 : 4;
-  BlkOffs o;
-  const uint32_t b0 = (i0 / kRowBlock) * BB, b1 = (i1 / kRowBlock) * BB;
-  const uint32_t q0 = i0 % kRowBlock, q1 = i1 % kRowBlock;
-  o.c0 = b0 + q0 * RB + blk * CW;
-  o.m0 = b0 + q0 * MB + blk * MW;
-  o.a0 = b0 + q0 * 2;
-  o.c1 = b1 + q1 * RB + blk * CW;
-  o.m1 = b1 + q1 * MB + blk * MW;
-  o.a1 = b1 + q1 * 2;
-  o.s0 = o.s1 = 0;
-  return o;
-}
-
 // Calls f(integral_constant<int, I>) for I = B .. E-1.
 template <int B, int E, class F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -467,33 +379,6 @@ __device__ __forceinline__ void load_tile(Tile<D, NC, CB>& T, const CompRsrc (&R
   });
 }
 
-// UNIFORM: a contiguous cache whose wave tiles start on block edges (D = 64 and
-// 128): a lane's rows sit at the same place in every tile's blocks, so the lane
-// offsets are fixed (lane[c]) and only the scalar block offsets change; else
-// (D = 96, paged caches) every tile's offsets are computed from the rows.
-template <int D, int NC, uint32_t CB, bool UNIFORM>
-__device__ __forceinline__ void load_tile_blocked(Tile<D, NC, CB>& T, const CompRsrc (&R)[NC], const DecodeParams& p,
-                                                  const BlkOffs (&lane)[NC], uint32_t i0, uint32_t i1, uint32_t blk,
-                                                  uint32_t tblock) {
-  static_for<0, NC>([&](auto ic) {
-    constexpr int c = decltype(ic)::value;
-    constexpr int K = ckind<CB, c>();
-    const uint32_t BB = p.blockb[c];
-    BlkOffs o;
-    if constexpr (UNIFORM) {
-      // token t1 = t0 + TPW: 16 rows further in the same block (D = 128) or the same
-      // row of the next block (D = 64)
-      constexpr int TPW = 64 / (D / 32);
-      o = lane[c];
-      o.s0 = tblock * BB;
-      o.s1 = TPW == kRowBlock ? o.s0 + BB : o.s0;
-    } else {
-      o = blk_offs<D, K>(BB, i0, i1, blk);
-    }
-    load_comp_blocked<D, K>(tc<c>(T), R[c], c > 0, o);
-  });
-}
-
 // Waves per SIMD the register budget is tuned for: three for plans whose tile
 // data is small enough (one INT4 and one INT2 component at most), two otherwise.
 // The 21-bit query (a third of its registers more) does not fit three waves'
@@ -529,7 +414,7 @@ enum : int { kContig = 0, kPagedLane = 1 };
 
 // One (b, h, slot) work item: stream the slot's tokens of the compressed
 // cache and store the slot's partial.
-template <int D, int NC, uint32_t CB, int DEPTH, int MODE, int LIMBS, bool BLOCKED>
+template <int D, int NC, uint32_t CB, int DEPTH, int MODE, int LIMBS>
 __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   constexpr int G = D / 32;
   constexpr int TPW = 64 / G;
@@ -593,17 +478,15 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   // paged cache's descriptors cover the whole pool; a token past the end, or
   // with an invalid block id, is pointed at the first row past the pool, which
   // also loads zeros.
-  // (Blocked layout: the descriptors cover the (b, h) series' blocks, rows
-  // numbered by token; rows past the slot are read and masked, see below.)
-  const size_t row0 = MODE == kContig ? (size_t)bh * p.T_max + (BLOCKED ? 0 : start) : 0;
-  const uint32_t ntok = MODE == kContig ? (BLOCKED ? (uint32_t)p.T_max : (uint32_t)(end - start)) : p.pool_rows;
+  const size_t row0 = MODE == kContig ? (size_t)bh * p.T_max + start : 0;
+  const uint32_t ntok = MODE == kContig ? (uint32_t)(end - start) : p.pool_rows;
   const int pi = lane / G, gi = lane % G;
   const bool lane_on = pi < TPW;
   const int gsel = lane_on ? gi : 0;
   CompRsrc R[NC];
   static_for<0, NC>([&](auto ic) {
     constexpr int c = decltype(ic)::value;
-    R[c] = comp_rsrc<D, ckind<CB, c>(), BLOCKED>(p, c, row0, ntok);
+    R[c] = comp_rsrc<D, ckind<CB, c>()>(p, c, row0, ntok);
   });
 
   constexpr int STRIDE = kWaves * TILE;  // tokens between a wave's consecutive tiles
@@ -631,63 +514,33 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     }
     return ((uint32_t)blk * (uint32_t)p.H + (uint32_t)h) * (1u << p.lbs) + ((uint32_t)t & ((1u << p.lbs) - 1u));
   };
-  // Blocked layout over a contiguous cache with tiles on block edges: this lane's
-  // fixed offsets within a tile's blocks, per component.
-  constexpr bool kUniform = BLOCKED && MODE == kContig && TILE % kRowBlock == 0;
-  BlkOffs lane_offs[NC];
-  if constexpr (kUniform) {
-    static_for<0, NC>([&](auto ic) {
-      constexpr int c = decltype(ic)::value;
-      lane_offs[c] = blk_offs<D, ckind<CB, c>()>(0u, (uint32_t)pi, (uint32_t)(TPW < kRowBlock ? pi + TPW : pi),
-                                                 (uint32_t)gsel);
-    });
-  }
   auto fetch = [&](Tile<D, NC, CB>& T, int base) {
-    if constexpr (BLOCKED) {
-      uint32_t i0 = 0, i1 = 0;
-      if constexpr (MODE == kPagedLane) {
-        const int32_t b0 = tq[0][0], b1 = tq[0][1];
+    Offs o;
+    if constexpr (MODE == kPagedLane) {
+      const int32_t b0 = tq[0][0], b1 = tq[0][1];
 #pragma unroll
-        for (int k = 0; k + 1 < TAHEAD; ++k) {
-          tq[k][0] = tq[k + 1][0];
-          tq[k][1] = tq[k + 1][1];
-        }
-        table_load(base + TAHEAD * STRIDE, tq[TAHEAD - 1]);
-        i0 = page_row(base + pi, b0);
-        i1 = page_row(base + pi + TPW, b1);
-      } else if constexpr (!kUniform) {
-        i0 = (uint32_t)(base + pi);
-        i1 = i0 + TPW;
+      for (int k = 0; k + 1 < TAHEAD; ++k) {
+        tq[k][0] = tq[k + 1][0];
+        tq[k][1] = tq[k + 1][1];
       }
-      load_tile_blocked<D, NC, CB, kUniform>(T, R, p, lane_offs, i0, i1, (uint32_t)gsel,
-                                             (uint32_t)base / kRowBlock);    } else {
-      Offs o;
-      if constexpr (MODE == kPagedLane) {
-        const int32_t b0 = tq[0][0], b1 = tq[0][1];
-#pragma unroll
-        for (int k = 0; k + 1 < TAHEAD; ++k) {
-          tq[k][0] = tq[k + 1][0];
-          tq[k][1] = tq[k + 1][1];
-        }
-        table_load(base + TAHEAD * STRIDE, tq[TAHEAD - 1]);
-        const uint32_t r0 = page_row(base + pi, b0), r1 = page_row(base + pi + TPW, b1);
-        o.c4 = r0 * (D / 2) + gsel * 16;
-        o.c2 = r0 * (D / 4) + gsel * 8;
-        o.m = (r0 * G + gsel) * 4;
-        o.a = r0 * 2;
-        o.c4_1 = r1 * (D / 2) + gsel * 16;
-        o.c2_1 = r1 * (D / 4) + gsel * 8;
-        o.m_1 = (r1 * G + gsel) * 4;
-        o.a_1 = r1 * 2;
-      } else {
-        const uint32_t rel = (uint32_t)(base - start) + (uint32_t)pi;  // row of token t0 in the range
-        o.c4 = rel * (D / 2) + gsel * 16;
-        o.c2 = rel * (D / 4) + gsel * 8;
-        o.m = (rel * G + gsel) * 4;
-        o.a = rel * 2;
-      }
-      load_tile<D, NC, CB, MODE == kPagedLane>(T, R, o);
+      table_load(base + TAHEAD * STRIDE, tq[TAHEAD - 1]);
+      const uint32_t r0 = page_row(base + pi, b0), r1 = page_row(base + pi + TPW, b1);
+      o.c4 = r0 * (D / 2) + gsel * 16;
+      o.c2 = r0 * (D / 4) + gsel * 8;
+      o.m = (r0 * G + gsel) * 4;
+      o.a = r0 * 2;
+      o.c4_1 = r1 * (D / 2) + gsel * 16;
+      o.c2_1 = r1 * (D / 4) + gsel * 8;
+      o.m_1 = (r1 * G + gsel) * 4;
+      o.a_1 = r1 * 2;
+    } else {
+      const uint32_t rel = (uint32_t)(base - start) + (uint32_t)pi;  // row of token t0 in the range
+      o.c4 = rel * (D / 2) + gsel * 16;
+      o.c2 = rel * (D / 4) + gsel * 8;
+      o.m = (rel * G + gsel) * 4;
+      o.a = rel * 2;
     }
+    load_tile<D, NC, CB, MODE == kPagedLane>(T, R, o);
   };
 
   // Each wave keeps DEPTH tiles in flight: tile i is
@@ -877,15 +730,6 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     float Wa[NC][2], Wb[NC][2];  // [component][half of the block]
     auto vweight = [&](auto& C, int c, auto kind_tag) {
       constexpr int KK = decltype(kind_tag)::value;
-      if constexpr (BLOCKED && MODE == kContig) {
-        // rows past the slot hold whatever the caller's buffer holds there; the
-        // weights are zero, but 0 * NaN is not, so their metadata is zeroed
-#pragma unroll
-        for (int hh = 0; hh < (kg16(KK) ? 2 : 1); ++hh) {
-          C.vm0[hh] = ok0 ? C.vm0[hh] : 0u;
-          C.vm1[hh] = ok1 ? C.vm1[hh] : 0u;
-        }
-      }
       const float pb0 = ok0 ? p0 * vb0[c] : 0.0f, pb1 = ok1 ? p1 * vb1[c] : 0.0f;
 #pragma unroll
       for (int hh = 0; hh < (kg16(KK) ? 2 : 1); ++hh) {
@@ -968,16 +812,16 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
                                p.part + ((size_t)bh * p.nsplit + split) * part_floats(D));
 }
 
-template <int D, int NC, uint32_t CB, int DEPTH, int LIMBS, bool BLOCKED = false>
+template <int D, int NC, uint32_t CB, int DEPTH, int LIMBS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_for<NC, CB, LIMBS>()))) void decode_fused(
     DecodeParams p) {
-  decode_body<D, NC, CB, DEPTH, kContig, LIMBS, BLOCKED>(p);
+  decode_body<D, NC, CB, DEPTH, kContig, LIMBS>(p);
 }
 
-template <int D, int NC, uint32_t CB, int DEPTH, int LIMBS, bool BLOCKED = false>
+template <int D, int NC, uint32_t CB, int DEPTH, int LIMBS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_for_paged<NC, CB, LIMBS>()))) void
 decode_fused_paged(DecodeParams p) {
-  decode_body<D, NC, CB, DEPTH, kPagedLane, LIMBS, BLOCKED>(p);
+  decode_body<D, NC, CB, DEPTH, kPagedLane, LIMBS>(p);
 }
 
 

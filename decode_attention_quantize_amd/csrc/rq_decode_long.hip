@@ -23,11 +23,6 @@ namespace {
 const PlanEntry kLongTable[] = {RQ_LONG(64, 2), RQ_LONG(96, 2), RQ_LONG(128, 2),
                                 RQ_LONG(64, 3), RQ_LONG(96, 3), RQ_LONG(128, 3)};
 #undef RQ_E
-// the same chains in the blocked layout (rq_layer_cache.block_bytes)
-#define RQ_E(D, NC, CB, LB) {D, NC, CB, LB, decode_fused<D, NC, CB, RQ_DEPTH, LB, true>}
-const PlanEntry kLongBlockedTable[] = {RQ_LONG(64, 2), RQ_LONG(96, 2), RQ_LONG(128, 2),
-                                       RQ_LONG(64, 3), RQ_LONG(96, 3), RQ_LONG(128, 3)};
-#undef RQ_E
 
 }  // namespace
 
@@ -37,7 +32,7 @@ bool have_decode_kernel_long(int D, int nc, const int* bits, int limbs) {
 
 int launch_decode_long(const DecodeParams& p, int D, int nc, const int* bits, int limbs, int nsplit,
                        void* stream) {
-  const PlanEntry* e = find_plan(p.blocked ? kLongBlockedTable : kLongTable, D, nc, bits, limbs);
+  const PlanEntry* e = find_plan(kLongTable, D, nc, bits, limbs);
   if (!e || p.table) return -1;
   const dim3 grid((unsigned)(nsplit * p.B * p.H));
   hipLaunchKernelGGL(e->fn, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), p);

@@ -20,8 +20,6 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int groups_of(int D) { return D / 32; }
 constexpr int pairs_per_wave(int D) { return 64 / groups_of(D); }
 constexpr int tile_tokens(int D) { return 2 * pairs_per_wave(D); }
-// Rows per block of the blocked cache layout (rq.h, rq_layer_cache.block_bytes).
-constexpr int kRowBlock = 32;
 
 
 // Split of the token axis: every (b, h) has nsplit slots. The slot length is
@@ -74,11 +72,6 @@ struct DecodeParams {
   const uint8_t* vcodes[kMaxComp];
   const uint32_t* vmeta[kMaxComp];
   const uint16_t* valpha[kMaxComp];
-  // blocked = 1: component c's codes, metadata and alpha (K and V alike) share
-  // blocks of kRowBlock rows, blockb[c] bytes each (rq_layer_cache.block_bytes);
-  // 0: each array is its own buffer of back-to-back rows
-  uint32_t blockb[kMaxComp];
-  int blocked;
   const float* rotk;                  // fp32 [H][D][D]
   const uint16_t* q;                  // bf16 [B][H][D]
   const int32_t* past_len;
@@ -117,7 +110,6 @@ struct AppendParams {
   const int32_t* table;     // paged cache: block table [B][maxblk], blocks of 2^lbs tokens; else null
   int maxblk, lbs, num_blocks;
   int bits[RQ_MAX_LOOPS];
-  uint32_t blockb[RQ_MAX_LOOPS];  // per loop: 0 (separate buffers) or the bytes of a block of kRowBlock rows
 };
 
 // One-token (or few-token) appends, one workgroup per (token, head, tensor,
@@ -140,7 +132,6 @@ struct UnitParams {
   int nl;                   // layers in this launch
   int upw;                  // (sequence, token) units per workgroup
   int bits[RQ_MAX_LOOPS];
-  uint32_t blockb[RQ_MAX_LOOPS];  // per loop, the same for every layer of the launch (see AppendParams)
   const void* slot[kUnitSlots];
 };
 static_assert(sizeof(UnitParams) <= 4096, "kernel arguments must stay within 4 KB");
@@ -165,10 +156,6 @@ int launch_append_unit(const UnitParams& p, int D, void* stream);
 // ncomp components of kinds bits[0..ncomp-1], the rotated query in `limbs` 7-bit
 // limbs (2 or 3); returns -1 if no kernel exists.
 int launch_decode(const DecodeParams& p, int D, int ncomp, const int* bits, int limbs, int nsplit, void* stream);
-int launch_decode_blocked(const DecodeParams& p, int D, int ncomp, const int* bits, int limbs, int nsplit,
-                          void* stream);
-int launch_decode_paged_blocked(const DecodeParams& p, int D, int ncomp, const int* bits, int limbs, int nsplit,
-                                void* stream);
 int launch_decode_paged(const DecodeParams& p, int D, int ncomp, const int* bits, int limbs, int nsplit,
                         void* stream);
 int launch_bf16(const Bf16Params& p, int D, int nsplit, void* stream);

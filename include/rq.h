@@ -138,21 +138,7 @@ typedef struct {
  *   a pool [num_blocks][H][BS][row] with the rows above; token t of sequence b,
  *   head h, is row (block_table[b][t / BS] * H + h) * BS + t % BS. Each of a
  *   block's heads thus holds BS consecutive tokens. Every pool buffer must stay
- *   below 4 GiB - 64 KiB (RQ_E_SHAPE otherwise).
- * Blocked layout (block_bytes[r] = BB > 0): the six arrays of loop r share one
- *   allocation. Rows are grouped in blocks of 32 (rows 32j .. 32j+31, row numbers
- *   as above), and row i of an array lies at its pointer + (i / 32) * BB +
- *   (i % 32) * its row width: each block holds 32 rows of every array, each array
- *   contiguous within it, so that a decode reads one stretch of memory per loop
- *   and tile instead of six. The caller places the six arrays at distinct
- *   offsets of the first block (no overlap; the library cannot check this), e.g.
- *   K codes, V codes, K meta, V meta, K alpha, V alpha, BB = 32 *
- *   rq_loop_row_bytes(desc, r). BB is a multiple of 16 and at least 32 *
- *   rq_loop_row_bytes; max_tokens (contiguous) or block_size (paged) is a
- *   multiple of 32; the series' (or pool's) blocks must stay within 32-bit
- *   offsets; alignment as above (RQ_E_SHAPE / RQ_E_ALIGN otherwise). A decode
- *   call's stored loops, and the caches of one multi-layer append, use one
- *   layout. */
+ *   below 4 GiB - 64 KiB (RQ_E_SHAPE otherwise). */
 typedef struct {
   uint8_t* codes[2][RQ_MAX_LOOPS];
   uint16_t* meta[2][RQ_MAX_LOOPS];
@@ -163,20 +149,11 @@ typedef struct {
                                 * holding tokens j*BS .. j*BS+BS-1 of sequence b. Entries covering
                                 * tokens an append writes or a decode reads must lie in
                                 * [0, num_blocks); others are never read. */
-  int32_t block_bytes[RQ_MAX_LOOPS];  /* 0 (separate arrays), or the blocked layout's BB of loop r (above) */
 } rq_layer_cache;
 
 /* Bytes of one cache buffer of `loop` for one tensor (K or V): kind 0 = codes,
- * 1 = meta, 2 = alpha (separate arrays); kind 3 = the blocked layout's one
- * allocation of the loop (rows * rq_loop_row_bytes). Returns 0 if the descriptor
- * or arguments are invalid. */
+ * 1 = meta, 2 = alpha. Returns 0 if the descriptor or arguments are invalid. */
 size_t rq_buffer_bytes(const rq_desc* desc, int kind, int loop);
-
-/* Bytes one token row of `loop` takes over its K and V codes, metadata and alpha
- * (alpha only for loops that are not their group's anchor); 32 times this is the
- * smallest block of the blocked layout (rq_layer_cache.block_bytes). 0 if
- * invalid. */
-size_t rq_loop_row_bytes(const rq_desc* desc, int loop);
 
 /* Bytes of device workspace rq_decode_attn / rq_decode_attn_bf16 need (0 if
  * invalid). The split of the token axis, and so this size, depends on the

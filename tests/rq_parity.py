@@ -115,9 +115,8 @@ def host_copy(cache: rq.LayerCache) -> dict:
     {(kv, loop): (codes, meta, alpha)}."""
     d = cache.desc
     view = (lambda a: logical_rows(cache, a)) if d.block_size else (lambda a: a)
-    arr = cache.logical
-    return {(kv, r): (view(arr("codes", kv, r).cpu().numpy()), view(u16(arr("meta", kv, r))),
-                      None if cache.alpha[kv][r] is None else view(u16(arr("alpha", kv, r))))
+    return {(kv, r): (view(cache.codes[kv][r].cpu().numpy()), view(u16(cache.meta[kv][r])),
+                      None if cache.alpha[kv][r] is None else view(u16(cache.alpha[kv][r])))
             for kv in range(2) for r in range(d.loops)}
 
 
@@ -208,16 +207,16 @@ def max_rel_err(gpu_out: torch.Tensor, ref: dict) -> float:
 
 def build_gpu_layer(X: torch.Tensor, rot_k, rot_v, bits, policy, T_max: int, T: int,
                     steps_of_one: int = 0, pos0=None, chunk: int = 1, loop_group: int = 0,
-                    groups=32, paging=None, blocked: bool = False) -> rq.LayerCache:
+                    groups=32, paging=None) -> rq.LayerCache:
     """Fill a GPU cache with tokens [0, T) of X (bf16 [2][L][B][H][*][D] on the GPU): one
     bulk append of the first T - steps_of_one tokens, then appends of `chunk` tokens
     (the last one shorter) until T. paging = (block_size, num_blocks, block table) makes
-    it a paged cache; blocked stores it in the blocked layout (rq.h)."""
+    it a paged cache."""
     _, L, B, H, _, D = X.shape
     bs, nb, table = paging if paging else (0, 0, None)
     d = rq.make_desc(B, H, D, bits, T_max, policy, group=groups, loop_group=loop_group, block_size=bs,
                      num_blocks=nb)
-    cache = rq.LayerCache.allocate(d, rot_k, rot_v, block_table=table, blocked=blocked)
+    cache = rq.LayerCache.allocate(d, rot_k, rot_v, block_table=table)
     n0 = T - steps_of_one
     pos = torch.zeros(B, dtype=torch.int32, device="cuda") if pos0 is None else pos0
     if n0 > 0:

@@ -513,54 +513,3 @@ def test_read_calibration_library_validation():
     assert call((32, 16), unit=0) == -1
     assert call((32, 16), sink=None) == -1
     assert call((32, 16), b=(ctypes.c_void_p * 2)(0x100000, None)) == -1
-
-
-def test_blocked_layout_sizes_and_validation():
-    """The blocked layout (rq_layer_cache.block_bytes): the loop row width and the
-    one-allocation size, then the checks a blocked cache meets before any launch:
-    the block size (a multiple of 16, at least 32 rows), whole blocks per series
-    or page, 32-bit addressable blocks, one layout per decode call and per
-    multi-layer append."""
-    L, by = rq.lib, ctypes.byref
-    d = _desc(max_tokens=96)                          # B2 H3 D128 [2,2,4,4], Last-loop: anchor loop 3
-    rows = [100, 100, 164, 160]                       # 2 (codes + meta) + 4 bytes of alpha off the anchor
-    assert [rq.loop_row_bytes(d, r) for r in range(4)] == rows
-    assert [rq.buffer_bytes(d, 3, r) for r in range(4)] == [2 * 3 * 96 * w for w in rows]
-    assert rq.loop_row_bytes(d, 4) == 0 and rq.buffer_bytes(d, 4, 0) == 0
-    dg = _desc(head_dim=96, bits=[2, 2, 2, 4], group=[16, 16, 16, 32], policy=1)   # Previous-loop: anchor 0
-    assert [rq.loop_row_bytes(dg, r) for r in range(4)] == [96, 100, 100, 124]
-    ws = rq.workspace_bytes(d)
-
-    def decode(c, loop=0, dd=d, q=FAKE):
-        return L.rq_decode_attn(by(dd), by(c), loop, q, FAKE, FAKE, FAKE, ctypes.c_float(0.1), FAKE, FAKE,
-                                rq.workspace_bytes(dd), None, 0)
-
-    def blocked(dd=d):
-        c = _cache(dd)
-        for r in range(dd.loops):
-            c.block_bytes[r] = 32 * rq.loop_row_bytes(dd, r)
-        return c
-    assert decode(blocked(), q=None) == 1            # a valid blocked cache: a NULL q stops the call
-    for r, bad in ((0, 3184), (0, 3208), (3, 5104), (2, -16), (1, 3201)):   # too small, not a multiple of 16
-        c = blocked()
-        c.block_bytes[r] = bad
-        assert decode(c, loop=r if r < 3 else 0) == 2, (r, bad)
-        assert L.rq_quantize_append(by(d), by(c), FAKE, FAKE, 1, None, 0) == 2, (r, bad)
-    c = blocked()
-    c.block_bytes[0] = 1 << 30                        # 3 blocks of 1 GiB per series: past 32-bit offsets
-    assert decode(c) == 2
-    d100 = _desc(max_tokens=100)                      # series not a whole number of blocks
-    assert decode(blocked(d100), dd=d100) == 2
-    dp = _desc(max_tokens=64, block_size=16, num_blocks=40)
-    cp = blocked(dp)
-    cp.block_table = 0x100000
-    assert decode(cp, dd=dp) == 2                     # pool pages of 16 rows: not whole blocks
-    c = blocked()
-    c.codes[1][0] = 0x100008                          # alignment as in separate arrays
-    assert decode(c) == 10
-    assert L.rq_quantize_append(by(d), by(c), FAKE, FAKE, 1, None, 0) == 10
-    c = blocked()
-    c.block_bytes[3] = 0                              # loop 0 blocked, its anchor (loop 3) separate
-    assert decode(c) == 2
-    arr = (rq.LayerCacheC * 2)(blocked(), _cache(d))  # one multi-layer append, two layouts
-    assert L.rq_quantize_append_layers(by(d), arr, 2, FAKE, FAKE, 1, None, 0) == 2
