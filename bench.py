@@ -163,6 +163,8 @@ def summarize_profile(directory, title, command):
                       r"append_kernel|append_unit|prefill_attn_kernel|prefill_vt_kernel)<[^>]*>)", name)
         if m:
             return m.group(1)
+        if "read_slots" in name:
+            return "read_slots (read-rate calibration, librq_calib.so)"
         if COPY_KERNEL in name:
             return "elementwise " + COPY_KERNEL + " (1 GiB in, 1 GiB out)"
         return "torch/runtime: " + re.sub(r"\s+", " ", name)[:60]
