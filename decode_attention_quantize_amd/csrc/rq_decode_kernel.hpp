@@ -108,6 +108,22 @@ struct QFix {
 __host__ __device__ constexpr int int4_elem(int j, int m, int b) { return (b >> 1) * 16 + 4 * j + 2 * (b & 1) + m; }
 __host__ __device__ constexpr int int2_elem(int j, int s, int b) { return (b >> 1) * 16 + 8 * j + 4 * (b & 1) + s; }
 __host__ __device__ constexpr int int2h_elem(int j, int s, int b) { return 16 * j + 4 * b + s; }
+// Their inverses: word (j * 2 + m, or j * 4 + s) and byte of element e in each table.
+__host__ __device__ constexpr int int4_word(int e) { return ((e & 15) >> 2) * 2 + (e & 1); }
+__host__ __device__ constexpr int int4_byte(int e) { return 2 * (e >> 4) + ((e >> 1) & 1); }
+__host__ __device__ constexpr int int2_word(int e) { return ((e & 15) >> 3) * 4 + (e & 3); }
+__host__ __device__ constexpr int int2_byte(int e) { return 2 * (e >> 4) + ((e >> 2) & 1); }
+__host__ __device__ constexpr int int2h_word(int e) { return (e >> 4) * 4 + (e & 3); }
+__host__ __device__ constexpr int int2h_byte(int e) { return (e >> 2) & 3; }
+constexpr bool tables_invert() {
+  for (int e = 0; e < 32; ++e)
+    if (int4_elem(int4_word(e) >> 1, int4_word(e) & 1, int4_byte(e)) != e ||
+        int2_elem(int2_word(e) >> 2, int2_word(e) & 3, int2_byte(e)) != e ||
+        int2h_elem(int2h_word(e) >> 2, int2h_word(e) & 3, int2h_byte(e)) != e)
+      return false;
+  return true;
+}
+static_assert(tables_invert(), "word and byte positions invert the element maps");
 
 // Component kind, one nibble of a plan: the bit width in bits 0-2, and
 // kGroup16 for INT2 in groups of 16 channels (else one group of 32).
@@ -249,6 +265,17 @@ template <uint32_t CB, int NC>
 constexpr bool any_g16() {
   bool r = false;
   for (int c = 0; c < NC; ++c) r = r || kg16((int)((CB >> (4 * c)) & 0xF));
+  return r;
+}
+
+// Whether some component is BITS wide with the given group size (g16: 16).
+template <uint32_t CB, int NC>
+constexpr bool any_bits(int bits, bool g16) {
+  bool r = false;
+  for (int c = 0; c < NC; ++c) {
+    const int k = (int)((CB >> (4 * c)) & 0xF);
+    r = r || (kbits(k) == bits && kg16(k) == g16);
+  }
   return r;
 }
 
@@ -422,7 +449,6 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   static_assert(TILE == tile_tokens(D), "slot unit must be the wave tile");
   constexpr int REF = ref_bits<CB, NC>();
   __shared__ float red[kWaves][64][33];
-  __shared__ float qr[D];
   __shared__ PartialLds S;
 
   int split, b, h;
@@ -566,7 +592,17 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   __syncthreads();
 
   // ---- q' = scale log2(e) H_K q for this (b, h): two threads per row, each
-  // with half of the row and half of q
+  // with half of the row and half of q. Wave w then holds group w of q' (rows
+  // 32 w .. 32 w + 31, element e in lanes 2e and 2e + 1) and turns it into fixed
+  // point once for the workgroup (per-group exponent): the limbs go into LDS at
+  // the byte positions of the packed words each key table needs (see kdot), and
+  // the group's qsum and scale beside them. qsum, which multiplies the group
+  // offsets, is the sum of the same fixed-point values, so a stored value
+  // o + s c meets one consistent q'.
+  constexpr int QW = 8 * LIMBS;                 // words of one key table of one group
+  constexpr bool T4 = any_bits<CB, NC>(4, false), T2 = any_bits<CB, NC>(2, false), T2H = any_g16<CB, NC>();
+  __shared__ __attribute__((aligned(16))) uint32_t qtab[3][G][QW];  // INT4, INT2, INT2 in groups of 16
+  __shared__ float4 qmeta[G];                   // qsum, scale, qsum of each 16-channel half
   if (rot_on) {
     const int row = tid >> 1, half = tid & 1;
     float a0 = 0.0f, a1 = 0.0f;
@@ -585,67 +621,61 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     }
     float acc = a0 + a1;
     acc += __shfl_xor(acc, 1, 64);
-    if (half == 0) qr[row] = acc * p.scale_log2;
+    const float qv = acc * p.scale_log2;          // q'_e, e = row mod 32, of group `wave`
+    float mx = fabsf(qv);
+#pragma unroll
+    for (int s = 2; s < 64; s <<= 1) mx = fmaxf(mx, __shfl_xor(mx, s, 64));
+    int ex = 0;
+    (void)frexpf(mx, &ex);                        // mx in [2^(ex-1), 2^ex)
+    const int E = mx > 0.0f ? fix_bits<LIMBS>() - ex : 0;  // |q' 2^E| < 2^FIX
+    const float qscale = ldexpf(1.0f, -E);
+    int v = __float2int_rn(ldexpf(qv, E));
+    int vh = v;                                   // sum over the element's 16-channel half
+#pragma unroll
+    for (int s = 2; s < 32; s <<= 1) vh += __shfl_xor(vh, s, 64);
+    const int vo = __shfl_xor(vh, 32, 64);        // and over the other half
+    if (lane == 0) qmeta[wave] = make_float4((float)(vh + vo) * qscale, qscale, (float)vh * qscale, (float)vo * qscale);
+    const int e = row & 31;
+    uint8_t* tb = reinterpret_cast<uint8_t*>(&qtab[0][0][0]);
+#pragma unroll
+    for (int l = LIMBS - 1; l >= 0; --l) {        // balanced base-256 digits, least significant first
+      const int d = l == 0 ? v : ((v + 128) & 255) - 128;
+      v = (v - d) >> 8;
+      const uint8_t byte = (uint8_t)(d & 255);
+      // the even lane of a pair writes the INT4 table, the odd one the INT2 tables
+      if (half == 0) {
+        if constexpr (T4) tb[((0 * G + wave) * QW + int4_word(e) * LIMBS + l) * 4 + int4_byte(e)] = byte;
+      } else {
+        if constexpr (T2) tb[((1 * G + wave) * QW + int2_word(e) * LIMBS + l) * 4 + int2_byte(e)] = byte;
+        if constexpr (T2H) tb[((2 * G + wave) * QW + int2h_word(e) * LIMBS + l) * 4 + int2h_byte(e)] = byte;
+      }
+    }
   }
   __syncthreads();
 
-  // This lane's group of q' in fixed point (per-group exponent). qsum, which
-  // multiplies the group offsets, is the sum of the same fixed-point values, so a
-  // stored value o + s c meets one consistent q'.
+  // This lane's group: its key tables and sums, read back from LDS.
   QFix<LIMBS> Q;
   float qsum, qscale, qsum_h[2];  // qsum_h: the two 16-channel halves of the lane's block
   {
-    float qv[32], mx = 0.0f;
+    const float4 qm = qmeta[gsel];
+    qsum = qm.x;
+    qscale = qm.y;
+    qsum_h[0] = qm.z;
+    qsum_h[1] = qm.w;
+    auto read_table = [&](int t, auto&& put) {
+      const uint4* src = reinterpret_cast<const uint4*>(&qtab[t][gsel][0]);
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      qv[e] = qr[32 * gsel + e];
-      mx = fmaxf(mx, fabsf(qv[e]));
-    }
-    int ex = 0;
-    (void)frexpf(mx, &ex);                          // mx in [2^(ex-1), 2^ex)
-    const int E = mx > 0.0f ? fix_bits<LIMBS>() - ex : 0;  // |q' 2^E| < 2^FIX
-    qscale = ldexpf(1.0f, -E);
-    int lm[LIMBS][32];
-    int vsum = 0, vsum_h[2] = {0, 0};
-#pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      int v = __float2int_rn(ldexpf(qv[e], E));
-      vsum += v;
-      vsum_h[e >> 4] += v;
-#pragma unroll
-      for (int l = LIMBS - 1; l >= 0; --l) {       // balanced base-256 digits, least significant first
-        const int d = l == 0 ? v : ((v + 128) & 255) - 128;
-        lm[l][e] = d;
-        v = (v - d) >> 8;
+      for (int w4 = 0; w4 < QW / 4; ++w4) {
+        const uint4 x = src[w4];
+        put(4 * w4 + 0, x.x);
+        put(4 * w4 + 1, x.y);
+        put(4 * w4 + 2, x.z);
+        put(4 * w4 + 3, x.w);
       }
-    }
-    qsum = (float)vsum * qscale;
-    qsum_h[0] = (float)vsum_h[0] * qscale;
-    qsum_h[1] = (float)vsum_h[1] * qscale;
-    auto pack = [](int a, int b, int c, int d) {
-      return (uint32_t)(a & 255) | ((uint32_t)(b & 255) << 8) | ((uint32_t)(c & 255) << 16) | ((uint32_t)d << 24);
     };
-#pragma unroll
-    for (int l = 0; l < LIMBS; ++l) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-          Q.q4[j][m][l] = pack(lm[l][int4_elem(j, m, 0)], lm[l][int4_elem(j, m, 1)], lm[l][int4_elem(j, m, 2)],
-                               lm[l][int4_elem(j, m, 3)]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int f = 0; f < 4; ++f)
-          Q.q2[j][f][l] = pack(lm[l][int2_elem(j, f, 0)], lm[l][int2_elem(j, f, 1)], lm[l][int2_elem(j, f, 2)],
-                               lm[l][int2_elem(j, f, 3)]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int f = 0; f < 4; ++f)
-          Q.q2h[j][f][l] = pack(lm[l][int2h_elem(j, f, 0)], lm[l][int2h_elem(j, f, 1)],
-                                lm[l][int2h_elem(j, f, 2)], lm[l][int2h_elem(j, f, 3)]);
-    }
+    if constexpr (T4) read_table(0, [&](int w, uint32_t x) { Q.q4[w / (2 * LIMBS)][(w / LIMBS) % 2][w % LIMBS] = x; });
+    if constexpr (T2) read_table(1, [&](int w, uint32_t x) { Q.q2[w / (4 * LIMBS)][(w / LIMBS) % 4][w % LIMBS] = x; });
+    if constexpr (T2H) read_table(2, [&](int w, uint32_t x) { Q.q2h[w / (4 * LIMBS)][(w / LIMBS) % 4][w % LIMBS] = x; });
   }
 
   float acc[32];
