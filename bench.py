@@ -81,14 +81,15 @@ def call_bytes(D, bits, policy, r, G=0, groups=None):
 PROFILED_WORKLOAD = "ouro_16k"       # the workload the committed counter summaries cover
 
 
-def dom_kernel_name(D, bits, G, groups=None):
+def dom_kernel_name(D, bits, G, groups=None, rot16=True):
     """Instance name of the streaming kernel decoding loop 1 (anchor + loop-1 residual);
-    a component's nibble is its bit width, plus 8 for groups of 16 channels."""
+    a component's nibble is its bit width, plus 8 for groups of 16 channels; the last
+    parameter is 1 for rotations stored fp16."""
     G = G or len(bits)
     gs = _groups(bits, groups)
     kind = [b | (8 if g == 16 else 0) for b, g in zip(bits, gs)]
     cb = kind[G - 1] | (kind[0] << 4)
-    return f"decode_fused<{D}, 2, {cb}u, 2, 2>"
+    return f"decode_fused<{D}, 2, {cb}u, 2, 2, {1 if rot16 else 0}>"
 
 
 DOM_KERNEL = dom_kernel_name(128, [2, 2, 4, 4], 0)
@@ -204,7 +205,7 @@ def summarize_profile(directory, title, command):
 
 
 def measure(w, K, warmup, BS=0, want_rq=True, want_chained=True, want_bf16=True, want_percall=False,
-            call_reps=50):
+            call_reps=50, rot16=True, want_rot32=False):
     """Build workload w's caches (untimed) and time K decode steps of the enabled
     paths, each step captured as one HIP graph. Returns a dict of timings; every
     device buffer is released when it returns."""
@@ -229,10 +230,12 @@ def measure(w, K, warmup, BS=0, want_rq=True, want_chained=True, want_bf16=True,
         nblocks = B * (T_max // BS)
         perm = torch.randperm(nblocks, generator=torch.Generator().manual_seed(1234)).to(torch.int32)
         table = perm.view(B, T_max // BS).to(dev)
+    # rotations stored fp16 (as the pages keep the calibrated matrices) or fp32
+    rflag = rq.FLAG_ROT_F16 if rot16 else 0
     d_rq = rq.make_desc(B, H, D, bits, T_max, rq.POLICY_LAST_LOOP, group=gr, loop_group=G, block_size=BS,
-                        num_blocks=nblocks)
+                        num_blocks=nblocks, flags=rflag)
     d_ch = rq.make_desc(B, H, D, cbits, T_max, rq.POLICY_PREV_LOOP, group=cgr, loop_group=G, block_size=BS,
-                        num_blocks=nblocks)
+                        num_blocks=nblocks, flags=rflag)
     # the chained comparator runs where the library has a kernel for every loop's chain
     chain_ok = all(rq.check_decode(d_ch, r) == 0 for r in range(L))
     run_chained = want_chained and chain_ok
@@ -346,6 +349,19 @@ def measure(w, K, warmup, BS=0, want_rq=True, want_chained=True, want_bf16=True,
         del g_rq
         res["rq_bytes"] = sum(call_bytes(D, bits, "last", r, G, gr) for r in range(L)) * H * w.layers * B * mean_ctx
         log(f"{w.name} B{B}: RQ {K} steps in {res['rq_s'] * 1e3:.2f} ms")
+    caches32 = []
+    if want_rq and rot16 and want_rot32:
+        # The same caches with fp32 copies of the fp16 rotations (no RQ_FLAG_ROT_F16):
+        # bit-identical outputs and stores, so only the rotation reads differ.
+        d32 = rq.Desc.from_buffer_copy(d_rq)
+        d32.flags = d_rq.flags & ~rq.FLAG_ROT_F16
+        caches32 = [rq.LayerCache(d32, c.codes, c.meta, c.alpha, [c.rot[0].float(), c.rot[1].float()],
+                                  c.block_table) for c in caches]
+        log(f"{w.name} B{B}: capturing RQ steps with fp32 rotations")
+        g_32 = capture(lambda k: rq_step(k, caches32, ws))
+        res["rq32_s"] = run(g_32)
+        del g_32
+        log(f"{w.name} B{B}: RQ (fp32 rotations) {K} steps in {res['rq32_s'] * 1e3:.2f} ms")
     if want_chained and not chain_ok:
         res["chained_skipped"] = (f"no decode kernel for every loop of the chained plan {cbits} "
                                   f"(groups {cgr}, loop group {G or L}; see rq_check_decode)")
@@ -409,10 +425,13 @@ def measure(w, K, warmup, BS=0, want_rq=True, want_chained=True, want_bf16=True,
                 ms_p = events(lambda i: rq.decode_attn_partial(caches[i % w.layers], r, qs[0, 0, r], past_len,
                                                                scale, ws, flags=rq.FLAG_PRECISE_QUERY))
                 entry["precise_query_kernel_ms"] = ms_p
+                if caches32:
+                    entry["rot_fp32_kernel_ms"] = events(lambda i: rq.decode_attn_partial(
+                        caches32[i % w.layers], r, qs[0, 0, r], past_len, scale, ws))
                 entry["read_ceiling"] = read_ceiling(caches, d_rq, r, G or L, bits, gr, T, events, ms_k)
             percall[r] = entry
         res["percall"] = percall
-    del caches, chained, bf16, bf16_all, kvcur, qs, ws, ws_ch, out
+    del caches, caches32, chained, bf16, bf16_all, kvcur, qs, ws, ws_ch, out
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
@@ -519,6 +538,8 @@ def main():
     ap.add_argument("--batch", type=int, default=0, help="override batch (0: workload's)")
     ap.add_argument("--block-size", type=int, default=0,
                     help="paged compressed caches with blocks of this many tokens over a shuffled pool (0: contiguous)")
+    ap.add_argument("--rot", choices=("fp16", "fp32"), default="fp16",
+                    help="storage of the rotation matrices: fp16 as the pages keep them (App. G), or fp32")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-chained", action="store_true")
@@ -561,8 +582,10 @@ def main():
     G = w.loop_group
     gr = w.groups_for(bits)
 
+    rot16 = args.rot == "fp16"
     res = measure(w, K, args.warmup, BS, want_rq=True, want_chained=not args.no_chained,
-                  want_bf16=not args.no_bf16, want_percall=True, call_reps=args.call_reps)
+                  want_bf16=not args.no_bf16, want_percall=True, call_reps=args.call_reps, rot16=rot16,
+                  want_rot32=True)
     dt_rq = res["rq_s"]
     step_bytes = res["rq_bytes"]
     result = {
@@ -572,6 +595,7 @@ def main():
         "config": {"workload": w.name, "layers": w.layers, "batch": B, "heads": H, "head_dim": D, "loops": L,
                    "loop_group": G or L, "context": T, "bits": bits, "group": gr, "block_size": BS,
                    "codes": "int2/int4 + fp16 scale/offset + fp16 alpha",
+                   "rotation": ("fp16" if rot16 else "fp32") + " [H][D][D] per layer and tensor",
                    "arith": "keys: int8 dot products with a 14-bit fixed-point rotated query; values: fp32 "
                             "multiply-adds of fp16-exact codes; fp32 softmax and accumulation"},
         "hbm_gbps_step": step_bytes / (dt_rq / K) / 1e9,
@@ -587,6 +611,12 @@ def main():
                              "unit": "tokens/s", "ms_per_step": dt_ch * 1e3 / K,
                              "hbm_gbps_step": res["ch_bytes"] / (dt_ch / K) / 1e9,
                              "rq_speedup_over_chained": dt_ch / dt_rq}
+    if "rq32_s" in res:
+        # the same step with the rotations stored fp32 (same values, same outputs)
+        dt_32 = res["rq32_s"]
+        result["rot_fp32"] = {"value": B * K / dt_32, "unit": "tokens/s", "ms_per_step": dt_32 * 1e3 / K,
+                              "loop1_kernel_ms": res["percall"][0].get("rot_fp32_kernel_ms"),
+                              "rot_fp16_speedup": dt_32 / dt_rq}
     if "bf_s" in res:
         dt_bf = res["bf_s"]
         result["bf16"] = {"value": B * K / dt_bf, "unit": "tokens/s", "ms_per_step": dt_bf * 1e3 / K,
@@ -595,11 +625,11 @@ def main():
 
     percall = res["percall"]
     dom = percall[0]
-    traffic = None if BS else profiled_traffic(w.name)
+    traffic = None if BS or not rot16 else profiled_traffic(w.name)
     result["roofline"] = {"bound": "hbm", "achieved": dom["kernel_gbps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                           "frac": dom["kernel_gbps"] / HBM_PEAK_GBPS,
                           "traffic": None if traffic is None else traffic["bytes"],
-                          "kernel": dom_kernel_name(D, bits, G, gr).replace("fused", "fused_paged" if BS else "fused")
+                          "kernel": dom_kernel_name(D, bits, G, gr, rot16).replace("fused", "fused_paged" if BS else "fused")
                                     + " (rq_decode_attn_partial, loop 1: "
                                     f"INT{bits[(G or L) - 1]} anchor + INT{bits[0]} residual, K and V)",
                           "bytes_per_launch": dom["bytes"], "ms_per_launch": dom["kernel_ms"],
@@ -627,7 +657,8 @@ def main():
         pk, pv = Xp[0, 0].contiguous(), Xp[1, 0].contiguous()
         pout = torch.empty(B, H, T, D, dtype=torch.float32, device=dev)
         plens = torch.full((B,), T, dtype=torch.int32, device=dev)
-        d_p = rq.make_desc(B, H, D, bits, T, rq.POLICY_LAST_LOOP, group=gr, loop_group=G)
+        d_p = rq.make_desc(B, H, D, bits, T, rq.POLICY_LAST_LOOP, group=gr, loop_group=G,
+                           flags=rq.FLAG_ROT_F16 if rot16 else 0)
         pws = rq.alloc_prefill_workspace(d_p, T)
         scale = 1.0 / math.sqrt(D)
 
@@ -677,10 +708,12 @@ def main():
         cs = args.config_steps
         configs = {}
         for name, label in (("ouro_int2_4k", "uniform INT2, B1, 4k"), ("huginn_4k", "Huginn-shaped, B4, 4k")):
-            r = measure(synth.WORKLOADS[name], cs, 2, 0, want_rq=True, want_chained=True, want_bf16=True)
+            r = measure(synth.WORKLOADS[name], cs, 2, 0, want_rq=True, want_chained=True, want_bf16=True,
+                        rot16=rot16)
             configs[name] = sub_record(r, label)
         cap = synth.WORKLOADS["ouro_8k_capacity"]
-        r_rq = measure(cap.with_(batch=128), cs, 2, 0, want_rq=True, want_chained=False, want_bf16=False)
+        r_rq = measure(cap.with_(batch=128), cs, 2, 0, want_rq=True, want_chained=False, want_bf16=False,
+                       rot16=rot16)
         r_bf = measure(cap.with_(batch=32), cs, 2, 0, want_rq=False, want_chained=False, want_bf16=True)
         rec = sub_record(r_rq, "capacity 8k: RQ at batch 128")
         bf = sub_record(r_bf, "capacity 8k: BF16 at batch 32")["bf16"]
@@ -702,12 +735,12 @@ def main():
     # ---------------------------------------------------------------- CPU oracle baseline
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, bits, args.cpu_sample_units, args.cpu_seconds, torch, synth,
-                                              1.0 / math.sqrt(D))
+                                              1.0 / math.sqrt(D), rot16)
 
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(w, bits, units, min_seconds, torch, synth, scale):
+def cpu_baseline(w, bits, units, min_seconds, torch, synth, scale, rot16=True):
     """Time the CPU oracle's decode work on a bounded sample of (b, h) series of
     layer 0 (its own cache, built untimed), scaled to the whole step. The sample
     is repeated until at least min_seconds of wall time have been measured."""
@@ -726,7 +759,10 @@ def cpu_baseline(w, bits, units, min_seconds, torch, synth, scale):
     T, L, D = w.T, w.L, w.D
     pairs = [(u // w.heads % w.batch, u % w.heads) for u in range(units)]
     X = synth.kv(w, 0, 0, T + 1, device="cuda")
-    rk, rv = synth.rotation(w, 0, 0).numpy(), synth.rotation(w, 0, 1).numpy()
+    rk, rv = synth.rotation(w, 0, 0), synth.rotation(w, 0, 1)
+    if rot16:                                   # the matrices the GPU path stores
+        rk, rv = rk.half().float(), rv.half().float()
+    rk, rv = rk.numpy(), rv.numpy()
     u16 = lambda t: t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
     Xh = {p: u16(X[:, :, p[0], p[1]]) for p in pairs}
     qn = [u16(synth.query(w, 0, r, 0, device="cpu")) for r in range(L)]

@@ -28,6 +28,7 @@ SCRATCH_BYTES = 8 << 20                  # RQ_SCRATCH_BYTES of rq.h
 POLICY_LAST_LOOP, POLICY_PREV_LOOP, POLICY_FIRST_LOOP = 0, 1, 2
 DEVERR_CAPACITY, DEVERR_LENGTH, DEVERR_BLOCK, DEVERR_RANGE = 1, 2, 4, 8
 FLAG_PRECISE_QUERY = 1
+FLAG_ROT_F16 = 2                         # the cache's rotations are stored fp16 (rq.h RQ_FLAG_ROT_F16)
 
 
 class RQError(RuntimeError):
@@ -108,8 +109,8 @@ def make_desc(batch: int, heads: int, head_dim: int, bits, max_tokens: int,
               policy: int = POLICY_LAST_LOOP, group=32, loop_group: int = 0, block_size: int = 0,
               num_blocks: int = 0, flags: int = 0) -> Desc:
     """Descriptor of one layer's cache; `group` is one size for all loops or one per loop;
-    block_size > 0 makes it a paged cache of num_blocks blocks; flags: FLAG_PRECISE_QUERY
-    (see rq.h)."""
+    block_size > 0 makes it a paged cache of num_blocks blocks; flags: FLAG_PRECISE_QUERY,
+    FLAG_ROT_F16 (see rq.h)."""
     d = Desc()
     d.batch, d.heads, d.head_dim = batch, heads, head_dim
     d.loops, d.max_tokens, d.policy, d.loop_group = len(bits), max_tokens, policy, loop_group
@@ -121,6 +122,11 @@ def make_desc(batch: int, heads: int, head_dim: int, bits, max_tokens: int,
         d.bits[r] = b
         d.group[r] = g
     return d
+
+
+def rot_dtype(d: Desc):
+    """dtype of the cache's rotation matrices under d: float16 with FLAG_ROT_F16, else float32."""
+    return torch.float16 if d.flags & FLAG_ROT_F16 else torch.float32
 
 
 def anchor_of(d: Desc, r: int) -> int:
@@ -181,7 +187,7 @@ class LayerCache:
     codes: list      # [2][L] uint8 tensors [B][H][T_max][D*bits/8]  (paged: [NB][H][BS][..])
     meta: list       # [2][L] int16 tensors [B][H][T_max][D/g][2] (fp16 bit patterns)
     alpha: list      # [2][L] int16 tensors [B][H][T_max] or None for a group's anchor
-    rot: list        # [2] float32 [H][D][D]
+    rot: list        # [2] [H][D][D], float32 (float16 with FLAG_ROT_F16)
     block_table: torch.Tensor | None = None   # paged: int32 [B][T_max / BS]
 
     @staticmethod
@@ -200,8 +206,8 @@ class LayerCache:
                  for r in range(L)] for _ in range(2)]
         alpha = [[None if r == anchor_of(d, r) else torch.empty(*lead, dtype=torch.int16, device=device)
                   for r in range(L)] for _ in range(2)]
-        rot = [rot_k.to(device=device, dtype=torch.float32).contiguous(),
-               rot_v.to(device=device, dtype=torch.float32).contiguous()]
+        rdt = rot_dtype(d)   # fp16 storage rounds the given matrices to fp16
+        rot = [rot_k.to(device=device, dtype=rdt).contiguous(), rot_v.to(device=device, dtype=rdt).contiguous()]
         table = None if not d.block_size else block_table.to(device).contiguous()
         return LayerCache(d, codes, meta, alpha, rot, table)
 
@@ -224,7 +230,7 @@ class LayerCache:
                     if t.numel() * t.element_size() != want:
                         raise ValueError(f"cache {name}[{kv}][{r}]: {t.numel() * t.element_size()} bytes, "
                                          f"the descriptor needs {want}")
-            _need(self.rot[kv], (d.heads, d.head_dim, d.head_dim), torch.float32, f"cache rot[{kv}]")
+            _need(self.rot[kv], (d.heads, d.head_dim, d.head_dim), rot_dtype(d), f"cache rot[{kv}]")
         if d.block_size:
             _need(self.block_table, (d.batch, d.max_tokens // d.block_size), torch.int32, "block_table")
         bufs = {f"cache codes[{kv}][{r}]": self.codes[kv][r] for kv in range(2) for r in range(d.loops)}
@@ -373,8 +379,12 @@ def _need_step(d: Desc, q, past_len, k_cur=None, v_cur=None, out=None, full=True
 
 
 def _with_flags(d: Desc, flags) -> Desc:
-    """The descriptor as passed to a decode call: flags=None keeps the cache's own."""
-    if flags is None or flags == d.flags:
+    """The descriptor as passed to a decode call: flags=None keeps the cache's own; the
+    rotation storage (FLAG_ROT_F16) is the cache's and is never overridden."""
+    if flags is None:
+        return d
+    flags = (flags & ~FLAG_ROT_F16) | (d.flags & FLAG_ROT_F16)
+    if flags == d.flags:
         return d
     c = Desc.from_buffer_copy(d)
     c.flags = flags
@@ -425,7 +435,7 @@ def decode_combine(d: Desc, rot_v, q, k_cur, v_cur, past_len, scale: float, out,
                    stream=None):
     """Second launch of decode_attn: merge the workspace partials with the current token."""
     _need_step(d, q, past_len, k_cur, v_cur, out)
-    _need(rot_v, (d.heads, d.head_dim, d.head_dim), torch.float32, "rot_v", optional=True)
+    _need(rot_v, (d.heads, d.head_dim, d.head_dim), rot_dtype(d), "rot_v", optional=True)
     _need_err(dev_err)
     _need_bytes(workspace, 1, "workspace")
     _on_gpu(rot_v=rot_v, q=q, k_cur=k_cur, v_cur=v_cur, past_len=past_len, out=out, workspace=workspace,

@@ -74,7 +74,7 @@ int log2_of(int x) {
 rq_status check_shape(const rq_desc* d) {
   if (!d) return RQ_E_NULL;
   if (d->batch < 1 || d->heads < 1 || !dim_ok(d->head_dim) || d->loops < 1 || d->loops > RQ_MAX_LOOPS ||
-      d->max_tokens < 1 || (d->flags & ~RQ_FLAG_PRECISE_QUERY) != 0)
+      d->max_tokens < 1 || (d->flags & ~(RQ_FLAG_PRECISE_QUERY | RQ_FLAG_ROT_F16)) != 0)
     return RQ_E_SHAPE;
   return RQ_OK;
 }
@@ -119,7 +119,7 @@ size_t workspace_for(const rq_desc* d) {
 }
 
 CombineParams combine_params(const rq_desc* d, void* ws, const uint16_t* q, const uint16_t* k_cur,
-                             const uint16_t* v_cur, const int32_t* past_len, const float* rotv, float* out,
+                             const uint16_t* v_cur, const int32_t* past_len, const void* rotv, float* out,
                              int32_t* dev_err, float scale_log2) {
   const SplitPlan sp = split_plan(d);
   CombineParams a;
@@ -137,6 +137,7 @@ CombineParams combine_params(const rq_desc* d, void* ws, const uint16_t* q, cons
   a.T_max = d->max_tokens;
   a.unit = sp.unit;
   a.nsplit = sp.nsplit;
+  a.rot_f16 = (d->flags & RQ_FLAG_ROT_F16) ? 1 : 0;
   return a;
 }
 
@@ -260,6 +261,7 @@ rq_status append_layers(const rq_desc* d, const rq_layer_cache* caches, int32_t 
     p.maxblk = maxblk;
     p.lbs = lbs;
     p.num_blocks = d->num_blocks;
+    p.rot_f16 = (d->flags & RQ_FLAG_ROT_F16) ? 1 : 0;
     for (int r = 0; r < d->loops; ++r) p.bits[r] = d->bits[r];
     const int stride = unit_stride(d->loops);
     const int per = kUnitSlots / stride;
@@ -317,6 +319,7 @@ rq_status append_layers(const rq_desc* d, const rq_layer_cache* caches, int32_t 
     p.policy = d->policy;
     p.G = group_len(d);
     p.g16 = g16;
+    p.rot_f16 = (d->flags & RQ_FLAG_ROT_F16) ? 1 : 0;
     if (d->block_size) {
       p.table = c->block_table;
       p.maxblk = maxblk;
@@ -409,6 +412,7 @@ rq_status decode_partial(const rq_desc* d, const rq_layer_cache* c, int32_t loop
     }
   }
   p.rotk = c->rot[0];
+  p.rot_f16 = (d->flags & RQ_FLAG_ROT_F16) ? 1 : 0;
   p.q = q;
   p.past_len = past_len;
   p.part = static_cast<float*>(ws);
@@ -448,7 +452,7 @@ rq_status rq_decode_attn_partial(const rq_desc* d, const rq_layer_cache* c, int3
   return decode_partial(d, c, loop, q, past_len, softmax_scale, ws, ws_bytes, nullptr, stream);
 }
 
-rq_status rq_decode_combine(const rq_desc* d, const float* rot_v, const uint16_t* q, const uint16_t* k_cur,
+rq_status rq_decode_combine(const rq_desc* d, const void* rot_v, const uint16_t* q, const uint16_t* k_cur,
                             const uint16_t* v_cur, const int32_t* past_len, float softmax_scale, float* out,
                             const void* ws, size_t ws_bytes, int32_t* dev_err, void* stream) {
   rq_status s = check_shape(d);

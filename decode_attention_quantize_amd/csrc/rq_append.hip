@@ -235,7 +235,8 @@ constexpr int kAppendWaves = 8;
 constexpr int kAppendThreads = 64 * kAppendWaves;
 constexpr long long kAppendWorkgroups = 256;
 
-template <int D>
+// RH: the rotations are stored fp16 (RQ_FLAG_ROT_F16), else fp32.
+template <int D, int RH>
 __global__ __launch_bounds__(kAppendThreads, 1) void append_kernel(AppendParams p) {
   constexpr int NT = D / 16;        // 16-column tiles of the product
   constexpr int NG = D / 32;        // 32-channel groups
@@ -246,10 +247,18 @@ __global__ __launch_bounds__(kAppendThreads, 1) void append_kernel(AppendParams 
   const int kv = blockIdx.z, h = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   {
-    const float4* Hg = reinterpret_cast<const float4*>(p.rot[kv] + (size_t)h * D * D);
+    // four entries per piece: 16 bytes of fp32 or 8 bytes of fp16 (RQ_FLAG_ROT_F16),
+    // both converted exactly
+    const size_t e0 = (size_t)h * D * D;
     for (int idx = threadIdx.x; idx < D * D / 4; idx += kAppendThreads) {
       const int n = idx / (D / 4), c4 = idx % (D / 4);
-      const float4 v = Hg[idx];
+      float4 v;
+      if constexpr (RH) {
+        const uint2 x = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.rot[kv]) + e0)[idx];
+        v = make_float4(f16lo(x.x), f16hi(x.x), f16lo(x.y), f16hi(x.y));
+      } else {
+        v = reinterpret_cast<const float4*>(static_cast<const float*>(p.rot[kv]) + e0)[idx];
+      }
       double2* dst = reinterpret_cast<double2*>(&Hs[n * HS + 4 * c4]);
       dst[0] = make_double2((double)v.x, (double)v.y);
       dst[1] = make_double2((double)v.z, (double)v.w);
@@ -430,7 +439,7 @@ __global__ __launch_bounds__(kAppendThreads, 1) void append_kernel(AppendParams 
 // (Previous-loop, all groups together). LM bounds the loop count: the LDS
 // footprint grows with it, and at most 8 loops leave room for two workgroups
 // per compute unit at D = 128.
-template <int D, int LM>
+template <int D, int LM, int RH>
 __global__ __launch_bounds__(256) void append_unit(UnitParams p) {
   constexpr int kLoopsPerWave = LM / kWaves;
   constexpr int HS = D + 2;                // padded LDS row: 8-byte aligned pairs, 16 rows cover all banks
@@ -447,7 +456,7 @@ __global__ __launch_bounds__(256) void append_unit(UnitParams p) {
   const void* const* sl = p.slot + (size_t)layer * unit_stride(L);
   const int32_t* table = p.maxblk ? static_cast<const int32_t*>(sl[0]) : nullptr;
   const void* const* st = sl + 1 + kv * (1 + 3 * L);
-  const float* rot = static_cast<const float*>(st[0]);
+  const void* rot = st[0];                 // fp32, or fp16 (RH)
   auto codes_of = [&](int r) { return static_cast<uint8_t*>(const_cast<void*>(st[1 + r])); };
   auto meta_of = [&](int r) { return static_cast<uint32_t*>(const_cast<void*>(st[1 + L + r])); };
   auto alpha_of = [&](int r) { return static_cast<uint16_t*>(const_cast<void*>(st[1 + 2 * L + r])); };
@@ -455,10 +464,20 @@ __global__ __launch_bounds__(256) void append_unit(UnitParams p) {
 
   // ---- stage H (row-major, padded) once for all of the workgroup's units
   {
-    const float4* Hg = reinterpret_cast<const float4*>(rot + (size_t)h * D * D);
+    // four entries per piece: 16 bytes of fp32 or 8 bytes of fp16, converted exactly
     float4 hv[NF];
+    if constexpr (RH) {
+      const uint2* Hg = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(rot) + (size_t)h * D * D);
+      uint2 x[NF];
 #pragma unroll
-    for (int j = 0; j < NF; ++j) hv[j] = Hg[tid + j * kThreads];
+      for (int j = 0; j < NF; ++j) x[j] = Hg[tid + j * kThreads];
+#pragma unroll
+      for (int j = 0; j < NF; ++j) hv[j] = make_float4(f16lo(x[j].x), f16hi(x[j].x), f16lo(x[j].y), f16hi(x[j].y));
+    } else {
+      const float4* Hg = reinterpret_cast<const float4*>(static_cast<const float*>(rot) + (size_t)h * D * D);
+#pragma unroll
+      for (int j = 0; j < NF; ++j) hv[j] = Hg[tid + j * kThreads];
+    }
 #pragma unroll
     for (int j = 0; j < NF; ++j) {
       const int f = 4 * (tid + j * kThreads), n = f / D, k = f % D;
@@ -622,23 +641,22 @@ __global__ __launch_bounds__(256) void append_unit(UnitParams p) {
 
 }  // namespace
 
+namespace {
+template <int D, int RH>
+void launch_unit_d(const UnitParams& p, bool small, const dim3& grid, hipStream_t s) {
+  if (small) hipLaunchKernelGGL((append_unit<D, 8, RH>), grid, dim3(kThreads), 0, s, p);
+  else hipLaunchKernelGGL((append_unit<D, RQ_MAX_LOOPS, RH>), grid, dim3(kThreads), 0, s, p);
+}
+}  // namespace
+
 int launch_append_unit(const UnitParams& p, int D, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)((p.B * p.n + p.upw - 1) / p.upw), (unsigned)p.H, (unsigned)(2 * p.nl));
-  const bool small = p.L <= 8;
+  const bool small = p.L <= 8, rh = p.rot_f16 != 0;
   switch (D) {
-    case 64:
-      if (small) hipLaunchKernelGGL((append_unit<64, 8>), grid, dim3(kThreads), 0, s, p);
-      else hipLaunchKernelGGL((append_unit<64, RQ_MAX_LOOPS>), grid, dim3(kThreads), 0, s, p);
-      break;
-    case 96:
-      if (small) hipLaunchKernelGGL((append_unit<96, 8>), grid, dim3(kThreads), 0, s, p);
-      else hipLaunchKernelGGL((append_unit<96, RQ_MAX_LOOPS>), grid, dim3(kThreads), 0, s, p);
-      break;
-    case 128:
-      if (small) hipLaunchKernelGGL((append_unit<128, 8>), grid, dim3(kThreads), 0, s, p);
-      else hipLaunchKernelGGL((append_unit<128, RQ_MAX_LOOPS>), grid, dim3(kThreads), 0, s, p);
-      break;
+    case 64: rh ? launch_unit_d<64, 1>(p, small, grid, s) : launch_unit_d<64, 0>(p, small, grid, s); break;
+    case 96: rh ? launch_unit_d<96, 1>(p, small, grid, s) : launch_unit_d<96, 0>(p, small, grid, s); break;
+    case 128: rh ? launch_unit_d<128, 1>(p, small, grid, s) : launch_unit_d<128, 0>(p, small, grid, s); break;
     default: return -1;
   }
   return (int)hipGetLastError();
@@ -654,10 +672,20 @@ int launch_append(const AppendParams& p, int D, void* stream) {
   if (chunks > most) chunks = most;
   if (chunks < 1) chunks = 1;
   const dim3 grid((unsigned)chunks, (unsigned)p.H, 2);
+  const dim3 block(kAppendThreads);
   switch (D) {
-    case 64: hipLaunchKernelGGL(append_kernel<64>, grid, dim3(kAppendThreads), 0, s, p); break;
-    case 96: hipLaunchKernelGGL(append_kernel<96>, grid, dim3(kAppendThreads), 0, s, p); break;
-    case 128: hipLaunchKernelGGL(append_kernel<128>, grid, dim3(kAppendThreads), 0, s, p); break;
+    case 64:
+      if (p.rot_f16) hipLaunchKernelGGL((append_kernel<64, 1>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((append_kernel<64, 0>), grid, block, 0, s, p);
+      break;
+    case 96:
+      if (p.rot_f16) hipLaunchKernelGGL((append_kernel<96, 1>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((append_kernel<96, 0>), grid, block, 0, s, p);
+      break;
+    case 128:
+      if (p.rot_f16) hipLaunchKernelGGL((append_kernel<128, 1>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((append_kernel<128, 0>), grid, block, 0, s, p);
+      break;
     default: return -1;
   }
   return (int)hipGetLastError();

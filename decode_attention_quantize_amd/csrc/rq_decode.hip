@@ -22,7 +22,8 @@ namespace {
 // workgroups wrote its partials (both launches map consecutive (b, h) blocks to
 // XCDs in proportion, when their workgroup counts are multiples of the XCD
 // count), where the partials are still in L2.
-template <int D, int COLS>
+// RH: the value rotation is stored fp16 (RQ_FLAG_ROT_F16), else fp32.
+template <int D, int COLS, int RH>
 __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   constexpr int NS = D / COLS;               // workgroups per (b, h)
   constexpr int NR = kThreads / COLS;        // row parts of the product
@@ -61,9 +62,16 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   const uint16_t qh = p.q[qo], kh = p.kcur[qo], vh = p.vcur[(size_t)bh * D + col];
   float hv[RPT];
   if (rot && prod) {
-    const float* Hm = p.rotv + ((size_t)h * D + (size_t)r * RPT) * D + col;
+    const size_t e0 = ((size_t)h * D + (size_t)r * RPT) * D + col;
+    if constexpr (RH) {  // fp16 entries, converted exactly
+      const uint16_t* Hm = static_cast<const uint16_t*>(p.rotv) + e0;
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) hv[i] = Hm[(size_t)i * D];
+      for (int i = 0; i < RPT; ++i) hv[i] = f16u(Hm[(size_t)i * D]);
+    } else {
+      const float* Hm = static_cast<const float*>(p.rotv) + e0;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) hv[i] = Hm[(size_t)i * D];
+    }
   }
 
   if ((raw_len < 0 || raw_len > p.T_max) && h == 0 && slice == 0 && tid == 0 && p.dev_err)
@@ -130,7 +138,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
 }
 
 // ---------------------------------------------------------------- dispatch
-#define RQ_E(D, NC, CB, LB) {D, NC, CB, LB, decode_fused<D, NC, CB, RQ_DEPTH, LB>}
+#define RQ_E(D, NC, CB, LB) \
+  {D, NC, CB, LB, 0, decode_fused<D, NC, CB, RQ_DEPTH, LB, 0>}, {D, NC, CB, LB, 1, decode_fused<D, NC, CB, RQ_DEPTH, LB, 1>}
 const PlanEntry kTable[] = {RQ_PLANS(64), RQ_PLANS(96), RQ_PLANS(128)};
 #undef RQ_E
 
@@ -138,35 +147,36 @@ const PlanEntry kTable[] = {RQ_PLANS(64), RQ_PLANS(96), RQ_PLANS(128)};
 
 bool have_decode_kernel(int D, int nc, const int* bits, int limbs, bool paged) {
   if (nc > 4) return !paged && have_decode_kernel_long(D, nc, bits, limbs);
-  return find_plan(kTable, D, nc, bits, limbs) != nullptr;
+  return find_plan(kTable, D, nc, bits, limbs, 0) != nullptr;
 }
 
 int launch_decode(const DecodeParams& p, int D, int nc, const int* bits, int limbs, int nsplit, void* stream) {
   if (nc > 4) return launch_decode_long(p, D, nc, bits, limbs, nsplit, stream);
   if (p.table) return launch_decode_paged(p, D, nc, bits, limbs, nsplit, stream);
-  const PlanEntry* e = find_plan(kTable, D, nc, bits, limbs);
+  const PlanEntry* e = find_plan(kTable, D, nc, bits, limbs, p.rot_f16);
   if (!e) return -1;
   const dim3 grid((unsigned)(nsplit * p.B * p.H));
   hipLaunchKernelGGL(e->fn, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), p);
   return (int)hipGetLastError();
 }
 
+namespace {
+template <int D, int RH>
+void launch_combine_d(const CombineParams& p, bool narrow, const dim3& grid, hipStream_t s) {
+  if (narrow) hipLaunchKernelGGL((combine_kernel<D, 32, RH>), grid, dim3(kThreads), 0, s, p);
+  else hipLaunchKernelGGL((combine_kernel<D, D, RH>), grid, dim3(kThreads), 0, s, p);
+}
+}  // namespace
+
 int launch_combine(const CombineParams& p, int D, int cols, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)(p.B * p.H * (D / cols)));
-  const bool narrow = cols != D;
+  const bool narrow = cols != D, rh = p.rot_f16 && p.rotv;
   switch (D) {
-    case 64:
-      if (narrow) hipLaunchKernelGGL((combine_kernel<64, 32>), grid, dim3(kThreads), 0, s, p);
-      else hipLaunchKernelGGL((combine_kernel<64, 64>), grid, dim3(kThreads), 0, s, p);
-      break;
-    case 96:
-      if (narrow) hipLaunchKernelGGL((combine_kernel<96, 32>), grid, dim3(kThreads), 0, s, p);
-      else hipLaunchKernelGGL((combine_kernel<96, 96>), grid, dim3(kThreads), 0, s, p);
-      break;
+    case 64: rh ? launch_combine_d<64, 1>(p, narrow, grid, s) : launch_combine_d<64, 0>(p, narrow, grid, s); break;
+    case 96: rh ? launch_combine_d<96, 1>(p, narrow, grid, s) : launch_combine_d<96, 0>(p, narrow, grid, s); break;
     case 128:
-      if (narrow) hipLaunchKernelGGL((combine_kernel<128, 32>), grid, dim3(kThreads), 0, s, p);
-      else hipLaunchKernelGGL((combine_kernel<128, 128>), grid, dim3(kThreads), 0, s, p);
+      rh ? launch_combine_d<128, 1>(p, narrow, grid, s) : launch_combine_d<128, 0>(p, narrow, grid, s);
       break;
     default: return -1;
   }

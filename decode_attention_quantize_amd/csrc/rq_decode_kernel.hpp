@@ -441,7 +441,7 @@ enum : int { kContig = 0, kPagedLane = 1 };
 
 // One (b, h, slot) work item: stream the slot's tokens of the compressed
 // cache and store the slot's partial.
-template <int D, int NC, uint32_t CB, int DEPTH, int MODE, int LIMBS>
+template <int D, int NC, uint32_t CB, int DEPTH, int MODE, int LIMBS, int RH>
 __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   constexpr int G = D / 32;
   constexpr int TPW = 64 / G;
@@ -472,18 +472,33 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   const bool rot_on = tid < 2 * D;
   __shared__ uint4 qs[D / 8];
   uint4 qg = make_uint4(0, 0, 0, 0);
-  float4 hu[RJ], hw[RJ];
+  // The thread's half row of H_K as raw words, four entries per piece: fp32
+  // entries fill a piece, fp16 ones (RH: RQ_FLAG_ROT_F16) its first two words.
+  uint4 hu[RJ], hw[RJ];
   // Loaded by every thread, with clamped indices (only the threads that need
   // them use the values): loads outside branches keep the waits for later
   // loads exact.
   auto load_rotation = [&]() {
     qg = reinterpret_cast<const uint4*>(p.q + (size_t)bh * D)[tid % (D / 8)];
     const int row = min(tid >> 1, D - 1), half = tid & 1;
-    const float4* hr = reinterpret_cast<const float4*>(p.rotk + ((size_t)h * D + row) * D + half * (D / 2));
+    const size_t e0 = ((size_t)h * D + row) * D + half * (D / 2);  // first entry of the half row
+    if constexpr (RH) {
+      const uint2* hr = reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p.rotk) + e0);
 #pragma unroll
-    for (int j = 0; j < RJ; ++j) {
-      hu[j] = hr[2 * j];
-      hw[j] = hr[2 * j + 1];
+      for (int j = 0; j < RJ; ++j) {
+        const uint2 a = hr[2 * j], c = hr[2 * j + 1];
+        hu[j].x = a.x;
+        hu[j].y = a.y;
+        hw[j].x = c.x;
+        hw[j].y = c.y;
+      }
+    } else {
+      const uint4* hr = reinterpret_cast<const uint4*>(static_cast<const float*>(p.rotk) + e0);
+#pragma unroll
+      for (int j = 0; j < RJ; ++j) {
+        hu[j] = hr[2 * j];
+        hw[j] = hr[2 * j + 1];
+      }
     }
   };
   if constexpr (MODE == kContig) {
@@ -606,19 +621,29 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   if (rot_on) {
     const int row = tid >> 1, half = tid & 1;
     float a0 = 0.0f, a1 = 0.0f;
+    // the same products in the same order for either storage (fp16 entries are
+    // converted exactly), so equal matrix values give bit-equal q'
+    auto rotate = [&](auto entries) {
 #pragma unroll
-    for (int j = 0; j < RJ; ++j) {
-      const uint4 w = qs[half * RJ + j];
-      const float4 u = hu[j], v = hw[j];
-      a0 = fmaf(u.x, bf16lo(w.x), a0);
-      a1 = fmaf(u.y, bf16hi(w.x), a1);
-      a0 = fmaf(u.z, bf16lo(w.y), a0);
-      a1 = fmaf(u.w, bf16hi(w.y), a1);
-      a0 = fmaf(v.x, bf16lo(w.z), a0);
-      a1 = fmaf(v.y, bf16hi(w.z), a1);
-      a0 = fmaf(v.z, bf16lo(w.w), a0);
-      a1 = fmaf(v.w, bf16hi(w.w), a1);
-    }
+      for (int j = 0; j < RJ; ++j) {
+        const uint4 w = qs[half * RJ + j];
+        const float4 u = entries(hu[j]), v = entries(hw[j]);
+        a0 = fmaf(u.x, bf16lo(w.x), a0);
+        a1 = fmaf(u.y, bf16hi(w.x), a1);
+        a0 = fmaf(u.z, bf16lo(w.y), a0);
+        a1 = fmaf(u.w, bf16hi(w.y), a1);
+        a0 = fmaf(v.x, bf16lo(w.z), a0);
+        a1 = fmaf(v.y, bf16hi(w.z), a1);
+        a0 = fmaf(v.z, bf16lo(w.w), a0);
+        a1 = fmaf(v.w, bf16hi(w.w), a1);
+      }
+    };
+    if constexpr (RH)
+      rotate([](const uint4& x) { return make_float4(f16lo(x.x), f16hi(x.x), f16lo(x.y), f16hi(x.y)); });
+    else
+      rotate([](const uint4& x) {
+        return make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w));
+      });
     float acc = a0 + a1;
     acc += __shfl_xor(acc, 1, 64);
     const float qv = acc * p.scale_log2;          // q'_e, e = row mod 32, of group `wave`
@@ -842,16 +867,17 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
                                p.part + ((size_t)bh * p.nsplit + split) * part_floats(D));
 }
 
-template <int D, int NC, uint32_t CB, int DEPTH, int LIMBS>
+// RH: the rotation H_K is stored fp16 (RQ_FLAG_ROT_F16), else fp32.
+template <int D, int NC, uint32_t CB, int DEPTH, int LIMBS, int RH>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_for<NC, CB, LIMBS>()))) void decode_fused(
     DecodeParams p) {
-  decode_body<D, NC, CB, DEPTH, kContig, LIMBS>(p);
+  decode_body<D, NC, CB, DEPTH, kContig, LIMBS, RH>(p);
 }
 
-template <int D, int NC, uint32_t CB, int DEPTH, int LIMBS>
+template <int D, int NC, uint32_t CB, int DEPTH, int LIMBS, int RH>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_for_paged<NC, CB, LIMBS>()))) void
 decode_fused_paged(DecodeParams p) {
-  decode_body<D, NC, CB, DEPTH, kPagedLane, LIMBS>(p);
+  decode_body<D, NC, CB, DEPTH, kPagedLane, LIMBS, RH>(p);
 }
 
 
@@ -861,6 +887,7 @@ struct PlanEntry {
   int D, nc;
   uint32_t cb;
   int limbs;
+  int rh;  // rotation stored fp16
   MainFn fn;
 };
 
@@ -868,8 +895,9 @@ struct PlanEntry {
 #define RQ_DEPTH 2
 #endif
 // Plans with kernels: one nibble per component, anchor first (0xA = INT2 in
-// groups of 16). RQ_E(D, NC, CB, LIMBS) names the instance a table entry takes;
-// every plan has a 14-bit (2 limbs) and a 21-bit (3 limbs) query instance.
+// groups of 16). RQ_E(D, NC, CB, LIMBS) gives the table entries of a plan, one
+// per rotation storage (fp32, fp16); every plan has a 14-bit (2 limbs) and a
+// 21-bit (3 limbs) query instance.
 // Covered: one or two components of any kinds (every Last-loop and First-loop
 // plan), and chains of three or four whose INT4 components all precede their
 // INT2 ones, the INT2 ones in one group size (the descending Previous-loop plans).
@@ -884,11 +912,11 @@ struct PlanEntry {
 #define RQ_PLANS(D) RQ_PLANS_L(D, 2), RQ_PLANS_L(D, 3)
 
 template <size_t N>
-const PlanEntry* find_plan(const PlanEntry (&table)[N], int D, int nc, const int* kinds, int limbs) {
+const PlanEntry* find_plan(const PlanEntry (&table)[N], int D, int nc, const int* kinds, int limbs, int rh) {
   uint32_t cb = 0;
   for (int c = 0; c < nc; ++c) cb |= (uint32_t)kinds[c] << (4 * c);
   for (const PlanEntry& e : table)
-    if (e.D == D && e.nc == nc && e.cb == cb && e.limbs == limbs) return &e;
+    if (e.D == D && e.nc == nc && e.cb == cb && e.limbs == limbs && e.rh == rh) return &e;
   return nullptr;
 }
 

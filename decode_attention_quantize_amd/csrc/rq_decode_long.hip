@@ -19,7 +19,8 @@ namespace {
       RQ_E(D, 8, 0x22222224, LB), RQ_E(D, 5, 0x22244, LB), RQ_E(D, 6, 0x222244, LB),                         \
       RQ_E(D, 7, 0x2222244, LB), RQ_E(D, 8, 0x22222244, LB)
 
-#define RQ_E(D, NC, CB, LB) {D, NC, CB, LB, decode_fused<D, NC, CB, RQ_DEPTH, LB>}
+#define RQ_E(D, NC, CB, LB) \
+  {D, NC, CB, LB, 0, decode_fused<D, NC, CB, RQ_DEPTH, LB, 0>}, {D, NC, CB, LB, 1, decode_fused<D, NC, CB, RQ_DEPTH, LB, 1>}
 const PlanEntry kLongTable[] = {RQ_LONG(64, 2), RQ_LONG(96, 2), RQ_LONG(128, 2),
                                 RQ_LONG(64, 3), RQ_LONG(96, 3), RQ_LONG(128, 3)};
 #undef RQ_E
@@ -27,12 +28,12 @@ const PlanEntry kLongTable[] = {RQ_LONG(64, 2), RQ_LONG(96, 2), RQ_LONG(128, 2),
 }  // namespace
 
 bool have_decode_kernel_long(int D, int nc, const int* bits, int limbs) {
-  return find_plan(kLongTable, D, nc, bits, limbs) != nullptr;
+  return find_plan(kLongTable, D, nc, bits, limbs, 0) != nullptr;
 }
 
 int launch_decode_long(const DecodeParams& p, int D, int nc, const int* bits, int limbs, int nsplit,
                        void* stream) {
-  const PlanEntry* e = find_plan(kLongTable, D, nc, bits, limbs);
+  const PlanEntry* e = find_plan(kLongTable, D, nc, bits, limbs, p.rot_f16);
   if (!e || p.table) return -1;
   const dim3 grid((unsigned)(nsplit * p.B * p.H));
   hipLaunchKernelGGL(e->fn, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), p);

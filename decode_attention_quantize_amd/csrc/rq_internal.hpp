@@ -58,11 +58,12 @@ struct CombineParams {
   const uint16_t* q;        // bf16 [B][H][D]
   const uint16_t* kcur;     // bf16 [B][H][D]
   const uint16_t* vcur;     // bf16 [B][H][D]
-  const float* rotv;        // fp32 [H][D][D], or nullptr (no value rotation)
+  const void* rotv;         // [H][D][D] (fp32, or fp16 if rot_f16), or nullptr (no value rotation)
   float* out;               // fp32 [B][H][D]
   int32_t* dev_err;
   float scale_log2;         // softmax scale * log2(e)
   int B, H, T_max, unit, nsplit;
+  int rot_f16;              // rotv holds fp16 entries
 };
 
 struct DecodeParams {
@@ -72,12 +73,13 @@ struct DecodeParams {
   const uint8_t* vcodes[kMaxComp];
   const uint32_t* vmeta[kMaxComp];
   const uint16_t* valpha[kMaxComp];
-  const float* rotk;                  // fp32 [H][D][D]
+  const void* rotk;                   // [H][D][D], fp32 (or fp16 if rot_f16)
   const uint16_t* q;                  // bf16 [B][H][D]
   const int32_t* past_len;
   float* part;
   float scale_log2;
   int B, H, T_max, unit, nsplit;
+  int rot_f16;                        // rotk holds fp16 entries
   // paged cache (table == nullptr: contiguous): block table [B][maxblk], block
   // size 2^lbs tokens, pool of num_blocks blocks = pool_rows rows per buffer
   const int32_t* table;
@@ -100,7 +102,7 @@ struct AppendParams {
   uint8_t* codes[2][RQ_MAX_LOOPS];
   uint32_t* meta[2][RQ_MAX_LOOPS];
   uint16_t* alpha[2][RQ_MAX_LOOPS];
-  const float* rot[2];
+  const void* rot[2];       // [H][D][D] per tensor, fp32 (or fp16 if rot_f16)
   const uint16_t* kv;       // bf16 [2][L][B][H][n][D]
   const int32_t* pos;
   int32_t* dev_err;
@@ -109,6 +111,7 @@ struct AppendParams {
   uint32_t g16;             // bit r: loop r is INT2 in groups of 16 channels (else groups of 32)
   const int32_t* table;     // paged cache: block table [B][maxblk], blocks of 2^lbs tokens; else null
   int maxblk, lbs, num_blocks;
+  int rot_f16;              // the rotations hold fp16 entries
   int bits[RQ_MAX_LOOPS];
 };
 
@@ -131,6 +134,7 @@ struct UnitParams {
   int maxblk, lbs, num_blocks;  // paged cache (block size 2^lbs); maxblk = 0: contiguous
   int nl;                   // layers in this launch
   int upw;                  // (sequence, token) units per workgroup
+  int rot_f16;              // the rotations (slot per tensor) hold fp16 entries
   int bits[RQ_MAX_LOOPS];
   const void* slot[kUnitSlots];
 };

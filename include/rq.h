@@ -97,6 +97,16 @@ typedef enum { RQ_POLICY_LAST_LOOP = 0, RQ_POLICY_PREV_LOOP = 1, RQ_POLICY_FIRST
  * costs a few percent of the streaming kernel's time. Decode calls only. */
 #define RQ_FLAG_PRECISE_QUERY 1
 
+/* Rotation storage: the matrices rq_layer_cache.rot[kv] (and rq_decode_combine's
+ * rot_v) are fp16 instead of fp32, as the learned rotations are stored once
+ * calibrated (App. G: fixed matrices kept in FP16, multiplied with FP16 inputs
+ * and FP32 accumulation). Every kernel converts the entries to fp32/fp64
+ * exactly and keeps its arithmetic, so caches and outputs are bit-identical to
+ * those made with an fp32 copy holding the same values; the matrices take half
+ * the bytes (half the rotation reads of every decode and append call). A
+ * property of the cache: append and decode calls on it must agree. */
+#define RQ_FLAG_ROT_F16 2
+
 /* Shapes and the quantization plan of one layer's cache. */
 typedef struct {
   int32_t batch;       /* B >= 1 */
@@ -112,7 +122,7 @@ typedef struct {
                         * serving engine's paged KV blocks): tokens per block, a power of two in
                         * [16, 4096] dividing max_tokens; see rq_layer_cache.block_table */
   int32_t num_blocks;  /* paged cache: blocks in every buffer's pool (>= 1) */
-  int32_t flags;       /* 0 or RQ_FLAG_PRECISE_QUERY (other bits: RQ_E_SHAPE) */
+  int32_t flags;       /* RQ_FLAG_PRECISE_QUERY | RQ_FLAG_ROT_F16, or 0 (other bits: RQ_E_SHAPE) */
   uint8_t bits[RQ_MAX_LOOPS];   /* bit width per loop (0-based), 2 or 4 (§2.1, §3.4) */
   uint8_t group[RQ_MAX_LOOPS];  /* group size per loop along the rotated head_dim: 32, or 16 for
                                  * 2-bit loops (§5 "Quantization setup": g = 16 for INT2) */
@@ -132,8 +142,9 @@ typedef struct {
  *     dequantized value = o + s*code (§2.1).
  *   alpha[kv][r]: fp16 [B][H][T_max], the LS coefficient; unused (may be NULL)
  *     for the anchor loop of each group.
- *   rot[kv]: fp32 [H][D][D] row-major, z = rot[h] x. Any orthogonal matrix works
- *     (randomized Hadamard, §2.2, or learned rotations such as OptR-H, §3.3).
+ *   rot[kv]: fp32 [H][D][D] row-major (fp16 with RQ_FLAG_ROT_F16), z = rot[h] x.
+ *     Any orthogonal matrix works (randomized Hadamard, §2.2, or learned
+ *     rotations such as OptR-H, §3.3); the kernels use the entries as given.
  * Paged cache (desc.block_size = BS > 0): every codes, meta and alpha buffer is
  *   a pool [num_blocks][H][BS][row] with the rows above; token t of sequence b,
  *   head h, is row (block_table[b][t / BS] * H + h) * BS + t % BS. Each of a
@@ -143,7 +154,7 @@ typedef struct {
   uint8_t* codes[2][RQ_MAX_LOOPS];
   uint16_t* meta[2][RQ_MAX_LOOPS];
   uint16_t* alpha[2][RQ_MAX_LOOPS];
-  const float* rot[2];
+  const void* rot[2];
   const int32_t* block_table;  /* paged cache only (else ignored, may be NULL): device int32
                                 * [B][max_tokens / block_size]; entry [b][j] is the pool block
                                 * holding tokens j*BS .. j*BS+BS-1 of sequence b. Entries covering
@@ -261,14 +272,15 @@ rq_status rq_split_plan(const rq_desc* desc, int32_t* unit, int32_t* nsplit);
  * rq_decode_combine: merges the written slots of each (b, h) with the current
  *   token (score log2(e) * scale * <q, k_cur> in the original domain) and
  *   writes out = (rot_v^T acc + p_cur v_cur) / l, all slots rescaled to one
- *   max. rot_v: fp32 [H][D][D] (the cache's value rotation), or NULL when the
- *   partials are already in the original domain (as rq_decode_attn_bf16's are).
- *   Only batch, heads, head_dim and max_tokens of desc are used; desc must be
- *   the one the partials were made with. The workspace is only read. */
+ *   max. rot_v: [H][D][D] (the cache's value rotation; fp16 when desc has
+ *   RQ_FLAG_ROT_F16, else fp32), or NULL when the partials are already in the
+ *   original domain (as rq_decode_attn_bf16's are). Only batch, heads, head_dim,
+ *   max_tokens and RQ_FLAG_ROT_F16 of desc are used; desc must be the one the
+ *   partials were made with. The workspace is only read. */
 rq_status rq_decode_attn_partial(const rq_desc* desc, const rq_layer_cache* cache, int32_t loop,
                                  const uint16_t* q, const int32_t* past_len, float softmax_scale,
                                  void* workspace, size_t workspace_bytes, void* stream);
-rq_status rq_decode_combine(const rq_desc* desc, const float* rot_v, const uint16_t* q, const uint16_t* k_cur,
+rq_status rq_decode_combine(const rq_desc* desc, const void* rot_v, const uint16_t* q, const uint16_t* k_cur,
                             const uint16_t* v_cur, const int32_t* past_len, float softmax_scale, float* out,
                             const void* workspace, size_t workspace_bytes, int32_t* dev_err, void* stream);
 

@@ -207,16 +207,23 @@ def max_rel_err(gpu_out: torch.Tensor, ref: dict) -> float:
 
 def build_gpu_layer(X: torch.Tensor, rot_k, rot_v, bits, policy, T_max: int, T: int,
                     steps_of_one: int = 0, pos0=None, chunk: int = 1, loop_group: int = 0,
-                    groups=32, paging=None) -> rq.LayerCache:
+                    groups=32, paging=None, flags: int = 0, zero: bool = False) -> rq.LayerCache:
     """Fill a GPU cache with tokens [0, T) of X (bf16 [2][L][B][H][*][D] on the GPU): one
     bulk append of the first T - steps_of_one tokens, then appends of `chunk` tokens
     (the last one shorter) until T. paging = (block_size, num_blocks, block table) makes
-    it a paged cache."""
+    it a paged cache; flags go into the descriptor (FLAG_ROT_F16: rotations stored fp16);
+    zero=True clears every buffer first (rows never written then compare equal)."""
     _, L, B, H, _, D = X.shape
     bs, nb, table = paging if paging else (0, 0, None)
     d = rq.make_desc(B, H, D, bits, T_max, policy, group=groups, loop_group=loop_group, block_size=bs,
-                     num_blocks=nb)
+                     num_blocks=nb, flags=flags)
     cache = rq.LayerCache.allocate(d, rot_k, rot_v, block_table=table)
+    if zero:
+        for kv in range(2):
+            for r in range(L):
+                for t in (cache.codes[kv][r], cache.meta[kv][r], cache.alpha[kv][r]):
+                    if t is not None:
+                        t.zero_()
     n0 = T - steps_of_one
     pos = torch.zeros(B, dtype=torch.int32, device="cuda") if pos0 is None else pos0
     if n0 > 0:

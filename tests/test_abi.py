@@ -46,7 +46,7 @@ def _desc(**kw):
     (dict(bits=[2] * 32), 0), (dict(loop_group=2), 0), (dict(loop_group=4), 0), (dict(loop_group=1), 0),
     (dict(loop_group=3), 2), (dict(loop_group=5), 2), (dict(loop_group=-1), 2),
     (dict(bits=[2] * 32, loop_group=4), 0), (dict(bits=[2] * 32, loop_group=12), 2),
-    (dict(flags=1), 0), (dict(flags=2), 2), (dict(flags=-1), 2),
+    (dict(flags=1), 0), (dict(flags=2), 0), (dict(flags=3), 0), (dict(flags=4), 2), (dict(flags=-1), 2),
 ])
 def test_check_desc(kw, code):
     if code is None:
@@ -513,3 +513,28 @@ def test_read_calibration_library_validation():
     assert call((32, 16), unit=0) == -1
     assert call((32, 16), sink=None) == -1
     assert call((32, 16), b=(ctypes.c_void_p * 2)(0x100000, None)) == -1
+
+
+def test_fp16_rotation_storage_in_the_binding():
+    """FLAG_ROT_F16 (rq.h RQ_FLAG_ROT_F16) makes the cache's rotations fp16 tensors; a
+    tensor of the other dtype is refused; a per-call decode flag never changes the
+    cache's rotation storage."""
+    import torch
+    d16 = _desc(batch=2, heads=3, head_dim=64, bits=[2, 2, 2, 4], max_tokens=64, flags=rq.FLAG_ROT_F16)
+    d32 = _desc(batch=2, heads=3, head_dim=64, bits=[2, 2, 2, 4], max_tokens=64)
+    assert rq.check_desc(d16) == 0 and rq.check_decode(d16, 0) == 0
+    rk = torch.eye(64).expand(3, 64, 64).contiguous()
+    c = rq.LayerCache.allocate(d16, rk, rk, device="cpu")
+    assert c.rot[0].dtype == torch.float16 and c.rot[1].dtype == torch.float16
+    assert rq.rot_dtype(d16) == torch.float16 and rq.rot_dtype(d32) == torch.float32
+    c.rot[1] = rk.clone()
+    with pytest.raises(ValueError, match=r"cache rot\[1\]: expected torch.float16"):
+        c.validate()
+    assert rq._with_flags(d16, rq.FLAG_PRECISE_QUERY).flags == rq.FLAG_PRECISE_QUERY | rq.FLAG_ROT_F16
+    assert rq._with_flags(d16, 0).flags == rq.FLAG_ROT_F16
+    assert rq._with_flags(d32, rq.FLAG_ROT_F16).flags == 0
+    assert rq._with_flags(d16, None) is d16
+    q = torch.zeros(2, 3, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="rot_v: expected torch.float16"):
+        rq.decode_combine(d16, rk, q, q, q, torch.zeros(2, dtype=torch.int32), 0.1, torch.zeros(2, 3, 64),
+                          torch.zeros(256, dtype=torch.uint8))

@@ -53,4 +53,5 @@ def test_default_workload_totals():
     assert sum(per) * 16 * 24 == 385536
     assert per[0] * 8 * 16 * 16384 == 545259520
     assert [bench.call_bytes(128, [4, 4, 2, 2], "prev", r) for r in range(4)] == [160, 324, 424, 524]
-    assert bench.dom_kernel_name(128, bits, 0) == "decode_fused<128, 2, 36u, 2, 2>"
+    assert bench.dom_kernel_name(128, bits, 0) == "decode_fused<128, 2, 36u, 2, 2, 1>"
+    assert bench.dom_kernel_name(128, bits, 0, rot16=False) == "decode_fused<128, 2, 36u, 2, 2, 0>"
