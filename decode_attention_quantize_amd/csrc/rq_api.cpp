@@ -1,6 +1,5 @@
 // Host side of librq: argument validation, buffer sizes, split planning and
 // kernel dispatch for the C ABI declared in include/rq.h.
-#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -52,33 +51,6 @@ SplitPlan split_plan(const rq_desc* d) {
   p.unit = (int)unit;
   p.nsplit = (int)nsplit;
   return p;
-}
-
-#ifndef RQ_BAL_WGS_PER_CU
-#define RQ_BAL_WGS_PER_CU 2
-#endif
-
-BalPlan bal_plan(const rq_desc* d) {
-  // Where nsplit equal slots per (b, h) would give some compute units a whole
-  // slot more than others (B4 H55 at 4096 tokens: 440 workgroups on 256 units,
-  // two slots of 2048 tokens on 184 of them against a mean of 3520 tokens), the
-  // fused decode call cuts the tiles into RQ_BAL_WGS_PER_CU equal chunks per
-  // compute unit instead (rq_device.hpp). Contiguous caches, B <= 64.
-  BalPlan b;
-  b.nwg = 0;
-  b.pmax = 0;
-  if (d->block_size != 0 || d->batch > 64) return b;
-  const SplitPlan sp = split_plan(d);
-  const long long cus = device_cus();
-  const long long bh = (long long)d->batch * d->heads, wgs = bh * sp.nsplit;
-  if (wgs <= cus) return b;
-  const long long most = (wgs + cus - 1) / cus;  // slots on the busiest unit
-  if (most * cus * 100 < wgs * 108) return b;    // within 8 % of even: slots
-  long long nwg = RQ_BAL_WGS_PER_CU * cus;
-  nwg = (nwg + 7) / 8 * 8;
-  b.nwg = (int)nwg;
-  b.pmax = (int)((nwg + bh - 1) / bh + 2);
-  return b;
 }
 
 }  // namespace rq
@@ -142,9 +114,8 @@ int anchor_of(const rq_desc* d, int r) {
 
 size_t workspace_for(const rq_desc* d) {
   const SplitPlan sp = split_plan(d);
-  const BalPlan bp = bal_plan(d);
   const size_t bh = (size_t)d->batch * d->heads;
-  return bh * (size_t)std::max(sp.nsplit, bp.pmax) * part_floats(d->head_dim) * 4;
+  return bh * sp.nsplit * part_floats(d->head_dim) * 4;
 }
 
 CombineParams combine_params(const rq_desc* d, void* ws, const uint16_t* q, const uint16_t* k_cur,
@@ -167,7 +138,6 @@ CombineParams combine_params(const rq_desc* d, void* ws, const uint16_t* q, cons
   a.unit = sp.unit;
   a.nsplit = sp.nsplit;
   a.rot_f16 = (d->flags & RQ_FLAG_ROT_F16) ? 1 : 0;
-  a.nwg = 0;
   return a;
 }
 
@@ -403,10 +373,9 @@ bool decode_supported(const rq_desc* d, int32_t loop) {
   return have_decode_kernel(d->head_dim, nc, kinds, limbs, d->block_size != 0);
 }
 
-// bal: the balanced partition of the fused call (nwg = 0: the documented slots).
 rq_status decode_partial(const rq_desc* d, const rq_layer_cache* c, int32_t loop, const uint16_t* q,
                          const int32_t* past_len, float softmax_scale, void* ws, size_t ws_bytes, int32_t* dev_err,
-                         void* stream, BalPlan bal = BalPlan{0, 0}) {
+                         void* stream) {
   rq_status s = check_plan(d);
   if (s != RQ_OK) return s;
   if (!c) return RQ_E_NULL;
@@ -452,8 +421,7 @@ rq_status decode_partial(const rq_desc* d, const rq_layer_cache* c, int32_t loop
   p.H = d->heads;
   p.T_max = d->max_tokens;
   p.unit = sp.unit;
-  p.nsplit = bal.nwg > 0 ? bal.pmax : sp.nsplit;
-  p.nwg = bal.nwg;
+  p.nsplit = sp.nsplit;
   p.dev_err = dev_err;
   if (d->block_size) {
     if (!c->block_table) return RQ_E_NULL;
@@ -484,13 +452,9 @@ rq_status rq_decode_attn_partial(const rq_desc* d, const rq_layer_cache* c, int3
   return decode_partial(d, c, loop, q, past_len, softmax_scale, ws, ws_bytes, nullptr, stream);
 }
 
-}  // extern "C"
-
-namespace {
-
-rq_status combine_call(const rq_desc* d, const void* rot_v, const uint16_t* q, const uint16_t* k_cur,
-                       const uint16_t* v_cur, const int32_t* past_len, float softmax_scale, float* out,
-                       const void* ws, size_t ws_bytes, int32_t* dev_err, void* stream, BalPlan bal) {
+rq_status rq_decode_combine(const rq_desc* d, const void* rot_v, const uint16_t* q, const uint16_t* k_cur,
+                            const uint16_t* v_cur, const int32_t* past_len, float softmax_scale, float* out,
+                            const void* ws, size_t ws_bytes, int32_t* dev_err, void* stream) {
   rq_status s = check_shape(d);
   if (s != RQ_OK) return s;
   if (!q || !k_cur || !v_cur || !past_len || !out) return RQ_E_NULL;
@@ -499,28 +463,13 @@ rq_status combine_call(const rq_desc* d, const void* rot_v, const uint16_t* q, c
     return RQ_E_ALIGN;
   if (!ws || ws_bytes < workspace_for(d) || ((uintptr_t)ws & 255) != 0) return RQ_E_WORKSPACE;
   if (!std::isfinite(softmax_scale)) return RQ_E_SHAPE;
-  CombineParams cp = combine_params(d, const_cast<void*>(ws), q, k_cur, v_cur, past_len, rot_v, out, dev_err,
-                                    softmax_scale * kLog2e);
-  if (bal.nwg > 0) {
-    cp.nwg = bal.nwg;
-    cp.nsplit = bal.pmax;
-  }
+  const CombineParams cp = combine_params(d, const_cast<void*>(ws), q, k_cur, v_cur, past_len, rot_v, out,
+                                          dev_err, softmax_scale * kLog2e);
   // the value rotation's product spread over D/32 workgroups per (b, h) while
   // that leaves no more workgroups than compute units
   const long long narrow = (long long)d->batch * d->heads * (d->head_dim / 32);
   const int cols = (rot_v && narrow <= device_cus()) ? 32 : d->head_dim;
   return launch_combine(cp, d->head_dim, cols, stream) == 0 ? RQ_OK : RQ_E_HIP;
-}
-
-}  // namespace
-
-extern "C" {
-
-rq_status rq_decode_combine(const rq_desc* d, const void* rot_v, const uint16_t* q, const uint16_t* k_cur,
-                            const uint16_t* v_cur, const int32_t* past_len, float softmax_scale, float* out,
-                            const void* ws, size_t ws_bytes, int32_t* dev_err, void* stream) {
-  return combine_call(d, rot_v, q, k_cur, v_cur, past_len, softmax_scale, out, ws, ws_bytes, dev_err, stream,
-                      BalPlan{0, 0});
 }
 
 }  // extern "C"
@@ -553,15 +502,10 @@ rq_status rq_decode_attn(const rq_desc* d, const rq_layer_cache* c, int32_t loop
   if (s != RQ_OK) return s;
   // Validate everything the second launch needs before enqueuing the first.
   if (!ws || ws_bytes < workspace_for(d) || ((uintptr_t)ws & 255) != 0) return RQ_E_WORKSPACE;
-  // the balanced partition where the slots would load the compute units
-  // unevenly, for the plans of one or two components
-  int loops[RQ_MAX_LOOPS];
-  BalPlan bal = bal_plan(d);
-  if (components(d, loop, loops) > 2) bal = BalPlan{0, 0};
-  s = decode_partial(d, c, loop, q, past_len, softmax_scale, ws, ws_bytes, dev_err, stream, bal);
+  s = decode_partial(d, c, loop, q, past_len, softmax_scale, ws, ws_bytes, dev_err, stream);
   if (s != RQ_OK) return s;
-  return combine_call(d, c->rot[1], q, k_cur, v_cur, past_len, softmax_scale, out, ws, ws_bytes, dev_err, stream,
-                      bal);
+  return rq_decode_combine(d, c->rot[1], q, k_cur, v_cur, past_len, softmax_scale, out, ws, ws_bytes, dev_err,
+                           stream);
 }
 
 }  // extern "C"

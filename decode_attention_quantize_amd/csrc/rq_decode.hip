@@ -77,13 +77,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
   if ((raw_len < 0 || raw_len > p.T_max) && h == 0 && slice == 0 && tid == 0 && p.dev_err)
     atomicOr(p.dev_err, RQ_DEVERR_LENGTH);
   const int len = raw_len < 0 ? 0 : (raw_len > p.T_max ? p.T_max : raw_len);
-  int nvalid = slots_used(len, p.nsplit, p.unit);
-  if (p.nwg > 0) {  // the pieces of the balanced partition (rq_device.hpp)
-    const BalLens L = bal_lengths(p.past_len, p.B, p.T_max, p.unit);
-    const int c = bal_chunk(L, p.H, p.nwg, p.nsplit);
-    const int pre_b = __builtin_amdgcn_readlane(L.pre, b), n_b = __builtin_amdgcn_readlane(L.n, b);
-    nvalid = bal_pieces(n_b, pre_b, L.NB, h, c);
-  }
+  const int nvalid = slots_used(len, p.nsplit, p.unit);
 
   // Online merge of the splits' (m, l, acc) relative to their running max M
   // (the same M and l in every thread).
@@ -144,9 +138,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineParams p) {
 }
 
 // ---------------------------------------------------------------- dispatch
-#define RQ_E(D, NC, CB, LB)                                                                 \
-  {D, NC, CB, LB, 0, decode_fused<D, NC, CB, RQ_DEPTH, LB, 0>, bal_instance<D, NC, CB, LB, 0>()}, \
-      {D, NC, CB, LB, 1, decode_fused<D, NC, CB, RQ_DEPTH, LB, 1>, bal_instance<D, NC, CB, LB, 1>()}
+#define RQ_E(D, NC, CB, LB) \
+  {D, NC, CB, LB, 0, decode_fused<D, NC, CB, RQ_DEPTH, LB, 0>}, {D, NC, CB, LB, 1, decode_fused<D, NC, CB, RQ_DEPTH, LB, 1>}
 const PlanEntry kTable[] = {RQ_PLANS(64), RQ_PLANS(96), RQ_PLANS(128)};
 #undef RQ_E
 
@@ -162,9 +155,8 @@ int launch_decode(const DecodeParams& p, int D, int nc, const int* bits, int lim
   if (p.table) return launch_decode_paged(p, D, nc, bits, limbs, nsplit, stream);
   const PlanEntry* e = find_plan(kTable, D, nc, bits, limbs, p.rot_f16);
   if (!e) return -1;
-  if (p.nwg > 0 && !e->bal) return -1;
-  const dim3 grid((unsigned)(p.nwg > 0 ? p.nwg : nsplit * p.B * p.H));
-  hipLaunchKernelGGL(p.nwg > 0 ? e->bal : e->fn, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), p);
+  const dim3 grid((unsigned)(nsplit * p.B * p.H));
+  hipLaunchKernelGGL(e->fn, grid, dim3(kThreads), 0, static_cast<hipStream_t>(stream), p);
   return (int)hipGetLastError();
 }
 

@@ -441,15 +441,8 @@ enum : int { kContig = 0, kPagedLane = 1 };
 
 // One (b, h, slot) work item: stream the slot's tokens of the compressed
 // cache and store the slot's partial.
-// The piece of one (b, h) a workgroup streams: its partial row `split`, and,
-// with start >= 0, the token range [start, end) (balanced partition), else the
-// slot `split` of the sequence's length (slot_len).
-struct Seg {
-  int b, h, split, start, end;
-};
-
 template <int D, int NC, uint32_t CB, int DEPTH, int MODE, int LIMBS, int RH>
-__device__ __forceinline__ void decode_body(const DecodeParams& p, const Seg sg) {
+__device__ __forceinline__ void decode_body(const DecodeParams& p) {
   constexpr int G = D / 32;
   constexpr int TPW = 64 / G;
   constexpr int TILE = 2 * TPW;
@@ -458,7 +451,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, const Seg sg)
   __shared__ float red[kWaves][64][33];
   __shared__ PartialLds S;
 
-  const int split = sg.split, b = sg.b, h = sg.h;
+  int split, b, h;
+  split_item(p.nsplit, p.B, p.H, split, b, h);
   const int bh = b * p.H + h;
   // the wave index is uniform across the wave: say so, so that tile positions and
   // everything derived from them (paged descriptors) live in scalar registers
@@ -515,11 +509,10 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, const Seg sg)
   // A slot past the sequence's last used one streams nothing and stores no
   // partial; its workgroup still runs to the end (no return with loads in flight).
   len = len < 0 ? 0 : (len > p.T_max ? p.T_max : len);
-  const bool slots = sg.start < 0;
-  const bool active = !slots || split < slots_used(len, p.nsplit, p.unit);  // uniform over the workgroup
+  const bool active = split < slots_used(len, p.nsplit, p.unit);  // uniform over the workgroup
   const int chunk = slot_len(len, p.nsplit, p.unit);
-  const int start = slots ? (active ? split * chunk : 0) : sg.start;
-  const int end = slots ? (active ? min(start + chunk, len) : 0) : sg.end;
+  const int start = active ? split * chunk : 0;
+  const int end = active ? min(start + chunk, len) : 0;
 
   // This workgroup reads rows [start, end) of its (b, h); the descriptors cover
   // exactly that range, so tiles running past its end load zeros (masked). A
@@ -878,65 +871,13 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p, const Seg sg)
 template <int D, int NC, uint32_t CB, int DEPTH, int LIMBS, int RH>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_for<NC, CB, LIMBS>()))) void decode_fused(
     DecodeParams p) {
-  Seg sg;  // nsplit slots per (b, h)
-  split_item(p.nsplit, p.B, p.H, sg.split, sg.b, sg.h);
-  sg.start = -1;
-  sg.end = 0;
-  decode_body<D, NC, CB, DEPTH, kContig, LIMBS, RH>(p, sg);
-}
-
-// The balanced partition (rq_device.hpp; p.nwg workgroups): chunk w of the
-// head-major tile range, one piece per (b, h) it meets. Consecutive workgroup
-// ids go round-robin over the XCDs; each XCD takes a contiguous run of chunks.
-// The launch has two workgroups per compute unit, so the kernel is built for two
-// waves per SIMD: the loop over pieces holds its state in scalar registers and
-// LDS, and the body keeps its registers.
-template <int D, int NC, uint32_t CB, int DEPTH, int LIMBS, int RH>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_fused_bal(DecodeParams p) {
-  __shared__ int bal_n[64], bal_pre[64];  // per sequence: tiles, tiles before it
-  const int i = (int)blockIdx.x;
-  const int w = (p.nwg % kXcds == 0) ? (i % kXcds) * (p.nwg / kXcds) + i / kXcds : i;
-  const BalLens L = bal_lengths(p.past_len, p.B, p.T_max, p.unit);
-  const int c = bal_chunk(L, p.H, p.nwg, p.nsplit), NB = L.NB;
-  int g = w * c;
-  const int ge = min(g + c, p.H * NB);
-  if (g >= ge) return;  // uniform: past the last tile
-  if (threadIdx.x < 64) {
-    bal_n[threadIdx.x] = L.n;
-    bal_pre[threadIdx.x] = L.pre;
-  }
-  __syncthreads();
-  for (;;) {
-    const int h = g / NB, r = g - h * NB;
-    // the sequence holding tile r of head h: the one lane with pre <= r < pre + n
-    const int lane = threadIdx.x & 63, n_l = bal_n[lane], pre_l = bal_pre[lane];
-    const uint64_t hit = __ballot(n_l > 0 && pre_l <= r && r < pre_l + n_l);
-    const int b = (int)__builtin_ctzll(hit);
-    const int pre_b = __builtin_amdgcn_readlane(pre_l, b), n_b = __builtin_amdgcn_readlane(n_l, b);
-    const int t0 = r - pre_b, t1 = min(n_b, t0 + (ge - g));
-    int len = p.past_len[b];
-    len = len < 0 ? 0 : (len > p.T_max ? p.T_max : len);
-    Seg sg;
-    sg.b = b;
-    sg.h = h;
-    sg.split = w - (h * NB + pre_b) / c;
-    sg.start = t0 * p.unit;
-    sg.end = min(t1 * p.unit, len);
-    decode_body<D, NC, CB, DEPTH, kContig, LIMBS, RH>(p, sg);
-    g += t1 - t0;
-    if (g >= ge) break;
-    __syncthreads();  // the next piece rewrites the query tables in LDS
-  }
+  decode_body<D, NC, CB, DEPTH, kContig, LIMBS, RH>(p);
 }
 
 template <int D, int NC, uint32_t CB, int DEPTH, int LIMBS, int RH>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_for_paged<NC, CB, LIMBS>()))) void
 decode_fused_paged(DecodeParams p) {
-  Seg sg;  // paged caches use nsplit slots per (b, h)
-  split_item(p.nsplit, p.B, p.H, sg.split, sg.b, sg.h);
-  sg.start = -1;
-  sg.end = 0;
-  decode_body<D, NC, CB, DEPTH, kPagedLane, LIMBS, RH>(p, sg);
+  decode_body<D, NC, CB, DEPTH, kPagedLane, LIMBS, RH>(p);
 }
 
 
@@ -948,19 +889,11 @@ struct PlanEntry {
   int limbs;
   int rh;  // rotation stored fp16
   MainFn fn;
-  MainFn bal;  // balanced-partition instance (plans of one or two components), or null
 };
-
 
 #ifndef RQ_DEPTH
 #define RQ_DEPTH 2
 #endif
-// the balanced-partition instance of a plan (one or two components), else null
-template <int D, int NC, uint32_t CB, int LB, int RH>
-constexpr MainFn bal_instance() {
-  if constexpr (NC <= 2) return decode_fused_bal<D, NC, CB, RQ_DEPTH, LB, RH>;
-  else return nullptr;
-}
 // Plans with kernels: one nibble per component, anchor first (0xA = INT2 in
 // groups of 16). RQ_E(D, NC, CB, LIMBS) gives the table entries of a plan, one
 // per rotation storage (fp32, fp16); every plan has a 14-bit (2 limbs) and a

@@ -87,54 +87,6 @@ __device__ __forceinline__ void split_item(int nsplit, int B, int H, int& split,
   h = rest / B;
 }
 
-// Balanced partition of one fused decode call. The tiles of every (b, h) are laid
-// end to end, head-major: (h, b) covers tiles [h NB + pre_b, h NB + pre_b + n_b)
-// of N = H NB, where n_b = ceil(len_b / unit) and pre_b = n_0 + .. + n_{b-1}.
-// Workgroup w streams tiles [w c, (w + 1) c) of that range, a piece of each
-// (b, h) it meets, and stores one partial per piece, at row w - floor(P / c) of
-// the (b, h) (P = its first tile), so a (b, h) of n tiles has pieces
-// floor(P / c) .. floor((P + n - 1) / c). The chunk c is at least
-// ceil(N / nwg), kBalMinTiles, and ceil(n_max / (pmax - 1)), so that no
-// (b, h) has more than pmax pieces. Every compute unit then streams nearly the
-// same number of tiles, whatever B H is. Needs B <= 64 (one sequence per lane).
-constexpr int kBalMinTiles = 8;
-struct BalLens {
-  int n, pre;       // this lane's sequence (lane < B): tiles and tiles before it
-  int NB, nmax;     // wave-uniform: tiles of one head, the longest sequence's tiles
-};
-__device__ __forceinline__ BalLens bal_lengths(const int32_t* past_len, int B, int T_max, int unit) {
-  const int lane = threadIdx.x & 63;
-  int len = past_len[lane < B ? lane : 0];
-  len = (lane < B) ? (len < 0 ? 0 : (len > T_max ? T_max : len)) : 0;
-  BalLens r;
-  r.n = (len + unit - 1) / unit;
-  int x = r.n, m = r.n;
-#pragma unroll
-  for (int s = 1; s < 64; s <<= 1) {
-    const int y = __shfl_up(x, s, 64);
-    if (lane >= s) x += y;
-    m = max(m, __shfl_xor(m, s, 64));
-  }
-  r.pre = x - r.n;
-  r.NB = __builtin_amdgcn_readlane(x, 63);
-  r.nmax = __builtin_amdgcn_readfirstlane(m);
-  return r;
-}
-// The chunk for a call of H heads (N = H NB tiles in all).
-__device__ __forceinline__ int bal_chunk(const BalLens& L, int H, int nwg, int pmax) {
-  const int N = H * L.NB;
-  int c = (N + nwg - 1) / nwg;
-  c = max(c, kBalMinTiles);
-  c = max(c, (L.nmax + pmax - 2) / (pmax - 1));
-  return c;
-}
-// Pieces of sequence b (its lane values n, pre read into the wave) under head h.
-__device__ __forceinline__ int bal_pieces(int n_b, int pre_b, int NB, int h, int c) {
-  if (n_b <= 0) return 0;
-  const int P = h * NB + pre_b;
-  return (P + n_b - 1) / c - P / c + 1;
-}
-
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);

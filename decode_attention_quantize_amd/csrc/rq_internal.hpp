@@ -34,14 +34,6 @@ struct SplitPlan {
 };
 SplitPlan split_plan(const rq_desc* d);
 
-// Balanced partition for the fused decode call (rq_device.hpp, bal_*): used where
-// the slots above would load the compute units unevenly. nwg = 0: not used.
-struct BalPlan {
-  int nwg;   // workgroups of the streaming launch
-  int pmax;  // most pieces of one (b, h), the partial rows per (b, h)
-};
-BalPlan bal_plan(const rq_desc* d);
-
 __host__ __device__ inline int slot_len(int len, int nsplit, int unit) {
   int c = (len + nsplit - 1) / nsplit;
   c = (c + unit - 1) / unit * unit;
@@ -72,7 +64,6 @@ struct CombineParams {
   float scale_log2;         // softmax scale * log2(e)
   int B, H, T_max, unit, nsplit;
   int rot_f16;              // rotv holds fp16 entries
-  int nwg;                  // > 0: balanced partition over nwg workgroups, nsplit = pieces per (b, h)
 };
 
 struct DecodeParams {
@@ -89,8 +80,6 @@ struct DecodeParams {
   float scale_log2;
   int B, H, T_max, unit, nsplit;
   int rot_f16;                        // rotk holds fp16 entries
-  int nwg;                            // > 0: balanced partition over nwg workgroups (rq_device.hpp),
-                                      // nsplit = the most pieces of one (b, h); 0: nsplit slots per (b, h)
   // paged cache (table == nullptr: contiguous): block table [B][maxblk], block
   // size 2^lbs tokens, pool of num_blocks blocks = pool_rows rows per buffer
   const int32_t* table;

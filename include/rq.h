@@ -240,15 +240,7 @@ rq_status rq_quantize_append_layers(const rq_desc* desc, const rq_layer_cache* c
  * Two kernel launches: every workgroup of the first rotates the query
  * (q' = scale H_K q), scores a contiguous range of cached tokens against the
  * rotated keys and accumulates the rotated value sum; the second merges the
- * ranges of each (b, h) with the current token and applies H_V^T once.
- * The ranges are the slots of rq_split_plan, except where those would give
- * some compute units a whole slot more than others (B H nsplit above the unit
- * count and at least 8 % uneven) for a contiguous cache with B <= 64 and a plan
- * of one or two components (every Last-loop and First-loop decode): then the
- * tiles of all (b, h), laid end to end, are cut into equal chunks, two per
- * compute unit, and a workgroup scores the piece of each (b, h) its chunk
- * meets. The result is the same attention up to fp32 rounding (another merge
- * order than rq_decode_attn_partial + rq_decode_combine). */
+ * ranges of each (b, h) with the current token and applies H_V^T once. */
 rq_status rq_decode_attn(const rq_desc* desc, const rq_layer_cache* cache, int32_t loop,
                          const uint16_t* q, const uint16_t* k_cur, const uint16_t* v_cur,
                          const int32_t* past_len, float softmax_scale, float* out,
@@ -267,8 +259,7 @@ rq_status rq_split_plan(const rq_desc* desc, int32_t* unit, int32_t* nsplit);
  * partial results themselves (for instance over a token axis split across
  * devices, or with partials of another cache) or time the streaming kernel
  * alone. rq_decode_attn(...) is exactly rq_decode_attn_partial(...) followed by
- * rq_decode_combine(..., cache->rot[1], ...) on the same stream and workspace,
- * bit for bit, wherever it uses the slots (see rq_decode_attn).
+ * rq_decode_combine(..., cache->rot[1], ...) on the same stream and workspace.
  *
  * rq_decode_attn_partial: rotates q (q' = scale H_K q) and scores the cached
  *   tokens of each slot that holds any of the past_len[b] tokens (slot 0 always
