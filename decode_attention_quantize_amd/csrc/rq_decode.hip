@@ -16,9 +16,10 @@ namespace {
 // spread over D / COLS workgroups (COLS = 32), each producing COLS output
 // columns from a D x COLS block of H_V (16 KB at D = 128), so that no compute
 // unit waits for a whole matrix; each merges all D elements of the partials (a
-// few hundred bytes per slot). With many (b, h), or no rotation, one workgroup
-// per (b, h) (COLS = D) costs less: more workgroups than compute units only add
-// to the launch. split_item places a (b, h)'s workgroups on the XCD whose
+// few hundred bytes per slot). At D = 128, where D / 32 workgroups per (b, h)
+// would exceed the compute units but two would not, COLS = 64. With more (b, h),
+// or no rotation, one workgroup per (b, h) (COLS = D) costs less: more
+// workgroups than compute units only add to the launch. split_item places a (b, h)'s workgroups on the XCD whose
 // workgroups wrote its partials (both launches map consecutive (b, h) blocks to
 // XCDs in proportion, when their workgroup counts are multiples of the XCD
 // count), where the partials are still in L2.
@@ -162,8 +163,10 @@ int launch_decode(const DecodeParams& p, int D, int nc, const int* bits, int lim
 
 namespace {
 template <int D, int RH>
-void launch_combine_d(const CombineParams& p, bool narrow, const dim3& grid, hipStream_t s) {
-  if (narrow) hipLaunchKernelGGL((combine_kernel<D, 32, RH>), grid, dim3(kThreads), 0, s, p);
+void launch_combine_d(const CombineParams& p, int cols, const dim3& grid, hipStream_t s) {
+  if (cols == 32) hipLaunchKernelGGL((combine_kernel<D, 32, RH>), grid, dim3(kThreads), 0, s, p);
+  else if (cols == 64 && D == 128)  // (D == 128 ? 64 : D) only instantiates what D divides
+    hipLaunchKernelGGL((combine_kernel<D, (D == 128 ? 64 : D), RH>), grid, dim3(kThreads), 0, s, p);
   else hipLaunchKernelGGL((combine_kernel<D, D, RH>), grid, dim3(kThreads), 0, s, p);
 }
 }  // namespace
@@ -171,12 +174,12 @@ void launch_combine_d(const CombineParams& p, bool narrow, const dim3& grid, hip
 int launch_combine(const CombineParams& p, int D, int cols, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid((unsigned)(p.B * p.H * (D / cols)));
-  const bool narrow = cols != D, rh = p.rot_f16 && p.rotv;
+  const bool rh = p.rot_f16 && p.rotv;
   switch (D) {
-    case 64: rh ? launch_combine_d<64, 1>(p, narrow, grid, s) : launch_combine_d<64, 0>(p, narrow, grid, s); break;
-    case 96: rh ? launch_combine_d<96, 1>(p, narrow, grid, s) : launch_combine_d<96, 0>(p, narrow, grid, s); break;
+    case 64: rh ? launch_combine_d<64, 1>(p, cols, grid, s) : launch_combine_d<64, 0>(p, cols, grid, s); break;
+    case 96: rh ? launch_combine_d<96, 1>(p, cols, grid, s) : launch_combine_d<96, 0>(p, cols, grid, s); break;
     case 128:
-      rh ? launch_combine_d<128, 1>(p, narrow, grid, s) : launch_combine_d<128, 0>(p, narrow, grid, s);
+      rh ? launch_combine_d<128, 1>(p, cols, grid, s) : launch_combine_d<128, 0>(p, cols, grid, s);
       break;
     default: return -1;
   }
